@@ -1,0 +1,192 @@
+"""fp64 CPU oracle of the gated delta rule -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this module.  The product path (the HIP library and its Python binding)
+never calls it, and it shares no code with that path.
+
+What it computes, token by token and head by head, in float64:
+
+    S~_t = alpha_t * S_{t-1}                      decay first
+    vhat = S~_t k_t                               prediction of the decayed state
+    S_t  = S~_t + beta_t (v_t - vhat) k_t^T       delta write
+    o_t  = S_t q_t                                readout of the new state
+
+which equals S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T.
+
+Sources (page titles as published; sections/equations as the pages give them):
+  * DeltaNet write and readout, o_t = S_t q_t, S in R^{dv x dk}:
+    "On State Reduction in Linear Attention" (reading notes), Sec. 2.1,
+    Eqs. (1)-(2); gated variant adds a per-token scalar decay (same section)
+    and the update is written alpha_t S_{t-1} + u_t k_t^T in the proof of the
+    rank bound, Eq. (3).
+  * Ordering "decay, then compare with the target using the decayed state,
+    then write, then read the new state": "Linear Attention Architectures:
+    Mechanisms, Trade-offs, and Cross-Layer Routing" (reading notes),
+    Sec. 3.3 (GDN, Eqs. 15-17) and the per-token data flow of Eq. 8.
+  * Stable rank er(S) = ||S||_F^2 / ||S||_2^2: "On State Reduction in Linear
+    Attention", Sec. 2.2, Eq. (5); entropy effective rank and the numerical
+    rank threshold sigma_max * 128 * eps: "How much of its state does Gated
+    DeltaNet use?" (state-rank post), §1.
+  * Segment truncation (project the carried state onto its top-r left
+    singular directions at every 256-token boundary, r = 128 = no change):
+    state-rank post, §3.
+
+Readings where the pages leave a step open (each also listed in the design doc):
+  * No query scale: o_t = S_t q_t exactly.
+  * alpha is given (not log alpha), in (0, 1]; beta in [0, 1].
+  * Truncation happens only at boundaries between segments (t = 256 m with
+    t < T), never after the last token.
+"""
+
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# the recurrence
+# ---------------------------------------------------------------------------
+
+def gdn_head(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+             alpha: np.ndarray, beta: np.ndarray,
+             S0: Optional[np.ndarray] = None, *, erase: bool = True,
+             trunc_r: Optional[int] = None, trunc_every: int = 256
+             ) -> Tuple[np.ndarray, np.ndarray]:
+    """One head, one sequence.
+
+    q, k [T, dk]; v [T, dv]; alpha, beta [T]; S0 [dv, dk] or None (zero).
+    erase=False drops the erase term (S_t = alpha S_{t-1} + beta v k^T), used
+    only to pin the additive special case.
+    trunc_r: if set, after token t (1-based) with t % trunc_every == 0 and
+    t < T, replace S by its projection onto its top-trunc_r left singular
+    directions.
+    Returns o [T, dv], S_T [dv, dk] (float64).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    T, dk = k.shape
+    dv = v.shape[1]
+    S = np.zeros((dv, dk)) if S0 is None else np.array(S0, np.float64)
+    o = np.empty((T, dv))
+    for t in range(T):
+        S *= float(alpha[t])                       # decay first
+        if erase:
+            vhat = S @ k[t]                        # predict with decayed state
+            S += float(beta[t]) * np.outer(v[t] - vhat, k[t])
+        else:
+            S += float(beta[t]) * np.outer(v[t], k[t])
+        o[t] = S @ q[t]                            # read the new state
+        if trunc_r is not None and (t + 1) % trunc_every == 0 and t + 1 < T:
+            S = truncate_rank(S, trunc_r)
+    return o, S
+
+
+def gdn_prefill(q, k, v, alpha, beta, S0=None, *, erase=True, trunc_r=None,
+                trunc_every=256, heads=None):
+    """Batched layout: q, k [B, T, H, dk]; v [B, T, H, dv]; alpha, beta
+    [B, T, H]; S0 [B, H, dv, dk] or None.  Returns o [B, T, H, dv] and
+    S_T [B, H, dv, dk] (float64).  `heads`: optional list of (b, h) pairs to
+    compute (others are left as NaN) -- for sampled checks at full size."""
+    B, T, H, dk = np.shape(q)
+    dv = np.shape(v)[-1]
+    o = np.full((B, T, H, dv), np.nan)
+    ST = np.full((B, H, dv, dk), np.nan)
+    todo = heads if heads is not None else [(b, h) for b in range(B)
+                                            for h in range(H)]
+    for b, h in todo:
+        s0 = None if S0 is None else S0[b, h]
+        o[b, :, h], ST[b, h] = gdn_head(
+            q[b, :, h], k[b, :, h], v[b, :, h], alpha[b, :, h],
+            beta[b, :, h], s0, erase=erase, trunc_r=trunc_r,
+            trunc_every=trunc_every)
+    return o, ST
+
+
+def gdn_decode_step(q, k, v, alpha, beta, S):
+    """One token for a batch of carried states: q, k [B, H, dk]; v [B, H, dv];
+    alpha, beta [B, H]; S [B, H, dv, dk].  Returns o [B, H, dv], S' (fp64)."""
+    B, H, dk = np.shape(q)
+    dv = np.shape(v)[-1]
+    o = np.empty((B, H, dv))
+    S1 = np.empty((B, H, dv, dk))
+    for b in range(B):
+        for h in range(H):
+            ob, Sb = gdn_head(np.asarray(q)[b, h][None], np.asarray(k)[b, h][None],
+                              np.asarray(v)[b, h][None],
+                              np.asarray(alpha)[b, h][None],
+                              np.asarray(beta)[b, h][None], S[b, h])
+            o[b, h], S1[b, h] = ob[0], Sb
+    return o, S1
+
+
+# ---------------------------------------------------------------------------
+# spectral quantities and truncation
+# ---------------------------------------------------------------------------
+
+def singular_values(S: np.ndarray) -> np.ndarray:
+    return np.linalg.svd(np.asarray(S, np.float64), compute_uv=False)
+
+
+def stable_rank(S: np.ndarray) -> float:
+    """er(S) = ||S||_F^2 / sigma_1^2 (NaN for S == 0, where it is undefined)."""
+    s = singular_values(S)
+    if s[0] == 0.0:
+        return float("nan")
+    return float(np.sum(s ** 2) / s[0] ** 2)
+
+
+def utilisation(S: np.ndarray) -> float:
+    """u(S) = er(S) / min(dv, dk)."""
+    return stable_rank(S) / min(np.shape(S))
+
+
+def condition_number(S: np.ndarray) -> float:
+    """sigma_1 / sigma_min over the min(dv, dk) singular values."""
+    s = singular_values(S)
+    return float(s[0] / s[-1])
+
+
+def entropy_erank(S: np.ndarray) -> float:
+    """exp(-sum p_i log p_i), p_i = sigma_i / sum_j sigma_j (0 log 0 = 0)."""
+    s = singular_values(S)
+    p = s / np.sum(s)
+    p = p[p > 0]
+    return float(np.exp(-np.sum(p * np.log(p))))
+
+
+def numerical_rank(S: np.ndarray, eps: float = 2.0 ** -23,
+                   factor: float = 128.0) -> int:
+    """Count of sigma_i > sigma_max * factor * eps (fp32 eps by default)."""
+    s = singular_values(S)
+    return int(np.sum(s > s[0] * factor * eps))
+
+
+def truncate_rank(S: np.ndarray, r: int) -> np.ndarray:
+    """U_r U_r^T S with U_r the top-r left singular vectors (fp64 SVD).
+    r >= min(dv, dk) returns S unchanged."""
+    S = np.asarray(S, np.float64)
+    if r >= min(S.shape):
+        return S.copy()
+    U, _, _ = np.linalg.svd(S, full_matrices=False)
+    Ur = U[:, :r]
+    return Ur @ (Ur.T @ S)
+
+
+# ---------------------------------------------------------------------------
+# comparison metric
+# ---------------------------------------------------------------------------
+
+def rel_l2_per_head(x: np.ndarray, ref: np.ndarray, head_axes) -> np.ndarray:
+    """||x - ref||_2 / ||ref||_2 per head.
+
+    head_axes: the axes that index a head, e.g. (0, 2) for o [B, T, H, dv]
+    and (0, 1) for S [B, H, dv, dk].  Returns an array over those axes."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    red = tuple(a for a in range(ref.ndim) if a not in head_axes)
+    num = np.sqrt(np.sum((x - ref) ** 2, axis=red))
+    den = np.sqrt(np.sum(ref ** 2, axis=red))
+    return num / np.maximum(den, 1e-300)
