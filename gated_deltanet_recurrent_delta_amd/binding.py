@@ -1,0 +1,233 @@
+"""ctypes binding of libgdn.so (argument marshalling only).
+
+Every step of the recurrence runs in the library's HIP kernels; this module
+only checks tensor metadata, allocates outputs with PyTorch (device memory and
+streams are PyTorch's), and passes raw device pointers plus the current
+stream to the C ABI declared in include/gdn.h.  If the library is not built,
+importing this module raises ImportError: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch  # loaded first so libgdn binds to the HIP runtime torch uses
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_OK, GDN_EINVAL, GDN_ESHAPE, GDN_EWORKSPACE, GDN_EHIP = range(5)
+GDN_F32, GDN_BF16 = 0, 1
+_DTYPE_CODE = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+# name -> (restype, argtypes); the single source of the ABI on this side
+SIGNATURES = {
+    "gdn_status_str": (ctypes.c_char_p, [_i]),
+    "gdn_version": (ctypes.c_char_p, []),
+    "gdn_prefill_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "gdn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                         _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "gdn_prefill_prepare": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                                 _vp, _sz, _vp]),
+    "gdn_prefill_scan": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
+                              _i, _i, _i, _vp, _sz, _vp]),
+    "gdn_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _i, _i, _i, _i, _i, _i, _vp]),
+}
+
+
+class GdnError(RuntimeError):
+    """A non-zero status returned by libgdn."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)}")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run "
+            "`python -m gated_deltanet_recurrent_delta_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def status_str(status: int) -> str:
+    return lib.gdn_status_str(status).decode()
+
+
+def version() -> str:
+    return lib.gdn_version().decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != GDN_OK:
+        raise GdnError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(t: torch.Tensor, stream=None):
+    s = torch.cuda.current_stream(t.device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev_tensor(t: torch.Tensor, name: str, dtypes, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    return t
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+
+def prefill_workspace_bytes(B: int, T: int, H: int, dk: int, dv: int) -> int:
+    return int(lib.gdn_prefill_workspace_bytes(B, T, H, dk, dv))
+
+
+def _prefill_args(q, k, v, alpha, beta, S0):
+    _dev_tensor(q, "q", _DTYPE_CODE)
+    B, T, H, dk = q.shape
+    _dev_tensor(k, "k", (q.dtype,), q.shape)
+    _dev_tensor(v, "v", (q.dtype,))
+    if tuple(v.shape[:3]) != (B, T, H) or v.dim() != 4:
+        raise ValueError(f"v: shape {tuple(v.shape)} incompatible with q")
+    dv = v.shape[3]
+    _dev_tensor(alpha, "alpha", (torch.float32,), (B, T, H))
+    _dev_tensor(beta, "beta", (torch.float32,), (B, T, H))
+    if S0 is not None:
+        _dev_tensor(S0, "S0", (torch.float32,), (B, H, dv, dk))
+    return B, T, H, dk, dv
+
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+            alpha: torch.Tensor, beta: torch.Tensor,
+            S0: Optional[torch.Tensor] = None, *,
+            out_dtype: Optional[torch.dtype] = None,
+            o: Optional[torch.Tensor] = None,
+            ST: Optional[torch.Tensor] = None,
+            final_state: bool = True,
+            workspace: Optional[torch.Tensor] = None,
+            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Gated delta rule over whole sequences.
+
+    q, k [B, T, H, dk], v [B, T, H, dv] (float32 or bfloat16, same dtype);
+    alpha, beta [B, T, H] float32; S0 [B, H, dv, dk] float32 or None.
+    Returns (o [B, T, H, dv] in out_dtype (default: q's dtype), S_T or None).
+    ST may be S0 (in-place update).  `workspace`: optional uint8 GPU tensor
+    of at least prefill_workspace_bytes(...) bytes.
+    """
+    B, T, H, dk, dv = _prefill_args(q, k, v, alpha, beta, S0)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=q.device)
+    _dev_tensor(o, "o", (out_dtype,), (B, T, H, dv))
+    if ST is None and final_state:
+        ST = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    if ST is not None:
+        _dev_tensor(ST, "ST", (torch.float32,), (B, H, dv, dk))
+    need = prefill_workspace_bytes(B, T, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib.gdn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                         _ptr(S0), _ptr(o), _ptr(ST), B, T, H, dk, dv,
+                         _DTYPE_CODE[q.dtype], _DTYPE_CODE[out_dtype],
+                         _ptr(workspace), workspace.numel(),
+                         _stream_handle(q, stream))
+    _check(st, "gdn_prefill")
+    return o, ST
+
+
+def prefill_prepare(q, k, alpha, beta, dv: int, workspace: torch.Tensor,
+                    stream=None) -> None:
+    """First phase of prefill (chunk-local, state independent) into
+    `workspace`; see include/gdn.h."""
+    _dev_tensor(q, "q", _DTYPE_CODE)
+    B, T, H, dk = q.shape
+    _dev_tensor(k, "k", (q.dtype,), q.shape)
+    _dev_tensor(alpha, "alpha", (torch.float32,), (B, T, H))
+    _dev_tensor(beta, "beta", (torch.float32,), (B, T, H))
+    st = lib.gdn_prefill_prepare(_ptr(q), _ptr(k), _ptr(alpha), _ptr(beta),
+                                 B, T, H, dk, dv, _DTYPE_CODE[q.dtype],
+                                 _ptr(workspace), workspace.numel(),
+                                 _stream_handle(q, stream))
+    _check(st, "gdn_prefill_prepare")
+
+
+def prefill_scan(q, k, v, S0, o, ST, workspace: torch.Tensor,
+                 stream=None) -> None:
+    """Second phase of prefill (sequential over chunks) reading the
+    workspace written by prefill_prepare; see include/gdn.h."""
+    _dev_tensor(q, "q", _DTYPE_CODE)
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    _dev_tensor(o, "o", _DTYPE_CODE, (B, T, H, dv))
+    st = lib.gdn_prefill_scan(_ptr(q), _ptr(k), _ptr(v), _ptr(S0), _ptr(o),
+                              _ptr(ST), B, T, H, dk, dv, _DTYPE_CODE[q.dtype],
+                              _DTYPE_CODE[o.dtype], _ptr(workspace),
+                              workspace.numel(), _stream_handle(q, stream))
+    _check(st, "gdn_prefill_scan")
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                alpha: torch.Tensor, beta: torch.Tensor, S: torch.Tensor, *,
+                S_out: Optional[torch.Tensor] = None,
+                o: Optional[torch.Tensor] = None,
+                out_dtype: Optional[torch.dtype] = None,
+                stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """One token for a batch of carried states.
+
+    q, k [B, H, dk], v [B, H, dv] (float32 or bfloat16); alpha, beta [B, H]
+    float32; S [B, H, dv, dk] float32.  S_out may be S (in place; the
+    default allocates a new state).  Returns (o [B, H, dv], S_out).
+    """
+    _dev_tensor(q, "q", _DTYPE_CODE)
+    B, H, dk = q.shape
+    _dev_tensor(k, "k", (q.dtype,), q.shape)
+    _dev_tensor(v, "v", (q.dtype,))
+    if v.dim() != 3 or tuple(v.shape[:2]) != (B, H):
+        raise ValueError(f"v: shape {tuple(v.shape)} incompatible with q")
+    dv = v.shape[2]
+    _dev_tensor(alpha, "alpha", (torch.float32,), (B, H))
+    _dev_tensor(beta, "beta", (torch.float32,), (B, H))
+    _dev_tensor(S, "S", (torch.float32,), (B, H, dv, dk))
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=out_dtype, device=q.device)
+    _dev_tensor(o, "o", (out_dtype,), (B, H, dv))
+    if S_out is None:
+        S_out = torch.empty_like(S)
+    _dev_tensor(S_out, "S_out", (torch.float32,), (B, H, dv, dk))
+    st = lib.gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                             _ptr(beta), _ptr(S), _ptr(S_out), _ptr(o),
+                             B, H, dk, dv, _DTYPE_CODE[q.dtype],
+                             _DTYPE_CODE[out_dtype], _stream_handle(q, stream))
+    _check(st, "gdn_decode_step")
+    return o, S_out

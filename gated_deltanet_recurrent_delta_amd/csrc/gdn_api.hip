@@ -1,0 +1,150 @@
+// Exported C ABI of libgdn (declared in include/gdn.h): argument validation,
+// workspace sizing and dispatch to the gfx950 kernels.  Validation happens
+// before any HIP call, so argument errors can be tested without a GPU.
+#include <stdint.h>
+
+#include "../../include/gdn.h"
+#include "gdn_launch.hpp"
+
+namespace {
+
+bool dtype_ok(int d) { return d == GDN_F32 || d == GDN_BF16; }
+bool dims_ok(int dk, int dv) {
+  return (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
+}
+bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+int to_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_EHIP; }
+
+size_t prefill_ws_bytes(int B, int T, int H) {
+  if (B <= 0 || H <= 0 || T <= 0) return 0;
+  const size_t nchunks = ((size_t)T + gdn::kChunk - 1) / gdn::kChunk;
+  return (size_t)B * H * nchunks * gdn::kChunkWsFloats * sizeof(float);
+}
+
+// Common shape/dtype checks of the prefill entry points.
+int check_prefill_shape(int B, int T, int H, int dk, int dv, int in_dtype,
+                        int out_dtype) {
+  if (B <= 0 || H <= 0 || T < 0) return GDN_EINVAL;
+  if (B > 65535 || H > 65535) return GDN_EINVAL;     // grid y/z limits
+  if ((long long)B * H * (dv / 16) > 0x7FFFFFFFLL) return GDN_EINVAL;
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return GDN_ESHAPE;
+  if (!dims_ok(dk, dv)) return GDN_ESHAPE;
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_str(int status) {
+  switch (status) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_EINVAL: return "GDN_EINVAL: invalid argument (null pointer, bad size or misaligned buffer)";
+    case GDN_ESHAPE: return "GDN_ESHAPE: unsupported head size or dtype (dk, dv in {64, 128}; f32 or bf16)";
+    case GDN_EWORKSPACE: return "GDN_EWORKSPACE: workspace missing or smaller than gdn_prefill_workspace_bytes()";
+    case GDN_EHIP: return "GDN_EHIP: HIP launch failed";
+    default: return "GDN_UNKNOWN_STATUS";
+  }
+}
+
+const char* gdn_version(void) { return "0.1.0"; }
+
+size_t gdn_prefill_workspace_bytes(int B, int T, int H, int dk, int dv) {
+  (void)dk;
+  (void)dv;
+  return prefill_ws_bytes(B, T, H);
+}
+
+int gdn_prefill_prepare(const void* q, const void* k, const float* alpha,
+                        const float* beta, int B, int T, int H, int dk, int dv,
+                        int in_dtype, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  int st = check_prefill_shape(B, T, H, dk, dv, in_dtype, GDN_F32);
+  if (st != GDN_OK) return st;
+  if (T == 0) return GDN_OK;
+  if (!q || !k || !alpha || !beta) return GDN_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(alpha, 4) ||
+      !aligned(beta, 4))
+    return GDN_EINVAL;
+  if (!workspace || !aligned(workspace, 16)) return GDN_EWORKSPACE;
+  if (workspace_bytes < prefill_ws_bytes(B, T, H)) return GDN_EWORKSPACE;
+  return to_status(gdn::launch_prefill_prepare(
+      q, k, alpha, beta, static_cast<float*>(workspace), B, T, H, dk, in_dtype,
+      static_cast<hipStream_t>(stream)));
+}
+
+int gdn_prefill_scan(const void* q, const void* k, const void* v,
+                     const float* S0, void* o, float* ST, int B, int T, int H,
+                     int dk, int dv, int in_dtype, int out_dtype,
+                     const void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  int st = check_prefill_shape(B, T, H, dk, dv, in_dtype, out_dtype);
+  if (st != GDN_OK) return st;
+  if ((S0 && !aligned(S0, 16)) || (ST && !aligned(ST, 16))) return GDN_EINVAL;
+  const size_t nstate = (size_t)B * H * dv * dk;
+  if (ST && S0 && ST != S0 &&
+      (ST < S0 + nstate && S0 < ST + nstate))
+    return GDN_EINVAL;                               // partial overlap
+  if (T == 0)
+    return to_status(gdn::launch_state_fill(S0, ST, nstate,
+                                            static_cast<hipStream_t>(stream)));
+  if (!q || !k || !v || !o) return GDN_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+      !aligned(o, 16))
+    return GDN_EINVAL;
+  if (!workspace || !aligned(workspace, 16)) return GDN_EWORKSPACE;
+  if (workspace_bytes < prefill_ws_bytes(B, T, H)) return GDN_EWORKSPACE;
+  return to_status(gdn::launch_prefill_scan(
+      q, k, v, S0, o, ST, static_cast<const float*>(workspace), B, T, H, dk,
+      dv, in_dtype, out_dtype, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_prefill(const void* q, const void* k, const void* v,
+                const float* alpha, const float* beta, const float* S0,
+                void* o, float* ST, int B, int T, int H, int dk, int dv,
+                int in_dtype, int out_dtype, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  int st = check_prefill_shape(B, T, H, dk, dv, in_dtype, out_dtype);
+  if (st != GDN_OK) return st;
+  if (T > 0) {
+    // validate everything the scan needs before launching the prepare
+    if (!q || !k || !v || !o || !alpha || !beta) return GDN_EINVAL;
+    if (!aligned(v, 16) || !aligned(o, 16)) return GDN_EINVAL;
+    if ((S0 && !aligned(S0, 16)) || (ST && !aligned(ST, 16)))
+      return GDN_EINVAL;
+    const size_t nstate = (size_t)B * H * dv * dk;
+    if (ST && S0 && ST != S0 && (ST < S0 + nstate && S0 < ST + nstate))
+      return GDN_EINVAL;
+    st = gdn_prefill_prepare(q, k, alpha, beta, B, T, H, dk, dv, in_dtype,
+                             workspace, workspace_bytes, stream);
+    if (st != GDN_OK) return st;
+  }
+  return gdn_prefill_scan(q, k, v, S0, o, ST, B, T, H, dk, dv, in_dtype,
+                          out_dtype, workspace, workspace_bytes, stream);
+}
+
+int gdn_decode_step(const void* q, const void* k, const void* v,
+                    const float* alpha, const float* beta, const float* S_in,
+                    float* S_out, void* o, int B, int H, int dk, int dv,
+                    int in_dtype, int out_dtype, void* stream) {
+  if (B <= 0 || H <= 0) return GDN_EINVAL;
+  if ((long long)B * H * dv > 0x7FFFFFFFLL) return GDN_EINVAL;
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return GDN_ESHAPE;
+  if (!dims_ok(dk, dv)) return GDN_ESHAPE;
+  if (!q || !k || !v || !alpha || !beta || !S_in || !S_out || !o)
+    return GDN_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+      !aligned(o, 16) || !aligned(S_in, 16) || !aligned(S_out, 16) ||
+      !aligned(alpha, 4) || !aligned(beta, 4))
+    return GDN_EINVAL;
+  const size_t nstate = (size_t)B * H * dv * dk;
+  if (S_out != S_in && S_out < S_in + nstate && S_in < S_out + nstate)
+    return GDN_EINVAL;                               // partial overlap
+  return to_status(gdn::launch_decode(q, k, v, alpha, beta, S_in, S_out, o,
+                                      B * H, dk, dv, in_dtype, out_dtype,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,169 @@
+// Decode step of the gated delta rule: one token for a batch of carried
+// fp32 states, fused into a single streaming pass over each state row.
+//
+// Per state row s_i (value channel i, dk floats) of a head:
+//     p   = s_i . k          r  = s_i . q
+//     u_i = beta (v_i - alpha p)                 (error of the decayed state)
+//     s_i' = alpha s_i + u_i k                   (decay + delta write)
+//     o_i  = s_i' . q = alpha r + u_i (k . q)    (readout of the new state)
+// which is the per-row form of S' = alpha S (I - beta k k^T) + beta v k^T,
+// o = S' q ("On State Reduction in Linear Attention", Sec. 2.1, Eq. (2) with
+// the gated decay; rows evolve independently, Sec. 3.1).
+//
+// The step is HBM-bound (each state byte is read once and written once, at
+// 0.75 flop/byte), so the kernel is a coalesced stream: 8 lanes cover one row
+// with 16-byte loads (each wave instruction touches 8 full 128-byte lines),
+// every load of a wave is issued before any reduction, the two row dot
+// products are reduced with three DPP steps, and the state is written back
+// with non-temporal stores.
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+
+// DK: key width; G: row groups of 8 rows per wave (rows per wave = 8 G).
+template <int DK, int G, typename TIn, typename TOut>
+__global__ __launch_bounds__(256) void decode_kernel(
+    const TIn* __restrict__ q, const TIn* __restrict__ k,
+    const TIn* __restrict__ v, const float* __restrict__ alpha,
+    const float* __restrict__ beta, const float* S_in, float* S_out,
+    TOut* __restrict__ o, int BH, int dv, int slices_per_head) {
+  constexpr int F = DK / 32;            // float4 per lane per row
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int head = wave / slices_per_head;
+  if (head >= BH) return;
+  const int slice = wave - head * slices_per_head;
+  const int sub = lane & 7;             // column lane within the row
+  const int rg = lane >> 3;             // row within a group of 8
+  const int row0 = slice * (8 * G);
+
+  const size_t sbase = (size_t)head * dv * DK;
+  floatx4 s[G][F];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float* rowp = S_in + sbase + (size_t)(row0 + 8 * g + rg) * DK;
+#pragma unroll
+    for (int f = 0; f < F; ++f)
+      s[g][f] = __builtin_nontemporal_load(
+          reinterpret_cast<const floatx4*>(rowp + 32 * f + 4 * sub));
+  }
+
+  float4 kk[F], qq[F];
+#pragma unroll
+  for (int f = 0; f < F; ++f) {
+    kk[f] = load4(k + (size_t)head * DK + 32 * f + 4 * sub);
+    qq[f] = load4(q + (size_t)head * DK + 32 * f + 4 * sub);
+  }
+  const float a = alpha[head];
+  const float b = beta[head];
+  float vv[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) vv[g] = load1(v + (size_t)head * dv + row0 + 8 * g + rg);
+
+  float kq = 0.f;
+#pragma unroll
+  for (int f = 0; f < F; ++f)
+    kq += kk[f].x * qq[f].x + kk[f].y * qq[f].y + kk[f].z * qq[f].z +
+          kk[f].w * qq[f].w;
+  kq = sum8(kq);
+
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float p = 0.f, r = 0.f;
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      p += s[g][f][0] * kk[f].x + s[g][f][1] * kk[f].y + s[g][f][2] * kk[f].z +
+           s[g][f][3] * kk[f].w;
+      r += s[g][f][0] * qq[f].x + s[g][f][1] * qq[f].y + s[g][f][2] * qq[f].z +
+           s[g][f][3] * qq[f].w;
+    }
+    p = sum8(p);
+    r = sum8(r);
+    const float u = b * (vv[g] - a * p);
+    const int row = row0 + 8 * g + rg;
+    float* rowp = S_out + sbase + (size_t)row * DK;
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      floatx4 n;
+      n[0] = a * s[g][f][0] + u * kk[f].x;
+      n[1] = a * s[g][f][1] + u * kk[f].y;
+      n[2] = a * s[g][f][2] + u * kk[f].z;
+      n[3] = a * s[g][f][3] + u * kk[f].w;
+      __builtin_nontemporal_store(n, reinterpret_cast<floatx4*>(rowp + 32 * f + 4 * sub));
+    }
+    if (sub == 0) store1(o + (size_t)head * dv + row, a * r + u * kq);
+  }
+}
+
+template <int DK, int G, typename TIn, typename TOut>
+static void launch_decode_g(dim3 grid, hipStream_t stream, const void* q,
+                            const void* k, const void* v, const float* alpha,
+                            const float* beta, const float* S_in, float* S_out,
+                            void* o, int BH, int dv, int slices) {
+  hipLaunchKernelGGL((decode_kernel<DK, G, TIn, TOut>), grid, dim3(256), 0,
+                     stream, static_cast<const TIn*>(q),
+                     static_cast<const TIn*>(k), static_cast<const TIn*>(v),
+                     alpha, beta, S_in, S_out, static_cast<TOut*>(o), BH, dv,
+                     slices);
+}
+
+template <int DK, typename TIn, typename TOut>
+static hipError_t launch_decode_t(const void* q, const void* k, const void* v,
+                                  const float* alpha, const float* beta,
+                                  const float* S_in, float* S_out, void* o,
+                                  int BH, int dv, hipStream_t stream) {
+  // Rows per wave: as many as keep >= 2048 waves (2 per SIMD) in flight,
+  // capped so that a lane holds at most 64 state floats.
+  constexpr int GMAX = DK == 128 ? 4 : 8;
+  int G = GMAX;
+  while (G > 1 && (long)BH * dv / (8 * G) < 2048) G /= 2;
+  const int slices = dv / (8 * G);
+  const long waves = (long)BH * slices;
+  const dim3 grid((unsigned)((waves + 3) / 4));
+  switch (G) {
+    case 1:
+      launch_decode_g<DK, 1, TIn, TOut>(grid, stream, q, k, v, alpha, beta,
+                                        S_in, S_out, o, BH, dv, slices);
+      break;
+    case 2:
+      launch_decode_g<DK, 2, TIn, TOut>(grid, stream, q, k, v, alpha, beta,
+                                        S_in, S_out, o, BH, dv, slices);
+      break;
+    case 4:
+      launch_decode_g<DK, 4, TIn, TOut>(grid, stream, q, k, v, alpha, beta,
+                                        S_in, S_out, o, BH, dv, slices);
+      break;
+    default:
+      if constexpr (GMAX == 8)
+        launch_decode_g<DK, 8, TIn, TOut>(grid, stream, q, k, v, alpha, beta,
+                                          S_in, S_out, o, BH, dv, slices);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const void* q, const void* k, const void* v,
+                         const float* alpha, const float* beta,
+                         const float* S_in, float* S_out, void* o, int BH,
+                         int dk, int dv, int in_dtype, int out_dtype,
+                         hipStream_t stream) {
+#define GDN_DEC_DT(DK, TI, TO)                                               \
+  return launch_decode_t<DK, TI, TO>(q, k, v, alpha, beta, S_in, S_out, o,   \
+                                     BH, dv, stream)
+  const bool ib = in_dtype == 1, ob = out_dtype == 1;
+  if (dk == 128) {
+    if (ib && ob) GDN_DEC_DT(128, bf16, bf16);
+    if (ib && !ob) GDN_DEC_DT(128, bf16, float);
+    if (!ib && ob) GDN_DEC_DT(128, float, bf16);
+    GDN_DEC_DT(128, float, float);
+  } else {
+    if (ib && ob) GDN_DEC_DT(64, bf16, bf16);
+    if (ib && !ob) GDN_DEC_DT(64, bf16, float);
+    if (!ib && ob) GDN_DEC_DT(64, float, bf16);
+    GDN_DEC_DT(64, float, float);
+  }
+#undef GDN_DEC_DT
+}
+
+}  // namespace gdn

@@ -1,0 +1,144 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) gated delta rule library, libgdn.so.
+ *
+ * The operation (per head, per token t):
+ *
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = S_t q_t
+ *
+ * i.e. decay the carried state, predict v_t from the DECAYED state, write
+ * beta_t times the prediction error along k_t, then read the NEW state with
+ * q_t.  Sources: "On State Reduction in Linear Attention" (reading notes),
+ * Sec. 2.1, Eqs. (1)-(2) (DeltaNet write, readout o_t = S_t q_t, state
+ * S in R^{dv x dk}) with the input-dependent decay of Gated DeltaNet; and
+ * "Linear Attention Architectures: Mechanisms, Trade-offs, and Cross-Layer
+ * Routing" (reading notes), Sec. 3.3, Eqs. 15-17 (decay first, then compare
+ * with the target, then write) and the per-token data flow of Eq. 8 (the
+ * output reads the updated state).  No query scale is applied.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer (hipMalloc'd or equivalent),
+ *    owned by the caller.  The library never allocates, frees or
+ *    synchronises inside these calls; work is enqueued on `stream` (a
+ *    hipStream_t passed as void*, NULL = the null stream) and completes
+ *    asynchronously.
+ *  - Layouts are dense, contiguous, row-major:
+ *        q, k   [B, T, H, dk]      v, o  [B, T, H, dv]
+ *        alpha, beta  [B, T, H]    S     [B, H, dv, dk]   (a state row is
+ *                                                          one value channel)
+ *    The decode step drops the T axis.
+ *  - q/k/v use `in_dtype` (GDN_F32 or GDN_BF16); o uses `out_dtype`;
+ *    alpha, beta and the state are always float32.
+ *  - Supported head sizes: dk in {64, 128} (dk = 64 is the channel-pruned,
+ *    "state halved" width of "On State Reduction in Linear Attention",
+ *    Sec. 3.2-3.3), dv in {64, 128}.
+ *  - Preconditions not checked (checking would cost a pass over the data):
+ *    q and k are already unit-L2-normalised (and already gathered to the
+ *    kept channels when pruned); alpha in (0, 1]; beta in [0, 1].  Outside
+ *    these ranges the same formula is applied but results are untested.
+ *  - Errors: argument errors are returned synchronously BEFORE any HIP call
+ *    (GDN_EINVAL: null pointer, negative size, zero B/H; GDN_ESHAPE:
+ *    unsupported dk/dv or dtype; GDN_EWORKSPACE: workspace too small).  A
+ *    failed launch returns GDN_EHIP.  Faults during execution surface at the
+ *    caller's next synchronisation.  No exception or abort crosses the ABI.
+ *  - Results are bitwise deterministic for a given shape, dtype and device
+ *    (no atomics).  The library keeps no mutable global state.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum gdn_status {
+  GDN_OK = 0,
+  GDN_EINVAL = 1,
+  GDN_ESHAPE = 2,
+  GDN_EWORKSPACE = 3,
+  GDN_EHIP = 4
+};
+
+enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 };
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* gdn_status_str(int status);
+
+/* Library version string, "MAJOR.MINOR.PATCH". */
+const char* gdn_version(void);
+
+/* ------------------------------------------------------------------------
+ * Prefill over whole sequences (chunked form).
+ *
+ * Bytes of device workspace gdn_prefill needs for these sizes (0 for T = 0).
+ * Depends only on B, T, H: one 64-token chunk's triangular correction,
+ * masked query-key products and gate prefix sums (33,792 bytes per chunk per
+ * head).
+ */
+size_t gdn_prefill_workspace_bytes(int B, int T, int H, int dk, int dv);
+
+/*
+ * Runs the recurrence over T tokens for B*H independent heads.
+ *   q, k, v      inputs, in_dtype, layouts above.
+ *   alpha, beta  [B, T, H] float32.
+ *   S0           [B, H, dv, dk] float32 initial state, or NULL for zero.
+ *   o            [B, T, H, dv] out_dtype (may be NULL only if T == 0).
+ *   ST           [B, H, dv, dk] float32 final state, or NULL to skip it.
+ *                ST may be the same pointer as S0 (updated in place); no
+ *                other overlap between outputs and inputs is allowed.
+ *   workspace    device scratch of at least gdn_prefill_workspace_bytes().
+ * The result equals the token-by-token recurrence up to rounding; the
+ * chunked evaluation order is an exact re-association of it.
+ * T == 0 copies S0 (or zeros) into ST.
+ */
+int gdn_prefill(const void* q, const void* k, const void* v,
+                const float* alpha, const float* beta, const float* S0,
+                void* o, float* ST,
+                int B, int T, int H, int dk, int dv,
+                int in_dtype, int out_dtype,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two phases of gdn_prefill, exposed so a caller can time or schedule
+ * them separately.  gdn_prefill == gdn_prefill_prepare then gdn_prefill_scan
+ * on the same stream with the same workspace.
+ *   prepare: per 64-token chunk, independent of the state: the gate prefix
+ *            sums, the unit-lower-triangular delta correction
+ *            (I + A)^{-1} with A_ji = beta_j e^{g_j - g_i} k_j.k_i (i < j),
+ *            and the decay-masked query-key products; written to workspace.
+ *   scan:    sequential over chunks, parallel over heads and 16-row slices
+ *            of the state: reads q, k, v and the workspace, writes o and ST.
+ */
+int gdn_prefill_prepare(const void* q, const void* k,
+                        const float* alpha, const float* beta,
+                        int B, int T, int H, int dk, int dv, int in_dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+int gdn_prefill_scan(const void* q, const void* k, const void* v,
+                     const float* S0, void* o, float* ST,
+                     int B, int T, int H, int dk, int dv,
+                     int in_dtype, int out_dtype,
+                     const void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* ------------------------------------------------------------------------
+ * One decode token for a batch of carried states.
+ *   q, k [B, H, dk]; v [B, H, dv] (in_dtype); alpha, beta [B, H] float32;
+ *   S_in [B, H, dv, dk] float32; S_out same shape (S_out == S_in allowed:
+ *   in-place update; no partial overlap); o [B, H, dv] out_dtype.
+ * Each state element is read once and written once.  Uses no workspace.
+ */
+int gdn_decode_step(const void* q, const void* k, const void* v,
+                    const float* alpha, const float* beta,
+                    const float* S_in, float* S_out, void* o,
+                    int B, int H, int dk, int dv,
+                    int in_dtype, int out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

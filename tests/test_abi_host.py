@@ -1,0 +1,140 @@
+"""Host tests of the C ABI: every declared symbol is exported, and argument
+errors are reported before any HIP call (so these run without a GPU; the
+fake pointers below are never dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_deltanet_recurrent_delta_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+P = ctypes.c_void_p(0x10000)        # fake, 16-byte aligned, never touched
+MIS = ctypes.c_void_p(0x10004)      # fake, misaligned
+NULL = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(bd.SIGNATURES)
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(bd.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    assert bd.status_str(0) == "GDN_OK"
+    for s in range(1, 5):
+        assert bd.status_str(s).startswith("GDN_E")
+    assert bd.status_str(99) == "GDN_UNKNOWN_STATUS"
+    assert re.fullmatch(r"\d+\.\d+\.\d+", bd.version())
+
+
+def test_workspace_bytes():
+    ws = bd.prefill_workspace_bytes
+    assert ws(1, 64, 1, 128, 128) == 33792
+    assert ws(1, 65, 1, 128, 128) == 2 * 33792
+    assert ws(2, 16384, 16, 128, 128) == 2 * 16 * 256 * 33792
+    assert ws(1, 0, 16, 128, 128) == 0
+    assert ws(0, 10, 16, 128, 128) == 0
+
+
+def prefill(**kw):
+    a = dict(q=P, k=P, v=P, alpha=P, beta=P, S0=NULL, o=P, ST=P, B=1, T=100,
+             H=2, dk=128, dv=128, in_dtype=1, out_dtype=1, ws=P,
+             ws_bytes=10 ** 9, stream=NULL)
+    a.update(kw)
+    return bd.lib.gdn_prefill(a["q"], a["k"], a["v"], a["alpha"], a["beta"],
+                              a["S0"], a["o"], a["ST"], a["B"], a["T"],
+                              a["H"], a["dk"], a["dv"], a["in_dtype"],
+                              a["out_dtype"], a["ws"], a["ws_bytes"],
+                              a["stream"])
+
+
+def decode(**kw):
+    a = dict(q=P, k=P, v=P, alpha=P, beta=P, S_in=P, S_out=P, o=P, B=4, H=2,
+             dk=128, dv=128, in_dtype=1, out_dtype=1, stream=NULL)
+    a.update(kw)
+    return bd.lib.gdn_decode_step(a["q"], a["k"], a["v"], a["alpha"],
+                                  a["beta"], a["S_in"], a["S_out"], a["o"],
+                                  a["B"], a["H"], a["dk"], a["dv"],
+                                  a["in_dtype"], a["out_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), bd.GDN_EINVAL),
+    (dict(H=-1), bd.GDN_EINVAL),
+    (dict(T=-5), bd.GDN_EINVAL),
+    (dict(B=70000), bd.GDN_EINVAL),
+    (dict(dk=96), bd.GDN_ESHAPE),
+    (dict(dk=256), bd.GDN_ESHAPE),
+    (dict(dv=32), bd.GDN_ESHAPE),
+    (dict(in_dtype=2), bd.GDN_ESHAPE),
+    (dict(out_dtype=-1), bd.GDN_ESHAPE),
+    (dict(q=NULL), bd.GDN_EINVAL),
+    (dict(v=NULL), bd.GDN_EINVAL),
+    (dict(alpha=NULL), bd.GDN_EINVAL),
+    (dict(o=NULL), bd.GDN_EINVAL),
+    (dict(q=MIS), bd.GDN_EINVAL),
+    (dict(o=MIS), bd.GDN_EINVAL),
+    (dict(S0=MIS), bd.GDN_EINVAL),
+    (dict(ws=NULL), bd.GDN_EWORKSPACE),
+    (dict(ws_bytes=33792), bd.GDN_EWORKSPACE),          # needs 2 chunks x 2 heads
+    (dict(S0=ctypes.c_void_p(0x10000), ST=ctypes.c_void_p(0x10100)),
+     bd.GDN_EINVAL),                                     # partial overlap
+])
+def test_prefill_argument_errors(kw, status):
+    assert prefill(**kw) == status
+
+
+def test_prefill_empty_sequence_without_state_is_a_noop():
+    # T == 0 and no ST: nothing to launch, nothing touched
+    assert prefill(T=0, ST=NULL, q=NULL, k=NULL, v=NULL, o=NULL,
+                   ws=NULL, ws_bytes=0) == bd.GDN_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), bd.GDN_EINVAL),
+    (dict(H=0), bd.GDN_EINVAL),
+    (dict(dk=32), bd.GDN_ESHAPE),
+    (dict(dv=256), bd.GDN_ESHAPE),
+    (dict(in_dtype=5), bd.GDN_ESHAPE),
+    (dict(S_in=NULL), bd.GDN_EINVAL),
+    (dict(o=NULL), bd.GDN_EINVAL),
+    (dict(k=MIS), bd.GDN_EINVAL),
+    (dict(S_in=ctypes.c_void_p(0x100000), S_out=ctypes.c_void_p(0x100010)),
+     bd.GDN_EINVAL),                                     # partial overlap
+])
+def test_decode_argument_errors(kw, status):
+    assert decode(**kw) == status
+
+
+def test_prepare_and_scan_argument_errors():
+    lib = bd.lib
+    assert lib.gdn_prefill_prepare(P, P, P, P, 1, 64, 1, 128, 128, 1, NULL,
+                                   0, NULL) == bd.GDN_EWORKSPACE
+    assert lib.gdn_prefill_prepare(P, P, P, P, 1, 64, 1, 100, 128, 1, P,
+                                   10 ** 6, NULL) == bd.GDN_ESHAPE
+    assert lib.gdn_prefill_scan(P, P, P, NULL, P, P, 1, 64, 1, 128, 128, 1,
+                                1, P, 100, NULL) == bd.GDN_EWORKSPACE
+    assert lib.gdn_prefill_scan(NULL, P, P, NULL, P, P, 1, 64, 1, 128, 128, 1,
+                                1, P, 10 ** 6, NULL) == bd.GDN_EINVAL
+
+
+def test_python_wrappers_reject_host_tensors():
+    import torch
+    x = torch.zeros(1, 4, 2, 64)
+    with pytest.raises(ValueError):
+        bd.prefill(x, x, x, torch.ones(1, 4, 2), torch.ones(1, 4, 2))

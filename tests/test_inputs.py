@@ -103,3 +103,10 @@ def test_slicing_helpers():
     assert y.q.shape == (3, 4, 2, 8) and y.S0 is None
     z = x.slice_batch(1, 2)
     assert z.S0.shape == (1, 2, 4, 8)
+
+
+def test_row_subsets_regenerate_identically():
+    full = gi.batched_prefill(B=4, T=16, dk=64)
+    part = gi.batched_prefill(B=4, T=16, dk=64, rows=[1, 3])
+    for f in ["q", "k", "v", "alpha", "beta"]:
+        np.testing.assert_array_equal(getattr(part, f), getattr(full, f)[[1, 3]])

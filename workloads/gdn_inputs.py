@@ -32,7 +32,7 @@ Where the workloads come from
 from __future__ import annotations
 
 import dataclasses
-from typing import Optional
+from typing import Optional, Sequence
 
 import numpy as np
 
@@ -184,32 +184,44 @@ def _decay(rng, shape, lo, hi):
 def generic(B: int, T: int, H: int, dk: int, dv: int, seed: int,
             dtype: str = "f32", log_alpha_range=(0.001, 0.1),
             S0_scale: Optional[float] = None, name: str = "generic",
-            channel_idx: Optional[np.ndarray] = None) -> GdnInputs:
+            channel_idx: Optional[np.ndarray] = None,
+            rows: Optional[Sequence[int]] = None) -> GdnInputs:
     """Tiny-case distributions at any shape: q, k ~ N(0, I) normalised,
     v ~ N(0, I), beta = sigmoid(N(0, 1)), log alpha ~ -U(range).
 
+    Batch row b is drawn from its own stream PCG64(seed).jumped(b), so any
+    subset of rows can be regenerated alone: `rows` selects the batch rows to
+    draw (the result then has len(rows) rows; default all B).
     S0_scale: if given, S0 ~ S0_scale * N(0, 1) (else S0 = None, a zero state).
     channel_idx: if given ([H, dk'] int), draw raw dk-wide q/k, keep channels
     channel_idx[h] of head h and normalise over the kept channels.
     """
-    rng = np.random.Generator(np.random.PCG64(seed))
-    qr = rng.standard_normal((B, T, H, dk), dtype=np.float32)
-    kr = rng.standard_normal((B, T, H, dk), dtype=np.float32)
-    v = rng.standard_normal((B, T, H, dv), dtype=np.float32)
-    beta = _sigmoid(rng.standard_normal((B, T, H)))
-    alpha = _decay(rng, (B, T, H), *log_alpha_range)
-    S0 = None
-    if S0_scale is not None:
-        S0 = (S0_scale * rng.standard_normal((B, H, dv, dk))).astype(np.float32)
-    idx = None
-    if channel_idx is not None:
-        idx = np.asarray(channel_idx, dtype=np.int32)
-        assert idx.shape[0] == H and idx.shape[1] <= dk
-        qr, kr = gather_channels(qr, idx), gather_channels(kr, idx)
+    rows = list(range(B)) if rows is None else [int(r) for r in rows]
+    idx = None if channel_idx is None else np.asarray(channel_idx, np.int32)
+    dko = dk if idx is None else idx.shape[1]
+    n = len(rows)
+    q = np.empty((n, T, H, dko), np.float32)
+    k = np.empty((n, T, H, dko), np.float32)
+    v = np.empty((n, T, H, dv), np.float32)
+    beta = np.empty((n, T, H), np.float32)
+    alpha = np.empty((n, T, H), np.float32)
+    S0 = None if S0_scale is None else np.empty((n, H, dv, dko), np.float32)
+    for i, b in enumerate(rows):
+        assert 0 <= b < B
+        rng = np.random.Generator(np.random.PCG64(seed).jumped(b))
+        qr = rng.standard_normal((1, T, H, dk), dtype=np.float32)
+        kr = rng.standard_normal((1, T, H, dk), dtype=np.float32)
+        v[i] = rng.standard_normal((T, H, dv), dtype=np.float32)
+        beta[i] = _sigmoid(rng.standard_normal((T, H)))
+        alpha[i] = _decay(rng, (T, H), *log_alpha_range)
         if S0 is not None:
-            S0 = np.ascontiguousarray(S0[..., :idx.shape[1]])
-    return _finish(_unit(qr), _unit(kr), v, alpha, beta, S0, dtype, seed,
-                   name, idx)
+            s0 = (S0_scale * rng.standard_normal((H, dv, dk))).astype(np.float32)
+            S0[i] = s0 if idx is None else s0[..., :dko]
+        if idx is not None:
+            assert idx.shape[0] == H and idx.shape[1] <= dk
+            qr, kr = gather_channels(qr, idx), gather_channels(kr, idx)
+        q[i], k[i] = _unit(qr)[0], _unit(kr)[0]
+    return _finish(q, k, v, alpha, beta, S0, dtype, seed, name, idx)
 
 
 def pruning_subsets(config: int, H: int = 16, dk: int = 128,
@@ -265,7 +277,8 @@ def prefill_16k(T: int = 16384, H: int = 16, d: int = 128,
 
 
 def batched_prefill(B: int = 8, T: int = 4096, H: int = 16, dk: int = 128,
-                    dv: int = 128, seed: Optional[int] = None) -> GdnInputs:
+                    dv: int = 128, seed: Optional[int] = None,
+                    rows: Optional[Sequence[int]] = None) -> GdnInputs:
     """Batched prefill for the state-halving comparison: B=8, H=16, T=4096,
     dv=128, dk in {128, 64}, bf16 inputs, tiny-case distributions.  The
     dk=64 variant reuses the dk=128 raw draws through a per-head seeded
@@ -273,27 +286,29 @@ def batched_prefill(B: int = 8, T: int = 4096, H: int = 16, dk: int = 128,
     s = seed_for(4) if seed is None else seed
     idx = None if dk == 128 else pruning_subsets(4, H, 128, dk)
     return generic(B, T, H, 128, dv, s, "bf16", channel_idx=idx,
-                   name=f"batched-prefill-dk{dk}")
+                   name=f"batched-prefill-dk{dk}", rows=rows)
 
 
 def decode_prompt(B: int = 64, T: int = 2048, H: int = 16, dk: int = 128,
-                  dv: int = 128, seed: Optional[int] = None) -> GdnInputs:
+                  dv: int = 128, seed: Optional[int] = None,
+                  rows: Optional[Sequence[int]] = None) -> GdnInputs:
     """Prompt whose prefill initialises the carried decode states
     (tiny-case distributions, bf16 inputs, dk=64 by channel subset)."""
     s = seed_for(3, 0) if seed is None else seed
     idx = None if dk == 128 else pruning_subsets(3, H, 128, dk)
     return generic(B, T, H, 128, dv, s, "bf16", channel_idx=idx,
-                   name=f"decode-prompt-B{B}-dk{dk}")
+                   name=f"decode-prompt-B{B}-dk{dk}", rows=rows)
 
 
 def decode_steps(B: int = 64, n_steps: int = 512, H: int = 16, dk: int = 128,
-                 dv: int = 128, seed: Optional[int] = None) -> GdnInputs:
+                 dv: int = 128, seed: Optional[int] = None,
+                 rows: Optional[Sequence[int]] = None) -> GdnInputs:
     """`n_steps` fresh single-token inputs for the decode loop, laid out as a
     [B, n_steps, H, *] sequence (step t is [:, t])."""
     s = seed_for(3, 1) if seed is None else seed
     idx = None if dk == 128 else pruning_subsets(3, H, 128, dk)
     return generic(B, n_steps, H, 128, dv, s, "bf16", channel_idx=idx,
-                   name=f"decode-steps-B{B}-dk{dk}")
+                   name=f"decode-steps-B{B}-dk{dk}", rows=rows)
 
 
 def truncated_prefill(T: int = 16384, H: int = 16, d: int = 128,
