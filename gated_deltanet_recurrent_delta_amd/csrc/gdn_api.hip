@@ -3,7 +3,7 @@
 // before any HIP call, so argument errors can be tested without a GPU.
 #include <stdint.h>
 
-#include "../../include/gdn.h"
+#include "gdn.h"
 #include "gdn_launch.hpp"
 
 namespace {
@@ -17,10 +17,9 @@ bool aligned(const void* p, uintptr_t a) {
 }
 int to_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_EHIP; }
 
-size_t prefill_ws_bytes(int B, int T, int H) {
+size_t prefill_ws_bytes(int B, int T, int H, int dk, int dv) {
   if (B <= 0 || H <= 0 || T <= 0) return 0;
-  const size_t nchunks = ((size_t)T + gdn::kChunk - 1) / gdn::kChunk;
-  return (size_t)B * H * nchunks * gdn::kChunkWsFloats * sizeof(float);
+  return gdn::plan_prefill(B, T, H, dk, dv).total_bytes;
 }
 
 // Common shape/dtype checks of the prefill entry points.
@@ -52,9 +51,8 @@ const char* gdn_status_str(int status) {
 const char* gdn_version(void) { return "0.1.0"; }
 
 size_t gdn_prefill_workspace_bytes(int B, int T, int H, int dk, int dv) {
-  (void)dk;
-  (void)dv;
-  return prefill_ws_bytes(B, T, H);
+  if (!dims_ok(dk, dv)) return 0;
+  return prefill_ws_bytes(B, T, H, dk, dv);
 }
 
 int gdn_prefill_prepare(const void* q, const void* k, const float* alpha,
@@ -69,7 +67,7 @@ int gdn_prefill_prepare(const void* q, const void* k, const float* alpha,
       !aligned(beta, 4))
     return GDN_EINVAL;
   if (!workspace || !aligned(workspace, 16)) return GDN_EWORKSPACE;
-  if (workspace_bytes < prefill_ws_bytes(B, T, H)) return GDN_EWORKSPACE;
+  if (workspace_bytes < prefill_ws_bytes(B, T, H, dk, dv)) return GDN_EWORKSPACE;
   return to_status(gdn::launch_prefill_prepare(
       q, k, alpha, beta, static_cast<float*>(workspace), B, T, H, dk, in_dtype,
       static_cast<hipStream_t>(stream)));
@@ -78,7 +76,7 @@ int gdn_prefill_prepare(const void* q, const void* k, const float* alpha,
 int gdn_prefill_scan(const void* q, const void* k, const void* v,
                      const float* S0, void* o, float* ST, int B, int T, int H,
                      int dk, int dv, int in_dtype, int out_dtype,
-                     const void* workspace, size_t workspace_bytes,
+                     void* workspace, size_t workspace_bytes,
                      void* stream) {
   int st = check_prefill_shape(B, T, H, dk, dv, in_dtype, out_dtype);
   if (st != GDN_OK) return st;
@@ -95,10 +93,10 @@ int gdn_prefill_scan(const void* q, const void* k, const void* v,
       !aligned(o, 16))
     return GDN_EINVAL;
   if (!workspace || !aligned(workspace, 16)) return GDN_EWORKSPACE;
-  if (workspace_bytes < prefill_ws_bytes(B, T, H)) return GDN_EWORKSPACE;
+  if (workspace_bytes < prefill_ws_bytes(B, T, H, dk, dv)) return GDN_EWORKSPACE;
   return to_status(gdn::launch_prefill_scan(
-      q, k, v, S0, o, ST, static_cast<const float*>(workspace), B, T, H, dk,
-      dv, in_dtype, out_dtype, static_cast<hipStream_t>(stream)));
+      q, k, v, S0, o, ST, workspace, B, T, H, dk, dv,
+      in_dtype, out_dtype, static_cast<hipStream_t>(stream)));
 }
 
 int gdn_prefill(const void* q, const void* k, const void* v,

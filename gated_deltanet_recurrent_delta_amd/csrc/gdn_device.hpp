@@ -40,6 +40,15 @@ __device__ __forceinline__ void split8(const floatx8& x, bf16x8& hi,
   }
 }
 
+__device__ __forceinline__ void split4(const float* x, bf16x4& hi, bf16x4& lo) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    bf16 h = (bf16)x[j];
+    hi[j] = h;
+    lo[j] = (bf16)(x[j] - (float)h);
+  }
+}
+
 __device__ __forceinline__ bf16x8 to_bf16x8(const floatx8& x) {
   bf16x8 r;
 #pragma unroll

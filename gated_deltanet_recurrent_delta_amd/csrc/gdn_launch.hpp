@@ -13,6 +13,71 @@ constexpr int kSlice = 16;     // state rows per prefill scan workgroup
 // products P [64x64], gate block (g, beta, gamma, decay-to-end) [4x64].
 constexpr size_t kChunkWsFloats = 2 * kChunk * kChunk + 4 * kChunk;
 
+// Sequence segmentation of a prefill (used when B*H alone cannot fill the
+// chip).  The map from a segment's incoming state S_in to its outputs and
+// final state is affine: S_end = S_in X + S_loc and o_t = o_loc_t + S_in x^_t
+// with X = the product of the segment's transitions alpha (I - beta k k^T),
+// x^_t = X_t q_t.  Phase 1 runs every segment from a zero state (segment 0
+// from S0) together with dk "transition rows" that start at the identity and
+// see v = 0 (they evolve exactly like state rows, giving X and x^); phase 2
+// chains S_in(s) = S_end(s-1) over the segments; phase 3 adds S_in(s) x^_t
+// to the outputs of segments >= 1.
+struct SegArgs {
+  int nseg;          // segments per head (1: unsegmented, the fields below unused)
+  int seg_chunks;    // chunks per segment (the last may be shorter)
+  float* S_fin;      // [BH][nseg][dv][dk] final real-row state of each segment
+  float* X_fin;      // [BH][nseg][dk][dk] final transition rows (segments >= 1)
+  float* S_in;       // [BH][nseg][dv][dk] incoming state of each segment
+  void* xhat;        // [BH][T][dk] bf16, x^_t for tokens of segments >= 1
+};
+
+struct PrefillPlan {
+  int nchunks, nseg, seg_chunks;
+  size_t chunk_bytes;       // per-chunk tiles (prepare -> scan)
+  size_t xhat_off, sfin_off, xfin_off, sin_off;
+  size_t total_bytes;
+};
+
+// Scan workgroups the segmentation aims for (256 CUs, two rounds).
+constexpr int kScanTargetBlocks = 512;
+constexpr int kMinSegChunks = 8;
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Plan for bf16 inputs and outputs (the only case that is segmented); the
+// workspace it sizes also covers every other dtype combination.
+inline PrefillPlan plan_prefill(int B, int T, int H, int dk, int dv) {
+  PrefillPlan p{};
+  p.nchunks = (T + kChunk - 1) / kChunk;
+  p.chunk_bytes = (size_t)B * H * p.nchunks * kChunkWsFloats * sizeof(float);
+  p.nseg = 1;
+  p.seg_chunks = p.nchunks;
+  const int per_head_target = kScanTargetBlocks / (B * H > 0 ? B * H : 1);
+  const int g0 = dv / 64, gx = (dv + dk) / 64;
+  if (per_head_target > g0 && p.nchunks >= 2 * kMinSegChunks) {
+    int nseg = 1 + (per_head_target - g0) / gx;
+    nseg = nseg < p.nchunks / kMinSegChunks ? nseg : p.nchunks / kMinSegChunks;
+    if (nseg > 1) {
+      p.seg_chunks = (p.nchunks + nseg - 1) / nseg;
+      p.nseg = (p.nchunks + p.seg_chunks - 1) / p.seg_chunks;
+    }
+  }
+  size_t off = align256(p.chunk_bytes);
+  if (p.nseg > 1) {
+    const size_t BH = (size_t)B * H;
+    p.xhat_off = off;
+    off = align256(off + BH * T * dk * 2);
+    p.sfin_off = off;
+    off = align256(off + BH * p.nseg * dv * dk * 4);
+    p.xfin_off = off;
+    off = align256(off + BH * p.nseg * dk * dk * 4);
+    p.sin_off = off;
+    off = align256(off + BH * p.nseg * dv * dk * 4);
+  }
+  p.total_bytes = off;
+  return p;
+}
+
 hipError_t launch_decode(const void* q, const void* k, const void* v,
                          const float* alpha, const float* beta,
                          const float* S_in, float* S_out, void* o, int BH,
@@ -24,11 +89,12 @@ hipError_t launch_prefill_prepare(const void* q, const void* k,
                                   float* ws, int B, int T, int H, int dk,
                                   int in_dtype, hipStream_t stream);
 
+// Phase 1 (+ phases 2 and 3 when the plan segments the sequence).  `ws` is
+// the whole workspace (per-chunk tiles first, then the segment buffers).
 hipError_t launch_prefill_scan(const void* q, const void* k, const void* v,
-                               const float* S0, void* o, float* ST,
-                               const float* ws, int B, int T, int H, int dk,
-                               int dv, int in_dtype, int out_dtype,
-                               hipStream_t stream);
+                               const float* S0, void* o, float* ST, void* ws,
+                               int B, int T, int H, int dk, int dv,
+                               int in_dtype, int out_dtype, hipStream_t stream);
 
 hipError_t launch_state_fill(const float* S0, float* ST, size_t n,
                              hipStream_t stream);

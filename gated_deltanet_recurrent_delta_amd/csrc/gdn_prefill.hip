@@ -18,19 +18,28 @@
 // This is an exact re-association of the sequential recurrence.
 //
 // Two kernels:
-//  * prepare_kernel -- one workgroup per (batch, head, chunk), fully
-//    parallel: gate prefix sums, K K^T and Q K^T on bf16 MFMA, the
-//    triangular inverse T by forward substitution in fp32; writes T, P and
-//    the gate block to the workspace.
-//  * scan_kernel -- one workgroup per (batch, head, 16 state rows); the rows
-//    of the state evolve independently ("On State Reduction in Linear
-//    Attention", Sec. 3.1), so each workgroup carries a 16 x dk slice of S in
-//    MFMA accumulators and walks the chunks in order.  Every product that
-//    touches the state uses split-bf16 operands (x = hi + lo, three or two
-//    MFMAs) so the carried state keeps ~16 significant bits per operand and
-//    fp32 accumulation; outputs stored in bf16 use single-pass products.
-//    The next chunk's tiles are prefetched into registers while the current
-//    chunk computes.
+//  * prepare_kernel -- one wave per (batch, head, chunk), fully parallel.
+//    K and Q are read once from HBM straight into MFMA operand registers;
+//    the lower 16x16 tiles of K K^T and Q K^T run on bf16 MFMA; the decay
+//    factors are exp2 of differences of the scaled prefix sums (never of a
+//    single prefix sum, which can underflow); T is inverted in fp32 (the four
+//    16x16 diagonal blocks by forward substitution, one lane per column, then
+//    the off-diagonal blocks level by level).  T and P are written as bf16
+//    hi/lo tiles ready to be copied into LDS.
+//  * scan_kernel -- one workgroup per (batch, head, 16 NW state rows).  The
+//    rows of the state evolve independently ("On State Reduction in Linear
+//    Attention", Sec. 3.1), so each wave owns 16 rows and runs the whole
+//    chunk step for them in registers: the MFMA accumulator tiles of S, Y, Z
+//    and U are fed back as B operands without an LDS round trip (a lane's 8
+//    k-slots are the two 4-row runs it holds in the accumulator layout).
+//    The waves share one LDS copy of the chunk's K, Q, T, P and V tiles,
+//    staged with 16-byte copies from registers that were prefetched while
+//    the previous chunk computed; K^T and V^T operands come from the
+//    row-major tiles through the gfx950 transposing LDS read
+//    (ds_read_b64_tr_b16), so no transposed copy is kept.
+//    Products that touch the state use split-bf16 operands (x = hi + lo, two
+//    MFMAs when the other operand is an exact bf16 input, three otherwise)
+//    with fp32 accumulation; outputs stored in bf16 use single-pass products.
 #include <type_traits>
 
 #include "gdn_device.hpp"
@@ -41,91 +50,129 @@ namespace gdn {
 namespace {
 
 constexpr int C = kChunk;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Workspace layout of one (batch, head, chunk), in bytes from its start.
+constexpr int kWsTh = 0;                    // bf16 [64][64] hi part of T
+constexpr int kWsTl = 8192;                 // bf16 [64][64] lo part of T
+constexpr int kWsPh = 16384;                // bf16 [64][64] hi part of P
+constexpr int kWsPl = 24576;                // bf16 [64][64] lo part of P
+constexpr int kWsG = 32768;                 // fp32 [4][64]: g, beta, gamma, e^{g_C - g}
+static_assert(kWsG + 4 * 4 * C == kChunkWsFloats * 4, "workspace layout");
 
 // The 10 lower-triangular 16x16 tiles (mi >= ni) of a 64x64 matrix.
 __device__ __constant__ int kLowerMi[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
 __device__ __constant__ int kLowerNi[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 
-// k-slot j (0..7) of lane group g4 inside 32-wide k-block s.  A lane's slots
-// are two runs of 4 consecutive indices, which matches how an MFMA
-// accumulator tile holds its rows (4 consecutive rows per lane group), so
-// results can be fed back as B operands without any transpose.
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4v_t;
+
+// First index of half `half` (0/1) of lane group g4's k-slots in 32-wide
+// k-block s: slots 0..3 are kslot_base(s, g4, 0) + 0..3, slots 4..7 are
+// kslot_base(s, g4, 1) + 0..3.  These are exactly the rows an accumulator
+// tile pair (16s.., 16s+16..) holds in a lane, so accumulators feed B
+// operands directly.
 __device__ __forceinline__ int kslot_base(int s, int g4, int half) {
   return 32 * s + 16 * half + 4 * g4;
 }
 
-template <typename TIn>
-__device__ __forceinline__ void load8(const TIn* p, float* x) {
-  const float4 a = load4(p), b = load4(p + 4);
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+// 8 bf16 k-slots of row `row` from a row-major bf16 tile (row stride ld).
+__device__ __forceinline__ bf16x8 lds_slots(const bf16* X, int ld, int row,
+                                            int s, int g4) {
+  const uint2 a = *reinterpret_cast<const uint2*>(&X[row * ld + kslot_base(s, g4, 0)]);
+  const uint2 b = *reinterpret_cast<const uint2*>(&X[row * ld + kslot_base(s, g4, 1)]);
+  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+
+// Transposing read of a row-major bf16 tile X[row][col] (row stride ld):
+// returns, for lane (n = lane % 16), X[r0 + j][c0 + n], j = 0..3.
+// ds_read_b64_tr_b16 hands lane i of each 16-lane group element (i % 4) of
+// the 4 values read by lane 4 j + i / 4; lane n therefore reads row
+// r0 + n / 4, columns c0 + 4 (n % 4) .. + 3.
+__device__ __forceinline__ uint2 lds_tr4(const bf16* X, int ld, int r0, int c0,
+                                         int n) {
+  const bf16* p = &X[(r0 + (n >> 2)) * ld + c0 + 4 * (n & 3)];
+  const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_short4v_t*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// 8 k-slots of k-block s (rows of X are the contraction index) for output
+// column c0 + n: X[kslot][c0 + n] via two transposing reads.
+__device__ __forceinline__ bf16x8 lds_slots_tr(const bf16* X, int ld, int c0,
+                                               int s, int g4, int n) {
+  const uint2 a = lds_tr4(X, ld, kslot_base(s, g4, 0), c0, n);
+  const uint2 b = lds_tr4(X, ld, kslot_base(s, g4, 1), c0, n);
+  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+
+// Accumulator tiles (2s, 2s+1) of a lane as the 8 k-slots of k-block s.
+__device__ __forceinline__ floatx8 acc_slots(const floatx4& lo, const floatx4& hi) {
+  const floatx8 x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return x;
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return bf16_bits_to_f32(w & 0xFFFFu); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return bf16_bits_to_f32(w >> 16); }
+
+// 8 consecutive inputs as bf16 hi (and lo when the input is fp32).
+__device__ __forceinline__ void load_row8(const bf16* p, bf16x8& hi, bf16x8& lo) {
+  hi = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+  (void)lo;
+}
+__device__ __forceinline__ void load_row8(const float* p, bf16x8& hi, bf16x8& lo) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  const floatx8 x = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  split8(x, hi, lo);
 }
 
 }  // namespace
 
 // ===========================================================================
-// prepare
+// prepare: one wave per chunk
 // ===========================================================================
 
 template <int DK, typename TIn>
-__global__ __launch_bounds__(256) void prepare_kernel(
+__global__ __launch_bounds__(64) void prepare_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k,
     const float* __restrict__ alpha, const float* __restrict__ beta,
     float* __restrict__ ws, int T, int H, int nchunks) {
   constexpr bool SPLIT = std::is_same<TIn, float>::value;  // inputs not bf16
-  constexpr int LD = DK + 8;            // bf16 row stride of the K/Q tiles
-  constexpr int LDA = C + 4;            // fp32 row stride of A
-  __shared__ __attribute__((aligned(16))) bf16 Kh[C * LD];
-  __shared__ __attribute__((aligned(16))) bf16 Qh[C * LD];
-  __shared__ __attribute__((aligned(16))) bf16 Kl[SPLIT ? C * LD : 8];
-  __shared__ __attribute__((aligned(16))) bf16 Ql[SPLIT ? C * LD : 8];
+  constexpr int NKB = DK / 32;
+  constexpr int LDA = C + 4;            // fp32 row stride of A, P and T
+  constexpr int LDB = 16 + 4;           // fp32 row stride of 16x16 scratch
   __shared__ __attribute__((aligned(16))) float As[C * LDA];
-  __shared__ float gs[C], bs[C];
+  __shared__ __attribute__((aligned(16))) float PTs[C * LDA];   // P, then T
+  __shared__ __attribute__((aligned(16))) float tmp[16 * LDB];
+  __shared__ float g2s[C], bs[C];
 
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int t0 = chunk * C;
   const int nvalid = min(C, T - t0);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  float* wsc = ws + ((size_t)(b * H + h) * nchunks + chunk) * kChunkWsFloats;
-  float* Tw = wsc;
-  float* Pw = wsc + C * C;
-  float* Gw = wsc + 2 * C * C;
+  const int lane = threadIdx.x, n = lane & 15, g4 = lane >> 4;
+  char* wsc = reinterpret_cast<char*>(ws) +
+              ((size_t)(b * H + h) * nchunks + chunk) * kChunkWsFloats * 4;
 
-  // 1. stage K and Q (zero rows past the end of the sequence)
-  constexpr int SEGS = C * DK / 8;
-  for (int sg = tid; sg < SEGS; sg += 256) {
-    const int c = sg / (DK / 8), d0 = (sg % (DK / 8)) * 8;
-    float kx[8], qx[8];
-    if (c < nvalid) {
-      const size_t off = (((size_t)b * T + t0 + c) * H + h) * DK + d0;
-      load8(k + off, kx);
-      load8(q + off, qx);
-    } else {
+  // 1. K and Q rows 16 t + n, k-slots 32 s + 8 g4 .. + 7, straight from HBM
+  bf16x8 Kh[4][NKB], Kl[4][NKB], Qh[4][NKB], Ql[4][NKB];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kx[e] = qx[e] = 0.f;
-    }
-    bf16x8 kh, qh;
+  for (int t = 0; t < 4; ++t) {
+    const int c = 16 * t + n;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      kh[e] = (bf16)kx[e];
-      qh[e] = (bf16)qx[e];
-    }
-    *reinterpret_cast<bf16x8*>(&Kh[c * LD + d0]) = kh;
-    *reinterpret_cast<bf16x8*>(&Qh[c * LD + d0]) = qh;
-    if constexpr (SPLIT) {
-      bf16x8 kl, ql;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        kl[e] = (bf16)(kx[e] - (float)kh[e]);
-        ql[e] = (bf16)(qx[e] - (float)qh[e]);
+    for (int s = 0; s < NKB; ++s) {
+      const bf16x8 z = {};
+      Kh[t][s] = Kl[t][s] = Qh[t][s] = Ql[t][s] = z;
+      if (c < nvalid) {
+        const size_t off = (((size_t)b * T + t0 + c) * H + h) * DK + 32 * s + 8 * g4;
+        load_row8(k + off, Kh[t][s], Kl[t][s]);
+        load_row8(q + off, Qh[t][s], Ql[t][s]);
       }
-      *reinterpret_cast<bf16x8*>(&Kl[c * LD + d0]) = kl;
-      *reinterpret_cast<bf16x8*>(&Ql[c * LD + d0]) = ql;
     }
   }
 
   // 2. gates: inclusive prefix sum of log alpha inside the chunk
-  if (w == 0) {
+  {
     float a = 1.f, be = 0.f;                  // padding tokens: identity step
     if (lane < nvalid) {
       const size_t gi = ((size_t)b * T + t0 + lane) * H + h;
@@ -139,68 +186,140 @@ __global__ __launch_bounds__(256) void prepare_kernel(
       if (lane >= off) g += y;
     }
     const float glast = __shfl(g, 63, 64);
-    gs[lane] = g;
+    g2s[lane] = g * kLog2e;
     bs[lane] = be;
+    float* Gw = reinterpret_cast<float*>(wsc + kWsG);
     Gw[lane] = g;
     Gw[C + lane] = be;
     Gw[2 * C + lane] = expf(g);
     Gw[3 * C + lane] = expf(glast - g);
   }
-  // upper-triangle tiles of P are zero
-  for (int e = tid; e < C * C; e += 256) {
-    const int j = e / C, i = e % C;
-    if ((i >> 4) > (j >> 4)) Pw[e] = 0.f;
+  // zero the strictly upper tiles of P (T's are written from Tt later)
+  for (int e = lane; e < C * C / 4; e += 64) {
+    const int j = (4 * e) / C, i0 = (4 * e) % C;
+    if ((i0 >> 4) > (j >> 4))
+      *reinterpret_cast<float4*>(&PTs[j * LDA + i0]) = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   __syncthreads();
 
-  // 3. lower tiles of K K^T (-> A) and Q K^T (-> P), 20 tiles over 4 waves
-  const int n = lane & 15, g4 = lane >> 4;
-  for (int t = w; t < 20; t += 4) {
-    const bool isP = t >= 10;
-    const int mi = kLowerMi[isP ? t - 10 : t], ni = kLowerNi[isP ? t - 10 : t];
-    const bf16* Xh = isP ? Qh : Kh;
-    const bf16* Xl = isP ? Ql : Kl;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  // 3. lower tiles of K K^T (-> A) and Q K^T (-> P)
 #pragma unroll
-    for (int s = 0; s < DK / 32; ++s) {
-      const int col = 32 * s + 8 * g4;
-      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&Xh[(16 * mi + n) * LD + col]);
-      const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&Kh[(16 * ni + n) * LD + col]);
-      acc = mfma(ah, bh, acc);
+  for (int t = 0; t < 10; ++t) {
+    const int mi = kLowerMi[t], ni = kLowerNi[t];
+    floatx4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NKB; ++s) {
+      ak = mfma(Kh[mi][s], Kh[ni][s], ak);
+      aq = mfma(Qh[mi][s], Kh[ni][s], aq);
       if constexpr (SPLIT) {
-        const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Xl[(16 * mi + n) * LD + col]);
-        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&Kl[(16 * ni + n) * LD + col]);
-        acc = mfma(ah, bl, acc);
-        acc = mfma(al, bh, acc);
+        ak = mfma(Kh[mi][s], Kl[ni][s], ak);
+        ak = mfma(Kl[mi][s], Kh[ni][s], ak);
+        aq = mfma(Qh[mi][s], Kl[ni][s], aq);
+        aq = mfma(Ql[mi][s], Kh[ni][s], aq);
       }
     }
     const int i = 16 * ni + n;
+    const float gi2 = g2s[i];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int j = 16 * mi + 4 * g4 + e;
-      const float decay = expf(gs[j] - gs[i]);
-      if (isP) {
-        Pw[j * C + i] = (i <= j) ? decay * acc[e] : 0.f;
-      } else {
-        As[j * LDA + i] = (i < j) ? bs[j] * decay * acc[e] : 0.f;
-      }
+      const float decay = (i <= j) ? __builtin_amdgcn_exp2f(g2s[j] - gi2) : 0.f;
+      As[j * LDA + i] = (i < j) ? bs[j] * decay * ak[e] : 0.f;
+      PTs[j * LDA + i] = decay * aq[e];
     }
   }
   __syncthreads();
 
-  // 4. T = (I + A)^{-1} by forward substitution, one column per lane
-  if (w == 0) {
-    const int c = lane;
-    float tc[C];
+  // 4. P -> workspace as bf16 hi/lo (row j, 8 columns per store)
+  for (int e = lane; e < C * C / 8; e += 64) {
+    const int j = (8 * e) / C, i0 = (8 * e) % C;
+    const float4 a0 = *reinterpret_cast<const float4*>(&PTs[j * LDA + i0]);
+    const float4 a1 = *reinterpret_cast<const float4*>(&PTs[j * LDA + i0 + 4]);
+    const floatx8 x = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    bf16x8 hi, lo;
+    split8(x, hi, lo);
+    *reinterpret_cast<bf16x8*>(wsc + kWsPh + (j * C + i0) * 2) = hi;
+    *reinterpret_cast<bf16x8*>(wsc + kWsPl + (j * C + i0) * 2) = lo;
+  }
+  __syncthreads();
+  float* Tt = PTs;                 // P is written out; reuse for T
+
+  // 5. T = (I + A)^{-1}.  Diagonal blocks: lane (block g4, column n).
+  {
+    const int base = 16 * g4, c = n;
+    float tcol[16];
 #pragma unroll
-    for (int j = 0; j < C; ++j) {
-      float acc = (j == c) ? 1.f : 0.f;
+    for (int j = 0; j < 16; ++j) {
+      float acc0 = (j == c) ? 1.f : 0.f, acc1 = 0.f;
 #pragma unroll
-      for (int i = 0; i < j; ++i) acc -= As[j * LDA + i] * tc[i];
-      tc[j] = acc;
+      for (int i = 0; i < j; i += 2) {
+        acc0 -= As[(base + j) * LDA + base + i] * tcol[i];
+        if (i + 1 < j) acc1 -= As[(base + j) * LDA + base + i + 1] * tcol[i + 1];
+      }
+      tcol[j] = acc0 + acc1;
     }
 #pragma unroll
-    for (int j = 0; j < C; ++j) Tw[j * C + c] = tc[j];
+    for (int j = 0; j < 16; ++j) Tt[(base + j) * LDA + base + c] = tcol[j];
+    // zero the strictly upper blocks of T
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj)
+      if (bj > g4)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) Tt[(base + j) * LDA + 16 * bj + c] = 0.f;
+  }
+  __syncthreads();
+  // Off-diagonal blocks, nearest the diagonal first:
+  //   T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj   (i > j, 16x16 blocks)
+  // lane l computes block rows r = l / 4, columns 4 (l % 4) .. + 3.
+  {
+    const int r = lane >> 2, c0 = (lane & 3) * 4;
+#pragma unroll
+    for (int dist = 1; dist < 4; ++dist) {
+#pragma unroll
+      for (int bj = 0; bj + dist < 4; ++bj) {
+        const int bi = bj + dist;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int bk = bj; bk < bi; ++bk) {
+#pragma unroll
+          for (int kk = 0; kk < 16; ++kk) {
+            const float x = As[(16 * bi + r) * LDA + 16 * bk + kk];
+            const float4 y = *reinterpret_cast<const float4*>(&Tt[(16 * bk + kk) * LDA + 16 * bj + c0]);
+            acc[0] += x * y.x;
+            acc[1] += x * y.y;
+            acc[2] += x * y.z;
+            acc[3] += x * y.w;
+          }
+        }
+        *reinterpret_cast<float4*>(&tmp[r * LDB + c0]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        __syncthreads();
+        float out[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+          const float x = Tt[(16 * bi + r) * LDA + 16 * bi + kk];
+          const float4 y = *reinterpret_cast<const float4*>(&tmp[kk * LDB + c0]);
+          out[0] -= x * y.x;
+          out[1] -= x * y.y;
+          out[2] -= x * y.z;
+          out[3] -= x * y.w;
+        }
+        *reinterpret_cast<float4*>(&Tt[(16 * bi + r) * LDA + 16 * bj + c0]) =
+            make_float4(out[0], out[1], out[2], out[3]);
+        __syncthreads();
+      }
+    }
+  }
+
+  // 6. T -> workspace as bf16 hi/lo
+  for (int e = lane; e < C * C / 8; e += 64) {
+    const int j = (8 * e) / C, i0 = (8 * e) % C;
+    const float4 a0 = *reinterpret_cast<const float4*>(&Tt[j * LDA + i0]);
+    const float4 a1 = *reinterpret_cast<const float4*>(&Tt[j * LDA + i0 + 4]);
+    const floatx8 x = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    bf16x8 hi, lo;
+    split8(x, hi, lo);
+    *reinterpret_cast<bf16x8*>(wsc + kWsTh + (j * C + i0) * 2) = hi;
+    *reinterpret_cast<bf16x8*>(wsc + kWsTl + (j * C + i0) * 2) = lo;
   }
 }
 
@@ -208,70 +327,89 @@ __global__ __launch_bounds__(256) void prepare_kernel(
 // scan
 // ===========================================================================
 
-template <int DK, typename TIn>
+// Per-thread register staging of one chunk for NT threads.
+template <int DK, typename TIn, int NT, int ROWS>
 struct Stage {
-  static constexpr int UNITS_K = C * DK * (int)sizeof(TIn) / 16 / 256;  // 16B units/thread
+  static constexpr int UNITS_K = C * DK * (int)sizeof(TIn) / 16 / NT;    // 16B units
+  static constexpr int UNITS_TP = 4 * C * C * 2 / 16 / NT;               // T, P hi/lo
+  static constexpr int UNITS_V = C * ROWS * (int)sizeof(TIn) / 16 / NT;  // V rows of the WG
+  static_assert(UNITS_K * NT * 16 == C * DK * (int)sizeof(TIn), "K staging");
+  static_assert(UNITS_TP * NT * 16 == 4 * C * C * 2, "T/P staging");
+  static_assert(UNITS_V * NT * 16 == C * ROWS * (int)sizeof(TIn), "V staging");
   uint4 k[UNITS_K];
   uint4 q[UNITS_K];
-  float4 t[4];
-  float4 p[4];
-  float4 v;          // 4 values of the V slice (bf16 inputs use .x/.y bits)
+  uint4 tp[UNITS_TP];
+  uint4 v[UNITS_V];
   float g;
 };
 
-template <int DK, typename TIn, typename TOut>
-__global__ __launch_bounds__(256) void scan_kernel(
+template <int DK, typename TIn, typename TOut, int NW>
+__global__ __launch_bounds__(64 * NW) void scan_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const float* S0, TOut* __restrict__ o,
     float* ST, const float* __restrict__ ws, int T, int H, int DV,
-    int nchunks, int nblocks) {
+    int nchunks, int nblocks, SegArgs seg) {
   constexpr bool KEXACT = std::is_same<TIn, bf16>::value;   // q, k, v exact in bf16
   constexpr bool OPREC = std::is_same<TOut, float>::value;  // o stored in fp32
-  using KT = typename std::conditional<KEXACT, bf16, float>::type;
-  constexpr int LDK = KEXACT ? DK + 8 : DK + 4;   // K/Q tile row stride
-  constexpr int LDT = C + 8;                      // bf16 stride of T/P
-  constexpr int LDV = C + 4;                      // fp32 stride of [r][c] tiles
-  constexpr int LDS_ = DK + 4;                    // fp32 stride of the S slice
-  constexpr int NDT = DK / 64;                    // state d-tiles per wave
-  constexpr int EPU = 16 / (int)sizeof(TIn);      // elements per 16B unit
-  constexpr int UPR = DK / EPU;                   // 16B units per K/Q row
-  using St = Stage<DK, TIn>;
+  constexpr int NT = 64 * NW;           // threads
+  constexpr int ROWS = 16 * NW;         // state rows of the workgroup
+  constexpr int LDK = DK + 8;           // bf16 stride of the K / Q tiles
+  constexpr int LDT = C + 8;            // bf16 stride of the T / P tiles
+  constexpr int LDV = ROWS + 8;         // bf16 stride of the V tile [c][r]
+  constexpr int NDT = DK / 16;          // d-tiles of a 16-row state slice
+  constexpr int NKB = DK / 32;          // 32-wide k-blocks over d
+  constexpr int EPU = 16 / (int)sizeof(TIn);    // input elements per 16B unit
+  constexpr int UPR = DK / EPU;                 // 16B units per K/Q row
+  constexpr int VUPR = ROWS / EPU;              // 16B units per V row
+  using St = Stage<DK, TIn, NT, ROWS>;
 
-  __shared__ __attribute__((aligned(16))) KT Ks[C * LDK];
-  __shared__ __attribute__((aligned(16))) KT Qs[C * LDK];
-  __shared__ __attribute__((aligned(16))) bf16 Th[C * LDT];
-  __shared__ __attribute__((aligned(16))) bf16 Tl[C * LDT];
-  __shared__ __attribute__((aligned(16))) bf16 Ph[C * LDT];
-  __shared__ __attribute__((aligned(16))) bf16 Pl[OPREC ? C * LDT : 8];
-  __shared__ __attribute__((aligned(16))) float Vt[16 * LDV];
+  __shared__ __attribute__((aligned(16))) bf16 Khs[C * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 Kls[KEXACT ? 8 : C * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 Qhs[C * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 Qls[KEXACT ? 8 : C * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 TPs[4][C * LDT];   // Th, Tl, Ph, Pl
+  __shared__ __attribute__((aligned(16))) bf16 Vhs[C * LDV];
+  __shared__ __attribute__((aligned(16))) bf16 Vls[KEXACT ? 8 : C * LDV];
   __shared__ __attribute__((aligned(16))) float Gs[4 * C];
-  __shared__ __attribute__((aligned(16))) float Sx[16 * LDS_];
-  __shared__ __attribute__((aligned(16))) float Zt[16 * LDV];
-  __shared__ __attribute__((aligned(16))) float Ut[16 * LDV];
+  const bf16* Ths = TPs[0];
+  const bf16* Tls = TPs[1];
+  const bf16* Phs = TPs[2];
+  const bf16* Pls = TPs[3];
 
-  // workgroup -> (head, 16-row slice); the slices of one head are placed on
-  // one XCD (workgroups are dealt to the 8 XCDs round-robin) so they share
-  // that XCD's L2 copy of the chunk tiles.
+  // workgroup -> (head, segment, row group); the row groups of a head are
+  // placed on one XCD (workgroups are dealt to the 8 XCDs round-robin) so
+  // they share that XCD's L2 copy of the chunk tiles.  Segment 0 has the
+  // DV/ROWS groups of real state rows; every later segment also has DK/ROWS
+  // groups of transition rows (see SegArgs).
   int lin = blockIdx.x;
   if ((nblocks & 7) == 0) lin = (lin & 7) * (nblocks >> 3) + (lin >> 3);
-  const int NS = DV / 16;
-  const int bh = lin / NS, slice = lin - bh * NS;
+  const int NRG0 = DV / ROWS, NRGX = (DV + DK) / ROWS;
+  const int per_head = NRG0 + (seg.nseg - 1) * NRGX;
+  const int bh = lin / per_head;
+  int sg = 0, rg = lin - bh * per_head;
+  if (rg >= NRG0) {
+    sg = 1 + (rg - NRG0) / NRGX;
+    rg = (rg - NRG0) % NRGX;
+  }
+  const bool xrows = rg >= NRG0;            // transition rows (segments >= 1)
   const int b = bh / H, h = bh - b * H;
-  const int r0 = slice * 16;
+  const int r0 = (xrows ? rg - NRG0 : rg) * ROWS;   // first row of the group
+  const int c_begin = sg * seg.seg_chunks;
+  const int c_end = min(c_begin + seg.seg_chunks, nchunks);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 15, g4 = lane >> 4;
+  const int rw = 16 * w;                    // this wave's rows within the group
 
-  // ---- stage helpers ----
   auto load_stage = [&](St& st, int chunk) {
     const int t0 = chunk * C;
     const int nvalid = min(C, T - t0);
 #pragma unroll
     for (int i = 0; i < St::UNITS_K; ++i) {
-      const int u = tid + 256 * i;
+      const int u = tid + NT * i;
       const int c = u / UPR, cu = u - c * UPR;
-      // (written as two plain stores: a chained assignment here crashes the
-      // ROCm 7.2 backend's machine copy propagation)
+      // (two plain stores: a chained assignment here crashes the ROCm 7.2
+      // backend's machine copy propagation)
       st.k[i] = make_uint4(0, 0, 0, 0);
       st.q[i] = make_uint4(0, 0, 0, 0);
       if (c < nvalid) {
@@ -280,242 +418,258 @@ __global__ __launch_bounds__(256) void scan_kernel(
         st.q[i] = *reinterpret_cast<const uint4*>(q + row + cu * EPU);
       }
     }
-    const float* wsc = ws + ((size_t)bh * nchunks + chunk) * kChunkWsFloats;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      st.t[i] = *reinterpret_cast<const float4*>(wsc + 4 * (tid + 256 * i));
-      st.p[i] = *reinterpret_cast<const float4*>(wsc + C * C + 4 * (tid + 256 * i));
+    for (int i = 0; i < St::UNITS_V; ++i) {
+      const int u = tid + NT * i;
+      const int c = u / VUPR, cu = u - c * VUPR;
+      st.v[i] = make_uint4(0, 0, 0, 0);
+      if (c < nvalid && !xrows)
+        st.v[i] = *reinterpret_cast<const uint4*>(
+            v + (((size_t)b * T + t0 + c) * H + h) * DV + r0 + cu * EPU);
     }
-    st.g = wsc[2 * C * C + tid];
-    const int c = tid >> 2, r4 = (tid & 3) * 4;
-    if (c < nvalid) {
-      st.v = load4(v + (((size_t)b * T + t0 + c) * H + h) * DV + r0 + r4);
-    } else {
-      st.v = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    const char* wsc = reinterpret_cast<const char*>(ws) +
+                      ((size_t)bh * nchunks + chunk) * kChunkWsFloats * 4;
+#pragma unroll
+    for (int i = 0; i < St::UNITS_TP; ++i)
+      st.tp[i] = *reinterpret_cast<const uint4*>(wsc + 16 * (tid + NT * i));
+    st.g = (tid < 4 * C) ? reinterpret_cast<const float*>(wsc + kWsG)[tid] : 0.f;
   };
 
   auto commit_stage = [&](const St& st) {
 #pragma unroll
     for (int i = 0; i < St::UNITS_K; ++i) {
-      const int u = tid + 256 * i;
-      const int c = u / UPR, cu = u - c * UPR;
-      *reinterpret_cast<uint4*>(&Ks[c * LDK + cu * EPU]) = st.k[i];
-      *reinterpret_cast<uint4*>(&Qs[c * LDK + cu * EPU]) = st.q[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e0 = 4 * (tid + 256 * i);
-      const int j = e0 / C, i0 = e0 - j * C;
-      bf16x4 th, tl, ph, pl;
-      const float tv[4] = {st.t[i].x, st.t[i].y, st.t[i].z, st.t[i].w};
-      const float pv[4] = {st.p[i].x, st.p[i].y, st.p[i].z, st.p[i].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        th[e] = (bf16)tv[e];
-        tl[e] = (bf16)(tv[e] - (float)th[e]);
-        ph[e] = (bf16)pv[e];
-        pl[e] = (bf16)(pv[e] - (float)ph[e]);
+      const int u = tid + NT * i;
+      const int c = u / UPR, d0 = (u - c * UPR) * EPU;
+      if constexpr (KEXACT) {
+        *reinterpret_cast<uint4*>(&Khs[c * LDK + d0]) = st.k[i];
+        *reinterpret_cast<uint4*>(&Qhs[c * LDK + d0]) = st.q[i];
+      } else {
+        const float4 kf = __builtin_bit_cast(float4, st.k[i]);
+        const float4 qf = __builtin_bit_cast(float4, st.q[i]);
+        const float kx[4] = {kf.x, kf.y, kf.z, kf.w};
+        const float qx[4] = {qf.x, qf.y, qf.z, qf.w};
+        bf16x4 kh, kl, qh, ql;
+        split4(kx, kh, kl);
+        split4(qx, qh, ql);
+        *reinterpret_cast<bf16x4*>(&Khs[c * LDK + d0]) = kh;
+        *reinterpret_cast<bf16x4*>(&Kls[c * LDK + d0]) = kl;
+        *reinterpret_cast<bf16x4*>(&Qhs[c * LDK + d0]) = qh;
+        *reinterpret_cast<bf16x4*>(&Qls[c * LDK + d0]) = ql;
       }
-      *reinterpret_cast<bf16x4*>(&Th[j * LDT + i0]) = th;
-      *reinterpret_cast<bf16x4*>(&Tl[j * LDT + i0]) = tl;
-      *reinterpret_cast<bf16x4*>(&Ph[j * LDT + i0]) = ph;
-      if constexpr (OPREC) *reinterpret_cast<bf16x4*>(&Pl[j * LDT + i0]) = pl;
     }
-    const int c = tid >> 2, r4 = (tid & 3) * 4;
-    Vt[(r4 + 0) * LDV + c] = st.v.x;
-    Vt[(r4 + 1) * LDV + c] = st.v.y;
-    Vt[(r4 + 2) * LDV + c] = st.v.z;
-    Vt[(r4 + 3) * LDV + c] = st.v.w;
-    Gs[tid] = st.g;
-  };
-
-  // A operand: 8 k-slots of row `row` of a K/Q tile (bf16 hi [+ lo]).
-  auto read_kq = [&](const KT* X, int row, int s, bf16x8& hi, bf16x8& lo) {
-    if constexpr (KEXACT) {
-      const bf16x4 a = *reinterpret_cast<const bf16x4*>(&X[row * LDK + kslot_base(s, g4, 0)]);
-      const bf16x4 c2 = *reinterpret_cast<const bf16x4*>(&X[row * LDK + kslot_base(s, g4, 1)]);
-      hi = __builtin_shufflevector(a, c2, 0, 1, 2, 3, 4, 5, 6, 7);
-    } else {
-      const float4 a = *reinterpret_cast<const float4*>(&X[row * LDK + kslot_base(s, g4, 0)]);
-      const float4 c2 = *reinterpret_cast<const float4*>(&X[row * LDK + kslot_base(s, g4, 1)]);
-      const floatx8 x = {a.x, a.y, a.z, a.w, c2.x, c2.y, c2.z, c2.w};
-      split8(x, hi, lo);
-    }
-  };
-  // 8 k-slots of an fp32 [r][k] tile at row n (B operand of a k-block).
-  auto read_f8 = [&](const float* X, int ld, int s) -> floatx8 {
-    const float4 a = *reinterpret_cast<const float4*>(&X[n * ld + kslot_base(s, g4, 0)]);
-    const float4 c2 = *reinterpret_cast<const float4*>(&X[n * ld + kslot_base(s, g4, 1)]);
-    const floatx8 x = {a.x, a.y, a.z, a.w, c2.x, c2.y, c2.z, c2.w};
-    return x;
-  };
-  // 8 k-slots of row `row` of a bf16 [c][c'] tile.
-  auto read_t8 = [&](const bf16* X, int row, int s) -> bf16x8 {
-    const bf16x4 a = *reinterpret_cast<const bf16x4*>(&X[row * LDT + kslot_base(s, g4, 0)]);
-    const bf16x4 c2 = *reinterpret_cast<const bf16x4*>(&X[row * LDT + kslot_base(s, g4, 1)]);
-    return __builtin_shufflevector(a, c2, 0, 1, 2, 3, 4, 5, 6, 7);
-  };
-
-  // ---- carried state: wave w owns d-tiles w*NDT .. w*NDT+NDT-1 ----
-  floatx4 accS[NDT];
 #pragma unroll
-  for (int t = 0; t < NDT; ++t) {
-    const int d0 = 16 * (w * NDT + t) + 4 * g4;
-    if (S0 != nullptr) {
-      const float4 x = *reinterpret_cast<const float4*>(
-          S0 + ((size_t)bh * DV + r0 + n) * DK + d0);
-      accS[t] = floatx4{x.x, x.y, x.z, x.w};
-    } else {
-      accS[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < St::UNITS_TP; ++i) {
+      const int u = tid + NT * i;             // 16B unit of [4][64][64] bf16
+      const int m = u >> 9, rem = u & 511;    // 512 units per 64x64 matrix
+      const int j = rem >> 3, i0 = (rem & 7) * 8;
+      *reinterpret_cast<uint4*>(&TPs[m][j * LDT + i0]) = st.tp[i];
     }
+#pragma unroll
+    for (int i = 0; i < St::UNITS_V; ++i) {
+      const int u = tid + NT * i;
+      const int c = u / VUPR, rr = (u - c * VUPR) * EPU;
+      if constexpr (KEXACT) {
+        *reinterpret_cast<uint4*>(&Vhs[c * LDV + rr]) = st.v[i];
+      } else {
+        const float4 vf = __builtin_bit_cast(float4, st.v[i]);
+        const float vx[4] = {vf.x, vf.y, vf.z, vf.w};
+        bf16x4 vh, vl;
+        split4(vx, vh, vl);
+        *reinterpret_cast<bf16x4*>(&Vhs[c * LDV + rr]) = vh;
+        *reinterpret_cast<bf16x4*>(&Vls[c * LDV + rr]) = vl;
+      }
+    }
+    if (tid < 4 * C) Gs[tid] = st.g;
+  };
+
+  // ---- carried state of this wave: S^T tiles, lane holds
+  //      S^T[d = 16 dt + 4 g4 + i][r = n]  (i = 0..3) ----
+  // Initial state: S0 rows for segment 0 (or zero), zero for the real rows
+  // of later segments, identity rows for the transition rows.
+  floatx4 S[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    if (xrows) {
+      const int row = r0 + rw + n;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[dt][i] = (16 * dt + 4 * g4 + i == row) ? 1.f : 0.f;
+    } else if (S0 != nullptr && sg == 0) {
+      const float4 x = *reinterpret_cast<const float4*>(
+          S0 + ((size_t)bh * DV + r0 + rw + n) * DK + 16 * dt + 4 * g4);
+      S[dt] = floatx4{x.x, x.y, x.z, x.w};
+    } else {
+      S[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  // Outputs: o rows of the real state, or x^_t = X_t q_t of the transition
+  // rows ([BH][T][DK], bf16).
+  TOut* obase;
+  size_t ostride;
+  if (xrows) {
+    obase = reinterpret_cast<TOut*>(seg.xhat) + (size_t)bh * T * DK + r0 + rw + n;
+    ostride = DK;
+  } else {
+    obase = o + ((size_t)b * T * H + h) * DV + r0 + rw + n;
+    ostride = (size_t)H * DV;
   }
 
   St st;
-  load_stage(st, 0);
+  load_stage(st, c_begin);
 
-  for (int chunk = 0; chunk < nchunks; ++chunk) {
+  for (int chunk = c_begin; chunk < c_end; ++chunk) {
     const int t0 = chunk * C;
     const int nvalid = min(C, T - t0);
-    __syncthreads();                 // previous chunk done with the LDS tiles
+    __syncthreads();                   // everyone is done with the last tiles
     commit_stage(st);
-#pragma unroll
-    for (int t = 0; t < NDT; ++t) {
-      const int d0 = 16 * (w * NDT + t) + 4 * g4;
-      *reinterpret_cast<float4*>(&Sx[n * LDS_ + d0]) =
-          make_float4(accS[t][0], accS[t][1], accS[t][2], accS[t][3]);
-    }
     __syncthreads();
-    if (chunk + 1 < nchunks) load_stage(st, chunk + 1);   // prefetch
+    if (chunk + 1 < c_end) load_stage(st, chunk + 1);   // prefetch
 
-    const int crow = 16 * w + n;         // A-operand row of this wave's c-tile
-    const int cacc = 16 * w + 4 * g4;    // first accumulator row (c) of lane
-
-    // ---- Y = K S^T for c-tile w (state-touching: split S) ----
-    floatx4 accY = {0.f, 0.f, 0.f, 0.f};
+    // split the state into bf16 hi/lo B operands, one per 32-wide k-block
+    bf16x8 Sh[NKB], Sl[NKB];
 #pragma unroll
-    for (int s = 0; s < DK / 32; ++s) {
-      bf16x8 ah, al, bh, bl;
-      read_kq(Ks, crow, s, ah, al);
-      split8(read_f8(Sx, LDS_, s), bh, bl);
-      accY = mfma(ah, bh, accY);
-      accY = mfma(ah, bl, accY);
-      if constexpr (!KEXACT) accY = mfma(al, bh, accY);
+    for (int s = 0; s < NKB; ++s) split8(acc_slots(S[2 * s], S[2 * s + 1]), Sh[s], Sl[s]);
+
+    // ---- Y = K S^T  (c-tile ct: rows c = 16 ct + 4 g4 + i, col r = n) ----
+    floatx4 Y[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NKB; ++s) {
+        const bf16x8 kh = lds_slots(Khs, LDK, 16 * ct + n, s, g4);
+        acc = mfma(kh, Sh[s], acc);
+        acc = mfma(kh, Sl[s], acc);
+        if constexpr (!KEXACT) acc = mfma(lds_slots(Kls, LDK, 16 * ct + n, s, g4), Sh[s], acc);
+      }
+      Y[ct] = acc;
     }
 
-    // ---- Z = beta (V - gamma Y) -> Zt[r][c] ----
+    // ---- Z = beta (V - gamma Y), as split B operands over c ----
+    bf16x8 Zh[2], Zl[2];
     {
-      const float4 vv = *reinterpret_cast<const float4*>(&Vt[n * LDV + cacc]);
-      const float4 bb = *reinterpret_cast<const float4*>(&Gs[C + cacc]);
-      const float4 gg = *reinterpret_cast<const float4*>(&Gs[2 * C + cacc]);
-      float4 z;
-      z.x = bb.x * (vv.x - gg.x * accY[0]);
-      z.y = bb.y * (vv.y - gg.y * accY[1]);
-      z.z = bb.z * (vv.z - gg.z * accY[2]);
-      z.w = bb.w * (vv.w - gg.w * accY[3]);
-      *reinterpret_cast<float4*>(&Zt[n * LDV + cacc]) = z;
-    }
-    __syncthreads();
-
-    // ---- U = T Z for c-tile w (T lower triangular: k-blocks <= w/2) ----
-    floatx4 accU = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s <= (w >> 1); ++s) {
-      const bf16x8 th = read_t8(Th, crow, s), tl = read_t8(Tl, crow, s);
-      bf16x8 zh, zl;
-      split8(read_f8(Zt, LDV, s), zh, zl);
-      accU = mfma(th, zh, accU);
-      accU = mfma(th, zl, accU);
-      accU = mfma(tl, zh, accU);
-    }
-    *reinterpret_cast<float4*>(&Ut[n * LDV + cacc]) =
-        make_float4(accU[0], accU[1], accU[2], accU[3]);
-    __syncthreads();
-
-    // ---- O = diag(gamma) Q S^T + P U for c-tile w ----
-    {
-      floatx4 accO = {0.f, 0.f, 0.f, 0.f};
+      floatx4 Z[4];
 #pragma unroll
-      for (int s = 0; s < DK / 32; ++s) {
-        bf16x8 ah, al, bh, bl;
-        read_kq(Qs, crow, s, ah, al);
-        split8(read_f8(Sx, LDS_, s), bh, bl);
-        accO = mfma(ah, bh, accO);
+      for (int ct = 0; ct < 4; ++ct) {
+        const int c = 16 * ct + 4 * g4;
+        const uint2 vw = lds_tr4(Vhs, LDV, c, rw, n);    // V[c + j][rw + n]
+        float vv[4] = {bf16lo(vw.x), bf16hi(vw.x), bf16lo(vw.y), bf16hi(vw.y)};
+        if constexpr (!KEXACT) {
+          const uint2 vl = lds_tr4(Vls, LDV, c, rw, n);
+          vv[0] += bf16lo(vl.x);
+          vv[1] += bf16hi(vl.x);
+          vv[2] += bf16lo(vl.y);
+          vv[3] += bf16hi(vl.y);
+        }
+        const float4 bb = *reinterpret_cast<const float4*>(&Gs[C + c]);
+        const float4 gg = *reinterpret_cast<const float4*>(&Gs[2 * C + c]);
+        Z[ct] = floatx4{bb.x * (vv[0] - gg.x * Y[ct][0]), bb.y * (vv[1] - gg.y * Y[ct][1]),
+                        bb.z * (vv[2] - gg.z * Y[ct][2]), bb.w * (vv[3] - gg.w * Y[ct][3])};
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) split8(acc_slots(Z[2 * s], Z[2 * s + 1]), Zh[s], Zl[s]);
+    }
+
+    // ---- U = T Z  (T lower triangular: c-tile ct needs k-blocks <= ct/2) ----
+    floatx4 U[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s <= ct / 2; ++s) {
+        const bf16x8 th = lds_slots(Ths, LDT, 16 * ct + n, s, g4);
+        const bf16x8 tl = lds_slots(Tls, LDT, 16 * ct + n, s, g4);
+        acc = mfma(th, Zh[s], acc);
+        acc = mfma(th, Zl[s], acc);
+        acc = mfma(tl, Zh[s], acc);
+      }
+      U[ct] = acc;
+    }
+    bf16x8 Uh[2], Ul[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) split8(acc_slots(U[2 * s], U[2 * s + 1]), Uh[s], Ul[s]);
+
+    // ---- O = diag(gamma) Q S^T + P U ----
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NKB; ++s) {
+        const bf16x8 qh = lds_slots(Qhs, LDK, 16 * ct + n, s, g4);
+        acc = mfma(qh, Sh[s], acc);
         if constexpr (OPREC) {
-          accO = mfma(ah, bl, accO);
-          if constexpr (!KEXACT) accO = mfma(al, bh, accO);
+          acc = mfma(qh, Sl[s], acc);
+          if constexpr (!KEXACT) acc = mfma(lds_slots(Qls, LDK, 16 * ct + n, s, g4), Sh[s], acc);
         }
       }
-      const float4 gg = *reinterpret_cast<const float4*>(&Gs[2 * C + cacc]);
-      accO[0] *= gg.x;
-      accO[1] *= gg.y;
-      accO[2] *= gg.z;
-      accO[3] *= gg.w;
-      for (int s = 0; s <= (w >> 1); ++s) {
-        const bf16x8 ph = read_t8(Ph, crow, s);
-        bf16x8 uh, ul;
-        split8(read_f8(Ut, LDV, s), uh, ul);
-        accO = mfma(ph, uh, accO);
+      const int c = 16 * ct + 4 * g4;
+      const float4 gg = *reinterpret_cast<const float4*>(&Gs[2 * C + c]);
+      acc[0] *= gg.x;
+      acc[1] *= gg.y;
+      acc[2] *= gg.z;
+      acc[3] *= gg.w;
+#pragma unroll
+      for (int s = 0; s <= ct / 2; ++s) {
+        const bf16x8 ph = lds_slots(Phs, LDT, 16 * ct + n, s, g4);
+        acc = mfma(ph, Uh[s], acc);
         if constexpr (OPREC) {
-          const bf16x8 pl = read_t8(Pl, crow, s);
-          accO = mfma(ph, ul, accO);
-          accO = mfma(pl, uh, accO);
+          acc = mfma(ph, Ul[s], acc);
+          acc = mfma(lds_slots(Pls, LDT, 16 * ct + n, s, g4), Uh[s], acc);
         }
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int c = cacc + e;
-        if (c < nvalid)
-          store1(o + (((size_t)b * T + t0 + c) * H + h) * DV + r0 + n, accO[e]);
+        if (c + e < nvalid) store1(obase + (size_t)(t0 + c + e) * ostride, acc[e]);
       }
     }
 
-    // ---- S^T <- gamma_C S^T + K^T diag(e^{g_C - g}) U  (owned d-tiles) ----
+    // ---- S^T <- gamma_C S^T + K^T diag(e^{g_C - g}) U ----
     {
-      const float gC = Gs[2 * C + C - 1];
-      bf16x8 uh[2], ul[2];
+      bf16x8 Dh[2], Dl[2];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const floatx8 u8 = read_f8(Ut, LDV, s);
         const float4 d0 = *reinterpret_cast<const float4*>(&Gs[3 * C + kslot_base(s, g4, 0)]);
         const float4 d1 = *reinterpret_cast<const float4*>(&Gs[3 * C + kslot_base(s, g4, 1)]);
-        const floatx8 du = {u8[0] * d0.x, u8[1] * d0.y, u8[2] * d0.z, u8[3] * d0.w,
-                            u8[4] * d1.x, u8[5] * d1.y, u8[6] * d1.z, u8[7] * d1.w};
-        split8(du, uh[s], ul[s]);
+        const floatx4& ua = U[2 * s];
+        const floatx4& ub = U[2 * s + 1];
+        const floatx8 du = {ua[0] * d0.x, ua[1] * d0.y, ua[2] * d0.z, ua[3] * d0.w,
+                            ub[0] * d1.x, ub[1] * d1.y, ub[2] * d1.z, ub[3] * d1.w};
+        split8(du, Dh[s], Dl[s]);
       }
+      const float gC = Gs[3 * C - 1];
 #pragma unroll
-      for (int t = 0; t < NDT; ++t) {
-        const int dcol = 16 * (w * NDT + t) + n;   // A row = state column d
-        floatx4 acc = accS[t] * gC;
+      for (int dt = 0; dt < NDT; ++dt) {
+        floatx4 acc = S[dt] * gC;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          floatx8 kx;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            kx[e] = (float)Ks[(kslot_base(s, g4, 0) + e) * LDK + dcol];
-            kx[4 + e] = (float)Ks[(kslot_base(s, g4, 1) + e) * LDK + dcol];
-          }
-          bf16x8 kh, kl;
-          if constexpr (KEXACT) {
-            kh = to_bf16x8(kx);
-          } else {
-            split8(kx, kh, kl);
-          }
-          acc = mfma(kh, uh[s], acc);
-          acc = mfma(kh, ul[s], acc);
-          if constexpr (!KEXACT) acc = mfma(kl, uh[s], acc);
+          const bf16x8 kth = lds_slots_tr(Khs, LDK, 16 * dt, s, g4, n);   // K[kslot][16 dt + n]
+          acc = mfma(kth, Dh[s], acc);
+          acc = mfma(kth, Dl[s], acc);
+          if constexpr (!KEXACT) acc = mfma(lds_slots_tr(Kls, LDK, 16 * dt, s, g4, n), Dh[s], acc);
         }
-        accS[t] = acc;
+        S[dt] = acc;
       }
     }
   }
 
-  if (ST != nullptr) {
+  // Final state: ST directly when unsegmented; otherwise this segment's
+  // real rows or transition rows for the combine pass.
+  float* sdst = nullptr;
+  size_t srow = 0;
+  if (seg.nseg == 1) {
+    sdst = ST;
+    srow = (size_t)bh * DV + r0 + rw + n;
+  } else if (xrows) {
+    sdst = seg.X_fin;
+    srow = ((size_t)bh * seg.nseg + sg) * DK + r0 + rw + n;
+  } else {
+    sdst = seg.S_fin;
+    srow = ((size_t)bh * seg.nseg + sg) * DV + r0 + rw + n;
+  }
+  if (sdst != nullptr) {
 #pragma unroll
-    for (int t = 0; t < NDT; ++t) {
-      const int d0 = 16 * (w * NDT + t) + 4 * g4;
-      *reinterpret_cast<float4*>(ST + ((size_t)bh * DV + r0 + n) * DK + d0) =
-          make_float4(accS[t][0], accS[t][1], accS[t][2], accS[t][3]);
-    }
+    for (int dt = 0; dt < NDT; ++dt)
+      *reinterpret_cast<float4*>(sdst + srow * DK + 16 * dt + 4 * g4) =
+          make_float4(S[dt][0], S[dt][1], S[dt][2], S[dt][3]);
   }
 }
 
@@ -545,7 +699,7 @@ static void launch_prepare_t(const void* q, const void* k, const float* alpha,
                              const float* beta, float* ws, int B, int T, int H,
                              hipStream_t stream) {
   const int nchunks = (T + C - 1) / C;
-  hipLaunchKernelGGL((prepare_kernel<DK, TIn>), dim3(nchunks, H, B), dim3(256),
+  hipLaunchKernelGGL((prepare_kernel<DK, TIn>), dim3(nchunks, H, B), dim3(64),
                      0, stream, static_cast<const TIn*>(q),
                      static_cast<const TIn*>(k), alpha, beta, ws, T, H,
                      nchunks);
@@ -565,27 +719,187 @@ hipError_t launch_prefill_prepare(const void* q, const void* k,
   return hipGetLastError();
 }
 
+// ===========================================================================
+// segment combine (phase 2): S_in(s) = S_end(s-1), S_end(s) = S_in(s) X_s + S_loc(s)
+// ===========================================================================
+
+// One workgroup per (head, 64 state rows), sequential over the segments.
+// Each wave carries 16 rows as S^T tiles; X_s is staged in LDS as bf16 hi/lo
+// and read transposed, the product uses split-bf16 operands on both sides.
+template <int DK>
+__global__ __launch_bounds__(256) void segment_combine_kernel(SegArgs seg,
+                                                              float* ST, int DV) {
+  constexpr int LDX = DK + 8;
+  constexpr int NDT = DK / 16, NKB = DK / 32;
+  __shared__ __attribute__((aligned(16))) bf16 Xh[DK * LDX];
+  __shared__ __attribute__((aligned(16))) bf16 Xl[DK * LDX];
+  const int NRG = DV / 64;
+  const int bh = blockIdx.x / NRG, rg = blockIdx.x - bh * NRG;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = lane & 15, g4 = lane >> 4;
+  const int row = rg * 64 + 16 * w + n;          // this lane's state row
+  auto srow = [&](float* base, int s) {
+    return base + (((size_t)bh * seg.nseg + s) * DV + row) * DK;
+  };
+
+  floatx4 S[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    const float4 x = *reinterpret_cast<const float4*>(srow(seg.S_fin, 0) + 16 * dt + 4 * g4);
+    S[dt] = floatx4{x.x, x.y, x.z, x.w};
+  }
+  for (int s = 1; s < seg.nseg; ++s) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      *reinterpret_cast<float4*>(srow(seg.S_in, s) + 16 * dt + 4 * g4) =
+          make_float4(S[dt][0], S[dt][1], S[dt][2], S[dt][3]);
+    __syncthreads();                       // previous X_s no longer read
+    const float* X = seg.X_fin + ((size_t)bh * seg.nseg + s) * DK * DK;
+    for (int u = tid; u < DK * DK / 4; u += 256) {
+      const int e = (4 * u) / DK, d0 = (4 * u) % DK;
+      const float4 x = *reinterpret_cast<const float4*>(X + (size_t)e * DK + d0);
+      const float xv[4] = {x.x, x.y, x.z, x.w};
+      bf16x4 hi, lo;
+      split4(xv, hi, lo);
+      *reinterpret_cast<bf16x4*>(&Xh[e * LDX + d0]) = hi;
+      *reinterpret_cast<bf16x4*>(&Xl[e * LDX + d0]) = lo;
+    }
+    __syncthreads();
+    bf16x8 Sh[NKB], Sl[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) split8(acc_slots(S[2 * kb], S[2 * kb + 1]), Sh[kb], Sl[kb]);
+    floatx4 Sn[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const float4 x = *reinterpret_cast<const float4*>(srow(seg.S_fin, s) + 16 * dt + 4 * g4);
+      floatx4 acc = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 ah = lds_slots_tr(Xh, LDX, 16 * dt, kb, g4, n);   // X[e][16 dt + n]
+        const bf16x8 al = lds_slots_tr(Xl, LDX, 16 * dt, kb, g4, n);
+        acc = mfma(ah, Sh[kb], acc);
+        acc = mfma(ah, Sl[kb], acc);
+        acc = mfma(al, Sh[kb], acc);
+      }
+      Sn[dt] = acc;
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) S[dt] = Sn[dt];
+  }
+  if (ST != nullptr) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      *reinterpret_cast<float4*>(ST + ((size_t)bh * DV + row) * DK + 16 * dt + 4 * g4) =
+          make_float4(S[dt][0], S[dt][1], S[dt][2], S[dt][3]);
+  }
+}
+
+// ===========================================================================
+// segment correction (phase 3): o_t += S_in(s) x^_t for tokens of segments >= 1
+// ===========================================================================
+
+// One workgroup per (chunk of a segment >= 1, head, 64 state rows); wave w
+// handles 16 rows for the 64 tokens.  Single-pass bf16 (outputs are bf16).
+template <int DK>
+__global__ __launch_bounds__(256) void segment_correct_kernel(SegArgs seg, bf16* o,
+                                                              int T, int H, int DV) {
+  constexpr int NKB = DK / 32;
+  const int chunk = seg.seg_chunks + blockIdx.x;
+  const int s = chunk / seg.seg_chunks;
+  const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
+  const int t0 = chunk * C;
+  const int nvalid = min(C, T - t0);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n = lane & 15, g4 = lane >> 4;
+  const int row = blockIdx.z * 64 + 16 * w + n;
+  // B operand: S_in[row][32 kb + 8 g4 .. + 7]
+  bf16x8 Bs[NKB];
+  const float* sin_row = seg.S_in + (((size_t)bh * seg.nseg + s) * DV + row) * DK;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    const float4 a = *reinterpret_cast<const float4*>(sin_row + 32 * kb + 8 * g4);
+    const float4 c = *reinterpret_cast<const float4*>(sin_row + 32 * kb + 8 * g4 + 4);
+    Bs[kb] = to_bf16x8(floatx8{a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w});
+  }
+  const bf16* xh = reinterpret_cast<const bf16*>(seg.xhat) + (size_t)bh * T * DK;
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const int ta = 16 * tt + n;                 // A-operand token of this lane
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      bf16x8 a = {};
+      if (ta < nvalid)
+        a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                           xh + (size_t)(t0 + ta) * DK + 32 * kb + 8 * g4));
+      acc = mfma(a, Bs[kb], acc);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tc = 16 * tt + 4 * g4 + i;
+      if (tc < nvalid) {
+        bf16* p = o + (((size_t)b * T + t0 + tc) * H + h) * DV + row;
+        *p = (bf16)((float)*p + acc[i]);
+      }
+    }
+  }
+}
+
+// ===========================================================================
+// scan launcher
+// ===========================================================================
+
+// Waves per scan workgroup (16 state rows each).
+constexpr int kScanWaves = 4;
+
 template <int DK, typename TIn, typename TOut>
 static void launch_scan_t(const void* q, const void* k, const void* v,
                           const float* S0, void* o, float* ST, const float* ws,
-                          int B, int T, int H, int dv, hipStream_t stream) {
+                          int B, int T, int H, int dv, const SegArgs& seg,
+                          hipStream_t stream) {
   const int nchunks = (T + C - 1) / C;
-  const int nblocks = B * H * (dv / 16);
-  hipLaunchKernelGGL((scan_kernel<DK, TIn, TOut>), dim3(nblocks), dim3(256), 0,
-                     stream, static_cast<const TIn*>(q),
-                     static_cast<const TIn*>(k), static_cast<const TIn*>(v),
-                     S0, static_cast<TOut*>(o), ST, ws, T, H, dv, nchunks,
-                     nblocks);
+  constexpr int ROWS = 16 * kScanWaves;
+  const int per_head = dv / ROWS + (seg.nseg - 1) * ((dv + DK) / ROWS);
+  const int nblocks = B * H * per_head;
+  hipLaunchKernelGGL((scan_kernel<DK, TIn, TOut, kScanWaves>), dim3(nblocks),
+                     dim3(64 * kScanWaves), 0, stream,
+                     static_cast<const TIn*>(q), static_cast<const TIn*>(k),
+                     static_cast<const TIn*>(v), S0, static_cast<TOut*>(o), ST,
+                     ws, T, H, dv, nchunks, nblocks, seg);
+}
+
+template <int DK>
+static void launch_segment_tail(const SegArgs& seg, void* o, float* ST, int B,
+                                int T, int H, int dv, hipStream_t stream) {
+  const int nchunks = (T + C - 1) / C;
+  hipLaunchKernelGGL((segment_combine_kernel<DK>), dim3(B * H * (dv / 64)),
+                     dim3(256), 0, stream, seg, ST, dv);
+  hipLaunchKernelGGL((segment_correct_kernel<DK>),
+                     dim3(nchunks - seg.seg_chunks, B * H, dv / 64), dim3(256),
+                     0, stream, seg, static_cast<bf16*>(o), T, H, dv);
 }
 
 hipError_t launch_prefill_scan(const void* q, const void* k, const void* v,
-                               const float* S0, void* o, float* ST,
-                               const float* ws, int B, int T, int H, int dk,
-                               int dv, int in_dtype, int out_dtype,
-                               hipStream_t stream) {
-#define GDN_SCAN(DK, TI, TO) \
-  launch_scan_t<DK, TI, TO>(q, k, v, S0, o, ST, ws, B, T, H, dv, stream)
+                               const float* S0, void* o, float* ST, void* ws,
+                               int B, int T, int H, int dk, int dv,
+                               int in_dtype, int out_dtype, hipStream_t stream) {
   const bool ib = in_dtype == 1, ob = out_dtype == 1;
+  const PrefillPlan plan = plan_prefill(B, T, H, dk, dv);
+  SegArgs seg{};
+  seg.nseg = 1;
+  seg.seg_chunks = plan.nchunks;
+  char* wsb = static_cast<char*>(ws);
+  if (plan.nseg > 1 && ib && ob) {
+    seg.nseg = plan.nseg;
+    seg.seg_chunks = plan.seg_chunks;
+    seg.xhat = wsb + plan.xhat_off;
+    seg.S_fin = reinterpret_cast<float*>(wsb + plan.sfin_off);
+    seg.X_fin = reinterpret_cast<float*>(wsb + plan.xfin_off);
+    seg.S_in = reinterpret_cast<float*>(wsb + plan.sin_off);
+  }
+  const float* wsf = static_cast<const float*>(ws);
+#define GDN_SCAN(DK, TI, TO) \
+  launch_scan_t<DK, TI, TO>(q, k, v, S0, o, ST, wsf, B, T, H, dv, seg, stream)
   if (dk == 128) {
     if (ib && ob) GDN_SCAN(128, bf16, bf16);
     else if (ib) GDN_SCAN(128, bf16, float);
@@ -598,6 +912,10 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v,
     else GDN_SCAN(64, float, float);
   }
 #undef GDN_SCAN
+  if (seg.nseg > 1) {
+    if (dk == 128) launch_segment_tail<128>(seg, o, ST, B, T, H, dv, stream);
+    else launch_segment_tail<64>(seg, o, ST, B, T, H, dv, stream);
+  }
   return hipGetLastError();
 }
 

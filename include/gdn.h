@@ -73,10 +73,14 @@ const char* gdn_version(void);
 /* ------------------------------------------------------------------------
  * Prefill over whole sequences (chunked form).
  *
- * Bytes of device workspace gdn_prefill needs for these sizes (0 for T = 0).
- * Depends only on B, T, H: one 64-token chunk's triangular correction,
- * masked query-key products and gate prefix sums (33,792 bytes per chunk per
- * head).
+ * Bytes of device workspace gdn_prefill needs for these sizes (0 for T = 0 or
+ * an unsupported dk/dv).  It holds, per 64-token chunk and head, the
+ * chunk's triangular delta correction, its decay-masked query-key products
+ * and its gate prefix sums (33,792 bytes), and, when B*H heads alone are too
+ * few to fill the GPU and T spans at least 16 chunks, buffers for splitting
+ * each sequence into segments that run in parallel (per head: T*dk*2 bytes
+ * plus three dv*dk / dk*dk fp32 matrices per segment).  The size covers
+ * every dtype combination.
  */
 size_t gdn_prefill_workspace_bytes(int B, int T, int H, int dk, int dv);
 
@@ -109,8 +113,13 @@ int gdn_prefill(const void* q, const void* k, const void* v,
  *            sums, the unit-lower-triangular delta correction
  *            (I + A)^{-1} with A_ji = beta_j e^{g_j - g_i} k_j.k_i (i < j),
  *            and the decay-masked query-key products; written to workspace.
- *   scan:    sequential over chunks, parallel over heads and 16-row slices
- *            of the state: reads q, k, v and the workspace, writes o and ST.
+ *   scan:    sequential over chunks, parallel over heads and 64-row groups
+ *            of the state: reads q, k, v and the chunk tiles, writes o and
+ *            ST.  With bf16 inputs and outputs and few heads it also splits
+ *            each sequence into segments (extra "transition" rows give each
+ *            segment's affine map of its incoming state), chains the
+ *            segment states, and corrects the outputs of later segments;
+ *            it then also writes the segment buffers of the workspace.
  */
 int gdn_prefill_prepare(const void* q, const void* k,
                         const float* alpha, const float* beta,
@@ -121,7 +130,7 @@ int gdn_prefill_scan(const void* q, const void* k, const void* v,
                      const float* S0, void* o, float* ST,
                      int B, int T, int H, int dk, int dv,
                      int in_dtype, int out_dtype,
-                     const void* workspace, size_t workspace_bytes,
+                     void* workspace, size_t workspace_bytes,
                      void* stream);
 
 /* ------------------------------------------------------------------------

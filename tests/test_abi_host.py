@@ -44,11 +44,18 @@ def test_status_strings_and_version():
 
 def test_workspace_bytes():
     ws = bd.prefill_workspace_bytes
-    assert ws(1, 64, 1, 128, 128) == 33792
-    assert ws(1, 65, 1, 128, 128) == 2 * 33792
-    assert ws(2, 16384, 16, 128, 128) == 2 * 16 * 256 * 33792
+    chunk = 33792                                # per head per 64-token chunk
+    assert ws(1, 64, 1, 128, 128) == chunk
+    assert ws(1, 65, 1, 128, 128) == 2 * chunk
+    # many heads: no segmentation, only the chunk tiles
+    assert ws(8, 4096, 16, 128, 128) == 8 * 16 * 64 * chunk
+    # few heads, long sequence: chunk tiles plus segment buffers
+    big = ws(1, 16384, 16, 128, 128)
+    assert big > 16 * 256 * chunk
+    assert big >= 16 * 256 * chunk + 16 * 16384 * 128 * 2
     assert ws(1, 0, 16, 128, 128) == 0
     assert ws(0, 10, 16, 128, 128) == 0
+    assert ws(1, 64, 1, 96, 128) == 0
 
 
 def prefill(**kw):

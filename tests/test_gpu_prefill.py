@@ -183,3 +183,25 @@ def test_two_phase_entry_points_match_composite():
     gdn.prefill_scan(d["q"], d["k"], d["v"], d["S0"], o, ST, ws)
     torch.cuda.synchronize()
     assert torch.equal(o, o_ref) and torch.equal(ST, S_ref)
+
+
+@pytest.mark.parametrize("T,dk,dv", [(2048, 128, 128), (1024 + 37, 128, 128),
+                                     (1500, 64, 128), (2048, 128, 64),
+                                     (3000, 64, 64)])
+def test_segmented_prefill_few_heads(T, dk, dv):
+    """Few heads and long sequences take the segment-parallel path (bf16 in
+    and out): transition rows, segment chaining and output correction."""
+    x = gi.generic(1, T, 2, dk, dv, 900 + T + dk + dv, "bf16", S0_scale=0.3)
+    check_full(x, "bf16", f"segmented T={T}")
+
+
+def test_segmented_prefill_in_place_state():
+    x = gi.generic(1, 1300, 3, 128, 128, 31, "bf16", S0_scale=0.5)
+    d = to_dev(x)
+    S = d["S0"].clone()
+    o, ST = gdn.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], S, ST=S)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_prefill(x)
+    assert ST.data_ptr() == S.data_ptr()
+    assert_close("o", errs_o(host(o), o_ref), TOL_BF16)
+    assert_close("S_T", errs_S(host(ST), S_ref), TOL_F32)
