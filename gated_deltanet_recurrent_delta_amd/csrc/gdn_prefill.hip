@@ -141,10 +141,8 @@ __global__ __launch_bounds__(64) void prepare_kernel(
   constexpr bool SPLIT = std::is_same<TIn, float>::value;  // inputs not bf16
   constexpr int NKB = DK / 32;
   constexpr int LDA = C + 4;            // fp32 row stride of A, P and T
-  constexpr int LDB = 16 + 4;           // fp32 row stride of 16x16 scratch
   __shared__ __attribute__((aligned(16))) float As[C * LDA];
   __shared__ __attribute__((aligned(16))) float PTs[C * LDA];   // P, then T
-  __shared__ __attribute__((aligned(16))) float tmp[16 * LDB];
   __shared__ float g2s[C], bs[C];
 
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -154,7 +152,15 @@ __global__ __launch_bounds__(64) void prepare_kernel(
   char* wsc = reinterpret_cast<char*>(ws) +
               ((size_t)(b * H + h) * nchunks + chunk) * kChunkWsFloats * 4;
 
-  // 1. K and Q rows 16 t + n, k-slots 32 s + 8 g4 .. + 7, straight from HBM
+  // 1. gates of the chunk first (vector-memory results return in order, so
+  //    the prefix sum below does not wait for the K/Q tiles), then K and Q
+  //    rows 16 t + n, k-slots 32 s + 8 g4 .. + 7, straight from HBM.
+  float a_in = 1.f, be = 0.f;               // padding tokens: identity step
+  if (lane < nvalid) {
+    const size_t gi = ((size_t)b * T + t0 + lane) * H + h;
+    a_in = alpha[gi];
+    be = beta[gi];
+  }
   bf16x8 Kh[4][NKB], Kl[4][NKB], Qh[4][NKB], Ql[4][NKB];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -173,13 +179,7 @@ __global__ __launch_bounds__(64) void prepare_kernel(
 
   // 2. gates: inclusive prefix sum of log alpha inside the chunk
   {
-    float a = 1.f, be = 0.f;                  // padding tokens: identity step
-    if (lane < nvalid) {
-      const size_t gi = ((size_t)b * T + t0 + lane) * H + h;
-      a = alpha[gi];
-      be = beta[gi];
-    }
-    float g = logf(a);
+    float g = logf(a_in);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float y = __shfl_up(g, off, 64);
@@ -270,44 +270,35 @@ __global__ __launch_bounds__(64) void prepare_kernel(
   __syncthreads();
   // Off-diagonal blocks, nearest the diagonal first:
   //   T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj   (i > j, 16x16 blocks)
-  // lane l computes block rows r = l / 4, columns 4 (l % 4) .. + 3.
-  {
-    const int r = lane >> 2, c0 = (lane & 3) * 4;
+  // on fp32 MFMA (16x16x4, exact fp32 products).  A step kk of a 16x16x16
+  // product contracts over k = 4 g4 + kk, so the accumulator of the first
+  // product (lane holds rows 4 g4 + i) is the B operand of the second one
+  // without any data movement.
 #pragma unroll
-    for (int dist = 1; dist < 4; ++dist) {
+  for (int dist = 1; dist < 4; ++dist) {
 #pragma unroll
-      for (int bj = 0; bj + dist < 4; ++bj) {
-        const int bi = bj + dist;
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int bj = 0; bj + dist < 4; ++bj) {
+      const int bi = bj + dist;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int bk = bj; bk < bi; ++bk) {
+      for (int bk = bj; bk < bi; ++bk) {
 #pragma unroll
-          for (int kk = 0; kk < 16; ++kk) {
-            const float x = As[(16 * bi + r) * LDA + 16 * bk + kk];
-            const float4 y = *reinterpret_cast<const float4*>(&Tt[(16 * bk + kk) * LDA + 16 * bj + c0]);
-            acc[0] += x * y.x;
-            acc[1] += x * y.y;
-            acc[2] += x * y.z;
-            acc[3] += x * y.w;
-          }
+        for (int kk = 0; kk < 4; ++kk) {
+          const float x = As[(16 * bi + n) * LDA + 16 * bk + 4 * g4 + kk];
+          const float y = Tt[(16 * bk + 4 * g4 + kk) * LDA + 16 * bj + n];
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, acc, 0, 0, 0);
         }
-        *reinterpret_cast<float4*>(&tmp[r * LDB + c0]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        __syncthreads();
-        float out[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-          const float x = Tt[(16 * bi + r) * LDA + 16 * bi + kk];
-          const float4 y = *reinterpret_cast<const float4*>(&tmp[kk * LDB + c0]);
-          out[0] -= x * y.x;
-          out[1] -= x * y.y;
-          out[2] -= x * y.z;
-          out[3] -= x * y.w;
-        }
-        *reinterpret_cast<float4*>(&Tt[(16 * bi + r) * LDA + 16 * bj + c0]) =
-            make_float4(out[0], out[1], out[2], out[3]);
-        __syncthreads();
       }
+      floatx4 out = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const float x = Tt[(16 * bi + n) * LDA + 16 * bi + 4 * g4 + kk];
+        out = __builtin_amdgcn_mfma_f32_16x16x4f32(x, acc[kk], out, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Tt[(16 * bi + 4 * g4 + i) * LDA + 16 * bj + n] = -out[i];
     }
+    __syncthreads();
   }
 
   // 6. T -> workspace as bf16 hi/lo
@@ -371,6 +362,9 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
   __shared__ __attribute__((aligned(16))) bf16 Vhs[C * LDV];
   __shared__ __attribute__((aligned(16))) bf16 Vls[KEXACT ? 8 : C * LDV];
   __shared__ __attribute__((aligned(16))) float Gs[4 * C];
+  // per-wave O^T staging [16 r][C c] for 16-byte output stores (bf16 o)
+  constexpr int LDO = C + 8;
+  __shared__ __attribute__((aligned(16))) bf16 Ost[OPREC ? 8 : NW * 16 * LDO];
   const bf16* Ths = TPs[0];
   const bf16* Tls = TPs[1];
   const bf16* Phs = TPs[2];
@@ -401,31 +395,44 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
   const int n = lane & 15, g4 = lane >> 4;
   const int rw = 16 * w;                    // this wave's rows within the group
 
+  // Token rows of this sequence start at k_seq / q_seq / v_seq; one token
+  // is H * DK (H * DV) elements further.
+  const TIn* k_seq = k + ((size_t)b * T * H + h) * DK;
+  const TIn* q_seq = q + ((size_t)b * T * H + h) * DK;
+  const TIn* v_seq = v + ((size_t)b * T * H + h) * DV + r0;
+  const size_t tok_k = (size_t)H * DK, tok_v = (size_t)H * DV;
   auto load_stage = [&](St& st, int chunk) {
     const int t0 = chunk * C;
     const int nvalid = min(C, T - t0);
+    // Branch-free: rows past the end of the sequence load the last valid
+    // row (always in bounds) and are zeroed by a select.
+    const uint4 zero4 = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < St::UNITS_K; ++i) {
       const int u = tid + NT * i;
       const int c = u / UPR, cu = u - c * UPR;
-      // (two plain stores: a chained assignment here crashes the ROCm 7.2
-      // backend's machine copy propagation)
-      st.k[i] = make_uint4(0, 0, 0, 0);
-      st.q[i] = make_uint4(0, 0, 0, 0);
-      if (c < nvalid) {
-        const size_t row = (((size_t)b * T + t0 + c) * H + h) * DK;
-        st.k[i] = *reinterpret_cast<const uint4*>(k + row + cu * EPU);
-        st.q[i] = *reinterpret_cast<const uint4*>(q + row + cu * EPU);
-      }
+      const bool ok = c < nvalid;
+      const size_t off = (size_t)(t0 + (ok ? c : nvalid - 1)) * tok_k + cu * EPU;
+      const uint4 kx = *reinterpret_cast<const uint4*>(k_seq + off);
+      const uint4 qx = *reinterpret_cast<const uint4*>(q_seq + off);
+      const uint32_t mk = ok ? 0xFFFFFFFFu : 0u;   // (a select on uint4 spills)
+      st.k[i] = make_uint4(kx.x & mk, kx.y & mk, kx.z & mk, kx.w & mk);
+      st.q[i] = make_uint4(qx.x & mk, qx.y & mk, qx.z & mk, qx.w & mk);
     }
+    if (!xrows) {
 #pragma unroll
-    for (int i = 0; i < St::UNITS_V; ++i) {
-      const int u = tid + NT * i;
-      const int c = u / VUPR, cu = u - c * VUPR;
-      st.v[i] = make_uint4(0, 0, 0, 0);
-      if (c < nvalid && !xrows)
-        st.v[i] = *reinterpret_cast<const uint4*>(
-            v + (((size_t)b * T + t0 + c) * H + h) * DV + r0 + cu * EPU);
+      for (int i = 0; i < St::UNITS_V; ++i) {
+        const int u = tid + NT * i;
+        const int c = u / VUPR, cu = u - c * VUPR;
+        const bool ok = c < nvalid;
+        const uint4 vx = *reinterpret_cast<const uint4*>(
+            v_seq + (size_t)(t0 + (ok ? c : nvalid - 1)) * tok_v + cu * EPU);
+        const uint32_t mv = ok ? 0xFFFFFFFFu : 0u;
+        st.v[i] = make_uint4(vx.x & mv, vx.y & mv, vx.z & mv, vx.w & mv);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < St::UNITS_V; ++i) st.v[i] = zero4;
     }
     const char* wsc = reinterpret_cast<const char*>(ws) +
                       ((size_t)bh * nchunks + chunk) * kChunkWsFloats * 4;
@@ -503,13 +510,14 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
   }
   // Outputs: o rows of the real state, or x^_t = X_t q_t of the transition
   // rows ([BH][T][DK], bf16).
+  // obase + t * ostride is token t's first element of this wave's 16 rows.
   TOut* obase;
   size_t ostride;
   if (xrows) {
-    obase = reinterpret_cast<TOut*>(seg.xhat) + (size_t)bh * T * DK + r0 + rw + n;
+    obase = reinterpret_cast<TOut*>(seg.xhat) + (size_t)bh * T * DK + r0 + rw;
     ostride = DK;
   } else {
-    obase = o + ((size_t)b * T * H + h) * DV + r0 + rw + n;
+    obase = o + ((size_t)b * T * H + h) * DV + r0 + rw;
     ostride = (size_t)H * DV;
   }
 
@@ -529,19 +537,27 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
 #pragma unroll
     for (int s = 0; s < NKB; ++s) split8(acc_slots(S[2 * s], S[2 * s + 1]), Sh[s], Sl[s]);
 
-    // ---- Y = K S^T  (c-tile ct: rows c = 16 ct + 4 g4 + i, col r = n) ----
-    floatx4 Y[4];
+    // ---- Y = K S^T and Q S^T  (c-tile ct: rows c = 16 ct + 4 g4 + i,
+    //      col r = n); both contract the state over d ----
+    floatx4 Y[4], OQ[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f}, accq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NKB; ++s) {
         const bf16x8 kh = lds_slots(Khs, LDK, 16 * ct + n, s, g4);
+        const bf16x8 qh = lds_slots(Qhs, LDK, 16 * ct + n, s, g4);
         acc = mfma(kh, Sh[s], acc);
         acc = mfma(kh, Sl[s], acc);
         if constexpr (!KEXACT) acc = mfma(lds_slots(Kls, LDK, 16 * ct + n, s, g4), Sh[s], acc);
+        accq = mfma(qh, Sh[s], accq);
+        if constexpr (OPREC) {
+          accq = mfma(qh, Sl[s], accq);
+          if constexpr (!KEXACT) accq = mfma(lds_slots(Qls, LDK, 16 * ct + n, s, g4), Sh[s], accq);
+        }
       }
       Y[ct] = acc;
+      OQ[ct] = accq;
     }
 
     // ---- Z = beta (V - gamma Y), as split B operands over c ----
@@ -591,16 +607,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
     // ---- O = diag(gamma) Q S^T + P U ----
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < NKB; ++s) {
-        const bf16x8 qh = lds_slots(Qhs, LDK, 16 * ct + n, s, g4);
-        acc = mfma(qh, Sh[s], acc);
-        if constexpr (OPREC) {
-          acc = mfma(qh, Sl[s], acc);
-          if constexpr (!KEXACT) acc = mfma(lds_slots(Qls, LDK, 16 * ct + n, s, g4), Sh[s], acc);
-        }
-      }
+      floatx4 acc = OQ[ct];
       const int c = 16 * ct + 4 * g4;
       const float4 gg = *reinterpret_cast<const float4*>(&Gs[2 * C + c]);
       acc[0] *= gg.x;
@@ -616,9 +623,33 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
           acc = mfma(lds_slots(Pls, LDT, 16 * ct + n, s, g4), Uh[s], acc);
         }
       }
+      if constexpr (OPREC) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (c + e < nvalid) store1(obase + (size_t)(t0 + c + e) * ostride, acc[e]);
+        for (int e = 0; e < 4; ++e)
+          if (c + e < nvalid) obase[(size_t)(t0 + c + e) * ostride + n] = acc[e];
+      } else {
+        bf16x4 ob;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ob[e] = (bf16)acc[e];
+        *reinterpret_cast<bf16x4*>(&Ost[(16 * w + n) * LDO + c]) = ob;   // O^T[r][c]
+      }
+    }
+    if constexpr (!OPREC) {
+      // O^T of this wave -> 16-byte stores: lane takes token
+      // c = 32 m + 16 (g4 >> 1) + n and rows 8 (g4 & 1) .. + 7.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const bf16* Ow = &Ost[16 * w * LDO];
+      const int rr = 8 * (g4 & 1);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int c0 = 32 * m + 16 * (g4 >> 1);
+        const uint2 lo = lds_tr4(Ow, LDO, rr, c0, n);
+        const uint2 hi = lds_tr4(Ow, LDO, rr + 4, c0, n);
+        if (c0 + n < nvalid)
+          *reinterpret_cast<uint4*>(obase + (size_t)(t0 + c0 + n) * ostride + rr) =
+              make_uint4(lo.x, lo.y, hi.x, hi.y);
       }
     }
 
