@@ -67,17 +67,27 @@ def decode_bytes(B, H, dk, dv, io_bytes=2):
     return B * H * (8 * dv * dk + io_bytes * (2 * dk + 2 * dv) + 8)
 
 
-def prefill_mfma_flops(B, T, H, dk, dv):
-    """MFMA flops the two prefill kernels execute (bf16 in / bf16 out):
-    16x16x32 MFMAs of 16384 flops.  prepare: 20 tiles x dk/32 k-steps per
-    chunk.  scan, per 16-row workgroup and chunk: Y 4 waves x dk/32 x 2,
-    U 6 k-blocks x 3, Q S^T 4 x dk/32 x 1, P U 6 x 1, state update
-    4 waves x dk/64 tiles x 2 k-blocks x 2."""
+def prefill_mfma_flops(B, T, H, dk, dv, nseg, seg_chunks):
+    """bf16 MFMA flops the prefill kernels execute (bf16 in / bf16 out), from
+    their structure; one v_mfma_f32_16x16x32_bf16 = 16384 flops.
+      prepare: per chunk and head, 10 lower tiles of K K^T and of Q K^T,
+               dk/32 k-steps each.
+      scan:    per chunk and 16-row wave: K S^T 4 x dk/32 x 2 (split state),
+               Q S^T 4 x dk/32, T Z 6 k-blocks x 3, P U 6, state update
+               dk/16 tiles x 2 k-blocks x 2; transition rows (dk per head)
+               run for the chunks of segments >= 1.
+      combine: per later segment and 16-row wave: dk/16 x dk/32 x 3.
+      correct: per chunk of later segments and 16-row wave: 4 x dk/32."""
     nch = -(-T // C)
-    prep = 20 * (dk // 32)
-    scan = 4 * (dk // 32) * 2 + 6 * 3 + 4 * (dk // 32) + 6 + 4 * (dk // 64) * 2 * 2
+    nkb, ndt = dk // 32, dk // 16
     f = 16 * 16 * 32 * 2
-    return (B * H * nch * prep * f, B * H * (dv // 16) * nch * scan * f)
+    prep = B * H * nch * 20 * nkb
+    per_wave_chunk = 4 * nkb * 2 + 4 * nkb + 6 * 3 + 6 + ndt * 2 * 2
+    later = nch - seg_chunks if nseg > 1 else 0
+    scan = B * H * (dv // 16 * nch + dk // 16 * later) * per_wave_chunk
+    comb = B * H * (nseg - 1) * (dv // 16) * ndt * nkb * 3
+    corr = B * H * later * (dv // 16) * 4 * nkb
+    return prep * f, (scan + comb + corr) * f
 
 
 def prefill_algorithmic_flops(B, T, H, dk, dv):
@@ -157,6 +167,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--layers", type=int, default=18)
+    ap.add_argument("--skip-prefill", action="store_true",
+                    help="omit the 16K prefill step (for per-leg profiling; "
+                         "value is then null)")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-batched", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -196,54 +209,67 @@ def main(argv=None):
     # ---------------- prefill, 16K tokens (the step) ----------------
     B, T, H, dk = x2.q.shape
     dv = x2.v.shape[-1]
-    q, k, v, al, be = up(x2)
-    del x2
-    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
-    ST = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
-    ws = torch.empty(gdn.prefill_workspace_bytes(B, T, H, dk, dv),
-                     dtype=torch.uint8, device=dev)
+    value = ms_per_step = None
+    prefill_info, roof = {}, None
+    if not a.skip_prefill:
+        q, k, v, al, be = up(x2)
+        del x2
+        o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+        ST = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+        ws = torch.empty(gdn.prefill_workspace_bytes(B, T, H, dk, dv),
+                         dtype=torch.uint8, device=dev)
 
-    def prefill_step(evs=None):
-        if evs is not None:
-            evs[0].record(stream)
-        gdn.prefill_prepare(q, k, al, be, dv, ws)
-        if evs is not None:
-            evs[1].record(stream)
-        gdn.prefill_scan(q, k, v, None, o, ST, ws)
-        if evs is not None:
-            evs[2].record(stream)
+        def prefill_step(evs=None):
+            if evs is not None:
+                evs[0].record(stream)
+            gdn.prefill_prepare(q, k, al, be, dv, ws)
+            if evs is not None:
+                evs[1].record(stream)
+            gdn.prefill_scan(q, k, v, None, o, ST, ws)
+            if evs is not None:
+                evs[2].record(stream)
 
-    for _ in range(a.warmup):
-        prefill_step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-           for _ in range(a.steps)]
-    t0 = time.perf_counter()
-    for i in range(a.steps):
-        prefill_step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    call_ms = prep_ms + scan_ms
-    ms_per_step = wall * 1e3 / a.steps
-    tokens = B * T
-    value = tokens * a.steps / wall
-    pbytes = prefill_bytes(B, T, H, dk, dv)
-    f_prep, f_scan = prefill_mfma_flops(B, T, H, dk, dv)
-    log(f"prefill 16K: {ms_per_step * 1e3:.1f} us/step wall; events: prepare "
-        f"{prep_ms * 1e3:.1f} us, scan {scan_ms * 1e3:.1f} us; "
-        f"{value / 1e6:.1f} M tokens/s")
-    prefill_info = {
-        "kernels_us": {"prepare_kernel": prep_ms * 1e3, "scan_kernel": scan_ms * 1e3},
-        "mfma": {"executed_flops": f_prep + f_scan,
-                 "achieved_tflops": (f_prep + f_scan) / (call_ms * 1e-3) / 1e12,
-                 "frac_of_bf16_peak": (f_prep + f_scan) / (call_ms * 1e-3) / MFMA_BF16_PEAK,
-                 "scan_kernel_frac": f_scan / (scan_ms * 1e-3) / MFMA_BF16_PEAK,
-                 "prepare_kernel_frac": f_prep / (prep_ms * 1e-3) / MFMA_BF16_PEAK,
-                 "algorithmic_flops": prefill_algorithmic_flops(B, T, H, dk, dv)},
-    }
-    del q, k, v, al, be, o, ws
+        for _ in range(a.warmup):
+            prefill_step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+               for _ in range(a.steps)]
+        t0 = time.perf_counter()
+        for i in range(a.steps):
+            prefill_step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        call_ms = prep_ms + scan_ms
+        ms_per_step = wall * 1e3 / a.steps
+        tokens = B * T
+        value = tokens * a.steps / wall
+        pbytes = prefill_bytes(B, T, H, dk, dv)
+        nseg, seg_chunks = gdn.prefill_segments(B, T, H, dk, dv)
+        f_prep, f_scan = prefill_mfma_flops(B, T, H, dk, dv, nseg, seg_chunks)
+        log(f"prefill 16K: {ms_per_step * 1e3:.1f} us/step wall; events: prepare "
+            f"{prep_ms * 1e3:.1f} us, scan {scan_ms * 1e3:.1f} us; "
+            f"{value / 1e6:.1f} M tokens/s")
+        prefill_info = {
+            "segments": {"per_head": nseg, "chunks_per_segment": seg_chunks},
+            "kernels_us": {"prepare_kernel": prep_ms * 1e3,
+                           "scan (scan_kernel + segment combine + correction)": scan_ms * 1e3},
+            "mfma": {"executed_flops": f_prep + f_scan,
+                     "achieved_tflops": (f_prep + f_scan) / (call_ms * 1e-3) / 1e12,
+                     "frac_of_bf16_peak": (f_prep + f_scan) / (call_ms * 1e-3) / MFMA_BF16_PEAK,
+                     "scan_frac": f_scan / (scan_ms * 1e-3) / MFMA_BF16_PEAK,
+                     "prepare_kernel_frac": f_prep / (prep_ms * 1e-3) / MFMA_BF16_PEAK,
+                     "algorithmic_flops": prefill_algorithmic_flops(B, T, H, dk, dv)},
+        }
+        roof = {"bound": "hbm", "kernel": "gdn_prefill (prepare_kernel + scan)",
+                "achieved": pbytes / (call_ms * 1e-3) / 1e9,
+                "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                "frac": pbytes / (call_ms * 1e-3) / HBM_PEAK,
+                "traffic": measured_traffic("prefill"),
+                "algorithmic_bytes": pbytes,
+                "launch_us": call_ms * 1e3}
+        del q, k, v, al, be, o, ws
 
     # ---------------- decode, B=64 (dk 128, 64) and B=1 ----------------
     decode = {}
@@ -265,7 +291,8 @@ def main(argv=None):
         decode["speedup_dk64_vs_dk128_B1"] = (decode["B1_dk128"]["us_per_step"] /
                                               decode["B1_dk64"]["us_per_step"])
 
-    traffic = measured_traffic("prefill")
+    copy_bw = copy_bandwidth(torch, dev, stream)
+    log(f"device copy (512 MiB): {copy_bw / 1e9:.0f} GB/s read+write")
     out = {
         "metric": "GDN layer tokens/s (prefill T=16K; decode B=64) + % HBM/MFMA peak",
         "value": value,
@@ -283,17 +310,12 @@ def main(argv=None):
                                "T=16384, dk=dv=128, bf16 q/k/v/o, fp32 gates/state, "
                                "narrow-cone keys, 10 short / 6 long horizon heads",
                    "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "chunk": C},
-        "roofline": {"bound": "hbm", "kernel": "gdn_prefill (prepare_kernel + scan_kernel)",
-                     "achieved": pbytes / (call_ms * 1e-3) / 1e9,
-                     "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": pbytes / (call_ms * 1e-3) / HBM_PEAK,
-                     "traffic": traffic,
-                     "algorithmic_bytes": pbytes,
-                     "launch_us": call_ms * 1e3},
+        "roofline": roof,
         "prefill": prefill_info,
         "decode": decode,
         "batched_prefill": batched,
         "cpu_baseline": cpu,
+        "copy_bandwidth_GBps": copy_bw / 1e9,
         "host": platform.node(),
     }
     if cpu is not None:
@@ -301,6 +323,25 @@ def main(argv=None):
     if rank == 0:
         print(json.dumps(out), flush=True)
     return 0
+
+
+def copy_bandwidth(torch, dev, stream, nbytes=512 << 20, reps=20):
+    """Read + write bytes per second of a plain device-to-device copy
+    (torch's copy kernel) of `nbytes`: the achievable streaming rate that
+    the HBM-bound kernels are compared with."""
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    x.fill_(1.0)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3)
 
 
 def bench_decode(torch, gdn, dev, stream, B, dk, n_steps, layers, up):

@@ -2,8 +2,21 @@
 step as hand-written HIP kernels behind the C ABI of libgdn.so.
 
     from gated_deltanet_recurrent_delta_amd import prefill, decode_step
+
+The binding (and with it libgdn.so) is loaded on first use of one of these
+names, so `python -m gated_deltanet_recurrent_delta_amd.build` works before
+the library exists.
 """
 
-from .binding import (GdnError, decode_step, prefill, prefill_prepare,  # noqa: F401
-                      prefill_scan, prefill_workspace_bytes, status_str,
-                      version)
+_EXPORTS = ("GdnError", "decode_step", "prefill", "prefill_prepare",
+            "prefill_scan", "prefill_segments", "prefill_workspace_bytes",
+            "status_str", "version")
+
+__all__ = list(_EXPORTS)
+
+
+def __getattr__(name):
+    if name in _EXPORTS:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

@@ -31,6 +31,7 @@ SIGNATURES = {
     "gdn_status_str": (ctypes.c_char_p, [_i]),
     "gdn_version": (ctypes.c_char_p, []),
     "gdn_prefill_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "gdn_prefill_segments": (_i, [_i, _i, _i, _i, _i, _i, _i, _vp]),
     "gdn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                          _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "gdn_prefill_prepare": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
@@ -106,6 +107,17 @@ def _dev_tensor(t: torch.Tensor, name: str, dtypes, shape=None):
 
 def prefill_workspace_bytes(B: int, T: int, H: int, dk: int, dv: int) -> int:
     return int(lib.gdn_prefill_workspace_bytes(B, T, H, dk, dv))
+
+
+def prefill_segments(B: int, T: int, H: int, dk: int, dv: int,
+                     in_dtype=torch.bfloat16, out_dtype=torch.bfloat16):
+    """(segments per head, chunks per segment) gdn_prefill will use."""
+    sc = ctypes.c_int(0)
+    n = lib.gdn_prefill_segments(B, T, H, dk, dv, _DTYPE_CODE[in_dtype],
+                                 _DTYPE_CODE[out_dtype], ctypes.byref(sc))
+    if n == 0:
+        raise ValueError("invalid prefill sizes or dtypes")
+    return n, sc.value
 
 
 def _prefill_args(q, k, v, alpha, beta, S0):

@@ -55,6 +55,19 @@ size_t gdn_prefill_workspace_bytes(int B, int T, int H, int dk, int dv) {
   return prefill_ws_bytes(B, T, H, dk, dv);
 }
 
+int gdn_prefill_segments(int B, int T, int H, int dk, int dv, int in_dtype,
+                         int out_dtype, int* seg_chunks) {
+  if (check_prefill_shape(B, T, H, dk, dv, in_dtype, out_dtype) != GDN_OK) return 0;
+  if (T == 0) {
+    if (seg_chunks) *seg_chunks = 0;
+    return 1;
+  }
+  const gdn::PrefillPlan p = gdn::plan_prefill(B, T, H, dk, dv);
+  const bool seg = p.nseg > 1 && in_dtype == GDN_BF16 && out_dtype == GDN_BF16;
+  if (seg_chunks) *seg_chunks = seg ? p.seg_chunks : p.nchunks;
+  return seg ? p.nseg : 1;
+}
+
 int gdn_prefill_prepare(const void* q, const void* k, const float* alpha,
                         const float* beta, int B, int T, int H, int dk, int dv,
                         int in_dtype, void* workspace, size_t workspace_bytes,

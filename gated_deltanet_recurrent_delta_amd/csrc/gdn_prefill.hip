@@ -318,14 +318,16 @@ __global__ __launch_bounds__(64) void prepare_kernel(
 // scan
 // ===========================================================================
 
-// Per-thread register staging of one chunk for NT threads.
-template <int DK, typename TIn, int NT, int ROWS>
+// Per-thread register staging of one chunk for NT threads.  NTP of the four
+// bf16 64x64 tiles (T hi, T lo, P hi, P lo) are staged: P lo only feeds
+// fp32 outputs.
+template <int DK, typename TIn, int NT, int ROWS, int NTP>
 struct Stage {
   static constexpr int UNITS_K = C * DK * (int)sizeof(TIn) / 16 / NT;    // 16B units
-  static constexpr int UNITS_TP = 4 * C * C * 2 / 16 / NT;               // T, P hi/lo
+  static constexpr int UNITS_TP = NTP * C * C * 2 / 16 / NT;             // T, P tiles
   static constexpr int UNITS_V = C * ROWS * (int)sizeof(TIn) / 16 / NT;  // V rows of the WG
   static_assert(UNITS_K * NT * 16 == C * DK * (int)sizeof(TIn), "K staging");
-  static_assert(UNITS_TP * NT * 16 == 4 * C * C * 2, "T/P staging");
+  static_assert(UNITS_TP * NT * 16 == NTP * C * C * 2, "T/P staging");
   static_assert(UNITS_V * NT * 16 == C * ROWS * (int)sizeof(TIn), "V staging");
   uint4 k[UNITS_K];
   uint4 q[UNITS_K];
@@ -334,8 +336,12 @@ struct Stage {
   float g;
 };
 
-template <int DK, typename TIn, typename TOut, int NW>
-__global__ __launch_bounds__(64 * NW) void scan_kernel(
+// MINW: waves per SIMD the kernel is compiled for.  MINW = 2 lets two
+// workgroups share a CU so that one hides the other's LDS and memory
+// latency, at the price of a tighter register budget; it is used when the
+// grid has more workgroups than the GPU has CUs.
+template <int DK, typename TIn, typename TOut, int NW, int MINW>
+__global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const float* S0, TOut* __restrict__ o,
     float* ST, const float* __restrict__ ws, int T, int H, int DV,
@@ -346,29 +352,33 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
   constexpr int ROWS = 16 * NW;         // state rows of the workgroup
   constexpr int LDK = DK + 8;           // bf16 stride of the K / Q tiles
   constexpr int LDT = C + 8;            // bf16 stride of the T / P tiles
-  constexpr int LDV = ROWS + 8;         // bf16 stride of the V tile [c][r]
+  constexpr int LDV = 16 + 8;           // bf16 stride of a wave's V block [c][16 r]
+  constexpr int VBLK = C * LDV;         // elements per wave block
   constexpr int NDT = DK / 16;          // d-tiles of a 16-row state slice
   constexpr int NKB = DK / 32;          // 32-wide k-blocks over d
   constexpr int EPU = 16 / (int)sizeof(TIn);    // input elements per 16B unit
   constexpr int UPR = DK / EPU;                 // 16B units per K/Q row
   constexpr int VUPR = ROWS / EPU;              // 16B units per V row
-  using St = Stage<DK, TIn, NT, ROWS>;
+  constexpr int NTP = OPREC ? 4 : 3;    // staged T/P tiles
+  using St = Stage<DK, TIn, NT, ROWS, NTP>;
 
   __shared__ __attribute__((aligned(16))) bf16 Khs[C * LDK];
   __shared__ __attribute__((aligned(16))) bf16 Kls[KEXACT ? 8 : C * LDK];
   __shared__ __attribute__((aligned(16))) bf16 Qhs[C * LDK];
   __shared__ __attribute__((aligned(16))) bf16 Qls[KEXACT ? 8 : C * LDK];
-  __shared__ __attribute__((aligned(16))) bf16 TPs[4][C * LDT];   // Th, Tl, Ph, Pl
-  __shared__ __attribute__((aligned(16))) bf16 Vhs[C * LDV];
-  __shared__ __attribute__((aligned(16))) bf16 Vls[KEXACT ? 8 : C * LDV];
+  __shared__ __attribute__((aligned(16))) bf16 TPs[NTP][C * LDT];   // Th, Tl, Ph[, Pl]
+  // V tile blocked by wave (block w = rows 16 w .. 16 w + 15 of the group);
+  // once a wave has formed Z, its block is reused to stage its O^T tile.
+  __shared__ __attribute__((aligned(16))) bf16 Vhs[NW * VBLK];
+  __shared__ __attribute__((aligned(16))) bf16 Vls[KEXACT ? 8 : NW * VBLK];
   __shared__ __attribute__((aligned(16))) float Gs[4 * C];
   // per-wave O^T staging [16 r][C c] for 16-byte output stores (bf16 o)
   constexpr int LDO = C + 8;
-  __shared__ __attribute__((aligned(16))) bf16 Ost[OPREC ? 8 : NW * 16 * LDO];
+  static_assert(16 * LDO <= VBLK, "O^T staging fits in a wave's V block");
   const bf16* Ths = TPs[0];
   const bf16* Tls = TPs[1];
   const bf16* Phs = TPs[2];
-  const bf16* Pls = TPs[3];
+  const bf16* Pls = TPs[NTP - 1];       // (read only for fp32 outputs)
 
   // workgroup -> (head, segment, row group); the row groups of a head are
   // placed on one XCD (workgroups are dealt to the 8 XCDs round-robin) so
@@ -467,7 +477,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
 #pragma unroll
     for (int i = 0; i < St::UNITS_TP; ++i) {
       const int u = tid + NT * i;             // 16B unit of [4][64][64] bf16
-      const int m = u >> 9, rem = u & 511;    // 512 units per 64x64 matrix
+      const int m = u >> 9, rem = u & 511;    // 512 units per 64x64 matrix (m < NTP)
       const int j = rem >> 3, i0 = (rem & 7) * 8;
       *reinterpret_cast<uint4*>(&TPs[m][j * LDT + i0]) = st.tp[i];
     }
@@ -475,15 +485,16 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
     for (int i = 0; i < St::UNITS_V; ++i) {
       const int u = tid + NT * i;
       const int c = u / VUPR, rr = (u - c * VUPR) * EPU;
+      const int vb = (rr >> 4) * VBLK + c * LDV + (rr & 15);   // wave block, row c
       if constexpr (KEXACT) {
-        *reinterpret_cast<uint4*>(&Vhs[c * LDV + rr]) = st.v[i];
+        *reinterpret_cast<uint4*>(&Vhs[vb]) = st.v[i];
       } else {
         const float4 vf = __builtin_bit_cast(float4, st.v[i]);
         const float vx[4] = {vf.x, vf.y, vf.z, vf.w};
         bf16x4 vh, vl;
         split4(vx, vh, vl);
-        *reinterpret_cast<bf16x4*>(&Vhs[c * LDV + rr]) = vh;
-        *reinterpret_cast<bf16x4*>(&Vls[c * LDV + rr]) = vl;
+        *reinterpret_cast<bf16x4*>(&Vhs[vb]) = vh;
+        *reinterpret_cast<bf16x4*>(&Vls[vb]) = vl;
       }
     }
     if (tid < 4 * C) Gs[tid] = st.g;
@@ -567,10 +578,10 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         const int c = 16 * ct + 4 * g4;
-        const uint2 vw = lds_tr4(Vhs, LDV, c, rw, n);    // V[c + j][rw + n]
+        const uint2 vw = lds_tr4(Vhs + w * VBLK, LDV, c, 0, n);    // V[c + j][rw + n]
         float vv[4] = {bf16lo(vw.x), bf16hi(vw.x), bf16lo(vw.y), bf16hi(vw.y)};
         if constexpr (!KEXACT) {
-          const uint2 vl = lds_tr4(Vls, LDV, c, rw, n);
+          const uint2 vl = lds_tr4(Vls + w * VBLK, LDV, c, 0, n);
           vv[0] += bf16lo(vl.x);
           vv[1] += bf16hi(vl.x);
           vv[2] += bf16lo(vl.y);
@@ -631,7 +642,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
         bf16x4 ob;
 #pragma unroll
         for (int e = 0; e < 4; ++e) ob[e] = (bf16)acc[e];
-        *reinterpret_cast<bf16x4*>(&Ost[(16 * w + n) * LDO + c]) = ob;   // O^T[r][c]
+        *reinterpret_cast<bf16x4*>(&Vhs[w * VBLK + n * LDO + c]) = ob;   // O^T[r][c]
       }
     }
     if constexpr (!OPREC) {
@@ -640,7 +651,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const bf16* Ow = &Ost[16 * w * LDO];
+      const bf16* Ow = &Vhs[w * VBLK];
       const int rr = 8 * (g4 & 1);
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
@@ -757,11 +768,13 @@ hipError_t launch_prefill_prepare(const void* q, const void* k,
 // One workgroup per (head, 64 state rows), sequential over the segments.
 // Each wave carries 16 rows as S^T tiles; X_s is staged in LDS as bf16 hi/lo
 // and read transposed, the product uses split-bf16 operands on both sides.
+// X_{s+1} and S_loc(s+1) are loaded into registers while step s computes.
 template <int DK>
 __global__ __launch_bounds__(256) void segment_combine_kernel(SegArgs seg,
                                                               float* ST, int DV) {
   constexpr int LDX = DK + 8;
   constexpr int NDT = DK / 16, NKB = DK / 32;
+  constexpr int XU = DK * DK / 4 / 256;         // float4 of X per thread
   __shared__ __attribute__((aligned(16))) bf16 Xh[DK * LDX];
   __shared__ __attribute__((aligned(16))) bf16 Xl[DK * LDX];
   const int NRG = DV / 64;
@@ -772,50 +785,65 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(SegArgs seg,
   auto srow = [&](float* base, int s) {
     return base + (((size_t)bh * seg.nseg + s) * DV + row) * DK;
   };
-
-  floatx4 S[NDT];
+  auto load_x = [&](float4* xr, int s) {
+    const float* X = seg.X_fin + ((size_t)bh * seg.nseg + s) * DK * DK;
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    const float4 x = *reinterpret_cast<const float4*>(srow(seg.S_fin, 0) + 16 * dt + 4 * g4);
-    S[dt] = floatx4{x.x, x.y, x.z, x.w};
+    for (int i = 0; i < XU; ++i) xr[i] = *reinterpret_cast<const float4*>(X + 4 * (tid + 256 * i));
+  };
+  auto load_loc = [&](floatx4* Lr, int s) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const float4 x = *reinterpret_cast<const float4*>(srow(seg.S_fin, s) + 16 * dt + 4 * g4);
+      Lr[dt] = floatx4{x.x, x.y, x.z, x.w};
+    }
+  };
+
+  floatx4 S[NDT], L[NDT];
+  float4 xr[XU];
+  load_loc(S, 0);
+  if (seg.nseg > 1) {
+    load_x(xr, 1);
+    load_loc(L, 1);
   }
   for (int s = 1; s < seg.nseg; ++s) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
       *reinterpret_cast<float4*>(srow(seg.S_in, s) + 16 * dt + 4 * g4) =
           make_float4(S[dt][0], S[dt][1], S[dt][2], S[dt][3]);
-    __syncthreads();                       // previous X_s no longer read
-    const float* X = seg.X_fin + ((size_t)bh * seg.nseg + s) * DK * DK;
-    for (int u = tid; u < DK * DK / 4; u += 256) {
-      const int e = (4 * u) / DK, d0 = (4 * u) % DK;
-      const float4 x = *reinterpret_cast<const float4*>(X + (size_t)e * DK + d0);
-      const float xv[4] = {x.x, x.y, x.z, x.w};
+    __syncthreads();                       // previous X no longer read
+#pragma unroll
+    for (int i = 0; i < XU; ++i) {
+      const int e = (4 * (tid + 256 * i)) / DK, d0 = (4 * (tid + 256 * i)) % DK;
+      const float xv[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
       bf16x4 hi, lo;
       split4(xv, hi, lo);
       *reinterpret_cast<bf16x4*>(&Xh[e * LDX + d0]) = hi;
       *reinterpret_cast<bf16x4*>(&Xl[e * LDX + d0]) = lo;
     }
+    floatx4 acc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = L[dt];
     __syncthreads();
+    if (s + 1 < seg.nseg) {                // prefetch the next step
+      load_x(xr, s + 1);
+      load_loc(L, s + 1);
+    }
     bf16x8 Sh[NKB], Sl[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) split8(acc_slots(S[2 * kb], S[2 * kb + 1]), Sh[kb], Sl[kb]);
-    floatx4 Sn[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const float4 x = *reinterpret_cast<const float4*>(srow(seg.S_fin, s) + 16 * dt + 4 * g4);
-      floatx4 acc = {x.x, x.y, x.z, x.w};
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const bf16x8 ah = lds_slots_tr(Xh, LDX, 16 * dt, kb, g4, n);   // X[e][16 dt + n]
         const bf16x8 al = lds_slots_tr(Xl, LDX, 16 * dt, kb, g4, n);
-        acc = mfma(ah, Sh[kb], acc);
-        acc = mfma(ah, Sl[kb], acc);
-        acc = mfma(al, Sh[kb], acc);
+        acc[dt] = mfma(ah, Sh[kb], acc[dt]);
+        acc[dt] = mfma(ah, Sl[kb], acc[dt]);
+        acc[dt] = mfma(al, Sh[kb], acc[dt]);
       }
-      Sn[dt] = acc;
     }
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) S[dt] = Sn[dt];
+    for (int dt = 0; dt < NDT; ++dt) S[dt] = acc[dt];
   }
   if (ST != nullptr) {
 #pragma unroll
@@ -830,7 +858,9 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(SegArgs seg,
 // ===========================================================================
 
 // One workgroup per (chunk of a segment >= 1, head, 64 state rows); wave w
-// handles 16 rows for the 64 tokens.  Single-pass bf16 (outputs are bf16).
+// handles 16 rows for the 64 tokens.  The product is formed transposed,
+// O_corr^T = S_in x^^T, so a lane holds 4 consecutive rows of one token and
+// updates o with 8-byte accesses.  Single-pass bf16 (outputs are bf16).
 template <int DK>
 __global__ __launch_bounds__(256) void segment_correct_kernel(SegArgs seg, bf16* o,
                                                               int T, int H, int DV) {
@@ -842,37 +872,37 @@ __global__ __launch_bounds__(256) void segment_correct_kernel(SegArgs seg, bf16*
   const int nvalid = min(C, T - t0);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = lane & 15, g4 = lane >> 4;
-  const int row = blockIdx.z * 64 + 16 * w + n;
-  // B operand: S_in[row][32 kb + 8 g4 .. + 7]
-  bf16x8 Bs[NKB];
-  const float* sin_row = seg.S_in + (((size_t)bh * seg.nseg + s) * DV + row) * DK;
+  const int r0 = blockIdx.z * 64 + 16 * w;       // first row of this wave
+  // A operand: S_in[r0 + n][32 kb + 8 g4 .. + 7]
+  bf16x8 As[NKB];
+  const float* sin_row = seg.S_in + (((size_t)bh * seg.nseg + s) * DV + r0 + n) * DK;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     const float4 a = *reinterpret_cast<const float4*>(sin_row + 32 * kb + 8 * g4);
     const float4 c = *reinterpret_cast<const float4*>(sin_row + 32 * kb + 8 * g4 + 4);
-    Bs[kb] = to_bf16x8(floatx8{a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w});
+    As[kb] = to_bf16x8(floatx8{a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w});
   }
   const bf16* xh = reinterpret_cast<const bf16*>(seg.xhat) + (size_t)bh * T * DK;
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
-    const int ta = 16 * tt + n;                 // A-operand token of this lane
+    const int tl = 16 * tt + n;                  // token of this lane
+    const bool ok = tl < nvalid;
+    const int tc = ok ? tl : nvalid - 1;         // clamped (in bounds)
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      bf16x8 a = {};
-      if (ta < nvalid)
-        a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
-                                           xh + (size_t)(t0 + ta) * DK + 32 * kb + 8 * g4));
-      acc = mfma(a, Bs[kb], acc);
+      const bf16x8 bx = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                                       xh + (size_t)(t0 + tc) * DK + 32 * kb + 8 * g4));
+      acc = mfma(As[kb], bx, acc);
     }
+    // acc[i] = O_corr[token tl][row r0 + 4 g4 + i]
+    bf16* p = o + (((size_t)b * T + t0 + tc) * H + h) * DV + r0 + 4 * g4;
+    const uint2 old = *reinterpret_cast<const uint2*>(p);
+    const bf16x4 ov = __builtin_bit_cast(bf16x4, old);
+    bf16x4 nv;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tc = 16 * tt + 4 * g4 + i;
-      if (tc < nvalid) {
-        bf16* p = o + (((size_t)b * T + t0 + tc) * H + h) * DV + row;
-        *p = (bf16)((float)*p + acc[i]);
-      }
-    }
+    for (int i = 0; i < 4; ++i) nv[i] = (bf16)((float)ov[i] + acc[i]);
+    if (ok) *reinterpret_cast<uint2*>(p) = __builtin_bit_cast(uint2, nv);
   }
 }
 
@@ -883,6 +913,10 @@ __global__ __launch_bounds__(256) void segment_correct_kernel(SegArgs seg, bf16*
 // Waves per scan workgroup (16 state rows each).
 constexpr int kScanWaves = 4;
 
+// CUs of the target GPU (MI355X); grids larger than this use the
+// two-workgroups-per-CU build of the bf16 scan.
+constexpr int kNumCUs = 256;
+
 template <int DK, typename TIn, typename TOut>
 static void launch_scan_t(const void* q, const void* k, const void* v,
                           const float* S0, void* o, float* ST, const float* ws,
@@ -892,11 +926,20 @@ static void launch_scan_t(const void* q, const void* k, const void* v,
   constexpr int ROWS = 16 * kScanWaves;
   const int per_head = dv / ROWS + (seg.nseg - 1) * ((dv + DK) / ROWS);
   const int nblocks = B * H * per_head;
-  hipLaunchKernelGGL((scan_kernel<DK, TIn, TOut, kScanWaves>), dim3(nblocks),
-                     dim3(64 * kScanWaves), 0, stream,
-                     static_cast<const TIn*>(q), static_cast<const TIn*>(k),
-                     static_cast<const TIn*>(v), S0, static_cast<TOut*>(o), ST,
-                     ws, T, H, dv, nchunks, nblocks, seg);
+  constexpr bool BF16IO = std::is_same<TIn, bf16>::value && std::is_same<TOut, bf16>::value;
+  if (BF16IO && nblocks > kNumCUs) {
+    hipLaunchKernelGGL((scan_kernel<DK, TIn, TOut, kScanWaves, 2>), dim3(nblocks),
+                       dim3(64 * kScanWaves), 0, stream,
+                       static_cast<const TIn*>(q), static_cast<const TIn*>(k),
+                       static_cast<const TIn*>(v), S0, static_cast<TOut*>(o), ST,
+                       ws, T, H, dv, nchunks, nblocks, seg);
+  } else {
+    hipLaunchKernelGGL((scan_kernel<DK, TIn, TOut, kScanWaves, 1>), dim3(nblocks),
+                       dim3(64 * kScanWaves), 0, stream,
+                       static_cast<const TIn*>(q), static_cast<const TIn*>(k),
+                       static_cast<const TIn*>(v), S0, static_cast<TOut*>(o), ST,
+                       ws, T, H, dv, nchunks, nblocks, seg);
+  }
 }
 
 template <int DK>

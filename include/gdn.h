@@ -85,6 +85,16 @@ const char* gdn_version(void);
 size_t gdn_prefill_workspace_bytes(int B, int T, int H, int dk, int dv);
 
 /*
+ * How gdn_prefill will split the work for these sizes and dtypes: returns
+ * the number of sequence segments per head (1 = no segmentation, every head
+ * scanned start to end by one set of workgroups) and, if seg_chunks is not
+ * NULL, the number of 64-token chunks per segment.  Returns 0 for invalid
+ * arguments.  Pure host computation; no HIP call.
+ */
+int gdn_prefill_segments(int B, int T, int H, int dk, int dv, int in_dtype,
+                         int out_dtype, int* seg_chunks);
+
+/*
  * Runs the recurrence over T tokens for B*H independent heads.
  *   q, k, v      inputs, in_dtype, layouts above.
  *   alpha, beta  [B, T, H] float32.

@@ -58,6 +58,18 @@ def test_workspace_bytes():
     assert ws(1, 64, 1, 96, 128) == 0
 
 
+def test_prefill_segments_plan():
+    seg = bd.prefill_segments
+    assert seg(8, 4096, 16, 128, 128) == (1, 64)          # enough heads
+    n, sc = seg(1, 16384, 16, 128, 128)                   # few heads, long
+    assert n > 1 and sc >= 8 and n * sc >= 256 and (n - 1) * sc < 256
+    import torch
+    assert seg(1, 16384, 16, 128, 128, torch.float32, torch.float32) == (1, 256)
+    assert seg(1, 100, 1, 128, 128) == (1, 2)             # too short
+    with pytest.raises(ValueError):
+        seg(1, 100, 1, 96, 128)
+
+
 def prefill(**kw):
     a = dict(q=P, k=P, v=P, alpha=P, beta=P, S0=NULL, o=P, ST=P, B=1, T=100,
              H=2, dk=128, dv=128, in_dtype=1, out_dtype=1, ws=P,
