@@ -166,6 +166,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=512)
+    ap.add_argument("--decode-batch", type=int, nargs="+", default=[64, 1],
+                    help="decode batch sizes to measure (each at d_k 128 and 64)")
     ap.add_argument("--layers", type=int, default=18)
     ap.add_argument("--skip-prefill", action="store_true",
                     help="omit the 16K prefill step (for per-leg profiling; "
@@ -274,7 +276,7 @@ def main(argv=None):
     # ---------------- decode, B=64 (dk 128, 64) and B=1 ----------------
     decode = {}
     if not a.skip_decode:
-        for Bd, dkd in [(64, 128), (64, 64), (1, 128), (1, 64)]:
+        for Bd, dkd in [(bb, dd) for bb in a.decode_batch for dd in (128, 64)]:
             decode[f"B{Bd}_dk{dkd}"] = bench_decode(
                 torch, gdn, dev, stream, Bd, dkd, a.decode_steps, a.layers, up)
     # ---------------- batched prefill, dk 128 vs 64 ----------------
@@ -285,11 +287,10 @@ def main(argv=None):
                                                 max(3, a.steps // 2), a.warmup, up)
         batched["speedup_dk64_vs_dk128"] = (batched["dk128"]["us_per_call"] /
                                             batched["dk64"]["us_per_call"])
-    if "B64_dk128" in decode and "B64_dk64" in decode:
-        decode["speedup_dk64_vs_dk128_B64"] = (decode["B64_dk128"]["us_per_step"] /
-                                               decode["B64_dk64"]["us_per_step"])
-        decode["speedup_dk64_vs_dk128_B1"] = (decode["B1_dk128"]["us_per_step"] /
-                                              decode["B1_dk64"]["us_per_step"])
+    for bb in a.decode_batch:
+        if f"B{bb}_dk128" in decode and f"B{bb}_dk64" in decode:
+            decode[f"speedup_dk64_vs_dk128_B{bb}"] = (decode[f"B{bb}_dk128"]["us_per_step"] /
+                                                     decode[f"B{bb}_dk64"]["us_per_step"])
 
     copy_bw = copy_bandwidth(torch, dev, stream)
     log(f"device copy (512 MiB): {copy_bw / 1e9:.0f} GB/s read+write")
