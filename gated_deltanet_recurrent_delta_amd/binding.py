@@ -40,6 +40,8 @@ SIGNATURES = {
                               _i, _i, _i, _vp, _sz, _vp]),
     "gdn_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                              _i, _i, _i, _i, _i, _i, _vp]),
+    "gdn_truncate_workspace_bytes": (_sz, [_i, _i, _i]),
+    "gdn_truncate_rank": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
 }
 
 
@@ -243,3 +245,75 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                              _DTYPE_CODE[out_dtype], _stream_handle(q, stream))
     _check(st, "gdn_decode_step")
     return o, S_out
+
+
+# ---------------------------------------------------------------------------
+# rank-r truncation
+# ---------------------------------------------------------------------------
+
+def truncate_workspace_bytes(BH: int, dv: int, dk: int) -> int:
+    return int(lib.gdn_truncate_workspace_bytes(BH, dv, dk))
+
+
+def truncate_rank(S: torch.Tensor, r: int, *, stable_rank: bool = True,
+                  workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> Optional[torch.Tensor]:
+    """Project every state in S [..., dv, dk] (float32, updated in place)
+    onto its top-r left singular directions; r >= min(dv, dk) leaves S
+    unchanged.  Returns the stable rank of each result (float32, shape
+    S.shape[:-2]; NaN for a zero state) if `stable_rank`, else None."""
+    _dev_tensor(S, "S", (torch.float32,))
+    if S.dim() < 2:
+        raise ValueError("S must be [..., dv, dk]")
+    dv, dk = S.shape[-2:]
+    BH = S.numel() // (dv * dk) if S.numel() else 0
+    er = (torch.empty(S.shape[:-2], dtype=torch.float32, device=S.device)
+          if stable_rank else None)
+    if BH == 0:
+        return er
+    need = truncate_workspace_bytes(BH, dv, dk) if r < min(dv, dk) else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=S.device)
+    st = lib.gdn_truncate_rank(_ptr(S), BH, dv, dk, int(r), _ptr(er),
+                               _ptr(workspace),
+                               0 if workspace is None else workspace.numel(),
+                               _stream_handle(S, stream))
+    _check(st, "gdn_truncate_rank")
+    return er
+
+
+def prefill_truncated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                      alpha: torch.Tensor, beta: torch.Tensor, r: int,
+                      S0: Optional[torch.Tensor] = None, *,
+                      segment: int = 256,
+                      out_dtype: Optional[torch.dtype] = None,
+                      stream=None):
+    """Segment-truncated prefill: the recurrence runs over `segment`-token
+    pieces, and between pieces every carried state is replaced by its
+    rank-r truncation (never after the last token).  Returns (o, S_T,
+    stable rank of S_T).  Each piece is one gdn_prefill call on a
+    contiguous slice (one call per batch row when B > 1), each boundary one
+    gdn_truncate_rank call; all of it is enqueued on one stream."""
+    B, T, H, dk, dv = _prefill_args(q, k, v, alpha, beta, S0)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    o = torch.empty((B, T, H, dv), dtype=out_dtype, device=q.device)
+    S = (torch.zeros((B, H, dv, dk), dtype=torch.float32, device=q.device)
+         if S0 is None else S0.clone())
+    lengths = {min(segment, T - t0) for t0 in range(0, T, segment)}
+    seg_ws = torch.empty(max([16] + [prefill_workspace_bytes(1, n, H, dk, dv)
+                                     for n in lengths]),
+                         dtype=torch.uint8, device=q.device)
+    tr_ws = torch.empty(max(truncate_workspace_bytes(B * H, dv, dk), 16),
+                        dtype=torch.uint8, device=q.device)
+    for t0 in range(0, T, segment):
+        t1 = min(T, t0 + segment)
+        for b in range(B):
+            sl = (slice(b, b + 1), slice(t0, t1))
+            prefill(q[sl], k[sl], v[sl], alpha[sl], beta[sl], S[b:b + 1],
+                    out_dtype=out_dtype, o=o[sl], ST=S[b:b + 1],
+                    workspace=seg_ws, stream=stream)
+        if t1 < T:
+            truncate_rank(S, r, stable_rank=False, workspace=tr_ws,
+                          stream=stream)
+    er = truncate_rank(S, min(dv, dk), stable_rank=True, stream=stream)
+    return o, S, er

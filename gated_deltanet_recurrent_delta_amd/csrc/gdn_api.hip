@@ -158,4 +158,26 @@ int gdn_decode_step(const void* q, const void* k, const void* v,
                                       static_cast<hipStream_t>(stream)));
 }
 
+size_t gdn_truncate_workspace_bytes(int BH, int dv, int dk) {
+  if (BH <= 0 || !dims_ok(dk, dv)) return 0;
+  return (size_t)BH * (dv < dk ? dv : dk) * dv * sizeof(float);
+}
+
+int gdn_truncate_rank(float* S, int BH, int dv, int dk, int r, float* er_out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (BH <= 0 || BH > 65535 || r < 1) return GDN_EINVAL;
+  if (!dims_ok(dk, dv)) return GDN_ESHAPE;
+  if (!S || !aligned(S, 16)) return GDN_EINVAL;
+  if (er_out && !aligned(er_out, 4)) return GDN_EINVAL;
+  const bool project = r < (dv < dk ? dv : dk);
+  if (project) {
+    if (!workspace || !aligned(workspace, 16)) return GDN_EWORKSPACE;
+    if (workspace_bytes < gdn_truncate_workspace_bytes(BH, dv, dk))
+      return GDN_EWORKSPACE;
+  }
+  return to_status(gdn::launch_truncate(
+      S, BH, dv, dk, r, er_out, static_cast<float*>(workspace),
+      static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

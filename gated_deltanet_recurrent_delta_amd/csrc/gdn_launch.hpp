@@ -96,6 +96,12 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v,
                                int B, int T, int H, int dk, int dv,
                                int in_dtype, int out_dtype, hipStream_t stream);
 
+// Rank-r truncation S <- U_r U_r^T S of BH states [dv, dk] in place, and
+// er[BH] (may be NULL) = stable rank of the result; U is a workspace of
+// BH * min(dv, dk) * dv floats (unused when r >= min(dv, dk)).
+hipError_t launch_truncate(float* S, int BH, int dv, int dk, int r, float* er,
+                           float* U, hipStream_t stream);
+
 hipError_t launch_state_fill(const float* S0, float* ST, size_t n,
                              hipStream_t stream);
 

@@ -156,6 +156,40 @@ int gdn_decode_step(const void* q, const void* k, const void* v,
                     int B, int H, int dk, int dv,
                     int in_dtype, int out_dtype, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Rank-r truncation of carried states.
+ *
+ * Replaces each state S (dv x dk) by U_r U_r^T S, where U_r holds the r
+ * leading left singular vectors of S, i.e. projects the state onto its top-r
+ * left singular directions.  "How much of its state does Gated DeltaNet
+ * use?", Sec. 3, applies this to every head's carried state at each
+ * 256-token segment boundary (r equal to the state width is the unchanged
+ * model).  The stable rank er(S) = ||S||_F^2 / sigma_1(S)^2 is "On State
+ * Reduction in Linear Attention", Sec. 2.2, Eq. (5).
+ *
+ * Bytes of workspace gdn_truncate_rank needs when r < min(dv, dk):
+ * BH * min(dv, dk) * dv * 4 (the unit singular vectors, fp32).  0 for
+ * invalid sizes.
+ */
+size_t gdn_truncate_workspace_bytes(int BH, int dv, int dk);
+
+/*
+ *   S          [BH, dv, dk] float32 states, updated in place.
+ *   BH         number of states (1 .. 65535).
+ *   r          rank kept, >= 1.  r >= min(dv, dk) leaves S unchanged.
+ *   er_out     [BH] float32: the stable rank of each RESULT (NaN for a zero
+ *              state), or NULL to skip it.
+ *   workspace  device scratch of at least gdn_truncate_workspace_bytes();
+ *              may be NULL when r >= min(dv, dk).
+ * The singular vectors come from a Householder QR of S^T followed by a
+ * one-sided Jacobi SVD of R^T, both in fp64; the projection is fp32.  When
+ * sigma_r == sigma_{r+1} the leading r-dimensional subspace is not unique
+ * and the result is one valid choice.  Errors as for the other entry points
+ * (GDN_EINVAL for r < 1, a null S, BH out of range or misalignment).
+ */
+int gdn_truncate_rank(float* S, int BH, int dv, int dk, int r, float* er_out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

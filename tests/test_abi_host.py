@@ -157,3 +157,45 @@ def test_python_wrappers_reject_host_tensors():
     x = torch.zeros(1, 4, 2, 64)
     with pytest.raises(ValueError):
         bd.prefill(x, x, x, torch.ones(1, 4, 2), torch.ones(1, 4, 2))
+
+
+def test_truncate_workspace_bytes():
+    ws = bd.truncate_workspace_bytes
+    assert ws(16, 128, 128) == 16 * 128 * 128 * 4
+    assert ws(16, 128, 64) == 16 * 64 * 128 * 4
+    assert ws(16, 64, 128) == 16 * 64 * 64 * 4
+    assert ws(0, 128, 128) == 0
+    assert ws(4, 96, 128) == 0
+
+
+def truncate(**kw):
+    a = dict(S=P, BH=16, dv=128, dk=128, r=4, er=P, ws=P, ws_bytes=10 ** 9,
+             stream=NULL)
+    a.update(kw)
+    return bd.lib.gdn_truncate_rank(a["S"], a["BH"], a["dv"], a["dk"],
+                                    a["r"], a["er"], a["ws"], a["ws_bytes"],
+                                    a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(BH=0), bd.GDN_EINVAL),
+    (dict(BH=70000), bd.GDN_EINVAL),
+    (dict(r=0), bd.GDN_EINVAL),
+    (dict(r=-3), bd.GDN_EINVAL),
+    (dict(S=NULL), bd.GDN_EINVAL),
+    (dict(S=MIS), bd.GDN_EINVAL),
+    (dict(dk=32), bd.GDN_ESHAPE),
+    (dict(dv=256), bd.GDN_ESHAPE),
+    (dict(ws=NULL), bd.GDN_EWORKSPACE),
+    (dict(ws_bytes=16 * 128 * 128 * 4 - 1), bd.GDN_EWORKSPACE),
+    (dict(dk=64, ws_bytes=16 * 64 * 128 * 4 - 4), bd.GDN_EWORKSPACE),
+])
+def test_truncate_argument_errors(kw, status):
+    assert truncate(**kw) == status
+
+
+def test_truncate_full_rank_needs_no_workspace_or_launch():
+    # r >= min(dv, dk) with no stable rank requested: nothing to do, and no
+    # workspace is needed (the fake S is never touched)
+    assert truncate(r=128, er=NULL, ws=NULL, ws_bytes=0) == bd.GDN_OK
+    assert truncate(dk=64, r=64, er=NULL, ws=NULL, ws_bytes=0) == bd.GDN_OK
