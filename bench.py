@@ -174,6 +174,11 @@ def main(argv=None):
                          "value is then null)")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-batched", action="store_true")
+    ap.add_argument("--eager-decode", action="store_true",
+                    help="launch the decode steps one by one instead of "
+                         "replaying a HIP graph (for counter collection)")
+    ap.add_argument("--skip-truncated", action="store_true",
+                    help="skip the segment-truncated prefill leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16384)
     a = ap.parse_args(argv)
@@ -278,7 +283,8 @@ def main(argv=None):
     if not a.skip_decode:
         for Bd, dkd in [(bb, dd) for bb in a.decode_batch for dd in (128, 64)]:
             decode[f"B{Bd}_dk{dkd}"] = bench_decode(
-                torch, gdn, dev, stream, Bd, dkd, a.decode_steps, a.layers, up)
+                torch, gdn, dev, stream, Bd, dkd, a.decode_steps, a.layers, up,
+                eager=a.eager_decode)
     # ---------------- batched prefill, dk 128 vs 64 ----------------
     batched = {}
     if not a.skip_batched:
@@ -291,6 +297,11 @@ def main(argv=None):
         if f"B{bb}_dk128" in decode and f"B{bb}_dk64" in decode:
             decode[f"speedup_dk64_vs_dk128_B{bb}"] = (decode[f"B{bb}_dk128"]["us_per_step"] /
                                                      decode[f"B{bb}_dk64"]["us_per_step"])
+
+    # ---------------- segment-truncated prefill, r in {1, 4, 12, 32} ----------
+    truncated = {}
+    if not a.skip_truncated:
+        truncated = bench_truncated(torch, gdn, dev, stream, up)
 
     copy_bw = copy_bandwidth(torch, dev, stream)
     log(f"device copy (512 MiB): {copy_bw / 1e9:.0f} GB/s read+write")
@@ -315,6 +326,7 @@ def main(argv=None):
         "prefill": prefill_info,
         "decode": decode,
         "batched_prefill": batched,
+        "truncated_prefill": truncated,
         "cpu_baseline": cpu,
         "copy_bandwidth_GBps": copy_bw / 1e9,
         "host": platform.node(),
@@ -345,8 +357,11 @@ def copy_bandwidth(torch, dev, stream, nbytes=512 << 20, reps=20):
     return 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3)
 
 
-def bench_decode(torch, gdn, dev, stream, B, dk, n_steps, layers, up):
-    """512 decode steps x `layers` state sets, captured in one HIP graph."""
+def bench_decode(torch, gdn, dev, stream, B, dk, n_steps, layers, up,
+                 eager=False):
+    """512 decode steps x `layers` state sets, captured in one HIP graph
+    (or launched one by one with `eager`, which then times launch gaps
+    too)."""
     H, dv = 16, 128
     log(f"decode B={B} dk={dk}: prompt prefill (2048 tokens) ...")
     pr = gi.decode_prompt(B=B, dk=dk)
@@ -368,17 +383,25 @@ def bench_decode(torch, gdn, dev, stream, B, dk, n_steps, layers, up):
     for l in range(layers):
         one(0, l)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+
+    def all_steps():
         for t in range(n_steps):
             for l in range(layers):
                 one(t, l)
+
+    if eager:
+        replay = all_steps
+    else:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            all_steps()
+        replay = g.replay
     torch.cuda.synchronize()
-    g.replay()                       # untimed replay
+    replay()                         # untimed pass
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    g.replay()
+    replay()
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
@@ -387,6 +410,7 @@ def bench_decode(torch, gdn, dev, stream, B, dk, n_steps, layers, up):
     nbytes = decode_bytes(B, H, dk, dv)
     res = {"us_per_step": us, "tokens_per_s": B / (us * 1e-6),
            "launches_timed": launches, "state_sets": layers,
+           "graph": not eager,
            "roofline": {"bound": "hbm", "kernel": "decode_kernel",
                         "achieved": nbytes / (us * 1e-6) / 1e9,
                         "peak": HBM_PEAK / 1e9, "unit": "GB/s",
@@ -395,7 +419,7 @@ def bench_decode(torch, gdn, dev, stream, B, dk, n_steps, layers, up):
                         "algorithmic_bytes": nbytes}}
     log(f"  decode B={B} dk={dk}: {us:.2f} us/step, "
         f"{res['roofline']['achieved']:.0f} GB/s ({100 * res['roofline']['frac']:.1f} % of HBM)")
-    del g, states, qs, ks, vs, als, bes, S
+    del replay, states, qs, ks, vs, als, bes, S
     torch.cuda.empty_cache()
     return res
 
@@ -425,10 +449,78 @@ def bench_batched(torch, gdn, dev, stream, dk, steps, warmup, up):
            "roofline": {"bound": "hbm", "achieved": nbytes / (us * 1e-6) / 1e9,
                         "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                         "frac": nbytes / (us * 1e-6) / HBM_PEAK,
+                        "traffic": measured_traffic(f"batched_dk{dk}"),
                         "algorithmic_bytes": nbytes}}
     log(f"batched prefill B=8 T=4096 dk={dk}: {us:.1f} us, "
         f"{res['tokens_per_s'] / 1e6:.1f} M tokens/s")
     del q, k, v, al, be, o, ST, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_truncated(torch, gdn, dev, stream, up, ranks=(1, 4, 12, 32),
+                    segment=256):
+    """Segment-truncated prefill: B=1, H=16, T=16384, dk=dv=128; at each of
+    the 63 boundaries between 256-token segments every head's state is
+    projected onto its top-r left singular directions.  Each r's whole pass
+    (64 prefill calls + 63 truncations) is captured in one HIP graph and
+    replayed; r = 128 is the untruncated control.  The truncation alone is
+    also timed on the 16 states met at the first boundary."""
+    x = gi.truncated_prefill()
+    B, T, H, dk = x.q.shape
+    dv = x.v.shape[-1]
+    q, k, v, al, be = up(x)
+    del x
+    _, S_b1 = gdn.prefill(q[:, :segment], k[:, :segment], v[:, :segment],
+                          al[:, :segment], be[:, :segment])
+    ws = torch.empty(gdn.truncate_workspace_bytes(B * H, dv, dk),
+                     dtype=torch.uint8, device=dev)
+    res = {"workload": f"B={B}, H={H}, T={T}, dk=dv={dk}, bf16 in/out, "
+                       f"truncation every {segment} tokens",
+           "boundaries": (T - 1) // segment}
+    for r in (*ranks, min(dk, dv)):
+        def run():
+            return gdn.prefill_truncated(q, k, v, al, be, r, segment=segment)
+        run()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            _, _, er = run()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        erv = er.float().cpu().numpy().reshape(-1)
+        item = {"ms_per_pass": ms, "tokens_per_s": B * T / (ms * 1e-3),
+                "stable_rank_at_T": {"mean": float(np.mean(erv)),
+                                     "min": float(np.min(erv)),
+                                     "max": float(np.max(erv)),
+                                     "per_head": [round(float(e), 3) for e in erv]}}
+        if r < min(dk, dv):
+            times = []
+            for _ in range(5):
+                Sx = S_b1.clone()
+                torch.cuda.synchronize()
+                e0.record(stream)
+                gdn.truncate_rank(Sx, r, stable_rank=False, workspace=ws)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            item["one_boundary_truncate_us"] = float(np.median(times)) * 1e3
+        res[f"r{r}"] = item
+        log(f"truncated prefill r={r}: {ms:.2f} ms/pass, er(S_T) mean "
+            f"{np.mean(erv):.2f}" + (f", one boundary {item['one_boundary_truncate_us']:.0f} us"
+                                     if "one_boundary_truncate_us" in item else ""))
+        del g, er
+    base = res[f"r{min(dk, dv)}"]["ms_per_pass"]
+    for r in ranks:
+        res[f"r{r}"]["truncation_ms"] = res[f"r{r}"]["ms_per_pass"] - base
+    del q, k, v, al, be, S_b1, ws
     torch.cuda.empty_cache()
     return res
 
