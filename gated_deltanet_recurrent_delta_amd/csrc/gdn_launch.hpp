@@ -38,8 +38,14 @@ struct PrefillPlan {
   size_t total_bytes;
 };
 
-// Scan workgroups the segmentation aims for (256 CUs, two rounds).
-constexpr int kScanTargetBlocks = 512;
+// Segmentation aims for one scan workgroup (one head-segment) per CU of
+// the 256 on MI355X, and is used only when B*H heads leave at least
+// kMinSegsPerHead segments per head to fill it.
+#ifndef GDN_SCAN_TARGET_BLOCKS
+#define GDN_SCAN_TARGET_BLOCKS 256
+#endif
+constexpr int kScanTargetBlocks = GDN_SCAN_TARGET_BLOCKS;
+constexpr int kMinSegsPerHead = 4;
 constexpr int kMinSegChunks = 8;
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -53,9 +59,8 @@ inline PrefillPlan plan_prefill(int B, int T, int H, int dk, int dv) {
   p.nseg = 1;
   p.seg_chunks = p.nchunks;
   const int per_head_target = kScanTargetBlocks / (B * H > 0 ? B * H : 1);
-  const int g0 = dv / 64, gx = (dv + dk) / 64;
-  if (per_head_target > g0 && p.nchunks >= 2 * kMinSegChunks) {
-    int nseg = 1 + (per_head_target - g0) / gx;
+  if (per_head_target >= kMinSegsPerHead && p.nchunks >= 2 * kMinSegChunks) {
+    int nseg = per_head_target;
     nseg = nseg < p.nchunks / kMinSegChunks ? nseg : p.nchunks / kMinSegChunks;
     if (nseg > 1) {
       p.seg_chunks = (p.nchunks + nseg - 1) / nseg;

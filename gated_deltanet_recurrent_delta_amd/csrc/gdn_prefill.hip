@@ -411,34 +411,29 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
   const TIn* q_seq = q + ((size_t)b * T * H + h) * DK;
   const TIn* v_seq = v + ((size_t)b * T * H + h) * DV + r0;
   const size_t tok_k = (size_t)H * DK, tok_v = (size_t)H * DV;
+  // Rows past the end of the sequence load the last valid row (always in
+  // bounds); commit_stage zeroes them.  Nothing reads the loaded registers
+  // before the commit, so the loads stay in flight while the previous chunk
+  // computes.
   auto load_stage = [&](St& st, int chunk) {
     const int t0 = chunk * C;
     const int nvalid = min(C, T - t0);
-    // Branch-free: rows past the end of the sequence load the last valid
-    // row (always in bounds) and are zeroed by a select.
     const uint4 zero4 = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < St::UNITS_K; ++i) {
       const int u = tid + NT * i;
       const int c = u / UPR, cu = u - c * UPR;
-      const bool ok = c < nvalid;
-      const size_t off = (size_t)(t0 + (ok ? c : nvalid - 1)) * tok_k + cu * EPU;
-      const uint4 kx = *reinterpret_cast<const uint4*>(k_seq + off);
-      const uint4 qx = *reinterpret_cast<const uint4*>(q_seq + off);
-      const uint32_t mk = ok ? 0xFFFFFFFFu : 0u;   // (a select on uint4 spills)
-      st.k[i] = make_uint4(kx.x & mk, kx.y & mk, kx.z & mk, kx.w & mk);
-      st.q[i] = make_uint4(qx.x & mk, qx.y & mk, qx.z & mk, qx.w & mk);
+      const size_t off = (size_t)(t0 + min(c, nvalid - 1)) * tok_k + cu * EPU;
+      st.k[i] = *reinterpret_cast<const uint4*>(k_seq + off);
+      st.q[i] = *reinterpret_cast<const uint4*>(q_seq + off);
     }
     if (!xrows) {
 #pragma unroll
       for (int i = 0; i < St::UNITS_V; ++i) {
         const int u = tid + NT * i;
         const int c = u / VUPR, cu = u - c * VUPR;
-        const bool ok = c < nvalid;
-        const uint4 vx = *reinterpret_cast<const uint4*>(
-            v_seq + (size_t)(t0 + (ok ? c : nvalid - 1)) * tok_v + cu * EPU);
-        const uint32_t mv = ok ? 0xFFFFFFFFu : 0u;
-        st.v[i] = make_uint4(vx.x & mv, vx.y & mv, vx.z & mv, vx.w & mv);
+        st.v[i] = *reinterpret_cast<const uint4*>(
+            v_seq + (size_t)(t0 + min(c, nvalid - 1)) * tok_v + cu * EPU);
       }
     } else {
 #pragma unroll
@@ -452,17 +447,20 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
     st.g = (tid < 4 * C) ? reinterpret_cast<const float*>(wsc + kWsG)[tid] : 0.f;
   };
 
-  auto commit_stage = [&](const St& st) {
+  auto commit_stage = [&](const St& st, int nvalid) {
 #pragma unroll
     for (int i = 0; i < St::UNITS_K; ++i) {
       const int u = tid + NT * i;
       const int c = u / UPR, d0 = (u - c * UPR) * EPU;
+      const uint32_t mk = c < nvalid ? 0xFFFFFFFFu : 0u;   // (a select on uint4 spills)
+      const uint4 kx = make_uint4(st.k[i].x & mk, st.k[i].y & mk, st.k[i].z & mk, st.k[i].w & mk);
+      const uint4 qx = make_uint4(st.q[i].x & mk, st.q[i].y & mk, st.q[i].z & mk, st.q[i].w & mk);
       if constexpr (KEXACT) {
-        *reinterpret_cast<uint4*>(&Khs[c * LDK + d0]) = st.k[i];
-        *reinterpret_cast<uint4*>(&Qhs[c * LDK + d0]) = st.q[i];
+        *reinterpret_cast<uint4*>(&Khs[c * LDK + d0]) = kx;
+        *reinterpret_cast<uint4*>(&Qhs[c * LDK + d0]) = qx;
       } else {
-        const float4 kf = __builtin_bit_cast(float4, st.k[i]);
-        const float4 qf = __builtin_bit_cast(float4, st.q[i]);
+        const float4 kf = __builtin_bit_cast(float4, kx);
+        const float4 qf = __builtin_bit_cast(float4, qx);
         const float kx[4] = {kf.x, kf.y, kf.z, kf.w};
         const float qx[4] = {qf.x, qf.y, qf.z, qf.w};
         bf16x4 kh, kl, qh, ql;
@@ -486,10 +484,12 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
       const int u = tid + NT * i;
       const int c = u / VUPR, rr = (u - c * VUPR) * EPU;
       const int vb = (rr >> 4) * VBLK + c * LDV + (rr & 15);   // wave block, row c
+      const uint32_t mv = c < nvalid ? 0xFFFFFFFFu : 0u;
+      const uint4 vx = make_uint4(st.v[i].x & mv, st.v[i].y & mv, st.v[i].z & mv, st.v[i].w & mv);
       if constexpr (KEXACT) {
-        *reinterpret_cast<uint4*>(&Vhs[vb]) = st.v[i];
+        *reinterpret_cast<uint4*>(&Vhs[vb]) = vx;
       } else {
-        const float4 vf = __builtin_bit_cast(float4, st.v[i]);
+        const float4 vf = __builtin_bit_cast(float4, vx);
         const float vx[4] = {vf.x, vf.y, vf.z, vf.w};
         bf16x4 vh, vl;
         split4(vx, vh, vl);
@@ -539,7 +539,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
     const int t0 = chunk * C;
     const int nvalid = min(C, T - t0);
     __syncthreads();                   // everyone is done with the last tiles
-    commit_stage(st);
+    commit_stage(st, nvalid);
     __syncthreads();
     if (chunk + 1 < c_end) load_stage(st, chunk + 1);   // prefetch
 
@@ -712,6 +712,330 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
     for (int dt = 0; dt < NDT; ++dt)
       *reinterpret_cast<float4*>(sdst + srow * DK + 16 * dt + 4 * g4) =
           make_float4(S[dt][0], S[dt][1], S[dt][2], S[dt][3]);
+  }
+}
+
+// ===========================================================================
+// scan, segmented bf16 path: one workgroup per (batch, head, segment)
+// ===========================================================================
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void glb_cvoid_t;
+// 16 bytes per lane from global memory straight into LDS: lane L's bytes go
+// to lds_block + 16 L (lds_block is the same for the whole wave).
+__device__ __forceinline__ void dma16(const void* g, void* lds_block) {
+  __builtin_amdgcn_global_load_lds((glb_cvoid_t*)g, (lds_void_t*)lds_block, 16, 0, 0);
+}
+
+// The rows a segment evolves are the DV state rows and, for segments >= 1,
+// the DK transition rows (see SegArgs).  One workgroup carries all of them:
+// wave w owns rows 16 NH w .. 16 NH (w + 1) - 1 of that combined row space
+// as NH 16-row slices.  The chunk's K, Q, T, P, V and gate tiles are loaded
+// once per workgroup, straight from global memory into one of two LDS
+// buffers (direct loads: each wave instruction fills 1 KB, 16 bytes per
+// lane) while the previous chunk computes from the other; every operand a
+// wave reads from LDS (K, Q, T, P, K^T) serves all NH of its slices.  The
+// outputs are formed transposed, O^T = S Q^T diag(gamma) + U^T P^T, so a
+// lane holds 4 consecutive rows of one token and stores them directly.
+// Segment 0 has no transition rows; its transition waves only load tiles.
+template <int DK, int DV, int NH>
+__global__ __launch_bounds__(64 * (DV + DK) / (16 * NH), 1) void scan_wide_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k,
+    const bf16* __restrict__ v, const float* S0, bf16* __restrict__ o,
+    const float* __restrict__ ws, int T, int H, int nchunks, SegArgs seg) {
+  constexpr int RPW = 16 * NH;          // rows per wave
+  static_assert(DV % RPW == 0 && DK % RPW == 0, "waves hold state or transition rows only");
+  constexpr int NW = (DV + DK) / RPW;   // waves
+  constexpr int NDT = DK / 16;          // d-tiles of a 16-row state slice
+  constexpr int NKB = DK / 32;          // 32-wide k-blocks over d
+  // Tiles are row-major bf16 with one 16-byte pad unit per row (strides of
+  // an odd number of 16-byte units keep row-parallel reads on distinct
+  // banks).  UK, UT, UV: 16-byte units per row including the pad.
+  constexpr int LDK = DK + 8, LDT = C + 8, LDV = DV + 8;
+  constexpr int UK = LDK / 8, UT = LDT / 8, UV = LDV / 8;
+  // one buffer: K, Q [C][LDK]; T hi, T lo, P hi [C][LDT]; V [C][LDV]; gates fp32 [4][C]
+  constexpr int OFF_Q = C * LDK, OFF_T = 2 * C * LDK, OFF_V = OFF_T + 3 * C * LDT;
+  constexpr int OFF_G = OFF_V + C * LDV;
+  constexpr int BUF = OFF_G + 2 * 4 * C;                 // bf16 elements
+  // 1 KB load blocks per buffer (64 rows of U units = U blocks per tile)
+  constexpr int NBK = UK, NBT = 3 * UT, NBV = UV;
+  constexpr int NB = 2 * NBK + NBT + NBV + 1;
+  __shared__ __attribute__((aligned(16))) bf16 buf0[BUF];
+  __shared__ __attribute__((aligned(16))) bf16 buf1[BUF];
+
+  const int bh = blockIdx.x / seg.nseg, sg = blockIdx.x - bh * seg.nseg;
+  const int b = bh / H, h = bh - b * H;
+  const int c_begin = sg * seg.seg_chunks;
+  const int c_end = min(c_begin + seg.seg_chunks, nchunks);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
+  const int n = lane & 15, g4 = lane >> 4;
+  const int row0 = RPW * w;                 // first row (combined space)
+  const bool xrows = row0 >= DV;            // transition rows
+  const bool active = !xrows || sg > 0;
+
+  const bf16* k_seq = k + ((size_t)b * T * H + h) * DK;
+  const bf16* q_seq = q + ((size_t)b * T * H + h) * DK;
+  const bf16* v_seq = v + ((size_t)b * T * H + h) * DV;
+  const size_t tok_k = (size_t)H * DK, tok_v = (size_t)H * DV;
+
+  // Issue this wave's share of the load blocks of `chunk` into buffer X.
+  // A lane whose 16 bytes land on a pad unit fetches the row's first unit
+  // (never read).  Token rows past the end of the sequence load the last
+  // valid row: their beta is 0 and their decay 1, so they contribute
+  // nothing (finite values times zero) and their outputs are not stored.
+  auto issue = [&](bf16* X, int chunk) {
+    const int t0 = chunk * C;
+    const int last = min(C, T - t0) - 1;
+    const char* wsc = reinterpret_cast<const char*>(ws) +
+                      ((size_t)bh * nchunks + chunk) * kChunkWsFloats * 4;
+    for (int ib = w; ib < NB; ib += NW) {
+      const bf16* src;
+      bf16* dst = X + 512 * ib;               // blocks tile the buffer in order
+      if (ib < 2 * NBK) {                     // K, then Q
+        const int jb = ib < NBK ? ib : ib - NBK;
+        const int idx = 64 * jb + lane, row = idx / UK, u = idx - row * UK;
+        src = (ib < NBK ? k_seq : q_seq) + (size_t)(t0 + min(row, last)) * tok_k +
+              8 * (u < UK - 1 ? u : 0);
+      } else if (ib < 2 * NBK + NBT) {        // T hi, T lo, P hi
+        const int idx = 64 * (ib - 2 * NBK) + lane;
+        const int m = idx / (C * UT), rm = idx - m * (C * UT);
+        const int row = rm / UT, u = rm - row * UT;
+        src = reinterpret_cast<const bf16*>(wsc + m * (C * C * 2) + row * (C * 2) +
+                                            16 * (u < UT - 1 ? u : 0));
+      } else if (ib < 2 * NBK + NBT + NBV) {  // V
+        const int idx = 64 * (ib - 2 * NBK - NBT) + lane, row = idx / UV, u = idx - row * UV;
+        src = v_seq + (size_t)(t0 + min(row, last)) * tok_v + 8 * (u < UV - 1 ? u : 0);
+      } else {                                // gates
+        src = reinterpret_cast<const bf16*>(wsc + kWsG + 16 * lane);
+      }
+      dma16(src, dst);
+    }
+  };
+  static_assert(OFF_Q == 512 * NBK && OFF_T == 512 * 2 * NBK &&
+                OFF_V == 512 * (2 * NBK + NBT) && OFF_G == 512 * (2 * NBK + NBT + NBV),
+                "load blocks tile the buffer");
+
+  // ---- carried state: S^T tiles of each slice, lane holds
+  //      S^T[d = 16 dt + 4 g4 + i][row = 16 hf + n] ----
+  floatx4 S[NH][NDT];
+#pragma unroll
+  for (int hf = 0; hf < NH; ++hf) {
+    const int r = row0 + 16 * hf + n;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      if (xrows) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          S[hf][dt][i] = (16 * dt + 4 * g4 + i == r - DV) ? 1.f : 0.f;
+      } else if (S0 != nullptr && sg == 0) {
+        const float4 x = *reinterpret_cast<const float4*>(
+            S0 + ((size_t)bh * DV + r) * DK + 16 * dt + 4 * g4);
+        S[hf][dt] = floatx4{x.x, x.y, x.z, x.w};
+      } else {
+        S[hf][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  }
+  // Outputs: o for state rows, x^_t = X_t q_t ([BH][T][DK]) for transition
+  // rows; obase + t * ostride is token t's element for this wave's row 0.
+  bf16* obase;
+  size_t ostride;
+  if (xrows) {
+    obase = reinterpret_cast<bf16*>(seg.xhat) + (size_t)bh * T * DK + (row0 - DV);
+    ostride = DK;
+  } else {
+    obase = o + ((size_t)b * T * H + h) * DV + row0;
+    ostride = (size_t)H * DV;
+  }
+
+  // One chunk from buffer X (loaded), prefetching chunk + 1 into buffer Nx.
+  auto step = [&](const bf16* X, bf16* Nx, int chunk) {
+    const int t0 = chunk * C;
+    const int nvalid = min(C, T - t0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's loads of X
+    __syncthreads();                          // everyone's loads of X; Nx is free
+    if (chunk + 1 < c_end) issue(Nx, chunk + 1);
+    if (!active) return;
+    const bf16* Ks = X;
+    const bf16* Qs = X + OFF_Q;
+    const bf16* Ths = X + OFF_T;
+    const bf16* Tls = Ths + C * LDT;
+    const bf16* Phs = Tls + C * LDT;
+    const bf16* Vs = X + OFF_V;
+    const float* Gs = reinterpret_cast<const float*>(X + OFF_G);
+
+    // ---- Y = K S^T for all slices (c-tile ct: rows c = 16 ct + 4 g4 + i,
+    //      col = row n of the slice) ----
+    floatx4 Y[NH][4];
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) Y[hf][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NKB; ++s) {
+      bf16x8 Sh[NH], Sl[NH];
+#pragma unroll
+      for (int hf = 0; hf < NH; ++hf)
+        split8(acc_slots(S[hf][2 * s], S[hf][2 * s + 1]), Sh[hf], Sl[hf]);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const bf16x8 kh = lds_slots(Ks, LDK, 16 * ct + n, s, g4);
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf) {
+          Y[hf][ct] = mfma(kh, Sh[hf], Y[hf][ct]);
+          Y[hf][ct] = mfma(kh, Sl[hf], Y[hf][ct]);
+        }
+      }
+    }
+
+    // ---- Z = beta (V - gamma Y), as split B operands over c ----
+    bf16x8 Zh[NH][2], Zl[NH][2];
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
+      floatx4 Z[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int c = 16 * ct + 4 * g4;
+        // V[c + j][row]; transition rows read column 0 and scale it by 0
+        // (branch-free, so the read stays in the block the load tracking
+        // knows does not touch the buffer being filled)
+        const uint2 vw = lds_tr4(Vs, LDV, c, xrows ? 0 : row0 + 16 * hf, n);
+        const float vs = xrows ? 0.f : 1.f;
+        const float vv[4] = {vs * bf16lo(vw.x), vs * bf16hi(vw.x), vs * bf16lo(vw.y),
+                             vs * bf16hi(vw.y)};
+        const float4 bb = *reinterpret_cast<const float4*>(&Gs[C + c]);
+        const float4 gg = *reinterpret_cast<const float4*>(&Gs[2 * C + c]);
+        Z[ct] = floatx4{bb.x * (vv[0] - gg.x * Y[hf][ct][0]), bb.y * (vv[1] - gg.y * Y[hf][ct][1]),
+                        bb.z * (vv[2] - gg.z * Y[hf][ct][2]), bb.w * (vv[3] - gg.w * Y[hf][ct][3])};
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) split8(acc_slots(Z[2 * s], Z[2 * s + 1]), Zh[hf][s], Zl[hf][s]);
+    }
+
+    // ---- U = T Z  (T lower triangular: c-tile ct needs k-blocks <= ct/2) ----
+    floatx4 U[NH][4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+      for (int hf = 0; hf < NH; ++hf) U[hf][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s <= ct / 2; ++s) {
+        const bf16x8 th = lds_slots(Ths, LDT, 16 * ct + n, s, g4);
+        const bf16x8 tl = lds_slots(Tls, LDT, 16 * ct + n, s, g4);
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf) {
+          U[hf][ct] = mfma(th, Zh[hf][s], U[hf][ct]);
+          U[hf][ct] = mfma(th, Zl[hf][s], U[hf][ct]);
+          U[hf][ct] = mfma(tl, Zh[hf][s], U[hf][ct]);
+        }
+      }
+    }
+
+    // ---- O^T = S Q^T diag(gamma) + U^T P^T (single-pass bf16: o is bf16);
+    //      tile ct: rows r = 4 g4 + i of the slice, token c = 16 ct + n ----
+    {
+      floatx4 OT[NH][4];
+#pragma unroll
+      for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) OT[hf][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NKB; ++s) {
+        bf16x8 Sb[NH];
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf) Sb[hf] = to_bf16x8(acc_slots(S[hf][2 * s], S[hf][2 * s + 1]));
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const bf16x8 qh = lds_slots(Qs, LDK, 16 * ct + n, s, g4);
+#pragma unroll
+          for (int hf = 0; hf < NH; ++hf) OT[hf][ct] = mfma(Sb[hf], qh, OT[hf][ct]);
+        }
+      }
+      bf16x8 Uh[NH][2];
+#pragma unroll
+      for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) Uh[hf][s] = to_bf16x8(acc_slots(U[hf][2 * s], U[hf][2 * s + 1]));
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const float gam = Gs[2 * C + 16 * ct + n];
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf) OT[hf][ct] *= gam;
+#pragma unroll
+        for (int s = 0; s <= ct / 2; ++s) {
+          const bf16x8 ph = lds_slots(Phs, LDT, 16 * ct + n, s, g4);
+#pragma unroll
+          for (int hf = 0; hf < NH; ++hf) OT[hf][ct] = mfma(Uh[hf][s], ph, OT[hf][ct]);
+        }
+        const int c = 16 * ct + n;
+        if (c < nvalid) {
+#pragma unroll
+          for (int hf = 0; hf < NH; ++hf) {
+            bf16x4 ob;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ob[e] = (bf16)OT[hf][ct][e];
+            *reinterpret_cast<bf16x4*>(obase + (size_t)(t0 + c) * ostride + 16 * hf + 4 * g4) = ob;
+          }
+        }
+      }
+    }
+
+    // ---- S^T <- gamma_C S^T + K^T diag(e^{g_C - g}) U, all slices ----
+    {
+      bf16x8 Dh[NH][2], Dl[NH][2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const float4 d0 = *reinterpret_cast<const float4*>(&Gs[3 * C + kslot_base(s, g4, 0)]);
+        const float4 d1 = *reinterpret_cast<const float4*>(&Gs[3 * C + kslot_base(s, g4, 1)]);
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf) {
+          const floatx4& ua = U[hf][2 * s];
+          const floatx4& ub = U[hf][2 * s + 1];
+          const floatx8 du = {ua[0] * d0.x, ua[1] * d0.y, ua[2] * d0.z, ua[3] * d0.w,
+                              ub[0] * d1.x, ub[1] * d1.y, ub[2] * d1.z, ub[3] * d1.w};
+          split8(du, Dh[hf][s], Dl[hf][s]);
+        }
+      }
+      const float gC = Gs[3 * C - 1];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        floatx4 acc[NH];
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf) acc[hf] = S[hf][dt] * gC;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16x8 kth = lds_slots_tr(Ks, LDK, 16 * dt, s, g4, n);   // K[kslot][16 dt + n]
+#pragma unroll
+          for (int hf = 0; hf < NH; ++hf) {
+            acc[hf] = mfma(kth, Dh[hf][s], acc[hf]);
+            acc[hf] = mfma(kth, Dl[hf][s], acc[hf]);
+          }
+        }
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf) S[hf][dt] = acc[hf];
+      }
+    }
+  };
+
+  issue(buf0, c_begin);
+  for (int chunk = c_begin; chunk < c_end; chunk += 2) {
+    step(buf0, buf1, chunk);
+    if (chunk + 1 < c_end) step(buf1, buf0, chunk + 1);
+  }
+
+  // Final rows of this segment for the combine pass.
+  if (active) {
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
+      const int r = row0 + 16 * hf + n;
+      float* dst = xrows ? seg.X_fin + (((size_t)bh * seg.nseg + sg) * DK + (r - DV)) * DK
+                         : seg.S_fin + (((size_t)bh * seg.nseg + sg) * DV + r) * DK;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<float4*>(dst + 16 * dt + 4 * g4) =
+            make_float4(S[hf][dt][0], S[hf][dt][1], S[hf][dt][2], S[hf][dt][3]);
+    }
   }
 }
 
@@ -913,6 +1237,26 @@ __global__ __launch_bounds__(256) void segment_correct_kernel(SegArgs seg, bf16*
 // Waves per scan workgroup (16 state rows each).
 constexpr int kScanWaves = 4;
 
+// Segmented bf16 prefills use scan_wide_kernel (one workgroup per head and
+// segment) when set, else scan_kernel.
+#ifndef GDN_USE_WIDE
+#define GDN_USE_WIDE 1
+#endif
+constexpr bool kUseWide = GDN_USE_WIDE != 0;
+
+// 16-row slices per wave of the segmented scan.
+#ifndef GDN_WIDE_SLICES
+#define GDN_WIDE_SLICES 2
+#endif
+constexpr int kWideSlices = GDN_WIDE_SLICES;
+
+// Whether grids larger than the CU count use the two-workgroups-per-CU
+// build of the bf16 scan.
+#ifndef GDN_SCAN_OCC2
+#define GDN_SCAN_OCC2 1
+#endif
+constexpr bool kScanOcc2 = GDN_SCAN_OCC2 != 0;
+
 // CUs of the target GPU (MI355X); grids larger than this use the
 // two-workgroups-per-CU build of the bf16 scan.
 constexpr int kNumCUs = 256;
@@ -923,11 +1267,26 @@ static void launch_scan_t(const void* q, const void* k, const void* v,
                           int B, int T, int H, int dv, const SegArgs& seg,
                           hipStream_t stream) {
   const int nchunks = (T + C - 1) / C;
+  if constexpr (kUseWide && std::is_same<TIn, bf16>::value && std::is_same<TOut, bf16>::value) {
+    if (seg.nseg > 1) {
+      // segmented: one workgroup per (batch, head, segment)
+#define GDN_WIDE(DV_, NH_)                                                          \
+  hipLaunchKernelGGL((scan_wide_kernel<DK, DV_, NH_>), dim3(B * H * seg.nseg),      \
+                     dim3(64 * (DV_ + DK) / (16 * NH_)), 0, stream,                 \
+                     static_cast<const bf16*>(q), static_cast<const bf16*>(k),      \
+                     static_cast<const bf16*>(v), S0, static_cast<bf16*>(o), ws, T, \
+                     H, nchunks, seg)
+      if (dv == 128) GDN_WIDE(128, kWideSlices);
+      else GDN_WIDE(64, kWideSlices);
+#undef GDN_WIDE
+      return;
+    }
+  }
   constexpr int ROWS = 16 * kScanWaves;
   const int per_head = dv / ROWS + (seg.nseg - 1) * ((dv + DK) / ROWS);
   const int nblocks = B * H * per_head;
   constexpr bool BF16IO = std::is_same<TIn, bf16>::value && std::is_same<TOut, bf16>::value;
-  if (BF16IO && nblocks > kNumCUs) {
+  if (BF16IO && kScanOcc2 && nblocks > kNumCUs) {
     hipLaunchKernelGGL((scan_kernel<DK, TIn, TOut, kScanWaves, 2>), dim3(nblocks),
                        dim3(64 * kScanWaves), 0, stream,
                        static_cast<const TIn*>(q), static_cast<const TIn*>(k),
