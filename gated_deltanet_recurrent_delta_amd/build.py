@@ -32,6 +32,11 @@ FLAGS = [
     # keep packed-fp32 VALU ops out of device code (a hipcc device flag; the
     # host pass warns that it does not know it)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in architectural VGPRs: otherwise values loaded
+    # from memory and later used as accumulators are copied into AGPRs right
+    # at the load, which forces a wait on the load (and on every vector
+    # memory operation issued before it, prefetches included)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

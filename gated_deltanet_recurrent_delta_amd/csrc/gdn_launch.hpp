@@ -26,7 +26,7 @@ struct SegArgs {
   int nseg;          // segments per head (1: unsegmented, the fields below unused)
   int seg_chunks;    // chunks per segment (the last may be shorter)
   float* S_fin;      // [BH][nseg][dv][dk] final real-row state of each segment
-  float* X_fin;      // [BH][nseg][dk][dk] final transition rows (segments >= 1)
+  void* X_fin;       // [BH][nseg][2][dk][dk] bf16: X^T of segments >= 1, hi then lo part
   float* S_in;       // [BH][nseg][dv][dk] incoming state of each segment
   void* xhat;        // [BH][T][dk] bf16, x^_t for tokens of segments >= 1
 };

@@ -345,7 +345,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const float* S0, TOut* __restrict__ o,
     float* ST, const float* __restrict__ ws, int T, int H, int DV,
-    int nchunks, int nblocks, SegArgs seg) {
+    int nchunks, int nblocks) {
   constexpr bool KEXACT = std::is_same<TIn, bf16>::value;   // q, k, v exact in bf16
   constexpr bool OPREC = std::is_same<TOut, float>::value;  // o stored in fp32
   constexpr int NT = 64 * NW;           // threads
@@ -380,26 +380,15 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
   const bf16* Phs = TPs[2];
   const bf16* Pls = TPs[NTP - 1];       // (read only for fp32 outputs)
 
-  // workgroup -> (head, segment, row group); the row groups of a head are
-  // placed on one XCD (workgroups are dealt to the 8 XCDs round-robin) so
-  // they share that XCD's L2 copy of the chunk tiles.  Segment 0 has the
-  // DV/ROWS groups of real state rows; every later segment also has DK/ROWS
-  // groups of transition rows (see SegArgs).
+  // workgroup -> (head, row group); the row groups of a head are placed on
+  // one XCD (workgroups are dealt to the 8 XCDs round-robin) so they share
+  // that XCD's L2 copy of the chunk tiles.
   int lin = blockIdx.x;
   if ((nblocks & 7) == 0) lin = (lin & 7) * (nblocks >> 3) + (lin >> 3);
-  const int NRG0 = DV / ROWS, NRGX = (DV + DK) / ROWS;
-  const int per_head = NRG0 + (seg.nseg - 1) * NRGX;
-  const int bh = lin / per_head;
-  int sg = 0, rg = lin - bh * per_head;
-  if (rg >= NRG0) {
-    sg = 1 + (rg - NRG0) / NRGX;
-    rg = (rg - NRG0) % NRGX;
-  }
-  const bool xrows = rg >= NRG0;            // transition rows (segments >= 1)
+  const int NRG = DV / ROWS;
+  const int bh = lin / NRG, rg = lin - bh * NRG;
   const int b = bh / H, h = bh - b * H;
-  const int r0 = (xrows ? rg - NRG0 : rg) * ROWS;   // first row of the group
-  const int c_begin = sg * seg.seg_chunks;
-  const int c_end = min(c_begin + seg.seg_chunks, nchunks);
+  const int r0 = rg * ROWS;                 // first row of the group
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 15, g4 = lane >> 4;
@@ -418,7 +407,6 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
   auto load_stage = [&](St& st, int chunk) {
     const int t0 = chunk * C;
     const int nvalid = min(C, T - t0);
-    const uint4 zero4 = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < St::UNITS_K; ++i) {
       const int u = tid + NT * i;
@@ -427,17 +415,12 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
       st.k[i] = *reinterpret_cast<const uint4*>(k_seq + off);
       st.q[i] = *reinterpret_cast<const uint4*>(q_seq + off);
     }
-    if (!xrows) {
 #pragma unroll
-      for (int i = 0; i < St::UNITS_V; ++i) {
-        const int u = tid + NT * i;
-        const int c = u / VUPR, cu = u - c * VUPR;
-        st.v[i] = *reinterpret_cast<const uint4*>(
-            v_seq + (size_t)(t0 + min(c, nvalid - 1)) * tok_v + cu * EPU);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < St::UNITS_V; ++i) st.v[i] = zero4;
+    for (int i = 0; i < St::UNITS_V; ++i) {
+      const int u = tid + NT * i;
+      const int c = u / VUPR, cu = u - c * VUPR;
+      st.v[i] = *reinterpret_cast<const uint4*>(
+          v_seq + (size_t)(t0 + min(c, nvalid - 1)) * tok_v + cu * EPU);
     }
     const char* wsc = reinterpret_cast<const char*>(ws) +
                       ((size_t)bh * nchunks + chunk) * kChunkWsFloats * 4;
@@ -502,16 +485,10 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
 
   // ---- carried state of this wave: S^T tiles, lane holds
   //      S^T[d = 16 dt + 4 g4 + i][r = n]  (i = 0..3) ----
-  // Initial state: S0 rows for segment 0 (or zero), zero for the real rows
-  // of later segments, identity rows for the transition rows.
   floatx4 S[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
-    if (xrows) {
-      const int row = r0 + rw + n;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S[dt][i] = (16 * dt + 4 * g4 + i == row) ? 1.f : 0.f;
-    } else if (S0 != nullptr && sg == 0) {
+    if (S0 != nullptr) {
       const float4 x = *reinterpret_cast<const float4*>(
           S0 + ((size_t)bh * DV + r0 + rw + n) * DK + 16 * dt + 4 * g4);
       S[dt] = floatx4{x.x, x.y, x.z, x.w};
@@ -519,29 +496,20 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
       S[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
   }
-  // Outputs: o rows of the real state, or x^_t = X_t q_t of the transition
-  // rows ([BH][T][DK], bf16).
   // obase + t * ostride is token t's first element of this wave's 16 rows.
-  TOut* obase;
-  size_t ostride;
-  if (xrows) {
-    obase = reinterpret_cast<TOut*>(seg.xhat) + (size_t)bh * T * DK + r0 + rw;
-    ostride = DK;
-  } else {
-    obase = o + ((size_t)b * T * H + h) * DV + r0 + rw;
-    ostride = (size_t)H * DV;
-  }
+  TOut* const obase = o + ((size_t)b * T * H + h) * DV + r0 + rw;
+  const size_t ostride = (size_t)H * DV;
 
   St st;
-  load_stage(st, c_begin);
+  load_stage(st, 0);
 
-  for (int chunk = c_begin; chunk < c_end; ++chunk) {
+  for (int chunk = 0; chunk < nchunks; ++chunk) {
     const int t0 = chunk * C;
     const int nvalid = min(C, T - t0);
     __syncthreads();                   // everyone is done with the last tiles
     commit_stage(st, nvalid);
     __syncthreads();
-    if (chunk + 1 < c_end) load_stage(st, chunk + 1);   // prefetch
+    if (chunk + 1 < nchunks) load_stage(st, chunk + 1);   // prefetch
 
     // split the state into bf16 hi/lo B operands, one per 32-wide k-block
     bf16x8 Sh[NKB], Sl[NKB];
@@ -693,24 +661,11 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
     }
   }
 
-  // Final state: ST directly when unsegmented; otherwise this segment's
-  // real rows or transition rows for the combine pass.
-  float* sdst = nullptr;
-  size_t srow = 0;
-  if (seg.nseg == 1) {
-    sdst = ST;
-    srow = (size_t)bh * DV + r0 + rw + n;
-  } else if (xrows) {
-    sdst = seg.X_fin;
-    srow = ((size_t)bh * seg.nseg + sg) * DK + r0 + rw + n;
-  } else {
-    sdst = seg.S_fin;
-    srow = ((size_t)bh * seg.nseg + sg) * DV + r0 + rw + n;
-  }
-  if (sdst != nullptr) {
+  if (ST != nullptr) {
+    const size_t srow = (size_t)bh * DV + r0 + rw + n;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
-      *reinterpret_cast<float4*>(sdst + srow * DK + 16 * dt + 4 * g4) =
+      *reinterpret_cast<float4*>(ST + srow * DK + 16 * dt + 4 * g4) =
           make_float4(S[dt][0], S[dt][1], S[dt][2], S[dt][3]);
   }
 }
@@ -999,21 +954,21 @@ __global__ __launch_bounds__(64 * (DV + DK) / (16 * NH), 1) void scan_wide_kerne
       }
       const float gC = Gs[3 * C - 1];
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        floatx4 acc[NH];
+      for (int hf = 0; hf < NH; ++hf)
 #pragma unroll
-        for (int hf = 0; hf < NH; ++hf) acc[hf] = S[hf][dt] * gC;
+        for (int dt = 0; dt < NDT; ++dt) S[hf][dt] *= gC;
+      // k-block outer: the NH * NDT state tiles are independent MFMA chains
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
           const bf16x8 kth = lds_slots_tr(Ks, LDK, 16 * dt, s, g4, n);   // K[kslot][16 dt + n]
 #pragma unroll
           for (int hf = 0; hf < NH; ++hf) {
-            acc[hf] = mfma(kth, Dh[hf][s], acc[hf]);
-            acc[hf] = mfma(kth, Dl[hf][s], acc[hf]);
+            S[hf][dt] = mfma(kth, Dh[hf][s], S[hf][dt]);
+            S[hf][dt] = mfma(kth, Dl[hf][s], S[hf][dt]);
           }
         }
-#pragma unroll
-        for (int hf = 0; hf < NH; ++hf) S[hf][dt] = acc[hf];
       }
     }
   };
@@ -1024,17 +979,34 @@ __global__ __launch_bounds__(64 * (DV + DK) / (16 * NH), 1) void scan_wide_kerne
     if (chunk + 1 < c_end) step(buf1, buf0, chunk + 1);
   }
 
-  // Final rows of this segment for the combine pass.
-  if (active) {
+  // Final rows of this segment for the combine pass: state rows as fp32,
+  // transition rows as X^T split into bf16 hi and lo parts (the combine
+  // reads X^T rows as MFMA operands).
+  if (active && !xrows) {
 #pragma unroll
     for (int hf = 0; hf < NH; ++hf) {
-      const int r = row0 + 16 * hf + n;
-      float* dst = xrows ? seg.X_fin + (((size_t)bh * seg.nseg + sg) * DK + (r - DV)) * DK
-                         : seg.S_fin + (((size_t)bh * seg.nseg + sg) * DV + r) * DK;
+      float* dst = seg.S_fin + (((size_t)bh * seg.nseg + sg) * DV + row0 + 16 * hf + n) * DK;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
         *reinterpret_cast<float4*>(dst + 16 * dt + 4 * g4) =
             make_float4(S[hf][dt][0], S[hf][dt][1], S[hf][dt][2], S[hf][dt][3]);
+    }
+  } else if (active) {
+    bf16* xh = reinterpret_cast<bf16*>(seg.X_fin) + ((size_t)bh * seg.nseg + sg) * 2 * DK * DK;
+    bf16* xl = xh + DK * DK;
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
+      const int e = row0 - DV + 16 * hf + n;             // row of X
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = 16 * dt + 4 * g4 + i;            // column of X
+          bf16 hi, lo;
+          split_bf16(S[hf][dt][i], hi, lo);
+          xh[d * DK + e] = hi;
+          xl[d * DK + e] = lo;
+        }
     }
   }
 }
@@ -1089,30 +1061,50 @@ hipError_t launch_prefill_prepare(const void* q, const void* k,
 // segment combine (phase 2): S_in(s) = S_end(s-1), S_end(s) = S_in(s) X_s + S_loc(s)
 // ===========================================================================
 
-// One workgroup per (head, 64 state rows), sequential over the segments.
-// Each wave carries 16 rows as S^T tiles; X_s is staged in LDS as bf16 hi/lo
-// and read transposed, the product uses split-bf16 operands on both sides.
-// X_{s+1} and S_loc(s+1) are loaded into registers while step s computes.
+// One workgroup per (batch, head, 16 NWC state rows), sequential over the
+// segments; wave w carries 16 rows as S^T tiles.  X_s arrives from the scan
+// as X^T split into bf16 hi and lo parts, so it is loaded straight into LDS
+// (padded rows, direct loads; X_{s+1} while step s computes) and read as
+// MFMA operands by rows; the state side is split into hi/lo in registers.
+// S_loc(s+1) is loaded into registers at the end of step s.
+#ifndef GDN_COMBINE_WAVES
+#define GDN_COMBINE_WAVES 2
+#endif
+constexpr int kCombineWaves = GDN_COMBINE_WAVES;
+
 template <int DK>
-__global__ __launch_bounds__(256) void segment_combine_kernel(SegArgs seg,
-                                                              float* ST, int DV) {
-  constexpr int LDX = DK + 8;
+__global__ __launch_bounds__(64 * kCombineWaves) void segment_combine_kernel(
+    SegArgs seg, float* ST, int DV) {
+  constexpr int NWC = kCombineWaves;
   constexpr int NDT = DK / 16, NKB = DK / 32;
-  constexpr int XU = DK * DK / 4 / 256;         // float4 of X per thread
-  __shared__ __attribute__((aligned(16))) bf16 Xh[DK * LDX];
-  __shared__ __attribute__((aligned(16))) bf16 Xl[DK * LDX];
-  const int NRG = DV / 64;
+  constexpr int LDX = DK + 8, UX = LDX / 8;     // padded row, 16-byte units
+  constexpr int XT = DK * LDX;                  // elements of one part (hi or lo)
+  constexpr int NBX = 2 * DK * UX / 64;         // 1 KB load blocks of hi + lo
+  __shared__ __attribute__((aligned(16))) bf16 xb0[2 * XT];
+  __shared__ __attribute__((aligned(16))) bf16 xb1[2 * XT];
+  const int NRG = DV / (16 * NWC);
   const int bh = blockIdx.x / NRG, rg = blockIdx.x - bh * NRG;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g4 = lane >> 4;
-  const int row = rg * 64 + 16 * w + n;          // this lane's state row
+  const int row = rg * 16 * NWC + 16 * w + n;   // this lane's state row
   auto srow = [&](float* base, int s) {
     return base + (((size_t)bh * seg.nseg + s) * DV + row) * DK;
   };
-  auto load_x = [&](float4* xr, int s) {
-    const float* X = seg.X_fin + ((size_t)bh * seg.nseg + s) * DK * DK;
+  // X^T hi/lo of segment s into buffer X: part m, row d, unit u (pad units
+  // fetch unit 0 of the row and are never read)
+  auto issue = [&](bf16* X, int s) {
+    const bf16* src0 = reinterpret_cast<const bf16*>(seg.X_fin) +
+                       ((size_t)bh * seg.nseg + s) * 2 * DK * DK;
+    static_assert(NBX % NWC == 0, "load blocks split evenly over the waves");
 #pragma unroll
-    for (int i = 0; i < XU; ++i) xr[i] = *reinterpret_cast<const float4*>(X + 4 * (tid + 256 * i));
+    for (int j = 0; j < NBX / NWC; ++j) {     // (fixed trip count: unrolled)
+      const int ib = j * NWC + w;
+      const int idx = 64 * ib + lane, m = idx / (DK * UX), rm = idx - m * (DK * UX);
+      const int d = rm / UX, u = rm - d * UX;
+      dma16(src0 + (size_t)m * DK * DK + (size_t)d * DK + 8 * (u < UX - 1 ? u : 0),
+            X + 512 * ib);
+    }
   };
   auto load_loc = [&](floatx4* Lr, int s) {
 #pragma unroll
@@ -1123,44 +1115,36 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(SegArgs seg,
   };
 
   floatx4 S[NDT], L[NDT];
-  float4 xr[XU];
   load_loc(S, 0);
-  if (seg.nseg > 1) {
-    load_x(xr, 1);
-    load_loc(L, 1);
-  }
-  for (int s = 1; s < seg.nseg; ++s) {
+  issue(xb0, 1);
+  load_loc(L, 1);
+  // S_end(s) = S_in(s) X_s + S_loc(s) from buffer X (X_s loaded); prefetch
+  // X_{s+1} into Nx
+  auto step = [&](const bf16* X, bf16* Nx, int s) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's loads of X
+    __syncthreads();                          // everyone's loads of X; Nx is free
+    if (s + 1 < seg.nseg) issue(Nx, s + 1);
+    // S_in(s) for the correction pass (stored after the wait, so that it is
+    // never waited on in the step that issues it)
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
       *reinterpret_cast<float4*>(srow(seg.S_in, s) + 16 * dt + 4 * g4) =
           make_float4(S[dt][0], S[dt][1], S[dt][2], S[dt][3]);
-    __syncthreads();                       // previous X no longer read
-#pragma unroll
-    for (int i = 0; i < XU; ++i) {
-      const int e = (4 * (tid + 256 * i)) / DK, d0 = (4 * (tid + 256 * i)) % DK;
-      const float xv[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
-      bf16x4 hi, lo;
-      split4(xv, hi, lo);
-      *reinterpret_cast<bf16x4*>(&Xh[e * LDX + d0]) = hi;
-      *reinterpret_cast<bf16x4*>(&Xl[e * LDX + d0]) = lo;
-    }
     floatx4 acc[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[dt] = L[dt];
-    __syncthreads();
-    if (s + 1 < seg.nseg) {                // prefetch the next step
-      load_x(xr, s + 1);
-      load_loc(L, s + 1);
-    }
     bf16x8 Sh[NKB], Sl[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) split8(acc_slots(S[2 * kb], S[2 * kb + 1]), Sh[kb], Sl[kb]);
+    const bf16* Xh = X;
+    const bf16* Xl = X + XT;
+    // k-block outer: the NDT accumulators are independent MFMA chains
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
+    for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 ah = lds_slots_tr(Xh, LDX, 16 * dt, kb, g4, n);   // X[e][16 dt + n]
-        const bf16x8 al = lds_slots_tr(Xl, LDX, 16 * dt, kb, g4, n);
+      for (int dt = 0; dt < NDT; ++dt) {
+        const bf16x8 ah = lds_slots(Xh, LDX, 16 * dt + n, kb, g4);   // X^T[16 dt + n][e]
+        const bf16x8 al = lds_slots(Xl, LDX, 16 * dt + n, kb, g4);
         acc[dt] = mfma(ah, Sh[kb], acc[dt]);
         acc[dt] = mfma(ah, Sl[kb], acc[dt]);
         acc[dt] = mfma(al, Sh[kb], acc[dt]);
@@ -1168,6 +1152,12 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(SegArgs seg,
     }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) S[dt] = acc[dt];
+    // S_loc(s+1), waited on at the next step's wait
+    if (s + 1 < seg.nseg) load_loc(L, s + 1);
+  };
+  for (int s = 1; s < seg.nseg; s += 2) {
+    step(xb0, xb1, s);
+    if (s + 1 < seg.nseg) step(xb1, xb0, s + 1);
   }
   if (ST != nullptr) {
 #pragma unroll
@@ -1181,52 +1171,73 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(SegArgs seg,
 // segment correction (phase 3): o_t += S_in(s) x^_t for tokens of segments >= 1
 // ===========================================================================
 
-// One workgroup per (chunk of a segment >= 1, head, 64 state rows); wave w
-// handles 16 rows for the 64 tokens.  The product is formed transposed,
-// O_corr^T = S_in x^^T, so a lane holds 4 consecutive rows of one token and
-// updates o with 8-byte accesses.  Single-pass bf16 (outputs are bf16).
-template <int DK>
-__global__ __launch_bounds__(256) void segment_correct_kernel(SegArgs seg, bf16* o,
-                                                              int T, int H, int DV) {
+// One workgroup per (batch, head, chunk of a segment >= 1); wave w handles
+// state rows 16 w .. 16 w + 15 for the chunk's 64 tokens.  The product is
+// formed transposed, O_corr^T = S_in x^^T (S_in as the A operand), so a lane
+// holds 4 consecutive rows of one token and updates o with 8-byte accesses.
+// Each wave issues all of its loads before any store: with stores in flight
+// the vector-memory counter can only be waited down to zero, so the kernel
+// relies on many resident waves rather than a per-wave pipeline to hide
+// memory latency.  Single-pass bf16 (outputs are bf16).
+template <int DK, int DV>
+__global__ __launch_bounds__(4 * DV) void segment_correct_kernel(SegArgs seg, bf16* o,
+                                                                 int T, int H,
+                                                                 int nlater) {
   constexpr int NKB = DK / 32;
-  const int chunk = seg.seg_chunks + blockIdx.x;
+  // work item -> (head, chunk of a segment >= 1).  Workgroups are dealt to
+  // the 8 XCDs round-robin; consecutive work items (the chunks of one
+  // segment, which share S_in) are kept on one XCD so its L2 fetches S_in
+  // once.
+  int lin = blockIdx.x;
+  if ((gridDim.x & 7) == 0) lin = (lin & 7) * (gridDim.x >> 3) + (lin >> 3);
+  const int bh = lin / nlater, b = bh / H, h = bh - b * H;
+  const int chunk = seg.seg_chunks + (lin - bh * nlater);   // chunks of segments >= 1
   const int s = chunk / seg.seg_chunks;
-  const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
   const int t0 = chunk * C;
   const int nvalid = min(C, T - t0);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g4 = lane >> 4;
-  const int r0 = blockIdx.z * 64 + 16 * w;       // first row of this wave
-  // A operand: S_in[r0 + n][32 kb + 8 g4 .. + 7]
-  bf16x8 As[NKB];
+  const int r0 = 16 * w;                         // first row of this wave
   const float* sin_row = seg.S_in + (((size_t)bh * seg.nseg + s) * DV + r0 + n) * DK;
+  const bf16* xh = reinterpret_cast<const bf16*>(seg.xhat) + (size_t)bh * T * DK;
+  bf16* ob = o + ((size_t)b * T * H + h) * DV + r0 + 4 * g4;   // + t * H * DV
+  const size_t tok_o = (size_t)H * DV;
+  // loads: S_in rows (A operand), x^ of token 16 tt + n, o of that token
+  // (tokens past the end load the last one and are not stored)
+  float4 sa[NKB][2];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
-    const float4 a = *reinterpret_cast<const float4*>(sin_row + 32 * kb + 8 * g4);
-    const float4 c = *reinterpret_cast<const float4*>(sin_row + 32 * kb + 8 * g4 + 4);
-    As[kb] = to_bf16x8(floatx8{a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w});
+    sa[kb][0] = *reinterpret_cast<const float4*>(sin_row + 32 * kb + 8 * g4);
+    sa[kb][1] = *reinterpret_cast<const float4*>(sin_row + 32 * kb + 8 * g4 + 4);
   }
-  const bf16* xh = reinterpret_cast<const bf16*>(seg.xhat) + (size_t)bh * T * DK;
+  uint4 xb[4][NKB];
+  uint2 ov[4];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
-    const int tl = 16 * tt + n;                  // token of this lane
-    const bool ok = tl < nvalid;
-    const int tc = ok ? tl : nvalid - 1;         // clamped (in bounds)
+    const int t = t0 + min(16 * tt + n, nvalid - 1);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+      xb[tt][kb] = *reinterpret_cast<const uint4*>(xh + (size_t)t * DK + 32 * kb + 8 * g4);
+    ov[tt] = *reinterpret_cast<const uint2*>(ob + (size_t)t * tok_o);
+  }
+  bf16x8 As[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+    As[kb] = to_bf16x8(floatx8{sa[kb][0].x, sa[kb][0].y, sa[kb][0].z, sa[kb][0].w,
+                               sa[kb][1].x, sa[kb][1].y, sa[kb][1].z, sa[kb][1].w});
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const bf16x8 bx = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
-                                                       xh + (size_t)(t0 + tc) * DK + 32 * kb + 8 * g4));
-      acc = mfma(As[kb], bx, acc);
-    }
-    // acc[i] = O_corr[token tl][row r0 + 4 g4 + i]
-    bf16* p = o + (((size_t)b * T + t0 + tc) * H + h) * DV + r0 + 4 * g4;
-    const uint2 old = *reinterpret_cast<const uint2*>(p);
-    const bf16x4 ov = __builtin_bit_cast(bf16x4, old);
+    for (int kb = 0; kb < NKB; ++kb) acc = mfma(As[kb], __builtin_bit_cast(bf16x8, xb[tt][kb]), acc);
+    // acc[i] = O_corr[token 16 tt + n][row r0 + 4 g4 + i]
+    const bf16x4 old = __builtin_bit_cast(bf16x4, ov[tt]);
     bf16x4 nv;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) nv[i] = (bf16)((float)ov[i] + acc[i]);
-    if (ok) *reinterpret_cast<uint2*>(p) = __builtin_bit_cast(uint2, nv);
+    for (int i = 0; i < 4; ++i) nv[i] = (bf16)((float)old[i] + acc[i]);
+    if (16 * tt + n < nvalid)
+      *reinterpret_cast<uint2*>(ob + (size_t)(t0 + 16 * tt + n) * tok_o) = __builtin_bit_cast(uint2, nv);
   }
 }
 
@@ -1234,82 +1245,71 @@ __global__ __launch_bounds__(256) void segment_correct_kernel(SegArgs seg, bf16*
 // scan launcher
 // ===========================================================================
 
-// Waves per scan workgroup (16 state rows each).
+// Waves per scan_kernel workgroup (16 state rows each).
 constexpr int kScanWaves = 4;
 
-// Segmented bf16 prefills use scan_wide_kernel (one workgroup per head and
-// segment) when set, else scan_kernel.
-#ifndef GDN_USE_WIDE
-#define GDN_USE_WIDE 1
-#endif
-constexpr bool kUseWide = GDN_USE_WIDE != 0;
-
-// 16-row slices per wave of the segmented scan.
-#ifndef GDN_WIDE_SLICES
-#define GDN_WIDE_SLICES 2
-#endif
-constexpr int kWideSlices = GDN_WIDE_SLICES;
-
-// Whether grids larger than the CU count use the two-workgroups-per-CU
-// build of the bf16 scan.
-#ifndef GDN_SCAN_OCC2
-#define GDN_SCAN_OCC2 1
-#endif
-constexpr bool kScanOcc2 = GDN_SCAN_OCC2 != 0;
+// 16-row slices per wave of scan_wide_kernel.
+constexpr int kWideSlices = 2;
 
 // CUs of the target GPU (MI355X); grids larger than this use the
 // two-workgroups-per-CU build of the bf16 scan.
 constexpr int kNumCUs = 256;
 
+// Unsegmented scans run scan_kernel (one workgroup per head and 64 state
+// rows); segmented ones (bf16 in and out only) run scan_wide_kernel, one
+// workgroup per head and segment.
 template <int DK, typename TIn, typename TOut>
 static void launch_scan_t(const void* q, const void* k, const void* v,
                           const float* S0, void* o, float* ST, const float* ws,
                           int B, int T, int H, int dv, const SegArgs& seg,
                           hipStream_t stream) {
   const int nchunks = (T + C - 1) / C;
-  if constexpr (kUseWide && std::is_same<TIn, bf16>::value && std::is_same<TOut, bf16>::value) {
+  constexpr bool BF16IO = std::is_same<TIn, bf16>::value && std::is_same<TOut, bf16>::value;
+  if constexpr (BF16IO) {
     if (seg.nseg > 1) {
-      // segmented: one workgroup per (batch, head, segment)
-#define GDN_WIDE(DV_, NH_)                                                          \
-  hipLaunchKernelGGL((scan_wide_kernel<DK, DV_, NH_>), dim3(B * H * seg.nseg),      \
-                     dim3(64 * (DV_ + DK) / (16 * NH_)), 0, stream,                 \
+#define GDN_WIDE(DV_)                                                               \
+  hipLaunchKernelGGL((scan_wide_kernel<DK, DV_, kWideSlices>), dim3(B * H * seg.nseg), \
+                     dim3(64 * (DV_ + DK) / (16 * kWideSlices)), 0, stream,         \
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),      \
                      static_cast<const bf16*>(v), S0, static_cast<bf16*>(o), ws, T, \
                      H, nchunks, seg)
-      if (dv == 128) GDN_WIDE(128, kWideSlices);
-      else GDN_WIDE(64, kWideSlices);
+      if (dv == 128) GDN_WIDE(128);
+      else GDN_WIDE(64);
 #undef GDN_WIDE
       return;
     }
   }
   constexpr int ROWS = 16 * kScanWaves;
-  const int per_head = dv / ROWS + (seg.nseg - 1) * ((dv + DK) / ROWS);
-  const int nblocks = B * H * per_head;
-  constexpr bool BF16IO = std::is_same<TIn, bf16>::value && std::is_same<TOut, bf16>::value;
-  if (BF16IO && kScanOcc2 && nblocks > kNumCUs) {
+  const int nblocks = B * H * (dv / ROWS);
+  if (BF16IO && nblocks > kNumCUs) {
     hipLaunchKernelGGL((scan_kernel<DK, TIn, TOut, kScanWaves, 2>), dim3(nblocks),
                        dim3(64 * kScanWaves), 0, stream,
                        static_cast<const TIn*>(q), static_cast<const TIn*>(k),
                        static_cast<const TIn*>(v), S0, static_cast<TOut*>(o), ST,
-                       ws, T, H, dv, nchunks, nblocks, seg);
+                       ws, T, H, dv, nchunks, nblocks);
   } else {
     hipLaunchKernelGGL((scan_kernel<DK, TIn, TOut, kScanWaves, 1>), dim3(nblocks),
                        dim3(64 * kScanWaves), 0, stream,
                        static_cast<const TIn*>(q), static_cast<const TIn*>(k),
                        static_cast<const TIn*>(v), S0, static_cast<TOut*>(o), ST,
-                       ws, T, H, dv, nchunks, nblocks, seg);
+                       ws, T, H, dv, nchunks, nblocks);
   }
 }
 
 template <int DK>
 static void launch_segment_tail(const SegArgs& seg, void* o, float* ST, int B,
                                 int T, int H, int dv, hipStream_t stream) {
-  const int nchunks = (T + C - 1) / C;
-  hipLaunchKernelGGL((segment_combine_kernel<DK>), dim3(B * H * (dv / 64)),
-                     dim3(256), 0, stream, seg, ST, dv);
-  hipLaunchKernelGGL((segment_correct_kernel<DK>),
-                     dim3(nchunks - seg.seg_chunks, B * H, dv / 64), dim3(256),
-                     0, stream, seg, static_cast<bf16*>(o), T, H, dv);
+  hipLaunchKernelGGL((segment_combine_kernel<DK>),
+                     dim3(B * H * (dv / (16 * kCombineWaves))), dim3(64 * kCombineWaves),
+                     0, stream, seg, ST, dv);
+  const int nlater = (T + C - 1) / C - seg.seg_chunks;   // chunks of segments >= 1
+  const dim3 grid(nlater * B * H);
+  if (dv == 128)
+    hipLaunchKernelGGL((segment_correct_kernel<DK, 128>), grid, dim3(4 * 128), 0, stream,
+                       seg, static_cast<bf16*>(o), T, H, nlater);
+  else
+    hipLaunchKernelGGL((segment_correct_kernel<DK, 64>), grid, dim3(4 * 64), 0, stream,
+                       seg, static_cast<bf16*>(o), T, H, nlater);
 }
 
 hipError_t launch_prefill_scan(const void* q, const void* k, const void* v,
@@ -1327,7 +1327,7 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v,
     seg.seg_chunks = plan.seg_chunks;
     seg.xhat = wsb + plan.xhat_off;
     seg.S_fin = reinterpret_cast<float*>(wsb + plan.sfin_off);
-    seg.X_fin = reinterpret_cast<float*>(wsb + plan.xfin_off);
+    seg.X_fin = wsb + plan.xfin_off;
     seg.S_in = reinterpret_cast<float*>(wsb + plan.sin_off);
   }
   const float* wsf = static_cast<const float*>(ws);
