@@ -1171,73 +1171,135 @@ __global__ __launch_bounds__(64 * kCombineWaves) void segment_combine_kernel(
 // segment correction (phase 3): o_t += S_in(s) x^_t for tokens of segments >= 1
 // ===========================================================================
 
-// One workgroup per (batch, head, chunk of a segment >= 1); wave w handles
-// state rows 16 w .. 16 w + 15 for the chunk's 64 tokens.  The product is
-// formed transposed, O_corr^T = S_in x^^T (S_in as the A operand), so a lane
-// holds 4 consecutive rows of one token and updates o with 8-byte accesses.
-// Each wave issues all of its loads before any store: with stores in flight
-// the vector-memory counter can only be waited down to zero, so the kernel
-// relies on many resident waves rather than a per-wave pipeline to hide
-// memory latency.  Single-pass bf16 (outputs are bf16).
+// One workgroup per (batch, head, segment >= 1), in two roles:
+//  * NLW loader waves move the segment's x^ and (old) o tiles, 64 tokens at a
+//    time, straight from global memory into a ring of three LDS buffers, two
+//    tiles ahead.  They issue nothing but these loads, so waiting for the
+//    oldest tile is an exact partial wait on their own load counter.
+//  * DV/16 compute waves (wave w: state rows 16 w .. 16 w + 15) form
+//    O_corr^T = S_in x^^T for each tile (S_in as the resident A operand; a
+//    lane holds 4 consecutive rows of one token), add the old o from LDS and
+//    store.  They never wait on memory: with stores in flight, a wave's load
+//    counter could only be waited down to zero.
+// The roles run separate loops (the branch is uniform per wave) that pass
+// the same barriers, one per tile.  Single-pass bf16 (outputs are bf16).
+constexpr int kCorrLoaders = 2;
+
+// Workgroup execution barrier without a memory fence: orders this wave's
+// memory accesses in the compiler only.  Data handed over through it must
+// already be complete (here: an explicit wait on the loads that fill LDS),
+// and nothing before it waits on this wave's outstanding memory operations.
+__device__ __forceinline__ void exec_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int DK, int DV>
-__global__ __launch_bounds__(4 * DV) void segment_correct_kernel(SegArgs seg, bf16* o,
-                                                                 int T, int H,
-                                                                 int nlater) {
+__global__ __launch_bounds__(64 * (DV / 16 + kCorrLoaders)) void segment_correct_kernel(
+    SegArgs seg, bf16* o, int T, int H) {
   constexpr int NKB = DK / 32;
-  // work item -> (head, chunk of a segment >= 1).  Workgroups are dealt to
-  // the 8 XCDs round-robin; consecutive work items (the chunks of one
-  // segment, which share S_in) are kept on one XCD so its L2 fetches S_in
-  // once.
-  int lin = blockIdx.x;
-  if ((gridDim.x & 7) == 0) lin = (lin & 7) * (gridDim.x >> 3) + (lin >> 3);
-  const int bh = lin / nlater, b = bh / H, h = bh - b * H;
-  const int chunk = seg.seg_chunks + (lin - bh * nlater);   // chunks of segments >= 1
-  const int s = chunk / seg.seg_chunks;
-  const int t0 = chunk * C;
-  const int nvalid = min(C, T - t0);
+  constexpr int NCW = DV / 16;                   // compute waves
+  constexpr int NLW = kCorrLoaders;              // loader waves
+  constexpr int LDXH = DK + 8, UXH = LDXH / 8;   // padded x^ tile row (16-byte units)
+  constexpr int LDOT = DV + 8, UOT = LDOT / 8;   // padded o tile row
+  constexpr int XT = C * LDXH, OT = C * LDOT;    // elements per tile
+  constexpr int NBG = UXH + UOT;                 // 1 KB load blocks per 64-token group
+  static_assert(NBG % NLW == 0, "load blocks split evenly over the loaders");
+  constexpr int NBL = NBG / NLW;                 // blocks per loader wave per group
+  static_assert(NBL <= 63, "one group's loads fit the load counter");
+  constexpr int NBUF = 3;
+  __shared__ __attribute__((aligned(16))) bf16 ring[NBUF][XT + OT];
+
+  const int nsl = seg.nseg - 1;
+  const int bh = blockIdx.x / nsl, s = 1 + (blockIdx.x - (blockIdx.x / nsl) * nsl);
+  const int b = bh / H, h = bh - b * H;
+  const int t_begin = s * seg.seg_chunks * C;
+  const int t_end = min(T, t_begin + seg.seg_chunks * C);
+  const int ngroups = (t_end - t_begin + C - 1) / C;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g4 = lane >> 4;
+  const bf16* xh = reinterpret_cast<const bf16*>(seg.xhat) + (size_t)bh * T * DK;
+  bf16* ob = o + ((size_t)b * T * H + h) * DV;   // + t * H * DV
+  const size_t tok_o = (size_t)H * DV;
+
+  if (w >= NCW) {
+    // ---------------- loader ----------------
+    const int lw = w - NCW;
+    // this lane's (row, unit) in each of its blocks of a group; pad units
+    // fetch unit 0 of their row (never read)
+    int rowof[NBL], offof[NBL];
+#pragma unroll
+    for (int j = 0; j < NBL; ++j) {
+      const int ib = j * NLW + lw;
+      if (ib < UXH) {
+        const int idx = 64 * ib + lane, row = idx / UXH, u = idx - row * UXH;
+        rowof[j] = row;
+        offof[j] = 8 * (u < UXH - 1 ? u : 0);
+      } else {
+        const int idx = 64 * (ib - UXH) + lane, row = idx / UOT, u = idx - row * UOT;
+        rowof[j] = row;
+        offof[j] = 8 * (u < UOT - 1 ? u : 0);
+      }
+    }
+    auto issue = [&](int g) {
+      bf16* buf = ring[g % NBUF];
+      const int t0 = t_begin + C * g;
+#pragma unroll
+      for (int j = 0; j < NBL; ++j) {
+        const int ib = j * NLW + lw;
+        const int t = min(t0 + rowof[j], t_end - 1);   // rows past the segment: not stored
+        if (ib < UXH)
+          dma16(xh + (size_t)t * DK + offof[j], buf + 512 * ib);
+        else
+          dma16(ob + (size_t)t * tok_o + offof[j], buf + 512 * ib);
+      }
+    };
+    issue(0);
+    if (ngroups > 1) issue(1);
+    for (int g = 0; g < ngroups; ++g) {
+      // tile g complete (tile g + 1 may still be in flight)
+      if (g + 1 < ngroups)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (NBL & 15) | ((NBL >> 4) << 14));
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+      exec_barrier();                  // tile g visible; tile g - 1's buffer is free
+      if (g + 2 < ngroups) issue(g + 2);
+    }
+    return;
+  }
+
+  // ---------------- compute ----------------
   const int r0 = 16 * w;                         // first row of this wave
   const float* sin_row = seg.S_in + (((size_t)bh * seg.nseg + s) * DV + r0 + n) * DK;
-  const bf16* xh = reinterpret_cast<const bf16*>(seg.xhat) + (size_t)bh * T * DK;
-  bf16* ob = o + ((size_t)b * T * H + h) * DV + r0 + 4 * g4;   // + t * H * DV
-  const size_t tok_o = (size_t)H * DV;
-  // loads: S_in rows (A operand), x^ of token 16 tt + n, o of that token
-  // (tokens past the end load the last one and are not stored)
-  float4 sa[NKB][2];
+  bf16x8 As[NKB];                                // A operand: S_in[r0 + n][32 kb + 8 g4 .. + 7]
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
-    sa[kb][0] = *reinterpret_cast<const float4*>(sin_row + 32 * kb + 8 * g4);
-    sa[kb][1] = *reinterpret_cast<const float4*>(sin_row + 32 * kb + 8 * g4 + 4);
+    const float4 a = *reinterpret_cast<const float4*>(sin_row + 32 * kb + 8 * g4);
+    const float4 c = *reinterpret_cast<const float4*>(sin_row + 32 * kb + 8 * g4 + 4);
+    As[kb] = to_bf16x8(floatx8{a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w});
   }
-  uint4 xb[4][NKB];
-  uint2 ov[4];
+  for (int g = 0; g < ngroups; ++g) {
+    exec_barrier();                    // tile g loaded
+    const bf16* xs = ring[g % NBUF];
+    const bf16* os = xs + XT;
+    const int t0 = t_begin + C * g;
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    const int t = t0 + min(16 * tt + n, nvalid - 1);
+    for (int tt = 0; tt < 4; ++tt) {
+      const int c = 16 * tt + n;                 // token of this lane
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-      xb[tt][kb] = *reinterpret_cast<const uint4*>(xh + (size_t)t * DK + 32 * kb + 8 * g4);
-    ov[tt] = *reinterpret_cast<const uint2*>(ob + (size_t)t * tok_o);
-  }
-  bf16x8 As[NKB];
+      for (int kb = 0; kb < NKB; ++kb)   // k-slots d = 32 kb + 8 g4 .. + 7, as in As
+        acc = mfma(As[kb], *reinterpret_cast<const bf16x8*>(&xs[c * LDXH + 32 * kb + 8 * g4]), acc);
+      // acc[i] = O_corr[token c][row r0 + 4 g4 + i]
+      const bf16x4 old = *reinterpret_cast<const bf16x4*>(&os[c * LDOT + r0 + 4 * g4]);
+      bf16x4 nv;
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-    As[kb] = to_bf16x8(floatx8{sa[kb][0].x, sa[kb][0].y, sa[kb][0].z, sa[kb][0].w,
-                               sa[kb][1].x, sa[kb][1].y, sa[kb][1].z, sa[kb][1].w});
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) acc = mfma(As[kb], __builtin_bit_cast(bf16x8, xb[tt][kb]), acc);
-    // acc[i] = O_corr[token 16 tt + n][row r0 + 4 g4 + i]
-    const bf16x4 old = __builtin_bit_cast(bf16x4, ov[tt]);
-    bf16x4 nv;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) nv[i] = (bf16)((float)old[i] + acc[i]);
-    if (16 * tt + n < nvalid)
-      *reinterpret_cast<uint2*>(ob + (size_t)(t0 + 16 * tt + n) * tok_o) = __builtin_bit_cast(uint2, nv);
+      for (int i = 0; i < 4; ++i) nv[i] = (bf16)((float)old[i] + acc[i]);
+      if (t0 + c < t_end)
+        *reinterpret_cast<bf16x4*>(ob + (size_t)(t0 + c) * tok_o + r0 + 4 * g4) = nv;
+    }
   }
 }
 
@@ -1302,14 +1364,15 @@ static void launch_segment_tail(const SegArgs& seg, void* o, float* ST, int B,
   hipLaunchKernelGGL((segment_combine_kernel<DK>),
                      dim3(B * H * (dv / (16 * kCombineWaves))), dim3(64 * kCombineWaves),
                      0, stream, seg, ST, dv);
-  const int nlater = (T + C - 1) / C - seg.seg_chunks;   // chunks of segments >= 1
-  const dim3 grid(nlater * B * H);
+  const dim3 grid(B * H * (seg.nseg - 1));
   if (dv == 128)
-    hipLaunchKernelGGL((segment_correct_kernel<DK, 128>), grid, dim3(4 * 128), 0, stream,
-                       seg, static_cast<bf16*>(o), T, H, nlater);
+    hipLaunchKernelGGL((segment_correct_kernel<DK, 128>), grid,
+                       dim3(64 * (128 / 16 + kCorrLoaders)), 0, stream, seg,
+                       static_cast<bf16*>(o), T, H);
   else
-    hipLaunchKernelGGL((segment_correct_kernel<DK, 64>), grid, dim3(4 * 64), 0, stream,
-                       seg, static_cast<bf16*>(o), T, H, nlater);
+    hipLaunchKernelGGL((segment_correct_kernel<DK, 64>), grid,
+                       dim3(64 * (64 / 16 + kCorrLoaders)), 0, stream, seg,
+                       static_cast<bf16*>(o), T, H);
 }
 
 hipError_t launch_prefill_scan(const void* q, const void* k, const void* v,
