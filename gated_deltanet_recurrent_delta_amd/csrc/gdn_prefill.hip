@@ -1057,87 +1057,107 @@ hipError_t launch_prefill_prepare(const void* q, const void* k,
   return hipGetLastError();
 }
 
+// Workgroup execution barrier without a memory fence: orders this wave's
+// memory accesses in the compiler only.  Data handed over through it must
+// already be complete (here: an explicit wait on the loads that fill LDS),
+// and nothing before it waits on this wave's outstanding memory operations.
+__device__ __forceinline__ void exec_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ===========================================================================
 // segment combine (phase 2): S_in(s) = S_end(s-1), S_end(s) = S_in(s) X_s + S_loc(s)
 // ===========================================================================
 
 // One workgroup per (batch, head, 16 NWC state rows), sequential over the
-// segments; wave w carries 16 rows as S^T tiles.  X_s arrives from the scan
-// as X^T split into bf16 hi and lo parts, so it is loaded straight into LDS
-// (padded rows, direct loads; X_{s+1} while step s computes) and read as
-// MFMA operands by rows; the state side is split into hi/lo in registers.
-// S_loc(s+1) is loaded into registers at the end of step s.
-#ifndef GDN_COMBINE_WAVES
-#define GDN_COMBINE_WAVES 2
-#endif
-constexpr int kCombineWaves = GDN_COMBINE_WAVES;
+// segments, in two roles:
+//  * NLC loader waves move X_{s+1} (the scan stores X as X^T split into bf16
+//    hi and lo parts) straight from global memory into the LDS buffer not in
+//    use while step s computes, and wait on their own loads exactly.
+//  * NWC compute waves (wave w: 16 rows as S^T tiles) read X_s from LDS by
+//    rows as MFMA operands against the hi/lo split of S_in(s), add S_loc(s)
+//    (loaded at the start of the step and waited on only at its end), and
+//    store S_in(s) for the correction pass.
+// The roles pass fence-free execution barriers, one per step.
+constexpr int kCombineWaves = 2;
+constexpr int kCombineLoaders = 2;
 
 template <int DK>
-__global__ __launch_bounds__(64 * kCombineWaves) void segment_combine_kernel(
+__global__ __launch_bounds__(64 * (kCombineWaves + kCombineLoaders)) void segment_combine_kernel(
     SegArgs seg, float* ST, int DV) {
-  constexpr int NWC = kCombineWaves;
+  constexpr int NWC = kCombineWaves, NLC = kCombineLoaders;
   constexpr int NDT = DK / 16, NKB = DK / 32;
   constexpr int LDX = DK + 8, UX = LDX / 8;     // padded row, 16-byte units
   constexpr int XT = DK * LDX;                  // elements of one part (hi or lo)
   constexpr int NBX = 2 * DK * UX / 64;         // 1 KB load blocks of hi + lo
-  __shared__ __attribute__((aligned(16))) bf16 xb0[2 * XT];
-  __shared__ __attribute__((aligned(16))) bf16 xb1[2 * XT];
+  static_assert(NBX % NLC == 0 && NBX / NLC <= 63, "load blocks split over the loaders");
+  constexpr int NBL = NBX / NLC;
+  __shared__ __attribute__((aligned(16))) bf16 xbuf[2][2 * XT];
   const int NRG = DV / (16 * NWC);
   const int bh = blockIdx.x / NRG, rg = blockIdx.x - bh * NRG;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g4 = lane >> 4;
+
+  if (w >= NWC) {
+    // ---------------- loader ----------------
+    const int lw = w - NWC;
+    int offof[NBL];                               // element offset in the hi/lo pair
+#pragma unroll
+    for (int j = 0; j < NBL; ++j) {
+      const int idx = 64 * (j * NLC + lw) + lane, m = idx / (DK * UX), rm = idx - m * (DK * UX);
+      const int d = rm / UX, u = rm - d * UX;
+      offof[j] = m * DK * DK + d * DK + 8 * (u < UX - 1 ? u : 0);   // pad units: unit 0
+    }
+    auto issue = [&](int s) {
+      const bf16* src = reinterpret_cast<const bf16*>(seg.X_fin) +
+                        ((size_t)bh * seg.nseg + s) * 2 * DK * DK;
+      bf16* X = xbuf[(s - 1) & 1];
+#pragma unroll
+      for (int j = 0; j < NBL; ++j) dma16(src + offof[j], X + 512 * (j * NLC + lw));
+    };
+    issue(1);
+    for (int s = 1; s < seg.nseg; ++s) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): X_s
+      exec_barrier();                           // X_s visible; X_{s-1}'s buffer free
+      if (s + 1 < seg.nseg) issue(s + 1);
+    }
+    return;
+  }
+
+  // ---------------- compute ----------------
   const int row = rg * 16 * NWC + 16 * w + n;   // this lane's state row
   auto srow = [&](float* base, int s) {
     return base + (((size_t)bh * seg.nseg + s) * DV + row) * DK;
   };
-  // X^T hi/lo of segment s into buffer X: part m, row d, unit u (pad units
-  // fetch unit 0 of the row and are never read)
-  auto issue = [&](bf16* X, int s) {
-    const bf16* src0 = reinterpret_cast<const bf16*>(seg.X_fin) +
-                       ((size_t)bh * seg.nseg + s) * 2 * DK * DK;
-    static_assert(NBX % NWC == 0, "load blocks split evenly over the waves");
+  floatx4 S[NDT];
 #pragma unroll
-    for (int j = 0; j < NBX / NWC; ++j) {     // (fixed trip count: unrolled)
-      const int ib = j * NWC + w;
-      const int idx = 64 * ib + lane, m = idx / (DK * UX), rm = idx - m * (DK * UX);
-      const int d = rm / UX, u = rm - d * UX;
-      dma16(src0 + (size_t)m * DK * DK + (size_t)d * DK + 8 * (u < UX - 1 ? u : 0),
-            X + 512 * ib);
-    }
-  };
-  auto load_loc = [&](floatx4* Lr, int s) {
+  for (int dt = 0; dt < NDT; ++dt) {
+    const float4 x = *reinterpret_cast<const float4*>(srow(seg.S_fin, 0) + 16 * dt + 4 * g4);
+    S[dt] = floatx4{x.x, x.y, x.z, x.w};
+  }
+  for (int s = 1; s < seg.nseg; ++s) {
+    exec_barrier();                             // X_s loaded
+    floatx4 L[NDT];                             // S_loc(s), used at the end
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const float4 x = *reinterpret_cast<const float4*>(srow(seg.S_fin, s) + 16 * dt + 4 * g4);
-      Lr[dt] = floatx4{x.x, x.y, x.z, x.w};
+      L[dt] = floatx4{x.x, x.y, x.z, x.w};
     }
-  };
-
-  floatx4 S[NDT], L[NDT];
-  load_loc(S, 0);
-  issue(xb0, 1);
-  load_loc(L, 1);
-  // S_end(s) = S_in(s) X_s + S_loc(s) from buffer X (X_s loaded); prefetch
-  // X_{s+1} into Nx
-  auto step = [&](const bf16* X, bf16* Nx, int s) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's loads of X
-    __syncthreads();                          // everyone's loads of X; Nx is free
-    if (s + 1 < seg.nseg) issue(Nx, s + 1);
-    // S_in(s) for the correction pass (stored after the wait, so that it is
-    // never waited on in the step that issues it)
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+    for (int dt = 0; dt < NDT; ++dt)            // S_in(s) for the correction pass
       *reinterpret_cast<float4*>(srow(seg.S_in, s) + 16 * dt + 4 * g4) =
           make_float4(S[dt][0], S[dt][1], S[dt][2], S[dt][3]);
-    floatx4 acc[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[dt] = L[dt];
     bf16x8 Sh[NKB], Sl[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) split8(acc_slots(S[2 * kb], S[2 * kb + 1]), Sh[kb], Sl[kb]);
-    const bf16* Xh = X;
-    const bf16* Xl = X + XT;
+    const bf16* Xh = xbuf[(s - 1) & 1];
+    const bf16* Xl = Xh + XT;
+    floatx4 acc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
     // k-block outer: the NDT accumulators are independent MFMA chains
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -1151,13 +1171,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void segment_combine_kernel(
       }
     }
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) S[dt] = acc[dt];
-    // S_loc(s+1), waited on at the next step's wait
-    if (s + 1 < seg.nseg) load_loc(L, s + 1);
-  };
-  for (int s = 1; s < seg.nseg; s += 2) {
-    step(xb0, xb1, s);
-    if (s + 1 < seg.nseg) step(xb1, xb0, s + 1);
+    for (int dt = 0; dt < NDT; ++dt) S[dt] = acc[dt] + L[dt];
   }
   if (ST != nullptr) {
 #pragma unroll
@@ -1185,15 +1199,6 @@ __global__ __launch_bounds__(64 * kCombineWaves) void segment_combine_kernel(
 // the same barriers, one per tile.  Single-pass bf16 (outputs are bf16).
 constexpr int kCorrLoaders = 2;
 
-// Workgroup execution barrier without a memory fence: orders this wave's
-// memory accesses in the compiler only.  Data handed over through it must
-// already be complete (here: an explicit wait on the loads that fill LDS),
-// and nothing before it waits on this wave's outstanding memory operations.
-__device__ __forceinline__ void exec_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 template <int DK, int DV>
 __global__ __launch_bounds__(64 * (DV / 16 + kCorrLoaders)) void segment_correct_kernel(
@@ -1362,8 +1367,8 @@ template <int DK>
 static void launch_segment_tail(const SegArgs& seg, void* o, float* ST, int B,
                                 int T, int H, int dv, hipStream_t stream) {
   hipLaunchKernelGGL((segment_combine_kernel<DK>),
-                     dim3(B * H * (dv / (16 * kCombineWaves))), dim3(64 * kCombineWaves),
-                     0, stream, seg, ST, dv);
+                     dim3(B * H * (dv / (16 * kCombineWaves))),
+                     dim3(64 * (kCombineWaves + kCombineLoaders)), 0, stream, seg, ST, dv);
   const dim3 grid(B * H * (seg.nseg - 1));
   if (dv == 128)
     hipLaunchKernelGGL((segment_correct_kernel<DK, 128>), grid,
