@@ -33,6 +33,26 @@ int check_prefill_shape(int B, int T, int H, int dk, int dv, int in_dtype,
   return GDN_OK;
 }
 
+// Validation and launch of the prepare phase.  write_pl: also store the lo
+// part of P, which only the fp32-output scan reads.
+int prepare_checked(const void* q, const void* k, const float* alpha,
+                    const float* beta, int B, int T, int H, int dk, int dv,
+                    int in_dtype, bool write_pl, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int st = check_prefill_shape(B, T, H, dk, dv, in_dtype, GDN_F32);
+  if (st != GDN_OK) return st;
+  if (T == 0) return GDN_OK;
+  if (!q || !k || !alpha || !beta) return GDN_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(alpha, 4) ||
+      !aligned(beta, 4))
+    return GDN_EINVAL;
+  if (!workspace || !aligned(workspace, 16)) return GDN_EWORKSPACE;
+  if (workspace_bytes < prefill_ws_bytes(B, T, H, dk, dv)) return GDN_EWORKSPACE;
+  return to_status(gdn::launch_prefill_prepare(
+      q, k, alpha, beta, static_cast<float*>(workspace), B, T, H, dk, in_dtype,
+      write_pl, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -72,18 +92,9 @@ int gdn_prefill_prepare(const void* q, const void* k, const float* alpha,
                         const float* beta, int B, int T, int H, int dk, int dv,
                         int in_dtype, void* workspace, size_t workspace_bytes,
                         void* stream) {
-  int st = check_prefill_shape(B, T, H, dk, dv, in_dtype, GDN_F32);
-  if (st != GDN_OK) return st;
-  if (T == 0) return GDN_OK;
-  if (!q || !k || !alpha || !beta) return GDN_EINVAL;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(alpha, 4) ||
-      !aligned(beta, 4))
-    return GDN_EINVAL;
-  if (!workspace || !aligned(workspace, 16)) return GDN_EWORKSPACE;
-  if (workspace_bytes < prefill_ws_bytes(B, T, H, dk, dv)) return GDN_EWORKSPACE;
-  return to_status(gdn::launch_prefill_prepare(
-      q, k, alpha, beta, static_cast<float*>(workspace), B, T, H, dk, in_dtype,
-      static_cast<hipStream_t>(stream)));
+  // the scan may follow with either output dtype: keep every tile
+  return prepare_checked(q, k, alpha, beta, B, T, H, dk, dv, in_dtype, true,
+                         workspace, workspace_bytes, stream);
 }
 
 int gdn_prefill_scan(const void* q, const void* k, const void* v,
@@ -128,8 +139,8 @@ int gdn_prefill(const void* q, const void* k, const void* v,
     const size_t nstate = (size_t)B * H * dv * dk;
     if (ST && S0 && ST != S0 && (ST < S0 + nstate && S0 < ST + nstate))
       return GDN_EINVAL;
-    st = gdn_prefill_prepare(q, k, alpha, beta, B, T, H, dk, dv, in_dtype,
-                             workspace, workspace_bytes, stream);
+    st = prepare_checked(q, k, alpha, beta, B, T, H, dk, dv, in_dtype,
+                         out_dtype == GDN_F32, workspace, workspace_bytes, stream);
     if (st != GDN_OK) return st;
   }
   return gdn_prefill_scan(q, k, v, S0, o, ST, B, T, H, dk, dv, in_dtype,

@@ -30,30 +30,54 @@ __device__ __forceinline__ void split_bf16(float x, bf16& hi, bf16& lo) {
   lo = (bf16)(x - (float)hi);
 }
 
+// Two values rounded to bf16 by one packed conversion: hi2 holds the pair,
+// ha and hb the same two roundings as fp32 (exact: a bf16 is the top half
+// of an fp32), taken from the packed word by a shift and a mask.
+__device__ __forceinline__ void round_pair(float a, float b, uint32_t& hi2,
+                                           float& ha, float& hb) {
+  typedef float floatx2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const floatx2 p = {a, b};
+  hi2 = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
+  ha = __builtin_bit_cast(float, hi2 << 16);
+  hb = __builtin_bit_cast(float, hi2 & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float floatx2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const floatx2 p = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
+}
+
 __device__ __forceinline__ void split8(const floatx8& x, bf16x8& hi,
                                        bf16x8& lo) {
+  uint32_t h[4], l[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    bf16 h = (bf16)x[j];
-    hi[j] = h;
-    lo[j] = (bf16)(x[j] - (float)h);
+  for (int j = 0; j < 4; ++j) {
+    float ha, hb;
+    round_pair(x[2 * j], x[2 * j + 1], h[j], ha, hb);
+    l[j] = pack_bf16x2(x[2 * j] - ha, x[2 * j + 1] - hb);
   }
+  hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+  lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
 }
 
 __device__ __forceinline__ void split4(const float* x, bf16x4& hi, bf16x4& lo) {
+  uint32_t h[2], l[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    bf16 h = (bf16)x[j];
-    hi[j] = h;
-    lo[j] = (bf16)(x[j] - (float)h);
+  for (int j = 0; j < 2; ++j) {
+    float ha, hb;
+    round_pair(x[2 * j], x[2 * j + 1], h[j], ha, hb);
+    l[j] = pack_bf16x2(x[2 * j] - ha, x[2 * j + 1] - hb);
   }
+  hi = __builtin_bit_cast(bf16x4, make_uint2(h[0], h[1]));
+  lo = __builtin_bit_cast(bf16x4, make_uint2(l[0], l[1]));
 }
 
 __device__ __forceinline__ bf16x8 to_bf16x8(const floatx8& x) {
-  bf16x8 r;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) r[j] = (bf16)x[j];
-  return r;
+  return __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                               pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])));
 }
 
 // Load 4 consecutive input elements (bf16 or f32) as float4.

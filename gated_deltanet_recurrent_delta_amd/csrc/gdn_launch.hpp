@@ -89,10 +89,11 @@ hipError_t launch_decode(const void* q, const void* k, const void* v,
                          int dk, int dv, int in_dtype, int out_dtype,
                          hipStream_t stream);
 
+// write_pl: also store the lo part of P (read only when outputs are fp32).
 hipError_t launch_prefill_prepare(const void* q, const void* k,
                                   const float* alpha, const float* beta,
                                   float* ws, int B, int T, int H, int dk,
-                                  int in_dtype, hipStream_t stream);
+                                  int in_dtype, bool write_pl, hipStream_t stream);
 
 // Phase 1 (+ phases 2 and 3 when the plan segments the sequence).  `ws` is
 // the whole workspace (per-chunk tiles first, then the segment buffers).

@@ -60,10 +60,6 @@ constexpr int kWsPl = 24576;                // bf16 [64][64] lo part of P
 constexpr int kWsG = 32768;                 // fp32 [4][64]: g, beta, gamma, e^{g_C - g}
 static_assert(kWsG + 4 * 4 * C == kChunkWsFloats * 4, "workspace layout");
 
-// The 10 lower-triangular 16x16 tiles (mi >= ni) of a 64x64 matrix.
-__device__ __constant__ int kLowerMi[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__device__ __constant__ int kLowerNi[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4v_t;
 
@@ -133,17 +129,32 @@ __device__ __forceinline__ void load_row8(const float* p, bf16x8& hi, bf16x8& lo
 // prepare: one wave per chunk
 // ===========================================================================
 
+// Index of the strictly lower 16x16 tile (mi > ni) among the six of a 64x64
+// matrix: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2).
+__device__ __forceinline__ constexpr int lower_tile(int mi, int ni) {
+  return mi * (mi - 1) / 2 + ni;
+}
+
+// The chunk products are formed in row orientation: for a 16x16 tile
+// (mi, ni) lane (n, g4) holds element [16 mi + n][16 ni + 4 g4 + e],
+// e = 0..3 (the MFMA computes K_ni K_mi^T, whose lane layout is that of the
+// transposed tile).  A lane thus holds four consecutive columns of one row:
+// P leaves with one 8-byte store per tile, and the off-diagonal tiles of A
+// are, as they stand, the A operand of the fp32 MFMAs that build T.  Only T
+// (with A's diagonal blocks before it) passes through LDS, 17.9 KB per
+// wave, so eight waves share a CU and one wave's loads overlap another's
+// arithmetic.
 template <int DK, typename TIn>
 __global__ __launch_bounds__(64) void prepare_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k,
     const float* __restrict__ alpha, const float* __restrict__ beta,
-    float* __restrict__ ws, int T, int H, int nchunks) {
+    float* __restrict__ ws, int T, int H, int nchunks, int write_pl) {
   constexpr bool SPLIT = std::is_same<TIn, float>::value;  // inputs not bf16
   constexpr int NKB = DK / 32;
-  constexpr int LDA = C + 4;            // fp32 row stride of A, P and T
-  __shared__ __attribute__((aligned(16))) float As[C * LDA];
-  __shared__ __attribute__((aligned(16))) float PTs[C * LDA];   // P, then T
-  __shared__ float g2s[C], bs[C];
+  constexpr int LDA = C + 4;            // fp32 row stride of the T tile
+  __shared__ __attribute__((aligned(16))) float Ts[C * LDA];   // A's diagonal blocks, then T
+  __shared__ __attribute__((aligned(16))) float g2s[C];
+  __shared__ float bs[C];
 
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int t0 = chunk * C;
@@ -194,57 +205,62 @@ __global__ __launch_bounds__(64) void prepare_kernel(
     Gw[2 * C + lane] = expf(g);
     Gw[3 * C + lane] = expf(glast - g);
   }
-  // zero the strictly upper tiles of P (T's are written from Tt later)
-  for (int e = lane; e < C * C / 4; e += 64) {
-    const int j = (4 * e) / C, i0 = (4 * e) % C;
-    if ((i0 >> 4) > (j >> 4))
-      *reinterpret_cast<float4*>(&PTs[j * LDA + i0]) = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
   __syncthreads();
 
-  // 3. lower tiles of K K^T (-> A) and Q K^T (-> P)
+  // 3. lower tiles of A (decay- and beta-weighted K K^T, strictly lower) and
+  //    of P (decay-masked Q K^T), row orientation; P straight to the
+  //    workspace, its strictly upper tiles as zeros.
+  floatx4 Ao[6];
 #pragma unroll
-  for (int t = 0; t < 10; ++t) {
-    const int mi = kLowerMi[t], ni = kLowerNi[t];
-    floatx4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+  for (int mi = 0; mi < 4; ++mi) {
+    const int j = 16 * mi + n;                // row of this lane
+    const float gj = g2s[j], bj = bs[j];
 #pragma unroll
-    for (int s = 0; s < NKB; ++s) {
-      ak = mfma(Kh[mi][s], Kh[ni][s], ak);
-      aq = mfma(Qh[mi][s], Kh[ni][s], aq);
-      if constexpr (SPLIT) {
-        ak = mfma(Kh[mi][s], Kl[ni][s], ak);
-        ak = mfma(Kl[mi][s], Kh[ni][s], ak);
-        aq = mfma(Qh[mi][s], Kl[ni][s], aq);
-        aq = mfma(Ql[mi][s], Kh[ni][s], aq);
+    for (int ni = 0; ni <= mi; ++ni) {
+      floatx4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NKB; ++s) {
+        ak = mfma(Kh[ni][s], Kh[mi][s], ak);
+        aq = mfma(Kh[ni][s], Qh[mi][s], aq);
+        if constexpr (SPLIT) {
+          ak = mfma(Kl[ni][s], Kh[mi][s], ak);
+          ak = mfma(Kh[ni][s], Kl[mi][s], ak);
+          aq = mfma(Kl[ni][s], Qh[mi][s], aq);
+          aq = mfma(Kh[ni][s], Ql[mi][s], aq);
+        }
       }
-    }
-    const int i = 16 * ni + n;
-    const float gi2 = g2s[i];
+      const int i0 = 16 * ni + 4 * g4;        // first column of this lane
+      const float4 gi4 = *reinterpret_cast<const float4*>(&g2s[i0]);
+      const float gi[4] = {gi4.x, gi4.y, gi4.z, gi4.w};
+      float a[4], p[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = 16 * mi + 4 * g4 + e;
-      const float decay = (i <= j) ? __builtin_amdgcn_exp2f(g2s[j] - gi2) : 0.f;
-      As[j * LDA + i] = (i < j) ? bs[j] * decay * ak[e] : 0.f;
-      PTs[j * LDA + i] = decay * aq[e];
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + e;
+        const float decay = (i <= j) ? __builtin_amdgcn_exp2f(gj - gi[e]) : 0.f;
+        a[e] = (i < j) ? bj * decay * ak[e] : 0.f;
+        p[e] = decay * aq[e];
+      }
+      bf16x4 ph, pl;
+      split4(p, ph, pl);
+      *reinterpret_cast<bf16x4*>(wsc + kWsPh + (j * C + i0) * 2) = ph;
+      if (write_pl) *reinterpret_cast<bf16x4*>(wsc + kWsPl + (j * C + i0) * 2) = pl;
+      if (ni == mi)
+        *reinterpret_cast<float4*>(&Ts[j * LDA + i0]) = make_float4(a[0], a[1], a[2], a[3]);
+      else
+        Ao[lower_tile(mi, ni)] = floatx4{a[0], a[1], a[2], a[3]};
+    }
+    const bf16x4 zero4 = {};
+#pragma unroll
+    for (int ni = mi + 1; ni < 4; ++ni) {
+      *reinterpret_cast<bf16x4*>(wsc + kWsPh + (j * C + 16 * ni + 4 * g4) * 2) = zero4;
+      if (write_pl) *reinterpret_cast<bf16x4*>(wsc + kWsPl + (j * C + 16 * ni + 4 * g4) * 2) = zero4;
     }
   }
   __syncthreads();
 
-  // 4. P -> workspace as bf16 hi/lo (row j, 8 columns per store)
-  for (int e = lane; e < C * C / 8; e += 64) {
-    const int j = (8 * e) / C, i0 = (8 * e) % C;
-    const float4 a0 = *reinterpret_cast<const float4*>(&PTs[j * LDA + i0]);
-    const float4 a1 = *reinterpret_cast<const float4*>(&PTs[j * LDA + i0 + 4]);
-    const floatx8 x = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-    bf16x8 hi, lo;
-    split8(x, hi, lo);
-    *reinterpret_cast<bf16x8*>(wsc + kWsPh + (j * C + i0) * 2) = hi;
-    *reinterpret_cast<bf16x8*>(wsc + kWsPl + (j * C + i0) * 2) = lo;
-  }
-  __syncthreads();
-  float* Tt = PTs;                 // P is written out; reuse for T
-
-  // 5. T = (I + A)^{-1}.  Diagonal blocks: lane (block g4, column n).
+  // 4. T = (I + A)^{-1}.  Diagonal blocks by forward substitution, lane
+  //    (block g4, column n), reading A's diagonal block from Ts and then
+  //    overwriting it with T's.
   {
     const int base = 16 * g4, c = n;
     float tcol[16];
@@ -253,27 +269,28 @@ __global__ __launch_bounds__(64) void prepare_kernel(
       float acc0 = (j == c) ? 1.f : 0.f, acc1 = 0.f;
 #pragma unroll
       for (int i = 0; i < j; i += 2) {
-        acc0 -= As[(base + j) * LDA + base + i] * tcol[i];
-        if (i + 1 < j) acc1 -= As[(base + j) * LDA + base + i + 1] * tcol[i + 1];
+        acc0 -= Ts[(base + j) * LDA + base + i] * tcol[i];
+        if (i + 1 < j) acc1 -= Ts[(base + j) * LDA + base + i + 1] * tcol[i + 1];
       }
       tcol[j] = acc0 + acc1;
     }
+    __syncthreads();                          // every lane has read its block of A
 #pragma unroll
-    for (int j = 0; j < 16; ++j) Tt[(base + j) * LDA + base + c] = tcol[j];
+    for (int j = 0; j < 16; ++j) Ts[(base + j) * LDA + base + c] = tcol[j];
     // zero the strictly upper blocks of T
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj)
       if (bj > g4)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) Tt[(base + j) * LDA + 16 * bj + c] = 0.f;
+        for (int j = 0; j < 16; ++j) Ts[(base + j) * LDA + 16 * bj + c] = 0.f;
   }
   __syncthreads();
   // Off-diagonal blocks, nearest the diagonal first:
   //   T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj   (i > j, 16x16 blocks)
   // on fp32 MFMA (16x16x4, exact fp32 products).  A step kk of a 16x16x16
-  // product contracts over k = 4 g4 + kk, so the accumulator of the first
-  // product (lane holds rows 4 g4 + i) is the B operand of the second one
-  // without any data movement.
+  // product contracts over k = 4 g4 + kk: the row-oriented A tiles supply
+  // the A operand as they are, and the accumulator of the first product
+  // (lane holds rows 4 g4 + i) is the B operand of the second one.
 #pragma unroll
   for (int dist = 1; dist < 4; ++dist) {
 #pragma unroll
@@ -284,28 +301,27 @@ __global__ __launch_bounds__(64) void prepare_kernel(
       for (int bk = bj; bk < bi; ++bk) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const float x = As[(16 * bi + n) * LDA + 16 * bk + 4 * g4 + kk];
-          const float y = Tt[(16 * bk + 4 * g4 + kk) * LDA + 16 * bj + n];
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, acc, 0, 0, 0);
+          const float y = Ts[(16 * bk + 4 * g4 + kk) * LDA + 16 * bj + n];
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Ao[lower_tile(bi, bk)][kk], y, acc, 0, 0, 0);
         }
       }
       floatx4 out = {0.f, 0.f, 0.f, 0.f};
+      const float4 tii = *reinterpret_cast<const float4*>(&Ts[(16 * bi + n) * LDA + 16 * bi + 4 * g4]);
+      const float tv[4] = {tii.x, tii.y, tii.z, tii.w};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const float x = Tt[(16 * bi + n) * LDA + 16 * bi + 4 * g4 + kk];
-        out = __builtin_amdgcn_mfma_f32_16x16x4f32(x, acc[kk], out, 0, 0, 0);
-      }
+      for (int kk = 0; kk < 4; ++kk)
+        out = __builtin_amdgcn_mfma_f32_16x16x4f32(tv[kk], acc[kk], out, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Tt[(16 * bi + 4 * g4 + i) * LDA + 16 * bj + n] = -out[i];
+      for (int i = 0; i < 4; ++i) Ts[(16 * bi + 4 * g4 + i) * LDA + 16 * bj + n] = -out[i];
     }
     __syncthreads();
   }
 
-  // 6. T -> workspace as bf16 hi/lo
+  // 5. T -> workspace as bf16 hi/lo
   for (int e = lane; e < C * C / 8; e += 64) {
     const int j = (8 * e) / C, i0 = (8 * e) % C;
-    const float4 a0 = *reinterpret_cast<const float4*>(&Tt[j * LDA + i0]);
-    const float4 a1 = *reinterpret_cast<const float4*>(&Tt[j * LDA + i0 + 4]);
+    const float4 a0 = *reinterpret_cast<const float4*>(&Ts[j * LDA + i0]);
+    const float4 a1 = *reinterpret_cast<const float4*>(&Ts[j * LDA + i0 + 4]);
     const floatx8 x = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
     bf16x8 hi, lo;
     split8(x, hi, lo);
@@ -735,36 +751,78 @@ __global__ __launch_bounds__(64 * (DV + DK) / (16 * NH), 1) void scan_wide_kerne
   const size_t tok_k = (size_t)H * DK, tok_v = (size_t)H * DV;
 
   // Issue this wave's share of the load blocks of `chunk` into buffer X.
-  // A lane whose 16 bytes land on a pad unit fetches the row's first unit
-  // (never read).  Token rows past the end of the sequence load the last
-  // valid row: their beta is 0 and their decay 1, so they contribute
-  // nothing (finite values times zero) and their outputs are not stored.
+  // Every wave takes the same number of blocks of each tile (block
+  // w + NW j): their types are known at compile time, the code is
+  // branch-free, and K, Q (and V, when its rows have the same length) share
+  // one row/unit computation.  The few blocks left over, and the gate block,
+  // go one per wave.  A lane whose 16 bytes land on a pad unit fetches the
+  // row's first unit (never read).  Token rows past the end of the sequence
+  // load the last valid row: their beta is 0 and their decay 1, so they
+  // contribute nothing (finite values times zero) and their outputs are not
+  // stored.
+  constexpr int MK = NBK / NW, MT = NBT / NW, MV = NBV / NW;   // blocks per wave
+  constexpr int EK = NBK - NW * MK, ET = NBT - NW * MT, EV = NBV - NW * MV;
+  constexpr int NE = 2 * EK + ET + EV + 1;                      // left over
   auto issue = [&](bf16* X, int chunk) {
     const int t0 = chunk * C;
     const int last = min(C, T - t0) - 1;
     const char* wsc = reinterpret_cast<const char*>(ws) +
                       ((size_t)bh * nchunks + chunk) * kChunkWsFloats * 4;
-    for (int ib = w; ib < NB; ib += NW) {
-      const bf16* src;
-      bf16* dst = X + 512 * ib;               // blocks tile the buffer in order
-      if (ib < 2 * NBK) {                     // K, then Q
-        const int jb = ib < NBK ? ib : ib - NBK;
-        const int idx = 64 * jb + lane, row = idx / UK, u = idx - row * UK;
-        src = (ib < NBK ? k_seq : q_seq) + (size_t)(t0 + min(row, last)) * tok_k +
-              8 * (u < UK - 1 ? u : 0);
-      } else if (ib < 2 * NBK + NBT) {        // T hi, T lo, P hi
-        const int idx = 64 * (ib - 2 * NBK) + lane;
-        const int m = idx / (C * UT), rm = idx - m * (C * UT);
-        const int row = rm / UT, u = rm - row * UT;
-        src = reinterpret_cast<const bf16*>(wsc + m * (C * C * 2) + row * (C * 2) +
-                                            16 * (u < UT - 1 ? u : 0));
-      } else if (ib < 2 * NBK + NBT + NBV) {  // V
-        const int idx = 64 * (ib - 2 * NBK - NBT) + lane, row = idx / UV, u = idx - row * UV;
-        src = v_seq + (size_t)(t0 + min(row, last)) * tok_v + 8 * (u < UV - 1 ? u : 0);
-      } else {                                // gates
-        src = reinterpret_cast<const bf16*>(wsc + kWsG + 16 * lane);
+    const bf16* kc = k_seq + (size_t)t0 * tok_k;
+    const bf16* qc = q_seq + (size_t)t0 * tok_k;
+    const bf16* vc = v_seq + (size_t)t0 * tok_v;
+    // The per-lane offsets below do not depend on the chunk; an opaque copy
+    // of the lane index keeps the compiler from hoisting them out of the
+    // chunk loop, where they would take registers the compute needs.
+    unsigned ln = lane;
+    asm volatile("" : "+v"(ln));
+    const unsigned lastu = last;
+    // element offset, from the chunk's first row, of lane's unit in block jb
+    // of a tile with U units per row and a row stride of tok elements
+    auto row_off = [&](unsigned jb, unsigned U, unsigned tok) -> unsigned {
+      const unsigned idx = 64 * jb + ln, row = idx / U, u = idx - row * U;
+      return min(row, lastu) * tok + 8 * (u < U - 1 ? u : 0);
+    };
+    // byte offset in the chunk's workspace of lane's unit in block jt of the
+    // T hi / T lo / P hi tiles
+    auto tp_off = [&](unsigned jt) -> unsigned {
+      const unsigned idx = 64 * jt + ln;
+      const unsigned m = idx / (C * UT), rm = idx - m * (C * UT);
+      const unsigned row = rm / UT, u = rm - row * UT;
+      return m * (C * C * 2) + row * (C * 2) + 16 * (u < UT - 1 ? u : 0);
+    };
+#pragma unroll
+    for (int j = 0; j < MK; ++j) {
+      const int jb = w + NW * j;
+      const unsigned off = row_off(jb, UK, tok_k);
+      dma16(kc + off, X + 512 * jb);
+      dma16(qc + off, X + OFF_Q + 512 * jb);
+      if constexpr (DV == DK) dma16(vc + off, X + OFF_V + 512 * jb);   // same geometry
+    }
+#pragma unroll
+    for (int j = (DV == DK ? MK : 0); j < MV; ++j) {
+      const int jb = w + NW * j;
+      dma16(vc + row_off(jb, UV, tok_v), X + OFF_V + 512 * jb);
+    }
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+      const int jt = w + NW * j;
+      dma16(wsc + tp_off(jt), X + OFF_T + 512 * jt);
+    }
+    for (int e = w; e < NE; e += NW) {
+      if (e < 2 * EK) {
+        const int jb = NW * MK + (e < EK ? e : e - EK);
+        dma16((e < EK ? kc : qc) + row_off(jb, UK, tok_k),
+              X + (e < EK ? 0 : OFF_Q) + 512 * jb);
+      } else if (e < 2 * EK + ET) {
+        const int jt = NW * MT + e - 2 * EK;
+        dma16(wsc + tp_off(jt), X + OFF_T + 512 * jt);
+      } else if (e < 2 * EK + ET + EV) {
+        const int jb = NW * MV + e - 2 * EK - ET;
+        dma16(vc + row_off(jb, UV, tok_v), X + OFF_V + 512 * jb);
+      } else {
+        dma16(wsc + kWsG + 16 * ln, X + OFF_G);
       }
-      dma16(src, dst);
     }
   };
   static_assert(OFF_Q == 512 * NBK && OFF_T == 512 * 2 * NBK &&
@@ -1035,24 +1093,24 @@ hipError_t launch_state_fill(const float* S0, float* ST, size_t n,
 template <int DK, typename TIn>
 static void launch_prepare_t(const void* q, const void* k, const float* alpha,
                              const float* beta, float* ws, int B, int T, int H,
-                             hipStream_t stream) {
+                             bool write_pl, hipStream_t stream) {
   const int nchunks = (T + C - 1) / C;
   hipLaunchKernelGGL((prepare_kernel<DK, TIn>), dim3(nchunks, H, B), dim3(64),
                      0, stream, static_cast<const TIn*>(q),
                      static_cast<const TIn*>(k), alpha, beta, ws, T, H,
-                     nchunks);
+                     nchunks, write_pl ? 1 : 0);
 }
 
 hipError_t launch_prefill_prepare(const void* q, const void* k,
                                   const float* alpha, const float* beta,
                                   float* ws, int B, int T, int H, int dk,
-                                  int in_dtype, hipStream_t stream) {
+                                  int in_dtype, bool write_pl, hipStream_t stream) {
   if (in_dtype == 1) {
-    if (dk == 128) launch_prepare_t<128, bf16>(q, k, alpha, beta, ws, B, T, H, stream);
-    else launch_prepare_t<64, bf16>(q, k, alpha, beta, ws, B, T, H, stream);
+    if (dk == 128) launch_prepare_t<128, bf16>(q, k, alpha, beta, ws, B, T, H, write_pl, stream);
+    else launch_prepare_t<64, bf16>(q, k, alpha, beta, ws, B, T, H, write_pl, stream);
   } else {
-    if (dk == 128) launch_prepare_t<128, float>(q, k, alpha, beta, ws, B, T, H, stream);
-    else launch_prepare_t<64, float>(q, k, alpha, beta, ws, B, T, H, stream);
+    if (dk == 128) launch_prepare_t<128, float>(q, k, alpha, beta, ws, B, T, H, write_pl, stream);
+    else launch_prepare_t<64, float>(q, k, alpha, beta, ws, B, T, H, write_pl, stream);
   }
   return hipGetLastError();
 }
