@@ -27,7 +27,7 @@ struct SegArgs {
   int seg_chunks;    // chunks per segment (the last may be shorter)
   float* S_fin;      // [BH][nseg][dv][dk] final real-row state of each segment
   void* X_fin;       // [BH][nseg][2][dk][dk] bf16: X^T of segments >= 1, hi then lo part
-  float* S_in;       // [BH][nseg][dv][dk] incoming state of each segment
+  void* S_in;        // [BH][nseg][dv][dk] bf16: incoming state of each segment, rounded
   void* xhat;        // [BH][T][dk] bf16, x^_t for tokens of segments >= 1
 };
 
@@ -77,7 +77,7 @@ inline PrefillPlan plan_prefill(int B, int T, int H, int dk, int dv) {
     p.xfin_off = off;
     off = align256(off + BH * p.nseg * dk * dk * 4);
     p.sin_off = off;
-    off = align256(off + BH * p.nseg * dv * dk * 4);
+    off = align256(off + BH * p.nseg * dv * dk * 2);
   }
   p.total_bytes = off;
   return p;

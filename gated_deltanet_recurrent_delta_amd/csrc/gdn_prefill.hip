@@ -698,6 +698,20 @@ __device__ __forceinline__ void dma16(const void* g, void* lds_block) {
   __builtin_amdgcn_global_load_lds((glb_cvoid_t*)g, (lds_void_t*)lds_block, 16, 0, 0);
 }
 
+// Index, within one part (hi or lo) of a segment's X^T, at which the scan
+// stores element (d, e) (row d of X^T is column d of X; e is the
+// contraction index of the combine).  The combine's wave w = d / 16 feeds
+// the MFMA, for k-block kb = e / 32, lane (n = d % 16, g4) the 8 k-slots
+// e = 32 kb + 4 g4 + i and 32 kb + 16 + 4 g4 + i (i = 0..3); those are
+// stored as 16 contiguous bytes, and the 64 lanes' operands for one
+// (w, kb) as one contiguous kilobyte, so every operand load reads whole
+// cache lines.
+template <int DK>
+__device__ __forceinline__ int xfin_index(int d, int e) {
+  return ((d >> 4) * (DK / 32) + (e >> 5)) * 512 + (d & 15) * 32 + ((e >> 2) & 3) * 8 +
+         ((e >> 4) & 1) * 4 + (e & 3);
+}
+
 // The rows a segment evolves are the DV state rows and, for segments >= 1,
 // the DK transition rows (see SegArgs).  One workgroup carries all of them:
 // wave w owns rows 16 NH w .. 16 NH (w + 1) - 1 of that combined row space
@@ -1038,8 +1052,8 @@ __global__ __launch_bounds__(64 * (DV + DK) / (16 * NH), 1) void scan_wide_kerne
   }
 
   // Final rows of this segment for the combine pass: state rows as fp32,
-  // transition rows as X^T split into bf16 hi and lo parts (the combine
-  // reads X^T rows as MFMA operands).
+  // transition rows as X^T split into bf16 hi and lo parts, in the order
+  // xfin_index gives (the combine loads them as MFMA operands).
   if (active && !xrows) {
 #pragma unroll
     for (int hf = 0; hf < NH; ++hf) {
@@ -1062,8 +1076,8 @@ __global__ __launch_bounds__(64 * (DV + DK) / (16 * NH), 1) void scan_wide_kerne
           const int d = 16 * dt + 4 * g4 + i;            // column of X
           bf16 hi, lo;
           split_bf16(S[hf][dt][i], hi, lo);
-          xh[d * DK + e] = hi;
-          xl[d * DK + e] = lo;
+          xh[xfin_index<DK>(d, e)] = hi;
+          xl[xfin_index<DK>(d, e)] = lo;
         }
     }
   }
@@ -1129,114 +1143,135 @@ __device__ __forceinline__ void exec_barrier() {
 // segment combine (phase 2): S_in(s) = S_end(s-1), S_end(s) = S_in(s) X_s + S_loc(s)
 // ===========================================================================
 
-// One workgroup per (batch, head, 16 NWC state rows), sequential over the
-// segments, in two roles:
-//  * NLC loader waves move X_{s+1} (the scan stores X as X^T split into bf16
-//    hi and lo parts) straight from global memory into the LDS buffer not in
-//    use while step s computes, and wait on their own loads exactly.
-//  * NWC compute waves (wave w: 16 rows as S^T tiles) read X_s from LDS by
-//    rows as MFMA operands against the hi/lo split of S_in(s), add S_loc(s)
-//    (loaded at the start of the step and waited on only at its end), and
-//    store S_in(s) for the correction pass.
-// The roles pass fence-free execution barriers, one per step.
-constexpr int kCombineWaves = 2;
-constexpr int kCombineLoaders = 2;
-
+// One workgroup per (batch, head, 16 state rows), sequential over the
+// segments.  DK / 16 compute waves; wave w forms columns 16 w .. 16 w + 15
+// of S_end(s) = S_in(s) X_s + S_loc(s) for the 16 rows with three short
+// MFMA chains (hi x hi, hi x lo, lo x hi).  Its operand rows of X_s^T
+// (8 KB) and its S_loc tile come straight from global memory into
+// registers two segments ahead (a ring of three register sets, the loop
+// unrolled by three so every index is static), so the loads' latency is
+// hidden behind two steps.  The waves exchange the hi/lo split of S_in(s)
+// through a double-buffered LDS tile, one fence-free barrier per segment.
+// Compute waves issue no store inside the loop (their partial load waits
+// stay exact); a copier wave writes the hi part of S_in(s), i.e. S_in(s)
+// rounded to bf16, out for the correction pass.
 template <int DK>
-__global__ __launch_bounds__(64 * (kCombineWaves + kCombineLoaders)) void segment_combine_kernel(
+__global__ __launch_bounds__(64 * (DK / 16 + 1)) void segment_combine_kernel(
     SegArgs seg, float* ST, int DV) {
-  constexpr int NWC = kCombineWaves, NLC = kCombineLoaders;
-  constexpr int NDT = DK / 16, NKB = DK / 32;
-  constexpr int LDX = DK + 8, UX = LDX / 8;     // padded row, 16-byte units
-  constexpr int XT = DK * LDX;                  // elements of one part (hi or lo)
-  constexpr int NBX = 2 * DK * UX / 64;         // 1 KB load blocks of hi + lo
-  static_assert(NBX % NLC == 0 && NBX / NLC <= 63, "load blocks split over the loaders");
-  constexpr int NBL = NBX / NLC;
-  __shared__ __attribute__((aligned(16))) bf16 xbuf[2][2 * XT];
-  const int NRG = DV / (16 * NWC);
-  const int bh = blockIdx.x / NRG, rg = blockIdx.x - bh * NRG;
+  constexpr int NWC = DK / 16;
+  constexpr int NKB = DK / 32;
+  constexpr int LDE = DK + 8;                   // padded row of the exchanged S_in split
+  constexpr int ET = 16 * LDE;                  // elements of one part of it
+  constexpr int NBS = 16 * DK * 2 / 1024;       // 1 KB blocks of the 16 rows' bf16 S_in
+  __shared__ __attribute__((aligned(16))) bf16 sx[2][2 * ET];
+  // Consecutive workgroups go to different XCDs (each with its own L2).
+  // Workgroup i takes head i % BH: when BH is a multiple of the XCD count,
+  // the row groups of one head share an XCD, and its L2 serves their
+  // common reads of X.
+  const int BH = gridDim.x / (DV / 16);
+  const int bh = blockIdx.x % BH, rg = blockIdx.x / BH;
+  const int r0 = 16 * rg;                       // first state row of the workgroup
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g4 = lane >> 4;
+  const int nseg = seg.nseg;
 
-  if (w >= NWC) {
-    // ---------------- loader ----------------
-    const int lw = w - NWC;
-    int offof[NBL];                               // element offset in the hi/lo pair
+  // Steps run in groups of three (the compute loop is unrolled by three so
+  // that no load sits in a conditional branch, which would make the
+  // compiler's load-count waits drain everything); steps past the last
+  // segment pass the barrier and publish nothing.
+  const int nsteps = 3 * ((nseg - 1 + 2) / 3);
+
+  if (w == NWC) {
+    // ---------------- copier ----------------
+    for (int s = 1; s <= nsteps; ++s) {
+      exec_barrier();                           // the split of S_in(s) is in LDS
+      if (s >= nseg) continue;
 #pragma unroll
-    for (int j = 0; j < NBL; ++j) {
-      const int idx = 64 * (j * NLC + lw) + lane, m = idx / (DK * UX), rm = idx - m * (DK * UX);
-      const int d = rm / UX, u = rm - d * UX;
-      offof[j] = m * DK * DK + d * DK + 8 * (u < UX - 1 ? u : 0);   // pad units: unit 0
-    }
-    auto issue = [&](int s) {
-      const bf16* src = reinterpret_cast<const bf16*>(seg.X_fin) +
-                        ((size_t)bh * seg.nseg + s) * 2 * DK * DK;
-      bf16* X = xbuf[(s - 1) & 1];
-#pragma unroll
-      for (int j = 0; j < NBL; ++j) dma16(src + offof[j], X + 512 * (j * NLC + lw));
-    };
-    issue(1);
-    for (int s = 1; s < seg.nseg; ++s) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): X_s
-      exec_barrier();                           // X_s visible; X_{s-1}'s buffer free
-      if (s + 1 < seg.nseg) issue(s + 1);
+      for (int j = 0; j < NBS; ++j) {
+        const int idx = 64 * j + lane, row = idx / (DK / 8), u = idx - row * (DK / 8);
+        const uint4 x = *reinterpret_cast<const uint4*>(&sx[s & 1][row * LDE + 8 * u]);
+        bf16* dst = reinterpret_cast<bf16*>(seg.S_in) +
+                    (((size_t)bh * nseg + s) * DV + r0 + row) * DK + 8 * u;
+        *reinterpret_cast<uint4*>(dst) = x;
+      }
     }
     return;
   }
 
   // ---------------- compute ----------------
-  const int row = rg * 16 * NWC + 16 * w + n;   // this lane's state row
-  auto srow = [&](float* base, int s) {
-    return base + (((size_t)bh * seg.nseg + s) * DV + row) * DK;
+  // lane holds S[r0 + n][16 w + 4 g4 + i], i = 0..3 (an S^T accumulator tile)
+  auto tile = [&](int s) {
+    const float4 x = *reinterpret_cast<const float4*>(
+        seg.S_fin + (((size_t)bh * nseg + s) * DV + r0 + n) * DK + 16 * w + 4 * g4);
+    return floatx4{x.x, x.y, x.z, x.w};
   };
-  floatx4 S[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    const float4 x = *reinterpret_cast<const float4*>(srow(seg.S_fin, 0) + 16 * dt + 4 * g4);
-    S[dt] = floatx4{x.x, x.y, x.z, x.w};
-  }
-  for (int s = 1; s < seg.nseg; ++s) {
-    exec_barrier();                             // X_s loaded
-    floatx4 L[NDT];                             // S_loc(s), used at the end
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const float4 x = *reinterpret_cast<const float4*>(srow(seg.S_fin, s) + 16 * dt + 4 * g4);
-      L[dt] = floatx4{x.x, x.y, x.z, x.w};
-    }
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)            // S_in(s) for the correction pass
-      *reinterpret_cast<float4*>(srow(seg.S_in, s) + 16 * dt + 4 * g4) =
-          make_float4(S[dt][0], S[dt][1], S[dt][2], S[dt][3]);
-    bf16x8 Sh[NKB], Sl[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) split8(acc_slots(S[2 * kb], S[2 * kb + 1]), Sh[kb], Sl[kb]);
-    const bf16* Xh = xbuf[(s - 1) & 1];
-    const bf16* Xl = Xh + XT;
-    floatx4 acc[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    // k-block outer: the NDT accumulators are independent MFMA chains
+  // X_s^T row 16 w + n, k-slots of lane group g4 (xfin_index: k-block kb
+  // is 512 elements further): hi parts [0, NKB), lo parts [NKB, 2 NKB), and
+  // S_loc(s).  Segments past the end load the last
+  // one (never used), so the loads are unconditional.
+  auto load = [&](bf16x8* X, floatx4& L, int s) {
+    s = min(s, nseg - 1);
+    const bf16* src = reinterpret_cast<const bf16*>(seg.X_fin) +
+                      ((size_t)bh * nseg + s) * 2 * DK * DK + xfin_index<DK>(16 * w + n, 4 * g4);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const bf16x8 ah = lds_slots(Xh, LDX, 16 * dt + n, kb, g4);   // X^T[16 dt + n][e]
-        const bf16x8 al = lds_slots(Xl, LDX, 16 * dt + n, kb, g4);
-        acc[dt] = mfma(ah, Sh[kb], acc[dt]);
-        acc[dt] = mfma(ah, Sl[kb], acc[dt]);
-        acc[dt] = mfma(al, Sh[kb], acc[dt]);
-      }
+      X[kb] = *reinterpret_cast<const bf16x8*>(src + 512 * kb);
+      X[NKB + kb] = *reinterpret_cast<const bf16x8*>(src + DK * DK + 512 * kb);
     }
+    L = tile(s);
+  };
+  // hi/lo split of this lane's 4 values into exchange buffer e
+  auto publish = [&](const floatx4& v, int e) {
+    const float x[4] = {v[0], v[1], v[2], v[3]};
+    bf16x4 hi, lo;
+    split4(x, hi, lo);
+    *reinterpret_cast<bf16x4*>(&sx[e][n * LDE + 16 * w + 4 * g4]) = hi;
+    *reinterpret_cast<bf16x4*>(&sx[e][ET + n * LDE + 16 * w + 4 * g4]) = lo;
+  };
+  floatx4 S, Sfinal;
+  // segment s with operands X, L; reloads the set for segment s + 2 into Xn, Ln
+  auto step = [&](int s, const bf16x8* X, const floatx4& L, bf16x8* Xn, floatx4& Ln) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);         // lgkmcnt(0): this wave's split is in LDS
+    exec_barrier();                             // everyone's split of S_in(s) visible
+    const bf16* E = sx[s & 1];
+    // all operand reads first (one LDS latency), and the loads for segment
+    // s + 2 before the products, so the address units drain them meanwhile
+    bf16x8 bh8[NKB], bl8[NKB];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) S[dt] = acc[dt] + L[dt];
-  }
-  if (ST != nullptr) {
+    for (int kb = 0; kb < NKB; ++kb) {
+      bh8[kb] = lds_slots(E, LDE, n, kb, g4);         // S_in(s)[r0 + n][e], hi
+      bl8[kb] = lds_slots(E + ET, LDE, n, kb, g4);    // lo
+    }
+    load(Xn, Ln, s + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    floatx4 a0 = L, a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-      *reinterpret_cast<float4*>(ST + ((size_t)bh * DV + row) * DK + 16 * dt + 4 * g4) =
-          make_float4(S[dt][0], S[dt][1], S[dt][2], S[dt][3]);
+    for (int kb = 0; kb < NKB; ++kb) {
+      a0 = mfma(X[kb], bh8[kb], a0);
+      a1 = mfma(X[kb], bl8[kb], a1);
+      a2 = mfma(X[NKB + kb], bh8[kb], a2);
+    }
+    S = a0 + (a1 + a2);                         // S_end(s)
+    const bool last = s == nseg - 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Sfinal[i] = last ? S[i] : Sfinal[i];
+    if (s + 1 < nseg) publish(S, (s + 1) & 1);
+  };
+  bf16x8 XA[2 * NKB], XB[2 * NKB], XC[2 * NKB];
+  floatx4 LA, LB, LC;
+  S = tile(0);                                  // S_end(0), the first load waited on
+  load(XA, LA, 1);
+  load(XB, LB, 2);
+  publish(S, 1);
+  for (int s = 1; s <= nsteps; s += 3) {
+    step(s, XA, LA, XC, LC);
+    step(s + 1, XB, LB, XA, LA);
+    step(s + 2, XC, LC, XB, LB);
   }
+  if (ST != nullptr)
+    *reinterpret_cast<float4*>(ST + ((size_t)bh * DV + r0 + n) * DK + 16 * w + 4 * g4) =
+        make_float4(Sfinal[0], Sfinal[1], Sfinal[2], Sfinal[3]);
 }
 
 // ===========================================================================
@@ -1335,14 +1370,12 @@ __global__ __launch_bounds__(64 * (DV / 16 + kCorrLoaders)) void segment_correct
 
   // ---------------- compute ----------------
   const int r0 = 16 * w;                         // first row of this wave
-  const float* sin_row = seg.S_in + (((size_t)bh * seg.nseg + s) * DV + r0 + n) * DK;
+  const bf16* sin_row = reinterpret_cast<const bf16*>(seg.S_in) +
+                        (((size_t)bh * seg.nseg + s) * DV + r0 + n) * DK;
   bf16x8 As[NKB];                                // A operand: S_in[r0 + n][32 kb + 8 g4 .. + 7]
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    const float4 a = *reinterpret_cast<const float4*>(sin_row + 32 * kb + 8 * g4);
-    const float4 c = *reinterpret_cast<const float4*>(sin_row + 32 * kb + 8 * g4 + 4);
-    As[kb] = to_bf16x8(floatx8{a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w});
-  }
+  for (int kb = 0; kb < NKB; ++kb)
+    As[kb] = *reinterpret_cast<const bf16x8*>(sin_row + 32 * kb + 8 * g4);
   for (int g = 0; g < ngroups; ++g) {
     exec_barrier();                    // tile g loaded
     const bf16* xs = ring[g % NBUF];
@@ -1424,9 +1457,8 @@ static void launch_scan_t(const void* q, const void* k, const void* v,
 template <int DK>
 static void launch_segment_tail(const SegArgs& seg, void* o, float* ST, int B,
                                 int T, int H, int dv, hipStream_t stream) {
-  hipLaunchKernelGGL((segment_combine_kernel<DK>),
-                     dim3(B * H * (dv / (16 * kCombineWaves))),
-                     dim3(64 * (kCombineWaves + kCombineLoaders)), 0, stream, seg, ST, dv);
+  hipLaunchKernelGGL((segment_combine_kernel<DK>), dim3(B * H * (dv / 16)),
+                     dim3(64 * (DK / 16 + 1)), 0, stream, seg, ST, dv);
   const dim3 grid(B * H * (seg.nseg - 1));
   if (dv == 128)
     hipLaunchKernelGGL((segment_correct_kernel<DK, 128>), grid,
@@ -1454,7 +1486,7 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v,
     seg.xhat = wsb + plan.xhat_off;
     seg.S_fin = reinterpret_cast<float*>(wsb + plan.sfin_off);
     seg.X_fin = wsb + plan.xfin_off;
-    seg.S_in = reinterpret_cast<float*>(wsb + plan.sin_off);
+    seg.S_in = wsb + plan.sin_off;
   }
   const float* wsf = static_cast<const float*>(ws);
 #define GDN_SCAN(DK, TI, TO) \
