@@ -229,7 +229,7 @@ def main(argv=None):
         def prefill_step(evs=None):
             if evs is not None:
                 evs[0].record(stream)
-            gdn.prefill_prepare(q, k, al, be, dv, ws)
+            gdn.prefill_prepare(q, k, al, be, dv, ws, out_dtype=o.dtype)
             if evs is not None:
                 evs[1].record(stream)
             gdn.prefill_scan(q, k, v, None, o, ST, ws)

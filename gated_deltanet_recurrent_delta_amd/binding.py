@@ -34,7 +34,7 @@ SIGNATURES = {
     "gdn_prefill_segments": (_i, [_i, _i, _i, _i, _i, _i, _i, _vp]),
     "gdn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                          _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
-    "gdn_prefill_prepare": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
+    "gdn_prefill_prepare": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                                  _vp, _sz, _vp]),
     "gdn_prefill_scan": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
                               _i, _i, _i, _vp, _sz, _vp]),
@@ -176,16 +176,21 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 
 
 def prefill_prepare(q, k, alpha, beta, dv: int, workspace: torch.Tensor,
-                    stream=None) -> None:
+                    out_dtype=None, stream=None) -> None:
     """First phase of prefill (chunk-local, state independent) into
-    `workspace`; see include/gdn.h."""
+    `workspace`, for a scan whose outputs have `out_dtype` (default: q's
+    dtype); see include/gdn.h."""
     _dev_tensor(q, "q", _DTYPE_CODE)
     B, T, H, dk = q.shape
     _dev_tensor(k, "k", (q.dtype,), q.shape)
     _dev_tensor(alpha, "alpha", (torch.float32,), (B, T, H))
     _dev_tensor(beta, "beta", (torch.float32,), (B, T, H))
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out_dtype not in _DTYPE_CODE:
+        raise ValueError(f"out_dtype {out_dtype} not in {tuple(_DTYPE_CODE)}")
     st = lib.gdn_prefill_prepare(_ptr(q), _ptr(k), _ptr(alpha), _ptr(beta),
                                  B, T, H, dk, dv, _DTYPE_CODE[q.dtype],
+                                 _DTYPE_CODE[out_dtype],
                                  _ptr(workspace), workspace.numel(),
                                  _stream_handle(q, stream))
     _check(st, "gdn_prefill_prepare")

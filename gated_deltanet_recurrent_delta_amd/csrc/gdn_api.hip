@@ -33,13 +33,13 @@ int check_prefill_shape(int B, int T, int H, int dk, int dv, int in_dtype,
   return GDN_OK;
 }
 
-// Validation and launch of the prepare phase.  write_pl: also store the lo
-// part of P, which only the fp32-output scan reads.
+// Validation and launch of the prepare phase.  fp32 outputs: also store the
+// lo part of P, which only the fp32-output scan reads.
 int prepare_checked(const void* q, const void* k, const float* alpha,
                     const float* beta, int B, int T, int H, int dk, int dv,
-                    int in_dtype, bool write_pl, void* workspace,
+                    int in_dtype, int out_dtype, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  int st = check_prefill_shape(B, T, H, dk, dv, in_dtype, GDN_F32);
+  int st = check_prefill_shape(B, T, H, dk, dv, in_dtype, out_dtype);
   if (st != GDN_OK) return st;
   if (T == 0) return GDN_OK;
   if (!q || !k || !alpha || !beta) return GDN_EINVAL;
@@ -50,7 +50,7 @@ int prepare_checked(const void* q, const void* k, const float* alpha,
   if (workspace_bytes < prefill_ws_bytes(B, T, H, dk, dv)) return GDN_EWORKSPACE;
   return to_status(gdn::launch_prefill_prepare(
       q, k, alpha, beta, static_cast<float*>(workspace), B, T, H, dk, in_dtype,
-      write_pl, static_cast<hipStream_t>(stream)));
+      out_dtype == GDN_F32, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -90,10 +90,9 @@ int gdn_prefill_segments(int B, int T, int H, int dk, int dv, int in_dtype,
 
 int gdn_prefill_prepare(const void* q, const void* k, const float* alpha,
                         const float* beta, int B, int T, int H, int dk, int dv,
-                        int in_dtype, void* workspace, size_t workspace_bytes,
-                        void* stream) {
-  // the scan may follow with either output dtype: keep every tile
-  return prepare_checked(q, k, alpha, beta, B, T, H, dk, dv, in_dtype, true,
+                        int in_dtype, int out_dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return prepare_checked(q, k, alpha, beta, B, T, H, dk, dv, in_dtype, out_dtype,
                          workspace, workspace_bytes, stream);
 }
 
@@ -140,7 +139,7 @@ int gdn_prefill(const void* q, const void* k, const void* v,
     if (ST && S0 && ST != S0 && (ST < S0 + nstate && S0 < ST + nstate))
       return GDN_EINVAL;
     st = prepare_checked(q, k, alpha, beta, B, T, H, dk, dv, in_dtype,
-                         out_dtype == GDN_F32, workspace, workspace_bytes, stream);
+                         out_dtype, workspace, workspace_bytes, stream);
     if (st != GDN_OK) return st;
   }
   return gdn_prefill_scan(q, k, v, S0, o, ST, B, T, H, dk, dv, in_dtype,

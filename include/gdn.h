@@ -118,7 +118,11 @@ int gdn_prefill(const void* q, const void* k, const void* v,
 /*
  * The two phases of gdn_prefill, exposed so a caller can time or schedule
  * them separately.  gdn_prefill == gdn_prefill_prepare then gdn_prefill_scan
- * on the same stream with the same workspace.
+ * on the same stream with the same workspace and the same dtypes (prepare
+ * takes the output dtype because only fp32 outputs read the low half of the
+ * split query-key tile, which it then also writes; a scan with another
+ * out_dtype than its prepare's is not supported and its outputs are
+ * undefined).
  *   prepare: per 64-token chunk, independent of the state: the gate prefix
  *            sums, the unit-lower-triangular delta correction
  *            (I + A)^{-1} with A_ji = beta_j e^{g_j - g_i} k_j.k_i (i < j),
@@ -134,7 +138,8 @@ int gdn_prefill(const void* q, const void* k, const void* v,
 int gdn_prefill_prepare(const void* q, const void* k,
                         const float* alpha, const float* beta,
                         int B, int T, int H, int dk, int dv, int in_dtype,
-                        void* workspace, size_t workspace_bytes, void* stream);
+                        int out_dtype, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 int gdn_prefill_scan(const void* q, const void* k, const void* v,
                      const float* S0, void* o, float* ST,

@@ -142,9 +142,11 @@ def test_decode_argument_errors(kw, status):
 
 def test_prepare_and_scan_argument_errors():
     lib = bd.lib
-    assert lib.gdn_prefill_prepare(P, P, P, P, 1, 64, 1, 128, 128, 1, NULL,
+    assert lib.gdn_prefill_prepare(P, P, P, P, 1, 64, 1, 128, 128, 1, 1, NULL,
                                    0, NULL) == bd.GDN_EWORKSPACE
-    assert lib.gdn_prefill_prepare(P, P, P, P, 1, 64, 1, 100, 128, 1, P,
+    assert lib.gdn_prefill_prepare(P, P, P, P, 1, 64, 1, 100, 128, 1, 1, P,
+                                   10 ** 6, NULL) == bd.GDN_ESHAPE
+    assert lib.gdn_prefill_prepare(P, P, P, P, 1, 64, 1, 128, 128, 1, 7, P,
                                    10 ** 6, NULL) == bd.GDN_ESHAPE
     assert lib.gdn_prefill_scan(P, P, P, NULL, P, P, 1, 64, 1, 128, 128, 1,
                                 1, P, 100, NULL) == bd.GDN_EWORKSPACE

@@ -171,15 +171,21 @@ def test_empty_sequence_copies_state():
     assert torch.count_nonzero(ST) == 0
 
 
-def test_two_phase_entry_points_match_composite():
-    x = gi.generic(1, 300, 4, 128, 128, 21, "bf16", S0_scale=0.3)
+@pytest.mark.parametrize("T,H,out_dt", [(300, 4, "bf16"), (300, 4, "f32"),
+                                        (2048 + 37, 2, "bf16")])
+def test_two_phase_entry_points_match_composite(T, H, out_dt):
+    """prepare (told the output dtype) then scan == gdn_prefill, bit for bit,
+    for fp32 outputs (which read the lo half of P), bf16 outputs, and the
+    segmented path."""
+    x = gi.generic(1, T, H, 128, 128, 21 + T, "bf16", S0_scale=0.3)
     d = to_dev(x)
-    o_ref, S_ref = run(x)
-    nb = gdn.prefill_workspace_bytes(1, 300, 4, 128, 128)
+    o_ref, S_ref = run(x, out_dtype=tdtype(out_dt))
+    nb = gdn.prefill_workspace_bytes(1, T, H, 128, 128)
     ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
     o = torch.empty_like(o_ref)
     ST = torch.empty_like(S_ref)
-    gdn.prefill_prepare(d["q"], d["k"], d["alpha"], d["beta"], 128, ws)
+    gdn.prefill_prepare(d["q"], d["k"], d["alpha"], d["beta"], 128, ws,
+                        out_dtype=o.dtype)
     gdn.prefill_scan(d["q"], d["k"], d["v"], d["S0"], o, ST, ws)
     torch.cuda.synchronize()
     assert torch.equal(o, o_ref) and torch.equal(ST, S_ref)
