@@ -35,8 +35,29 @@ constexpr int kSvdThreads = 512;
 constexpr int kMaxSweeps = 30;
 constexpr int kProjCols = 32;
 
-__device__ __forceinline__ double xor_sum(double x, int width) {
-  for (int m = 1; m < width; m <<= 1) x += __shfl_xor(x, m);
+// One DPP move of a double (both 32-bit halves with the same control).
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over aligned groups of W lanes (W a power of two, 2..64), the same
+// value on every lane of a group.  Within a 16-lane row the partners come
+// from DPP moves (pairs, quads, then the mirrored half row and row), across
+// rows from LDS permutes.  Each step adds a lane's own partial sum to the
+// other half's, as a butterfly does, so every lane of a group ends with the
+// same bits.
+template <int W>
+__device__ __forceinline__ double lane_sum(double x) {
+  if constexpr (W >= 2) x += dpp_d<0xB1>(x);    // quad_perm [1,0,3,2]
+  if constexpr (W >= 4) x += dpp_d<0x4E>(x);    // quad_perm [2,3,0,1]
+  if constexpr (W >= 8) x += dpp_d<0x141>(x);   // row_half_mirror
+  if constexpr (W >= 16) x += dpp_d<0x140>(x);  // row_mirror
+  if constexpr (W >= 32) x += __shfl_xor(x, 16);
+  if constexpr (W >= 64) x += __shfl_xor(x, 32);
   return x;
 }
 
@@ -73,7 +94,7 @@ svd_left_kernel(const float* __restrict__ S, int r, float* __restrict__ U,
     X[(e % N) * LD + e / N] = x;
     fro += x * x;
   }
-  fro = xor_sum(fro, 64);
+  fro = lane_sum<64>(fro);
   if ((tid & 63) == 0) red[tid >> 6] = fro;
   __syncthreads();
   fro = 0.0;
@@ -88,7 +109,7 @@ svd_left_kernel(const float* __restrict__ S, int r, float* __restrict__ U,
         const double x = X[j * LD + k];
         s += x * x;
       }
-      s = xor_sum(s, 64);
+      s = lane_sum<64>(s);
       const double x0 = X[k * LD + k];
       double tau = 0.0, v0 = 1.0, diag = x0;
       if (s > 0.0) {
@@ -158,9 +179,9 @@ svd_left_kernel(const float* __restrict__ S, int r, float* __restrict__ U,
         be += b[j] * b[j];
         ga += a[j] * b[j];
       }
-      al = xor_sum(al, TPP);
-      be = xor_sum(be, TPP);
-      ga = xor_sum(ga, TPP);
+      al = lane_sum<TPP>(al);
+      be = lane_sum<TPP>(be);
+      ga = lane_sum<TPP>(ga);
       // every lane of the group holds the same sums (the butterfly adds the
       // same two values in both orders), so they all take the same branch
       if (fmin(al, be) > negl && fabs(ga) > tol * sqrt(al) * sqrt(be)) {
@@ -196,8 +217,8 @@ svd_left_kernel(const float* __restrict__ S, int r, float* __restrict__ U,
       s0 += x0 * x0;
       s1 += x1 * x1;
     }
-    s0 = xor_sum(s0, TPP);
-    s1 = xor_sum(s1, TPP);
+    s0 = lane_sum<TPP>(s0);
+    s1 = lane_sum<TPP>(s1);
     if (sub == 0) {
       nrm[j0] = s0;
       nrm[j1] = s1;
