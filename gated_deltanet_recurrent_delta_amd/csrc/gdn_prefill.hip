@@ -1279,10 +1279,13 @@ __global__ __launch_bounds__(64 * (DK / 16 + 1)) void segment_combine_kernel(
 // ===========================================================================
 
 // One workgroup per (batch, head, segment >= 1), in two roles:
-//  * NLW loader waves move the segment's x^ and (old) o tiles, 64 tokens at a
-//    time, straight from global memory into a ring of three LDS buffers, two
-//    tiles ahead.  They issue nothing but these loads, so waiting for the
-//    oldest tile is an exact partial wait on their own load counter.
+//  * two loader waves, one for the segment's x^ tiles and one for its (old)
+//    o tiles, move them 64 tokens at a time straight from global memory into
+//    a ring of three LDS buffers, two tiles ahead.  They issue nothing but
+//    these loads, so waiting for the oldest tile is an exact partial wait on
+//    their own load counter.  (Issuing a tile takes as long as the memory
+//    system accepts it: the pass runs at about 4.3 TB/s, and a deeper ring
+//    or cheaper address arithmetic measured no faster.)
 //  * DV/16 compute waves (wave w: state rows 16 w .. 16 w + 15) form
 //    O_corr^T = S_in x^^T for each tile (S_in as the resident A operand; a
 //    lane holds 4 consecutive rows of one token), add the old o from LDS and
@@ -1292,20 +1295,16 @@ __global__ __launch_bounds__(64 * (DK / 16 + 1)) void segment_combine_kernel(
 // the same barriers, one per tile.  Single-pass bf16 (outputs are bf16).
 constexpr int kCorrLoaders = 2;
 
-
 template <int DK, int DV>
 __global__ __launch_bounds__(64 * (DV / 16 + kCorrLoaders)) void segment_correct_kernel(
     SegArgs seg, bf16* o, int T, int H) {
   constexpr int NKB = DK / 32;
   constexpr int NCW = DV / 16;                   // compute waves
-  constexpr int NLW = kCorrLoaders;              // loader waves
   constexpr int LDXH = DK + 8, UXH = LDXH / 8;   // padded x^ tile row (16-byte units)
   constexpr int LDOT = DV + 8, UOT = LDOT / 8;   // padded o tile row
   constexpr int XT = C * LDXH, OT = C * LDOT;    // elements per tile
-  constexpr int NBG = UXH + UOT;                 // 1 KB load blocks per 64-token group
-  static_assert(NBG % NLW == 0, "load blocks split evenly over the loaders");
-  constexpr int NBL = NBG / NLW;                 // blocks per loader wave per group
-  static_assert(NBL <= 63, "one group's loads fit the load counter");
+  static_assert(kCorrLoaders == 2, "one loader wave per tile");
+  static_assert(UXH <= 63 && UOT <= 63, "one tile's loads fit the load counter");
   constexpr int NBUF = 3;
   __shared__ __attribute__((aligned(16))) bf16 ring[NBUF][XT + OT];
 
@@ -1323,48 +1322,52 @@ __global__ __launch_bounds__(64 * (DV / 16 + kCorrLoaders)) void segment_correct
   const size_t tok_o = (size_t)H * DV;
 
   if (w >= NCW) {
-    // ---------------- loader ----------------
-    const int lw = w - NCW;
-    // this lane's (row, unit) in each of its blocks of a group; pad units
-    // fetch unit 0 of their row (never read)
-    int rowof[NBL], offof[NBL];
+    // ---------------- loaders: the first x^ tiles, the second o tiles ----
+    // A tile of 64 rows of U 16-byte units (one of them padding) is U blocks
+    // of 1 KB.  Each lane's offset in every block, from the tile's first
+    // row, is computed once; a tile then costs a scalar base and one add per
+    // block.  Rows past the sequence end (its last, partial tile only) load
+    // the last row instead and are never stored.
+    auto run = [&](auto u_c, const bf16* src, int stride, int dst_off) {
+      constexpr int U = decltype(u_c)::value;
+      int off[U];
 #pragma unroll
-    for (int j = 0; j < NBL; ++j) {
-      const int ib = j * NLW + lw;
-      if (ib < UXH) {
-        const int idx = 64 * ib + lane, row = idx / UXH, u = idx - row * UXH;
-        rowof[j] = row;
-        offof[j] = 8 * (u < UXH - 1 ? u : 0);
-      } else {
-        const int idx = 64 * (ib - UXH) + lane, row = idx / UOT, u = idx - row * UOT;
-        rowof[j] = row;
-        offof[j] = 8 * (u < UOT - 1 ? u : 0);
+      for (int j = 0; j < U; ++j) {
+        const int idx = 64 * j + lane, row = idx / U, u = idx - row * U;
+        off[j] = row * stride + 8 * (u < U - 1 ? u : 0);   // pad units: unit 0
       }
-    }
-    auto issue = [&](int g) {
-      bf16* buf = ring[g % NBUF];
-      const int t0 = t_begin + C * g;
+      auto issue = [&](int g) {
+        bf16* buf = ring[g % NBUF] + dst_off;
+        const int t0 = t_begin + C * g;
+        const bf16* base = src + (size_t)t0 * stride;
+        if (t0 + C <= t_end) {
 #pragma unroll
-      for (int j = 0; j < NBL; ++j) {
-        const int ib = j * NLW + lw;
-        const int t = min(t0 + rowof[j], t_end - 1);   // rows past the segment: not stored
-        if (ib < UXH)
-          dma16(xh + (size_t)t * DK + offof[j], buf + 512 * ib);
+          for (int j = 0; j < U; ++j) dma16(base + off[j], buf + 512 * j);
+        } else {
+#pragma unroll
+          for (int j = 0; j < U; ++j) {
+            const int idx = 64 * j + lane, row = idx / U, u = idx - row * U;
+            dma16(base + min(row, t_end - 1 - t0) * stride + 8 * (u < U - 1 ? u : 0),
+                  buf + 512 * j);
+          }
+        }
+      };
+      issue(0);
+      if (ngroups > 1) issue(1);
+      for (int g = 0; g < ngroups; ++g) {
+        // tile g complete (tile g + 1 may still be in flight)
+        if (g + 1 < ngroups)
+          __builtin_amdgcn_s_waitcnt(0x0F70 | (U & 15) | ((U >> 4) << 14));
         else
-          dma16(ob + (size_t)t * tok_o + offof[j], buf + 512 * ib);
+          __builtin_amdgcn_s_waitcnt(0x0F70);
+        exec_barrier();                // tile g visible; tile g - 1's buffer is free
+        if (g + 2 < ngroups) issue(g + 2);
       }
     };
-    issue(0);
-    if (ngroups > 1) issue(1);
-    for (int g = 0; g < ngroups; ++g) {
-      // tile g complete (tile g + 1 may still be in flight)
-      if (g + 1 < ngroups)
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (NBL & 15) | ((NBL >> 4) << 14));
-      else
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-      exec_barrier();                  // tile g visible; tile g - 1's buffer is free
-      if (g + 2 < ngroups) issue(g + 2);
-    }
+    if (w == NCW)
+      run(std::integral_constant<int, UXH>{}, xh, DK, 0);
+    else
+      run(std::integral_constant<int, UOT>{}, ob, (int)tok_o, XT);
     return;
   }
 
