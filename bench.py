@@ -261,7 +261,7 @@ def main(argv=None):
         prefill_info = {
             "segments": {"per_head": nseg, "chunks_per_segment": seg_chunks},
             "kernels_us": {"prepare_kernel": prep_ms * 1e3,
-                           "scan (scan_kernel + segment combine + correction)": scan_ms * 1e3},
+                           "scan (scan_wide_kernel + segment_combine_kernel + segment_correct_kernel)": scan_ms * 1e3},
             "mfma": {"executed_flops": f_prep + f_scan,
                      "achieved_tflops": (f_prep + f_scan) / (call_ms * 1e-3) / 1e12,
                      "frac_of_bf16_peak": (f_prep + f_scan) / (call_ms * 1e-3) / MFMA_BF16_PEAK,
