@@ -191,12 +191,18 @@ def test_two_phase_entry_points_match_composite(T, H, out_dt):
     assert torch.equal(o, o_ref) and torch.equal(ST, S_ref)
 
 
-@pytest.mark.parametrize("T,dk,dv", [(2048, 128, 128), (1024 + 37, 128, 128),
-                                     (1500, 64, 128), (2048, 128, 64),
-                                     (3000, 64, 64)])
-def test_segmented_prefill_few_heads(T, dk, dv):
+# (T, dk, dv, segments): the combine chains the segments in steps of three
+# (its loop is unrolled by three), so the cases cover 1 to 4 chaining steps
+# (every remainder modulo 3), ragged last segments and chunks, and all four
+# head-size pairs.
+@pytest.mark.parametrize("T,dk,dv,nseg", [(2048, 128, 128, 4), (1024 + 37, 128, 128, 2),
+                                          (1600, 128, 128, 3), (2600, 128, 128, 5),
+                                          (1500, 64, 128, 3), (2048, 128, 64, 4),
+                                          (3000, 64, 64, 5)])
+def test_segmented_prefill_few_heads(T, dk, dv, nseg):
     """Few heads and long sequences take the segment-parallel path (bf16 in
     and out): transition rows, segment chaining and output correction."""
+    assert gdn.prefill_segments(1, T, 2, dk, dv)[0] == nseg
     x = gi.generic(1, T, 2, dk, dv, 900 + T + dk + dv, "bf16", S0_scale=0.3)
     check_full(x, "bf16", f"segmented T={T}")
 
