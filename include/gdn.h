@@ -78,8 +78,8 @@ const char* gdn_version(void);
  * chunk's triangular delta correction, its decay-masked query-key products
  * and its gate prefix sums (33,792 bytes), and, when B*H heads alone are too
  * few to fill the GPU and T spans at least 16 chunks, buffers for splitting
- * each sequence into segments that run in parallel (per head: T*dk*2 bytes
- * plus three dv*dk / dk*dk fp32 matrices per segment).  The size covers
+ * each sequence into segments that run in parallel (per head: T*dk*2 bytes,
+ * and per segment dv*dk*4 + dk*dk*4 + dv*dk*2 bytes).  The size covers
  * every dtype combination.
  */
 size_t gdn_prefill_workspace_bytes(int B, int T, int H, int dk, int dv);
