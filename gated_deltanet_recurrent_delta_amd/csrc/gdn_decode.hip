@@ -11,65 +11,68 @@
 // the gated decay; rows evolve independently, Sec. 3.1).
 //
 // The step is HBM-bound (each state byte is read once and written once, at
-// 0.75 flop/byte), so the kernel is a coalesced stream: 8 lanes cover one row
-// with 16-byte loads (each wave instruction touches 8 full 128-byte lines),
-// every load of a wave is issued before any reduction, the two row dot
-// products are reduced with three DPP steps, and the state is written back
-// with non-temporal stores.
+// 0.75 flop/byte), so the kernel is a coalesced stream.  16 lanes cover 64
+// columns of a row with 16-byte loads: at dk=64 one wave instruction reads
+// four whole consecutive rows (1 KB), at dk=128 the first or second halves
+// of four rows.  A wave issues its few vector loads (k, q, v) first and then
+// every state load, and reduces and stores each group of four rows as soon
+// as its loads have arrived, so stores start while later rows are still in
+// flight.  The two row dot products are reduced with four DPP steps and the
+// state is read and written with non-temporal accesses.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
 namespace gdn {
 
-// DK: key width; G: row groups of 8 rows per wave (rows per wave = 8 G).
-template <int DK, int G, typename TIn, typename TOut>
+// DK: key width; NG: groups of 4 rows per wave (rows per wave = 4 NG).
+template <int DK, int NG, typename TIn, typename TOut>
 __global__ __launch_bounds__(256) void decode_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, const float* S_in, float* S_out,
     TOut* __restrict__ o, int BH, int dv, int slices_per_head) {
-  constexpr int F = DK / 32;            // float4 per lane per row
+  constexpr int F = DK / 64;            // float4 per lane per row
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int head = wave / slices_per_head;
   if (head >= BH) return;
   const int slice = wave - head * slices_per_head;
-  const int sub = lane & 7;             // column lane within the row
-  const int rg = lane >> 3;             // row within a group of 8
-  const int row0 = slice * (8 * G);
-
-  const size_t sbase = (size_t)head * dv * DK;
-  floatx4 s[G][F];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float* rowp = S_in + sbase + (size_t)(row0 + 8 * g + rg) * DK;
-#pragma unroll
-    for (int f = 0; f < F; ++f)
-      s[g][f] = __builtin_nontemporal_load(
-          reinterpret_cast<const floatx4*>(rowp + 32 * f + 4 * sub));
-  }
+  const int sub = lane & 15;            // column lane within the row
+  const int rg = lane >> 4;             // row within a group of 4
+  const int row0 = slice * (4 * NG);
 
   float4 kk[F], qq[F];
 #pragma unroll
   for (int f = 0; f < F; ++f) {
-    kk[f] = load4(k + (size_t)head * DK + 32 * f + 4 * sub);
-    qq[f] = load4(q + (size_t)head * DK + 32 * f + 4 * sub);
+    kk[f] = load4(k + (size_t)head * DK + 64 * f + 4 * sub);
+    qq[f] = load4(q + (size_t)head * DK + 64 * f + 4 * sub);
   }
   const float a = alpha[head];
   const float b = beta[head];
-  float vv[G];
+  float vv[NG];
 #pragma unroll
-  for (int g = 0; g < G; ++g) vv[g] = load1(v + (size_t)head * dv + row0 + 8 * g + rg);
+  for (int g = 0; g < NG; ++g) vv[g] = load1(v + (size_t)head * dv + row0 + 4 * g + rg);
+
+  const size_t sbase = (size_t)head * dv * DK;
+  floatx4 s[NG][F];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const float* rowp = S_in + sbase + (size_t)(row0 + 4 * g + rg) * DK;
+#pragma unroll
+    for (int f = 0; f < F; ++f)
+      s[g][f] = __builtin_nontemporal_load(
+          reinterpret_cast<const floatx4*>(rowp + 64 * f + 4 * sub));
+  }
 
   float kq = 0.f;
 #pragma unroll
   for (int f = 0; f < F; ++f)
     kq += kk[f].x * qq[f].x + kk[f].y * qq[f].y + kk[f].z * qq[f].z +
           kk[f].w * qq[f].w;
-  kq = sum8(kq);
+  kq = sum16(kq);
 
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
+  for (int g = 0; g < NG; ++g) {
     float p = 0.f, r = 0.f;
 #pragma unroll
     for (int f = 0; f < F; ++f) {
@@ -78,10 +81,10 @@ __global__ __launch_bounds__(256) void decode_kernel(
       r += s[g][f][0] * qq[f].x + s[g][f][1] * qq[f].y + s[g][f][2] * qq[f].z +
            s[g][f][3] * qq[f].w;
     }
-    p = sum8(p);
-    r = sum8(r);
+    p = sum16(p);
+    r = sum16(r);
     const float u = b * (vv[g] - a * p);
-    const int row = row0 + 8 * g + rg;
+    const int row = row0 + 4 * g + rg;
     float* rowp = S_out + sbase + (size_t)row * DK;
 #pragma unroll
     for (int f = 0; f < F; ++f) {
@@ -90,18 +93,21 @@ __global__ __launch_bounds__(256) void decode_kernel(
       n[1] = a * s[g][f][1] + u * kk[f].y;
       n[2] = a * s[g][f][2] + u * kk[f].z;
       n[3] = a * s[g][f][3] + u * kk[f].w;
-      __builtin_nontemporal_store(n, reinterpret_cast<floatx4*>(rowp + 32 * f + 4 * sub));
+      __builtin_nontemporal_store(n, reinterpret_cast<floatx4*>(rowp + 64 * f + 4 * sub));
     }
     if (sub == 0) store1(o + (size_t)head * dv + row, a * r + u * kq);
   }
 }
 
-template <int DK, int G, typename TIn, typename TOut>
-static void launch_decode_g(dim3 grid, hipStream_t stream, const void* q,
-                            const void* k, const void* v, const float* alpha,
+template <int DK, int NG, typename TIn, typename TOut>
+static void launch_decode_g(hipStream_t stream, const void* q, const void* k,
+                            const void* v, const float* alpha,
                             const float* beta, const float* S_in, float* S_out,
-                            void* o, int BH, int dv, int slices) {
-  hipLaunchKernelGGL((decode_kernel<DK, G, TIn, TOut>), grid, dim3(256), 0,
+                            void* o, int BH, int dv) {
+  const int slices = dv / (4 * NG);
+  const long waves = (long)BH * slices;
+  const dim3 grid((unsigned)((waves + 3) / 4));
+  hipLaunchKernelGGL((decode_kernel<DK, NG, TIn, TOut>), grid, dim3(256), 0,
                      stream, static_cast<const TIn*>(q),
                      static_cast<const TIn*>(k), static_cast<const TIn*>(v),
                      alpha, beta, S_in, S_out, static_cast<TOut*>(o), BH, dv,
@@ -113,32 +119,32 @@ static hipError_t launch_decode_t(const void* q, const void* k, const void* v,
                                   const float* alpha, const float* beta,
                                   const float* S_in, float* S_out, void* o,
                                   int BH, int dv, hipStream_t stream) {
-  // One row group (8 rows) per wave: the most waves, hence the most
-  // independent 16-byte requests in flight per CU.  Measured on MI355X at
-  // B=64, H=16, dv=128 over 18 rotating state sets: 8 rows/wave streams
-  // 5.85 TB/s at dk=128 (16 and 32 rows/wave: 5.63 and 5.55 TB/s).
-  constexpr int GMAX = DK == 128 ? 4 : 8;
-  int G = 1;
-  const int slices = dv / (8 * G);
-  const long waves = (long)BH * slices;
-  const dim3 grid((unsigned)((waves + 3) / 4));
-  switch (G) {
-    case 1:
-      launch_decode_g<DK, 1, TIn, TOut>(grid, stream, q, k, v, alpha, beta,
-                                        S_in, S_out, o, BH, dv, slices);
+  // Rows per wave, measured on MI355X at H=16, dv=128 over 18 rotating state
+  // sets (one job, same box): at dk=128 four rows per wave is best at every
+  // batch (B=64: 22.9 us per step, against 23.0 with 8 rows and 23.5 with
+  // the 8-lanes-per-row mapping).  At dk=64, 16 rows per wave (4 KB, one
+  // resident wave per 4 KB of state at B=64) streams best once the grid
+  // still fills the chip with them (B=64: 12.57 us, against 12.75 with 8
+  // rows and 13.4 with 4), and 4 rows per wave when few heads need the most
+  // waves (B=1: 2.13 us, against 2.36 with 16 rows).
+  constexpr long kFill = 8192;          // 32 resident waves on each of 256 CUs
+  int ng = 1;
+  if (DK == 64) {
+    if ((long)BH * dv / 16 >= kFill && dv % 16 == 0) ng = 4;
+    else if ((long)BH * dv / 8 >= kFill && dv % 8 == 0) ng = 2;
+  }
+  switch (ng) {
+    case 4:
+      launch_decode_g<DK, 4, TIn, TOut>(stream, q, k, v, alpha, beta, S_in,
+                                        S_out, o, BH, dv);
       break;
     case 2:
-      launch_decode_g<DK, 2, TIn, TOut>(grid, stream, q, k, v, alpha, beta,
-                                        S_in, S_out, o, BH, dv, slices);
-      break;
-    case 4:
-      launch_decode_g<DK, 4, TIn, TOut>(grid, stream, q, k, v, alpha, beta,
-                                        S_in, S_out, o, BH, dv, slices);
+      launch_decode_g<DK, 2, TIn, TOut>(stream, q, k, v, alpha, beta, S_in,
+                                        S_out, o, BH, dv);
       break;
     default:
-      if constexpr (GMAX == 8)
-        launch_decode_g<DK, 8, TIn, TOut>(grid, stream, q, k, v, alpha, beta,
-                                          S_in, S_out, o, BH, dv, slices);
+      launch_decode_g<DK, 1, TIn, TOut>(stream, q, k, v, alpha, beta, S_in,
+                                        S_out, o, BH, dv);
       break;
   }
   return hipGetLastError();

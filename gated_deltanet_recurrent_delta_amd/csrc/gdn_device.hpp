@@ -1,5 +1,5 @@
 // Device helpers shared by the gfx950 kernels of libgdn: bf16 conversions,
-// the 16x16x32 bf16 MFMA, split-bf16 operands and 8-lane DPP reductions.
+// the 16x16x32 bf16 MFMA, split-bf16 operands and 16-lane DPP reductions.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -114,7 +114,7 @@ __device__ __forceinline__ floatx4 mfma(const bf16x8& a, const bf16x8& b,
 }
 
 // ---------------------------------------------------------------------------
-// DPP sums over groups of 8 consecutive lanes (result in all 8 lanes)
+// DPP sums over groups of 16 consecutive lanes (result in all 16 lanes)
 // ---------------------------------------------------------------------------
 
 template <int CTRL>
@@ -124,10 +124,11 @@ __device__ __forceinline__ float dpp(float x) {
                                          0xF, 0xF, false));
 }
 
-__device__ __forceinline__ float sum8(float x) {
+__device__ __forceinline__ float sum16(float x) {
   x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]: pairs
   x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]: quads
   x += dpp<0x141>(x);   // row_half_mirror: lane i <-> 7 - i within 8
+  x += dpp<0x140>(x);   // row_mirror: lane i <-> 15 - i within 16
   return x;
 }
 

@@ -23,6 +23,9 @@ def one_step_inputs(B, H, dk, dv, dtype, seed, S_scale=0.5):
 @pytest.mark.parametrize("in_dt,out_dt", [("bf16", "bf16"), ("f32", "f32"),
                                           ("bf16", "f32")])
 def test_decode_matches_oracle(B, H, dk, dv, in_dt, out_dt):
+    """One step against the oracle.  At dk=64 the launch picks the rows per
+    wave from the number of heads: B=3 runs 4-row waves, B=64 with dv=64
+    8-row waves and B=64 with dv=128 16-row waves, so all three are covered."""
     x = one_step_inputs(B, H, dk, dv, in_dt, seed=1000 + dk + dv + B)
     d = to_dev(x)
     o, S1 = gdn.decode_step(d["q"][:, 0].contiguous(), d["k"][:, 0].contiguous(),
