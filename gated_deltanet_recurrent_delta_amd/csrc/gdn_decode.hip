@@ -120,33 +120,30 @@ static hipError_t launch_decode_t(const void* q, const void* k, const void* v,
                                   const float* S_in, float* S_out, void* o,
                                   int BH, int dv, hipStream_t stream) {
   // Rows per wave, measured on MI355X at H=16, dv=128 over 18 rotating state
-  // sets (one job, same box): at dk=128 four rows per wave is best at every
+  // sets (one process, one GPU): at dk=128 four rows per wave is best at every
   // batch (B=64: 22.9 us per step, against 23.0 with 8 rows and 23.5 with
-  // the 8-lanes-per-row mapping).  At dk=64, 16 rows per wave (4 KB, one
-  // resident wave per 4 KB of state at B=64) streams best once the grid
-  // still fills the chip with them (B=64: 12.57 us, against 12.75 with 8
-  // rows and 13.4 with 4), and 4 rows per wave when few heads need the most
-  // waves (B=1: 2.13 us, against 2.36 with 16 rows).
+  // the 8-lanes-per-row mapping).  At dk=64, 16 rows per wave (4 KB each)
+  // is best while the grid still has kFill such waves, so that every CU is
+  // full from the first dispatch (B=64: 12.57 us, against 12.75 with 8 rows
+  // and 13.4 with 4); with few heads, 4 rows per wave gives the most waves
+  // (B=1: 2.13 us, against 2.36 with 16 rows).
   constexpr long kFill = 8192;          // 32 resident waves on each of 256 CUs
-  int ng = 1;
-  if (DK == 64) {
-    if ((long)BH * dv / 16 >= kFill && dv % 16 == 0) ng = 4;
-    else if ((long)BH * dv / 8 >= kFill && dv % 8 == 0) ng = 2;
-  }
-  switch (ng) {
-    case 4:
+  // dv is 64 or 128 (checked by the entry point), so 4, 8 and 16 rows
+  // divide it.
+  if constexpr (DK == 64) {
+    if ((long)BH * dv / 16 >= kFill) {
       launch_decode_g<DK, 4, TIn, TOut>(stream, q, k, v, alpha, beta, S_in,
                                         S_out, o, BH, dv);
-      break;
-    case 2:
+      return hipGetLastError();
+    }
+    if ((long)BH * dv / 8 >= kFill) {
       launch_decode_g<DK, 2, TIn, TOut>(stream, q, k, v, alpha, beta, S_in,
                                         S_out, o, BH, dv);
-      break;
-    default:
-      launch_decode_g<DK, 1, TIn, TOut>(stream, q, k, v, alpha, beta, S_in,
-                                        S_out, o, BH, dv);
-      break;
+      return hipGetLastError();
+    }
   }
+  launch_decode_g<DK, 1, TIn, TOut>(stream, q, k, v, alpha, beta, S_in, S_out,
+                                    o, BH, dv);
   return hipGetLastError();
 }
 
