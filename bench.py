@@ -11,9 +11,11 @@ tokens/s with inputs resident in HBM.  The same JSON line also carries the
 decode step at B=64 (dk=128 and the channel-pruned dk=64) and B=1, and the
 batched prefill B=8, T=4096 at dk=128 vs 64, each with its own roofline.
 
-Timing: W untimed steps, then K steps bracketed by device synchronisation;
-kernel durations come from HIP events recorded on the stream the kernels are
-launched on (torch's current stream, which the binding passes to libgdn).
+Timing: W untimed steps, then K steps launched eagerly with HIP events around
+each phase (the per-kernel durations, recorded on the stream the kernels are
+launched on: torch's current stream, which the binding passes to libgdn);
+then the timed K steps, bracketed by device synchronisation, as replays of a
+HIP graph that holds one step.
 Decode timing captures 512 steps x 18 state sets (one per GDN layer of a
 Qwen3.5-0.8B-sized model) in one HIP graph, so consecutive launches touch
 different 64 MiB states and the state streams from HBM rather than the
@@ -239,13 +241,27 @@ def main(argv=None):
         for _ in range(a.warmup):
             prefill_step()
         torch.cuda.synchronize()
+        # per-phase kernel times: eager steps bracketed by events
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
                for _ in range(a.steps)]
         t0 = time.perf_counter()
         for i in range(a.steps):
             prefill_step(evs[i])
         torch.cuda.synchronize()
+        eager_wall = time.perf_counter() - t0
+        # the timed steps: one step (prepare + scan) captured in a HIP graph,
+        # replayed K times
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            prefill_step()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(a.steps):
+            g.replay()
+        torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        del g
         prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
         scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
         call_ms = prep_ms + scan_ms
@@ -255,10 +271,13 @@ def main(argv=None):
         pbytes = prefill_bytes(B, T, H, dk, dv)
         nseg, seg_chunks = gdn.prefill_segments(B, T, H, dk, dv)
         f_prep, f_scan = prefill_mfma_flops(B, T, H, dk, dv, nseg, seg_chunks)
-        log(f"prefill 16K: {ms_per_step * 1e3:.1f} us/step wall; events: prepare "
+        log(f"prefill 16K: {ms_per_step * 1e3:.1f} us/step wall (HIP graph), "
+            f"{eager_wall * 1e6 / a.steps:.1f} us launched eagerly; events: prepare "
             f"{prep_ms * 1e3:.1f} us, scan {scan_ms * 1e3:.1f} us; "
             f"{value / 1e6:.1f} M tokens/s")
         prefill_info = {
+            "timed": "K replays of a HIP graph holding one step (prepare + scan)",
+            "eager_us_per_step": eager_wall * 1e6 / a.steps,
             "segments": {"per_head": nseg, "chunks_per_segment": seg_chunks},
             "kernels_us": {"prepare_kernel": prep_ms * 1e3,
                            "scan (scan_wide_kernel + segment_combine_kernel + segment_correct_kernel)": scan_ms * 1e3},

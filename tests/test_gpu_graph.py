@@ -1,0 +1,99 @@
+"""HIP graph capture of the entry points.
+
+A caller may capture a prefill step (prepare + scan) or a chain of decode
+steps in a HIP graph and replay it.  Every replay must reproduce the eager
+results bit for bit (the kernels use no atomics and the workspace carries
+nothing from one call to the next), also when the outputs and the workspace
+hold garbage before the replay and eager work runs between replays.
+"""
+
+import pytest
+import torch
+
+from gated_deltanet_recurrent_delta_amd import binding as gdn
+from tests.gpu_util import to_dev
+from workloads import gdn_inputs as gi
+
+pytestmark = pytest.mark.gpu
+
+REPLAYS = 3
+
+
+def _other_eager_work(dev):
+    """Unrelated eager work between replays: a prefill with its own
+    workspace and a torch reduction."""
+    y = to_dev(gi.generic(1, 300, 2, 64, 64, seed=77, dtype="bf16"))
+    gdn.prefill(y["q"], y["k"], y["v"], y["alpha"], y["beta"])
+    torch.randn(1 << 20, device=dev).sum().item()
+
+
+@pytest.mark.parametrize("B,T,H", [(1, 2085, 2), (2, 700, 8)])
+def test_prefill_graph_replays_match_eager(B, T, H):
+    dk = dv = 128
+    dev = torch.device("cuda")
+    x = gi.generic(B, T, H, dk, dv, seed=4242 + T, dtype="bf16", S0_scale=0.3)
+    d = to_dev(x)
+    ws = torch.empty(gdn.prefill_workspace_bytes(B, T, H, dk, dv),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    ST = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+
+    def step():
+        gdn.prefill_prepare(d["q"], d["k"], d["alpha"], d["beta"], dv, ws,
+                            out_dtype=o.dtype)
+        gdn.prefill_scan(d["q"], d["k"], d["v"], d["S0"], o, ST, ws)
+
+    step()
+    torch.cuda.synchronize()
+    o_ref, S_ref = o.clone(), ST.clone()
+    assert torch.isfinite(o_ref.float()).all() and torch.isfinite(S_ref).all()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(REPLAYS):
+        o.fill_(float("nan"))
+        ST.fill_(float("nan"))
+        ws.fill_(0xFF)                  # every byte 0xFF: NaN in fp32 and bf16
+        _other_eager_work(dev)
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"  replay {rep}: o equal {torch.equal(o, o_ref)}, "
+              f"S_T equal {torch.equal(ST, S_ref)}", flush=True)
+        assert torch.equal(o, o_ref), f"replay {rep}: o differs"
+        assert torch.equal(ST, S_ref), f"replay {rep}: S_T differs"
+
+
+@pytest.mark.parametrize("B,dk", [(64, 128), (64, 64), (1, 64)])
+def test_decode_graph_replays_match_eager(B, dk):
+    H, dv, n = 16, 128, 4
+    dev = torch.device("cuda")
+    x = gi.generic(B, n, H, dk, dv, seed=990 + B + dk, dtype="bf16", S0_scale=0.5)
+    d = to_dev(x)
+    steps = [tuple(d[name][:, t].contiguous()
+                   for name in ("q", "k", "v", "alpha", "beta"))
+             for t in range(n)]
+    S = d["S0"].clone()
+    outs = torch.empty((n, B, H, dv), dtype=torch.bfloat16, device=dev)
+
+    def chain():
+        for t in range(n):
+            gdn.decode_step(*steps[t], S, S_out=S, o=outs[t])
+
+    chain()
+    torch.cuda.synchronize()
+    o_ref, S_ref = outs.clone(), S.clone()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        chain()
+    torch.cuda.synchronize()
+    for rep in range(REPLAYS):
+        S.copy_(d["S0"])
+        outs.fill_(float("nan"))
+        _other_eager_work(dev)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(outs, o_ref), f"replay {rep}: o differs"
+        assert torch.equal(S, S_ref), f"replay {rep}: S differs"
