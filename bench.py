@@ -11,11 +11,13 @@ tokens/s with inputs resident in HBM.  The same JSON line also carries the
 decode step at B=64 (dk=128 and the channel-pruned dk=64) and B=1, and the
 batched prefill B=8, T=4096 at dk=128 vs 64, each with its own roofline.
 
-Timing: W untimed steps, then K steps launched eagerly with HIP events around
-each phase (the per-kernel durations, recorded on the stream the kernels are
-launched on: torch's current stream, which the binding passes to libgdn);
-then the timed K steps, bracketed by device synchronisation, as replays of a
-HIP graph that holds one step.
+Timing: W untimed steps, continued until at least 0.1 s of back-to-back load
+has passed (the GPU's clocks take ~30 ms of sustained load to settle, so every
+leg is timed in steady state); then K steps launched eagerly with HIP events
+around each phase (the per-kernel durations, recorded on the stream the
+kernels are launched on: torch's current stream, which the binding passes to
+libgdn); then the timed K steps, bracketed by device synchronisation, as
+replays of a HIP graph that holds one step.
 Decode timing captures 512 steps x 18 state sets (one per GDN layer of a
 Qwen3.5-0.8B-sized model) in one HIP graph, so consecutive launches touch
 different 64 MiB states and the state streams from HBM rather than the
@@ -95,6 +97,26 @@ def prefill_mfma_flops(B, T, H, dk, dv, nseg, seg_chunks):
 def prefill_algorithmic_flops(B, T, H, dk, dv):
     """Chunked-form flops per token-head: 6 C dk + 4 C dv + 6 dk dv."""
     return B * H * T * (6 * C * dk + 4 * C * dv + 6 * dk * dv)
+
+
+# Sustained load this long before any timed region.  Measured on MI355X: from
+# an idle GPU the scan kernel of the 16K step takes ~145 us, rises to ~170 us
+# within 4 ms and settles at ~132 us after ~30 ms of back-to-back steps (the
+# clocks settle under load); after 50 ms idle the same ramp repeats.
+SETTLE_S = 0.1
+
+
+def settle(torch, fn, min_calls):
+    """Untimed warm-up: call fn() at least min_calls times and until SETTLE_S
+    seconds of back-to-back work have passed; returns the number of calls."""
+    calls, t0 = 0, time.perf_counter()
+    while calls < min_calls or time.perf_counter() - t0 < SETTLE_S:
+        fn()
+        calls += 1
+        if calls % 16 == 0:
+            torch.cuda.synchronize()      # keep the host at most 16 calls ahead
+    torch.cuda.synchronize()
+    return calls
 
 
 def kernel_source_hash():
@@ -238,9 +260,7 @@ def main(argv=None):
             if evs is not None:
                 evs[2].record(stream)
 
-        for _ in range(a.warmup):
-            prefill_step()
-        torch.cuda.synchronize()
+        warm_calls = settle(torch, prefill_step, a.warmup)
         # per-phase kernel times: eager steps bracketed by events
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
                for _ in range(a.steps)]
@@ -254,8 +274,7 @@ def main(argv=None):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             prefill_step()
-        g.replay()
-        torch.cuda.synchronize()
+        settle(torch, g.replay, 1)
         t0 = time.perf_counter()
         for i in range(a.steps):
             g.replay()
@@ -277,6 +296,7 @@ def main(argv=None):
             f"{value / 1e6:.1f} M tokens/s")
         prefill_info = {
             "timed": "K replays of a HIP graph holding one step (prepare + scan)",
+            "untimed_warmup_steps": warm_calls,
             "eager_us_per_step": eager_wall * 1e6 / a.steps,
             "segments": {"per_head": nseg, "chunks_per_segment": seg_chunks},
             "kernels_us": {"prepare_kernel": prep_ms * 1e3,
@@ -416,8 +436,7 @@ def bench_decode(torch, gdn, dev, stream, B, dk, n_steps, layers, up,
             all_steps()
         replay = g.replay
     torch.cuda.synchronize()
-    replay()                         # untimed pass
-    torch.cuda.synchronize()
+    settle(torch, replay, 1)         # untimed passes
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     replay()
@@ -453,9 +472,8 @@ def bench_batched(torch, gdn, dev, stream, dk, steps, warmup, up):
     ST = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
     ws = torch.empty(gdn.prefill_workspace_bytes(B, T, H, dk, dv),
                      dtype=torch.uint8, device=dev)
-    for _ in range(warmup):
-        gdn.prefill(q, k, v, al, be, o=o, ST=ST, workspace=ws)
-    torch.cuda.synchronize()
+    settle(torch, lambda: gdn.prefill(q, k, v, al, be, o=o, ST=ST, workspace=ws),
+           warmup)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(steps):
