@@ -53,6 +53,9 @@ constexpr int C = kChunk;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Workspace layout of one (batch, head, chunk), in bytes from its start.
+// The 64x64 tiles are lower triangular in 16x16 blocks; the scans read
+// 32-wide k-blocks at or below the diagonal only, so blocks (0,1) and (2,3)
+// hold zeros and rows 0..31, columns 32..63 are never written or read.
 constexpr int kWsTh = 0;                    // bf16 [64][64] hi part of T
 constexpr int kWsTl = 8192;                 // bf16 [64][64] lo part of T
 constexpr int kWsPh = 16384;                // bf16 [64][64] hi part of P
@@ -209,7 +212,7 @@ __global__ __launch_bounds__(64) void prepare_kernel(
 
   // 3. lower tiles of A (decay- and beta-weighted K K^T, strictly lower) and
   //    of P (decay-masked Q K^T), row orientation; P straight to the
-  //    workspace, its strictly upper tiles as zeros.
+  //    workspace, with zeros in its upper tiles (0,1) and (2,3).
   floatx4 Ao[6];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
@@ -249,9 +252,12 @@ __global__ __launch_bounds__(64) void prepare_kernel(
       else
         Ao[lower_tile(mi, ni)] = floatx4{a[0], a[1], a[2], a[3]};
     }
+    // zeros only in the upper tile that shares a 32-wide k-block with the
+    // diagonal one ((0,1) and (2,3)): the scans read k-blocks s <= ct / 2
+    // only, so rows 0..31 never read columns 32..63, which stay unwritten
     const bf16x4 zero4 = {};
-#pragma unroll
-    for (int ni = mi + 1; ni < 4; ++ni) {
+    if ((mi & 1) == 0) {
+      const int ni = mi + 1;
       *reinterpret_cast<bf16x4*>(wsc + kWsPh + (j * C + 16 * ni + 4 * g4) * 2) = zero4;
       if (write_pl) *reinterpret_cast<bf16x4*>(wsc + kWsPl + (j * C + 16 * ni + 4 * g4) * 2) = zero4;
     }
@@ -277,10 +283,10 @@ __global__ __launch_bounds__(64) void prepare_kernel(
     __syncthreads();                          // every lane has read its block of A
 #pragma unroll
     for (int j = 0; j < 16; ++j) Ts[(base + j) * LDA + base + c] = tcol[j];
-    // zero the strictly upper blocks of T
+    // zero the upper blocks of T that are stored: (0,1) and (2,3)
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj)
-      if (bj > g4)
+      if (bj > g4 && (bj >> 1) == (g4 >> 1))
 #pragma unroll
         for (int j = 0; j < 16; ++j) Ts[(base + j) * LDA + 16 * bj + c] = 0.f;
   }
@@ -317,9 +323,11 @@ __global__ __launch_bounds__(64) void prepare_kernel(
     __syncthreads();
   }
 
-  // 5. T -> workspace as bf16 hi/lo
+  // 5. T -> workspace as bf16 hi/lo (rows 0..31, columns 32..63 are never
+  //    read and stay unwritten)
   for (int e = lane; e < C * C / 8; e += 64) {
     const int j = (8 * e) / C, i0 = (8 * e) % C;
+    if (j < C / 2 && i0 >= C / 2) continue;
     const float4 a0 = *reinterpret_cast<const float4*>(&Ts[j * LDA + i0]);
     const float4 a1 = *reinterpret_cast<const float4*>(&Ts[j * LDA + i0 + 4]);
     const floatx8 x = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
