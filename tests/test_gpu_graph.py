@@ -11,7 +11,8 @@ import pytest
 import torch
 
 from gated_deltanet_recurrent_delta_amd import binding as gdn
-from tests.gpu_util import to_dev
+from tests.gpu_util import (TOL_BF16, TOL_F32, assert_close, errs_o, errs_S,
+                            host, oracle_prefill, tdtype, to_dev)
 from workloads import gdn_inputs as gi
 
 pytestmark = pytest.mark.gpu
@@ -27,15 +28,23 @@ def _other_eager_work(dev):
     torch.randn(1 << 20, device=dev).sum().item()
 
 
-@pytest.mark.parametrize("B,T,H", [(1, 2085, 2), (2, 700, 8)])
-def test_prefill_graph_replays_match_eager(B, T, H):
-    dk = dv = 128
+# segmented and unsegmented plans, both key widths, and fp32 outputs (the
+# scan that also reads the lo part of P); the NaN-filled workspace also shows
+# that no scan reads the chunk-tile blocks prepare leaves unwritten
+@pytest.mark.parametrize("B,T,H,dk,dv,out_dt", [
+    (1, 2085, 2, 128, 128, "bf16"), (2, 700, 8, 128, 128, "bf16"),
+    (1, 2085, 2, 64, 128, "bf16"), (2, 700, 8, 64, 64, "bf16"),
+    (1, 300, 4, 128, 128, "f32"), (1, 300, 4, 64, 128, "f32")])
+def test_prefill_graph_replays_match_eager(B, T, H, dk, dv, out_dt):
     dev = torch.device("cuda")
-    x = gi.generic(B, T, H, dk, dv, seed=4242 + T, dtype="bf16", S0_scale=0.3)
+    x = gi.generic(B, T, H, dk, dv, seed=4242 + T + dk, dtype="bf16", S0_scale=0.3)
     d = to_dev(x)
+    nseg = gdn.prefill_segments(B, T, H, dk, dv, out_dtype=tdtype(out_dt))[0]
+    print(f"  B={B} T={T} H={H} dk={dk} dv={dv} out={out_dt}: {nseg} segments", flush=True)
     ws = torch.empty(gdn.prefill_workspace_bytes(B, T, H, dk, dv),
                      dtype=torch.uint8, device=dev)
-    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    ws.fill_(0xFF)
+    o = torch.empty((B, T, H, dv), dtype=tdtype(out_dt), device=dev)
     ST = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
 
     def step():
@@ -47,6 +56,10 @@ def test_prefill_graph_replays_match_eager(B, T, H):
     torch.cuda.synchronize()
     o_ref, S_ref = o.clone(), ST.clone()
     assert torch.isfinite(o_ref.float()).all() and torch.isfinite(S_ref).all()
+    # the eager result itself, from the NaN-filled workspace, against the oracle
+    o_or, S_or = oracle_prefill(x)
+    assert_close("o (eager)", errs_o(host(o_ref), o_or), TOL_F32 if out_dt == "f32" else TOL_BF16)
+    assert_close("S_T (eager)", errs_S(host(S_ref), S_or), TOL_F32)
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
