@@ -31,11 +31,17 @@ Sources (page titles as published; sections/equations as the pages give them):
     singular directions at every 256-token boundary, r = 128 = no change):
     state-rank post, §3.
 
-Readings where the pages leave a step open (each also listed in the design doc):
+  * Input path of a channel-pruned layer (qk_transform): keep a per-head
+    subset of query/key coordinates and renormalise over the kept ones:
+    "On State Reduction in Linear Attention", Sec. 3.2-3.3.
+
+Readings where the pages leave a step open:
   * No query scale: o_t = S_t q_t exactly.
   * alpha is given (not log alpha), in (0, 1]; beta in [0, 1].
   * Truncation happens only at boundaries between segments (t = 256 m with
     t < T), never after the last token.
+  * The input path selects, then normalises, then scales (queries only); a
+    vector whose kept coordinates are all zero maps to zero.
 """
 
 from __future__ import annotations
@@ -120,6 +126,57 @@ def gdn_decode_step(q, k, v, alpha, beta, S):
                               np.asarray(beta)[b, h][None], S[b, h])
             o[b, h], S1[b, h] = ob[0], Sb
     return o, S1
+
+
+# ---------------------------------------------------------------------------
+# the input path of a channel-pruned layer
+# ---------------------------------------------------------------------------
+
+def qk_transform(x, channels=None, l2norm: bool = True, scale: float = 1.0):
+    """Query/key vectors as the recurrence consumes them, from the raw
+    projection output.
+
+    x [..., H, dk_in] (any leading axes; the head axis is second to last).
+    channels: None, or int [H, dk] -- head h keeps coordinates channels[h]
+      of its dk_in-wide vector, in that order (the coordinate selection
+      P_I of "On State Reduction in Linear Attention", Sec. 3.2-3.3, one
+      subset per head).
+    l2norm: divide each kept vector by its L2 norm, computed over the KEPT
+      coordinates only (the same page: normalisation is recomputed on the
+      retained channels).  A vector whose kept coordinates are all zero stays
+      zero.
+    scale: multiplies the result (a query scale; 1 for keys).
+    Returns float64 [..., H, dk].
+    """
+    x = np.asarray(x, np.float64)
+    if channels is not None:
+        ch = np.asarray(channels)
+        H = x.shape[-2]
+        assert ch.ndim == 2 and ch.shape[0] == H
+        x = np.stack([x[..., h, :][..., ch[h]] for h in range(H)], axis=-2)
+    if l2norm:
+        nrm = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+        safe = np.where(nrm > 0.0, nrm, 1.0)
+        x = np.where(nrm > 0.0, x / safe, 0.0)
+    return x * float(scale)
+
+
+def gdn_prefill_qk(q_raw, k_raw, v, alpha, beta, S0=None, *, channels=None,
+                   l2norm=True, q_scale=1.0, heads=None):
+    """The recurrence on transformed inputs: q = qk_transform(q_raw, ...,
+    scale=q_scale), k = qk_transform(k_raw, ...) (no scale), then
+    gdn_prefill.  q_raw, k_raw [B, T, H, dk_in]."""
+    q = qk_transform(q_raw, channels, l2norm, q_scale)
+    k = qk_transform(k_raw, channels, l2norm, 1.0)
+    return gdn_prefill(q, k, v, alpha, beta, S0, heads=heads)
+
+
+def gdn_decode_step_qk(q_raw, k_raw, v, alpha, beta, S, *, channels=None,
+                       l2norm=True, q_scale=1.0):
+    """One decode token on transformed inputs; q_raw, k_raw [B, H, dk_in]."""
+    q = qk_transform(q_raw, channels, l2norm, q_scale)
+    k = qk_transform(k_raw, channels, l2norm, 1.0)
+    return gdn_decode_step(q, k, v, alpha, beta, S)
 
 
 # ---------------------------------------------------------------------------

@@ -91,3 +91,84 @@ def test_mutant_is_caught(monkeypatch, mutation):
         except (AssertionError, ValueError, IndexError):
             failures += 1
     assert failures > 0, f"no pin catches the '{mutation}' slip"
+
+
+# --- the input path (qk_transform / gdn_prefill_qk / gdn_decode_step_qk) ---
+
+from tests import test_oracle_qk_pins as qk_pins  # noqa: E402
+
+QK_PIN_TESTS = [
+    qk_pins.test_worked_example_kept_channels,
+    qk_pins.test_selection_indexes_per_head,
+    qk_pins.test_unit_norm_over_kept_and_direction,
+    qk_pins.test_norm_is_per_token_and_scale_invariant,
+    qk_pins.test_zero_vector_maps_to_zero_and_only_decays_the_state,
+    qk_pins.test_query_scale_scales_outputs_only,
+    qk_pins.test_zero_padding_embedding,
+    qk_pins.test_decode_step_qk_is_one_token_of_prefill_qk,
+    qk_pins.test_beta_one_write_stores_value_along_normalised_key,
+]
+
+QK_MUTANTS = ["normalise_before_select", "next_heads_subset", "scale_on_keys",
+              "norm_over_tokens", "no_renormalisation"]
+
+
+def _make_qk(mutation):
+    def transform(x, channels=None, l2norm=True, scale=1.0):
+        x = np.asarray(x, np.float64)
+        if mutation == "normalise_before_select" and l2norm:
+            x = x / np.linalg.norm(x, axis=-1, keepdims=True)
+        if channels is not None:
+            ch = np.asarray(channels)
+            H = x.shape[-2]
+            off = 1 if mutation == "next_heads_subset" else 0
+            x = np.stack([x[..., h, :][..., ch[(h + off) % H]] for h in range(H)], axis=-2)
+        if l2norm and mutation not in ("normalise_before_select", "no_renormalisation"):
+            if mutation == "norm_over_tokens" and x.ndim >= 3:
+                nrm = np.sqrt(np.mean(np.sum(x * x, axis=-1, keepdims=True), axis=-3,
+                                      keepdims=True))
+            else:
+                nrm = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+            x = np.where(nrm > 0, x / np.where(nrm > 0, nrm, 1.0), 0.0)
+        return x * float(scale)
+
+    def prefill_qk(q_raw, k_raw, v, alpha, beta, S0=None, *, channels=None,
+                   l2norm=True, q_scale=1.0, heads=None):
+        ks = q_scale if mutation == "scale_on_keys" else 1.0
+        q = transform(q_raw, channels, l2norm, q_scale)
+        k = transform(k_raw, channels, l2norm, ks)
+        return orc.gdn_prefill(q, k, v, alpha, beta, S0, heads=heads)
+
+    def decode_qk(q_raw, k_raw, v, alpha, beta, S, *, channels=None,
+                  l2norm=True, q_scale=1.0):
+        ks = q_scale if mutation == "scale_on_keys" else 1.0
+        q = transform(q_raw, channels, l2norm, q_scale)
+        k = transform(k_raw, channels, l2norm, ks)
+        return orc.gdn_decode_step(q, k, v, alpha, beta, S)
+
+    return transform, prefill_qk, decode_qk
+
+
+def _swap_qk(monkeypatch, mutation):
+    t, p, d = _make_qk(mutation)
+    monkeypatch.setattr(orc, "qk_transform", t)
+    monkeypatch.setattr(orc, "gdn_prefill_qk", p)
+    monkeypatch.setattr(orc, "gdn_decode_step_qk", d)
+
+
+def test_unmutated_input_path_copy_passes(monkeypatch):
+    _swap_qk(monkeypatch, "none")
+    for t in QK_PIN_TESTS:
+        t()
+
+
+@pytest.mark.parametrize("mutation", QK_MUTANTS)
+def test_input_path_mutant_is_caught(monkeypatch, mutation):
+    _swap_qk(monkeypatch, mutation)
+    failures = 0
+    for t in QK_PIN_TESTS:
+        try:
+            t()
+        except (AssertionError, ValueError, IndexError):
+            failures += 1
+    assert failures > 0, f"no pin catches the '{mutation}' slip"

@@ -224,6 +224,45 @@ def generic(B: int, T: int, H: int, dk: int, dv: int, seed: int,
     return _finish(q, k, v, alpha, beta, S0, dtype, seed, name, idx)
 
 
+def raw_qk(B: int, T: int, H: int, dk_in: int, dv: int, seed: int,
+           dtype: str = "bf16", channel_idx: Optional[np.ndarray] = None,
+           log_alpha_range=(0.001, 0.1), S0_scale: Optional[float] = None,
+           rows: Optional[Sequence[int]] = None,
+           name: str = "raw-qk") -> GdnInputs:
+    """Inputs of a layer whose query/key normalisation and channel selection
+    are left to the recurrence's own input path: q and k are raw
+    dk_in-wide projection outputs, NOT normalised and NOT gathered.
+
+    q, k = N(0, I) directions times a per-token magnitude exp(N(0, 0.5^2)),
+    so every token has its own norm; v ~ N(0, I); beta = sigmoid(N(0, 1));
+    log alpha ~ -U(range); S0 ~ S0_scale * N(0, 1) of the kept width, or
+    None.  channel_idx ([H, dk] int) is returned as .channel_idx and only
+    sets the width of S0.  Row b is drawn from PCG64(seed).jumped(b).
+    """
+    rows = list(range(B)) if rows is None else [int(r) for r in rows]
+    idx = None if channel_idx is None else np.asarray(channel_idx, np.int32)
+    dk = dk_in if idx is None else idx.shape[1]
+    n = len(rows)
+    q = np.empty((n, T, H, dk_in), np.float32)
+    k = np.empty((n, T, H, dk_in), np.float32)
+    v = np.empty((n, T, H, dv), np.float32)
+    beta = np.empty((n, T, H), np.float32)
+    alpha = np.empty((n, T, H), np.float32)
+    S0 = None if S0_scale is None else np.empty((n, H, dv, dk), np.float32)
+    for i, b in enumerate(rows):
+        assert 0 <= b < B
+        rng = np.random.Generator(np.random.PCG64(seed).jumped(b))
+        for x in (q, k):
+            mag = np.exp(0.5 * rng.standard_normal((T, H, 1))).astype(np.float32)
+            x[i] = mag * rng.standard_normal((T, H, dk_in), dtype=np.float32)
+        v[i] = rng.standard_normal((T, H, dv), dtype=np.float32)
+        beta[i] = _sigmoid(rng.standard_normal((T, H)))
+        alpha[i] = _decay(rng, (T, H), *log_alpha_range)
+        if S0 is not None:
+            S0[i] = (S0_scale * rng.standard_normal((H, dv, dk))).astype(np.float32)
+    return _finish(q, k, v, alpha, beta, S0, dtype, seed, name, idx)
+
+
 def pruning_subsets(config: int, H: int = 16, dk: int = 128,
                     dk_keep: int = 64) -> np.ndarray:
     """The fixed per-head channel subsets P_I of a channel-pruned layer
