@@ -40,6 +40,13 @@ SIGNATURES = {
                               _i, _i, _i, _vp, _sz, _vp]),
     "gdn_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                              _i, _i, _i, _i, _i, _i, _vp]),
+    "gdn_prefill_qk_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "gdn_prefill_qk": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                            _i, _i, _i, _i, _i, _i, _vp, _i, ctypes.c_float,
+                            _i, _i, _vp, _sz, _vp]),
+    "gdn_decode_step_qk": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _i, _i, _i, _i, _i, _vp, _i, ctypes.c_float,
+                                _i, _i, _vp]),
     "gdn_truncate_workspace_bytes": (_sz, [_i, _i, _i]),
     "gdn_truncate_rank": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
 }
@@ -209,6 +216,120 @@ def prefill_scan(q, k, v, S0, o, ST, workspace: torch.Tensor,
                               _DTYPE_CODE[o.dtype], _ptr(workspace),
                               workspace.numel(), _stream_handle(q, stream))
     _check(st, "gdn_prefill_scan")
+
+
+# ---------------------------------------------------------------------------
+# the input path fused into the kernels (channel subset, L2 norm, q scale)
+# ---------------------------------------------------------------------------
+
+def _channels_arg(channels, H: int, dk_in: int, dev, validate: bool):
+    """(channels tensor or None, kept width)."""
+    if channels is None:
+        return None, dk_in
+    _dev_tensor(channels, "channels", (torch.int32,))
+    if channels.dim() != 2 or channels.shape[0] != H:
+        raise ValueError(f"channels: shape {tuple(channels.shape)} is not [H={H}, dk]")
+    if channels.device != dev:
+        raise ValueError("channels must be on the same device as q")
+    if validate and channels.numel() and (int(channels.min()) < 0 or
+                                          int(channels.max()) >= dk_in):
+        raise ValueError(f"channels: indices must lie in [0, {dk_in})")
+    return channels, channels.shape[1]
+
+
+def prefill_qk_workspace_bytes(B: int, T: int, H: int, dk: int, dv: int,
+                               in_dtype=torch.bfloat16, gather: bool = False) -> int:
+    return int(lib.gdn_prefill_qk_workspace_bytes(B, T, H, dk, dv,
+                                                  _DTYPE_CODE[in_dtype], int(gather)))
+
+
+def prefill_qk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+               alpha: torch.Tensor, beta: torch.Tensor,
+               S0: Optional[torch.Tensor] = None, *,
+               channels: Optional[torch.Tensor] = None,
+               l2norm: bool = True, q_scale: float = 1.0,
+               out_dtype: Optional[torch.dtype] = None,
+               o: Optional[torch.Tensor] = None,
+               ST: Optional[torch.Tensor] = None,
+               final_state: bool = True,
+               workspace: Optional[torch.Tensor] = None,
+               validate: bool = True,
+               stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Prefill from the raw projection output: q, k [B, T, H, dk_in] are
+    reduced to the channels `channels[h]` of each head h (int32 [H, dk],
+    dk in {64, 128}; None keeps all dk_in = dk channels), normalised over
+    the kept channels (if l2norm) and q is multiplied by q_scale, all inside
+    the kernels.  Other arguments as prefill().  `validate` checks the
+    channel indices on the host (one device sync); the library does not."""
+    _dev_tensor(q, "q", _DTYPE_CODE)
+    B, T, H, dk_in = q.shape
+    _dev_tensor(k, "k", (q.dtype,), q.shape)
+    channels, dk = _channels_arg(channels, H, dk_in, q.device, validate)
+    _dev_tensor(v, "v", (q.dtype,))
+    if tuple(v.shape[:3]) != (B, T, H) or v.dim() != 4:
+        raise ValueError(f"v: shape {tuple(v.shape)} incompatible with q")
+    dv = v.shape[3]
+    _dev_tensor(alpha, "alpha", (torch.float32,), (B, T, H))
+    _dev_tensor(beta, "beta", (torch.float32,), (B, T, H))
+    if S0 is not None:
+        _dev_tensor(S0, "S0", (torch.float32,), (B, H, dv, dk))
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=q.device)
+    _dev_tensor(o, "o", (out_dtype,), (B, T, H, dv))
+    if ST is None and final_state:
+        ST = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    if ST is not None:
+        _dev_tensor(ST, "ST", (torch.float32,), (B, H, dv, dk))
+    need = prefill_qk_workspace_bytes(B, T, H, dk, dv, q.dtype, channels is not None)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib.gdn_prefill_qk(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                            _ptr(S0), _ptr(o), _ptr(ST), B, T, H, dk, dv, dk_in,
+                            _ptr(channels), int(l2norm), float(q_scale),
+                            _DTYPE_CODE[q.dtype], _DTYPE_CODE[out_dtype],
+                            _ptr(workspace), workspace.numel(),
+                            _stream_handle(q, stream))
+    _check(st, "gdn_prefill_qk")
+    return o, ST
+
+
+def decode_step_qk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                   alpha: torch.Tensor, beta: torch.Tensor, S: torch.Tensor, *,
+                   channels: Optional[torch.Tensor] = None,
+                   l2norm: bool = True, q_scale: float = 1.0,
+                   S_out: Optional[torch.Tensor] = None,
+                   o: Optional[torch.Tensor] = None,
+                   out_dtype: Optional[torch.dtype] = None,
+                   validate: bool = True,
+                   stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """One decode token from the raw projection output q, k [B, H, dk_in];
+    the input path as in prefill_qk, the rest as decode_step()."""
+    _dev_tensor(q, "q", _DTYPE_CODE)
+    B, H, dk_in = q.shape
+    _dev_tensor(k, "k", (q.dtype,), q.shape)
+    channels, dk = _channels_arg(channels, H, dk_in, q.device, validate)
+    _dev_tensor(v, "v", (q.dtype,))
+    if v.dim() != 3 or tuple(v.shape[:2]) != (B, H):
+        raise ValueError(f"v: shape {tuple(v.shape)} incompatible with q")
+    dv = v.shape[2]
+    _dev_tensor(alpha, "alpha", (torch.float32,), (B, H))
+    _dev_tensor(beta, "beta", (torch.float32,), (B, H))
+    _dev_tensor(S, "S", (torch.float32,), (B, H, dv, dk))
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=out_dtype, device=q.device)
+    _dev_tensor(o, "o", (out_dtype,), (B, H, dv))
+    if S_out is None:
+        S_out = torch.empty_like(S)
+    _dev_tensor(S_out, "S_out", (torch.float32,), (B, H, dv, dk))
+    st = lib.gdn_decode_step_qk(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                _ptr(beta), _ptr(S), _ptr(S_out), _ptr(o),
+                                B, H, dk, dv, dk_in, _ptr(channels), int(l2norm),
+                                float(q_scale), _DTYPE_CODE[q.dtype],
+                                _DTYPE_CODE[out_dtype], _stream_handle(q, stream))
+    _check(st, "gdn_decode_step_qk")
+    return o, S_out
 
 
 # ---------------------------------------------------------------------------

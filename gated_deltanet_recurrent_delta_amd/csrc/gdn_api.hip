@@ -33,24 +33,58 @@ int check_prefill_shape(int B, int T, int H, int dk, int dv, int in_dtype,
   return GDN_OK;
 }
 
+// Checks of the input-path arguments: without channels the rows are dk
+// wide; with them any width up to 2^20, the index table 16-byte aligned.
+int check_qk(int dk, int dk_in, const int* channels, int l2norm) {
+  if (l2norm != 0 && l2norm != 1) return GDN_EINVAL;
+  if (channels == nullptr) return dk_in == dk ? GDN_OK : GDN_ESHAPE;
+  if (dk_in < 1 || dk_in > (1 << 20)) return GDN_ESHAPE;
+  if (!aligned(channels, 16)) return GDN_EINVAL;
+  return GDN_OK;
+}
+
+// Bytes of workspace of a prefill with the input path: the plain prefill's,
+// then (with a channel subset) the gathered q/k copy.
+size_t prefill_qk_ws_bytes(int B, int T, int H, int dk, int dv, int in_dtype,
+                           bool gather) {
+  const size_t base = prefill_ws_bytes(B, T, H, dk, dv);
+  if (base == 0 || !gather) return base;
+  return gdn::align256(base) + gdn::qk_copy_bytes(B, T, H, dk, in_dtype);
+}
+
 // Validation and launch of the prepare phase.  fp32 outputs: also store the
-// lo part of P, which only the fp32-output scan reads.
+// lo part of P, which only the fp32-output scan reads.  q/k rows read whole
+// need 16-byte alignment; gathered ones only their element's.
 int prepare_checked(const void* q, const void* k, const float* alpha,
                     const float* beta, int B, int T, int H, int dk, int dv,
-                    int in_dtype, int out_dtype, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    int in_dtype, int out_dtype, const gdn::QkArgs& qa,
+                    void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_prefill_shape(B, T, H, dk, dv, in_dtype, out_dtype);
   if (st != GDN_OK) return st;
   if (T == 0) return GDN_OK;
   if (!q || !k || !alpha || !beta) return GDN_EINVAL;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(alpha, 4) ||
+  const uintptr_t qa_align = qa.chan ? (in_dtype == GDN_BF16 ? 2 : 4) : 16;
+  if (!aligned(q, qa_align) || !aligned(k, qa_align) || !aligned(alpha, 4) ||
       !aligned(beta, 4))
     return GDN_EINVAL;
   if (!workspace || !aligned(workspace, 16)) return GDN_EWORKSPACE;
-  if (workspace_bytes < prefill_ws_bytes(B, T, H, dk, dv)) return GDN_EWORKSPACE;
+  if (workspace_bytes < prefill_qk_ws_bytes(B, T, H, dk, dv, in_dtype, qa.chan != nullptr))
+    return GDN_EWORKSPACE;
   return to_status(gdn::launch_prefill_prepare(
       q, k, alpha, beta, static_cast<float*>(workspace), B, T, H, dk, in_dtype,
-      out_dtype == GDN_F32, static_cast<hipStream_t>(stream)));
+      out_dtype == GDN_F32, qa, static_cast<hipStream_t>(stream)));
+}
+
+// The scan's checks that do not depend on q/k (shared by the prefills).
+int check_scan_rest(const void* v, void* o, const float* S0, const float* ST,
+                    int B, int H, int dk, int dv) {
+  if (!v || !o) return GDN_EINVAL;
+  if (!aligned(v, 16) || !aligned(o, 16)) return GDN_EINVAL;
+  if ((S0 && !aligned(S0, 16)) || (ST && !aligned(ST, 16))) return GDN_EINVAL;
+  const size_t nstate = (size_t)B * H * dv * dk;
+  if (ST && S0 && ST != S0 && (ST < S0 + nstate && S0 < ST + nstate))
+    return GDN_EINVAL;                               // partial overlap
+  return GDN_OK;
 }
 
 }  // namespace
@@ -93,7 +127,7 @@ int gdn_prefill_prepare(const void* q, const void* k, const float* alpha,
                         int in_dtype, int out_dtype, void* workspace,
                         size_t workspace_bytes, void* stream) {
   return prepare_checked(q, k, alpha, beta, B, T, H, dk, dv, in_dtype, out_dtype,
-                         workspace, workspace_bytes, stream);
+                         gdn::qk_identity(dk), workspace, workspace_bytes, stream);
 }
 
 int gdn_prefill_scan(const void* q, const void* k, const void* v,
@@ -139,7 +173,8 @@ int gdn_prefill(const void* q, const void* k, const void* v,
     if (ST && S0 && ST != S0 && (ST < S0 + nstate && S0 < ST + nstate))
       return GDN_EINVAL;
     st = prepare_checked(q, k, alpha, beta, B, T, H, dk, dv, in_dtype,
-                         out_dtype, workspace, workspace_bytes, stream);
+                         out_dtype, gdn::qk_identity(dk), workspace,
+                         workspace_bytes, stream);
     if (st != GDN_OK) return st;
   }
   return gdn_prefill_scan(q, k, v, S0, o, ST, B, T, H, dk, dv, in_dtype,
@@ -164,8 +199,83 @@ int gdn_decode_step(const void* q, const void* k, const void* v,
   if (S_out != S_in && S_out < S_in + nstate && S_in < S_out + nstate)
     return GDN_EINVAL;                               // partial overlap
   return to_status(gdn::launch_decode(q, k, v, alpha, beta, S_in, S_out, o,
-                                      B * H, dk, dv, in_dtype, out_dtype,
+                                      B * H, H, dk, dv, in_dtype, out_dtype,
+                                      gdn::qk_identity(dk),
                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t gdn_prefill_qk_workspace_bytes(int B, int T, int H, int dk, int dv,
+                                      int in_dtype, int gather) {
+  if (!dims_ok(dk, dv) || !dtype_ok(in_dtype)) return 0;
+  return prefill_qk_ws_bytes(B, T, H, dk, dv, in_dtype, gather != 0);
+}
+
+int gdn_prefill_qk(const void* q, const void* k, const void* v,
+                   const float* alpha, const float* beta, const float* S0,
+                   void* o, float* ST, int B, int T, int H, int dk, int dv,
+                   int dk_in, const int* channels, int l2norm, float q_scale,
+                   int in_dtype, int out_dtype, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  int st = check_prefill_shape(B, T, H, dk, dv, in_dtype, out_dtype);
+  if (st != GDN_OK) return st;
+  st = check_qk(dk, dk_in, channels, l2norm);
+  if (st != GDN_OK) return st;
+  if (T == 0) {
+    // no token: the final state is the initial one (q, k never read)
+    return gdn_prefill_scan(q, k, v, S0, o, ST, B, T, H, dk, dv, in_dtype,
+                            out_dtype, workspace, workspace_bytes, stream);
+  }
+  st = check_scan_rest(v, o, S0, ST, B, H, dk, dv);
+  if (st != GDN_OK) return st;
+  gdn::QkArgs qa{channels, dk_in, l2norm, q_scale, nullptr};
+  if (channels) {
+    if (!workspace) return GDN_EWORKSPACE;
+    qa.qk_out = static_cast<char*>(workspace) +
+                gdn::align256(prefill_ws_bytes(B, T, H, dk, dv));
+  }
+  st = prepare_checked(q, k, alpha, beta, B, T, H, dk, dv, in_dtype,
+                       out_dtype, qa, workspace, workspace_bytes, stream);
+  if (st != GDN_OK) return st;
+  // the scan reads the kept channels: the gathered copy, or q/k themselves
+  const void* qs = q;
+  const void* ks = k;
+  if (channels) {
+    ks = qa.qk_out;
+    qs = static_cast<const char*>(qa.qk_out) +
+         gdn::qk_copy_bytes(B, T, H, dk, in_dtype) / 2;
+  }
+  return to_status(gdn::launch_prefill_scan(
+      qs, ks, v, S0, o, ST, workspace, B, T, H, dk, dv, in_dtype, out_dtype,
+      static_cast<hipStream_t>(stream)));
+}
+
+int gdn_decode_step_qk(const void* q, const void* k, const void* v,
+                       const float* alpha, const float* beta,
+                       const float* S_in, float* S_out, void* o, int B, int H,
+                       int dk, int dv, int dk_in, const int* channels,
+                       int l2norm, float q_scale, int in_dtype, int out_dtype,
+                       void* stream) {
+  if (B <= 0 || H <= 0) return GDN_EINVAL;
+  if ((long long)B * H * dv > 0x7FFFFFFFLL) return GDN_EINVAL;
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return GDN_ESHAPE;
+  if (!dims_ok(dk, dv)) return GDN_ESHAPE;
+  int st = check_qk(dk, dk_in, channels, l2norm);
+  if (st != GDN_OK) return st;
+  if (!q || !k || !v || !alpha || !beta || !S_in || !S_out || !o)
+    return GDN_EINVAL;
+  const uintptr_t qk_align = channels ? (in_dtype == GDN_BF16 ? 2 : 4) : 16;
+  if (!aligned(q, qk_align) || !aligned(k, qk_align) || !aligned(v, 16) ||
+      !aligned(o, 16) || !aligned(S_in, 16) || !aligned(S_out, 16) ||
+      !aligned(alpha, 4) || !aligned(beta, 4))
+    return GDN_EINVAL;
+  if ((long long)B * H * dk_in > 0x7FFFFFFFLL) return GDN_EINVAL;
+  const size_t nstate = (size_t)B * H * dv * dk;
+  if (S_out != S_in && S_out < S_in + nstate && S_in < S_out + nstate)
+    return GDN_EINVAL;                               // partial overlap
+  const gdn::QkArgs qa{channels, dk_in, l2norm, q_scale, nullptr};
+  return to_status(gdn::launch_decode(q, k, v, alpha, beta, S_in, S_out, o,
+                                      B * H, H, dk, dv, in_dtype, out_dtype,
+                                      qa, static_cast<hipStream_t>(stream)));
 }
 
 size_t gdn_truncate_workspace_bytes(int BH, int dv, int dk) {

@@ -17,7 +17,10 @@
 // of four rows.  A wave issues its few vector loads (k, q, v) first and then
 // every state load, and reduces and stores each group of four rows as soon
 // as its loads have arrived, so stores start while later rows are still in
-// flight.  The two row dot products are reduced with four DPP steps and the
+// flight.  The optional input path (per-head channel subset of dk_in-wide
+// q/k rows, L2 normalisation over the kept channels, query scale; "On State
+// Reduction in Linear Attention", Sec. 3.2-3.3) is applied to k and q in
+// registers before the row loop.  The two row dot products are reduced with four DPP steps and the
 // state is read and written with non-temporal accesses.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
@@ -25,12 +28,15 @@
 namespace gdn {
 
 // DK: key width; NG: groups of 4 rows per wave (rows per wave = 4 NG).
-template <int DK, int NG, typename TIn, typename TOut>
+// GATHER: q and k are dk_in-wide rows of which head h keeps the channels
+// qa.chan[h][0 .. DK-1] (the input path of a channel-pruned layer).
+template <int DK, int NG, typename TIn, typename TOut, bool GATHER>
 __global__ __launch_bounds__(256) void decode_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, const float* S_in, float* S_out,
-    TOut* __restrict__ o, int BH, int dv, int slices_per_head) {
+    TOut* __restrict__ o, int BH, int dv, int slices_per_head, int H,
+    QkArgs qa) {
   constexpr int F = DK / 64;            // float4 per lane per row
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -42,10 +48,22 @@ __global__ __launch_bounds__(256) void decode_kernel(
   const int row0 = slice * (4 * NG);
 
   float4 kk[F], qq[F];
+  if constexpr (GATHER) {
+    const int* ch = qa.chan + (size_t)(head % H) * DK;
+    const TIn* kr = k + (size_t)head * qa.dk_in;
+    const TIn* qr = q + (size_t)head * qa.dk_in;
 #pragma unroll
-  for (int f = 0; f < F; ++f) {
-    kk[f] = load4(k + (size_t)head * DK + 64 * f + 4 * sub);
-    qq[f] = load4(q + (size_t)head * DK + 64 * f + 4 * sub);
+    for (int f = 0; f < F; ++f) {
+      const int4 c = *reinterpret_cast<const int4*>(ch + 64 * f + 4 * sub);
+      kk[f] = make_float4(load1(kr + c.x), load1(kr + c.y), load1(kr + c.z), load1(kr + c.w));
+      qq[f] = make_float4(load1(qr + c.x), load1(qr + c.y), load1(qr + c.z), load1(qr + c.w));
+    }
+  } else {
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      kk[f] = load4(k + (size_t)head * DK + 64 * f + 4 * sub);
+      qq[f] = load4(q + (size_t)head * DK + 64 * f + 4 * sub);
+    }
   }
   const float a = alpha[head];
   const float b = beta[head];
@@ -62,6 +80,31 @@ __global__ __launch_bounds__(256) void decode_kernel(
     for (int f = 0; f < F; ++f)
       s[g][f] = __builtin_nontemporal_load(
           reinterpret_cast<const floatx4*>(rowp + 64 * f + 4 * sub));
+  }
+
+  // input path: normalise k and q over the kept channels (the 16 lanes of
+  // a row hold all DK of them), scale q
+  if (qa.l2norm) {
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      sk += kk[f].x * kk[f].x + kk[f].y * kk[f].y + kk[f].z * kk[f].z + kk[f].w * kk[f].w;
+      sq += qq[f].x * qq[f].x + qq[f].y * qq[f].y + qq[f].z * qq[f].z + qq[f].w * qq[f].w;
+    }
+    sk = sum16(sk);
+    sq = sum16(sq);
+    const float nk = sk > 0.f ? 1.f / sqrtf(sk) : 0.f;
+    const float nq = (sq > 0.f ? 1.f / sqrtf(sq) : 0.f) * qa.qscale;
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      kk[f].x *= nk; kk[f].y *= nk; kk[f].z *= nk; kk[f].w *= nk;
+      qq[f].x *= nq; qq[f].y *= nq; qq[f].z *= nq; qq[f].w *= nq;
+    }
+  } else if (qa.qscale != 1.f) {
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      qq[f].x *= qa.qscale; qq[f].y *= qa.qscale; qq[f].z *= qa.qscale; qq[f].w *= qa.qscale;
+    }
   }
 
   float kq = 0.f;
@@ -103,22 +146,27 @@ template <int DK, int NG, typename TIn, typename TOut>
 static void launch_decode_g(hipStream_t stream, const void* q, const void* k,
                             const void* v, const float* alpha,
                             const float* beta, const float* S_in, float* S_out,
-                            void* o, int BH, int dv) {
+                            void* o, int BH, int H, int dv, const QkArgs& qa) {
   const int slices = dv / (4 * NG);
   const long waves = (long)BH * slices;
   const dim3 grid((unsigned)((waves + 3) / 4));
-  hipLaunchKernelGGL((decode_kernel<DK, NG, TIn, TOut>), grid, dim3(256), 0,
-                     stream, static_cast<const TIn*>(q),
-                     static_cast<const TIn*>(k), static_cast<const TIn*>(v),
-                     alpha, beta, S_in, S_out, static_cast<TOut*>(o), BH, dv,
-                     slices);
+#define GDN_DEC_K(G)                                                               \
+  hipLaunchKernelGGL((decode_kernel<DK, NG, TIn, TOut, G>), grid, dim3(256), 0,     \
+                     stream, static_cast<const TIn*>(q),                           \
+                     static_cast<const TIn*>(k), static_cast<const TIn*>(v),       \
+                     alpha, beta, S_in, S_out, static_cast<TOut*>(o), BH, dv,      \
+                     slices, H, qa)
+  if (qa.chan != nullptr) GDN_DEC_K(true);
+  else GDN_DEC_K(false);
+#undef GDN_DEC_K
 }
 
 template <int DK, typename TIn, typename TOut>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v,
                                   const float* alpha, const float* beta,
                                   const float* S_in, float* S_out, void* o,
-                                  int BH, int dv, hipStream_t stream) {
+                                  int BH, int H, int dv, const QkArgs& qa,
+                                  hipStream_t stream) {
   // Rows per wave, measured on MI355X at H=16, dv=128 over 18 rotating state
   // sets (one process, one GPU): at dk=128 four rows per wave is best at every
   // batch (B=64: 22.9 us per step, against 23.0 with 8 rows and 23.5 with
@@ -133,28 +181,28 @@ static hipError_t launch_decode_t(const void* q, const void* k, const void* v,
   if constexpr (DK == 64) {
     if ((long)BH * dv / 16 >= kFill) {
       launch_decode_g<DK, 4, TIn, TOut>(stream, q, k, v, alpha, beta, S_in,
-                                        S_out, o, BH, dv);
+                                        S_out, o, BH, H, dv, qa);
       return hipGetLastError();
     }
     if ((long)BH * dv / 8 >= kFill) {
       launch_decode_g<DK, 2, TIn, TOut>(stream, q, k, v, alpha, beta, S_in,
-                                        S_out, o, BH, dv);
+                                        S_out, o, BH, H, dv, qa);
       return hipGetLastError();
     }
   }
   launch_decode_g<DK, 1, TIn, TOut>(stream, q, k, v, alpha, beta, S_in, S_out,
-                                    o, BH, dv);
+                                    o, BH, H, dv, qa);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const void* q, const void* k, const void* v,
                          const float* alpha, const float* beta,
                          const float* S_in, float* S_out, void* o, int BH,
-                         int dk, int dv, int in_dtype, int out_dtype,
-                         hipStream_t stream) {
+                         int H, int dk, int dv, int in_dtype, int out_dtype,
+                         const QkArgs& qa, hipStream_t stream) {
 #define GDN_DEC_DT(DK, TI, TO)                                               \
   return launch_decode_t<DK, TI, TO>(q, k, v, alpha, beta, S_in, S_out, o,   \
-                                     BH, dv, stream)
+                                     BH, H, dv, qa, stream)
   const bool ib = in_dtype == 1, ob = out_dtype == 1;
   if (dk == 128) {
     if (ib && ob) GDN_DEC_DT(128, bf16, bf16);

@@ -31,6 +31,26 @@ struct SegArgs {
   void* xhat;        // [BH][T][dk] bf16, x^_t for tokens of segments >= 1
 };
 
+// The input path of a channel-pruned layer, applied inside the kernels
+// ("On State Reduction in Linear Attention", Sec. 3.2-3.3: keep a per-head
+// subset of the query/key channels and recompute the normalisation over the
+// kept channels), plus an optional query scale.
+struct QkArgs {
+  const int* chan;   // [H][dk] kept channels of each head's dk_in-wide q/k
+                     // rows, or nullptr: the rows are dk wide, all kept
+  int dk_in;         // width of the q/k rows in memory (dk without chan)
+  int l2norm;        // 1: divide q and k by their norms over the kept channels
+  float qscale;      // multiplies the (normalised) query
+  void* qk_out;      // prefill with chan: the gathered copy, k then q,
+                     // [2][B][T][H][dk] in the input type (the scan reads it)
+};
+inline QkArgs qk_identity(int dk) { return QkArgs{nullptr, dk, 0, 1.f, nullptr}; }
+
+// Bytes of the gathered q/k copy of a prefill with a channel subset.
+inline size_t qk_copy_bytes(int B, int T, int H, int dk, int in_dtype) {
+  return 2 * (size_t)B * T * H * dk * (in_dtype == 1 ? 2 : 4);
+}
+
 struct PrefillPlan {
   int nchunks, nseg, seg_chunks;
   size_t chunk_bytes;       // per-chunk tiles (prepare -> scan)
@@ -86,14 +106,15 @@ inline PrefillPlan plan_prefill(int B, int T, int H, int dk, int dv) {
 hipError_t launch_decode(const void* q, const void* k, const void* v,
                          const float* alpha, const float* beta,
                          const float* S_in, float* S_out, void* o, int BH,
-                         int dk, int dv, int in_dtype, int out_dtype,
-                         hipStream_t stream);
+                         int H, int dk, int dv, int in_dtype, int out_dtype,
+                         const QkArgs& qa, hipStream_t stream);
 
 // write_pl: also store the lo part of P (read only when outputs are fp32).
 hipError_t launch_prefill_prepare(const void* q, const void* k,
                                   const float* alpha, const float* beta,
                                   float* ws, int B, int T, int H, int dk,
-                                  int in_dtype, bool write_pl, hipStream_t stream);
+                                  int in_dtype, bool write_pl, const QkArgs& qa,
+                                  hipStream_t stream);
 
 // Phase 1 (+ phases 2 and 3 when the plan segments the sequence).  `ws` is
 // the whole workspace (per-chunk tiles first, then the segment buffers).

@@ -15,7 +15,15 @@
 //     O   = diag(gamma) Q S^T + P U,  P_ji = e^{g_j - g_i} q_j.k_i (i <= j)
 //     S' = gamma_C S + U^T diag(e^{g_C - g}) K
 //
-// This is an exact re-association of the sequential recurrence.
+// This is an exact re-association of the sequential recurrence.  The
+// workspace holds T diag(beta) (so the scan forms V - diag(gamma) K S^T and
+// one product), and the optional input path (keep a per-head subset of the
+// query/key channels, renormalise over the kept channels, scale the query;
+// "On State Reduction in Linear Attention", Sec. 3.2-3.3) enters only as
+// per-token factors: with q_j = nq_j q~_j and k_j = nk_j k~_j (q~, k~ the
+// kept raw channels, nq_j = scale / |q~_j|, nk_j = 1 / |k~_j|), the raw
+// rows stay exact MFMA operands and nk, nq are folded into A, P and the
+// per-token decay rows the scan reads (gamma nq, gamma nk, e^{g_C - g} nk).
 //
 // Two kernels:
 //  * prepare_kernel -- one wave per (batch, head, chunk), fully parallel.
@@ -60,7 +68,11 @@ constexpr int kWsTh = 0;                    // bf16 [64][64] hi part of T
 constexpr int kWsTl = 8192;                 // bf16 [64][64] lo part of T
 constexpr int kWsPh = 16384;                // bf16 [64][64] hi part of P
 constexpr int kWsPl = 24576;                // bf16 [64][64] lo part of P
-constexpr int kWsG = 32768;                 // fp32 [4][64]: g, beta, gamma, e^{g_C - g}
+// fp32 [4][64] per-token rows: gamma nq (query side, for diag(gamma) Q S^T),
+// gamma_C (the chunk's total decay, repeated), gamma nk (key side, for
+// V - diag(gamma) K S^T) and e^{g_C - g} nk (for the state update); nq = nk
+// = 1 without the input path.
+constexpr int kWsG = 32768;
 static_assert(kWsG + 4 * 4 * C == kChunkWsFloats * 4, "workspace layout");
 
 typedef short short4v __attribute__((ext_vector_type(4)));
@@ -126,6 +138,67 @@ __device__ __forceinline__ void load_row8(const float* p, bf16x8& hi, bf16x8& lo
   split8(x, hi, lo);
 }
 
+// 8 inputs as fp32: consecutive, or gathered at channel indices ci.
+__device__ __forceinline__ void ld8(const bf16* p, float (&x)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = bf16lo(w[j]);
+    x[2 * j + 1] = bf16hi(w[j]);
+  }
+}
+__device__ __forceinline__ void ld8(const float* p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void ld8_gather(const bf16* row, const int (&ci)[8], float (&x)[8]) {
+  const uint16_t* r = reinterpret_cast<const uint16_t*>(row);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = bf16_bits_to_f32(r[ci[e]]);
+}
+__device__ __forceinline__ void ld8_gather(const float* row, const int (&ci)[8], float (&x)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = row[ci[e]];
+}
+// 8 values stored exactly in the input type
+__device__ __forceinline__ void st8(bf16* p, const float (&x)[8]) {
+  const floatx8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  *reinterpret_cast<bf16x8*>(p) = to_bf16x8(v);      // exact: x holds bf16 values
+}
+__device__ __forceinline__ void st8(float* p, const float (&x)[8]) {
+  *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+}
+// MFMA operands of 8 input values: bf16 inputs exactly, fp32 as hi + lo.
+template <bool SPLIT>
+__device__ __forceinline__ void pack8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+  const floatx8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  if constexpr (SPLIT) split8(v, hi, lo);
+  else hi = to_bf16x8(v);
+}
+__device__ __forceinline__ float sumsq8(const float (&x)[8]) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s += x[e] * x[e];
+  return s;
+}
+__device__ __forceinline__ float sumsq8(const bf16x8& x) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float f = (float)x[e];
+    s += f * f;
+  }
+  return s;
+}
+// 1 / |x| from |x|^2 (0 for a zero vector), or 1 without normalisation.
+__device__ __forceinline__ float inv_norm(float ss, int l2norm) {
+  return l2norm ? (ss > 0.f ? 1.f / sqrtf(ss) : 0.f) : 1.f;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -147,17 +220,19 @@ __device__ __forceinline__ constexpr int lower_tile(int mi, int ni) {
 // (with A's diagonal blocks before it) passes through LDS, 17.9 KB per
 // wave, so eight waves share a CU and one wave's loads overlap another's
 // arithmetic.
-template <int DK, typename TIn>
+template <int DK, typename TIn, bool GATHER>
 __global__ __launch_bounds__(64) void prepare_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k,
     const float* __restrict__ alpha, const float* __restrict__ beta,
-    float* __restrict__ ws, int T, int H, int nchunks, int write_pl) {
+    float* __restrict__ ws, int T, int H, int nchunks, int write_pl, QkArgs qa) {
   constexpr bool SPLIT = std::is_same<TIn, float>::value;  // inputs not bf16
   constexpr int NKB = DK / 32;
   constexpr int LDA = C + 4;            // fp32 row stride of the T tile
   __shared__ __attribute__((aligned(16))) float Ts[C * LDA];   // A's diagonal blocks, then T
   __shared__ __attribute__((aligned(16))) float g2s[C];
-  __shared__ float bs[C];
+  __shared__ __attribute__((aligned(16))) float bs[C];
+  __shared__ __attribute__((aligned(16))) float nks[C];       // 1 / |k~_j| (or 1)
+  __shared__ __attribute__((aligned(16))) float nqs[C];       // scale / |q~_j| (or scale)
 
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int t0 = chunk * C;
@@ -168,30 +243,76 @@ __global__ __launch_bounds__(64) void prepare_kernel(
 
   // 1. gates of the chunk first (vector-memory results return in order, so
   //    the prefix sum below does not wait for the K/Q tiles), then K and Q
-  //    rows 16 t + n, k-slots 32 s + 8 g4 .. + 7, straight from HBM.
+  //    rows 16 t + n, k-slots 32 s + 8 g4 .. + 7, straight from HBM: the
+  //    row itself, or (GATHER) the kept channels chan[h][32 s + 8 g4 + e] of
+  //    the dk_in-wide row, which are also written out as the gathered copy
+  //    the scan reads.  ssk/ssq: this lane's part of |k~|^2 and |q~|^2.
   float a_in = 1.f, be = 0.f;               // padding tokens: identity step
   if (lane < nvalid) {
     const size_t gi = ((size_t)b * T + t0 + lane) * H + h;
     a_in = alpha[gi];
     be = beta[gi];
   }
+  int ci[GATHER ? NKB : 1][8];
+  if constexpr (GATHER) {
+#pragma unroll
+    for (int s = 0; s < NKB; ++s) {
+      const int4 c0 = *reinterpret_cast<const int4*>(qa.chan + (size_t)h * DK + 32 * s + 8 * g4);
+      const int4 c1 = *reinterpret_cast<const int4*>(qa.chan + (size_t)h * DK + 32 * s + 8 * g4 + 4);
+      ci[s][0] = c0.x; ci[s][1] = c0.y; ci[s][2] = c0.z; ci[s][3] = c0.w;
+      ci[s][4] = c1.x; ci[s][5] = c1.y; ci[s][6] = c1.z; ci[s][7] = c1.w;
+    }
+  }
+  const int ldin = GATHER ? qa.dk_in : DK;  // row width of q, k in memory
+  TIn* kg = nullptr;                        // GATHER: the gathered copy of k, then q
+  TIn* qg = nullptr;
+  if constexpr (GATHER) {
+    kg = static_cast<TIn*>(qa.qk_out);
+    qg = kg + (size_t)gridDim.z * T * H * DK;
+  }
   bf16x8 Kh[4][NKB], Kl[4][NKB], Qh[4][NKB], Ql[4][NKB];
+  float ssk[4], ssq[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int c = 16 * t + n;
+    const size_t row = ((size_t)b * T + t0 + c) * H + h;           // token row
+    ssk[t] = ssq[t] = 0.f;
 #pragma unroll
     for (int s = 0; s < NKB; ++s) {
       const bf16x8 z = {};
       Kh[t][s] = Kl[t][s] = Qh[t][s] = Ql[t][s] = z;
       if (c < nvalid) {
-        const size_t off = (((size_t)b * T + t0 + c) * H + h) * DK + 32 * s + 8 * g4;
-        load_row8(k + off, Kh[t][s], Kl[t][s]);
-        load_row8(q + off, Qh[t][s], Ql[t][s]);
+        const size_t off = row * DK + 32 * s + 8 * g4;              // kept-width layout
+        if constexpr (GATHER || SPLIT) {
+          float xk[8], xq[8];
+          if constexpr (GATHER) {
+            ld8_gather(k + row * ldin, ci[s], xk);
+            ld8_gather(q + row * ldin, ci[s], xq);
+            st8(kg + off, xk);
+            st8(qg + off, xq);
+          } else {
+            ld8(k + off, xk);
+            ld8(q + off, xq);
+          }
+          pack8<SPLIT>(xk, Kh[t][s], Kl[t][s]);
+          pack8<SPLIT>(xq, Qh[t][s], Ql[t][s]);
+          ssk[t] += sumsq8(xk);
+          ssq[t] += sumsq8(xq);
+        } else {
+          Kh[t][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(k + off));
+          Qh[t][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(q + off));
+          if (qa.l2norm) {
+            ssk[t] += sumsq8(Kh[t][s]);
+            ssq[t] += sumsq8(Qh[t][s]);
+          }
+        }
       }
     }
   }
 
-  // 2. gates: inclusive prefix sum of log alpha inside the chunk
+  // 2. gates: inclusive prefix sum of log alpha inside the chunk (lane =
+  //    token j); the rows that need the norms are written in step 2b
+  float gam, dec, gamC;
   {
     float g = logf(a_in);
 #pragma unroll
@@ -202,13 +323,38 @@ __global__ __launch_bounds__(64) void prepare_kernel(
     const float glast = __shfl(g, 63, 64);
     g2s[lane] = g * kLog2e;
     bs[lane] = be;
-    float* Gw = reinterpret_cast<float*>(wsc + kWsG);
-    Gw[lane] = g;
-    Gw[C + lane] = be;
-    Gw[2 * C + lane] = expf(g);
-    Gw[3 * C + lane] = expf(glast - g);
+    gam = expf(g);
+    dec = expf(glast - g);
+    gamC = expf(glast);
+  }
+
+  // 2b. per-token factors of the input path: the four lanes of a token
+  //     (g4 = 0..3) hold its k-slots; 1 and qscale without normalisation
+  {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float sk = ssk[t], sq = ssq[t];
+      if (qa.l2norm) {
+        sk += __shfl_xor(sk, 16, 64);
+        sk += __shfl_xor(sk, 32, 64);
+        sq += __shfl_xor(sq, 16, 64);
+        sq += __shfl_xor(sq, 32, 64);
+      }
+      if (g4 == 0) {
+        nks[16 * t + n] = inv_norm(sk, qa.l2norm);
+        nqs[16 * t + n] = inv_norm(sq, qa.l2norm) * qa.qscale;
+      }
+    }
   }
   __syncthreads();
+  {
+    float* Gw = reinterpret_cast<float*>(wsc + kWsG);
+    const float nk = nks[lane], nq = nqs[lane];
+    Gw[lane] = gam * nq;
+    Gw[C + lane] = gamC;
+    Gw[2 * C + lane] = gam * nk;
+    Gw[3 * C + lane] = dec * nk;
+  }
 
   // 3. lower tiles of A (decay- and beta-weighted K K^T, strictly lower) and
   //    of P (decay-masked Q K^T), row orientation; P straight to the
@@ -217,7 +363,7 @@ __global__ __launch_bounds__(64) void prepare_kernel(
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
     const int j = 16 * mi + n;                // row of this lane
-    const float gj = g2s[j], bj = bs[j];
+    const float gj = g2s[j], bj = bs[j] * nks[j], qj = nqs[j];
 #pragma unroll
     for (int ni = 0; ni <= mi; ++ni) {
       floatx4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
@@ -235,13 +381,15 @@ __global__ __launch_bounds__(64) void prepare_kernel(
       const int i0 = 16 * ni + 4 * g4;        // first column of this lane
       const float4 gi4 = *reinterpret_cast<const float4*>(&g2s[i0]);
       const float gi[4] = {gi4.x, gi4.y, gi4.z, gi4.w};
+      const float4 nk4 = *reinterpret_cast<const float4*>(&nks[i0]);
+      const float nki[4] = {nk4.x, nk4.y, nk4.z, nk4.w};
       float a[4], p[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = i0 + e;
-        const float decay = (i <= j) ? __builtin_amdgcn_exp2f(gj - gi[e]) : 0.f;
+        const float decay = (i <= j) ? __builtin_amdgcn_exp2f(gj - gi[e]) * nki[e] : 0.f;
         a[e] = (i < j) ? bj * decay * ak[e] : 0.f;
-        p[e] = decay * aq[e];
+        p[e] = qj * decay * aq[e];
       }
       bf16x4 ph, pl;
       split4(p, ph, pl);
@@ -323,14 +471,17 @@ __global__ __launch_bounds__(64) void prepare_kernel(
     __syncthreads();
   }
 
-  // 5. T -> workspace as bf16 hi/lo (rows 0..31, columns 32..63 are never
-  //    read and stay unwritten)
+  // 5. T diag(beta) -> workspace as bf16 hi/lo (rows 0..31, columns
+  //    32..63 are never read and stay unwritten)
   for (int e = lane; e < C * C / 8; e += 64) {
     const int j = (8 * e) / C, i0 = (8 * e) % C;
     if (j < C / 2 && i0 >= C / 2) continue;
     const float4 a0 = *reinterpret_cast<const float4*>(&Ts[j * LDA + i0]);
     const float4 a1 = *reinterpret_cast<const float4*>(&Ts[j * LDA + i0 + 4]);
-    const floatx8 x = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const float4 b0 = *reinterpret_cast<const float4*>(&bs[i0]);
+    const float4 b1 = *reinterpret_cast<const float4*>(&bs[i0 + 4]);
+    const floatx8 x = {a0.x * b0.x, a0.y * b0.y, a0.z * b0.z, a0.w * b0.w,
+                       a1.x * b1.x, a1.y * b1.y, a1.z * b1.z, a1.w * b1.w};
     bf16x8 hi, lo;
     split8(x, hi, lo);
     *reinterpret_cast<bf16x8*>(wsc + kWsTh + (j * C + i0) * 2) = hi;
@@ -563,7 +714,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
       OQ[ct] = accq;
     }
 
-    // ---- Z = beta (V - gamma Y), as split B operands over c ----
+    // ---- Z = V - gamma nk Y (beta is in T), as split B operands over c ----
     bf16x8 Zh[2], Zl[2];
     {
       floatx4 Z[4];
@@ -579,16 +730,15 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
           vv[2] += bf16lo(vl.y);
           vv[3] += bf16hi(vl.y);
         }
-        const float4 bb = *reinterpret_cast<const float4*>(&Gs[C + c]);
-        const float4 gg = *reinterpret_cast<const float4*>(&Gs[2 * C + c]);
-        Z[ct] = floatx4{bb.x * (vv[0] - gg.x * Y[ct][0]), bb.y * (vv[1] - gg.y * Y[ct][1]),
-                        bb.z * (vv[2] - gg.z * Y[ct][2]), bb.w * (vv[3] - gg.w * Y[ct][3])};
+        const float4 gg = *reinterpret_cast<const float4*>(&Gs[2 * C + c]);   // gamma nk
+        Z[ct] = floatx4{vv[0] - gg.x * Y[ct][0], vv[1] - gg.y * Y[ct][1],
+                        vv[2] - gg.z * Y[ct][2], vv[3] - gg.w * Y[ct][3]};
       }
 #pragma unroll
       for (int s = 0; s < 2; ++s) split8(acc_slots(Z[2 * s], Z[2 * s + 1]), Zh[s], Zl[s]);
     }
 
-    // ---- U = T Z  (T lower triangular: c-tile ct needs k-blocks <= ct/2) ----
+    // ---- U = T diag(beta) Z  (lower triangular: c-tile ct needs k-blocks <= ct/2) ----
     floatx4 U[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
@@ -612,7 +762,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
     for (int ct = 0; ct < 4; ++ct) {
       floatx4 acc = OQ[ct];
       const int c = 16 * ct + 4 * g4;
-      const float4 gg = *reinterpret_cast<const float4*>(&Gs[2 * C + c]);
+      const float4 gg = *reinterpret_cast<const float4*>(&Gs[c]);          // gamma nq
       acc[0] *= gg.x;
       acc[1] *= gg.y;
       acc[2] *= gg.z;
@@ -669,7 +819,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
                             ub[0] * d1.x, ub[1] * d1.y, ub[2] * d1.z, ub[3] * d1.w};
         split8(du, Dh[s], Dl[s]);
       }
-      const float gC = Gs[3 * C - 1];
+      const float gC = Gs[C];
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         floatx4 acc = S[dt] * gC;
@@ -924,7 +1074,7 @@ __global__ __launch_bounds__(64 * (DV + DK) / (16 * NH), 1) void scan_wide_kerne
       }
     }
 
-    // ---- Z = beta (V - gamma Y), as split B operands over c ----
+    // ---- Z = V - gamma nk Y (beta is in T), as split B operands over c ----
     bf16x8 Zh[NH][2], Zl[NH][2];
 #pragma unroll
     for (int hf = 0; hf < NH; ++hf) {
@@ -939,16 +1089,15 @@ __global__ __launch_bounds__(64 * (DV + DK) / (16 * NH), 1) void scan_wide_kerne
         const float vs = xrows ? 0.f : 1.f;
         const float vv[4] = {vs * bf16lo(vw.x), vs * bf16hi(vw.x), vs * bf16lo(vw.y),
                              vs * bf16hi(vw.y)};
-        const float4 bb = *reinterpret_cast<const float4*>(&Gs[C + c]);
-        const float4 gg = *reinterpret_cast<const float4*>(&Gs[2 * C + c]);
-        Z[ct] = floatx4{bb.x * (vv[0] - gg.x * Y[hf][ct][0]), bb.y * (vv[1] - gg.y * Y[hf][ct][1]),
-                        bb.z * (vv[2] - gg.z * Y[hf][ct][2]), bb.w * (vv[3] - gg.w * Y[hf][ct][3])};
+        const float4 gg = *reinterpret_cast<const float4*>(&Gs[2 * C + c]);   // gamma nk
+        Z[ct] = floatx4{vv[0] - gg.x * Y[hf][ct][0], vv[1] - gg.y * Y[hf][ct][1],
+                        vv[2] - gg.z * Y[hf][ct][2], vv[3] - gg.w * Y[hf][ct][3]};
       }
 #pragma unroll
       for (int s = 0; s < 2; ++s) split8(acc_slots(Z[2 * s], Z[2 * s + 1]), Zh[hf][s], Zl[hf][s]);
     }
 
-    // ---- U = T Z  (T lower triangular: c-tile ct needs k-blocks <= ct/2) ----
+    // ---- U = T diag(beta) Z  (lower triangular: c-tile ct needs k-blocks <= ct/2) ----
     floatx4 U[NH][4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
@@ -994,7 +1143,7 @@ __global__ __launch_bounds__(64 * (DV + DK) / (16 * NH), 1) void scan_wide_kerne
         for (int s = 0; s < 2; ++s) Uh[hf][s] = to_bf16x8(acc_slots(U[hf][2 * s], U[hf][2 * s + 1]));
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
-        const float gam = Gs[2 * C + 16 * ct + n];
+        const float gam = Gs[16 * ct + n];                                 // gamma nq
 #pragma unroll
         for (int hf = 0; hf < NH; ++hf) OT[hf][ct] *= gam;
 #pragma unroll
@@ -1032,7 +1181,7 @@ __global__ __launch_bounds__(64 * (DV + DK) / (16 * NH), 1) void scan_wide_kerne
           split8(du, Dh[hf][s], Dl[hf][s]);
         }
       }
-      const float gC = Gs[3 * C - 1];
+      const float gC = Gs[C];
 #pragma unroll
       for (int hf = 0; hf < NH; ++hf)
 #pragma unroll
@@ -1112,28 +1261,33 @@ hipError_t launch_state_fill(const float* S0, float* ST, size_t n,
 // launchers
 // ===========================================================================
 
-template <int DK, typename TIn>
+template <int DK, typename TIn, bool GATHER>
 static void launch_prepare_t(const void* q, const void* k, const float* alpha,
                              const float* beta, float* ws, int B, int T, int H,
-                             bool write_pl, hipStream_t stream) {
+                             bool write_pl, const QkArgs& qa, hipStream_t stream) {
   const int nchunks = (T + C - 1) / C;
-  hipLaunchKernelGGL((prepare_kernel<DK, TIn>), dim3(nchunks, H, B), dim3(64),
+  hipLaunchKernelGGL((prepare_kernel<DK, TIn, GATHER>), dim3(nchunks, H, B), dim3(64),
                      0, stream, static_cast<const TIn*>(q),
                      static_cast<const TIn*>(k), alpha, beta, ws, T, H,
-                     nchunks, write_pl ? 1 : 0);
+                     nchunks, write_pl ? 1 : 0, qa);
 }
 
 hipError_t launch_prefill_prepare(const void* q, const void* k,
                                   const float* alpha, const float* beta,
                                   float* ws, int B, int T, int H, int dk,
-                                  int in_dtype, bool write_pl, hipStream_t stream) {
+                                  int in_dtype, bool write_pl, const QkArgs& qa,
+                                  hipStream_t stream) {
+#define GDN_PREP(DK, TI, G) \
+  launch_prepare_t<DK, TI, G>(q, k, alpha, beta, ws, B, T, H, write_pl, qa, stream)
+  const bool g = qa.chan != nullptr;
   if (in_dtype == 1) {
-    if (dk == 128) launch_prepare_t<128, bf16>(q, k, alpha, beta, ws, B, T, H, write_pl, stream);
-    else launch_prepare_t<64, bf16>(q, k, alpha, beta, ws, B, T, H, write_pl, stream);
+    if (dk == 128) { if (g) GDN_PREP(128, bf16, true); else GDN_PREP(128, bf16, false); }
+    else { if (g) GDN_PREP(64, bf16, true); else GDN_PREP(64, bf16, false); }
   } else {
-    if (dk == 128) launch_prepare_t<128, float>(q, k, alpha, beta, ws, B, T, H, write_pl, stream);
-    else launch_prepare_t<64, float>(q, k, alpha, beta, ws, B, T, H, write_pl, stream);
+    if (dk == 128) { if (g) GDN_PREP(128, float, true); else GDN_PREP(128, float, false); }
+    else { if (g) GDN_PREP(64, float, true); else GDN_PREP(64, float, false); }
   }
+#undef GDN_PREP
   return hipGetLastError();
 }
 

@@ -35,7 +35,8 @@
  *    Sec. 3.2-3.3), dv in {64, 128}.
  *  - Preconditions not checked (checking would cost a pass over the data):
  *    q and k are already unit-L2-normalised (and already gathered to the
- *    kept channels when pruned); alpha in (0, 1]; beta in [0, 1].  Outside
+ *    kept channels when pruned; the *_qk entry points below do both inside
+ *    the kernels); alpha in (0, 1]; beta in [0, 1].  Outside
  *    these ranges the same formula is applied but results are untested.
  *  - Errors: argument errors are returned synchronously BEFORE any HIP call
  *    (GDN_EINVAL: null pointer, negative size, zero B/H; GDN_ESHAPE:
@@ -124,9 +125,10 @@ int gdn_prefill(const void* q, const void* k, const void* v,
  * out_dtype than its prepare's is not supported and its outputs are
  * undefined).
  *   prepare: per 64-token chunk, independent of the state: the gate prefix
- *            sums, the unit-lower-triangular delta correction
- *            (I + A)^{-1} with A_ji = beta_j e^{g_j - g_i} k_j.k_i (i < j),
- *            and the decay-masked query-key products; written to workspace.
+ *            sums and per-token decay factors, the unit-lower-triangular
+ *            delta correction (I + A)^{-1} with A_ji = beta_j e^{g_j - g_i}
+ *            k_j.k_i (i < j), stored times diag(beta), and the
+ *            decay-masked query-key products; written to workspace.
  *   scan:    sequential over chunks, parallel over heads and 64-row groups
  *            of the state: reads q, k, v and the chunk tiles, writes o and
  *            ST.  With bf16 inputs and outputs and few heads it also splits
@@ -160,6 +162,52 @@ int gdn_decode_step(const void* q, const void* k, const void* v,
                     const float* S_in, float* S_out, void* o,
                     int B, int H, int dk, int dv,
                     int in_dtype, int out_dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * The input path of a channel-pruned layer, fused into the kernels.
+ *
+ * "On State Reduction in Linear Attention", Sec. 3.2-3.3, prunes a layer by
+ * keeping a per-head subset I_h of the query/key channels and recomputing
+ * the L2 normalisation over the kept channels.  These variants take q and
+ * k as the raw projection output, rows of dk_in elements, and apply
+ *     q_t <- q_scale * P_I q_t / |P_I q_t|,   k_t <- P_I k_t / |P_I k_t|
+ * (P_I keeps channels[h][0..dk-1] of head h's row, in that order; without
+ * l2norm the division is skipped; a kept vector that is all zero stays
+ * zero) before the recurrence, with no pass over q/k outside the kernels.
+ *   channels   [H, dk] int32 device array, 16-byte aligned, each entry in
+ *              [0, dk_in) (NOT checked: an index outside the row is an
+ *              out-of-bounds read), or NULL: the rows are dk wide and all
+ *              kept (dk_in must equal dk, else GDN_ESHAPE).
+ *   dk_in      row width of q and k in memory (1 .. 2^20 with channels).
+ *   l2norm     1: normalise q and k over the kept channels; 0: do not.
+ *   q_scale    multiplies the (normalised) query; 1 for none.
+ * With channels, q and k need only their element alignment (2 or 4 bytes);
+ * without, 16 bytes as elsewhere.  All other arguments, layouts (with dk
+ * the kept width of S0/ST/S) and errors are those of gdn_prefill and
+ * gdn_decode_step.  With channels == NULL, l2norm == 0 and q_scale == 1
+ * the results equal gdn_prefill's / gdn_decode_step's bitwise.
+ *
+ * Workspace of gdn_prefill_qk: gdn_prefill's, plus (gather != 0, i.e.
+ * channels given) a gathered copy of the kept q/k channels,
+ * 2 * B*T*H*dk elements of in_dtype, that the scan reads.  0 for an
+ * unsupported dk/dv/dtype or T == 0.
+ */
+size_t gdn_prefill_qk_workspace_bytes(int B, int T, int H, int dk, int dv,
+                                      int in_dtype, int gather);
+
+int gdn_prefill_qk(const void* q, const void* k, const void* v,
+                   const float* alpha, const float* beta, const float* S0,
+                   void* o, float* ST, int B, int T, int H, int dk, int dv,
+                   int dk_in, const int* channels, int l2norm, float q_scale,
+                   int in_dtype, int out_dtype, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+int gdn_decode_step_qk(const void* q, const void* k, const void* v,
+                       const float* alpha, const float* beta,
+                       const float* S_in, float* S_out, void* o, int B, int H,
+                       int dk, int dv, int dk_in, const int* channels,
+                       int l2norm, float q_scale, int in_dtype, int out_dtype,
+                       void* stream);
 
 /* ------------------------------------------------------------------------
  * Rank-r truncation of carried states.

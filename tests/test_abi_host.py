@@ -201,3 +201,84 @@ def test_truncate_full_rank_needs_no_workspace_or_launch():
     # workspace is needed (the fake S is never touched)
     assert truncate(r=128, er=NULL, ws=NULL, ws_bytes=0) == bd.GDN_OK
     assert truncate(dk=64, r=64, er=NULL, ws=NULL, ws_bytes=0) == bd.GDN_OK
+
+
+# --- the input path (gdn_prefill_qk / gdn_decode_step_qk) -----------------
+
+def test_prefill_qk_workspace_bytes():
+    ws = bd.lib.gdn_prefill_qk_workspace_bytes
+    chunk = 33792
+    assert ws(1, 64, 1, 128, 128, 1, 0) == chunk                 # no gather: gdn_prefill's
+    assert ws(1, 64, 1, 128, 128, 1, 1) == chunk + 2 * 64 * 128 * 2
+    assert ws(1, 64, 1, 64, 128, 0, 1) == chunk + 2 * 64 * 64 * 4
+    assert ws(2, 100, 3, 64, 64, 1, 1) == (
+        2 * 3 * 2 * chunk + 2 * 2 * 100 * 3 * 64 * 2)
+    assert ws(1, 0, 1, 128, 128, 1, 1) == 0
+    assert ws(1, 64, 1, 96, 128, 1, 1) == 0
+    assert ws(1, 64, 1, 128, 128, 3, 1) == 0
+
+
+def prefill_qk(**kw):
+    a = dict(q=P, k=P, v=P, alpha=P, beta=P, S0=NULL, o=P, ST=P, B=1, T=100,
+             H=2, dk=64, dv=128, dk_in=128, ch=P, l2norm=1, scale=1.0,
+             in_dtype=1, out_dtype=1, ws=P, ws_bytes=10 ** 9, stream=NULL)
+    a.update(kw)
+    return bd.lib.gdn_prefill_qk(a["q"], a["k"], a["v"], a["alpha"], a["beta"],
+                                 a["S0"], a["o"], a["ST"], a["B"], a["T"],
+                                 a["H"], a["dk"], a["dv"], a["dk_in"], a["ch"],
+                                 a["l2norm"], a["scale"], a["in_dtype"],
+                                 a["out_dtype"], a["ws"], a["ws_bytes"],
+                                 a["stream"])
+
+
+def decode_qk(**kw):
+    a = dict(q=P, k=P, v=P, alpha=P, beta=P, S_in=P, S_out=P, o=P, B=4, H=2,
+             dk=64, dv=128, dk_in=128, ch=P, l2norm=1, scale=1.0, in_dtype=1,
+             out_dtype=1, stream=NULL)
+    a.update(kw)
+    return bd.lib.gdn_decode_step_qk(a["q"], a["k"], a["v"], a["alpha"],
+                                     a["beta"], a["S_in"], a["S_out"], a["o"],
+                                     a["B"], a["H"], a["dk"], a["dv"],
+                                     a["dk_in"], a["ch"], a["l2norm"],
+                                     a["scale"], a["in_dtype"],
+                                     a["out_dtype"], a["stream"])
+
+
+QK_ERRORS = [
+    (dict(ch=NULL), bd.GDN_ESHAPE),                    # no subset: dk_in must be dk
+    (dict(ch=NULL, dk_in=64, dk=128), bd.GDN_ESHAPE),
+    (dict(dk_in=0), bd.GDN_ESHAPE),
+    (dict(dk_in=(1 << 20) + 1), bd.GDN_ESHAPE),
+    (dict(l2norm=2), bd.GDN_EINVAL),
+    (dict(ch=MIS), bd.GDN_EINVAL),                      # index table not 16-byte aligned
+    (dict(q=ctypes.c_void_p(0x10001)), bd.GDN_EINVAL),  # bf16 element misaligned
+    (dict(q=ctypes.c_void_p(0x10002), in_dtype=0), bd.GDN_EINVAL),   # fp32 element misaligned
+    (dict(ch=NULL, dk_in=64, q=ctypes.c_void_p(0x10008)), bd.GDN_EINVAL),  # whole rows: 16 B
+    (dict(dk=96), bd.GDN_ESHAPE),
+    (dict(B=0), bd.GDN_EINVAL),
+    (dict(k=NULL), bd.GDN_EINVAL),
+    (dict(S_in=NULL), bd.GDN_EINVAL),
+]
+
+
+@pytest.mark.parametrize("kw,status", QK_ERRORS + [
+    (dict(ws=NULL), bd.GDN_EWORKSPACE),
+    # gdn_prefill's workspace is not enough once the gathered copy is needed
+    (dict(ws_bytes=2 * 2 * 33792), bd.GDN_EWORKSPACE),
+    (dict(alpha=NULL), bd.GDN_EINVAL),
+    (dict(o=MIS), bd.GDN_EINVAL),
+    (dict(S0=ctypes.c_void_p(0x10000), ST=ctypes.c_void_p(0x10100)), bd.GDN_EINVAL),
+])
+def test_prefill_qk_argument_errors(kw, status):
+    kw = {("S0" if k == "S_in" else k): v for k, v in kw.items()}
+    if "S0" in kw and kw["S0"] is NULL and "ST" not in kw:
+        kw["v"] = NULL                                   # no S_in in prefill: test v
+    assert prefill_qk(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", QK_ERRORS + [
+    (dict(S_in=ctypes.c_void_p(0x100000), S_out=ctypes.c_void_p(0x100010)),
+     bd.GDN_EINVAL),
+])
+def test_decode_step_qk_argument_errors(kw, status):
+    assert decode_qk(**kw) == status

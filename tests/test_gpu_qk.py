@@ -1,0 +1,203 @@
+"""GPU parity of the fused input path (gdn_prefill_qk, gdn_decode_step_qk)
+against the oracle: per-head channel subset of the raw q/k rows, L2
+renormalisation over the kept channels and a query scale ("On State
+Reduction in Linear Attention", Sec. 3.2-3.3), then the recurrence."""
+
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_recurrent_delta_amd import binding as gdn
+from oracle import gdn_oracle as orc
+from tests.gpu_util import (TOL_BF16, TOL_F32, assert_close, errs_S, errs_o,
+                            host, tdtype, to_dev)
+from workloads import gdn_inputs as gi
+
+pytestmark = pytest.mark.gpu
+
+QSCALE = float(1.0 / np.sqrt(128.0))
+
+
+def subsets(seed, H, dk_in, dk, permute=False):
+    """Per-head channel subsets; permute=True keeps them in a random order
+    (the kernels must follow the given order, not sort it)."""
+    r = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for _ in range(H):
+        ch = r.permutation(dk_in)[:dk]
+        out.append(ch if permute else np.sort(ch))
+    return np.stack(out).astype(np.int32)
+
+
+def dev_channels(ch):
+    return None if ch is None else torch.from_numpy(np.ascontiguousarray(ch)).to("cuda")
+
+
+def run_prefill_qk(x, ch, l2norm, q_scale, out_dt):
+    d = to_dev(x)
+    o, ST = gdn.prefill_qk(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"],
+                           channels=dev_channels(ch), l2norm=l2norm, q_scale=q_scale,
+                           out_dtype=tdtype(out_dt))
+    torch.cuda.synchronize()
+    return o, ST
+
+
+def check_prefill_qk(x, ch, l2norm=True, q_scale=1.0, out_dt=None, label="", heads=None):
+    out_dt = x.dtype if out_dt is None else out_dt
+    print(f"  case {label}: {x.q.shape} dk={None if ch is None else ch.shape[1]} "
+          f"l2norm={l2norm} q_scale={q_scale} out={out_dt}", flush=True)
+    o, ST = run_prefill_qk(x, ch, l2norm, q_scale, out_dt)
+    o_ref, S_ref = orc.gdn_prefill_qk(x.q, x.k, x.v, x.alpha, x.beta, x.S0,
+                                      channels=ch, l2norm=l2norm, q_scale=q_scale,
+                                      heads=heads)
+    tol_o = TOL_F32 if out_dt == "f32" else TOL_BF16
+    assert_close(f"{label} o", errs_o(host(o), o_ref, heads), tol_o)
+    assert_close(f"{label} S_T", errs_S(host(ST), S_ref, heads), TOL_F32)
+
+
+@pytest.mark.parametrize("T", [1, 63, 65, 200])
+@pytest.mark.parametrize("dk_in,dk,dv", [(128, 64, 128), (128, 128, 64), (100, 64, 64)])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_prefill_qk_subset_norm_scale(T, dk_in, dk, dv, dt):
+    """Raw rows of dk_in channels, per-token magnitudes; dk=128 of 128 is a
+    per-head permutation, dk_in=100 an odd row width."""
+    ch = subsets(3000 + T + dk_in + dk, 3, dk_in, dk, permute=(dk == dk_in))
+    x = gi.raw_qk(2, T, 3, dk_in, dv, 4000 + T + dk + dv, dt, channel_idx=ch,
+                  S0_scale=0.3)
+    check_prefill_qk(x, ch, True, QSCALE, label=f"T={T}")
+
+
+@pytest.mark.parametrize("dk", [128, 64])
+@pytest.mark.parametrize("dt,out_dt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32")])
+def test_prefill_qk_norm_only(dk, dt, out_dt):
+    """No channel subset: the kernels normalise the dk-wide rows in place."""
+    x = gi.raw_qk(2, 300, 4, dk, 128, 4100 + dk, dt, S0_scale=0.3)
+    check_prefill_qk(x, None, True, 0.5, out_dt, label="norm only")
+
+
+def test_prefill_qk_subset_without_normalisation():
+    ch = subsets(4200, 2, 128, 64)
+    x = gi.raw_qk(1, 150, 2, 128, 128, 4201, "f32", channel_idx=ch, S0_scale=0.3)
+    # without normalisation the keys are used as given: give each token's
+    # kept channels a norm in [0.5, 1.2] (beta |k|^2 <= 2 keeps the
+    # recurrence a contraction), the other channels stay raw
+    r = np.random.Generator(np.random.PCG64(4202))
+    for h in range(2):
+        kh = x.k[0, :, h]                                        # [T, 128] view
+        kept = kh[:, ch[h]].astype(np.float64)                    # [T, 64]
+        want = r.uniform(0.5, 1.2, size=(kept.shape[0], 1))
+        kh[:, ch[h]] = (kept / np.linalg.norm(kept, axis=1, keepdims=True)
+                        * want).astype(np.float32)
+    check_prefill_qk(x, ch, False, 1.0, label="subset, no norm")
+
+
+@pytest.mark.parametrize("T,dk", [(2048, 64), (1500, 128)])
+def test_prefill_qk_segmented(T, dk):
+    """Few heads, long sequences: the segment-parallel scan reads the
+    gathered copy; transition rows carry the folded key/query factors."""
+    assert gdn.prefill_segments(1, T, 2, dk, 128)[0] > 1
+    ch = subsets(4300 + T, 2, 128, dk, permute=True)
+    x = gi.raw_qk(1, T, 2, 128, 128, 4301 + T, "bf16", channel_idx=ch, S0_scale=0.3)
+    check_prefill_qk(x, ch, True, QSCALE, label=f"segmented T={T}")
+
+
+def test_prefill_qk_zero_rows():
+    """Tokens whose kept q or k channels are all zero: the normalised vector
+    is zero (the key writes nothing, the query reads zero)."""
+    ch = subsets(4400, 2, 128, 64)
+    x = gi.raw_qk(1, 130, 2, 128, 128, 4401, "bf16", channel_idx=ch, S0_scale=0.3)
+    for h in range(2):
+        x.k[0, 5, h, ch[h]] = 0.0
+        x.k[0, 64, h, ch[h]] = 0.0
+        x.q[0, 7, h, ch[h]] = 0.0
+        x.q[0, 129, h, ch[h]] = 0.0
+    check_prefill_qk(x, ch, True, 1.0, "f32", label="zero rows")
+
+
+@pytest.mark.parametrize("dt,out_dt,T", [("bf16", "bf16", 200), ("f32", "f32", 70),
+                                         ("bf16", "bf16", 2048)])
+def test_prefill_qk_identity_equals_prefill_bitwise(dt, out_dt, T):
+    x = gi.generic(1, T, 2, 128, 128, 4500 + T, dt, S0_scale=0.3)
+    d = to_dev(x)
+    o1, S1 = gdn.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"],
+                         out_dtype=tdtype(out_dt))
+    o2, S2 = gdn.prefill_qk(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"],
+                            channels=None, l2norm=False, q_scale=1.0,
+                            out_dtype=tdtype(out_dt))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_prefill_qk_batched_full_size_sampled_heads():
+    """The batched prefill's shape (B=8, H=16, T=4096, dv=128) at dk=64
+    from 128-wide raw rows, in the benchmark's launch configuration; the
+    oracle follows three (batch, head) pairs."""
+    ch = gi.pruning_subsets(4, 16, 128, 64)
+    x = gi.raw_qk(8, 4096, 16, 128, 128, gi.seed_for(4, 5), "bf16", channel_idx=ch)
+    heads = [(0, 0), (3, 7), (7, 15)]
+    check_prefill_qk(x, ch, True, QSCALE, label="B=8 T=4096 dk=64<-128", heads=heads)
+
+
+# --- decode ----------------------------------------------------------------
+
+def decode_inputs(B, H, dk_in, dk, dv, dt, seed, permute=False):
+    ch = subsets(seed, H, dk_in, dk, permute) if dk_in != dk or permute else None
+    x = gi.raw_qk(B, 1, H, dk_in, dv, seed + 1, dt, channel_idx=ch, S0_scale=0.5)
+    return x, ch
+
+
+@pytest.mark.parametrize("B,H", [(3, 4), (64, 16)])
+@pytest.mark.parametrize("dk_in,dk,dv,permute", [(128, 64, 128, False), (128, 128, 128, True),
+                                                 (100, 64, 64, False), (64, 64, 128, False)])
+@pytest.mark.parametrize("in_dt,out_dt", [("bf16", "bf16"), ("f32", "f32")])
+def test_decode_qk_matches_oracle(B, H, dk_in, dk, dv, permute, in_dt, out_dt):
+    x, ch = decode_inputs(B, H, dk_in, dk, dv, in_dt, 5000 + B + dk_in + dk + dv, permute)
+    d = to_dev(x)
+    sq = lambda t: t[:, 0].contiguous()
+    o, S1 = gdn.decode_step_qk(sq(d["q"]), sq(d["k"]), sq(d["v"]), sq(d["alpha"]),
+                               sq(d["beta"]), d["S0"], channels=dev_channels(ch),
+                               l2norm=True, q_scale=QSCALE, out_dtype=tdtype(out_dt))
+    torch.cuda.synchronize()
+    o_ref, S_ref = orc.gdn_decode_step_qk(x.q[:, 0], x.k[:, 0], x.v[:, 0], x.alpha[:, 0],
+                                          x.beta[:, 0], x.S0, channels=ch, l2norm=True,
+                                          q_scale=QSCALE)
+    tol_o = TOL_F32 if out_dt == "f32" else TOL_BF16
+    assert_close("o", orc.rel_l2_per_head(host(o), o_ref, (0, 1)), tol_o)
+    assert_close("S'", orc.rel_l2_per_head(host(S1), S_ref, (0, 1)), TOL_F32)
+
+
+@pytest.mark.parametrize("dk", [128, 64])
+def test_decode_qk_identity_equals_decode_bitwise(dk):
+    x = gi.generic(64, 1, 16, dk, 128, 5100 + dk, "bf16", S0_scale=0.5)
+    d = to_dev(x)
+    args = [d[n][:, 0].contiguous() for n in ("q", "k", "v", "alpha", "beta")]
+    o1, S1 = gdn.decode_step(*args, d["S0"])
+    o2, S2 = gdn.decode_step_qk(*args, d["S0"], channels=None, l2norm=False, q_scale=1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_decode_qk_chain_matches_prefill_qk():
+    """A prompt by prefill_qk, then 40 decode_step_qk tokens in place, against
+    the oracle's token-by-token run over the same raw inputs."""
+    ch = subsets(5200, 4, 128, 64)
+    x = gi.raw_qk(2, 300, 4, 128, 128, 5201, "bf16", channel_idx=ch)
+    Tp = 260
+    d = to_dev(x)
+    chd = dev_channels(ch)
+    sl = lambda t: t[:, :Tp].contiguous()
+    o_p, S = gdn.prefill_qk(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["alpha"]),
+                            sl(d["beta"]), channels=chd, q_scale=QSCALE)
+    outs = []
+    for t in range(Tp, 300):
+        st = lambda n: d[n][:, t].contiguous()
+        o_t, _ = gdn.decode_step_qk(st("q"), st("k"), st("v"), st("alpha"), st("beta"),
+                                    S, S_out=S, channels=chd, q_scale=QSCALE)
+        outs.append(o_t)
+    torch.cuda.synchronize()
+    o_ref, S_ref = orc.gdn_prefill_qk(x.q, x.k, x.v, x.alpha, x.beta, channels=ch,
+                                      q_scale=QSCALE)
+    o_dec = torch.stack(outs, dim=1)
+    assert_close("prompt o", errs_o(host(o_p), o_ref[:, :Tp]), TOL_BF16)
+    assert_close("decode o", errs_o(host(o_dec), o_ref[:, Tp:]), TOL_BF16)
+    assert_close("S", errs_S(host(S), S_ref), TOL_F32)
