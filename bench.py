@@ -58,17 +58,22 @@ def log(*a):
 # algorithmic traffic and executed MFMA work
 # ---------------------------------------------------------------------------
 
-def prefill_bytes(B, T, H, dk, dv, io_bytes=2, with_S0=False):
+def prefill_bytes(B, T, H, dk, dv, io_bytes=2, with_S0=False, dk_in=None):
     """q, k, v read + o written (io dtype), alpha/beta read (fp32), final
-    state written (fp32), initial state read if given."""
-    per_tok = io_bytes * (2 * dk + 2 * dv) + 8
+    state written (fp32), initial state read if given.  dk_in: width of the
+    raw q/k rows the fused input path reads, default dk."""
+    dk_in = dk if dk_in is None else dk_in
+    per_tok = io_bytes * (2 * dk_in + 2 * dv) + 8
     state = 4 * dv * dk * (2 if with_S0 else 1)
     return B * H * (T * per_tok + state)
 
 
-def decode_bytes(B, H, dk, dv, io_bytes=2):
-    """State read + written once (fp32), q, k, v read, o written, gates."""
-    return B * H * (8 * dv * dk + io_bytes * (2 * dk + 2 * dv) + 8)
+def decode_bytes(B, H, dk, dv, io_bytes=2, dk_in=None):
+    """State read + written once (fp32), q, k, v read, o written, gates.
+    dk_in: width of the raw q/k rows the fused input path reads (a random
+    channel subset touches every cache line of the row), default dk."""
+    dk_in = dk if dk_in is None else dk_in
+    return B * H * (8 * dv * dk + io_bytes * (2 * dk_in + 2 * dv) + 8)
 
 
 def prefill_mfma_flops(B, T, H, dk, dv, nseg, seg_chunks):
@@ -143,6 +148,228 @@ def measured_traffic(kernel):
 
 
 # ---------------------------------------------------------------------------
+# HBM traffic from rocprofv3 counters (FETCH_SIZE, WRITE_SIZE)
+# ---------------------------------------------------------------------------
+
+# Which dispatches belong to which measured launch: kernel name, first
+# template argument (d_k), the gather flag where the kernel has one, and the
+# grid size (work-items) at the benchmark's shapes.  Kernels of the decode
+# prompts (prefills of B=64 or B=1) have other grids and are not counted.
+COUNTER_LEGS = {
+    # (kernel, d_k, last template argument or None, grid): the last template
+    # argument is prepare_kernel's gather flag (0, 1) and decode_kernel's
+    # input-path mode (0 none, 1 norm + scale, 2 channel subset + norm + scale)
+    # 16 heads x 16 segments: scan_wide 512 threads per head-segment,
+    # combine 8 row groups x 9 waves per head, correction 15 segments x 10
+    # waves per head (a B=1 decode prompt's combine has the same grid: count
+    # the B=1 decode legs in a run of their own)
+    "prefill": [("prepare_kernel", 128, 0, 256 * 16 * 64),
+                ("scan_wide_kernel", 128, None, 16 * 16 * 512),
+                ("segment_combine_kernel", 128, None, 16 * 8 * 576),
+                ("segment_correct_kernel", 128, None, 16 * 15 * 640)],
+    "decode_B64_dk128": [("decode_kernel", 128, 0, 64 * 16 * 32 * 64)],
+    "decode_B64_dk64": [("decode_kernel", 64, 0, 64 * 16 * 8 * 64)],
+    "decode_B1_dk128": [("decode_kernel", 128, 0, 16 * 32 * 64)],
+    "decode_B1_dk64": [("decode_kernel", 64, 0, 16 * 32 * 64)],
+    "batched_dk128": [("prepare_kernel", 128, 0, 64 * 16 * 8 * 64),
+                      ("scan_kernel", 128, None, 8 * 16 * 2 * 256)],
+    "batched_dk64": [("prepare_kernel", 64, 0, 64 * 16 * 8 * 64),
+                     ("scan_kernel", 64, None, 8 * 16 * 2 * 256)],
+    "batched_qk_dk64": [("prepare_kernel", 64, 1, 64 * 16 * 8 * 64),
+                        ("scan_kernel", 64, None, 8 * 16 * 2 * 256)],
+    "decode_qk_B64_dk64": [("decode_kernel", 64, 2, 64 * 16 * 8 * 64)],
+    "batched_qk_norm_dk64": [("prepare_kernel", 64, 0, 64 * 16 * 8 * 64),
+                             ("scan_kernel", 64, None, 8 * 16 * 2 * 256)],
+    "decode_qk_norm_B64_dk64": [("decode_kernel", 64, 1, 64 * 16 * 8 * 64)],
+    # generalised gates: the last template argument is the rows-per-wave
+    # group count (4 for the single-token instance, 1 for sequences)
+    "gated_decode_B64_dk128": [("gated_recurrent_kernel", 128, 4, 64 * 16 * 8 * 64)],
+    "gated_decode_B64_dk64": [("gated_recurrent_kernel", 64, 4, 64 * 16 * 8 * 64)],
+    "gated_prefill_B8_T4096_dk64": [("gated_recurrent_kernel", 64, 1, 8 * 16 * 32 * 64)],
+}
+
+
+def _legs_in_run(a):
+    legs = []
+    if not a.skip_prefill:
+        legs.append("prefill")
+    if not a.skip_decode:
+        legs += [f"decode_B{b}_dk{d}" for b in a.decode_batch for d in (128, 64)]
+    if not a.skip_batched:
+        legs += ["batched_dk128", "batched_dk64"]
+    if not a.skip_gated:
+        if 64 in a.decode_batch:
+            legs += ["gated_decode_B64_dk128", "gated_decode_B64_dk64"]
+        legs.append("gated_prefill_B8_T4096_dk64")
+    if not a.skip_qk:
+        legs.append("batched_qk_dk64")
+        if not a.qk_gather_only:
+            legs.append("batched_qk_norm_dk64")
+        if 64 in a.decode_batch:
+            legs.append("decode_qk_B64_dk64")
+            if not a.qk_gather_only:
+                legs.append("decode_qk_norm_B64_dk64")
+    return legs
+
+
+def _kernel_key(name):
+    """(base name, first template int, last template argument as an int, or
+    None) of a kernel name as rocprofv3 reports it: demangled ('void
+    gdn::prepare_kernel<128, __bf16, true>(...)') or, where its demangler
+    gives up, mangled ('_ZN3gdn14prepare_kernelILi128EDF16bLb1EEEv...')."""
+    import re
+    mm = re.match(r"_ZN3gdn(\d+)", name)
+    if mm:
+        n = int(mm.group(1))
+        base = name[mm.end():mm.end() + n]
+        rest = name[mm.end() + n:]
+        tmpl = rest.split("EEv", 1)[0] + "E"
+        di = re.match(r"ILi(\d+)E", rest)
+        last = re.findall(r"L[bi](\d+)E", tmpl)
+        return (base, int(di.group(1)) if di else None,
+                int(last[-1]) if len(last) > 1 or (last and not di) else None)
+    m = re.search(r"(\w+)<([^>]*)>", name)
+    if not m:
+        return re.sub(r"\(.*", "", name).split("::")[-1].strip(), None, None
+    args = [x.strip() for x in m.group(2).split(",")]
+    dk = int(args[0]) if args and args[0].lstrip("-").isdigit() else None
+    tail = args[-1] if len(args) > 1 else ""
+    flag = {"true": 1, "false": 0}.get(tail, int(tail) if tail.isdigit() else None)
+    return m.group(1), dk, flag
+
+
+def _read_counters(path, counter):
+    """{dispatch id: (kernel name, grid size, value)} from a rocprofv3
+    counter_collection.csv (values of one dispatch summed over its rows)."""
+    import csv
+    out = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") != counter:
+                continue
+            d = int(row["Dispatch_Id"])
+            name, grid, val = row["Kernel_Name"], int(row["Grid_Size"]), float(row["Counter_Value"])
+            if d in out:
+                val += out[d][2]
+            out[d] = (name, grid, val)
+    return out
+
+
+def summarize_counters(a, fetch_csv, write_csv, out_path=None):
+    fetch = _read_counters(fetch_csv, "FETCH_SIZE")
+    write = _read_counters(write_csv, "WRITE_SIZE")
+    # calibration: the 3 + 20 device copies of 512 MiB that copy_bandwidth()
+    # makes at the end of every run (the last 23 copy dispatches; earlier
+    # ones are uploads and state clones of other sizes)
+    copy_bytes = 512 << 20
+    cf = [fetch[d][2] for d in sorted(fetch) if "copyBuffer" in fetch[d][0]][-23:]
+    cw = [write[d][2] for d in sorted(write) if "copyBuffer" in write[d][0]][-23:]
+    if not cf or not cw:
+        raise SystemExit("no device-copy dispatches found for the calibration")
+    ffac = copy_bytes / 1024 / float(np.mean(cf))
+    wfac = copy_bytes / 1024 / float(np.mean(cw))
+    legs = _legs_in_run(a)
+    # every (name, dk, flag, grid) key must belong to one leg of this run
+    owner = {}
+    for leg in legs:
+        for spec in COUNTER_LEGS[leg]:
+            for other, ospec in owner.items():
+                if ospec[0] == spec[0] and ospec[1] == spec[1] and \
+                        (spec[2] is None or ospec[2] is None or ospec[2] == spec[2]) and \
+                        (spec[3] is None or ospec[3] is None or ospec[3] == spec[3]):
+                    raise SystemExit(f"{leg} and {other[0]} share kernel {spec}: run them apart")
+            owner[(leg, spec)] = spec
+
+    def match(spec, name, grid):
+        base, dk, flag = _kernel_key(name)
+        # a flag the demangler garbled (None) matches either value: the
+        # legs of one run never differ in the flag alone
+        return (base == spec[0] and dk == spec[1] and
+                (spec[2] is None or flag is None or flag == spec[2]) and
+                (spec[3] is None or grid == spec[3]))
+
+    tpath = out_path or os.path.join(ROOT, "profiles", "traffic.json")
+    src = kernel_source_hash()
+    data = {}
+    if os.path.exists(tpath):
+        with open(tpath) as f:
+            data = json.load(f)
+    if data.get("source_hash") != src:
+        data = {"source_hash": src, "kernels": {}}
+    data["calibration"] = {"copy_bytes": copy_bytes, "fetch_factor": ffac,
+                           "write_factor": wfac, "copy_fetch_kib": float(np.mean(cf)),
+                           "copy_write_kib": float(np.mean(cw)),
+                           "copy_dispatches": len(cf)}
+    for leg in legs:
+        parts, total = {}, 0.0
+        for spec in COUNTER_LEGS[leg]:
+            fv = [v for n, g, v in fetch.values() if match(spec, n, g)]
+            wv = [v for n, g, v in write.values() if match(spec, n, g)]
+            if not fv or not wv:
+                raise SystemExit(f"{leg}: no dispatches of {spec}")
+            b = float(np.mean(fv)) * 1024 * ffac + float(np.mean(wv)) * 1024 * wfac
+            parts[spec[0]] = {"fetch_kib": float(np.mean(fv)), "write_kib": float(np.mean(wv)),
+                              "dispatches": len(fv), "bytes": b}
+            total += b
+        data["kernels"][leg] = {"hbm_bytes_per_launch": total, "parts": parts}
+        log(f"{leg}: {total / 1e6:.1f} MB per launch " +
+            ", ".join(f"{k} {v['bytes'] / 1e6:.1f} MB" for k, v in parts.items()))
+    with open(tpath, "w") as f:
+        json.dump(data, f, indent=1)
+    log(f"wrote {tpath} (fetch factor {ffac:.4f}, write factor {wfac:.4f}, sources {src})")
+    return 0
+
+
+def summarize_trace(a, db, last=20):
+    """Kernel durations per leg from a rocprofv3 kernel-trace database: for
+    every kernel of every selected leg, the number of dispatches, the mean
+    over all of them and over the last `last` (the timed region, after the
+    warm-up), and the minimum, in microseconds."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    # mangled names from the symbol table (the demangled ones can be garbled)
+    rows = con.execute(
+        "select s.kernel_name, d.grid_size_x * d.grid_size_y * d.grid_size_z, d.start, d.end "
+        "from rocpd_kernel_dispatch d join rocpd_info_kernel_symbol s on d.kernel_id = s.id "
+        "order by d.start").fetchall()
+    print("| leg | kernel | grid (work-items) | dispatches | mean us | mean of last "
+          f"{last} us | min us |")
+    print("|---|---|---|---|---|---|---|")
+    legs = _legs_in_run(a)
+
+    def matches(spec):
+        out = []
+        for name, grid, t0, t1 in rows:
+            base, dk, flag = _kernel_key(name)
+            if (base == spec[0] and dk == spec[1] and
+                    (spec[2] is None or flag is None or flag == spec[2]) and
+                    (spec[3] is None or grid == spec[3])):
+                out.append((t0, t1))
+        return out
+
+    for leg in legs:
+        for spec in COUNTER_LEGS[leg]:
+            d = matches(spec)
+            # legs of this run that launch the same kernel at the same grid
+            # run one after the other, seconds apart (input generation):
+            # split the dispatches at the largest gaps, in leg order
+            sharing = [l for l in legs if spec in COUNTER_LEGS[l]]
+            if len(sharing) > 1 and len(d) > len(sharing):
+                gaps = sorted(range(1, len(d)), key=lambda i: d[i][0] - d[i - 1][1])
+                cuts = sorted(gaps[-(len(sharing) - 1):])
+                bounds = [0] + cuts + [len(d)]
+                i = sharing.index(leg)
+                d = d[bounds[i]:bounds[i + 1]]
+            d = [(t1 - t0) / 1e3 for t0, t1 in d]
+            if not d:
+                continue
+            g = spec[3] if spec[3] is not None else "-"
+            print(f"| {leg} | {spec[0]}<{spec[1]}{'' if spec[2] is None else f', {spec[2]}'}> "
+                  f"| {g} | {len(d)} | {np.mean(d):.2f} | {np.mean(d[-last:]):.2f} | {np.min(d):.2f} |")
+    return 0
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle on the host cores (before GPU init)
 # ---------------------------------------------------------------------------
 
@@ -203,9 +430,33 @@ def main(argv=None):
                          "replaying a HIP graph (for counter collection)")
     ap.add_argument("--skip-truncated", action="store_true",
                     help="skip the segment-truncated prefill leg")
+    ap.add_argument("--skip-qk", action="store_true",
+                    help="skip the fused input-path legs (channel subset + "
+                         "L2 norm + query scale inside the kernels)")
+    ap.add_argument("--skip-gated", action="store_true",
+                    help="skip the generalised-gate legs (per-key-channel "
+                         "retention, split erase/write gates; recurrent form)")
+    ap.add_argument("--qk-gather-only", action="store_true",
+                    help="of the fused input-path legs run only those with a "
+                         "channel subset (for counter collection: the others "
+                         "launch the same kernels at the same grids)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16384)
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no benchmark: turn the counter_collection.csv files of "
+                         "two rocprofv3 runs of this script (--pmc FETCH_SIZE, "
+                         "--pmc WRITE_SIZE; same leg options) into per-launch HBM "
+                         "bytes, merged into profiles/traffic.json")
+    ap.add_argument("--summarize-trace", metavar="RESULTS_DB",
+                    help="no benchmark: print, per measured launch of the legs "
+                         "selected by the same options, the kernel durations of a "
+                         "rocprofv3 --kernel-trace run of this script (its "
+                         "*_results.db) as a markdown table")
     a = ap.parse_args(argv)
+    if a.summarize_counters:
+        return summarize_counters(a, *a.summarize_counters)
+    if a.summarize_trace:
+        return summarize_trace(a, a.summarize_trace)
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the gated delta rule's heads "
@@ -337,6 +588,38 @@ def main(argv=None):
             decode[f"speedup_dk64_vs_dk128_B{bb}"] = (decode[f"B{bb}_dk128"]["us_per_step"] /
                                                      decode[f"B{bb}_dk64"]["us_per_step"])
 
+    # ---------------- the fused input path (raw 128-wide q/k) ----------------
+    qk = {}
+    if not a.skip_qk:
+        variants = ((True,) if a.qk_gather_only else (True, False))
+        for name, gth in (("batched_dk64_from128", True), ("batched_dk64_norm", False)):
+            if gth not in variants:
+                continue
+            qk[name] = bench_batched_qk(torch, gdn, dev, stream, max(3, a.steps // 2),
+                                        a.warmup, up, gather=gth)
+            if "dk64" in batched:
+                qk[name]["time_vs_plain_dk64"] = (qk[name]["us_per_call"] /
+                                                  batched["dk64"]["us_per_call"])
+        if 64 in a.decode_batch:
+            for name, gth in (("decode_B64_dk64_from128", True), ("decode_B64_dk64_norm", False)):
+                if gth not in variants:
+                    continue
+                qk[name] = bench_decode(torch, gdn, dev, stream, 64, 64, a.decode_steps,
+                                        a.layers, up, eager=a.eager_decode, fused=True,
+                                        gather=gth)
+                if "B64_dk64" in decode:
+                    qk[name]["time_vs_plain_dk64"] = (qk[name]["us_per_step"] /
+                                                      decode["B64_dk64"]["us_per_step"])
+
+    # ---------------- generalised gates (recurrent form) ----------------
+    gated = {}
+    if not a.skip_gated:
+        if 64 in a.decode_batch:
+            for dkg in (128, 64):
+                gated[f"decode_B64_dk{dkg}"] = bench_gated_decode(
+                    torch, gdn, dev, stream, 64, dkg, min(a.decode_steps, 64), a.layers, up)
+        gated["prefill_B8_T4096_dk64"] = bench_gated_prefill(torch, gdn, dev, stream, up)
+
     # ---------------- segment-truncated prefill, r in {1, 4, 12, 32} ----------
     truncated = {}
     if not a.skip_truncated:
@@ -365,6 +648,8 @@ def main(argv=None):
         "prefill": prefill_info,
         "decode": decode,
         "batched_prefill": batched,
+        "fused_input_path": qk,
+        "generalised_gates": gated,
         "truncated_prefill": truncated,
         "cpu_baseline": cpu,
         "copy_bandwidth_GBps": copy_bw / 1e9,
@@ -397,26 +682,45 @@ def copy_bandwidth(torch, dev, stream, nbytes=512 << 20, reps=20):
 
 
 def bench_decode(torch, gdn, dev, stream, B, dk, n_steps, layers, up,
-                 eager=False):
+                 eager=False, fused=False, gather=True):
     """512 decode steps x `layers` state sets, captured in one HIP graph
     (or launched one by one with `eager`, which then times launch gaps
-    too)."""
+    too).  fused: q/k are raw rows that the kernel normalises (over the
+    layer's per-head channel subset of 128-wide rows with `gather`, else
+    over the dk-wide rows) before it scales q."""
     H, dv = 16, 128
-    log(f"decode B={B} dk={dk}: prompt prefill (2048 tokens) ...")
-    pr = gi.decode_prompt(B=B, dk=dk)
-    q, k, v, al, be = up(pr)
-    del pr
-    _, S = gdn.prefill(q, k, v, al, be)
+    tag = f"decode B={B} dk={dk}" + ((" (fused input path, from 128)" if gather else
+                                      " (fused input path, norm + scale)") if fused else "")
+    log(f"{tag}: prompt prefill (2048 tokens) ...")
+    if fused:
+        chn = gi.pruning_subsets(3, H, 128, dk) if gather else None
+        ch = torch.from_numpy(chn).to(dev) if gather else None
+        wid = 128 if gather else dk
+        pr = gi.raw_qk(B, 2048, H, wid, dv, gi.seed_for(3, 5), "bf16", channel_idx=chn)
+        q, k, v, al, be = up(pr)
+        del pr
+        _, S = gdn.prefill_qk(q, k, v, al, be, channels=ch, q_scale=dk ** -0.5)
+        st = gi.raw_qk(B, n_steps, H, wid, dv, gi.seed_for(3, 6), "bf16", channel_idx=chn)
+    else:
+        pr = gi.decode_prompt(B=B, dk=dk)
+        q, k, v, al, be = up(pr)
+        del pr
+        _, S = gdn.prefill(q, k, v, al, be)
+        st = gi.decode_steps(B=B, n_steps=n_steps, dk=dk)
     del q, k, v, al, be
-    st = gi.decode_steps(B=B, n_steps=n_steps, dk=dk)
     qs, ks, vs, als, bes = [t.transpose(0, 1).contiguous() for t in up(st)]
     del st
     states = [S.clone() for _ in range(layers)]
     o = torch.empty((B, H, dv), dtype=torch.bfloat16, device=dev)
 
     def one(t, l):
-        gdn.decode_step(qs[t], ks[t], vs[t], als[t], bes[t], states[l],
-                        S_out=states[l], o=o)
+        if fused:
+            gdn.decode_step_qk(qs[t], ks[t], vs[t], als[t], bes[t], states[l],
+                               S_out=states[l], o=o, channels=ch,
+                               q_scale=dk ** -0.5, validate=False)
+        else:
+            gdn.decode_step(qs[t], ks[t], vs[t], als[t], bes[t], states[l],
+                            S_out=states[l], o=o)
 
     # warm up (also compiles nothing; checks the path eagerly)
     for l in range(layers):
@@ -445,7 +749,8 @@ def bench_decode(torch, gdn, dev, stream, B, dk, n_steps, layers, up,
     ms = e0.elapsed_time(e1)
     launches = n_steps * layers
     us = ms * 1e3 / launches
-    nbytes = decode_bytes(B, H, dk, dv)
+    nbytes = decode_bytes(B, H, dk, dv, dk_in=128 if fused and gather else dk)
+    key = (f"decode_qk_B{B}_dk{dk}" if gather else None) if fused else f"decode_B{B}_dk{dk}"
     res = {"us_per_step": us, "tokens_per_s": B / (us * 1e-6),
            "launches_timed": launches, "state_sets": layers,
            "graph": not eager,
@@ -453,9 +758,9 @@ def bench_decode(torch, gdn, dev, stream, B, dk, n_steps, layers, up,
                         "achieved": nbytes / (us * 1e-6) / 1e9,
                         "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                         "frac": nbytes / (us * 1e-6) / HBM_PEAK,
-                        "traffic": measured_traffic(f"decode_B{B}_dk{dk}"),
+                        "traffic": measured_traffic(key) if key else None,
                         "algorithmic_bytes": nbytes}}
-    log(f"  decode B={B} dk={dk}: {us:.2f} us/step, "
+    log(f"  {tag}: {us:.2f} us/step, "
         f"{res['roofline']['achieved']:.0f} GB/s ({100 * res['roofline']['frac']:.1f} % of HBM)")
     del replay, states, qs, ks, vs, als, bes, S
     torch.cuda.empty_cache()
@@ -491,6 +796,147 @@ def bench_batched(torch, gdn, dev, stream, dk, steps, warmup, up):
     log(f"batched prefill B=8 T=4096 dk={dk}: {us:.1f} us, "
         f"{res['tokens_per_s'] / 1e6:.1f} M tokens/s")
     del q, k, v, al, be, o, ST, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_batched_qk(torch, gdn, dev, stream, steps, warmup, up, gather=True):
+    """The batched prefill (B=8, H=16, T=4096, dv=128) at dk=64 from raw,
+    unnormalised q/k rows.  gather: the rows are 128 wide and the prepare
+    kernel keeps each head's channel subset (the scan reads the gathered
+    copy it writes); else the rows are the 64 kept channels already (the
+    projection weights permuted offline).  Either way the kernels normalise
+    over the kept channels and fold the norms and a 1/sqrt(64) query scale
+    into the chunk products."""
+    H, dk = 16, 64
+    ch_np = gi.pruning_subsets(4, H, 128, dk) if gather else None
+    x = gi.raw_qk(8, 4096, H, 128 if gather else dk, 128, gi.seed_for(4, 5), "bf16",
+                  channel_idx=ch_np)
+    B, T, _, dk_in = x.q.shape
+    dv = x.v.shape[-1]
+    q, k, v, al, be = up(x)
+    del x
+    ch = torch.from_numpy(ch_np).to(dev) if gather else None
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    ST = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.prefill_qk_workspace_bytes(B, T, H, dk, dv, torch.bfloat16, gather),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        gdn.prefill_qk(q, k, v, al, be, channels=ch, q_scale=dk ** -0.5, o=o, ST=ST,
+                       workspace=ws, validate=False)
+    settle(torch, call, warmup)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nbytes = prefill_bytes(B, T, H, dk, dv, dk_in=dk_in)
+    res = {"us_per_call": us, "tokens_per_s": B * T / (us * 1e-6),
+           "inputs": (f"raw bf16 q/k [8, 4096, 16, {dk_in}]; "
+                      + ("per-head 64-channel subset, " if gather else "")
+                      + "L2 norm over the kept channels and q scale 1/8 inside the kernels"),
+           "roofline": {"bound": "hbm", "achieved": nbytes / (us * 1e-6) / 1e9,
+                        "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                        "frac": nbytes / (us * 1e-6) / HBM_PEAK,
+                        "traffic": measured_traffic("batched_qk_dk64") if gather else None,
+                        "algorithmic_bytes": nbytes}}
+    log(f"batched prefill B=8 T=4096 dk=64 from raw {dk_in}-wide q/k (fused input path"
+        f"{', gather' if gather else ', norm + scale'}): "
+        f"{us:.1f} us, {res['tokens_per_s'] / 1e6:.1f} M tokens/s")
+    del q, k, v, al, be, o, ST, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def gated_decode_bytes(B, H, dk, dv, io_bytes=2):
+    """State read + written (fp32); q, k, v read and o written (io dtype);
+    the per-channel gates alpha, b (fp32, dk each) and w (fp32, dv)."""
+    return B * H * (8 * dv * dk + io_bytes * (2 * dk + 2 * dv) + 4 * (2 * dk + dv))
+
+
+def bench_gated_decode(torch, gdn, dev, stream, B, dk, n_steps, layers, up):
+    """Decode steps (T = 1) of the generalised gates over `layers` rotating
+    state sets, captured in one HIP graph, like the plain decode leg."""
+    H, dv = 16, 128
+    x = gi.generic(B, n_steps, H, dk, dv, gi.seed_for(3, 7), "bf16")
+    al, bg, wg = gi.gate_vectors(B, n_steps, H, dk, dv, gi.seed_for(3, 8))
+    q, k, v, _, _ = [t.transpose(0, 1).contiguous()[:, :, None] for t in up(x)]
+    f32 = lambda z: torch.from_numpy(z).to(dev).transpose(0, 1).contiguous()[:, :, None]
+    al, bg, wg = f32(al), f32(bg), f32(wg)          # [steps, B, 1, H, *]
+    del x
+    g0 = torch.Generator(device="cpu").manual_seed(gi.seed_for(3, 9))
+    S_init = (0.1 * torch.randn((B, H, dv, dk), generator=g0)).to(dev)
+    states = [S_init.clone() for _ in range(layers)]
+    del S_init
+    o = torch.empty((B, 1, H, dv), dtype=torch.bfloat16, device=dev)
+
+    def one(t, l):
+        gdn.gated_recurrent(q[t], k[t], v[t], al[t], bg[t], wg[t], states[l], o=o,
+                            ST=states[l])
+
+    for l in range(layers):
+        one(0, l)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for t in range(n_steps):
+            for l in range(layers):
+                one(t, l)
+    settle(torch, g.replay, 1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (n_steps * layers)
+    nbytes = gated_decode_bytes(B, H, dk, dv)
+    res = {"us_per_step": us, "tokens_per_s": B / (us * 1e-6),
+           "launches_timed": n_steps * layers, "state_sets": layers, "graph": True,
+           "roofline": {"bound": "hbm", "kernel": "gated_recurrent_kernel (T=1)",
+                        "achieved": nbytes / (us * 1e-6) / 1e9,
+                        "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                        "frac": nbytes / (us * 1e-6) / HBM_PEAK,
+                        "traffic": measured_traffic(f"gated_decode_B{B}_dk{dk}"),
+                        "algorithmic_bytes": nbytes}}
+    log(f"  generalised-gate decode B={B} dk={dk}: {us:.2f} us/step, "
+        f"{res['roofline']['achieved']:.0f} GB/s ({100 * res['roofline']['frac']:.1f} % of HBM)")
+    del g, states, q, k, v, al, bg, wg
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_gated_prefill(torch, gdn, dev, stream, up, B=8, T=4096, H=16, dk=64, dv=128,
+                        calls=3):
+    """The generalised gates over whole sequences in recurrent form (the
+    batched prefill's shape at dk = 64).  Its bound is the per-token
+    dependency chain, not HBM: reported as time and tokens/s."""
+    x = gi.generic(B, T, H, dk, dv, gi.seed_for(4, 7), "bf16")
+    al, bg, wg = gi.gate_vectors(B, T, H, dk, dv, gi.seed_for(4, 8))
+    q, k, v, _, _ = up(x)
+    del x
+    al, bg, wg = (torch.from_numpy(z).to(dev) for z in (al, bg, wg))
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    ST = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+
+    def call():
+        gdn.gated_recurrent(q, k, v, al, bg, wg, o=o, ST=ST)
+    settle(torch, call, 1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(calls):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    res = {"us_per_call": us, "tokens_per_s": B * T / (us * 1e-6),
+           "us_per_token_step": us / T,
+           "bound": "latency of the per-token dependency chain (recurrent form)"}
+    log(f"generalised-gate prefill B={B} T={T} dk={dk} (recurrent form): {us:.0f} us, "
+        f"{res['tokens_per_s'] / 1e6:.2f} M tokens/s, {us / T * 1e3:.0f} ns per token step")
+    del q, k, v, al, bg, wg, o, ST
     torch.cuda.empty_cache()
     return res
 

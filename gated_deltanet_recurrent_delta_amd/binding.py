@@ -47,6 +47,8 @@ SIGNATURES = {
     "gdn_decode_step_qk": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _i, _i, _i, _i, _i, _vp, _i, ctypes.c_float,
                                 _i, _i, _vp]),
+    "gdn_gated_recurrent": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _i, _i, _i, _i, _i, _i, _i, _vp]),
     "gdn_truncate_workspace_bytes": (_sz, [_i, _i, _i]),
     "gdn_truncate_rank": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
 }
@@ -371,6 +373,51 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                              _DTYPE_CODE[out_dtype], _stream_handle(q, stream))
     _check(st, "gdn_decode_step")
     return o, S_out
+
+
+# ---------------------------------------------------------------------------
+# generalised gates (per-key-channel retention, split erase / write gates)
+# ---------------------------------------------------------------------------
+
+def gated_recurrent(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    alpha: torch.Tensor, b: torch.Tensor, w: torch.Tensor,
+                    S0: Optional[torch.Tensor] = None, *,
+                    out_dtype: Optional[torch.dtype] = None,
+                    o: Optional[torch.Tensor] = None,
+                    ST: Optional[torch.Tensor] = None,
+                    final_state: bool = True,
+                    stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """S_t = S_{t-1} diag(alpha_t) (I - (b_t*k_t) k_t^T) + (w_t*v_t) k_t^T,
+    o_t = S_t q_t, token by token (see include/gdn.h).  q, k [B, T, H, dk],
+    v [B, T, H, dv] (float32 or bfloat16); alpha, b [B, T, H, dk] and w
+    [B, T, H, dv] float32; S0 [B, H, dv, dk] float32 or None.  T == 1 is a
+    decode step.  Returns (o, S_T)."""
+    _dev_tensor(q, "q", _DTYPE_CODE)
+    B, T, H, dk = q.shape
+    _dev_tensor(k, "k", (q.dtype,), q.shape)
+    _dev_tensor(v, "v", (q.dtype,))
+    if tuple(v.shape[:3]) != (B, T, H) or v.dim() != 4:
+        raise ValueError(f"v: shape {tuple(v.shape)} incompatible with q")
+    dv = v.shape[3]
+    _dev_tensor(alpha, "alpha", (torch.float32,), (B, T, H, dk))
+    _dev_tensor(b, "b", (torch.float32,), (B, T, H, dk))
+    _dev_tensor(w, "w", (torch.float32,), (B, T, H, dv))
+    if S0 is not None:
+        _dev_tensor(S0, "S0", (torch.float32,), (B, H, dv, dk))
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=q.device)
+    _dev_tensor(o, "o", (out_dtype,), (B, T, H, dv))
+    if ST is None and final_state:
+        ST = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    if ST is not None:
+        _dev_tensor(ST, "ST", (torch.float32,), (B, H, dv, dk))
+    st = lib.gdn_gated_recurrent(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b),
+                                 _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), B, T, H, dk, dv,
+                                 _DTYPE_CODE[q.dtype], _DTYPE_CODE[out_dtype],
+                                 _stream_handle(q, stream))
+    _check(st, "gdn_gated_recurrent")
+    return o, ST
 
 
 # ---------------------------------------------------------------------------

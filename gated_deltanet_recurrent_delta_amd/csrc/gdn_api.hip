@@ -278,6 +278,30 @@ int gdn_decode_step_qk(const void* q, const void* k, const void* v,
                                       qa, static_cast<hipStream_t>(stream)));
 }
 
+int gdn_gated_recurrent(const void* q, const void* k, const void* v,
+                        const float* alpha, const float* b, const float* w,
+                        const float* S0, void* o, float* ST, int B, int T,
+                        int H, int dk, int dv, int in_dtype, int out_dtype,
+                        void* stream) {
+  int st = check_prefill_shape(B, T, H, dk, dv, in_dtype, out_dtype);
+  if (st != GDN_OK) return st;
+  if ((S0 && !aligned(S0, 16)) || (ST && !aligned(ST, 16))) return GDN_EINVAL;
+  const size_t nstate = (size_t)B * H * dv * dk;
+  if (ST && S0 && ST != S0 && (ST < S0 + nstate && S0 < ST + nstate))
+    return GDN_EINVAL;                               // partial overlap
+  if (T == 0)
+    return to_status(gdn::launch_state_fill(S0, ST, nstate,
+                                            static_cast<hipStream_t>(stream)));
+  if (!q || !k || !v || !alpha || !b || !w || !o) return GDN_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(alpha, 16) ||
+      !aligned(b, 16) || !aligned(v, in_dtype == GDN_BF16 ? 2 : 4) ||
+      !aligned(w, 4) || !aligned(o, out_dtype == GDN_BF16 ? 2 : 4))
+    return GDN_EINVAL;
+  return to_status(gdn::launch_gated_recurrent(
+      q, k, v, alpha, b, w, S0, ST, o, B, T, H, dk, dv, in_dtype, out_dtype,
+      static_cast<hipStream_t>(stream)));
+}
+
 size_t gdn_truncate_workspace_bytes(int BH, int dv, int dk) {
   if (BH <= 0 || !dims_ok(dk, dv)) return 0;
   return (size_t)BH * (dv < dk ? dv : dk) * dv * sizeof(float);

@@ -132,4 +132,12 @@ hipError_t launch_truncate(float* S, int BH, int dv, int dk, int r, float* er,
 hipError_t launch_state_fill(const float* S0, float* ST, size_t n,
                              hipStream_t stream);
 
+// The generalised gates (per-key-channel retention alpha [B,T,H,dk], erase
+// gate b [B,T,H,dk], write gate w [B,T,H,dv]) in recurrent form, T >= 1.
+hipError_t launch_gated_recurrent(const void* q, const void* k, const void* v,
+                                  const float* alpha, const float* bgate,
+                                  const float* wgate, const float* S0, float* ST,
+                                  void* o, int B, int T, int H, int dk, int dv,
+                                  int in_dtype, int out_dtype, hipStream_t stream);
+
 }  // namespace gdn

@@ -272,8 +272,32 @@ __global__ __launch_bounds__(64) void prepare_kernel(
   }
   bf16x8 Kh[4][NKB], Kl[4][NKB], Qh[4][NKB], Ql[4][NKB];
   float ssk[4], ssq[4];
+  // The pruned width from bf16 rows 128 wide (16-byte aligned): every raw
+  // row is read whole with 16-byte loads, staged in LDS (the space of the T
+  // tile, not in use yet) and the kept channels are picked there; other
+  // widths read the kept channels one element at a time.
+  constexpr bool STAGE = GATHER && !SPLIT && DK == 64;
+  constexpr int LDR = 136;                   // staged row stride (one 16-byte pad unit)
+  static_assert(C * LDR * 2 <= C * LDA * 4, "staged rows fit in the T tile");
+  bool staged = false;
+  uint4 rk[STAGE ? 16 : 1], rq[STAGE ? 16 : 1];   // lane: unit n of rows 4 j + g4
+  if constexpr (STAGE) {
+    staged = qa.dk_in == 128 && ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k)) & 15) == 0;
+    if (staged) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+      for (int j = 0; j < 16; ++j) {
+        const int row = 4 * j + g4;
+        rk[j] = rq[j] = make_uint4(0u, 0u, 0u, 0u);
+        if (row < nvalid) {
+          const size_t off = (((size_t)b * T + t0 + row) * H + h) * 128 + 8 * n;
+          rk[j] = *reinterpret_cast<const uint4*>(k + off);
+          rq[j] = *reinterpret_cast<const uint4*>(q + off);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 4 && !staged; ++t) {
     const int c = 16 * t + n;
     const size_t row = ((size_t)b * T + t0 + c) * H + h;           // token row
     ssk[t] = ssq[t] = 0.f;
@@ -301,10 +325,6 @@ __global__ __launch_bounds__(64) void prepare_kernel(
         } else {
           Kh[t][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(k + off));
           Qh[t][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(q + off));
-          if (qa.l2norm) {
-            ssk[t] += sumsq8(Kh[t][s]);
-            ssq[t] += sumsq8(Qh[t][s]);
-          }
         }
       }
     }
@@ -328,9 +348,56 @@ __global__ __launch_bounds__(64) void prepare_kernel(
     gamC = expf(glast);
   }
 
+  // 1b. staged rows: pick the kept channels from LDS (after the gate prefix
+  //     sum, which then does not wait for the rows)
+  if constexpr (STAGE) {
+    if (staged) {
+      bf16* stg = reinterpret_cast<bf16*>(Ts);
+      auto pick = [&](const uint4 (&raw)[16], bf16x8 (&X)[4][NKB], float (&ss)[4], bf16* copy) {
+        __syncthreads();                       // earlier reads of the staging area are done
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          *reinterpret_cast<uint4*>(&stg[(4 * j + g4) * LDR + 8 * n]) = raw[j];
+        __syncthreads();
+        const uint16_t* s16 = reinterpret_cast<const uint16_t*>(stg);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int c = 16 * t + n;
+          ss[t] = 0.f;
+#pragma unroll
+          for (int s = 0; s < NKB; ++s) {
+            uint32_t w[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+              w[p] = (uint32_t)s16[c * LDR + ci[s][2 * p]] |
+                     ((uint32_t)s16[c * LDR + ci[s][2 * p + 1]] << 16);
+            X[t][s] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+            if (c < nvalid)
+              *reinterpret_cast<uint4*>(copy + (((size_t)b * T + t0 + c) * H + h) * DK +
+                                        32 * s + 8 * g4) = make_uint4(w[0], w[1], w[2], w[3]);
+            ss[t] += sumsq8(X[t][s]);
+          }
+        }
+      };
+      pick(rk, Kh, ssk, kg);
+      pick(rq, Qh, ssq, qg);
+    }
+  }
+
   // 2b. per-token factors of the input path: the four lanes of a token
   //     (g4 = 0..3) hold its k-slots; 1 and qscale without normalisation
   {
+    if constexpr (!GATHER && !SPLIT) {
+      if (qa.l2norm) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int s = 0; s < NKB; ++s) {
+            ssk[t] += sumsq8(Kh[t][s]);
+            ssq[t] += sumsq8(Qh[t][s]);
+          }
+      }
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       float sk = ssk[t], sq = ssq[t];

@@ -210,6 +210,37 @@ int gdn_decode_step_qk(const void* q, const void* k, const void* v,
                        void* stream);
 
 /* ------------------------------------------------------------------------
+ * Generalised gates, recurrent form.
+ *
+ * "Linear Attention Architectures" (reading notes), Sec. 2.5 (Kimi Delta
+ * Attention) and Sec. 2.6 (Gated DeltaNet-2) refine the scalar gates of the
+ * gated delta rule: a retention alpha per KEY channel, applied on the key
+ * side of the state, and separate erase (b, key side) and write (w, value
+ * side) gates.  Per head and token:
+ *     S~  = S_{t-1} diag(alpha_t)
+ *     S_t = S~ (I - (b_t * k_t) k_t^T) + (w_t * v_t) k_t^T
+ *     o_t = S_t q_t
+ * (* element-wise).  b = w = beta_t * 1 is Kimi Delta Attention; with
+ * alpha_t = a_t * 1 as well it is gdn_prefill's recurrence.
+ *   q, k         [B, T, H, dk] in_dtype, 16-byte aligned.
+ *   v            [B, T, H, dv] in_dtype.
+ *   alpha, b     [B, T, H, dk] float32, 16-byte aligned; alpha in (0, 1].
+ *   w            [B, T, H, dv] float32.
+ *   S0           [B, H, dv, dk] float32 or NULL (zero); ST the final state
+ *                or NULL; ST may alias S0.
+ *   o            [B, T, H, dv] out_dtype.
+ * T == 1 is the decode step (one streaming pass over the state).  The
+ * kernel runs the tokens in order (no chunked form), so long sequences are
+ * bound by the per-token dependency chain.  Uses no workspace.  Errors as
+ * for gdn_prefill; T == 0 copies S0 (or zeros) into ST.
+ */
+int gdn_gated_recurrent(const void* q, const void* k, const void* v,
+                        const float* alpha, const float* b, const float* w,
+                        const float* S0, void* o, float* ST, int B, int T,
+                        int H, int dk, int dv, int in_dtype, int out_dtype,
+                        void* stream);
+
+/* ------------------------------------------------------------------------
  * Rank-r truncation of carried states.
  *
  * Replaces each state S (dv x dk) by U_r U_r^T S, where U_r holds the r

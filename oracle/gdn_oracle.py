@@ -31,6 +31,11 @@ Sources (page titles as published; sections/equations as the pages give them):
     singular directions at every 256-token boundary, r = 128 = no change):
     state-rank post, §3.
 
+  * Generalised gates (gdn2_head): a per-key-channel decay applied on the
+    right of the state (Kimi Delta Attention) and split key-side erase /
+    value-side write gates whose outer products keep k_t on the right
+    (Gated DeltaNet-2): "Linear Attention Architectures" reading notes,
+    Secs. 2.5-2.6 and the mechanism table after them.
   * Input path of a channel-pruned layer (qk_transform): keep a per-head
     subset of query/key coordinates and renormalise over the kept ones:
     "On State Reduction in Linear Attention", Sec. 3.2-3.3.
@@ -126,6 +131,61 @@ def gdn_decode_step(q, k, v, alpha, beta, S):
                               np.asarray(beta)[b, h][None], S[b, h])
             o[b, h], S1[b, h] = ob[0], Sb
     return o, S1
+
+
+# ---------------------------------------------------------------------------
+# generalised gates: per-key-channel decay (KDA), split erase/write (GDN2)
+# ---------------------------------------------------------------------------
+
+def gdn2_head(q, k, v, alpha, b, w, S0=None):
+    """One head with the generalised gates, token by token in float64.
+
+    q, k [T, dk]; v [T, dv]; alpha [T, dk] per-key-channel retention;
+    b [T, dk] key-side erase gate; w [T, dv] value-side write gate;
+    S0 [dv, dk] or None.  Per token ("Linear Attention Architectures"
+    reading notes, Sec. 2.5 Kimi Delta Attention and Sec. 2.6 Gated
+    DeltaNet-2):
+        S~ = S_{t-1} diag(alpha_t)       decay on the key-feature side (right)
+        e  = b_t * k_t                    the direction the erase reads
+        z  = w_t * v_t                    the content written
+        S_t = S~ (I - e k_t^T) + z k_t^T  erase and write both along k_t
+        o_t = S_t q_t
+    b = w = beta * 1 is Kimi Delta Attention; with alpha = a * 1 as well it
+    is the gated delta rule of gdn_head.  Returns o [T, dv], S_T [dv, dk].
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    alpha = np.asarray(alpha, np.float64)
+    b = np.asarray(b, np.float64)
+    w = np.asarray(w, np.float64)
+    T, dk = k.shape
+    dv = v.shape[1]
+    S = np.zeros((dv, dk)) if S0 is None else np.array(S0, np.float64)
+    o = np.empty((T, dv))
+    for t in range(T):
+        S = S * alpha[t][None, :]                   # S diag(alpha): scales columns
+        e = b[t] * k[t]
+        z = w[t] * v[t]
+        S = S - np.outer(S @ e, k[t]) + np.outer(z, k[t])
+        o[t] = S @ q[t]
+    return o, S
+
+
+def gdn2_prefill(q, k, v, alpha, b, w, S0=None, heads=None):
+    """Batched layout: q, k [B, T, H, dk]; v [B, T, H, dv]; alpha, b
+    [B, T, H, dk]; w [B, T, H, dv]; S0 [B, H, dv, dk] or None.  Returns o
+    [B, T, H, dv], S_T [B, H, dv, dk]; `heads` as in gdn_prefill."""
+    B, T, H, dk = np.shape(q)
+    dv = np.shape(v)[-1]
+    o = np.full((B, T, H, dv), np.nan)
+    ST = np.full((B, H, dv, dk), np.nan)
+    todo = heads if heads is not None else [(bb, h) for bb in range(B) for h in range(H)]
+    for bb, h in todo:
+        s0 = None if S0 is None else S0[bb, h]
+        o[bb, :, h], ST[bb, h] = gdn2_head(q[bb, :, h], k[bb, :, h], v[bb, :, h],
+                                           alpha[bb, :, h], b[bb, :, h], w[bb, :, h], s0)
+    return o, ST
 
 
 # ---------------------------------------------------------------------------

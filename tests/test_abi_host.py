@@ -282,3 +282,36 @@ def test_prefill_qk_argument_errors(kw, status):
 ])
 def test_decode_step_qk_argument_errors(kw, status):
     assert decode_qk(**kw) == status
+
+
+# --- generalised gates (gdn_gated_recurrent) --------------------------------
+
+def gated(**kw):
+    a = dict(q=P, k=P, v=P, alpha=P, b=P, w=P, S0=NULL, o=P, ST=P, B=1, T=10, H=2,
+             dk=128, dv=128, in_dtype=1, out_dtype=1, stream=NULL)
+    a.update(kw)
+    return bd.lib.gdn_gated_recurrent(a["q"], a["k"], a["v"], a["alpha"], a["b"], a["w"],
+                                      a["S0"], a["o"], a["ST"], a["B"], a["T"], a["H"],
+                                      a["dk"], a["dv"], a["in_dtype"], a["out_dtype"],
+                                      a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), bd.GDN_EINVAL),
+    (dict(T=-1), bd.GDN_EINVAL),
+    (dict(dk=96), bd.GDN_ESHAPE),
+    (dict(dv=32), bd.GDN_ESHAPE),
+    (dict(in_dtype=3), bd.GDN_ESHAPE),
+    (dict(q=NULL), bd.GDN_EINVAL),
+    (dict(alpha=NULL), bd.GDN_EINVAL),
+    (dict(b=NULL), bd.GDN_EINVAL),
+    (dict(w=NULL), bd.GDN_EINVAL),
+    (dict(o=NULL), bd.GDN_EINVAL),
+    (dict(k=MIS), bd.GDN_EINVAL),
+    (dict(alpha=MIS), bd.GDN_EINVAL),
+    (dict(w=ctypes.c_void_p(0x10002)), bd.GDN_EINVAL),
+    (dict(S0=MIS), bd.GDN_EINVAL),
+    (dict(S0=ctypes.c_void_p(0x10000), ST=ctypes.c_void_p(0x10100)), bd.GDN_EINVAL),
+])
+def test_gated_argument_errors(kw, status):
+    assert gated(**kw) == status

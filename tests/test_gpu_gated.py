@@ -1,0 +1,102 @@
+"""GPU parity of the generalised gates (gdn_gated_recurrent: a retention per
+key channel, a key-side erase gate and a value-side write gate) against the
+oracle's gdn2_prefill, and its reductions to Kimi Delta Attention and to the
+gated delta rule of gdn_prefill ("Linear Attention Architectures" reading
+notes, Secs. 2.5-2.6)."""
+
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_recurrent_delta_amd import binding as gdn
+from oracle import gdn_oracle as orc
+from tests.gpu_util import (TOL_BF16, TOL_F32, assert_close, errs_S, errs_o,
+                            host, tdtype, to_dev)
+from workloads import gdn_inputs as gi
+
+pytestmark = pytest.mark.gpu
+
+
+def dev32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda")
+
+
+def run(x, al, b, w, out_dt, S0=None, ST=None):
+    d = to_dev(x)
+    s0 = d["S0"] if S0 is None else S0
+    o, S = gdn.gated_recurrent(d["q"], d["k"], d["v"], dev32(al), dev32(b), dev32(w), s0,
+                               out_dtype=tdtype(out_dt), ST=ST)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def check(x, al, b, w, out_dt=None, label="", heads=None):
+    out_dt = x.dtype if out_dt is None else out_dt
+    print(f"  case {label}: {x.q.shape} out={out_dt}", flush=True)
+    o, S = run(x, al, b, w, out_dt)
+    o_ref, S_ref = orc.gdn2_prefill(x.q, x.k, x.v, al, b, w, x.S0, heads=heads)
+    tol_o = TOL_F32 if out_dt == "f32" else TOL_BF16
+    assert_close(f"{label} o", errs_o(host(o), o_ref, heads), tol_o)
+    assert_close(f"{label} S_T", errs_S(host(S), S_ref, heads), TOL_F32)
+
+
+@pytest.mark.parametrize("T", [1, 5, 37])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_gated_matches_oracle(T, dk, dv, dt):
+    x = gi.generic(2, T, 3, dk, dv, 6000 + T + dk + dv, dt, S0_scale=0.3)
+    al, b, w = gi.gate_vectors(2, T, 3, dk, dv, 6100 + T + dk + dv)
+    check(x, al, b, w, label=f"T={T}")
+
+
+def test_gated_long_sequence_fp32_out():
+    """Several ring turns and a ragged tail (T = 601 = 4 * 150 + 1)."""
+    x = gi.generic(1, 601, 2, 128, 128, 6200, "bf16", S0_scale=0.3)
+    al, b, w = gi.gate_vectors(1, 601, 2, 128, 128, 6201)
+    check(x, al, b, w, "f32", label="T=601")
+
+
+def test_gated_decode_batch64():
+    """T = 1 over B=64, H=16 carried states: the decode step."""
+    for dk in (128, 64):
+        x = gi.generic(64, 1, 16, dk, 128, 6300 + dk, "bf16", S0_scale=0.5)
+        al, b, w = gi.gate_vectors(64, 1, 16, dk, 128, 6301 + dk)
+        check(x, al, b, w, label=f"decode B=64 dk={dk}")
+
+
+def test_kda_and_gdn_reductions_match_chunked_prefill():
+    """b = w = beta broadcast is Kimi Delta Attention; with alpha broadcast
+    from the scalar gate too, the result must match gdn_prefill's chunked
+    kernels (and the oracle)."""
+    B, T, H, dk, dv = 1, 300, 4, 128, 128
+    x = gi.generic(B, T, H, dk, dv, 6400, "bf16", S0_scale=0.3)
+    al = np.repeat(x.alpha[..., None], dk, -1)
+    b = np.repeat(x.beta[..., None], dk, -1)
+    w = np.repeat(x.beta[..., None], dv, -1)
+    o_g, S_g = run(x, al, b, w, "f32")
+    d = to_dev(x)
+    o_c, S_c = gdn.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"],
+                           out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, S_ref = orc.gdn_prefill(x.q, x.k, x.v, x.alpha, x.beta, x.S0)
+    assert_close("gated o vs oracle", errs_o(host(o_g), o_ref), TOL_F32)
+    assert_close("gated S vs oracle", errs_S(host(S_g), S_ref), TOL_F32)
+    assert_close("gated o vs chunked", errs_o(host(o_g), host(o_c)), TOL_F32)
+    assert_close("gated S vs chunked", errs_S(host(S_g), host(S_c)), TOL_F32)
+
+
+def test_gated_in_place_and_empty():
+    x = gi.generic(2, 20, 3, 64, 128, 6500, "f32", S0_scale=0.3)
+    al, b, w = gi.gate_vectors(2, 20, 3, 64, 128, 6501)
+    d = to_dev(x)
+    S = d["S0"].clone()
+    o1, S1 = run(x, al, b, w, "f32")
+    o2, S2 = run(x, al, b, w, "f32", S0=S, ST=S)
+    assert S2.data_ptr() == S.data_ptr()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    # T = 0 copies the initial state
+    e = torch.empty((2, 0, 3, 64), dtype=torch.float32, device="cuda")
+    ev = torch.empty((2, 0, 3, 128), dtype=torch.float32, device="cuda")
+    o0, S0c = gdn.gated_recurrent(e, e, ev, e, e, ev, d["S0"])
+    torch.cuda.synchronize()
+    assert o0.numel() == 0 and torch.equal(S0c, d["S0"])

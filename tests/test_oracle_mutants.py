@@ -172,3 +172,64 @@ def test_input_path_mutant_is_caught(monkeypatch, mutation):
         except (AssertionError, ValueError, IndexError):
             failures += 1
     assert failures > 0, f"no pin catches the '{mutation}' slip"
+
+
+# --- the generalised gates (gdn2_head) --------------------------------------
+
+from tests import test_oracle_gdn2_pins as g2_pins  # noqa: E402
+
+G2_PIN_TESTS = [
+    g2_pins.test_worked_one_token,
+    lambda: g2_pins.test_reduces_to_gated_delta_rule(8, 5),
+    lambda: g2_pins.test_reduces_to_gated_delta_rule(6, 6),
+    g2_pins.test_kda_write_stores_value_exactly,
+    g2_pins.test_zero_gates_only_decay_per_channel,
+    g2_pins.test_unkeyed_channel_keeps_its_column,
+    g2_pins.test_write_gate_scales_value_rows_only,
+]
+
+G2_MUTANTS = ["decay_on_value_side", "erase_outer_along_e", "erase_read_along_k",
+              "decay_after_erase", "write_gate_on_key"]
+
+
+def _make_g2(mutation):
+    def head(q, k, v, alpha, b, w, S0=None):
+        q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+        alpha, b, w = (np.asarray(x, np.float64) for x in (alpha, b, w))
+        T, dk = k.shape
+        dv = v.shape[1]
+        S = np.zeros((dv, dk)) if S0 is None else np.array(S0, np.float64)
+        o = np.empty((T, dv))
+        for t in range(T):
+            e = b[t] * k[t]
+            z = (w[t] * v[t]) if mutation != "write_gate_on_key" else (
+                v[t] * np.resize(b[t], dv))
+            if mutation == "decay_on_value_side" and dv == dk:
+                S = alpha[t][:, None] * S
+            elif mutation != "decay_after_erase":
+                S = S * alpha[t][None, :]
+            rd = S @ (k[t] if mutation == "erase_read_along_k" else e)
+            S = S - np.outer(rd, e if mutation == "erase_outer_along_e" else k[t]) + np.outer(z, k[t])
+            if mutation == "decay_after_erase":
+                S = S * alpha[t][None, :]
+            o[t] = S @ q[t]
+        return o, S
+    return head
+
+
+@pytest.mark.parametrize("mutation", G2_MUTANTS)
+def test_generalised_gate_mutant_is_caught(monkeypatch, mutation):
+    monkeypatch.setattr(orc, "gdn2_head", _make_g2(mutation))
+    failures = 0
+    for t in G2_PIN_TESTS:
+        try:
+            t()
+        except (AssertionError, ValueError, IndexError):
+            failures += 1
+    assert failures > 0, f"no pin catches the '{mutation}' slip"
+
+
+def test_unmutated_generalised_gate_copy_passes(monkeypatch):
+    monkeypatch.setattr(orc, "gdn2_head", _make_g2("none"))
+    for t in G2_PIN_TESTS:
+        t()

@@ -263,6 +263,19 @@ def raw_qk(B: int, T: int, H: int, dk_in: int, dv: int, seed: int,
     return _finish(q, k, v, alpha, beta, S0, dtype, seed, name, idx)
 
 
+def gate_vectors(B: int, T: int, H: int, dk: int, dv: int, seed: int,
+                 log_alpha_range=(0.001, 0.1)):
+    """Gates of the generalised recurrence, float32: a retention per key
+    channel alpha = exp(-U(range)) [B, T, H, dk], an erase gate per key
+    channel b = sigmoid(N(0, 1)) [B, T, H, dk] and a write gate per value
+    channel w = sigmoid(N(0, 1)) [B, T, H, dv]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    alpha = _decay(rng, (B, T, H, dk), *log_alpha_range)
+    b = _sigmoid(rng.standard_normal((B, T, H, dk)))
+    w = _sigmoid(rng.standard_normal((B, T, H, dv)))
+    return alpha, b, w
+
+
 def pruning_subsets(config: int, H: int = 16, dk: int = 128,
                     dk_keep: int = 64) -> np.ndarray:
     """The fixed per-head channel subsets P_I of a channel-pruned layer
