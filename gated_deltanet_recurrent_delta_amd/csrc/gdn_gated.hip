@@ -43,8 +43,10 @@ struct TokIn {
 
 // P: tokens whose inputs are in flight (a register ring); NG: groups of 4
 // rows per wave (the token's key-side inputs are loaded once for all of
-// them).
-template <int DK, int P, int NG, typename TIn, typename TOut>
+// them); HAS_S0: an initial state is given (a compile-time choice keeps the
+// state loads out of a branch, after which the compiler's waits would drain
+// every load in flight).
+template <int DK, int P, int NG, bool HAS_S0, typename TIn, typename TOut>
 __global__ __launch_bounds__(256) void gated_recurrent_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const float* __restrict__ alpha,
@@ -60,22 +62,6 @@ __global__ __launch_bounds__(256) void gated_recurrent_kernel(
   const int row0 = (wave - head * slices) * 4 * NG + (lane >> 4);   // row of group 0
   const int sub = lane & 15;
   const int b = head / H, h = head - b * H;
-
-  // rows row0 + 4 g of the state, lane's columns 64 f + 4 sub .. + 3
-  floatx4 s[NG][F];
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const size_t srow = ((size_t)head * dv + row0 + 4 * g) * DK;
-#pragma unroll
-    for (int f = 0; f < F; ++f) {
-      if (S0 != nullptr) {
-        s[g][f] = __builtin_nontemporal_load(
-            reinterpret_cast<const floatx4*>(S0 + srow + 64 * f + 4 * sub));
-      } else {
-        s[g][f] = floatx4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-  }
 
   // inputs of token t (0 <= t < T)
   auto load_tok = [&](TokIn<F, NG>& x, int t) {
@@ -98,6 +84,25 @@ __global__ __launch_bounds__(256) void gated_recurrent_kernel(
   TokIn<F, NG> ring[P];
 #pragma unroll
   for (int i = 0; i < P; ++i) load_tok(ring[i], min(i, T - 1));
+
+  // rows row0 + 4 g of the state, lane's columns 64 f + 4 sub .. + 3; loaded
+  // after the first tokens' inputs, which the first step needs first
+  // (vector-memory loads return in order)
+  floatx4 s[NG][F];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const size_t srow = ((size_t)head * dv + row0 + 4 * g) * DK;
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      if constexpr (HAS_S0) {
+        s[g][f] = __builtin_nontemporal_load(
+            reinterpret_cast<const floatx4*>(S0 + srow + 64 * f + 4 * sub));
+      } else {
+        s[g][f] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  }
+
 
   for (int t0 = 0; t0 < T; t0 += P) {
     float ob[P][NG];
@@ -178,12 +183,17 @@ hipError_t launch_gated_recurrent(const void* q, const void* k, const void* v,
   // sequences: 4 rows per wave (more waves to hide the per-token latency)
   // and a ring of 4 tokens in flight (measured at B=8, T=4096, dk=64: 2.8 ms
   // against 3.7 ms with 2).
-#define GDN_GATED_P(DK, P, NG, TI, TO)                                                       \
-  hipLaunchKernelGGL((gated_recurrent_kernel<DK, P, NG, TI, TO>),                            \
+#define GDN_GATED_K(DK, P, NG, S0_, TI, TO)                                                  \
+  hipLaunchKernelGGL((gated_recurrent_kernel<DK, P, NG, S0_, TI, TO>),                       \
                      dim3((unsigned)(((long)BH * (dv / (4 * NG)) + 3) / 4)), dim3(256), 0,   \
                      stream, static_cast<const TI*>(q), static_cast<const TI*>(k),           \
                      static_cast<const TI*>(v), alpha, bgate, wgate, S0, ST,                  \
                      static_cast<TO*>(o), BH, H, T, dv)
+#define GDN_GATED_P(DK, P, NG, TI, TO)                          \
+  do {                                                          \
+    if (S0 != nullptr) GDN_GATED_K(DK, P, NG, true, TI, TO);    \
+    else GDN_GATED_K(DK, P, NG, false, TI, TO);                 \
+  } while (0)
 #define GDN_GATED(DK, TI, TO)                      \
   do {                                             \
     if (T == 1) GDN_GATED_P(DK, 1, 4, TI, TO);     \
@@ -203,6 +213,7 @@ hipError_t launch_gated_recurrent(const void* q, const void* k, const void* v,
   }
 #undef GDN_GATED
 #undef GDN_GATED_P
+#undef GDN_GATED_K
   return hipGetLastError();
 }
 

@@ -110,3 +110,100 @@ def test_decode_graph_replays_match_eager(B, dk):
         torch.cuda.synchronize()
         assert torch.equal(outs, o_ref), f"replay {rep}: o differs"
         assert torch.equal(S, S_ref), f"replay {rep}: S differs"
+
+
+# --- the fused input path and the generalised gates --------------------------
+
+@pytest.mark.parametrize("B,T,H", [(1, 2085, 2), (4, 300, 8)])
+def test_prefill_qk_graph_replays_match_eager(B, T, H):
+    """Channel subset 128 -> 64, normalisation and query scale inside the
+    kernels (the gathered copy lives in the workspace), segmented and not."""
+    dev = torch.device("cuda")
+    r = __import__("numpy").random.Generator(__import__("numpy").random.PCG64(515 + T))
+    ch_np = __import__("numpy").stack([__import__("numpy").sort(r.permutation(128)[:64])
+                                       for _ in range(H)]).astype("int32")
+    x = gi.raw_qk(B, T, H, 128, 128, 516 + T, "bf16", channel_idx=ch_np, S0_scale=0.3)
+    d = to_dev(x)
+    ch = torch.from_numpy(ch_np).to(dev)
+    ws = torch.empty(gdn.prefill_qk_workspace_bytes(B, T, H, 64, 128, torch.bfloat16, True),
+                     dtype=torch.uint8, device=dev)
+    ws.fill_(0xFF)
+    o = torch.empty((B, T, H, 128), dtype=torch.bfloat16, device=dev)
+    ST = torch.empty((B, H, 128, 64), dtype=torch.float32, device=dev)
+
+    def step():
+        gdn.prefill_qk(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], channels=ch,
+                       q_scale=0.125, o=o, ST=ST, workspace=ws, validate=False)
+
+    step()
+    torch.cuda.synchronize()
+    o_ref, S_ref = o.clone(), ST.clone()
+    assert torch.isfinite(o_ref.float()).all() and torch.isfinite(S_ref).all()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(REPLAYS):
+        o.fill_(float("nan"))
+        ST.fill_(float("nan"))
+        ws.fill_(0xFF)
+        _other_eager_work(dev)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref), f"replay {rep}: o differs"
+        assert torch.equal(ST, S_ref), f"replay {rep}: S_T differs"
+
+
+@pytest.mark.parametrize("kind", ["decode_qk", "gated_decode", "gated_prefill"])
+def test_new_entry_points_graph_replays_match_eager(kind):
+    import numpy as np
+    dev = torch.device("cuda")
+    B, H, dv, n = 64, 16, 128, 3
+    S0 = (0.3 * torch.randn((B, H, dv, 64), generator=torch.Generator().manual_seed(9))).to(dev)
+    S = S0.clone()
+    if kind == "decode_qk":
+        ch_np = gi.pruning_subsets(3, H, 128, 64)
+        x = gi.raw_qk(B, n, H, 128, dv, 8100, "bf16", channel_idx=ch_np)
+        d = to_dev(x)
+        ch = torch.from_numpy(ch_np).to(dev)
+        outs = torch.empty((n, B, H, dv), dtype=torch.bfloat16, device=dev)
+
+        steps = [[d[nm][:, t].contiguous() for nm in ("q", "k", "v", "alpha", "beta")]
+                 for t in range(n)]
+
+        def run():
+            for t in range(n):
+                gdn.decode_step_qk(*steps[t], S, S_out=S, o=outs[t], channels=ch,
+                                   q_scale=0.125, validate=False)
+    else:
+        T = 1 if kind == "gated_decode" else 37
+        reps = n if kind == "gated_decode" else 1
+        x = gi.generic(B if T == 1 else 2, T, H, 64, dv, 8200 + T, "bf16")
+        al, bg, wg = (torch.from_numpy(z).to(dev) for z in
+                      gi.gate_vectors(x.q.shape[0], T, H, 64, dv, 8300 + T))
+        d = to_dev(x)
+        if T > 1:
+            S0 = S0[:2].contiguous()
+            S = S0.clone()
+        outs = torch.empty((reps,) + tuple(x.v.shape), dtype=torch.bfloat16, device=dev)
+
+        def run():
+            for t in range(reps):
+                gdn.gated_recurrent(d["q"], d["k"], d["v"], al, bg, wg, S, o=outs[t], ST=S)
+    run()
+    torch.cuda.synchronize()
+    o_ref, S_ref = outs.clone(), S.clone()
+    assert torch.isfinite(o_ref.float()).all()
+    g = torch.cuda.CUDAGraph()
+    S.copy_(S0)
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(REPLAYS):
+        S.copy_(S0)
+        outs.fill_(float("nan"))
+        _other_eager_work(dev)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(outs, o_ref), f"replay {rep}: o differs"
+        assert torch.equal(S, S_ref), f"replay {rep}: S differs"
