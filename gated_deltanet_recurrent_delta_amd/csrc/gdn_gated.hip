@@ -104,23 +104,30 @@ __global__ __launch_bounds__(256) void gated_recurrent_kernel(
   }
 
 
-  for (int t0 = 0; t0 < T; t0 += P) {
-    float ob[P][NG];
+  // Tokens run in groups of SP = P * R (R ring turns); the outputs of a
+  // group are stored after it, so the compiler's drain of every load in
+  // flight (which it inserts at the first load wait after a store) happens
+  // once per group instead of once per ring turn.
+  constexpr int R = P > 1 ? 4 : 1;
+  constexpr int SP = P * R;
+  for (int t0 = 0; t0 < T; t0 += SP) {
+    float ob[SP][NG];
 #pragma unroll
-    for (int i = 0; i < P; ++i) {
+    for (int j = 0; j < SP; ++j) {
+      const int i = j % P;                // ring slot of token t0 + j
       const TokIn<F, NG> x = ring[i];
       // unconditional (clamped) prefetch: a load under a branch would make
       // the compiler's waits after it drain every load in flight.  The
       // one-token instance (launched for T == 1) skips it: there is no
       // next token, and its loads are all needed at once anyway.
       if constexpr (P > 1) {
-        load_tok(ring[i], min(t0 + i + P, T - 1));
+        load_tok(ring[i], min(t0 + j + P, T - 1));
       } else {
-        if (T > 1) load_tok(ring[i], min(t0 + i + P, T - 1));
+        if (T > 1) load_tok(ring[i], min(t0 + j + P, T - 1));
       }
 #pragma unroll
-      for (int g = 0; g < NG; ++g) ob[i][g] = 0.f;
-      if (t0 + i >= T) continue;          // past the last token (uniform per wave)
+      for (int g = 0; g < NG; ++g) ob[j][g] = 0.f;
+      if (t0 + j >= T) continue;          // past the last token (uniform per wave)
       float kq = 0.f;
 #pragma unroll
       for (int f = 0; f < F; ++f)
@@ -147,16 +154,16 @@ __global__ __launch_bounds__(256) void gated_recurrent_kernel(
         for (int f = 0; f < F; ++f)
           s[g][f] = floatx4{sa[f][0] + u * x.k[f].x, sa[f][1] + u * x.k[f].y,
                             sa[f][2] + u * x.k[f].z, sa[f][3] + u * x.k[f].w};
-        ob[i][g] = r + u * kq;
+        ob[j][g] = r + u * kq;
       }
     }
     if (sub == 0) {
 #pragma unroll
-      for (int i = 0; i < P; ++i)
+      for (int j = 0; j < SP; ++j)
 #pragma unroll
         for (int g = 0; g < NG; ++g)
-          if (t0 + i < T)
-            store1(o + (((size_t)b * T + t0 + i) * H + h) * dv + row0 + 4 * g, ob[i][g]);
+          if (t0 + j < T)
+            store1(o + (((size_t)b * T + t0 + j) * H + h) * dv + row0 + 4 * g, ob[j][g]);
     }
   }
 
@@ -172,6 +179,8 @@ __global__ __launch_bounds__(256) void gated_recurrent_kernel(
   }
 }
 
+constexpr long kSimds = 1024;   // 256 CUs x 4 SIMDs
+
 hipError_t launch_gated_recurrent(const void* q, const void* k, const void* v,
                                   const float* alpha, const float* bgate,
                                   const float* wgate, const float* S0, float* ST,
@@ -179,10 +188,13 @@ hipError_t launch_gated_recurrent(const void* q, const void* k, const void* v,
                                   int in_dtype, int out_dtype, hipStream_t stream) {
   const int BH = B * H;
   // T == 1 (decode): 16 rows per wave, so a token's key-side inputs (k, q
-  // and the two per-channel gates) are read once per 16 rows; longer
-  // sequences: 4 rows per wave (more waves to hide the per-token latency)
-  // and a ring of 4 tokens in flight (measured at B=8, T=4096, dk=64: 2.8 ms
-  // against 3.7 ms with 2).
+  // and the two per-channel gates) are read once per 16 rows.  Longer
+  // sequences: a ring of 4 tokens in flight (at B=8, T=4096, dk=64, 4 rows
+  // per wave: 2.8 ms against 3.7 ms with 2), and as many rows per wave as
+  // still leave one wave per SIMD: the sequence form is bound by VALU issue,
+  // and the per-token work shared by a wave's rows (k.q, b * k, the
+  // addresses and conversions) is then spread over more rows (same shape:
+  // 2.68 ms with 4 rows, 1.67 ms with 8, 1.64 ms with 16 per wave).
 #define GDN_GATED_K(DK, P, NG, S0_, TI, TO)                                                  \
   hipLaunchKernelGGL((gated_recurrent_kernel<DK, P, NG, S0_, TI, TO>),                       \
                      dim3((unsigned)(((long)BH * (dv / (4 * NG)) + 3) / 4)), dim3(256), 0,   \
@@ -194,10 +206,12 @@ hipError_t launch_gated_recurrent(const void* q, const void* k, const void* v,
     if (S0 != nullptr) GDN_GATED_K(DK, P, NG, true, TI, TO);    \
     else GDN_GATED_K(DK, P, NG, false, TI, TO);                 \
   } while (0)
-#define GDN_GATED(DK, TI, TO)                      \
-  do {                                             \
-    if (T == 1) GDN_GATED_P(DK, 1, 4, TI, TO);     \
-    else GDN_GATED_P(DK, 4, 1, TI, TO);            \
+#define GDN_GATED(DK, TI, TO)                                    \
+  do {                                                           \
+    if (T == 1) GDN_GATED_P(DK, 1, 4, TI, TO);                   \
+    else if ((long)BH * dv / 16 >= kSimds) GDN_GATED_P(DK, 4, 4, TI, TO); \
+    else if ((long)BH * dv / 8 >= kSimds) GDN_GATED_P(DK, 4, 2, TI, TO);  \
+    else GDN_GATED_P(DK, 4, 1, TI, TO);                          \
   } while (0)
   const bool ib = in_dtype == 1, ob = out_dtype == 1;
   if (dk == 128) {

@@ -100,3 +100,14 @@ def test_gated_in_place_and_empty():
     o0, S0c = gdn.gated_recurrent(e, e, ev, e, e, ev, d["S0"])
     torch.cuda.synchronize()
     assert o0.numel() == 0 and torch.equal(S0c, d["S0"])
+
+
+@pytest.mark.parametrize("B,H,T,dk,dv", [(8, 16, 40, 64, 128), (4, 16, 33, 128, 128),
+                                         (8, 16, 21, 128, 64)])
+def test_gated_many_heads_row_groupings(B, H, T, dk, dv):
+    """Enough heads for the sequence form to carry 16 (B=8, H=16, dv=128) or
+    8 (B=4, H=16; B=8 with dv=64) rows per wave; every head against the
+    oracle."""
+    x = gi.generic(B, T, H, dk, dv, 6600 + B + T + dk + dv, "bf16", S0_scale=0.3)
+    al, b, w = gi.gate_vectors(B, T, H, dk, dv, 6700 + B + T + dk + dv)
+    check(x, al, b, w, "f32", label=f"B={B} H={H} T={T}")
