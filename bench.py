@@ -181,11 +181,11 @@ COUNTER_LEGS = {
     "batched_qk_norm_dk64": [("prepare_kernel", 64, 0, 64 * 16 * 8 * 64),
                              ("scan_kernel", 64, None, 8 * 16 * 2 * 256)],
     "decode_qk_norm_B64_dk64": [("decode_kernel", 64, 1, 64 * 16 * 8 * 64)],
-    # generalised gates: the decode (16 rows per wave) and sequence (4 rows
-    # per wave) instances differ in grid
+    # generalised gates, 16 rows per wave in both: the decode (B=64) and
+    # sequence (B=8) launches differ in grid
     "gated_decode_B64_dk128": [("gated_recurrent_kernel", 128, None, 64 * 16 * 8 * 64)],
     "gated_decode_B64_dk64": [("gated_recurrent_kernel", 64, None, 64 * 16 * 8 * 64)],
-    "gated_prefill_B8_T4096_dk64": [("gated_recurrent_kernel", 64, None, 8 * 16 * 32 * 64)],
+    "gated_prefill_B8_T4096_dk64": [("gated_recurrent_kernel", 64, None, 8 * 16 * 8 * 64)],
 }
 
 
