@@ -124,10 +124,20 @@ def settle(torch, fn, min_calls):
     return calls
 
 
+# Host-only sources (argument checks and dispatch, the host channel
+# selection) do not change what a kernel moves; every other source file in
+# csrc/ is hashed.
+HOST_ONLY_SOURCES = ("gdn_api.hip", "gdn_select.hip")
+
+
 def kernel_source_hash():
+    """Hash of the GPU kernel sources (and their launch code): the counter
+    traffic stored in profiles/traffic.json is valid while it is unchanged."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_deltanet_recurrent_delta_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if f in HOST_ONLY_SOURCES:
+            continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -625,6 +635,9 @@ def main(argv=None):
     if not a.skip_truncated:
         truncated = bench_truncated(torch, gdn, dev, stream, up)
 
+    # ---------------- DRRQR channel selection (host, calibration time) ----------
+    selection = bench_drrqr(gdn)
+
     copy_bw = copy_bandwidth(torch, dev, stream)
     log(f"device copy (512 MiB): {copy_bw / 1e9:.0f} GB/s read+write")
     out = {
@@ -651,6 +664,7 @@ def main(argv=None):
         "fused_input_path": qk,
         "generalised_gates": gated,
         "truncated_prefill": truncated,
+        "channel_selection": selection,
         "cpu_baseline": cpu,
         "copy_bandwidth_GBps": copy_bw / 1e9,
         "host": platform.node(),
@@ -848,6 +862,26 @@ def bench_batched_qk(torch, gdn, dev, stream, steps, warmup, up, gather=True):
         f"{us:.1f} us, {res['tokens_per_s'] / 1e6:.1f} M tokens/s")
     del q, k, v, al, be, o, ST, ws
     torch.cuda.empty_cache()
+    return res
+
+
+def bench_drrqr(gdn, n_tokens=8192, d=128, k=64, f=1.1, heads=4):
+    """The library's host DRRQR on the calibration matrix of each of `heads`
+    heads: raw key and query projections of n_tokens seeded tokens stacked
+    ([2 n_tokens, d] fp64), keeping k channels."""
+    x = gi.raw_qk(1, n_tokens, heads, d, 8, gi.seed_for(4, 6))
+    times, swaps = [], []
+    for h in range(heads):
+        M = np.concatenate([x.k[0, :, h], x.q[0, :, h]], axis=0).astype(np.float64)
+        t0 = time.perf_counter()
+        _, sw, rho = gdn.drrqr_select(M, k, f)
+        times.append(time.perf_counter() - t0)
+        swaps.append(sw)
+    res = {"ms_per_head": 1e3 * float(np.median(times)), "swaps": swaps,
+           "matrix": f"[{2 * n_tokens}, {d}] fp64 (K and Q samples of one head), k={k}, f={f}",
+           "where": "host code in libgdn (calibration time, not a per-token kernel)"}
+    log(f"DRRQR channel selection: {res['ms_per_head']:.0f} ms per head ({res['matrix']}), "
+        f"trades {swaps}")
     return res
 
 

@@ -49,6 +49,7 @@ SIGNATURES = {
                                 _i, _i, _vp]),
     "gdn_gated_recurrent": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "gdn_drrqr_select": (_i, [_vp, _i, _i, _i, ctypes.c_double, _i, _vp, _vp, _vp]),
     "gdn_truncate_workspace_bytes": (_sz, [_i, _i, _i]),
     "gdn_truncate_rank": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
 }
@@ -418,6 +419,35 @@ def gated_recurrent(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                  _stream_handle(q, stream))
     _check(st, "gdn_gated_recurrent")
     return o, ST
+
+
+# ---------------------------------------------------------------------------
+# DRRQR channel selection (host)
+# ---------------------------------------------------------------------------
+
+def drrqr_select(M, k: int, f: float = 2.0, max_swaps: int = 10000):
+    """Kept channels of one head from calibration samples M [rows, n] (a
+    numpy array or CPU tensor; samples as rows, K and Q samples stacked),
+    by the library's host DRRQR (see include/gdn.h).  Returns (int32 array
+    of the k kept channels, swaps made, final max rho)."""
+    import numpy as np
+    if isinstance(M, torch.Tensor):
+        if M.is_cuda:
+            raise ValueError("M must be in host memory")
+        M = M.numpy()
+    M = np.ascontiguousarray(M, dtype=np.float64)
+    if M.ndim != 2:
+        raise ValueError("M must be [rows, n]")
+    rows, n = M.shape
+    sel = np.empty(max(int(k), 1), dtype=np.int32)
+    sw = ctypes.c_int(0)
+    rho = ctypes.c_double(0.0)
+    st = lib.gdn_drrqr_select(M.ctypes.data_as(ctypes.c_void_p), rows, n, int(k),
+                              float(f), int(max_swaps),
+                              sel.ctypes.data_as(ctypes.c_void_p), ctypes.byref(sw),
+                              ctypes.byref(rho))
+    _check(st, "gdn_drrqr_select")
+    return sel[:k], sw.value, rho.value
 
 
 # ---------------------------------------------------------------------------

@@ -23,7 +23,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 
 SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_gated.hip", "gdn_prefill.hip",
-           "gdn_truncate.hip"]
+           "gdn_select.hip", "gdn_truncate.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -302,6 +302,17 @@ int gdn_gated_recurrent(const void* q, const void* k, const void* v,
       static_cast<hipStream_t>(stream)));
 }
 
+int gdn_drrqr_select(const double* M, int rows, int n, int k, double f,
+                     int max_swaps, int* selected, int* swaps, double* rho_max) {
+  if (!M || !selected) return GDN_EINVAL;
+  if (n < 2 || n > 4096 || k < 1 || k >= n || rows < n || max_swaps < 0)
+    return GDN_EINVAL;
+  if (!(f >= 1.0)) return GDN_EINVAL;
+  return gdn::drrqr_select(M, rows, n, k, f, max_swaps, selected, swaps, rho_max) == 0
+             ? GDN_OK
+             : GDN_EINVAL;
+}
+
 size_t gdn_truncate_workspace_bytes(int BH, int dv, int dk) {
   if (BH <= 0 || !dims_ok(dk, dv)) return 0;
   return (size_t)BH * (dv < dk ? dv : dk) * dv * sizeof(float);

@@ -132,6 +132,10 @@ hipError_t launch_truncate(float* S, int BH, int dv, int dk, int r, float* er,
 hipError_t launch_state_fill(const float* S0, float* ST, size_t n,
                              hipStream_t stream);
 
+// DRRQR channel selection on host memory (fp64): 0, or 1 if rank(M) < k.
+int drrqr_select(const double* M, int rows, int n, int k, double f, int max_swaps,
+                 int* selected, int* swaps_out, double* rho_out);
+
 // The generalised gates (per-key-channel retention alpha [B,T,H,dk], erase
 // gate b [B,T,H,dk], write gate w [B,T,H,dv]) in recurrent form, T >= 1.
 hipError_t launch_gated_recurrent(const void* q, const void* k, const void* v,

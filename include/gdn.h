@@ -241,6 +241,34 @@ int gdn_gated_recurrent(const void* q, const void* k, const void* v,
                         void* stream);
 
 /* ------------------------------------------------------------------------
+ * DRRQR channel selection (calibration time, HOST memory and host code).
+ *
+ * "On State Reduction in Linear Attention" (reading notes), Sec. 3.4 with
+ * Algorithm 2 and App. B.2: choose which k of a head's n key/query channels
+ * a pruned layer keeps, from calibration samples M = [K_cal; Q_cal] (rows =
+ * samples, one column per channel).  A QR with column pivoting gives the
+ * first choice; then, while some rho_ij = sqrt((A^{-1}B)_ij^2 +
+ * (gamma_j / omega_i)^2) exceeds f (A, B, C the blocks of the triangular
+ * factor, omega_i = 1 / ||row i of A^{-1}||, gamma_j = ||column j of C||),
+ * the kept column i and the dropped column j of the largest rho_ij trade
+ * places (strong rank-revealing QR).  At the end every such trade would
+ * grow the volume spanned by the kept columns by at most a factor f, and
+ * with c_f = sqrt(1 + f^2 k (n - k)): sigma_i(A) >= sigma_i(M) / c_f,
+ * ||C||_2 <= c_f sigma_{k+1}(M).
+ *   M          [rows, n] float64, row-major, HOST pointer; rows >= n.
+ *   k          channels kept, 1 <= k < n (n <= 4096).
+ *   f          tolerance >= 1 (the swap threshold).
+ *   max_swaps  bound on the number of trades (>= 0).
+ *   selected   [k] int32 HOST output: the kept channel indices, in the
+ *              order of the final factor's first k columns.
+ *   swaps      trades made, or NULL;  rho_max  final largest rho_ij, or NULL.
+ * fp64 throughout; no GPU work, no stream.  GDN_EINVAL for bad sizes, a
+ * null pointer, f < 1, or rank(M) < k.
+ */
+int gdn_drrqr_select(const double* M, int rows, int n, int k, double f,
+                     int max_swaps, int* selected, int* swaps, double* rho_max);
+
+/* ------------------------------------------------------------------------
  * Rank-r truncation of carried states.
  *
  * Replaces each state S (dv x dk) by U_r U_r^T S, where U_r holds the r

@@ -36,6 +36,10 @@ Sources (page titles as published; sections/equations as the pages give them):
     value-side write gates whose outer products keep k_t on the right
     (Gated DeltaNet-2): "Linear Attention Architectures" reading notes,
     Secs. 2.5-2.6 and the mechanism table after them.
+  * DRRQR channel selection (drrqr_select): a column-pivoted QR of the
+    calibration matrix of key and query samples, then strong-RRQR swaps
+    until every rho_ij <= f: "On State Reduction in Linear Attention",
+    Sec. 3.4 (Algorithm 2, App. B.2).
   * Input path of a channel-pruned layer (qk_transform): keep a per-head
     subset of query/key coordinates and renormalise over the kept ones:
     "On State Reduction in Linear Attention", Sec. 3.2-3.3.
@@ -237,6 +241,70 @@ def gdn_decode_step_qk(q_raw, k_raw, v, alpha, beta, S, *, channels=None,
     q = qk_transform(q_raw, channels, l2norm, q_scale)
     k = qk_transform(k_raw, channels, l2norm, 1.0)
     return gdn_decode_step(q, k, v, alpha, beta, S)
+
+
+# ---------------------------------------------------------------------------
+# DRRQR channel selection (strong rank-revealing QR on calibration samples)
+# ---------------------------------------------------------------------------
+
+def _qr_r(X):
+    """R factor (n x n, upper triangular) of a tall X with rows >= n."""
+    return np.linalg.qr(np.asarray(X, np.float64), mode="r")[: X.shape[1]]
+
+
+def drrqr_select(M, k: int, f: float = 2.0, max_swaps: int = 10000):
+    """Keep k of the n columns of the calibration matrix M = [K_cal; Q_cal]
+    (2N x n, samples as rows, one column per key/query channel).
+
+    "On State Reduction in Linear Attention" (reading notes), Sec. 3.4 and
+    its Algorithm 2 / App. B.2: a QR with column pivoting gives an initial
+    permutation, M P = Q [[A_k, B_k], [0, C_k]]; then, with
+    U = A_k^{-1} B_k, omega_i = 1 / ||row i of A_k^{-1}||, gamma_j =
+    ||column j of C_k|| and rho_ij = sqrt(U_ij^2 + (gamma_j / omega_i)^2),
+    while the largest rho_ij exceeds f, selected column i and candidate
+    column j trade places and the factor is re-triangularised.  Returns
+    (the k kept original channel indices in permutation order, the number
+    of swaps, the final max rho_ij).
+    """
+    M = np.asarray(M, np.float64)
+    n = M.shape[1]
+    assert M.shape[0] >= n and 1 <= k < n
+    # column-pivoted QR by hand: at each step the remaining column of largest
+    # norm (in the part below the rows already reduced) goes next
+    perm = list(range(n))
+    X = M.copy()
+    for c in range(n):
+        norms = np.linalg.norm(X[c:, c:], axis=0)
+        j = c + int(np.argmax(norms))
+        if j != c:
+            X[:, [c, j]] = X[:, [j, c]]
+            perm[c], perm[j] = perm[j], perm[c]
+        # Householder reflection zeroing X[c+1:, c]
+        x = X[c:, c]
+        nx = np.linalg.norm(x)
+        if nx == 0.0:
+            continue
+        v = x.copy()
+        v[0] += np.copysign(nx, x[0]) if x[0] != 0 else nx
+        v /= np.linalg.norm(v)
+        X[c:, c:] -= 2.0 * np.outer(v, v @ X[c:, c:])
+    R = np.triu(X[:n])
+    swaps = 0
+    while True:
+        A, B, Cm = R[:k, :k], R[:k, k:], R[k:, k:]
+        Ainv = np.linalg.inv(A)
+        U = Ainv @ B
+        omega = 1.0 / np.linalg.norm(Ainv, axis=1)
+        gamma = np.linalg.norm(Cm, axis=0)
+        rho = np.sqrt(U ** 2 + (gamma[None, :] / omega[:, None]) ** 2)
+        i, j = np.unravel_index(int(np.argmax(rho)), rho.shape)
+        if rho[i, j] <= f or swaps >= max_swaps:
+            return np.array(perm[:k]), swaps, float(rho[i, j])
+        a, b = int(i), k + int(j)
+        R[:, [a, b]] = R[:, [b, a]]
+        perm[a], perm[b] = perm[b], perm[a]
+        R = _qr_r(R)
+        swaps += 1
 
 
 # ---------------------------------------------------------------------------
