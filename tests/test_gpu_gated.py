@@ -111,3 +111,12 @@ def test_gated_many_heads_row_groupings(B, H, T, dk, dv):
     x = gi.generic(B, T, H, dk, dv, 6600 + B + T + dk + dv, "bf16", S0_scale=0.3)
     al, b, w = gi.gate_vectors(B, T, H, dk, dv, 6700 + B + T + dk + dv)
     check(x, al, b, w, "f32", label=f"B={B} H={H} T={T}")
+
+
+@pytest.mark.parametrize("B,H,T", [(2, 3, 37), (8, 16, 20), (64, 16, 1)])
+def test_gated_zero_initial_state(B, H, T):
+    """S0 = None (the kernels' zero-state instance) at every row grouping."""
+    x = gi.generic(B, T, H, 64, 128, 6800 + B + T, "bf16")
+    assert x.S0 is None
+    al, b, w = gi.gate_vectors(B, T, H, 64, 128, 6900 + B + T)
+    check(x, al, b, w, "f32", label=f"S0=None B={B} T={T}")

@@ -201,3 +201,46 @@ def test_decode_qk_chain_matches_prefill_qk():
     assert_close("prompt o", errs_o(host(o_p), o_ref[:, :Tp]), TOL_BF16)
     assert_close("decode o", errs_o(host(o_dec), o_ref[:, Tp:]), TOL_BF16)
     assert_close("S", errs_S(host(S), S_ref), TOL_F32)
+
+
+@pytest.mark.parametrize("T", [0, 130, 1500])
+def test_prefill_qk_in_place_state_and_empty(T):
+    """ST aliasing S0 (segmented at T=1500), and T = 0 copying S0."""
+    H = 2
+    ch = subsets(4600 + T, H, 128, 64)
+    x = gi.raw_qk(1, max(T, 1), H, 128, 128, 4601 + T, "bf16", channel_idx=ch, S0_scale=0.3)
+    d = to_dev(x)
+    if T == 0:
+        d = {n: (t[:, :0].contiguous() if n in ("q", "k", "v", "alpha", "beta") else t)
+             for n, t in d.items()}
+    S = d["S0"].clone()
+    o, ST = gdn.prefill_qk(d["q"], d["k"], d["v"], d["alpha"], d["beta"], S, ST=S,
+                           channels=dev_channels(ch), q_scale=QSCALE)
+    torch.cuda.synchronize()
+    assert ST.data_ptr() == S.data_ptr()
+    if T == 0:
+        assert torch.equal(ST, d["S0"])
+        return
+    o_ref, S_ref = orc.gdn_prefill_qk(x.q, x.k, x.v, x.alpha, x.beta, x.S0, channels=ch,
+                                      q_scale=QSCALE)
+    assert_close("o", errs_o(host(o), o_ref), TOL_BF16)
+    assert_close("S_T", errs_S(host(ST), S_ref), TOL_F32)
+
+
+def test_prefill_qk_zero_initial_state_and_decode_in_place():
+    ch = subsets(4700, 4, 128, 64)
+    x = gi.raw_qk(2, 90, 4, 128, 128, 4701, "bf16", channel_idx=ch)
+    check_prefill_qk(x, ch, True, QSCALE, label="S0=None")
+    y = gi.raw_qk(8, 1, 4, 128, 128, 4702, "bf16", channel_idx=ch, S0_scale=0.4)
+    d = to_dev(y)
+    sq = lambda t: t[:, 0].contiguous()
+    S = d["S0"].clone()
+    o, S1 = gdn.decode_step_qk(sq(d["q"]), sq(d["k"]), sq(d["v"]), sq(d["alpha"]),
+                               sq(d["beta"]), S, S_out=S, channels=dev_channels(ch),
+                               q_scale=QSCALE)
+    torch.cuda.synchronize()
+    assert S1.data_ptr() == S.data_ptr()
+    o_ref, S_ref = orc.gdn_decode_step_qk(y.q[:, 0], y.k[:, 0], y.v[:, 0], y.alpha[:, 0],
+                                          y.beta[:, 0], y.S0, channels=ch, q_scale=QSCALE)
+    assert_close("o", orc.rel_l2_per_head(host(o), o_ref, (0, 1)), TOL_BF16)
+    assert_close("S'", orc.rel_l2_per_head(host(S1), S_ref, (0, 1)), TOL_F32)
