@@ -25,9 +25,11 @@
 // rows stay exact MFMA operands and nk, nq are folded into A, P and the
 // per-token decay rows the scan reads (gamma nq, gamma nk, e^{g_C - g} nk).
 //
-// Two kernels:
+// The kernels:
 //  * prepare_kernel -- one wave per (batch, head, chunk), fully parallel.
-//    K and Q are read once from HBM straight into MFMA operand registers;
+//    K and Q are read once from HBM straight into MFMA operand registers
+//    (with a channel subset: the kept channels, also written out as the
+//    gathered copy the scan reads);
 //    the lower 16x16 tiles of K K^T and Q K^T run on bf16 MFMA; the decay
 //    factors are exp2 of differences of the scaled prefix sums (never of a
 //    single prefix sum, which can underflow); T is inverted in fp32 (the four
@@ -48,6 +50,11 @@
 //    Products that touch the state use split-bf16 operands (x = hi + lo, two
 //    MFMAs when the other operand is an exact bf16 input, three otherwise)
 //    with fp32 accumulation; outputs stored in bf16 use single-pass products.
+//  * scan_wide_kernel, segment_combine_kernel, segment_correct_kernel --
+//    the segmented scan for few heads and long sequences (bf16 in and out):
+//    every segment runs from a zero state together with transition rows
+//    that give its affine map, the segment states are chained, and the
+//    outputs of later segments are corrected (see SegArgs).
 #include <type_traits>
 
 #include "gdn_device.hpp"
