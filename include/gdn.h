@@ -19,8 +19,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every tensor pointer is a DEVICE pointer (hipMalloc'd or equivalent),
- *    owned by the caller.  The library never allocates, frees or
- *    synchronises inside these calls; work is enqueued on `stream` (a
+ *    owned by the caller, except in the host-side channel selection
+ *    (gdn_drrqr_select).  The library never allocates device memory, frees
+ *    or synchronises inside these calls; work is enqueued on `stream` (a
  *    hipStream_t passed as void*, NULL = the null stream) and completes
  *    asynchronously.
  *  - Layouts are dense, contiguous, row-major:
@@ -262,8 +263,10 @@ int gdn_gated_recurrent(const void* q, const void* k, const void* v,
  *   selected   [k] int32 HOST output: the kept channel indices, in the
  *              order of the final factor's first k columns.
  *   swaps      trades made, or NULL;  rho_max  final largest rho_ij, or NULL.
- * fp64 throughout; no GPU work, no stream.  GDN_EINVAL for bad sizes, a
- * null pointer, f < 1, or rank(M) < k.
+ * fp64 throughout; no GPU work, no stream.  Unlike the other entry points it
+ * allocates HOST memory (a column-major copy of M, rows * n doubles, and
+ * O(n^2) more), freed before it returns.  GDN_EINVAL for bad sizes, a null
+ * pointer, f < 1, or rank(M) < k.
  */
 int gdn_drrqr_select(const double* M, int rows, int n, int k, double f,
                      int max_swaps, int* selected, int* swaps, double* rho_max);
