@@ -244,3 +244,15 @@ def test_prefill_qk_zero_initial_state_and_decode_in_place():
                                           y.beta[:, 0], y.S0, channels=ch, q_scale=QSCALE)
     assert_close("o", orc.rel_l2_per_head(host(o), o_ref, (0, 1)), TOL_BF16)
     assert_close("S'", orc.rel_l2_per_head(host(S1), S_ref, (0, 1)), TOL_F32)
+
+
+@pytest.mark.parametrize("dk_in,dk", [(128, 64), (128, 128)])
+def test_prefill_qk_16k_segmented_sampled_heads(dk_in, dk):
+    """The 16K-token layer shape (B=1, H=16, T=16384, dv=128) from raw rows:
+    128 -> 64 through the channel subset, or 128 wide with normalisation
+    only; the segmented path; the oracle follows two heads."""
+    H, T = 16, 16384
+    ch = gi.pruning_subsets(2, H, dk_in, dk) if dk != dk_in else None
+    assert gdn.prefill_segments(1, T, H, dk, 128)[0] > 1
+    x = gi.raw_qk(1, T, H, dk_in, 128, gi.seed_for(2, 5), "bf16", channel_idx=ch)
+    check_prefill_qk(x, ch, True, QSCALE, label=f"16K {dk_in}->{dk}", heads=[(0, 3), (0, 12)])
