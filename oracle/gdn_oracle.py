@@ -31,6 +31,11 @@ Sources (page titles as published; sections/equations as the pages give them):
     singular directions at every 256-token boundary, r = 128 = no change):
     state-rank post, §3.
 
+  * Backward pass (gdn_head_backward): the gradient of
+    sum_t do_t . o_t + <dST, S_T> with respect to q, k, v, alpha, beta and
+    S_0, by the chain rule over the tokens in reverse.  The pages train
+    these layers but print no backward pass; it is pinned to central finite
+    differences of gdn_head and to the closed form of the beta = 0 case.
   * Generalised gates (gdn2_head): a per-key-channel decay applied on the
     right of the state (Kimi Delta Attention) and split key-side erase /
     value-side write gates whose outer products keep k_t on the right
@@ -135,6 +140,92 @@ def gdn_decode_step(q, k, v, alpha, beta, S):
                               np.asarray(beta)[b, h][None], S[b, h])
             o[b, h], S1[b, h] = ob[0], Sb
     return o, S1
+
+
+# ---------------------------------------------------------------------------
+# backward pass: the exact gradient of the recurrence above
+# ---------------------------------------------------------------------------
+
+def gdn_head_backward(q, k, v, alpha, beta, S0, do, dST):
+    """Gradients of L = sum_t do_t . o_t + <dST, S_T> through one head of
+    gdn_head (erase on, no truncation), by the chain rule taken backwards
+    over the tokens in float64.
+
+    The pages train these layers end to end ("Linear Attention
+    Architectures" reading notes, the training set-ups of its experiments;
+    "On State Reduction in Linear Attention", recovery fine-tuning after
+    pruning) but print no backward pass: this is the derivative of the
+    forward definition and nothing more.  Per token, with S~ = alpha S_prev,
+    w = v - S~ k, u = beta w and S = S~ + u k^T:
+        G      = dS + do q^T              gradient reaching S_t
+        dq     = S^T do
+        du     = G k;   dk = G^T u - beta S~^T du
+        dbeta  = du . w;   dv = beta du
+        dS~    = G - beta du k^T
+        dalpha = <dS~, S_prev>;   dS_prev = alpha dS~
+    q, k [T, dk]; v, do [T, dv]; alpha, beta [T]; S0, dST [dv, dk] or None
+    (zero).  Returns dq, dk [T, dk], dv [T, dv], dalpha, dbeta [T] and
+    dS0 [dv, dk], all float64.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    do = np.asarray(do, np.float64)
+    T, dk = k.shape
+    dv = v.shape[1]
+    S = np.zeros((dv, dk)) if S0 is None else np.array(S0, np.float64)
+    prev = np.empty((T, dv, dk))                   # S_{t-1} for every token
+    for t in range(T):
+        prev[t] = S
+        S = float(alpha[t]) * S
+        S = S + float(beta[t]) * np.outer(v[t] - S @ k[t], k[t])
+    G = np.zeros((dv, dk)) if dST is None else np.array(dST, np.float64)
+    dq = np.empty((T, dk))
+    dkk = np.empty((T, dk))
+    dvv = np.empty((T, dv))
+    da = np.empty(T)
+    db = np.empty(T)
+    for t in range(T - 1, -1, -1):
+        a, b = float(alpha[t]), float(beta[t])
+        St = a * prev[t]                           # S~
+        w = v[t] - St @ k[t]
+        u = b * w
+        Snew = St + np.outer(u, k[t])
+        G = G + np.outer(do[t], q[t])
+        dq[t] = Snew.T @ do[t]
+        du = G @ k[t]
+        dkk[t] = G.T @ u - b * (St.T @ du)
+        db[t] = du @ w
+        dvv[t] = b * du
+        dSt = G - b * np.outer(du, k[t])
+        da[t] = np.sum(dSt * prev[t])
+        G = a * dSt
+    return dq, dkk, dvv, da, db, G
+
+
+def gdn_backward(q, k, v, alpha, beta, S0, do, dST=None, heads=None):
+    """Batched layout of gdn_head_backward: q, k [B, T, H, dk]; v, do
+    [B, T, H, dv]; alpha, beta [B, T, H]; S0, dST [B, H, dv, dk] or None.
+    Returns dq, dk, dv, dalpha, dbeta, dS0 in the same layouts (float64;
+    heads not in `heads`, when given, are NaN)."""
+    B, T, H, dk = np.shape(q)
+    dv = np.shape(v)[-1]
+    dq = np.full((B, T, H, dk), np.nan)
+    dkk = np.full((B, T, H, dk), np.nan)
+    dvv = np.full((B, T, H, dv), np.nan)
+    da = np.full((B, T, H), np.nan)
+    db = np.full((B, T, H), np.nan)
+    dS0 = np.full((B, H, dv, dk), np.nan)
+    todo = heads if heads is not None else [(b, h) for b in range(B)
+                                            for h in range(H)]
+    for b, h in todo:
+        r = gdn_head_backward(
+            q[b, :, h], k[b, :, h], v[b, :, h], alpha[b, :, h], beta[b, :, h],
+            None if S0 is None else S0[b, h], do[b, :, h],
+            None if dST is None else dST[b, h])
+        dq[b, :, h], dkk[b, :, h], dvv[b, :, h] = r[0], r[1], r[2]
+        da[b, :, h], db[b, :, h], dS0[b, h] = r[3], r[4], r[5]
+    return dq, dkk, dvv, da, db, dS0
 
 
 # ---------------------------------------------------------------------------

@@ -233,3 +233,65 @@ def test_unmutated_generalised_gate_copy_passes(monkeypatch):
     monkeypatch.setattr(orc, "gdn2_head", _make_g2("none"))
     for t in G2_PIN_TESTS:
         t()
+
+
+# --- backward pass ---------------------------------------------------------
+
+def _make_backward(mutation):
+    def backward(q, k, v, alpha, beta, S0, do, dST):
+        q, k, v, do = (np.asarray(x, np.float64) for x in (q, k, v, do))
+        T, dk = k.shape
+        dv = v.shape[1]
+        S = np.zeros((dv, dk)) if S0 is None else np.array(S0, np.float64)
+        prev = []
+        for t in range(T):
+            prev.append(S)
+            S = alpha[t] * S
+            S = S + beta[t] * np.outer(v[t] - S @ k[t], k[t])
+        G = np.zeros((dv, dk)) if dST is None else np.array(dST, np.float64)
+        out = [np.empty((T, dk)), np.empty((T, dk)), np.empty((T, dv)), np.empty(T), np.empty(T)]
+        for t in range(T - 1, -1, -1):
+            a, b = float(alpha[t]), float(beta[t])
+            St = a * prev[t]
+            w = v[t] - St @ k[t]
+            u = b * w
+            Snew = St + np.outer(u, k[t])
+            G = G + np.outer(do[t], q[t])
+            out[0][t] = (prev[t] if mutation == "dq_old_state" else Snew).T @ do[t]
+            du = G @ k[t]
+            out[1][t] = G.T @ u - (0 if mutation == "dk_no_erase_term" else b * (St.T @ du))
+            out[4][t] = du @ (u if mutation == "dbeta_times_beta" else w)
+            out[2][t] = b * du
+            dSt = G - b * np.outer(du, k[t])
+            out[3][t] = np.sum(dSt * (St if mutation == "dalpha_decayed_state" else prev[t]))
+            G = dSt if mutation == "state_grad_undecayed" else a * dSt
+        return (*out, G)
+    return backward
+
+
+BACKWARD_MUTANTS = ["dq_old_state", "dk_no_erase_term", "dbeta_times_beta",
+                    "dalpha_decayed_state", "state_grad_undecayed"]
+
+
+def _backward_pins_fail():
+    from tests import test_oracle_backward_pins as bp
+    checks = [lambda: bp.test_matches_finite_differences(True, True),
+              bp.test_beta_zero_closed_form, bp.test_linear_in_cotangents]
+    failed = 0
+    for c in checks:
+        try:
+            c()
+        except AssertionError:
+            failed += 1
+    return failed
+
+
+def test_unmutated_backward_copy_passes(monkeypatch):
+    monkeypatch.setattr(orc, "gdn_head_backward", _make_backward(None))
+    assert _backward_pins_fail() == 0
+
+
+@pytest.mark.parametrize("mutation", BACKWARD_MUTANTS)
+def test_backward_mutant_is_caught(monkeypatch, mutation):
+    monkeypatch.setattr(orc, "gdn_head_backward", _make_backward(mutation))
+    assert _backward_pins_fail() > 0
