@@ -450,6 +450,8 @@ def main(argv=None):
                     help="of the fused input-path legs run only those with a "
                          "channel subset (for counter collection: the others "
                          "launch the same kernels at the same grids)")
+    ap.add_argument("--skip-backward", action="store_true",
+                    help="skip the backward pass leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16384)
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -630,6 +632,11 @@ def main(argv=None):
                     torch, gdn, dev, stream, 64, dkg, min(a.decode_steps, 64), a.layers, up)
         gated["prefill_B8_T4096_dk64"] = bench_gated_prefill(torch, gdn, dev, stream, up)
 
+    # ---------------- backward pass (recurrent form) ----------------
+    backward = {}
+    if not a.skip_backward:
+        backward = bench_backward(torch, gdn, dev, stream, up)
+
     # ---------------- segment-truncated prefill, r in {1, 4, 12, 32} ----------
     truncated = {}
     if not a.skip_truncated:
@@ -663,6 +670,7 @@ def main(argv=None):
         "batched_prefill": batched,
         "fused_input_path": qk,
         "generalised_gates": gated,
+        "backward": backward,
         "truncated_prefill": truncated,
         "channel_selection": selection,
         "cpu_baseline": cpu,
@@ -971,6 +979,56 @@ def bench_gated_prefill(torch, gdn, dev, stream, up, B=8, T=4096, H=16, dk=64, d
     log(f"generalised-gate prefill B={B} T={T} dk={dk} (recurrent form): {us:.0f} us, "
         f"{res['tokens_per_s'] / 1e6:.2f} M tokens/s, {us / T * 1e3:.0f} ns per token step")
     del q, k, v, al, bg, wg, o, ST
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_backward(torch, gdn, dev, stream, up, B=8, T=4096, H=16, dk=128, dv=128,
+                   calls=3):
+    """The backward pass (gradients of q, k, v, alpha, beta and S_0) at the
+    batched prefill's shape, bf16 inputs and d_o, fp32 gradients, in
+    recurrent form: bound by the per-token dependency chain, run three
+    times (forward to the checkpoints, forward again inside each block,
+    backward).  Reported as time, tokens/s and the HBM rate of its
+    algorithmic bytes (inputs, d_o, dST and S_0 read once; gradients
+    written once)."""
+    x = gi.generic(B, T, H, dk, dv, gi.seed_for(4, 9), "bf16", S0_scale=0.3)
+    d_o, dST = gi.cotangents(B, T, H, dk, dv, gi.seed_for(4, 10), "bf16")
+    q, k, v, al, be = up(x)
+    S0 = torch.from_numpy(x.S0).to(dev)
+    del x
+    d_o = torch.from_numpy(d_o).to(dev).to(torch.bfloat16)
+    dST = torch.from_numpy(dST).to(dev)
+    ws = torch.empty(gdn.backward_workspace_bytes(B, T, H, dk, dv), dtype=torch.uint8,
+                     device=dev)
+    out = {}
+
+    def call():
+        return gdn.backward(q, k, v, al, be, S0, d_o, dST, out=out, workspace=ws)
+    out.update(call())
+    settle(torch, call, 1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(calls):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    ntok = B * T * H
+    nbytes = (ntok * (2 * dk + 2 * dv) * 2 + ntok * 8 +        # q, k, v, d_o; alpha, beta
+              2 * B * H * dv * dk * 4 +                         # S_0, dST
+              ntok * (2 * dk + dv + 2) * 4 + B * H * dv * dk * 4)   # gradients, dS_0
+    res = {"workload": f"B={B}, T={T}, H={H}, dk={dk}, dv={dv}, bf16 q/k/v/d_o, "
+                       "fp32 gates, S_0, dS_T and gradients",
+           "us_per_call": us, "tokens_per_s": B * T / (us * 1e-6),
+           "us_per_token_step": us / T, "algorithmic_bytes": nbytes,
+           "hbm_frac": nbytes / (us * 1e-6) / HBM_PEAK,
+           "workspace_bytes": ws.numel(),
+           "bound": "latency of the per-token dependency chain (recurrent form)"}
+    log(f"backward B={B} T={T} H={H} dk={dk} (recurrent form): {us:.0f} us, "
+        f"{res['tokens_per_s'] / 1e6:.2f} M tokens/s, {us / T * 1e3:.0f} ns per token step, "
+        f"{100 * res['hbm_frac']:.1f} % of HBM for its algorithmic bytes")
+    del q, k, v, al, be, S0, d_o, dST, ws, out
     torch.cuda.empty_cache()
     return res
 

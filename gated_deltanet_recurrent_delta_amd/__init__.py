@@ -8,7 +8,7 @@ names, so `python -m gated_deltanet_recurrent_delta_amd.build` works before
 the library exists.
 """
 
-_EXPORTS = ("GdnError", "decode_step", "decode_step_qk", "drrqr_select", "gated_recurrent", "prefill",
+_EXPORTS = ("GdnError", "backward", "backward_workspace_bytes", "decode_step", "decode_step_qk", "drrqr_select", "gated_recurrent", "prefill",
             "prefill_prepare", "prefill_qk", "prefill_qk_workspace_bytes",
             "prefill_scan", "prefill_segments", "prefill_workspace_bytes",
             "status_str", "version")

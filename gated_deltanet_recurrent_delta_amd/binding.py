@@ -50,6 +50,8 @@ SIGNATURES = {
     "gdn_gated_recurrent": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _i, _i, _i, _i, _i, _i, _i, _vp]),
     "gdn_drrqr_select": (_i, [_vp, _i, _i, _i, ctypes.c_double, _i, _vp, _vp, _vp]),
+    "gdn_backward_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "gdn_backward": (_i, [_vp] * 14 + [_i] * 6 + [_vp, _sz, _vp]),
     "gdn_truncate_workspace_bytes": (_sz, [_i, _i, _i]),
     "gdn_truncate_rank": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
 }
@@ -419,6 +421,61 @@ def gated_recurrent(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                  _stream_handle(q, stream))
     _check(st, "gdn_gated_recurrent")
     return o, ST
+
+
+# ---------------------------------------------------------------------------
+# backward pass
+# ---------------------------------------------------------------------------
+
+def backward_workspace_bytes(B: int, T: int, H: int, dk: int, dv: int) -> int:
+    return int(lib.gdn_backward_workspace_bytes(B, T, H, dk, dv))
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+             alpha: torch.Tensor, beta: torch.Tensor, S0: Optional[torch.Tensor],
+             d_o: torch.Tensor, dST: Optional[torch.Tensor] = None, *,
+             want_dS0: bool = True, out: Optional[dict] = None,
+             workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Gradients of sum <d_o, o> + <dST, S_T> through prefill's recurrence
+    (see include/gdn.h): q, k [B, T, H, dk], v, d_o [B, T, H, dv] (float32
+    or bfloat16, one dtype); alpha, beta [B, T, H] float32; S0, dST
+    [B, H, dv, dk] float32 or None.  Returns a dict of float32 tensors dq,
+    dk, dv, dalpha, dbeta and dS0 (None unless want_dS0).  `out`: optional
+    dict of preallocated outputs under the same keys."""
+    _dev_tensor(q, "q", _DTYPE_CODE)
+    B, T, H, dk = q.shape
+    _dev_tensor(k, "k", (q.dtype,), q.shape)
+    _dev_tensor(v, "v", (q.dtype,))
+    if tuple(v.shape[:3]) != (B, T, H) or v.dim() != 4:
+        raise ValueError(f"v: shape {tuple(v.shape)} incompatible with q")
+    dv = v.shape[3]
+    _dev_tensor(d_o, "d_o", (q.dtype,), (B, T, H, dv))
+    _dev_tensor(alpha, "alpha", (torch.float32,), (B, T, H))
+    _dev_tensor(beta, "beta", (torch.float32,), (B, T, H))
+    if S0 is not None:
+        _dev_tensor(S0, "S0", (torch.float32,), (B, H, dv, dk))
+    if dST is not None:
+        _dev_tensor(dST, "dST", (torch.float32,), (B, H, dv, dk))
+    shapes = {"dq": (B, T, H, dk), "dk": (B, T, H, dk), "dv": (B, T, H, dv),
+              "dalpha": (B, T, H), "dbeta": (B, T, H), "dS0": (B, H, dv, dk)}
+    res = dict(out or {})
+    for name, shp in shapes.items():
+        if name == "dS0" and not want_dS0:
+            res[name] = None
+            continue
+        if res.get(name) is None:
+            res[name] = torch.empty(shp, dtype=torch.float32, device=q.device)
+        _dev_tensor(res[name], name, (torch.float32,), shp)
+    need = backward_workspace_bytes(B, T, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib.gdn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0),
+                          _ptr(d_o), _ptr(dST), _ptr(res["dq"]), _ptr(res["dk"]),
+                          _ptr(res["dv"]), _ptr(res["dalpha"]), _ptr(res["dbeta"]),
+                          _ptr(res["dS0"]), B, T, H, dk, dv, _DTYPE_CODE[q.dtype],
+                          _ptr(workspace), workspace.numel(), _stream_handle(q, stream))
+    _check(st, "gdn_backward")
+    return res
 
 
 # ---------------------------------------------------------------------------

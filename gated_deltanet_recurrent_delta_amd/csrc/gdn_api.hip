@@ -302,6 +302,43 @@ int gdn_gated_recurrent(const void* q, const void* k, const void* v,
       static_cast<hipStream_t>(stream)));
 }
 
+size_t gdn_backward_workspace_bytes(int B, int T, int H, int dk, int dv) {
+  if (check_prefill_shape(B, T, H, dk, dv, GDN_F32, GDN_F32) != GDN_OK) return 0;
+  return gdn::backward_ws_floats(B, T, H, dk, dv, nullptr) * sizeof(float);
+}
+
+int gdn_backward(const void* q, const void* k, const void* v, const float* alpha,
+                 const float* beta, const float* S0, const void* d_o, const float* dST,
+                 float* dq, float* dkey, float* dval, float* dalpha, float* dbeta,
+                 float* dS0, int B, int T, int H, int dk, int dv, int in_dtype,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_prefill_shape(B, T, H, dk, dv, in_dtype, GDN_F32);
+  if (st != GDN_OK) return st;
+  if ((long long)B * H * T * (2 * dk + 2) / 256 >= 0x7FFFFFFFLL) return GDN_EINVAL;
+  if ((S0 && !aligned(S0, 16)) || (dST && !aligned(dST, 16)) || (dS0 && !aligned(dS0, 16)))
+    return GDN_EINVAL;
+  const size_t nstate = (size_t)B * H * dv * dk;
+  auto partial = [&](const float* x) {
+    return x && dS0 && x != dS0 && (x < dS0 + nstate && dS0 < x + nstate);
+  };
+  if (partial(dST) || partial(S0)) return GDN_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) return dS0 ? to_status(gdn::launch_state_fill(dST, dS0, nstate, s)) : GDN_OK;
+  if (!q || !k || !v || !alpha || !beta || !d_o || !dq || !dkey || !dval || !dalpha || !dbeta)
+    return GDN_EINVAL;
+  const uintptr_t ev = in_dtype == GDN_BF16 ? 2 : 4;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, ev) || !aligned(d_o, ev) ||
+      !aligned(alpha, 4) || !aligned(beta, 4) || !aligned(dq, 4) || !aligned(dkey, 4) ||
+      !aligned(dval, 4) || !aligned(dalpha, 4) || !aligned(dbeta, 4))
+    return GDN_EINVAL;
+  if (!workspace || !aligned(workspace, 16)) return GDN_EWORKSPACE;
+  if (workspace_bytes < gdn::backward_ws_floats(B, T, H, dk, dv, nullptr) * sizeof(float))
+    return GDN_EWORKSPACE;
+  return to_status(gdn::launch_backward(q, k, v, alpha, beta, S0, d_o, dST, dq, dkey, dval,
+                                        dalpha, dbeta, dS0, B, T, H, dk, dv, in_dtype,
+                                        static_cast<float*>(workspace), s));
+}
+
 int gdn_drrqr_select(const double* M, int rows, int n, int k, double f,
                      int max_swaps, int* selected, int* swaps, double* rho_max) {
   if (!M || !selected) return GDN_EINVAL;

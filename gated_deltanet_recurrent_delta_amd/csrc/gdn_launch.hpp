@@ -144,4 +144,13 @@ hipError_t launch_gated_recurrent(const void* q, const void* k, const void* v,
                                   void* o, int B, int T, int H, int dk, int dv,
                                   int in_dtype, int out_dtype, hipStream_t stream);
 
+// Backward pass of the gated delta rule in recurrent form: workspace sizing
+// (floats; ckpt_floats gets the checkpoint part) and the launch (two kernels).
+size_t backward_ws_floats(int B, int T, int H, int dk, int dv, size_t* ckpt_floats);
+hipError_t launch_backward(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, const float* S0, const void* dO,
+                           const float* dST, float* dq, float* dk, float* dv_out,
+                           float* dalpha, float* dbeta, float* dS0, int B, int T, int H,
+                           int dkk, int dv, int in_dtype, float* ws, hipStream_t stream);
+
 }  // namespace gdn

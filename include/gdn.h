@@ -242,6 +242,48 @@ int gdn_gated_recurrent(const void* q, const void* k, const void* v,
                         void* stream);
 
 /* ------------------------------------------------------------------------
+ * Backward pass of gdn_prefill's recurrence (recurrent form).
+ *
+ * The pages train these layers ("Linear Attention Architectures" reading
+ * notes, the training set-ups of its experiments; "On State Reduction in
+ * Linear Attention", the recovery fine-tuning of pruned layers) but print
+ * no backward pass: these are the exact gradients of the forward step of
+ * gdn_prefill (S~ = alpha S_{t-1}, S_t = S~ + beta (v - S~ k) k^T,
+ * o_t = S_t q_t) for the loss L = sum_t <do_t, o_t> + <dST, S_T>.
+ *   q, k          [B, T, H, dk] in_dtype, 16-byte aligned.
+ *   v, d_o        [B, T, H, dv] in_dtype (d_o: the gradient of o).
+ *   alpha, beta   [B, T, H] float32.
+ *   S0            [B, H, dv, dk] float32 or NULL (zero initial state).
+ *   dST           [B, H, dv, dk] float32 or NULL (no gradient on S_T).
+ *   dq, dk        [B, T, H, dk] float32, 16-byte aligned (written).
+ *   dv            [B, T, H, dv] float32 (written).
+ *   dalpha, dbeta [B, T, H] float32 (written).
+ *   dS0           [B, H, dv, dk] float32 or NULL (not wanted); it may alias
+ *                 dST or S0 exactly (each state row is read before it is
+ *                 written, by the same wave), not partly.
+ *   workspace     device memory of at least gdn_backward_workspace_bytes()
+ *                 bytes, 16-byte aligned, owned by the caller (state
+ *                 checkpoints every 8 tokens and per-workgroup partial
+ *                 sums); NULL allowed when that size is 0 (T == 0).
+ * All pointers are device pointers; the call is asynchronous on `stream`.
+ * Each wave reruns its state rows forward, storing a checkpoint every 8
+ * tokens, then steps back through each 8-token block with the block's
+ * states in registers.  Sums over the dv rows of a head (dq, dk, dalpha,
+ * dbeta) are taken in a fixed order, so results are reproducible.
+ * Errors: GDN_ESHAPE for dk or dv outside {64, 128} or an unknown dtype;
+ * GDN_EINVAL for a NULL or misaligned required pointer, bad sizes or a
+ * partial overlap of dS0; GDN_EWORKSPACE for a missing or short workspace;
+ * GDN_EHIP if a launch fails.  T == 0 writes dS0 = dST (or zeros).
+ */
+size_t gdn_backward_workspace_bytes(int B, int T, int H, int dk, int dv);
+int gdn_backward(const void* q, const void* k, const void* v,
+                 const float* alpha, const float* beta, const float* S0,
+                 const void* d_o, const float* dST, float* dq, float* dk,
+                 float* dv_, float* dalpha, float* dbeta, float* dS0, int B,
+                 int T, int H, int dk_, int dv, int in_dtype, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * DRRQR channel selection (calibration time, HOST memory and host code).
  *
  * "On State Reduction in Linear Attention" (reading notes), Sec. 3.4 with

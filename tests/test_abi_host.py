@@ -315,3 +315,56 @@ def gated(**kw):
 ])
 def test_gated_argument_errors(kw, status):
     assert gated(**kw) == status
+
+
+# --- backward pass (gdn_backward) -------------------------------------------
+
+def test_backward_workspace_bytes():
+    # checkpoints every 8 tokens ([B H, ceil(T/8), dv, dk], rounded up to 64
+    # floats) + per-workgroup partials ([B H, T, dv / (16 or 32), 2 dk + 2])
+    f = bd.lib.gdn_backward_workspace_bytes
+    assert f(1, 8, 1, 128, 128) == 4 * (128 * 128 + 8 * 8 * 258)
+    ck = 2 * 3 * 2 * 64 * 128                  # B=2, H=3, T=9 -> 2 checkpoints, dv=64, dk=128
+    assert f(2, 9, 3, 128, 64) == 4 * (ck + 6 * 9 * 4 * 258)
+    ck = 2 * 3 * 64 * 64                       # dk=64: 32 rows per workgroup
+    assert f(1, 17, 2, 64, 64) == 4 * (ck + 2 * 17 * 2 * 130)
+    assert f(1, 0, 2, 64, 64) == 0
+    assert f(1, 8, 1, 96, 128) == 0 and f(0, 8, 1, 128, 128) == 0
+
+
+def backward(**kw):
+    a = dict(q=P, k=P, v=P, alpha=P, beta=P, S0=NULL, d_o=P, dST=NULL, dq=P, dk_=P, dv_=P,
+             dalpha=P, dbeta=P, dS0=P, B=1, T=10, H=2, dk=128, dv=128, in_dtype=1,
+             ws=P, ws_bytes=1 << 40, stream=NULL)
+    a.update(kw)
+    return bd.lib.gdn_backward(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S0"],
+                               a["d_o"], a["dST"], a["dq"], a["dk_"], a["dv_"], a["dalpha"],
+                               a["dbeta"], a["dS0"], a["B"], a["T"], a["H"], a["dk"], a["dv"],
+                               a["in_dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), bd.GDN_EINVAL),
+    (dict(T=-1), bd.GDN_EINVAL),
+    (dict(dk=96), bd.GDN_ESHAPE),
+    (dict(dv=32), bd.GDN_ESHAPE),
+    (dict(in_dtype=2), bd.GDN_ESHAPE),
+    (dict(q=NULL), bd.GDN_EINVAL),
+    (dict(d_o=NULL), bd.GDN_EINVAL),
+    (dict(dalpha=NULL), bd.GDN_EINVAL),
+    (dict(dk_=NULL), bd.GDN_EINVAL),
+    (dict(k=MIS), bd.GDN_EINVAL),
+    (dict(v=ctypes.c_void_p(0x10001)), bd.GDN_EINVAL),
+    (dict(S0=MIS), bd.GDN_EINVAL),
+    (dict(dS0=MIS), bd.GDN_EINVAL),
+    (dict(dST=ctypes.c_void_p(0x10000), dS0=ctypes.c_void_p(0x10100)), bd.GDN_EINVAL),
+    (dict(ws=NULL), bd.GDN_EWORKSPACE),
+    (dict(ws=MIS), bd.GDN_EWORKSPACE),
+    (dict(ws_bytes=1024), bd.GDN_EWORKSPACE),
+])
+def test_backward_argument_errors(kw, status):
+    assert backward(**kw) == status
+
+
+def test_backward_empty_sequence_without_dS0_is_a_noop():
+    assert backward(T=0, dS0=NULL, q=NULL, ws=NULL, ws_bytes=0) == bd.GDN_OK

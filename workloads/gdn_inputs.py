@@ -276,6 +276,27 @@ def gate_vectors(B: int, T: int, H: int, dk: int, dv: int, seed: int,
     return alpha, b, w
 
 
+def cotangents(B: int, T: int, H: int, dk: int, dv: int, seed: int,
+               dtype: str = "f32", rows: Optional[Sequence[int]] = None):
+    """Gradients flowing into a layer's outputs, for the backward pass:
+    d_o ~ N(0, 1) [B, T, H, dv] (rounded to bf16 when dtype is "bf16", the
+    storage dtype of o) and dST ~ N(0, 1) [B, H, dv, dk] float32.  Batch row
+    b from its own stream PCG64(seed).jumped(b), like generic()."""
+    rows = list(range(B)) if rows is None else [int(r) for r in rows]
+    d_o = np.empty((len(rows), T, H, dv), np.float32)
+    dST = np.empty((len(rows), H, dv, dk), np.float32)
+    for i, b in enumerate(rows):
+        assert 0 <= b < B
+        rng = np.random.Generator(np.random.PCG64(seed).jumped(b))
+        d_o[i] = rng.standard_normal((T, H, dv), dtype=np.float32)
+        dST[i] = rng.standard_normal((H, dv, dk), dtype=np.float32)
+    if dtype == "bf16":
+        d_o = round_bf16(d_o)
+    elif dtype != "f32":
+        raise ValueError(dtype)
+    return np.ascontiguousarray(d_o, np.float32), dST
+
+
 def pruning_subsets(config: int, H: int = 16, dk: int = 128,
                     dk_keep: int = 64) -> np.ndarray:
     """The fixed per-head channel subsets P_I of a channel-pruned layer
