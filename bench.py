@@ -196,6 +196,11 @@ COUNTER_LEGS = {
     "gated_decode_B64_dk128": [("gated_recurrent_kernel", 128, None, 64 * 16 * 8 * 64)],
     "gated_decode_B64_dk64": [("gated_recurrent_kernel", 64, None, 64 * 16 * 8 * 64)],
     "gated_prefill_B8_T4096_dk64": [("gated_recurrent_kernel", 64, None, 8 * 16 * 8 * 64)],
+    # backward pass at B=8, T=4096, H=16, dk=dv=128: 4 workgroups of 256
+    # threads per head, then one reduction thread per (head, token, partial
+    # element), 2 dk + 2 elements
+    "backward_B8_T4096_dk128": [("backward_kernel", 128, None, 8 * 16 * 4 * 256),
+                                ("backward_reduce_kernel", 128, None, 8 * 16 * 4096 * 258)],
 }
 
 
@@ -211,6 +216,8 @@ def _legs_in_run(a):
         if 64 in a.decode_batch:
             legs += ["gated_decode_B64_dk128", "gated_decode_B64_dk64"]
         legs.append("gated_prefill_B8_T4096_dk64")
+    if not a.skip_backward:
+        legs.append("backward_B8_T4096_dk128")
     if not a.skip_qk:
         legs.append("batched_qk_dk64")
         if not a.qk_gather_only:
@@ -1025,6 +1032,11 @@ def bench_backward(torch, gdn, dev, stream, up, B=8, T=4096, H=16, dk=128, dv=12
            "hbm_frac": nbytes / (us * 1e-6) / HBM_PEAK,
            "workspace_bytes": ws.numel(),
            "bound": "latency of the per-token dependency chain (recurrent form)"}
+    # HBM bytes per call from the committed counter runs (checkpoints and
+    # partial sums included), and the rate they are moved at
+    tr = measured_traffic("backward_B8_T4096_dk128")
+    res["traffic"] = tr
+    res["traffic_GBps"] = None if tr is None else tr / (us * 1e-6) / 1e9
     log(f"backward B={B} T={T} H={H} dk={dk} (recurrent form): {us:.0f} us, "
         f"{res['tokens_per_s'] / 1e6:.2f} M tokens/s, {us / T * 1e3:.0f} ns per token step, "
         f"{100 * res['hbm_frac']:.1f} % of HBM for its algorithmic bytes")

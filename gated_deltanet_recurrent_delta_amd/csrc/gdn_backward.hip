@@ -57,7 +57,11 @@ __device__ __forceinline__ float xsum_rows(float x) {   // over lanes l, l^16, l
 
 }  // namespace
 
-int backward_ng(int dk) { return dk == 128 ? 1 : 2; }
+// 8 rows per wave at either key width: at dk = 128 that is 254 registers and
+// two waves per SIMD, and the workgroups of a B=8, H=16 batch (512) are all
+// resident at once (4 rows per wave: 157 registers, 1024 workgroups in two
+// rounds, 21.1 ms against 15.0 ms at B=8, T=4096, H=16).
+int backward_ng(int) { return 2; }
 
 // Workgroups per head and the width of one partial (dq, dk, dalpha, dbeta).
 int backward_wgs(int dk, int dv) { return dv / (4 * backward_ng(dk) * kBwdWaves); }
@@ -99,23 +103,36 @@ __global__ __launch_bounds__(64 * kBwdWaves) void backward_kernel(
   auto crow = [&](int c, int g) {
     return (((size_t)head * nc + c) * dv + row0 + 4 * g) * DK;
   };
-  // one forward step of the NG rows held in s (token index ti)
-  auto fwd = [&](const floatx4 (&s)[NG][F], floatx4 (&out)[NG][F], size_t ti) {
-    const float a = alpha[ti], be = beta[ti];
-    float4 kk[F];
+  // Token inputs.  Every load is unconditional, from a clamped token index,
+  // and a token past the end gets the identity gates (alpha 1, beta 0, no
+  // output gradient): the loops over a block then have no branch, and the
+  // compiler is free to issue a block's loads ahead of its dependent chain.
+  struct Tok {
+    float4 k[F];
+    float a, be, v[NG];
+  };
+  auto load_tok = [&](Tok& x, int t) {
+    const size_t ti = tok(min(t, T - 1));
+    const bool ok = t < T;
 #pragma unroll
-    for (int f = 0; f < F; ++f) kk[f] = load4(k + ti * DK + 64 * f + 4 * sub);
+    for (int f = 0; f < F; ++f) x.k[f] = load4(k + ti * DK + 64 * f + 4 * sub);
+    x.a = ok ? alpha[ti] : 1.f;
+    x.be = ok ? beta[ti] : 0.f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) x.v[g] = load1(v + ti * dv + row0 + 4 * g);
+  };
+  // one forward step of the NG rows held in s
+  auto fwd = [&](const floatx4 (&s)[NG][F], floatx4 (&out)[NG][F], const Tok& x) {
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      const float vv = load1(v + ti * dv + row0 + 4 * g);
       floatx4 sa[F];
 #pragma unroll
-      for (int f = 0; f < F; ++f) sa[f] = s[g][f] * a;
-      const float u = be * (vv - sum16(dot4<F>(sa, kk)));
+      for (int f = 0; f < F; ++f) sa[f] = s[g][f] * x.a;
+      const float u = x.be * (x.v[g] - sum16(dot4<F>(sa, x.k)));
 #pragma unroll
       for (int f = 0; f < F; ++f)
-        out[g][f] = floatx4{sa[f][0] + u * kk[f].x, sa[f][1] + u * kk[f].y,
-                            sa[f][2] + u * kk[f].z, sa[f][3] + u * kk[f].w};
+        out[g][f] = floatx4{sa[f][0] + u * x.k[f].x, sa[f][1] + u * x.k[f].y,
+                            sa[f][2] + u * x.k[f].z, sa[f][3] + u * x.k[f].w};
     }
   };
 
@@ -128,15 +145,18 @@ __global__ __launch_bounds__(64 * kBwdWaves) void backward_kernel(
       for (int f = 0; f < F; ++f)
         s[g][f] = S0 ? *reinterpret_cast<const floatx4*>(S0 + srow(g) + 64 * f + 4 * sub)
                      : floatx4{0.f, 0.f, 0.f, 0.f};
-    for (int t = 0; t < T; ++t) {
-      if (t % L == 0) {
+    for (int c = 0; c < nc; ++c) {
 #pragma unroll
-        for (int g = 0; g < NG; ++g)
+      for (int g = 0; g < NG; ++g)
 #pragma unroll
-          for (int f = 0; f < F; ++f)
-            *reinterpret_cast<floatx4*>(ckpt + crow(t / L, g) + 64 * f + 4 * sub) = s[g][f];
+        for (int f = 0; f < F; ++f)
+          *reinterpret_cast<floatx4*>(ckpt + crow(c, g) + 64 * f + 4 * sub) = s[g][f];
+#pragma unroll
+      for (int i = 0; i < L; ++i) {
+        Tok x;
+        load_tok(x, c * L + i);
+        fwd(s, s, x);
       }
-      fwd(s, s, tok(t));
     }
   }
 
@@ -157,42 +177,43 @@ __global__ __launch_bounds__(64 * kBwdWaves) void backward_kernel(
       for (int f = 0; f < F; ++f)
         st[0][g][f] = *reinterpret_cast<const floatx4*>(ckpt + crow(c, g) + 64 * f + 4 * sub);
 #pragma unroll
-    for (int i = 0; i + 1 < L; ++i)
-      if (i + 1 < n) fwd(st[i], st[i + 1], tok(t0 + i));
+    for (int i = 0; i + 1 < L; ++i) {
+      Tok x;
+      load_tok(x, t0 + i);
+      fwd(st[i], st[i + 1], x);
+    }
 
 #pragma unroll
     for (int i = L - 1; i >= 0; --i) {
-      if (i >= n) continue;
-      const size_t ti = tok(t0 + i);
-      const float a = alpha[ti], be = beta[ti];
-      float4 kk[F], qq[F];
+      const int t = t0 + i;
+      const bool ok = i < n;
+      const size_t ti = tok(min(t, T - 1));
+      Tok x;
+      load_tok(x, t);
+      float4 qq[F];
 #pragma unroll
-      for (int f = 0; f < F; ++f) {
-        kk[f] = load4(k + ti * DK + 64 * f + 4 * sub);
-        qq[f] = load4(q + ti * DK + 64 * f + 4 * sub);
-      }
+      for (int f = 0; f < F; ++f) qq[f] = load4(q + ti * DK + 64 * f + 4 * sub);
       floatx4 dq[F], dk[F];
 #pragma unroll
       for (int f = 0; f < F; ++f) dq[f] = dk[f] = floatx4{0.f, 0.f, 0.f, 0.f};
       float da = 0.f, db = 0.f;
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        const float vv = load1(v + ti * dv + row0 + 4 * g);
-        const float dd = load1(dO + ti * dv + row0 + 4 * g);
+        const float dd = ok ? load1(dO + ti * dv + row0 + 4 * g) : 0.f;
         floatx4 sa[F], Gt[F];
 #pragma unroll
         for (int f = 0; f < F; ++f) {
-          sa[f] = st[i][g][f] * a;
+          sa[f] = st[i][g][f] * x.a;
           Gt[f] = floatx4{G[g][f][0] + dd * qq[f].x, G[g][f][1] + dd * qq[f].y,
                           G[g][f][2] + dd * qq[f].z, G[g][f][3] + dd * qq[f].w};
         }
-        const float w = vv - sum16(dot4<F>(sa, kk));
-        const float u = be * w;
-        const float du = sum16(dot4<F>(Gt, kk));
-        const float bdu = be * du;
+        const float w = x.v[g] - sum16(dot4<F>(sa, x.k));
+        const float u = x.be * w;
+        const float du = sum16(dot4<F>(Gt, x.k));
+        const float bdu = x.be * du;
 #pragma unroll
         for (int f = 0; f < F; ++f) {
-          const float kf[4] = {kk[f].x, kk[f].y, kk[f].z, kk[f].w};
+          const float kf[4] = {x.k[f].x, x.k[f].y, x.k[f].z, x.k[f].w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             dq[f][e] += dd * (sa[f][e] + u * kf[e]);
@@ -207,11 +228,12 @@ __global__ __launch_bounds__(64 * kBwdWaves) void backward_kernel(
           for (int e = 0; e < 4; ++e) pa += Gt[f][e] * st[i][g][f][e];
         da += sum16(pa);
         db += du * w;
-        if (sub == 0) dv_out[ti * dv + row0 + 4 * g] = bdu;
+        if (sub == 0 && ok) dv_out[ti * dv + row0 + 4 * g] = bdu;
 #pragma unroll
-        for (int f = 0; f < F; ++f) G[g][f] = Gt[f] * a;
+        for (int f = 0; f < F; ++f) G[g][f] = Gt[f] * x.a;
       }
       // over the wave's 4 row groups, then into the block's LDS partials
+      // (rows i >= n are written but never read)
 #pragma unroll
       for (int f = 0; f < F; ++f)
 #pragma unroll
@@ -293,8 +315,8 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const fl
                      dST, dv_out, dS0, ckpt, part, H, T, dv)
   const bool ib = in_dtype == 1;
   if (dkk == 128) {
-    if (ib) GDN_BWD(128, 1, bf16);
-    else GDN_BWD(128, 1, float);
+    if (ib) GDN_BWD(128, 2, bf16);
+    else GDN_BWD(128, 2, float);
   } else {
     if (ib) GDN_BWD(64, 2, bf16);
     else GDN_BWD(64, 2, float);

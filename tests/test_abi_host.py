@@ -321,12 +321,12 @@ def test_gated_argument_errors(kw, status):
 
 def test_backward_workspace_bytes():
     # checkpoints every 8 tokens ([B H, ceil(T/8), dv, dk], rounded up to 64
-    # floats) + per-workgroup partials ([B H, T, dv / (16 or 32), 2 dk + 2])
+    # floats) + per-workgroup partials ([B H, T, dv / 32, 2 dk + 2])
     f = bd.lib.gdn_backward_workspace_bytes
-    assert f(1, 8, 1, 128, 128) == 4 * (128 * 128 + 8 * 8 * 258)
+    assert f(1, 8, 1, 128, 128) == 4 * (128 * 128 + 8 * 4 * 258)
     ck = 2 * 3 * 2 * 64 * 128                  # B=2, H=3, T=9 -> 2 checkpoints, dv=64, dk=128
-    assert f(2, 9, 3, 128, 64) == 4 * (ck + 6 * 9 * 4 * 258)
-    ck = 2 * 3 * 64 * 64                       # dk=64: 32 rows per workgroup
+    assert f(2, 9, 3, 128, 64) == 4 * (ck + 6 * 9 * 2 * 258)
+    ck = 2 * 3 * 64 * 64
     assert f(1, 17, 2, 64, 64) == 4 * (ck + 2 * 17 * 2 * 130)
     assert f(1, 0, 2, 64, 64) == 0
     assert f(1, 8, 1, 96, 128) == 0 and f(0, 8, 1, 128, 128) == 0

@@ -36,13 +36,17 @@ def write_csv(path, counter, rows):
 def args(**kw):
     a = bench.main.__globals__["argparse"].Namespace(
         skip_prefill=True, skip_decode=True, skip_batched=True, skip_qk=True,
-        skip_gated=True, qk_gather_only=False, decode_batch=[64, 1])
+        skip_gated=True, skip_backward=True, qk_gather_only=False, decode_batch=[64, 1])
     for k, v in kw.items():
         setattr(a, k, v)
     return a
 
 
 def test_kernel_keys():
+    assert bench._kernel_key("_ZN3gdn15backward_kernelILi128ELi2EDF16bEEvPKT1_S3_S3_PKfS5_") == (
+        "backward_kernel", 128, 2)
+    assert bench._kernel_key("void gdn::backward_reduce_kernel<128>(float const*, float*)") == (
+        "backward_reduce_kernel", 128, None)
     assert bench._kernel_key(PREP64) == ("prepare_kernel", 64, 0)
     assert bench._kernel_key(PREP64G) == ("prepare_kernel", 64, None)
     assert bench._kernel_key(DEC64) == ("decode_kernel", 64, 0)
