@@ -116,8 +116,11 @@ __global__ __launch_bounds__(64 * kBwdWaves) void backward_kernel(
     const bool ok = t < T;
 #pragma unroll
     for (int f = 0; f < F; ++f) x.k[f] = load4(k + ti * DK + 64 * f + 4 * sub);
-    x.a = ok ? alpha[ti] : 1.f;
-    x.be = ok ? beta[ti] : 0.f;
+    // loaded unconditionally, then selected: a load under the condition
+    // becomes a branch, which ends the scheduling region at every token
+    const float a = alpha[ti], be = beta[ti];
+    x.a = ok ? a : 1.f;
+    x.be = ok ? be : 0.f;
 #pragma unroll
     for (int g = 0; g < NG; ++g) x.v[g] = load1(v + ti * dv + row0 + 4 * g);
   };
@@ -171,6 +174,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void backward_kernel(
   for (int c = nc - 1; c >= 0; --c) {
     const int t0 = c * L, n = min(L, T - t0);           // uniform in the workgroup
     floatx4 st[L][NG][F];                               // S before token t0 + i
+    float dvb[L][NG];                                   // dv of the block, stored after it
 #pragma unroll
     for (int g = 0; g < NG; ++g)
 #pragma unroll
@@ -199,7 +203,8 @@ __global__ __launch_bounds__(64 * kBwdWaves) void backward_kernel(
       float da = 0.f, db = 0.f;
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        const float dd = ok ? load1(dO + ti * dv + row0 + 4 * g) : 0.f;
+        const float ddl = load1(dO + ti * dv + row0 + 4 * g);
+        const float dd = ok ? ddl : 0.f;
         floatx4 sa[F], Gt[F];
 #pragma unroll
         for (int f = 0; f < F; ++f) {
@@ -228,12 +233,15 @@ __global__ __launch_bounds__(64 * kBwdWaves) void backward_kernel(
           for (int e = 0; e < 4; ++e) pa += Gt[f][e] * st[i][g][f][e];
         da += sum16(pa);
         db += du * w;
-        if (sub == 0 && ok) dv_out[ti * dv + row0 + 4 * g] = bdu;
+        dvb[i][g] = bdu;
 #pragma unroll
         for (int f = 0; f < F; ++f) G[g][f] = Gt[f] * x.a;
       }
       // over the wave's 4 row groups, then into the block's LDS partials
-      // (rows i >= n are written but never read)
+      // (rows i >= n are written but never read).  After the sums the four
+      // lanes of a column hold the same value, and every lane stores it: the
+      // same value to the same address, with no divergent branch to end the
+      // scheduling region.
 #pragma unroll
       for (int f = 0; f < F; ++f)
 #pragma unroll
@@ -254,6 +262,13 @@ __global__ __launch_bounds__(64 * kBwdWaves) void backward_kernel(
         red[i][wv][2 * DK] = da;
         red[i][wv][2 * DK + 1] = db;
       }
+    }
+    if (sub == 0) {
+#pragma unroll
+      for (int i = 0; i < L; ++i)
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+          if (i < n) dv_out[tok(t0 + i) * dv + row0 + 4 * g] = dvb[i][g];
     }
     __syncthreads();
     for (int e = threadIdx.x; e < n * PW; e += 64 * kBwdWaves) {
