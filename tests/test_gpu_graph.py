@@ -207,3 +207,47 @@ def test_new_entry_points_graph_replays_match_eager(kind):
         torch.cuda.synchronize()
         assert torch.equal(outs, o_ref), f"replay {rep}: o differs"
         assert torch.equal(S, S_ref), f"replay {rep}: S differs"
+
+
+@pytest.mark.parametrize("dk", [128, 64])
+def test_backward_graph_replays_match_eager(dk):
+    """gdn_backward captured once (T = 37: four checkpoint blocks and a
+    ragged one) and replayed with its outputs NaN, its workspace filled with
+    0xFF bytes (NaN floats) and dS0 written over dS_T; every replay equals
+    the eager call bitwise."""
+    dev = torch.device("cuda")
+    B, T, H, dv = 2, 37, 4, 128
+    x = gi.generic(B, T, H, dk, dv, 8400 + dk, "bf16", S0_scale=0.3)
+    d_o, dST = gi.cotangents(B, T, H, dk, dv, 8401 + dk, "bf16")
+    d = to_dev(x)
+    d_o = torch.from_numpy(d_o).to(dev).to(torch.bfloat16).contiguous()
+    dST0 = torch.from_numpy(dST).to(dev)
+    g_st = dST0.clone()
+    ws = torch.empty(gdn.backward_workspace_bytes(B, T, H, dk, dv), dtype=torch.uint8, device=dev)
+    names = ("dq", "dk", "dv", "dalpha", "dbeta")
+    out = {nm: torch.empty(sh, dtype=torch.float32, device=dev) for nm, sh in
+           zip(names, [(B, T, H, dk), (B, T, H, dk), (B, T, H, dv), (B, T, H), (B, T, H)])}
+    out["dS0"] = g_st
+
+    def run():
+        gdn.backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d_o, g_st,
+                     out=out, workspace=ws)
+    run()
+    torch.cuda.synchronize()
+    ref = {nm: t.clone() for nm, t in out.items()}
+    assert all(torch.isfinite(t).all() for t in ref.values())
+    g = torch.cuda.CUDAGraph()
+    g_st.copy_(dST0)
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(REPLAYS):
+        g_st.copy_(dST0)
+        for nm in names:
+            out[nm].fill_(float("nan"))
+        ws.fill_(255)
+        _other_eager_work(dev)
+        g.replay()
+        torch.cuda.synchronize()
+        for nm, t in out.items():
+            assert torch.equal(t, ref[nm]), f"replay {rep}: {nm} differs"
