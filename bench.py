@@ -201,6 +201,8 @@ COUNTER_LEGS = {
     # element), 2 dk + 2 elements
     "backward_B8_T4096_dk128": [("backward_kernel", 128, None, 8 * 16 * 4 * 256),
                                 ("backward_reduce_kernel", 128, None, 8 * 16 * 4096 * 258)],
+    "backward_B8_T4096_dk64": [("backward_kernel", 64, None, 8 * 16 * 4 * 256),
+                               ("backward_reduce_kernel", 64, None, 8 * 16 * 4096 * 130)],
 }
 
 
@@ -217,7 +219,7 @@ def _legs_in_run(a):
             legs += ["gated_decode_B64_dk128", "gated_decode_B64_dk64"]
         legs.append("gated_prefill_B8_T4096_dk64")
     if not a.skip_backward:
-        legs.append("backward_B8_T4096_dk128")
+        legs += ["backward_B8_T4096_dk128", "backward_B8_T4096_dk64"]
     if not a.skip_qk:
         legs.append("batched_qk_dk64")
         if not a.qk_gather_only:
@@ -642,7 +644,10 @@ def main(argv=None):
     # ---------------- backward pass (recurrent form) ----------------
     backward = {}
     if not a.skip_backward:
-        backward = bench_backward(torch, gdn, dev, stream, up)
+        for dkb in (128, 64):
+            backward[f"B8_T4096_dk{dkb}"] = bench_backward(torch, gdn, dev, stream, up, dk=dkb)
+        backward["time_dk64_vs_dk128"] = (backward["B8_T4096_dk64"]["us_per_call"] /
+                                          backward["B8_T4096_dk128"]["us_per_call"])
 
     # ---------------- segment-truncated prefill, r in {1, 4, 12, 32} ----------
     truncated = {}
@@ -993,7 +998,8 @@ def bench_gated_prefill(torch, gdn, dev, stream, up, B=8, T=4096, H=16, dk=64, d
 def bench_backward(torch, gdn, dev, stream, up, B=8, T=4096, H=16, dk=128, dv=128,
                    calls=3):
     """The backward pass (gradients of q, k, v, alpha, beta and S_0) at the
-    batched prefill's shape, bf16 inputs and d_o, fp32 gradients, in
+    batched prefill's shape (d_k = 128, or the pruned 64), bf16 inputs and
+    d_o, fp32 gradients, in
     recurrent form: bound by the per-token dependency chain, run three
     times (forward to the checkpoints, forward again inside each block,
     backward).  Reported as time, tokens/s and the HBM rate of its
@@ -1034,7 +1040,7 @@ def bench_backward(torch, gdn, dev, stream, up, B=8, T=4096, H=16, dk=128, dv=12
            "bound": "latency of the per-token dependency chain (recurrent form)"}
     # HBM bytes per call from the committed counter runs (checkpoints and
     # partial sums included), and the rate they are moved at
-    tr = measured_traffic("backward_B8_T4096_dk128")
+    tr = measured_traffic(f"backward_B8_T4096_dk{dk}")
     res["traffic"] = tr
     res["traffic_GBps"] = None if tr is None else tr / (us * 1e-6) / 1e9
     log(f"backward B={B} T={T} H={H} dk={dk} (recurrent form): {us:.0f} us, "
