@@ -109,21 +109,23 @@ def test_backward_is_reproducible():
         assert torch.equal(g1[name], g2[name]), name
 
 
-def test_backward_batched_shape_sampled_heads():
-    """B=8, T=4096, H=16, dk=dv=128, bf16 inputs (the batched prefill
-    shape), all heads on the GPU; the oracle on two sampled (b, h)."""
-    B, T, H, dk, dv = 8, 4096, 16, 128, 128
-    heads = [(2, 5), (7, 15)]
+@pytest.mark.parametrize("dk", [128, 64])
+def test_backward_batched_shape_sampled_heads(dk):
+    """B=8, T=4096, H=16, dv=128, dk=128 or the pruned 64, bf16 inputs (the
+    batched prefill shape, in the benchmark's launch configuration), all
+    heads on the GPU; the oracle on two sampled (b, h)."""
+    B, T, H, dv = 8, 4096, 16, 128
+    heads = [(2, 5), (7, 15)] if dk == 128 else [(0, 0), (5, 9)]
     rows = sorted({b for b, _ in heads})
-    x = gi.generic(B, T, H, dk, dv, 7700, "bf16", S0_scale=0.3)
-    d_o, dST = gi.cotangents(B, T, H, dk, dv, 7701, "bf16")
-    print(f"  case B=8 T=4096: workspace {gdn.backward_workspace_bytes(B, T, H, dk, dv) / 2**30:.2f} GiB",
+    x = gi.generic(B, T, H, dk, dv, 7700 + dk, "bf16", S0_scale=0.3)
+    d_o, dST = gi.cotangents(B, T, H, dk, dv, 7701 + dk, "bf16")
+    print(f"  case B=8 T=4096 dk={dk}: workspace {gdn.backward_workspace_bytes(B, T, H, dk, dv) / 2**30:.2f} GiB",
           flush=True)
     g = run(x, d_o, dST)
-    xs = gi.generic(B, T, H, dk, dv, 7700, "bf16", S0_scale=0.3, rows=rows)
-    do_s, dST_s = gi.cotangents(B, T, H, dk, dv, 7701, "bf16", rows=rows)
+    xs = gi.generic(B, T, H, dk, dv, 7700 + dk, "bf16", S0_scale=0.3, rows=rows)
+    do_s, dST_s = gi.cotangents(B, T, H, dk, dv, 7701 + dk, "bf16", rows=rows)
     remap = {b: i for i, b in enumerate(rows)}
     local = [(remap[b], h) for b, h in heads]
     ref = orc.gdn_backward(xs.q, xs.k, xs.v, xs.alpha, xs.beta, xs.S0, do_s, dST_s, heads=local)
     gs = {n: (None if g[n] is None else g[n][rows]) for n in NAMES}
-    compare("B=8 T=4096", gs, ref, local)
+    compare(f"B=8 T=4096 dk={dk}", gs, ref, local)
