@@ -237,27 +237,48 @@ __global__ __launch_bounds__(64 * kBwdWaves) void backward_kernel(
 #pragma unroll
         for (int f = 0; f < F; ++f) G[g][f] = Gt[f] * x.a;
       }
-      // over the wave's 4 row groups, then into the block's LDS partials
-      // (rows i >= n are written but never read).  After the sums the four
-      // lanes of a column hold the same value, and every lane stores it: the
-      // same value to the same address, with no divergent branch to end the
-      // scheduling region.
+      // Over the wave's 4 row groups (lanes l, l^16, l^32, l^48 hold the
+      // same columns), into the block's LDS partials (rows i >= n are
+      // written but never read).  A reduce-scatter: at each of the two
+      // exchange steps a lane sends the half of its values it gives away and
+      // adds the partner's copy of the half it keeps (12 shuffles for the
+      // 8 F dq and dk values instead of 16 F), and ends up owning one
+      // quarter of the sums, which it stores: lane (h32, h16) holds dq
+      // (h32 = 0) or dk (h32 = 1) at column 64 h16 + 4 sub .. + 3
+      // (d_k = 128) or 4 sub + 2 h16 .. + 1 (d_k = 64).
+      {
+        constexpr int NV = 8 * F;
+        float vals[NV];
 #pragma unroll
-      for (int f = 0; f < F; ++f)
+        for (int f = 0; f < F; ++f)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          dq[f][e] = xsum_rows(dq[f][e]);
-          dk[f][e] = xsum_rows(dk[f][e]);
+          for (int e = 0; e < 4; ++e) {
+            vals[4 * f + e] = dq[f][e];
+            vals[4 * F + 4 * f + e] = dk[f][e];
+          }
+        const bool h32 = (lane & 32) != 0, h16 = (lane & 16) != 0;
+        float v1[NV / 2], v2[NV / 4];
+#pragma unroll
+        for (int j = 0; j < NV / 2; ++j) {
+          const float keep = h32 ? vals[NV / 2 + j] : vals[j];
+          const float give = h32 ? vals[j] : vals[NV / 2 + j];
+          v1[j] = keep + __shfl_xor(give, 32, 64);
         }
-      da = xsum_rows(da);
-      db = xsum_rows(db);
-      if (lane < 16) {
 #pragma unroll
-        for (int f = 0; f < F; ++f) {
-          *reinterpret_cast<floatx4*>(&red[i][wv][64 * f + 4 * sub]) = dq[f];
-          *reinterpret_cast<floatx4*>(&red[i][wv][DK + 64 * f + 4 * sub]) = dk[f];
+        for (int j = 0; j < NV / 4; ++j) {
+          const float keep = h16 ? v1[NV / 4 + j] : v1[j];
+          const float give = h16 ? v1[j] : v1[NV / 4 + j];
+          v2[j] = keep + __shfl_xor(give, 16, 64);
+        }
+        float* dst = &red[i][wv][(h32 ? DK : 0) + (F == 2 ? 64 * h16 + 4 * sub : 4 * sub + 2 * h16)];
+        if constexpr (F == 2) {
+          *reinterpret_cast<floatx4*>(dst) = floatx4{v2[0], v2[1], v2[2], v2[3]};
+        } else {
+          *reinterpret_cast<float2*>(dst) = make_float2(v2[0], v2[1]);
         }
       }
+      da = xsum_rows(da);
+      db = xsum_rows(db);
       if (lane == 0) {
         red[i][wv][2 * DK] = da;
         red[i][wv][2 * DK + 1] = db;
