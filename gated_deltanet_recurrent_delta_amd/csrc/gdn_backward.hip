@@ -49,6 +49,21 @@ __device__ __forceinline__ float dot4(const floatx4 (&a)[F], const float4 (&b)[F
   return p;
 }
 
+// Inputs kept as loaded (bf16 bits, or fp32) until they are used, so that a
+// block's loads can be issued ahead of other work without the conversions
+// (which wait for the data) coming with them.
+__device__ __forceinline__ uint2 ld_raw4(const bf16* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ float4 ld_raw4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 cvt4(uint2 u) {
+  return make_float4(bf16_bits_to_f32(u.x & 0xFFFFu), bf16_bits_to_f32(u.x >> 16),
+                     bf16_bits_to_f32(u.y & 0xFFFFu), bf16_bits_to_f32(u.y >> 16));
+}
+__device__ __forceinline__ float4 cvt4(float4 x) { return x; }
+__device__ __forceinline__ uint16_t ld_raw1(const bf16* p) { return *reinterpret_cast<const uint16_t*>(p); }
+__device__ __forceinline__ float ld_raw1(const float* p) { return *p; }
+__device__ __forceinline__ float cvt1(uint16_t u) { return bf16_bits_to_f32(u); }
+__device__ __forceinline__ float cvt1(float x) { return x; }
+
 __device__ __forceinline__ float xsum_rows(float x) {   // over lanes l, l^16, l^32, l^48
   x += __shfl_xor(x, 16, 64);
   x += __shfl_xor(x, 32, 64);
@@ -107,35 +122,41 @@ __global__ __launch_bounds__(64 * kBwdWaves) void backward_kernel(
   // and a token past the end gets the identity gates (alpha 1, beta 0, no
   // output gradient): the loops over a block then have no branch, and the
   // compiler is free to issue a block's loads ahead of its dependent chain.
+  using RawK = decltype(ld_raw4(k));
+  using RawV = decltype(ld_raw1(v));
   struct Tok {
-    float4 k[F];
-    float a, be, v[NG];
+    RawK k[F];
+    float a, be;
+    RawV v[NG];
   };
   auto load_tok = [&](Tok& x, int t) {
     const size_t ti = tok(min(t, T - 1));
     const bool ok = t < T;
 #pragma unroll
-    for (int f = 0; f < F; ++f) x.k[f] = load4(k + ti * DK + 64 * f + 4 * sub);
+    for (int f = 0; f < F; ++f) x.k[f] = ld_raw4(k + ti * DK + 64 * f + 4 * sub);
     // loaded unconditionally, then selected: a load under the condition
     // becomes a branch, which ends the scheduling region at every token
     const float a = alpha[ti], be = beta[ti];
     x.a = ok ? a : 1.f;
     x.be = ok ? be : 0.f;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) x.v[g] = load1(v + ti * dv + row0 + 4 * g);
+    for (int g = 0; g < NG; ++g) x.v[g] = ld_raw1(v + ti * dv + row0 + 4 * g);
   };
   // one forward step of the NG rows held in s
   auto fwd = [&](const floatx4 (&s)[NG][F], floatx4 (&out)[NG][F], const Tok& x) {
+    float4 kk[F];
+#pragma unroll
+    for (int f = 0; f < F; ++f) kk[f] = cvt4(x.k[f]);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       floatx4 sa[F];
 #pragma unroll
       for (int f = 0; f < F; ++f) sa[f] = s[g][f] * x.a;
-      const float u = x.be * (x.v[g] - sum16(dot4<F>(sa, x.k)));
+      const float u = x.be * (cvt1(x.v[g]) - sum16(dot4<F>(sa, kk)));
 #pragma unroll
       for (int f = 0; f < F; ++f)
-        out[g][f] = floatx4{sa[f][0] + u * x.k[f].x, sa[f][1] + u * x.k[f].y,
-                            sa[f][2] + u * x.k[f].z, sa[f][3] + u * x.k[f].w};
+        out[g][f] = floatx4{sa[f][0] + u * kk[f].x, sa[f][1] + u * kk[f].y,
+                            sa[f][2] + u * kk[f].z, sa[f][3] + u * kk[f].w};
     }
   };
 
@@ -149,17 +170,20 @@ __global__ __launch_bounds__(64 * kBwdWaves) void backward_kernel(
         s[g][f] = S0 ? *reinterpret_cast<const floatx4*>(S0 + srow(g) + 64 * f + 4 * sub)
                      : floatx4{0.f, 0.f, 0.f, 0.f};
     for (int c = 0; c < nc; ++c) {
+      // the block's loads go out before the checkpoint stores: stores count
+      // in the same in-order counter as loads, so a wait for a load issued
+      // after them would also wait for the stores
+      Tok xs[L];
+#pragma unroll
+      for (int i = 0; i < L; ++i) load_tok(xs[i], c * L + i);
+      __builtin_amdgcn_sched_barrier(0);      // keep them there
 #pragma unroll
       for (int g = 0; g < NG; ++g)
 #pragma unroll
         for (int f = 0; f < F; ++f)
           *reinterpret_cast<floatx4*>(ckpt + crow(c, g) + 64 * f + 4 * sub) = s[g][f];
 #pragma unroll
-      for (int i = 0; i < L; ++i) {
-        Tok x;
-        load_tok(x, c * L + i);
-        fwd(s, s, x);
-      }
+      for (int i = 0; i < L; ++i) fwd(s, s, xs[i]);
     }
   }
 
@@ -194,6 +218,9 @@ __global__ __launch_bounds__(64 * kBwdWaves) void backward_kernel(
       const size_t ti = tok(min(t, T - 1));
       Tok x;
       load_tok(x, t);
+      float4 kx[F];
+#pragma unroll
+      for (int f = 0; f < F; ++f) kx[f] = cvt4(x.k[f]);
       float4 qq[F];
 #pragma unroll
       for (int f = 0; f < F; ++f) qq[f] = load4(q + ti * DK + 64 * f + 4 * sub);
@@ -212,13 +239,13 @@ __global__ __launch_bounds__(64 * kBwdWaves) void backward_kernel(
           Gt[f] = floatx4{G[g][f][0] + dd * qq[f].x, G[g][f][1] + dd * qq[f].y,
                           G[g][f][2] + dd * qq[f].z, G[g][f][3] + dd * qq[f].w};
         }
-        const float w = x.v[g] - sum16(dot4<F>(sa, x.k));
+        const float w = cvt1(x.v[g]) - sum16(dot4<F>(sa, kx));
         const float u = x.be * w;
-        const float du = sum16(dot4<F>(Gt, x.k));
+        const float du = sum16(dot4<F>(Gt, kx));
         const float bdu = x.be * du;
 #pragma unroll
         for (int f = 0; f < F; ++f) {
-          const float kf[4] = {x.k[f].x, x.k[f].y, x.k[f].z, x.k[f].w};
+          const float kf[4] = {kx[f].x, kx[f].y, kx[f].z, kx[f].w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             dq[f][e] += dd * (sa[f][e] + u * kf[e]);
