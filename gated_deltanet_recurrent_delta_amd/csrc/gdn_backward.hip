@@ -72,7 +72,7 @@ __device__ __forceinline__ float xsum_rows(float x) {   // over lanes l, l^16, l
 
 }  // namespace
 
-// 8 rows per wave at either key width: at dk = 128 that is 254 registers and
+// 8 rows per wave at either key width: at dk = 128 that is 250 registers and
 // two waves per SIMD, and the workgroups of a B=8, H=16 batch (512) are all
 // resident at once (4 rows per wave: 157 registers, 1024 workgroups in two
 // rounds, 21.1 ms against 15.0 ms at B=8, T=4096, H=16).
@@ -195,6 +195,22 @@ __global__ __launch_bounds__(64 * kBwdWaves) void backward_kernel(
     for (int f = 0; f < F; ++f)
       G[g][f] = dST ? *reinterpret_cast<const floatx4*>(dST + srow(g) + 64 * f + 4 * sub)
                     : floatx4{0.f, 0.f, 0.f, 0.f};
+  // A block's checkpoint and the inputs of its rerun are loaded before the
+  // previous block's stores (the loop carries them), for the same reason as
+  // in the forward pass; the block's states are dead by then, so they fit.
+  floatx4 stn[NG][F];
+  Tok xn[L - 1];
+  auto prefetch = [&](int c) {                          // block c (clamped to 0)
+    const int cc = max(c, 0);
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int f = 0; f < F; ++f)
+        stn[g][f] = *reinterpret_cast<const floatx4*>(ckpt + crow(cc, g) + 64 * f + 4 * sub);
+#pragma unroll
+    for (int i = 0; i + 1 < L; ++i) load_tok(xn[i], cc * L + i);
+  };
+  if (nc > 0) prefetch(nc - 1);
   for (int c = nc - 1; c >= 0; --c) {
     const int t0 = c * L, n = min(L, T - t0);           // uniform in the workgroup
     floatx4 st[L][NG][F];                               // S before token t0 + i
@@ -202,14 +218,9 @@ __global__ __launch_bounds__(64 * kBwdWaves) void backward_kernel(
 #pragma unroll
     for (int g = 0; g < NG; ++g)
 #pragma unroll
-      for (int f = 0; f < F; ++f)
-        st[0][g][f] = *reinterpret_cast<const floatx4*>(ckpt + crow(c, g) + 64 * f + 4 * sub);
+      for (int f = 0; f < F; ++f) st[0][g][f] = stn[g][f];
 #pragma unroll
-    for (int i = 0; i + 1 < L; ++i) {
-      Tok x;
-      load_tok(x, t0 + i);
-      fwd(st[i], st[i + 1], x);
-    }
+    for (int i = 0; i + 1 < L; ++i) fwd(st[i], st[i + 1], xn[i]);
 
 #pragma unroll
     for (int i = L - 1; i >= 0; --i) {
@@ -311,6 +322,8 @@ __global__ __launch_bounds__(64 * kBwdWaves) void backward_kernel(
         red[i][wv][2 * DK + 1] = db;
       }
     }
+    prefetch(c - 1);
+    __builtin_amdgcn_sched_barrier(0);                  // keep the loads ahead of the stores
     if (sub == 0) {
 #pragma unroll
       for (int i = 0; i < L; ++i)
