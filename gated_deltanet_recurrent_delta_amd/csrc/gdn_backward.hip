@@ -72,7 +72,7 @@ __device__ __forceinline__ float xsum_rows(float x) {   // over lanes l, l^16, l
 
 }  // namespace
 
-// 8 rows per wave at either key width: at dk = 128 that is 250 registers and
+// 8 rows per wave at either key width: at dk = 128 that is 254 registers and
 // two waves per SIMD, and the workgroups of a B=8, H=16 batch (512) are all
 // resident at once (4 rows per wave: 157 registers, 1024 workgroups in two
 // rounds, 21.1 ms against 15.0 ms at B=8, T=4096, H=16).
@@ -103,6 +103,9 @@ __global__ __launch_bounds__(64 * kBwdWaves) void backward_kernel(
   constexpr int PWS = 2 * DK + 4;         // its LDS stride (16-byte rows)
   constexpr int ROWS_WG = 4 * NG * kBwdWaves;
   __shared__ __attribute__((aligned(16))) float red[L][kBwdWaves][PWS];
+  // dalpha (lanes 0..31) and dbeta (lanes 32..63): a slot per lane, so the
+  // store needs no branch (which would end the scheduling region per token)
+  __shared__ float red2[L][kBwdWaves][64];
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int wgs = dv / ROWS_WG;                         // grid = B H wgs exactly
@@ -317,10 +320,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void backward_kernel(
       }
       da = xsum_rows(da);
       db = xsum_rows(db);
-      if (lane == 0) {
-        red[i][wv][2 * DK] = da;
-        red[i][wv][2 * DK + 1] = db;
-      }
+      red2[i][wv][lane] = lane < 32 ? da : db;
     }
     prefetch(c - 1);
     __builtin_amdgcn_sched_barrier(0);                  // keep the loads ahead of the stores
@@ -336,7 +336,8 @@ __global__ __launch_bounds__(64 * kBwdWaves) void backward_kernel(
       const int i = e / PW, j = e - i * PW;
       float x = 0.f;
 #pragma unroll
-      for (int w2 = 0; w2 < kBwdWaves; ++w2) x += red[i][w2][j];
+      for (int w2 = 0; w2 < kBwdWaves; ++w2)
+        x += j < 2 * DK ? red[i][w2][j] : red2[i][w2][j == 2 * DK ? 0 : 32];
       part[(((size_t)head * T + t0 + i) * wgs + wg) * PW + j] = x;
     }
     __syncthreads();                                    // red is reused by the next block
