@@ -466,3 +466,27 @@ def rel_l2_per_head(x: np.ndarray, ref: np.ndarray, head_axes) -> np.ndarray:
     num = np.sqrt(np.sum((x - ref) ** 2, axis=red))
     den = np.sqrt(np.sum(ref ** 2, axis=red))
     return num / np.maximum(den, 1e-300)
+
+
+def rel_err_per_token(x: np.ndarray, ref: np.ndarray, head_axes,
+                      token_axis) -> np.ndarray:
+    """||x_t - ref_t||_2 / rms_t ||ref_t||_2, per head and token.
+
+    x_t is one token's slice of a head (the axes that are neither head axes
+    nor the token axis, e.g. the dv values of o [B, T, H, dv] with
+    head_axes (0, 2) and token_axis 1; a scalar per token for [B, T, H]).
+    The denominator is the root mean square over the head's tokens of the
+    reference token norms, so a token whose own output is small is judged
+    on the scale of its head.  The mean of the squared result over a head's
+    tokens is the square of rel_l2_per_head; its maximum sees one bad token
+    that the per-head figure averages away.  Returns an array over the head
+    axes and the token axis, in that axis order."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    keep = tuple(sorted(tuple(head_axes) + (token_axis,)))
+    red = tuple(a for a in range(ref.ndim) if a not in keep)
+    num = np.sqrt(np.sum((x - ref) ** 2, axis=red))
+    tok_norm2 = np.sum(ref ** 2, axis=red)
+    t_pos = keep.index(token_axis)
+    rms = np.sqrt(np.mean(tok_norm2, axis=t_pos, keepdims=True))
+    return num / np.maximum(rms, 1e-300)

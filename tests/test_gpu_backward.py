@@ -1,7 +1,10 @@
 """GPU parity of the backward pass (gdn_backward: gradients of
 sum <d_o, o> + <dST, S_T> through the gated delta rule with respect to q, k,
-v, alpha, beta and S_0) against the oracle's gdn_backward, element by element
-as per-head relative L2 in fp32 (1e-3), at sizes that span several
+v, alpha, beta and S_0) against the oracle's gdn_backward: every value
+finite, the per-head relative L2 within the fp32 tolerance (1e-3), and each
+token (each state row, for dS_0) within 1e-4 of its head's rms token norm
+(measured errors are ~1e-6, so one wrong element or token fails), at sizes
+that span several
 checkpoint blocks of 8 tokens with ragged tails, at the batched prefill shape
 B=8, T=4096, H=16 on sampled heads, and for the edge cases (T = 0, T = 1, no
 initial state or state gradient, dS_0 written over dS_T)."""
@@ -12,12 +15,13 @@ import torch
 
 from gated_deltanet_recurrent_delta_amd import binding as gdn
 from oracle import gdn_oracle as orc
-from tests.gpu_util import TOL_F32, assert_close, errs_S, errs_o, host, tdtype, to_dev
+from tests.gpu_util import TOL_F32, check_o, check_S, host, tdtype, to_dev
 from workloads import gdn_inputs as gi
 
 pytestmark = pytest.mark.gpu
 
 NAMES = ["dq", "dk", "dv", "dalpha", "dbeta", "dS0"]
+TOKEN_TOL = 1e-4
 
 
 def dev32(a):
@@ -42,8 +46,8 @@ def compare(label, g, ref, heads=None, tol=TOL_F32):
         want = ref[i]
         if name in ("dalpha", "dbeta"):
             got, want = got[..., None], want[..., None]
-        err = errs_S(got, want, heads) if name == "dS0" else errs_o(got, want, heads)
-        assert_close(f"{label} {name}", err, tol)
+        chk = check_S if name == "dS0" else check_o
+        chk(f"{label} {name}", got, want, tol, heads, token_tol=TOKEN_TOL)
 
 
 def check(x, d_o, dST, label="", heads=None):

@@ -6,7 +6,7 @@ import torch
 
 from gated_deltanet_recurrent_delta_amd import binding as gdn
 from oracle import gdn_oracle as orc
-from tests.gpu_util import (TOL_BF16, TOL_F32, assert_close, errs_S, host,
+from tests.gpu_util import (TOL_BF16, TOL_F32, assert_close, check_o, check_S, check_step, host,
                             tdtype, to_dev, oracle_prefill)
 from workloads import gdn_inputs as gi
 
@@ -36,8 +36,8 @@ def test_decode_matches_oracle(B, H, dk, dv, in_dt, out_dt):
     o_ref, S_ref = orc.gdn_decode_step(x.q[:, 0], x.k[:, 0], x.v[:, 0],
                                        x.alpha[:, 0], x.beta[:, 0], x.S0)
     tol_o = TOL_F32 if out_dt == "f32" else TOL_BF16
-    assert_close("o", orc.rel_l2_per_head(host(o), o_ref, (0, 1)), tol_o)
-    assert_close("S'", orc.rel_l2_per_head(host(S1), S_ref, (0, 1)), TOL_F32)
+    check_step("o", host(o), o_ref, tol_o)
+    check_S("S'", host(S1), S_ref, TOL_F32)
 
 
 @pytest.mark.parametrize("dk", [128, 64])
@@ -98,19 +98,19 @@ def test_decode_chain_full_batch(dk):
     S_init = (0.3 * torch.randn((B, H, 128, dk), generator=g)).cuda()
     S_init[rows] = torch.from_numpy(S_prompt.astype(np.float32)).cuda()
     o_g, S_g = run_gpu(S_init)
-    assert_close("o (isolated)", orc.rel_l2_per_head(o_g, o_ref, (0, 2)), TOL_BF16)
-    assert_close("S_512 (isolated)", orc.rel_l2_per_head(S_g, S_ref, (0, 1)), TOL_F32)
+    check_o("o (isolated)", o_g, o_ref, TOL_BF16)
+    check_S("S_512 (isolated)", S_g, S_ref, TOL_F32)
 
     # (ii) end to end: GPU prefill of the sampled prompt rows
     dp = to_dev(prompt)
     _, S_p = gdn.prefill(dp["q"], dp["k"], dp["v"], dp["alpha"], dp["beta"])
     torch.cuda.synchronize()
-    assert_close("prompt state", errs_S(host(S_p), S_prompt), TOL_F32)
+    check_S("prompt state", host(S_p), S_prompt, TOL_F32)
     S_init2 = S_init.clone()
     S_init2[rows] = S_p
     o_g2, S_g2 = run_gpu(S_init2)
-    assert_close("o (end to end)", orc.rel_l2_per_head(o_g2, o_ref, (0, 2)), TOL_BF16)
-    assert_close("S_512 (end to end)", orc.rel_l2_per_head(S_g2, S_ref, (0, 1)), TOL_F32)
+    check_o("o (end to end)", o_g2, o_ref, TOL_BF16)
+    check_S("S_512 (end to end)", S_g2, S_ref, TOL_F32)
 
 
 def test_decode_equals_one_token_prefill():
@@ -123,5 +123,5 @@ def test_decode_equals_one_token_prefill():
     o_p, S_p = gdn.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"],
                            out_dtype=torch.float32)
     torch.cuda.synchronize()
-    assert_close("o", orc.rel_l2_per_head(host(o_p)[:, 0], host(o_d), (0, 1)), 1e-4)
-    assert_close("S", orc.rel_l2_per_head(host(S_p), host(S_d), (0, 1)), 1e-4)
+    check_step("o", host(o_p)[:, 0], host(o_d), 1e-4)
+    check_S("S", host(S_p), host(S_d), 1e-4)

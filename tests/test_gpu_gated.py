@@ -10,7 +10,7 @@ import torch
 
 from gated_deltanet_recurrent_delta_amd import binding as gdn
 from oracle import gdn_oracle as orc
-from tests.gpu_util import (TOL_BF16, TOL_F32, assert_close, errs_S, errs_o,
+from tests.gpu_util import (TOL_BF16, TOL_F32, assert_close, check_o, check_S, check_step,
                             host, tdtype, to_dev)
 from workloads import gdn_inputs as gi
 
@@ -36,8 +36,8 @@ def check(x, al, b, w, out_dt=None, label="", heads=None):
     o, S = run(x, al, b, w, out_dt)
     o_ref, S_ref = orc.gdn2_prefill(x.q, x.k, x.v, al, b, w, x.S0, heads=heads)
     tol_o = TOL_F32 if out_dt == "f32" else TOL_BF16
-    assert_close(f"{label} o", errs_o(host(o), o_ref, heads), tol_o)
-    assert_close(f"{label} S_T", errs_S(host(S), S_ref, heads), TOL_F32)
+    check_o(f"{label} o", host(o), o_ref, tol_o, heads)
+    check_S(f"{label} S_T", host(S), S_ref, TOL_F32, heads)
 
 
 @pytest.mark.parametrize("T", [1, 5, 37])
@@ -79,10 +79,10 @@ def test_kda_and_gdn_reductions_match_chunked_prefill():
                            out_dtype=torch.float32)
     torch.cuda.synchronize()
     o_ref, S_ref = orc.gdn_prefill(x.q, x.k, x.v, x.alpha, x.beta, x.S0)
-    assert_close("gated o vs oracle", errs_o(host(o_g), o_ref), TOL_F32)
-    assert_close("gated S vs oracle", errs_S(host(S_g), S_ref), TOL_F32)
-    assert_close("gated o vs chunked", errs_o(host(o_g), host(o_c)), TOL_F32)
-    assert_close("gated S vs chunked", errs_S(host(S_g), host(S_c)), TOL_F32)
+    check_o("gated o vs oracle", host(o_g), o_ref, TOL_F32)
+    check_S("gated S vs oracle", host(S_g), S_ref, TOL_F32)
+    check_o("gated o vs chunked", host(o_g), host(o_c), TOL_F32)
+    check_S("gated S vs chunked", host(S_g), host(S_c), TOL_F32)
 
 
 def test_gated_in_place_and_empty():

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 from gated_deltanet_recurrent_delta_amd import binding as gdn
-from tests.gpu_util import (TOL_BF16, TOL_F32, assert_close, errs_o, errs_S,
+from tests.gpu_util import (TOL_BF16, TOL_F32, assert_close, check_o, check_S, check_step,
                             host, oracle_prefill, tdtype, to_dev)
 from workloads import gdn_inputs as gi
 
@@ -58,8 +58,8 @@ def test_prefill_graph_replays_match_eager(B, T, H, dk, dv, out_dt):
     assert torch.isfinite(o_ref.float()).all() and torch.isfinite(S_ref).all()
     # the eager result itself, from the NaN-filled workspace, against the oracle
     o_or, S_or = oracle_prefill(x)
-    assert_close("o (eager)", errs_o(host(o_ref), o_or), TOL_F32 if out_dt == "f32" else TOL_BF16)
-    assert_close("S_T (eager)", errs_S(host(S_ref), S_or), TOL_F32)
+    check_o("o (eager)", host(o_ref), o_or, TOL_F32 if out_dt == "f32" else TOL_BF16)
+    check_S("S_T (eager)", host(S_ref), S_or, TOL_F32)
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):

@@ -6,7 +6,7 @@ import torch
 
 from gated_deltanet_recurrent_delta_amd import binding as gdn
 from oracle import gdn_oracle as orc
-from tests.gpu_util import (TOL_BF16, TOL_F32, assert_close, errs_S, errs_o,
+from tests.gpu_util import (TOL_BF16, TOL_F32, assert_close, check_o, check_S, check_step,
                             host, oracle_prefill, tdtype, to_dev)
 from workloads import gdn_inputs as gi
 
@@ -27,8 +27,8 @@ def check_full(x, out_dt=None, label=""):
     o, ST = run(x, out_dtype=tdtype(out_dt))
     o_ref, S_ref = oracle_prefill(x)
     tol_o = TOL_F32 if out_dt == "f32" else TOL_BF16
-    assert_close(f"{label} o", errs_o(host(o), o_ref), tol_o)
-    assert_close(f"{label} S_T", errs_S(host(ST), S_ref), TOL_F32)
+    check_o(f"{label} o", host(o), o_ref, tol_o)
+    check_S(f"{label} S_T", host(ST), S_ref, TOL_F32)
 
 
 def test_tiny_fp32_workload():
@@ -80,8 +80,8 @@ def test_qwen_shaped_prefill_full_length_sampled_heads():
     o, ST = run(x)
     print(f"  oracle on heads {heads}", flush=True)
     o_ref, S_ref = oracle_prefill(x, heads=heads)
-    assert_close("o", errs_o(host(o), o_ref, heads), TOL_BF16)
-    assert_close("S_T", errs_S(host(ST), S_ref, heads), TOL_F32)
+    check_o("o", host(o), o_ref, TOL_BF16, heads)
+    check_S("S_T", host(ST), S_ref, TOL_F32, heads)
     # spectra of the final state: stable rank bounds hold on every head
     S = host(ST)[0]
     for h in range(16):
@@ -96,8 +96,8 @@ def test_batched_prefill_sampled_heads(dk):
     heads = [(0, 0), (0, 9), (3, 4), (7, 15)]
     o, ST = run(x)
     o_ref, S_ref = oracle_prefill(x, heads=heads)
-    assert_close("o", errs_o(host(o), o_ref, heads), TOL_BF16)
-    assert_close("S_T", errs_S(host(ST), S_ref, heads), TOL_F32)
+    check_o("o", host(o), o_ref, TOL_BF16, heads)
+    check_S("S_T", host(ST), S_ref, TOL_F32, heads)
 
 
 def test_split_consistency_and_in_place_state():
@@ -117,8 +117,8 @@ def test_split_consistency_and_in_place_state():
     torch.cuda.synchronize()
     assert S2.data_ptr() == S1.data_ptr()
     o_split = torch.cat([o1, o2], dim=1)
-    assert_close("o split", errs_o(host(o_split), host(o_all)), 1e-4)
-    assert_close("S split", errs_S(host(S2), host(S_all)), 1e-4)
+    check_o("o split", host(o_split), host(o_all), 1e-4)
+    check_S("S split", host(S2), host(S_all), 1e-4)
 
 
 def test_zero_padding_embedding_ties_dk64_to_dk128():
@@ -143,8 +143,8 @@ def test_zero_padding_embedding_ties_dk64_to_dk128():
     S64s = np.zeros((2, 4, 128, 128))
     for h in range(4):
         S64s[:, h][:, :, idx[h]] = host(S64)[:, h]
-    assert_close("o", errs_o(host(o128), host(o64)), 1e-4)
-    assert_close("S", errs_S(host(S128), S64s), 1e-4)
+    check_o("o", host(o128), host(o64), 1e-4)
+    check_S("S", host(S128), S64s, 1e-4)
 
 
 def test_deterministic_bitwise():
@@ -215,5 +215,5 @@ def test_segmented_prefill_in_place_state():
     torch.cuda.synchronize()
     o_ref, S_ref = oracle_prefill(x)
     assert ST.data_ptr() == S.data_ptr()
-    assert_close("o", errs_o(host(o), o_ref), TOL_BF16)
-    assert_close("S_T", errs_S(host(ST), S_ref), TOL_F32)
+    check_o("o", host(o), o_ref, TOL_BF16)
+    check_S("S_T", host(ST), S_ref, TOL_F32)

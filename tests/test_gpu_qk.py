@@ -9,7 +9,7 @@ import torch
 
 from gated_deltanet_recurrent_delta_amd import binding as gdn
 from oracle import gdn_oracle as orc
-from tests.gpu_util import (TOL_BF16, TOL_F32, assert_close, errs_S, errs_o,
+from tests.gpu_util import (TOL_BF16, TOL_F32, assert_close, check_o, check_S, check_step,
                             host, tdtype, to_dev)
 from workloads import gdn_inputs as gi
 
@@ -51,8 +51,8 @@ def check_prefill_qk(x, ch, l2norm=True, q_scale=1.0, out_dt=None, label="", hea
                                       channels=ch, l2norm=l2norm, q_scale=q_scale,
                                       heads=heads)
     tol_o = TOL_F32 if out_dt == "f32" else TOL_BF16
-    assert_close(f"{label} o", errs_o(host(o), o_ref, heads), tol_o)
-    assert_close(f"{label} S_T", errs_S(host(ST), S_ref, heads), TOL_F32)
+    check_o(f"{label} o", host(o), o_ref, tol_o, heads)
+    check_S(f"{label} S_T", host(ST), S_ref, TOL_F32, heads)
 
 
 @pytest.mark.parametrize("T", [1, 63, 65, 200])
@@ -162,8 +162,8 @@ def test_decode_qk_matches_oracle(B, H, dk_in, dk, dv, permute, in_dt, out_dt):
                                           x.beta[:, 0], x.S0, channels=ch, l2norm=True,
                                           q_scale=QSCALE)
     tol_o = TOL_F32 if out_dt == "f32" else TOL_BF16
-    assert_close("o", orc.rel_l2_per_head(host(o), o_ref, (0, 1)), tol_o)
-    assert_close("S'", orc.rel_l2_per_head(host(S1), S_ref, (0, 1)), TOL_F32)
+    check_step("o", host(o), o_ref, tol_o)
+    check_S("S'", host(S1), S_ref, TOL_F32)
 
 
 @pytest.mark.parametrize("dk", [128, 64])
@@ -198,9 +198,9 @@ def test_decode_qk_chain_matches_prefill_qk():
     o_ref, S_ref = orc.gdn_prefill_qk(x.q, x.k, x.v, x.alpha, x.beta, channels=ch,
                                       q_scale=QSCALE)
     o_dec = torch.stack(outs, dim=1)
-    assert_close("prompt o", errs_o(host(o_p), o_ref[:, :Tp]), TOL_BF16)
-    assert_close("decode o", errs_o(host(o_dec), o_ref[:, Tp:]), TOL_BF16)
-    assert_close("S", errs_S(host(S), S_ref), TOL_F32)
+    check_o("prompt o", host(o_p), o_ref[:, :Tp], TOL_BF16)
+    check_o("decode o", host(o_dec), o_ref[:, Tp:], TOL_BF16)
+    check_S("S", host(S), S_ref, TOL_F32)
 
 
 @pytest.mark.parametrize("T", [0, 130, 1500])
@@ -223,8 +223,8 @@ def test_prefill_qk_in_place_state_and_empty(T):
         return
     o_ref, S_ref = orc.gdn_prefill_qk(x.q, x.k, x.v, x.alpha, x.beta, x.S0, channels=ch,
                                       q_scale=QSCALE)
-    assert_close("o", errs_o(host(o), o_ref), TOL_BF16)
-    assert_close("S_T", errs_S(host(ST), S_ref), TOL_F32)
+    check_o("o", host(o), o_ref, TOL_BF16)
+    check_S("S_T", host(ST), S_ref, TOL_F32)
 
 
 def test_prefill_qk_zero_initial_state_and_decode_in_place():
@@ -242,8 +242,8 @@ def test_prefill_qk_zero_initial_state_and_decode_in_place():
     assert S1.data_ptr() == S.data_ptr()
     o_ref, S_ref = orc.gdn_decode_step_qk(y.q[:, 0], y.k[:, 0], y.v[:, 0], y.alpha[:, 0],
                                           y.beta[:, 0], y.S0, channels=ch, q_scale=QSCALE)
-    assert_close("o", orc.rel_l2_per_head(host(o), o_ref, (0, 1)), TOL_BF16)
-    assert_close("S'", orc.rel_l2_per_head(host(S1), S_ref, (0, 1)), TOL_F32)
+    check_step("o", host(o), o_ref, TOL_BF16)
+    check_S("S'", host(S1), S_ref, TOL_F32)
 
 
 @pytest.mark.parametrize("dk_in,dk", [(128, 64), (128, 128)])

@@ -14,7 +14,7 @@ import torch
 
 from gated_deltanet_recurrent_delta_amd import binding as gdn
 from oracle import gdn_oracle as orc
-from tests.gpu_util import (TOL_BF16, TOL_F32, assert_close, errs_o, errs_S,
+from tests.gpu_util import (TOL_BF16, TOL_F32, assert_close, check_o, check_S, check_step,
                             host, oracle_prefill, to_dev)
 from workloads import gdn_inputs as gi
 
@@ -192,15 +192,13 @@ def check_truncated_prefill(x, r, heads, label, gap_min=1e-3):
     print(f"  {label}: unique up to {[until[bh] for bh in heads]} of {T}, "
           f"min gaps {[f'{gaps[bh]:.1e}' for bh in heads]}", flush=True)
     oh = host(o)
-    e_o = []
     for b, h in heads:
         n = until[(b, h)]
-        e_o.append(orc.rel_l2_per_head(oh[b:b + 1, :n, h:h + 1],
-                                       o_ref[b:b + 1, :n, h:h + 1], (0, 2)).max())
-    assert_close(f"{label} o", np.array(e_o), TOL_BF16)
+        check_o(f"{label} o (b={b}, h={h}, {n} tokens)", oh[b:b + 1, :n, h:h + 1],
+                o_ref[b:b + 1, :n, h:h + 1], TOL_BF16)
     full = [bh for bh in heads if until[bh] == T]
     if full:
-        assert_close(f"{label} S_T", errs_S(host(ST), S_ref, full), TOL_F32)
+        check_S(f"{label} S_T", host(ST), S_ref, TOL_F32, full)
         erh = er.cpu().numpy()
         for b, h in full:
             assert erh[b, h] == pytest.approx(orc.stable_rank(S_ref[b, h]),
@@ -230,8 +228,8 @@ def test_truncated_prefill_full_rank_equals_prefill():
     o2, S2 = gdn.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
                          out_dtype=f32)
     torch.cuda.synchronize()
-    assert_close("o", errs_o(host(o1), host(o2)), 1e-5)
-    assert_close("S", errs_S(host(S1), host(S2)), 1e-5)
+    check_o("o", host(o1), host(o2), 1e-5)
+    check_S("S", host(S1), host(S2), 1e-5)
 
 
 @pytest.mark.parametrize("r", [4, 32])
