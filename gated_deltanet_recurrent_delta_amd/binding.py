@@ -34,6 +34,8 @@ SIGNATURES = {
     "gdn_prefill_segments": (_i, [_i, _i, _i, _i, _i, _i, _i, _vp]),
     "gdn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                          _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "gdn_prefill_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _i, _i, _i, _i, _i, _i, _i, _vp]),
     "gdn_prefill_prepare": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                                  _vp, _sz, _vp]),
     "gdn_prefill_scan": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
@@ -185,6 +187,27 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                          _stream_handle(q, stream))
     _check(st, "gdn_prefill")
     return o, ST
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20      # GDN_NOALLOC_SCRATCH_BYTES in include/gdn.h
+
+
+def prefill_noalloc(q, k, v, alpha, beta, S0, o, ST, stream=None) -> None:
+    """gdn_prefill_noalloc: prefill into the caller's o and ST (ST may be S0
+    or None), its workspace in the library's static device scratch; the
+    binding allocates nothing either.  Calls that overlap on one device
+    race on that scratch; see include/gdn.h."""
+    B, T, H, dk, dv = _prefill_args(q, k, v, alpha, beta, S0)
+    if o.dtype not in _DTYPE_CODE:
+        raise ValueError(f"o: dtype {o.dtype} not in {tuple(_DTYPE_CODE)}")
+    _dev_tensor(o, "o", (o.dtype,), (B, T, H, dv))
+    if ST is not None:
+        _dev_tensor(ST, "ST", (torch.float32,), (B, H, dv, dk))
+    st = lib.gdn_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                 _ptr(S0), _ptr(o), _ptr(ST), B, T, H, dk, dv,
+                                 _DTYPE_CODE[q.dtype], _DTYPE_CODE[o.dtype],
+                                 _stream_handle(q, stream))
+    _check(st, "gdn_prefill_noalloc")
 
 
 def prefill_prepare(q, k, alpha, beta, dv: int, workspace: torch.Tensor,

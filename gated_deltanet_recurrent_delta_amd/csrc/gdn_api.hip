@@ -89,6 +89,28 @@ int check_scan_rest(const void* v, void* o, const float* S0, const float* ST,
 
 }  // namespace
 
+namespace gdn {
+
+// Every argument check of gdn_prefill except the workspace's; no HIP call.
+int prefill_args(const void* q, const void* k, const void* v, const float* alpha,
+                 const float* beta, const float* S0, const void* o, const float* ST,
+                 int B, int T, int H, int dk, int dv, int in_dtype, int out_dtype) {
+  int st = check_prefill_shape(B, T, H, dk, dv, in_dtype, out_dtype);
+  if (st != GDN_OK) return st;
+  if ((S0 && !aligned(S0, 16)) || (ST && !aligned(ST, 16))) return GDN_EINVAL;
+  const size_t nstate = (size_t)B * H * dv * dk;
+  if (ST && S0 && ST != S0 && (ST < S0 + nstate && S0 < ST + nstate))
+    return GDN_EINVAL;                               // partial overlap
+  if (T == 0) return GDN_OK;
+  if (!q || !k || !v || !o || !alpha || !beta) return GDN_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(alpha, 4) || !aligned(beta, 4))
+    return GDN_EINVAL;
+  return GDN_OK;
+}
+
+}  // namespace gdn
+
 extern "C" {
 
 const char* gdn_status_str(int status) {
@@ -96,7 +118,7 @@ const char* gdn_status_str(int status) {
     case GDN_OK: return "GDN_OK";
     case GDN_EINVAL: return "GDN_EINVAL: invalid argument (null pointer, bad size or misaligned buffer)";
     case GDN_ESHAPE: return "GDN_ESHAPE: unsupported head size or dtype (dk, dv in {64, 128}; f32 or bf16)";
-    case GDN_EWORKSPACE: return "GDN_EWORKSPACE: workspace missing or smaller than gdn_prefill_workspace_bytes()";
+    case GDN_EWORKSPACE: return "GDN_EWORKSPACE: workspace missing or too small (gdn_*_workspace_bytes()); for gdn_prefill_noalloc, the sizes need more than GDN_NOALLOC_SCRATCH_BYTES";
     case GDN_EHIP: return "GDN_EHIP: HIP launch failed";
     default: return "GDN_UNKNOWN_STATUS";
   }

@@ -70,6 +70,12 @@ constexpr int kMinSegChunks = 8;
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Every argument check of gdn_prefill except the workspace's (no HIP call);
+// returns a gdn_status.
+int prefill_args(const void* q, const void* k, const void* v, const float* alpha,
+                 const float* beta, const float* S0, const void* o, const float* ST,
+                 int B, int T, int H, int dk, int dv, int in_dtype, int out_dtype);
+
 // Plan for bf16 inputs and outputs (the only case that is segmented); the
 // workspace it sizes also covers every other dtype combination.
 inline PrefillPlan plan_prefill(int B, int T, int H, int dk, int dv) {

@@ -45,7 +45,8 @@
  *    failed launch returns GDN_EHIP.  Faults during execution surface at the
  *    caller's next synchronisation.  No exception or abort crosses the ABI.
  *  - Results are bitwise deterministic for a given shape, dtype and device
- *    (no atomics).  The library keeps no mutable global state.
+ *    (no atomics).  The library keeps no mutable global state, except the
+ *    device scratch of gdn_prefill_noalloc and its per-device address.
  */
 #ifndef GDN_H_
 #define GDN_H_
@@ -150,6 +151,31 @@ int gdn_prefill_scan(const void* q, const void* k, const void* v,
                      int in_dtype, int out_dtype,
                      void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/* ------------------------------------------------------------------------
+ * gdn_prefill without a caller workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.
+ *
+ * The workspace lives in a static device array of GDN_NOALLOC_SCRATCH_BYTES
+ * (256 MiB) that each device the library runs this call on holds until the
+ * process ends.  Sizes with gdn_prefill_workspace_bytes(B, T, H, dk, dv)
+ * above that return GDN_EWORKSPACE, checked before any HIP call (the
+ * 16-head, 16,384-token layer with dk = dv = 128 needs 236 MiB; B = 8,
+ * T = 4096, H = 16 needs 264 MiB and is rejected).  The first call on a
+ * device looks up that device's copy of the array (hipGetSymbolAddress);
+ * no call allocates or frees memory.  Every call on one device shares the
+ * array: calls that overlap on one device (different streams, or host
+ * threads without ordering between them) race and their results are
+ * undefined.  All other arguments, results, layouts and errors are those of
+ * gdn_prefill; the results equal gdn_prefill's bitwise.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+int gdn_prefill_noalloc(const void* q, const void* k, const void* v,
+                        const float* alpha, const float* beta, const float* S0,
+                        void* o, float* ST, int B, int T, int H, int dk, int dv,
+                        int in_dtype, int out_dtype, void* stream);
 
 /* ------------------------------------------------------------------------
  * One decode token for a batch of carried states.

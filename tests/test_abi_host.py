@@ -368,3 +368,44 @@ def test_backward_argument_errors(kw, status):
 
 def test_backward_empty_sequence_without_dS0_is_a_noop():
     assert backward(T=0, dS0=NULL, q=NULL, ws=NULL, ws_bytes=0) == bd.GDN_OK
+
+
+def prefill_noalloc(**kw):
+    a = dict(q=P, k=P, v=P, alpha=P, beta=P, S0=NULL, o=P, ST=P, B=1, T=100,
+             H=2, dk=128, dv=128, in_dtype=1, out_dtype=1, stream=NULL)
+    a.update(kw)
+    return bd.lib.gdn_prefill_noalloc(a["q"], a["k"], a["v"], a["alpha"], a["beta"],
+                                      a["S0"], a["o"], a["ST"], a["B"], a["T"],
+                                      a["H"], a["dk"], a["dv"], a["in_dtype"],
+                                      a["out_dtype"], a["stream"])
+
+
+def test_noalloc_scratch_size_matches_header():
+    m = re.search(r"#define GDN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)",
+                  open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == bd.NOALLOC_SCRATCH_BYTES
+    # the 16-head, 16K-token layer fits; the batched B=8 T=4096 H=16 does not
+    assert bd.prefill_workspace_bytes(1, 16384, 16, 128, 128) <= bd.NOALLOC_SCRATCH_BYTES
+    assert bd.prefill_workspace_bytes(8, 4096, 16, 128, 128) > bd.NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), bd.GDN_EINVAL),
+    (dict(T=-1), bd.GDN_EINVAL),
+    (dict(dk=96), bd.GDN_ESHAPE),
+    (dict(out_dtype=3), bd.GDN_ESHAPE),
+    (dict(q=NULL), bd.GDN_EINVAL),
+    (dict(beta=NULL), bd.GDN_EINVAL),
+    (dict(v=MIS), bd.GDN_EINVAL),
+    (dict(ST=MIS), bd.GDN_EINVAL),
+    (dict(S0=ctypes.c_void_p(0x10000), ST=ctypes.c_void_p(0x10100)), bd.GDN_EINVAL),
+    # more scratch than the static array holds: rejected before any HIP call
+    (dict(B=8, T=4096, H=16), bd.GDN_EWORKSPACE),
+    (dict(B=1, T=40000, H=16), bd.GDN_EWORKSPACE),
+])
+def test_prefill_noalloc_argument_errors(kw, status):
+    assert prefill_noalloc(**kw) == status
+
+
+def test_prefill_noalloc_empty_sequence_without_state_is_a_noop():
+    assert prefill_noalloc(T=0, ST=NULL, q=NULL, k=NULL, v=NULL, o=NULL) == bd.GDN_OK
