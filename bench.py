@@ -399,6 +399,49 @@ def _oracle_head(args):
     return q.shape[0]
 
 
+def _one_core_oracle(args):
+    """Runs in a fresh process with one BLAS/OpenMP thread, pinned to one
+    core: the oracle on the given heads, token by token."""
+    jobs, core = args
+    try:
+        os.sched_setaffinity(0, {core})
+    except OSError:
+        pass
+    t0 = time.perf_counter()
+    toks = sum(_oracle_head(j) for j in jobs)
+    return toks, time.perf_counter() - t0
+
+
+def cpu_baseline_one_core(x, T_sample, heads=2):
+    """The oracle on ONE host core (OPENBLAS_NUM_THREADS = OMP_NUM_THREADS =
+    1, a spawned process pinned to one core): `heads` heads of the prefill
+    workload, first T_sample tokens; scaled to layer tokens/s (all H heads)."""
+    H = x.q.shape[2]
+    jobs = [(x.q[0, :T_sample, h], x.k[0, :T_sample, h], x.v[0, :T_sample, h],
+             x.alpha[0, :T_sample, h], x.beta[0, :T_sample, h]) for h in range(heads)]
+    saved = {kk: os.environ.get(kk) for kk in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS",
+                                               "MKL_NUM_THREADS")}
+    for kk in saved:
+        os.environ[kk] = "1"
+    try:
+        core = sorted(os.sched_getaffinity(0))[0]
+        with mp.get_context("spawn").Pool(1) as pool:
+            toks, dt = pool.map(_one_core_oracle, [(jobs, core)])[0]
+    finally:
+        for kk, vv in saved.items():
+            if vv is None:
+                os.environ.pop(kk, None)
+            else:
+                os.environ[kk] = vv
+    return {"value": toks / H / dt, "unit": "tokens/s", "cores": 1,
+            "token_heads_per_s": toks / dt,
+            "sample": f"{heads} of {H} heads, first {T_sample} tokens ({toks} "
+                      f"token-heads), one process pinned to one core, "
+                      f"OPENBLAS_NUM_THREADS = OMP_NUM_THREADS = 1; {dt:.2f} s; "
+                      f"value = token-heads/s / {H} heads",
+            "seconds": dt}
+
+
 def cpu_baseline(x, T_sample):
     """Oracle over all heads of the prefill workload, first T_sample tokens,
     one worker process per head (fork pool; the GPU is not initialised)."""
@@ -494,6 +537,9 @@ def main(argv=None):
         log("timing the fp64 oracle on the host cores ...")
         cpu = cpu_baseline(x2, min(a.cpu_tokens, x2.q.shape[1]))
         log(f"  oracle: {cpu['value']:.0f} tokens/s ({cpu['sample']})")
+        one = cpu_baseline_one_core(x2, min(4096, x2.q.shape[1]))
+        log(f"  oracle, one core: {one['value']:.0f} tokens/s ({one['sample']})")
+        cpu["one_core"] = {kk: vv for kk, vv in one.items() if kk != "seconds"}
 
     import torch
     from gated_deltanet_recurrent_delta_amd import binding as gdn
@@ -578,7 +624,9 @@ def main(argv=None):
                      "frac_of_bf16_peak": (f_prep + f_scan) / (call_ms * 1e-3) / MFMA_BF16_PEAK,
                      "scan_frac": f_scan / (scan_ms * 1e-3) / MFMA_BF16_PEAK,
                      "prepare_kernel_frac": f_prep / (prep_ms * 1e-3) / MFMA_BF16_PEAK,
-                     "algorithmic_flops": prefill_algorithmic_flops(B, T, H, dk, dv)},
+                     "algorithmic_flops": prefill_algorithmic_flops(B, T, H, dk, dv),
+                     "frac_of_peak_algorithmic": prefill_algorithmic_flops(B, T, H, dk, dv) /
+                                                 (call_ms * 1e-3) / MFMA_BF16_PEAK},
         }
         roof = {"bound": "hbm", "kernel": "gdn_prefill (prepare_kernel + scan)",
                 "achieved": pbytes / (call_ms * 1e-3) / 1e9,
@@ -1078,7 +1126,7 @@ def bench_truncated(torch, gdn, dev, stream, up, ranks=(1, 4, 12, 32),
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            _, _, er = run()
+            _, S_T, er = run()
         g.replay()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -1089,11 +1137,27 @@ def bench_truncated(torch, gdn, dev, stream, up, ranks=(1, 4, 12, 32),
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
         erv = er.float().cpu().numpy().reshape(-1)
+        # secondary columns of the same final states, from their singular
+        # values (host fp64 SVD of the GPU's S_T): the entropy effective rank
+        # exp(-sum p log p), p = sigma / sum sigma, and the numerical rank
+        # #{sigma_i > sigma_1 * 128 * 2^-23} ("How much of its state does
+        # Gated DeltaNet use?", §1)
+        sv = np.linalg.svd(S_T.double().cpu().numpy().reshape(-1, dv, dk), compute_uv=False)
+        p = sv / np.maximum(sv.sum(axis=1, keepdims=True), 1e-300)
+        ent = np.exp(-np.sum(np.where(p > 0, p * np.log(np.where(p > 0, p, 1.0)), 0.0), axis=1))
+        nrank = np.sum(sv > sv[:, :1] * 128.0 * 2.0 ** -23, axis=1)
+
+        def stats(x, nd=3):
+            return {"mean": float(np.mean(x)), "min": float(np.min(x)),
+                    "max": float(np.max(x)), "per_head": [round(float(e), nd) for e in x]}
+
         item = {"ms_per_pass": ms, "tokens_per_s": B * T / (ms * 1e-3),
-                "stable_rank_at_T": {"mean": float(np.mean(erv)),
-                                     "min": float(np.min(erv)),
-                                     "max": float(np.max(erv)),
-                                     "per_head": [round(float(e), 3) for e in erv]}}
+                "stable_rank_at_T": stats(erv),
+                "entropy_erank_at_T": stats(ent),
+                "numerical_rank_at_T": stats(nrank, 0),
+                "rank_columns": "stable rank from gdn_truncate_rank's er_out (the "
+                                "primary figure); entropy erank and numerical rank "
+                                "from a host fp64 SVD of the same S_T"}
         if r < min(dk, dv):
             times = []
             for _ in range(5):
@@ -1109,7 +1173,7 @@ def bench_truncated(torch, gdn, dev, stream, up, ranks=(1, 4, 12, 32),
         log(f"truncated prefill r={r}: {ms:.2f} ms/pass, er(S_T) mean "
             f"{np.mean(erv):.2f}" + (f", one boundary {item['one_boundary_truncate_us']:.0f} us"
                                      if "one_boundary_truncate_us" in item else ""))
-        del g, er
+        del g, er, S_T
     base = res[f"r{min(dk, dv)}"]["ms_per_pass"]
     for r in ranks:
         res[f"r{r}"]["truncation_ms"] = res[f"r{r}"]["ms_per_pass"] - base

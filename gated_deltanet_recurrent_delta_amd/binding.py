@@ -16,7 +16,8 @@ from typing import Optional, Tuple
 import torch  # loaded first so libgdn binds to the HIP runtime torch uses
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgdn.so")
+# GDN_LIB_PATH overrides the library (the host-sanitized build of the tests)
+LIB_PATH = os.environ.get("GDN_LIB_PATH") or os.path.join(_HERE, "libgdn.so")
 
 GDN_OK, GDN_EINVAL, GDN_ESHAPE, GDN_EWORKSPACE, GDN_EHIP = range(5)
 GDN_F32, GDN_BF16 = 0, 1

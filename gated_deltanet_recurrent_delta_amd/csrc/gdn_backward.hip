@@ -1,8 +1,8 @@
 // Backward pass of the gated delta rule, recurrent form, on gfx950.
 //
 // The forward step (per head and token; "On State Reduction in Linear
-// Attention" reading notes, Sec. 2.1 with the per-token scalar decay, and
-// "Linear Attention Architectures" reading notes, Sec. 3.3 for the order
+// Attention" reading notes, paper Sec. 2.1 with the per-token scalar decay, and
+// "Linear Attention Architectures" reading notes, paper Sec. 3.3 for the order
 // decay -> predict -> write -> read):
 //     S~ = alpha S_prev,  w = v - S~ k,  u = beta w,  S = S~ + u k^T,  o = S q
 // The pages train these layers but print no backward pass; this is the

@@ -7,8 +7,8 @@
 //     s_i' = alpha s_i + u_i k                   (decay + delta write)
 //     o_i  = s_i' . q = alpha r + u_i (k . q)    (readout of the new state)
 // which is the per-row form of S' = alpha S (I - beta k k^T) + beta v k^T,
-// o = S' q ("On State Reduction in Linear Attention", Sec. 2.1, Eq. (2) with
-// the gated decay; rows evolve independently, Sec. 3.1).
+// o = S' q ("On State Reduction in Linear Attention", paper Sec. 2.1, Eq. (2) with
+// the gated decay; rows evolve independently, paper Sec. 3.1).
 //
 // The step is HBM-bound (each state byte is read once and written once, at
 // 0.75 flop/byte), so the kernel is a coalesced stream.  16 lanes cover 64
@@ -19,7 +19,7 @@
 // as its loads have arrived, so stores start while later rows are still in
 // flight.  The optional input path (per-head channel subset of dk_in-wide
 // q/k rows, L2 normalisation over the kept channels, query scale; "On State
-// Reduction in Linear Attention", Sec. 3.2-3.3) is applied to k and q in
+// Reduction in Linear Attention", paper Sec. 3.2-3.3) is applied to k and q in
 // registers before the row loop.  The two row dot products are reduced with four DPP steps and the
 // state is read and written with non-temporal accesses.
 #include "gdn_device.hpp"
@@ -61,7 +61,12 @@ __global__ __launch_bounds__(256) void decode_kernel(
     const TIn* qr = q + (size_t)head * qa.dk_in;
 #pragma unroll
     for (int f = 0; f < F; ++f) {
-      const int4 c = *reinterpret_cast<const int4*>(ch + 64 * f + 4 * sub);
+      int4 c = *reinterpret_cast<const int4*>(ch + 64 * f + 4 * sub);
+      // an index outside the row is clamped into it: never an out-of-bounds read
+      c.x = min(max(c.x, 0), qa.dk_in - 1);
+      c.y = min(max(c.y, 0), qa.dk_in - 1);
+      c.z = min(max(c.z, 0), qa.dk_in - 1);
+      c.w = min(max(c.w, 0), qa.dk_in - 1);
       kk[f] = make_float4(load1(kr + c.x), load1(kr + c.y), load1(kr + c.z), load1(kr + c.w));
       qq[f] = make_float4(load1(qr + c.x), load1(qr + c.y), load1(qr + c.z), load1(qr + c.w));
     }

@@ -1,7 +1,7 @@
 // The gated delta rule with generalised gates, in recurrent form, on gfx950.
 //
 // Per head and token ("Linear Attention Architectures" reading notes,
-// Sec. 2.5 Kimi Delta Attention and Sec. 2.6 Gated DeltaNet-2):
+// paper Sec. 3.4 Kimi Delta Attention and paper Sec. 3.5 Gated DeltaNet-2):
 //     S~  = S_{t-1} diag(alpha_t)        per-key-channel retention, applied on
 //                                        the key-feature side of the state
 //     e   = b_t * k_t                    direction the erase reads (key side)

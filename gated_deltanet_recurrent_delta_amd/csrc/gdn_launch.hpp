@@ -32,7 +32,7 @@ struct SegArgs {
 };
 
 // The input path of a channel-pruned layer, applied inside the kernels
-// ("On State Reduction in Linear Attention", Sec. 3.2-3.3: keep a per-head
+// ("On State Reduction in Linear Attention", paper Sec. 3.2-3.3: keep a per-head
 // subset of the query/key channels and recompute the normalisation over the
 // kept channels), plus an optional query scale.
 struct QkArgs {

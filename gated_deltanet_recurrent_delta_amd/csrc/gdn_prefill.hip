@@ -1,8 +1,8 @@
 // Chunked prefill of the gated delta rule on gfx950.
 //
 // The token recurrence (decay, predict with the decayed state, delta write,
-// read the new state; "On State Reduction in Linear Attention", Sec. 2.1,
-// Eq. (2) with gated decay, and "Linear Attention Architectures", Sec. 3.3)
+// read the new state; "On State Reduction in Linear Attention", paper Sec. 2.1,
+// Eq. (2) with gated decay, and "Linear Attention Architectures", paper Sec. 3.3)
 // is evaluated 64 tokens at a time.  Unrolling it inside a chunk of C tokens
 // with incoming state S, g = cumsum(log alpha) (inclusive, within the
 // chunk), gamma_j = e^{g_j}:
@@ -19,7 +19,7 @@
 // workspace holds T diag(beta) (so the scan forms V - diag(gamma) K S^T and
 // one product), and the optional input path (keep a per-head subset of the
 // query/key channels, renormalise over the kept channels, scale the query;
-// "On State Reduction in Linear Attention", Sec. 3.2-3.3) enters only as
+// "On State Reduction in Linear Attention", paper Sec. 3.2-3.3) enters only as
 // per-token factors: with q_j = nq_j q~_j and k_j = nk_j k~_j (q~, k~ the
 // kept raw channels, nq_j = scale / |q~_j|, nk_j = 1 / |k~_j|), the raw
 // rows stay exact MFMA operands and nk, nq are folded into A, P and the
@@ -38,7 +38,7 @@
 //    hi/lo tiles ready to be copied into LDS.
 //  * scan_kernel -- one workgroup per (batch, head, 16 NW state rows).  The
 //    rows of the state evolve independently ("On State Reduction in Linear
-//    Attention", Sec. 3.1), so each wave owns 16 rows and runs the whole
+//    Attention", paper Sec. 3.1), so each wave owns 16 rows and runs the whole
 //    chunk step for them in registers: the MFMA accumulator tiles of S, Y, Z
 //    and U are fed back as B operands without an LDS round trip (a lane's 8
 //    k-slots are the two 4-row runs it holds in the accumulator layout).
@@ -268,6 +268,9 @@ __global__ __launch_bounds__(64) void prepare_kernel(
       const int4 c1 = *reinterpret_cast<const int4*>(qa.chan + (size_t)h * DK + 32 * s + 8 * g4 + 4);
       ci[s][0] = c0.x; ci[s][1] = c0.y; ci[s][2] = c0.z; ci[s][3] = c0.w;
       ci[s][4] = c1.x; ci[s][5] = c1.y; ci[s][6] = c1.z; ci[s][7] = c1.w;
+      // an index outside the row is clamped into it: never an out-of-bounds read
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ci[s][e] = min(max(ci[s][e], 0), qa.dk_in - 1);
     }
   }
   const int ldin = GATHER ? qa.dk_in : DK;  // row width of q, k in memory

@@ -1,7 +1,7 @@
 // DRRQR channel selection, host code: which d_k' of the d_k key/query
 // channels a pruned layer keeps.
 //
-// "On State Reduction in Linear Attention" (reading notes), Sec. 3.4 with
+// "On State Reduction in Linear Attention" (reading notes), paper Sec. 3.4 with
 // its Algorithm 2 and App. B.2: on calibration samples M = [K_cal; Q_cal]
 // (2N x n, one column per channel), a QR with column pivoting gives an
 // initial permutation M P = Q [[A, B], [0, C]] (A: k x k); then, with

@@ -2,10 +2,10 @@
 //
 // S <- U_r U_r^T S, with U_r the r leading left singular vectors of S, is the
 // projection applied to every head's carried state at each 256-token segment
-// boundary in "How much of its state does Gated DeltaNet use?", Sec. 3 (how
+// boundary in "How much of its state does Gated DeltaNet use?", §3 (how
 // the low-energy directions are removed; r equal to the state width leaves
 // the model unchanged).  The stable rank er(S) = ||S||_F^2 / sigma_1^2 is
-// "On State Reduction in Linear Attention", Sec. 2.2, Eq. (5).
+// "On State Reduction in Linear Attention", paper Sec. 2.2, Eq. (5).
 //
 // Method, one workgroup per head, everything in fp64 in LDS:
 //  1. Householder QR of X = S^T (dk x dv, no pivoting).  S^T = Q R gives

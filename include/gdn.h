@@ -9,10 +9,10 @@
  * i.e. decay the carried state, predict v_t from the DECAYED state, write
  * beta_t times the prediction error along k_t, then read the NEW state with
  * q_t.  Sources: "On State Reduction in Linear Attention" (reading notes),
- * Sec. 2.1, Eqs. (1)-(2) (DeltaNet write, readout o_t = S_t q_t, state
+ * paper Sec. 2.1, Eqs. (1)-(2) (DeltaNet write, readout o_t = S_t q_t, state
  * S in R^{dv x dk}) with the input-dependent decay of Gated DeltaNet; and
  * "Linear Attention Architectures: Mechanisms, Trade-offs, and Cross-Layer
- * Routing" (reading notes), Sec. 3.3, Eqs. 15-17 (decay first, then compare
+ * Routing" (reading notes), paper Sec. 3.3, Eqs. 15-17 (decay first, then compare
  * with the target, then write) and the per-token data flow of Eq. 8 (the
  * output reads the updated state).  No query scale is applied.
  *
@@ -33,7 +33,7 @@
  *    alpha, beta and the state are always float32.
  *  - Supported head sizes: dk in {64, 128} (dk = 64 is the channel-pruned,
  *    "state halved" width of "On State Reduction in Linear Attention",
- *    Sec. 3.2-3.3), dv in {64, 128}.
+ *    paper Sec. 3.2-3.3), dv in {64, 128}.
  *  - Preconditions not checked (checking would cost a pass over the data):
  *    q and k are already unit-L2-normalised (and already gathered to the
  *    kept channels when pruned; the *_qk entry points below do both inside
@@ -193,7 +193,7 @@ int gdn_decode_step(const void* q, const void* k, const void* v,
 /* ------------------------------------------------------------------------
  * The input path of a channel-pruned layer, fused into the kernels.
  *
- * "On State Reduction in Linear Attention", Sec. 3.2-3.3, prunes a layer by
+ * "On State Reduction in Linear Attention", paper Sec. 3.2-3.3, prunes a layer by
  * keeping a per-head subset I_h of the query/key channels and recomputing
  * the L2 normalisation over the kept channels.  These variants take q and
  * k as the raw projection output, rows of dk_in elements, and apply
@@ -202,9 +202,12 @@ int gdn_decode_step(const void* q, const void* k, const void* v,
  * l2norm the division is skipped; a kept vector that is all zero stays
  * zero) before the recurrence, with no pass over q/k outside the kernels.
  *   channels   [H, dk] int32 device array, 16-byte aligned, each entry in
- *              [0, dk_in) (NOT checked: an index outside the row is an
- *              out-of-bounds read), or NULL: the rows are dk wide and all
- *              kept (dk_in must equal dk, else GDN_ESHAPE).
+ *              [0, dk_in), or NULL: the rows are dk wide and all kept (dk_in
+ *              must equal dk, else GDN_ESHAPE).  The kernels clamp an entry
+ *              outside [0, dk_in) to the nearest end of the row (0 or
+ *              dk_in - 1): no read leaves the row, and the results are those
+ *              of the clamped subset (no error is reported; checking on the
+ *              host would need a copy of the device array).
  *   dk_in      row width of q and k in memory (1 .. 2^20 with channels).
  *   l2norm     1: normalise q and k over the kept channels; 0: do not.
  *   q_scale    multiplies the (normalised) query; 1 for none.
@@ -239,8 +242,8 @@ int gdn_decode_step_qk(const void* q, const void* k, const void* v,
 /* ------------------------------------------------------------------------
  * Generalised gates, recurrent form.
  *
- * "Linear Attention Architectures" (reading notes), Sec. 2.5 (Kimi Delta
- * Attention) and Sec. 2.6 (Gated DeltaNet-2) refine the scalar gates of the
+ * "Linear Attention Architectures" (reading notes), paper Sec. 3.4 (Kimi
+ * Delta Attention, Eqs. 18-20) and paper Sec. 3.5 (Gated DeltaNet-2, Eqs. 21-24) refine the scalar gates of the
  * gated delta rule: a retention alpha per KEY channel, applied on the key
  * side of the state, and separate erase (b, key side) and write (w, value
  * side) gates.  Per head and token:
@@ -312,7 +315,7 @@ int gdn_backward(const void* q, const void* k, const void* v,
 /* ------------------------------------------------------------------------
  * DRRQR channel selection (calibration time, HOST memory and host code).
  *
- * "On State Reduction in Linear Attention" (reading notes), Sec. 3.4 with
+ * "On State Reduction in Linear Attention" (reading notes), paper Sec. 3.4 with
  * Algorithm 2 and App. B.2: choose which k of a head's n key/query channels
  * a pruned layer keeps, from calibration samples M = [K_cal; Q_cal] (rows =
  * samples, one column per channel).  A QR with column pivoting gives the
@@ -345,10 +348,10 @@ int gdn_drrqr_select(const double* M, int rows, int n, int k, double f,
  * Replaces each state S (dv x dk) by U_r U_r^T S, where U_r holds the r
  * leading left singular vectors of S, i.e. projects the state onto its top-r
  * left singular directions.  "How much of its state does Gated DeltaNet
- * use?", Sec. 3, applies this to every head's carried state at each
+ * use?", §3, applies this to every head's carried state at each
  * 256-token segment boundary (r equal to the state width is the unchanged
  * model).  The stable rank er(S) = ||S||_F^2 / sigma_1(S)^2 is "On State
- * Reduction in Linear Attention", Sec. 2.2, Eq. (5).
+ * Reduction in Linear Attention", paper Sec. 2.2, Eq. (5).
  *
  * Bytes of workspace gdn_truncate_rank needs when r < min(dv, dk):
  * BH * min(dv, dk) * dv * 4 (the unit singular vectors, fp32).  0 for

@@ -15,16 +15,16 @@ which equals S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T.
 
 Sources (page titles as published; sections/equations as the pages give them):
   * DeltaNet write and readout, o_t = S_t q_t, S in R^{dv x dk}:
-    "On State Reduction in Linear Attention" (reading notes), Sec. 2.1,
+    "On State Reduction in Linear Attention" (reading notes), paper Sec. 2.1,
     Eqs. (1)-(2); gated variant adds a per-token scalar decay (same section)
     and the update is written alpha_t S_{t-1} + u_t k_t^T in the proof of the
     rank bound, Eq. (3).
   * Ordering "decay, then compare with the target using the decayed state,
     then write, then read the new state": "Linear Attention Architectures:
     Mechanisms, Trade-offs, and Cross-Layer Routing" (reading notes),
-    Sec. 3.3 (GDN, Eqs. 15-17) and the per-token data flow of Eq. 8.
+    paper Sec. 3.3 (GDN, Eqs. 15-17) and the per-token data flow of Eq. 8.
   * Stable rank er(S) = ||S||_F^2 / ||S||_2^2: "On State Reduction in Linear
-    Attention", Sec. 2.2, Eq. (5); entropy effective rank and the numerical
+    Attention", paper Sec. 2.2, Eq. (5); entropy effective rank and the numerical
     rank threshold sigma_max * 128 * eps: "How much of its state does Gated
     DeltaNet use?" (state-rank post), §1.
   * Segment truncation (project the carried state onto its top-r left
@@ -39,15 +39,15 @@ Sources (page titles as published; sections/equations as the pages give them):
   * Generalised gates (gdn2_head): a per-key-channel decay applied on the
     right of the state (Kimi Delta Attention) and split key-side erase /
     value-side write gates whose outer products keep k_t on the right
-    (Gated DeltaNet-2): "Linear Attention Architectures" reading notes,
-    Secs. 2.5-2.6 and the mechanism table after them.
+    (Gated DeltaNet-2): "Linear Attention Architectures" reading notes on
+    the paper's Secs. 3.4-3.5 (Eqs. 18-24) and their mechanism table.
   * DRRQR channel selection (drrqr_select): a column-pivoted QR of the
     calibration matrix of key and query samples, then strong-RRQR swaps
     until every rho_ij <= f: "On State Reduction in Linear Attention",
-    Sec. 3.4 (Algorithm 2, App. B.2).
+    paper Sec. 3.4 (Algorithm 2, App. B.2).
   * Input path of a channel-pruned layer (qk_transform): keep a per-head
     subset of query/key coordinates and renormalise over the kept ones:
-    "On State Reduction in Linear Attention", Sec. 3.2-3.3.
+    "On State Reduction in Linear Attention", paper Sec. 3.2-3.3.
 
 Readings where the pages leave a step open:
   * No query scale: o_t = S_t q_t exactly.
@@ -238,7 +238,7 @@ def gdn2_head(q, k, v, alpha, b, w, S0=None):
     q, k [T, dk]; v [T, dv]; alpha [T, dk] per-key-channel retention;
     b [T, dk] key-side erase gate; w [T, dv] value-side write gate;
     S0 [dv, dk] or None.  Per token ("Linear Attention Architectures"
-    reading notes, Sec. 2.5 Kimi Delta Attention and Sec. 2.6 Gated
+    reading notes on paper Sec. 3.4 Kimi Delta Attention and paper Sec. 3.5 Gated
     DeltaNet-2):
         S~ = S_{t-1} diag(alpha_t)       decay on the key-feature side (right)
         e  = b_t * k_t                    the direction the erase reads
@@ -294,7 +294,7 @@ def qk_transform(x, channels=None, l2norm: bool = True, scale: float = 1.0):
     x [..., H, dk_in] (any leading axes; the head axis is second to last).
     channels: None, or int [H, dk] -- head h keeps coordinates channels[h]
       of its dk_in-wide vector, in that order (the coordinate selection
-      P_I of "On State Reduction in Linear Attention", Sec. 3.2-3.3, one
+      P_I of "On State Reduction in Linear Attention", paper Sec. 3.2-3.3, one
       subset per head).
     l2norm: divide each kept vector by its L2 norm, computed over the KEPT
       coordinates only (the same page: normalisation is recomputed on the
@@ -347,7 +347,7 @@ def drrqr_select(M, k: int, f: float = 2.0, max_swaps: int = 10000):
     """Keep k of the n columns of the calibration matrix M = [K_cal; Q_cal]
     (2N x n, samples as rows, one column per key/query channel).
 
-    "On State Reduction in Linear Attention" (reading notes), Sec. 3.4 and
+    "On State Reduction in Linear Attention" (reading notes), paper Sec. 3.4 and
     its Algorithm 2 / App. B.2: a QR with column pivoting gives an initial
     permutation, M P = Q [[A_k, B_k], [0, C_k]]; then, with
     U = A_k^{-1} B_k, omega_i = 1 / ||row i of A_k^{-1}||, gamma_j =

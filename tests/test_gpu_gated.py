@@ -2,7 +2,7 @@
 key channel, a key-side erase gate and a value-side write gate) against the
 oracle's gdn2_prefill, and its reductions to Kimi Delta Attention and to the
 gated delta rule of gdn_prefill ("Linear Attention Architectures" reading
-notes, Secs. 2.5-2.6)."""
+notes on paper Secs. 3.4-3.5)."""
 
 import numpy as np
 import pytest

@@ -1,7 +1,7 @@
 """GPU parity of the fused input path (gdn_prefill_qk, gdn_decode_step_qk)
 against the oracle: per-head channel subset of the raw q/k rows, L2
 renormalisation over the kept channels and a query scale ("On State
-Reduction in Linear Attention", Sec. 3.2-3.3), then the recurrence."""
+Reduction in Linear Attention", paper Sec. 3.2-3.3), then the recurrence."""
 
 import numpy as np
 import pytest
@@ -256,3 +256,36 @@ def test_prefill_qk_16k_segmented_sampled_heads(dk_in, dk):
     assert gdn.prefill_segments(1, T, H, dk, 128)[0] > 1
     x = gi.raw_qk(1, T, H, dk_in, 128, gi.seed_for(2, 5), "bf16", channel_idx=ch)
     check_prefill_qk(x, ch, True, QSCALE, label=f"16K {dk_in}->{dk}", heads=[(0, 3), (0, 12)])
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_out_of_range_channels_are_clamped(dt):
+    """Channel indices outside [0, dk_in) are clamped into the row by the
+    kernels (never read out of bounds): the results equal those of the
+    clamped subset, bitwise, and match the oracle on it.  bf16 rows 128 wide
+    take the prepare kernel's staged path, fp32 rows the element path."""
+    H, dk_in, dk = 3, 128, 64
+    ch = subsets(6100, H, dk_in, dk)
+    bad = ch.copy()
+    bad[0, 5], bad[1, 0], bad[2, 63], bad[2, 10] = -7, 1 << 20, dk_in, -(1 << 30)
+    good = np.clip(bad, 0, dk_in - 1).astype(np.int32)
+    x = gi.raw_qk(2, 150, H, dk_in, 128, 6101, dt, channel_idx=good, S0_scale=0.3)
+    d = to_dev(x)
+    res = []
+    for c in (bad, good):
+        res.append(gdn.prefill_qk(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"],
+                                  channels=dev_channels(c), q_scale=QSCALE,
+                                  validate=False))
+    sq = lambda t: t[:, 0].contiguous()
+    for c in (bad, good):
+        res.append(gdn.decode_step_qk(sq(d["q"]), sq(d["k"]), sq(d["v"]), sq(d["alpha"]),
+                                      sq(d["beta"]), d["S0"], channels=dev_channels(c),
+                                      q_scale=QSCALE, validate=False))
+    torch.cuda.synchronize()
+    for (o1, S1), (o2, S2) in ((res[0], res[1]), (res[2], res[3])):
+        assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    o_ref, S_ref = orc.gdn_prefill_qk(x.q, x.k, x.v, x.alpha, x.beta, x.S0,
+                                      channels=good, l2norm=True, q_scale=QSCALE)
+    tol_o = TOL_F32 if dt == "f32" else TOL_BF16
+    check_o("clamped o", host(res[0][0]), o_ref, tol_o)
+    check_S("clamped S_T", host(res[0][1]), S_ref, TOL_F32)

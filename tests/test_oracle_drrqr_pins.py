@@ -1,6 +1,6 @@
 """Pins of the oracle's DRRQR channel selection (drrqr_select).
 
-"On State Reduction in Linear Attention" (reading notes), Sec. 3.4 with
+"On State Reduction in Linear Attention" (reading notes), paper Sec. 3.4 with
 Algorithm 2 and App. B.2: a column-pivoted QR of the calibration matrix, then
 strong-RRQR trades until every rho_ij <= f; at that point, with
 c_f = sqrt(1 + f^2 k (n - k)), sigma_i(A_k) >= sigma_i(M) / c_f,

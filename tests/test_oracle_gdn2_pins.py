@@ -1,7 +1,7 @@
 """Pins of the oracle's generalised gates (gdn2_head / gdn2_prefill): a
 per-key-channel decay on the right of the state (Kimi Delta Attention) and a
 key-side erase gate b with a value-side write gate w (Gated DeltaNet-2),
-"Linear Attention Architectures" reading notes, Secs. 2.5-2.6.  Each pin is a
+"Linear Attention Architectures" reading notes on paper Secs. 3.4-3.5.  Each pin is a
 hand-worked value, an exact reduction to the already pinned gated delta rule,
 or an invariant, chosen so that a slip (decay on the wrong side, the erase
 outer product along e instead of k, the gates swapped) fails one of them."""

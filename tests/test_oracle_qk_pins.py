@@ -2,7 +2,7 @@
 
 The input path of a channel-pruned layer keeps a per-head subset of the
 query/key coordinates and recomputes the L2 normalisation over the kept
-coordinates ("On State Reduction in Linear Attention", Sec. 3.2-3.3); a query
+coordinates ("On State Reduction in Linear Attention", paper Sec. 3.2-3.3); a query
 scale, if any, multiplies the normalised query.  Each pin below checks a
 worked value, an exact identity or an invariance, chosen so that a slip in
 the oracle's input path (normalising before selecting, another head's
@@ -94,7 +94,7 @@ def test_zero_vector_maps_to_zero_and_only_decays_the_state():
 
 
 def test_query_scale_scales_outputs_only():
-    # o_t = S_t q_t is linear in q and q never enters the state (Sec. 2.1,
+    # o_t = S_t q_t is linear in q and q never enters the state (paper Sec. 2.1,
     # Eq. (1)): a query scale s gives s times the outputs and the same state
     r = rng(15)
     B, T, H, dk_in, dk, dv = 1, 40, 2, 16, 8, 5
@@ -110,7 +110,7 @@ def test_zero_padding_embedding():
     # raw vectors that vanish outside the kept set: renormalising over the
     # kept coordinates equals normalising over all of them, so the pruned
     # head reproduces the full-width head with S^(full) = S^(kept) P_I
-    # (State Reduction, Sec. 3.2-3.3; the unit-norm precondition)
+    # (State Reduction, paper Sec. 3.2-3.3; the unit-norm precondition)
     r = rng(16)
     B, T, H, dk_in, dk, dv = 1, 50, 2, 12, 5, 4
     ch = subsets(r, H, dk_in, dk)
@@ -144,7 +144,7 @@ def test_decode_step_qk_is_one_token_of_prefill_qk():
 def test_beta_one_write_stores_value_along_normalised_key():
     # with the key renormalised over the kept channels, a beta = 1 write
     # makes S_t k_t = v_t exactly (the delta rule's defining property,
-    # Linear Attention Architectures, Sec. 3.2), which fails if the key the
+    # Linear Attention Architectures, paper Sec. 3.2), which fails if the key the
     # recurrence uses is not unit-norm over the kept coordinates
     r = rng(18)
     H, dk_in, dk, dv = 2, 20, 7, 3

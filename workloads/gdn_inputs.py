@@ -25,8 +25,8 @@ Where the workloads come from
   about 61 % of heads forget within 256 tokens (§2); round(0.61 * 16) = 10.
 * The channel-pruned width dk' = dk/2 uses a per-head coordinate selection
   P_I shared by q and k, with normalisation recomputed over the kept
-  coordinates ("On State Reduction in Linear Attention", Sec. 3.2-3.3, and the
-  Rand selector of Sec. 3.4).
+  coordinates ("On State Reduction in Linear Attention", paper Sec. 3.2-3.3, and the
+  Rand selector of paper Sec. 3.4).
 """
 
 from __future__ import annotations
