@@ -53,7 +53,7 @@ SIGNATURES = {
     "gdn_gated_recurrent": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _i, _i, _i, _i, _i, _i, _i, _vp]),
     "gdn_drrqr_select": (_i, [_vp, _i, _i, _i, ctypes.c_double, _i, _vp, _vp, _vp]),
-    "gdn_backward_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "gdn_backward_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "gdn_backward": (_i, [_vp] * 14 + [_i] * 6 + [_vp, _sz, _vp]),
     "gdn_truncate_workspace_bytes": (_sz, [_i, _i, _i]),
     "gdn_truncate_rank": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
@@ -451,8 +451,9 @@ def gated_recurrent(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 # backward pass
 # ---------------------------------------------------------------------------
 
-def backward_workspace_bytes(B: int, T: int, H: int, dk: int, dv: int) -> int:
-    return int(lib.gdn_backward_workspace_bytes(B, T, H, dk, dv))
+def backward_workspace_bytes(B: int, T: int, H: int, dk: int, dv: int,
+                             in_dtype=torch.bfloat16) -> int:
+    return int(lib.gdn_backward_workspace_bytes(B, T, H, dk, dv, _DTYPE_CODE[in_dtype]))
 
 
 def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
@@ -490,7 +491,7 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         if res.get(name) is None:
             res[name] = torch.empty(shp, dtype=torch.float32, device=q.device)
         _dev_tensor(res[name], name, (torch.float32,), shp)
-    need = backward_workspace_bytes(B, T, H, dk, dv)
+    need = backward_workspace_bytes(B, T, H, dk, dv, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     st = lib.gdn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0),

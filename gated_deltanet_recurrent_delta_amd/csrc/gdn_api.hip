@@ -324,9 +324,10 @@ int gdn_gated_recurrent(const void* q, const void* k, const void* v,
       static_cast<hipStream_t>(stream)));
 }
 
-size_t gdn_backward_workspace_bytes(int B, int T, int H, int dk, int dv) {
-  if (check_prefill_shape(B, T, H, dk, dv, GDN_F32, GDN_F32) != GDN_OK) return 0;
-  return gdn::backward_ws_floats(B, T, H, dk, dv, nullptr) * sizeof(float);
+size_t gdn_backward_workspace_bytes(int B, int T, int H, int dk, int dv, int in_dtype) {
+  if (check_prefill_shape(B, T, H, dk, dv, in_dtype, GDN_F32) != GDN_OK || T == 0) return 0;
+  return in_dtype == GDN_BF16 ? gdn::backward_chunked_ws_bytes(B, T, H, dk, dv)
+                              : gdn::backward_ws_floats(B, T, H, dk, dv, nullptr) * sizeof(float);
 }
 
 int gdn_backward(const void* q, const void* k, const void* v, const float* alpha,
@@ -349,13 +350,18 @@ int gdn_backward(const void* q, const void* k, const void* v, const float* alpha
   if (!q || !k || !v || !alpha || !beta || !d_o || !dq || !dkey || !dval || !dalpha || !dbeta)
     return GDN_EINVAL;
   const uintptr_t ev = in_dtype == GDN_BF16 ? 2 : 4;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, ev) || !aligned(d_o, ev) ||
+  const uintptr_t eo = in_dtype == GDN_BF16 ? 16 : 4;     // bf16 d_o rows are read in 16-byte units
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, ev) || !aligned(d_o, eo) ||
       !aligned(alpha, 4) || !aligned(beta, 4) || !aligned(dq, 4) || !aligned(dkey, 4) ||
       !aligned(dval, 4) || !aligned(dalpha, 4) || !aligned(dbeta, 4))
     return GDN_EINVAL;
   if (!workspace || !aligned(workspace, 16)) return GDN_EWORKSPACE;
-  if (workspace_bytes < gdn::backward_ws_floats(B, T, H, dk, dv, nullptr) * sizeof(float))
+  if (workspace_bytes < gdn_backward_workspace_bytes(B, T, H, dk, dv, in_dtype))
     return GDN_EWORKSPACE;
+  if (in_dtype == GDN_BF16)
+    return to_status(gdn::launch_backward_chunked(q, k, v, alpha, beta, S0, d_o, dST, dq, dkey,
+                                                  dval, dalpha, dbeta, dS0, B, T, H, dk, dv,
+                                                  workspace, s));
   return to_status(gdn::launch_backward(q, k, v, alpha, beta, S0, d_o, dST, dq, dkey, dval,
                                         dalpha, dbeta, dS0, B, T, H, dk, dv, in_dtype,
                                         static_cast<float*>(workspace), s));

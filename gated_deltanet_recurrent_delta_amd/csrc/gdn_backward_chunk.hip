@@ -1,0 +1,812 @@
+// Backward pass of the gated delta rule in chunked form (bf16 inputs), on
+// gfx950.
+//
+// The forward step (per head and token; "On State Reduction in Linear
+// Attention" reading notes, paper Sec. 2.1 with the per-token scalar decay,
+// and "Linear Attention Architectures" reading notes, paper Sec. 3.3 for
+// the order decay -> predict -> write -> read) in chunked form: with the
+// chunk's incoming state S, g = inclusive cumsum of log alpha inside the
+// chunk, gamma_j = e^{g_j}, delta_j = e^{g_C - g_j} (g_C the chunk's last),
+// M_ji = e^{g_j - g_i} k_j.k_i (i < j), A = diag(beta) M, T = (I + A)^{-1},
+// P_ji = e^{g_j - g_i} q_j.k_i (i <= j):
+//     Z = V - diag(gamma) K S^T,   Ub = diag(beta) Z,   U = T Ub
+//     O = diag(gamma) Q S^T + P U,  S' = gamma_C S + U^T diag(delta) K.
+// The pages train these layers but print no backward pass; this is the
+// derivative of that map for L = sum <dO, O> + <dS_T, S_T>.  Given dO and
+// the gradient dS' reaching the chunk's final state:
+//     dU  = P^T dO + diag(delta) K dS'^T          dUb = T^T dU
+//     dZ  = diag(beta) dUb   (= dV)
+//     dS  = gamma_C dS' + dO^T diag(gamma) Q - dZ^T diag(gamma) K
+//     dP  = dO U^T (i <= j)    dA = -dUb U^T (i < j)    dM = diag(beta) dA
+//     dQ  = diag(gamma) dO S + (dP o E) K
+//     dK  = diag(delta) U dS' - diag(gamma beta) dUb S + (dP o E)^T Q
+//           + (dM o E) K + (dM o E)^T K          (E_ji = e^{g_j - g_i})
+//     dbeta_j = dUb_j . Z_j + sum_i dA_ji M_ji
+//     dg_j = gamma_j dgamma_j - delta_j ddelta_j + sum_i c_ji - sum_i c_ij,
+//            c = dP o P + dM o M,  dgamma_j = dO_j . (S q_j) - dZ_j . (S k_j),
+//            ddelta_j = U_j . (dS' k_j);  dg_C += sum_j delta_j ddelta_j
+//            + gamma_C <dS', S>;  dlog alpha = reverse cumsum of dg.
+// (dA = -T^T dT T^T with dT = dU Ub^T collapses to -dUb U^T.)
+//
+// Three sweeps over the chunks:
+//   1. forward (the prefill scan in its state-storing mode): the state at
+//      the start of every chunk;
+//   2. backward chain (bwd_chain_kernel): sequential over the chunks in
+//      reverse, the state gradient dS' at the end of every chunk and dS_0;
+//      rows of dS evolve independently (row i only sees value channel i),
+//      so it is parallel over heads and 64-row groups like the forward;
+//   3. chunk gradients (bwd_chunk_kernel): fully parallel over (batch,
+//      head, chunk): recomputes the chunk's intermediates from its stored
+//      S and dS' and forms dq, dk, dv, dalpha, dbeta with every sum over
+//      the value channels (and over tokens) inside MFMA contractions or
+//      the workgroup's LDS, in a fixed order (bitwise reproducible).
+// Every product that touches a state, a state gradient or an intermediate
+// uses split-bf16 operands (x = hi + lo) with fp32 accumulation; the bf16
+// inputs are exact operands.
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+#include "gdn_tiles.hpp"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kChainWaves = 4;     // 16 state-gradient rows per wave
+
+__device__ __forceinline__ float wave_sum(float x) {
+  x = sum16(x);
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+__device__ __forceinline__ void unpack8(const bf16x8& x, float (&f)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = (float)x[e];
+}
+
+}  // namespace
+
+// ===========================================================================
+// backward chain: one workgroup per (batch, head, 64 state-gradient rows)
+// ===========================================================================
+//
+// Wave w carries rows r0 + 16 w .. + 15 of dS as dS^T accumulator tiles
+// (lane holds dS^T[d = 16 dt + 4 g4 + i][row n]), exactly like the forward
+// scan carries S.  Per chunk, from the end:
+//   store dS' (the gradient at the chunk's end, read by the chunk kernel);
+//   Y' = K dS'^T (split dS'), dU = P^T dO + diag(delta) Y', dZ = Tb^T dU
+//   (Tb = T diag(beta), as the prepare phase stores it);
+//   dS^T <- gamma_C dS'^T + Q^T (diag(gamma) dO) - K^T (diag(gamma) dZ).
+// The chunk's K, Q, dO (the workgroup's rows), Tb, P tiles and gate rows
+// are staged in registers one chunk ahead and committed to LDS.
+template <int DK, int MINW>
+__global__ __launch_bounds__(64 * kChainWaves, MINW) void bwd_chain_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k,
+    const bf16* __restrict__ dout, const float* __restrict__ ws,
+    const float* dST, float* __restrict__ dSc, float* dS0, int T, int H, int DV,
+    int nchunks, int nblocks) {
+  constexpr int NW = kChainWaves;
+  constexpr int NT = 64 * NW;
+  constexpr int ROWS = 16 * NW;
+  constexpr int LDK = DK + 8, LDT = C + 8, LDV = 16 + 8;
+  constexpr int VBLK = C * LDV;
+  constexpr int NDT = DK / 16, NKB = DK / 32;
+  constexpr int UPR = DK / 8, VUPR = ROWS / 8;      // 16-byte units per row
+  constexpr int UK = C * UPR / NT, UV = C * VUPR / NT, UTP = 4 * C * C * 2 / 16 / NT;
+  static_assert(UK * NT == C * UPR && UV * NT == C * VUPR && UTP * NT * 16 == 4 * C * C * 2,
+                "staging covers the tiles");
+
+  __shared__ __attribute__((aligned(16))) bf16 Ks[C * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 Qs[C * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 TPs[4][C * LDT];   // Tb hi, Tb lo, P hi, P lo
+  __shared__ __attribute__((aligned(16))) bf16 Os[NW * VBLK];      // dO, blocked by wave
+  __shared__ __attribute__((aligned(16))) float Gs[4 * C];
+
+  int lin = blockIdx.x;
+  if ((nblocks & 7) == 0) lin = (lin & 7) * (nblocks >> 3) + (lin >> 3);
+  const int NRG = DV / ROWS;
+  const int bh = lin / NRG, rg = lin - bh * NRG;
+  const int b = bh / H, h = bh - b * H;
+  const int r0 = rg * ROWS;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = lane & 15, g4 = lane >> 4;
+  const int rw = 16 * w;
+
+  const bf16* k_seq = k + ((size_t)b * T * H + h) * DK;
+  const bf16* q_seq = q + ((size_t)b * T * H + h) * DK;
+  const bf16* o_seq = dout + ((size_t)b * T * H + h) * DV + r0;
+  const size_t tok_k = (size_t)H * DK, tok_v = (size_t)H * DV;
+
+  uint4 sk[UK], sq[UK], so[UV], stp[UTP];
+  float sg;
+  // Rows past the end of the sequence load the last valid row (in bounds);
+  // the commit zeroes them.
+  auto load = [&](int chunk) {
+    const int t0 = chunk * C, nvalid = min(C, T - t0);
+#pragma unroll
+    for (int i = 0; i < UK; ++i) {
+      const int u = tid + NT * i, c = u / UPR, cu = u - c * UPR;
+      const size_t off = (size_t)(t0 + min(c, nvalid - 1)) * tok_k + cu * 8;
+      sk[i] = *reinterpret_cast<const uint4*>(k_seq + off);
+      sq[i] = *reinterpret_cast<const uint4*>(q_seq + off);
+    }
+#pragma unroll
+    for (int i = 0; i < UV; ++i) {
+      const int u = tid + NT * i, c = u / VUPR, cu = u - c * VUPR;
+      so[i] = *reinterpret_cast<const uint4*>(o_seq + (size_t)(t0 + min(c, nvalid - 1)) * tok_v + cu * 8);
+    }
+    const char* wsc = reinterpret_cast<const char*>(ws) + ((size_t)bh * nchunks + chunk) * kChunkWsFloats * 4;
+#pragma unroll
+    for (int i = 0; i < UTP; ++i) stp[i] = *reinterpret_cast<const uint4*>(wsc + 16 * (tid + NT * i));
+    sg = (tid < 4 * C) ? reinterpret_cast<const float*>(wsc + kWsG)[tid] : 0.f;
+  };
+  auto commit = [&](int nvalid) {
+#pragma unroll
+    for (int i = 0; i < UK; ++i) {
+      const int u = tid + NT * i, c = u / UPR, d0 = (u - c * UPR) * 8;
+      const uint32_t m = c < nvalid ? 0xFFFFFFFFu : 0u;
+      *reinterpret_cast<uint4*>(&Ks[c * LDK + d0]) = make_uint4(sk[i].x & m, sk[i].y & m, sk[i].z & m, sk[i].w & m);
+      *reinterpret_cast<uint4*>(&Qs[c * LDK + d0]) = make_uint4(sq[i].x & m, sq[i].y & m, sq[i].z & m, sq[i].w & m);
+    }
+#pragma unroll
+    for (int i = 0; i < UV; ++i) {
+      const int u = tid + NT * i, c = u / VUPR, rr = (u - c * VUPR) * 8;
+      const uint32_t m = c < nvalid ? 0xFFFFFFFFu : 0u;
+      *reinterpret_cast<uint4*>(&Os[(rr >> 4) * VBLK + c * LDV + (rr & 15)]) =
+          make_uint4(so[i].x & m, so[i].y & m, so[i].z & m, so[i].w & m);
+    }
+#pragma unroll
+    for (int i = 0; i < UTP; ++i) {
+      const int u = tid + NT * i, m = u >> 9, rem = u & 511;
+      const int j = rem >> 3, i0 = (rem & 7) * 8;
+      *reinterpret_cast<uint4*>(&TPs[m][j * LDT + i0]) = stp[i];
+    }
+    if (tid < 4 * C) Gs[tid] = sg;
+  };
+
+  floatx4 dS[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    if (dST != nullptr) {
+      const float4 x = *reinterpret_cast<const float4*>(
+          dST + ((size_t)bh * DV + r0 + rw + n) * DK + 16 * dt + 4 * g4);
+      dS[dt] = floatx4{x.x, x.y, x.z, x.w};
+    } else {
+      dS[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  const bf16* Ow = Os + w * VBLK;
+  const bf16* Tbh = TPs[0];
+  const bf16* Tbl = TPs[1];
+  const bf16* Ph = TPs[2];
+  const bf16* Pl = TPs[3];
+
+  load(nchunks - 1);
+  for (int chunk = nchunks - 1; chunk >= 0; --chunk) {
+    const int nvalid = min(C, T - chunk * C);
+    __syncthreads();
+    commit(nvalid);
+    __syncthreads();
+    if (chunk > 0) load(chunk - 1);
+
+    {   // the gradient at the end of this chunk
+      const size_t srow = ((size_t)bh * nchunks + chunk) * DV + r0 + rw + n;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<float4*>(dSc + srow * DK + 16 * dt + 4 * g4) =
+            make_float4(dS[dt][0], dS[dt][1], dS[dt][2], dS[dt][3]);
+    }
+    // Y' = K dS'^T
+    floatx4 dU[4];
+    {
+      bf16x8 Dh[NKB], Dl[NKB];
+#pragma unroll
+      for (int s = 0; s < NKB; ++s) split8(acc_slots(dS[2 * s], dS[2 * s + 1]), Dh[s], Dl[s]);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        floatx4 yp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NKB; ++s) {
+          const bf16x8 kh = lds_slots(Ks, LDK, 16 * ct + n, s, g4);
+          yp = mfma(kh, Dh[s], yp);
+          yp = mfma(kh, Dl[s], yp);
+        }
+        // dU = P^T dO + diag(delta) Y'  (P^T upper triangular: k-blocks s >= ct/2)
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = ct / 2; s < 2; ++s) {
+          const bf16x8 ob = lds_slots_tr(Ow, LDV, 0, s, g4, n);
+          acc = mfma(lds_slots_tr(Ph, LDT, 16 * ct, s, g4, n), ob, acc);
+          acc = mfma(lds_slots_tr(Pl, LDT, 16 * ct, s, g4, n), ob, acc);
+        }
+        const float4 d4 = *reinterpret_cast<const float4*>(&Gs[3 * C + 16 * ct + 4 * g4]);
+        acc[0] += d4.x * yp[0];
+        acc[1] += d4.y * yp[1];
+        acc[2] += d4.z * yp[2];
+        acc[3] += d4.w * yp[3];
+        dU[ct] = acc;
+      }
+    }
+    // dZ = Tb^T dU
+    floatx4 dZ[4];
+    {
+      bf16x8 uh[2], ul[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) split8(acc_slots(dU[2 * s], dU[2 * s + 1]), uh[s], ul[s]);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = ct / 2; s < 2; ++s) {
+          const bf16x8 th = lds_slots_tr(Tbh, LDT, 16 * ct, s, g4, n);
+          const bf16x8 tl = lds_slots_tr(Tbl, LDT, 16 * ct, s, g4, n);
+          acc = mfma(th, uh[s], acc);
+          acc = mfma(th, ul[s], acc);
+          acc = mfma(tl, uh[s], acc);
+        }
+        dZ[ct] = acc;
+      }
+    }
+    // dS^T <- gamma_C dS'^T + Q^T (gamma dO) - K^T (gamma dZ)
+    {
+      bf16x8 goh[2], gol[2], zgh[2], zgl[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const float4 ga = *reinterpret_cast<const float4*>(&Gs[2 * C + kslot_base(s, g4, 0)]);
+        const float4 gb = *reinterpret_cast<const float4*>(&Gs[2 * C + kslot_base(s, g4, 1)]);
+        const float gv[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+        float ov[8];
+        unpack8(lds_slots_tr(Ow, LDV, 0, s, g4, n), ov);
+        const floatx8 z = acc_slots(dZ[2 * s], dZ[2 * s + 1]);
+        floatx8 go, zg;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          go[e] = gv[e] * ov[e];
+          zg[e] = -gv[e] * z[e];
+        }
+        split8(go, goh[s], gol[s]);
+        split8(zg, zgh[s], zgl[s]);
+      }
+      const float gC = Gs[C];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        floatx4 acc = dS[dt] * gC;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16x8 qt = lds_slots_tr(Qs, LDK, 16 * dt, s, g4, n);
+          const bf16x8 kt = lds_slots_tr(Ks, LDK, 16 * dt, s, g4, n);
+          acc = mfma(qt, goh[s], acc);
+          acc = mfma(qt, gol[s], acc);
+          acc = mfma(kt, zgh[s], acc);
+          acc = mfma(kt, zgl[s], acc);
+        }
+        dS[dt] = acc;
+      }
+    }
+  }
+  if (dS0 != nullptr) {
+    const size_t srow = (size_t)bh * DV + r0 + rw + n;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      *reinterpret_cast<float4*>(dS0 + srow * DK + 16 * dt + 4 * g4) =
+          make_float4(dS[dt][0], dS[dt][1], dS[dt][2], dS[dt][3]);
+  }
+}
+
+// ===========================================================================
+// chunk gradients: one workgroup per (batch, head, chunk)
+// ===========================================================================
+//
+// max(DK, DV) / 16 waves.  Phase A: wave w (w < DV/16) owns value channels
+// 16 w .. + 15 (the chunk's rows of S and dS' in registers) and forms Y, X,
+// Y', Z, Ub, U, dU, dUb and dZ for them, stores dv, its per-token partial
+// sums of dbeta, dgamma and ddelta, and U, dUb (split) into LDS.  Phase B:
+// the 10 lower 16x16 tiles of dP = dO U^T and of dA = -dUb U^T (contracted
+// over all value channels from LDS), their decay masks, dP o E and dM o E
+// (split, into LDS) and the tile sums that dg and dbeta need.  Phase C (one
+// wave): dalpha, dbeta.  Phase D: wave w (w < DK/16) owns key columns
+// 16 w .. + 15 and forms dq, dk for them, contracting over the value
+// channels with S and dS' columns (gathered from global memory, resident
+// in L2 since phase A read the same rows) and over tokens with the
+// masked C x C tiles.
+//
+// LDS (bf16 unless noted): K, Q, dO [C][d + 8]; four C x C tiles: T hi, T
+// lo, P hi, P lo (phase A; P also in B), then dP~ hi, lo, dM~ hi, lo;
+// U hi, U lo, dUb hi, dUb lo [C][DV]; fp32 gate rows and partial sums.
+// The never-written quadrant (rows 0..31, columns 32..63) of the T / P
+// tiles is never read: lower-triangular products take k-blocks s <= ct / 2
+// and their transposes s >= ct / 2.
+template <int DK, int DV>
+__global__ __launch_bounds__(64 * (DK > DV ? DK : DV) / 16, 1) void bwd_chunk_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k,
+    const bf16* __restrict__ v, const bf16* __restrict__ dout,
+    const float* __restrict__ alpha, const float* __restrict__ beta,
+    const float* __restrict__ ws, const char* __restrict__ tu,
+    const float* __restrict__ Sc, const float* __restrict__ dSc,
+    float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
+    float* __restrict__ dalpha, float* __restrict__ dbeta, int T, int H, int nchunks) {
+  constexpr int NW = (DK > DV ? DK : DV) / 16;
+  constexpr int NT = 64 * NW;
+  constexpr int NWV = DV / 16, NWK = DK / 16;
+  constexpr int NKB = DK / 32, NVB = DV / 32;
+  constexpr int NDT = DK / 16;
+  constexpr int LDK = DK + 8, LDO = DV + 8;
+  constexpr int NTILE = 20;              // 10 lower tiles of dP, then of dA
+
+  __shared__ __attribute__((aligned(16))) bf16 Ks[C * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 Qs[C * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 Os[C * LDO];
+  __shared__ __attribute__((aligned(16))) bf16 TT[4][C * C];   // T h/l, P h/l -> dP~ h/l, dM~ h/l
+  __shared__ __attribute__((aligned(16))) bf16 Ub[4][C * DV];  // U h/l, dUb h/l
+  __shared__ __attribute__((aligned(16))) float g2s[C], gams[C], dlts[C], bets[C], alps[C];
+  __shared__ __attribute__((aligned(16))) float sums[3][NWV][C];   // dbeta, dgamma, ddelta partials
+  __shared__ float sCw[NWV];
+  __shared__ __attribute__((aligned(16))) float tp[3][NTILE][16];  // tile row sums, col sums, row sums of dA M
+
+  const int chunk = blockIdx.x % nchunks;
+  const int bh = blockIdx.x / nchunks;
+  const int b = bh / H, h = bh - b * H;
+  const int t0 = chunk * C, nvalid = min(C, T - t0);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = lane & 15, g4 = lane >> 4;
+  const size_t tok0 = (size_t)b * T + t0;               // token row of chunk position 0
+
+  // ---- stage K, Q, dO (zero past the end), T, P; gate rows ----
+  {
+    constexpr int UPK = DK / 8, UPO = DV / 8;
+    for (int u = tid; u < C * UPK; u += NT) {
+      const int c = u / UPK, d0 = (u - c * UPK) * 8;
+      uint4 kx = make_uint4(0u, 0u, 0u, 0u), qx = kx;
+      if (c < nvalid) {
+        const size_t off = ((tok0 + c) * H + h) * DK + d0;
+        kx = *reinterpret_cast<const uint4*>(k + off);
+        qx = *reinterpret_cast<const uint4*>(q + off);
+      }
+      *reinterpret_cast<uint4*>(&Ks[c * LDK + d0]) = kx;
+      *reinterpret_cast<uint4*>(&Qs[c * LDK + d0]) = qx;
+    }
+    for (int u = tid; u < C * UPO; u += NT) {
+      const int c = u / UPO, d0 = (u - c * UPO) * 8;
+      uint4 ox = make_uint4(0u, 0u, 0u, 0u);
+      if (c < nvalid) ox = *reinterpret_cast<const uint4*>(dout + ((tok0 + c) * H + h) * DV + d0);
+      *reinterpret_cast<uint4*>(&Os[c * LDO + d0]) = ox;
+    }
+    const char* wsc = reinterpret_cast<const char*>(ws) + ((size_t)bh * nchunks + chunk) * kChunkWsFloats * 4;
+    const char* tuc = tu + ((size_t)bh * nchunks + chunk) * kTuBytes;
+    for (int u = tid; u < 4 * C * C / 8; u += NT) {
+      const int m = u / (C * C / 8), e = (u - m * (C * C / 8)) * 8;
+      const char* src = m < 2 ? tuc + m * C * C * 2 : wsc + (m == 2 ? kWsPh : kWsPl);
+      *reinterpret_cast<uint4*>(&TT[m][e]) = *reinterpret_cast<const uint4*>(src + 2 * e);
+    }
+    if (tid < C) {
+      const bool ok = tid < nvalid;
+      const float a = ok ? alpha[(tok0 + tid) * H + h] : 1.f;
+      const float be = ok ? beta[(tok0 + tid) * H + h] : 0.f;
+      float g = logf(a);
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(g, off, 64);
+        if (lane >= off) g += y;
+      }
+      const float glast = __shfl(g, 63, 64);
+      g2s[tid] = g * kLog2e;
+      gams[tid] = expf(g);
+      dlts[tid] = expf(glast - g);
+      bets[tid] = be;
+      alps[tid] = a;
+    }
+  }
+  __syncthreads();
+
+  const float* Sb = Sc + ((size_t)bh * nchunks + chunk) * DV * DK;
+  const float* dSb = dSc + ((size_t)bh * nchunks + chunk) * DV * DK;
+
+  // ===================== phase A: value channels =====================
+  if (w < NWV) {
+    const int rw = 16 * w;
+    floatx4 Y[4], X[4], Yp[4];
+    {
+      floatx4 Sr[NDT], Dr[NDT];
+      float sc = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const float4 a = *reinterpret_cast<const float4*>(Sb + (size_t)(rw + n) * DK + 16 * dt + 4 * g4);
+        const float4 c = *reinterpret_cast<const float4*>(dSb + (size_t)(rw + n) * DK + 16 * dt + 4 * g4);
+        Sr[dt] = floatx4{a.x, a.y, a.z, a.w};
+        Dr[dt] = floatx4{c.x, c.y, c.z, c.w};
+        sc += a.x * c.x + a.y * c.y + a.z * c.z + a.w * c.w;
+      }
+      sc = wave_sum(sc);
+      if (lane == 0) sCw[w] = sc;
+      bf16x8 Sh[NKB], Sl[NKB];
+#pragma unroll
+      for (int s = 0; s < NKB; ++s) split8(acc_slots(Sr[2 * s], Sr[2 * s + 1]), Sh[s], Sl[s]);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        floatx4 y = {0.f, 0.f, 0.f, 0.f}, x = y;
+#pragma unroll
+        for (int s = 0; s < NKB; ++s) {
+          const bf16x8 kh = lds_slots(Ks, LDK, 16 * ct + n, s, g4);
+          const bf16x8 qh = lds_slots(Qs, LDK, 16 * ct + n, s, g4);
+          y = mfma(kh, Sh[s], y);
+          y = mfma(kh, Sl[s], y);
+          x = mfma(qh, Sh[s], x);
+          x = mfma(qh, Sl[s], x);
+        }
+        Y[ct] = y;
+        X[ct] = x;
+      }
+#pragma unroll
+      for (int s = 0; s < NKB; ++s) split8(acc_slots(Dr[2 * s], Dr[2 * s + 1]), Sh[s], Sl[s]);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        floatx4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NKB; ++s) {
+          const bf16x8 kh = lds_slots(Ks, LDK, 16 * ct + n, s, g4);
+          y = mfma(kh, Sh[s], y);
+          y = mfma(kh, Sl[s], y);
+        }
+        Yp[ct] = y;
+      }
+    }
+    // Z = V - gamma Y;  Ub = beta Z
+    floatx4 Z[4], U[4];
+    {
+      bf16x8 ubh[2], ubl[2];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * ct + 4 * g4 + e;
+          const float vv = j < nvalid ? (float)v[((tok0 + j) * H + h) * DV + rw + n] : 0.f;
+          Z[ct][e] = vv - gams[j] * Y[ct][e];
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        floatx8 ub = acc_slots(Z[2 * s], Z[2 * s + 1]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ub[e] *= bets[kslot_base(s, g4, 0) + e];
+          ub[4 + e] *= bets[kslot_base(s, g4, 1) + e];
+        }
+        split8(ub, ubh[s], ubl[s]);
+      }
+      // U = T Ub  (T lower triangular: k-blocks s <= ct / 2)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s <= ct / 2; ++s) {
+          const bf16x8 th = lds_slots(TT[0], C, 16 * ct + n, s, g4);
+          const bf16x8 tl = lds_slots(TT[1], C, 16 * ct + n, s, g4);
+          acc = mfma(th, ubh[s], acc);
+          acc = mfma(th, ubl[s], acc);
+          acc = mfma(tl, ubh[s], acc);
+        }
+        U[ct] = acc;
+      }
+    }
+    // dU = P^T dO + diag(delta) Y';  dUb = T^T dU;  dZ = beta dUb
+    floatx4 dU[4], dUb[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = ct / 2; s < 2; ++s) {
+        const bf16x8 ob = lds_slots_tr(Os, LDO, rw, s, g4, n);
+        acc = mfma(lds_slots_tr(TT[2], C, 16 * ct, s, g4, n), ob, acc);
+        acc = mfma(lds_slots_tr(TT[3], C, 16 * ct, s, g4, n), ob, acc);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += dlts[16 * ct + 4 * g4 + e] * Yp[ct][e];
+      dU[ct] = acc;
+    }
+    {
+      bf16x8 uh[2], ul[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) split8(acc_slots(dU[2 * s], dU[2 * s + 1]), uh[s], ul[s]);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = ct / 2; s < 2; ++s) {
+          const bf16x8 th = lds_slots_tr(TT[0], C, 16 * ct, s, g4, n);
+          const bf16x8 tl = lds_slots_tr(TT[1], C, 16 * ct, s, g4, n);
+          acc = mfma(th, uh[s], acc);
+          acc = mfma(th, ul[s], acc);
+          acc = mfma(tl, uh[s], acc);
+        }
+        dUb[ct] = acc;
+      }
+    }
+    // dv; per-token partial sums over this wave's channels; U, dUb -> LDS
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const uint2 ow = lds_tr4(Os, LDO, 16 * ct + 4 * g4, rw, n);   // dO[j + e][rw + n]
+      const float ov[4] = {bf16lo(ow.x), bf16hi(ow.x), bf16lo(ow.y), bf16hi(ow.y)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 16 * ct + 4 * g4 + e;
+        const float dz = bets[j] * dUb[ct][e];
+        if (j < nvalid) dv[((tok0 + j) * H + h) * DV + rw + n] = dz;
+        const float sb = sum16(dUb[ct][e] * Z[ct][e]);
+        const float sgm = sum16(ov[e] * X[ct][e] - dz * Y[ct][e]);
+        const float sd = sum16(U[ct][e] * Yp[ct][e]);
+        if (n == 0) {
+          sums[0][w][j] = sb;
+          sums[1][w][j] = sgm;
+          sums[2][w][j] = sd;
+        }
+        bf16 uh, ul, dh, dl;
+        split_bf16(U[ct][e], uh, ul);
+        split_bf16(dUb[ct][e], dh, dl);
+        Ub[0][j * DV + rw + n] = uh;
+        Ub[1][j * DV + rw + n] = ul;
+        Ub[2][j * DV + rw + n] = dh;
+        Ub[3][j * DV + rw + n] = dl;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ===================== phase B: token x token tiles =====================
+  // S and dS' columns of this wave's key block for phase D: issued now so
+  // that they arrive while the tiles compute.  Lane (n, g4) takes column
+  // 16 w + n at the value channels of its k-slots.
+  float sg[NVB][8], dg[NVB][8];
+  if (w < NWK) {
+#pragma unroll
+    for (int s = 0; s < NVB; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int vr = kslot_base(s, g4, e >> 2) + (e & 3);
+        sg[s][e] = Sb[(size_t)vr * DK + 16 * w + n];
+        dg[s][e] = dSb[(size_t)vr * DK + 16 * w + n];
+      }
+  }
+  constexpr int kTilesPerWave = (NTILE + NW - 1) / NW;
+  float tv[kTilesPerWave][4];            // dP o E or dM o E of this wave's tiles
+#pragma unroll
+  for (int it_ = 0; it_ < kTilesPerWave; ++it_) {
+    const int t = w + NW * it_;
+    if (t >= NTILE) break;
+    const int kind = t / 10, pr = t - 10 * kind;
+    const int jt = pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
+    const int it = pr - jt * (jt + 1) / 2;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f}, kk = acc;
+#pragma unroll
+    for (int s = 0; s < NVB; ++s) {
+      const bf16x8 uh = lds_slots(Ub[0], DV, 16 * it + n, s, g4);
+      const bf16x8 ul = lds_slots(Ub[1], DV, 16 * it + n, s, g4);
+      if (kind == 0) {
+        const bf16x8 oa = lds_slots(Os, LDO, 16 * jt + n, s, g4);
+        acc = mfma(oa, uh, acc);
+        acc = mfma(oa, ul, acc);
+      } else {
+        const bf16x8 dh = lds_slots(Ub[2], DV, 16 * jt + n, s, g4);
+        const bf16x8 dl = lds_slots(Ub[3], DV, 16 * jt + n, s, g4);
+        acc = mfma(dh, uh, acc);
+        acc = mfma(dh, ul, acc);
+        acc = mfma(dl, uh, acc);
+      }
+    }
+    if (kind == 1) {
+#pragma unroll
+      for (int s = 0; s < NKB; ++s)
+        kk = mfma(lds_slots(Ks, LDK, 16 * jt + n, s, g4), lds_slots(Ks, LDK, 16 * it + n, s, g4), kk);
+    }
+    const int i = 16 * it + n;
+    const float gi = g2s[i];
+    float cs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 16 * jt + 4 * g4 + e;
+      const float E = (i <= j) ? __builtin_amdgcn_exp2f(g2s[j] - gi) : 0.f;
+      float c, d1, val;
+      if (kind == 0) {
+        const float dp = (i <= j) ? acc[e] : 0.f;
+        const float p = (float)TT[2][j * C + i] + (float)TT[3][j * C + i];
+        val = dp * E;
+        c = dp * p;
+        d1 = 0.f;
+      } else {
+        const float da = (i < j) ? -acc[e] : 0.f;
+        const float m = (i < j) ? E * kk[e] : 0.f;
+        const float dm = bets[j] * da;
+        val = (i < j) ? dm * E : 0.f;
+        c = dm * m;
+        d1 = da * m;
+      }
+      tv[it_][e] = val;
+      const float rs = sum16(c);
+      const float ds = sum16(d1);
+      if (n == 0) {
+        tp[0][t][4 * g4 + e] = rs;
+        tp[2][t][4 * g4 + e] = ds;
+      }
+      cs += c;
+    }
+    cs += __shfl_xor(cs, 16, 64);
+    cs += __shfl_xor(cs, 32, 64);
+    if (g4 == 0) tp[1][t][n] = cs;
+  }
+  __syncthreads();                        // every read of T and P is done
+  // dP~ -> TT[0] (hi) TT[1] (lo), dM~ -> TT[2], TT[3]; zeros in the upper
+  // tiles (0,1), (2,3) that share a 32-wide k-block with a diagonal tile
+#pragma unroll
+  for (int it_ = 0; it_ < kTilesPerWave; ++it_) {
+    const int t = w + NW * it_;
+    if (t >= NTILE) break;
+    const int kind = t / 10, pr = t - 10 * kind;
+    const int jt = pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
+    const int it = pr - jt * (jt + 1) / 2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 16 * jt + 4 * g4 + e, i = 16 * it + n;
+      bf16 hi, lo;
+      split_bf16(tv[it_][e], hi, lo);
+      TT[2 * kind][j * C + i] = hi;
+      TT[2 * kind + 1][j * C + i] = lo;
+    }
+  }
+  for (int u = tid; u < 4 * 2 * 256; u += NT) {
+    const int m = u >> 9, rem = u & 511, tile = rem >> 8, e = rem & 255;
+    const int j = 16 * (2 * tile) + (e >> 4), i = 16 * (2 * tile + 1) + (e & 15);
+    TT[m][j * C + i] = (bf16)0.f;
+  }
+  __syncthreads();
+
+  // ===================== phase C: dalpha, dbeta =====================
+  if (w == NW - 1) {
+    const int j = lane, jt = j >> 4, jr = j & 15;
+    float dgam = 0.f, ddl = 0.f, dbt = 0.f, dgc = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NWV; ++ww) {
+      dbt += sums[0][ww][j];
+      dgam += sums[1][ww][j];
+      ddl += sums[2][ww][j];
+      dgc += sCw[ww];
+    }
+    float rowc = 0.f, colc = 0.f;
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+      const int pr = t % 10;
+      const int tj = pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
+      const int ti = pr - tj * (tj + 1) / 2;
+      if (tj == jt) {
+        rowc += tp[0][t][jr];
+        if (t >= 10) dbt += tp[2][t][jr];
+      }
+      if (ti == jt) colc += tp[1][t][jr];
+    }
+    const float gm = gams[j], dl = dlts[j];
+    float dgj = gm * dgam - dl * ddl + rowc - colc;
+    const float tail = wave_sum(dl * ddl) + __shfl(gm, 63, 64) * dgc;
+    if (j == 63) dgj += tail;
+    // dlog alpha_j = sum_{j' >= j} dg_j'
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_down(dgj, off, 64);
+      if (j + off < 64) dgj += y;
+    }
+    if (j < nvalid) {
+      dalpha[(tok0 + j) * H + h] = dgj / alps[j];
+      dbeta[(tok0 + j) * H + h] = dbt;
+    }
+  }
+
+  // ===================== phase D: key columns =====================
+  if (w < NWK) {
+    const int cw = 16 * w;
+    bf16x8 sh[NVB], sl[NVB], dh[NVB], dl[NVB];
+#pragma unroll
+    for (int s = 0; s < NVB; ++s) {
+      const floatx8 a = {sg[s][0], sg[s][1], sg[s][2], sg[s][3], sg[s][4], sg[s][5], sg[s][6], sg[s][7]};
+      const floatx8 c = {dg[s][0], dg[s][1], dg[s][2], dg[s][3], dg[s][4], dg[s][5], dg[s][6], dg[s][7]};
+      split8(a, sh[s], sl[s]);
+      split8(c, dh[s], dl[s]);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      floatx4 q1 = {0.f, 0.f, 0.f, 0.f}, q2 = q1, k1 = q1, k2 = q1, k3 = q1;
+#pragma unroll
+      for (int s = 0; s < NVB; ++s) {
+        const bf16x8 oa = lds_slots(Os, LDO, 16 * ct + n, s, g4);
+        q1 = mfma(oa, sh[s], q1);
+        q1 = mfma(oa, sl[s], q1);
+        const bf16x8 uh = lds_slots(Ub[0], DV, 16 * ct + n, s, g4);
+        const bf16x8 ul = lds_slots(Ub[1], DV, 16 * ct + n, s, g4);
+        k1 = mfma(uh, dh[s], k1);
+        k1 = mfma(uh, dl[s], k1);
+        k1 = mfma(ul, dh[s], k1);
+        const bf16x8 bh_ = lds_slots(Ub[2], DV, 16 * ct + n, s, g4);
+        const bf16x8 bl_ = lds_slots(Ub[3], DV, 16 * ct + n, s, g4);
+        k2 = mfma(bh_, sh[s], k2);
+        k2 = mfma(bh_, sl[s], k2);
+        k2 = mfma(bl_, sh[s], k2);
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8 kt = lds_slots_tr(Ks, LDK, cw, s, g4, n);    // K[kslot][cw + n]
+        if (s <= ct / 2) {                                        // lower: dP~ K, dM~ K
+          q2 = mfma(lds_slots(TT[0], C, 16 * ct + n, s, g4), kt, q2);
+          q2 = mfma(lds_slots(TT[1], C, 16 * ct + n, s, g4), kt, q2);
+          k3 = mfma(lds_slots(TT[2], C, 16 * ct + n, s, g4), kt, k3);
+          k3 = mfma(lds_slots(TT[3], C, 16 * ct + n, s, g4), kt, k3);
+        }
+        if (s >= ct / 2) {                                        // upper: dP~^T Q, dM~^T K
+          const bf16x8 qt = lds_slots_tr(Qs, LDK, cw, s, g4, n);
+          k3 = mfma(lds_slots_tr(TT[0], C, 16 * ct, s, g4, n), qt, k3);
+          k3 = mfma(lds_slots_tr(TT[1], C, 16 * ct, s, g4, n), qt, k3);
+          k3 = mfma(lds_slots_tr(TT[2], C, 16 * ct, s, g4, n), kt, k3);
+          k3 = mfma(lds_slots_tr(TT[3], C, 16 * ct, s, g4, n), kt, k3);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 16 * ct + 4 * g4 + e;
+        if (j < nvalid) {
+          const size_t o = ((tok0 + j) * H + h) * DK + cw + n;
+          dq[o] = gams[j] * q1[e] + q2[e];
+          dk[o] = dlts[j] * k1[e] - gams[j] * bets[j] * k2[e] + k3[e];
+        }
+      }
+    }
+  }
+}
+
+// ===========================================================================
+// launcher
+// ===========================================================================
+
+size_t backward_chunked_ws_bytes(int B, int T, int H, int dk, int dv) {
+  const size_t BH = (size_t)B * H, nch = ((size_t)T + C - 1) / C;
+  return BH * nch * (kChunkWsFloats * 4 + kTuBytes + 2 * (size_t)dv * dk * 4);
+}
+
+hipError_t launch_backward_chunked(const void* q, const void* k, const void* v,
+                                   const float* alpha, const float* beta, const float* S0,
+                                   const void* d_o, const float* dST, float* dq, float* dkey,
+                                   float* dval, float* dalpha, float* dbeta, float* dS0,
+                                   int B, int T, int H, int dk, int dv, void* workspace,
+                                   hipStream_t stream) {
+  const size_t BH = (size_t)B * H;
+  const int nchunks = (T + C - 1) / C;
+  char* wsb = static_cast<char*>(workspace);
+  float* tiles = reinterpret_cast<float*>(wsb);
+  char* tu = wsb + BH * nchunks * kChunkWsFloats * 4;
+  float* Sc = reinterpret_cast<float*>(tu + BH * nchunks * kTuBytes);
+  float* dSc = Sc + BH * nchunks * (size_t)dv * dk;
+  QkArgs qa = qk_identity(dk);
+  qa.t_out = tu;
+  hipError_t e = launch_prefill_prepare(q, k, alpha, beta, tiles, B, T, H, dk, 1, true, qa, stream);
+  if (e != hipSuccess) return e;
+  e = launch_scan_states(k, v, S0, tiles, Sc, B, T, H, dk, dv, stream);
+  if (e != hipSuccess) return e;
+  const int nblocks = B * H * (dv / (16 * kChainWaves));
+#define GDN_CHAIN(DK_)                                                                        \
+  hipLaunchKernelGGL((bwd_chain_kernel<DK_, 1>), dim3(nblocks), dim3(64 * kChainWaves), 0,    \
+                     stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),        \
+                     static_cast<const bf16*>(d_o), tiles, dST, dSc, dS0, T, H, dv, nchunks, \
+                     nblocks)
+  if (dk == 128) GDN_CHAIN(128);
+  else GDN_CHAIN(64);
+#undef GDN_CHAIN
+  const dim3 grid((unsigned)(BH * nchunks));
+#define GDN_CHUNK(DK_, DV_)                                                                     \
+  hipLaunchKernelGGL((bwd_chunk_kernel<DK_, DV_>), grid, dim3(64 * ((DK_ > DV_ ? DK_ : DV_) / 16)), \
+                     0, stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),       \
+                     static_cast<const bf16*>(v), static_cast<const bf16*>(d_o), alpha, beta,   \
+                     tiles, tu, Sc, dSc, dq, dkey, dval, dalpha, dbeta, T, H, nchunks)
+  if (dk == 128 && dv == 128) GDN_CHUNK(128, 128);
+  else if (dk == 128) GDN_CHUNK(128, 64);
+  else if (dv == 128) GDN_CHUNK(64, 128);
+  else GDN_CHUNK(64, 64);
+#undef GDN_CHUNK
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -43,7 +43,11 @@ struct QkArgs {
   float qscale;      // multiplies the (normalised) query
   void* qk_out;      // prefill with chan: the gathered copy, k then q,
                      // [2][B][T][H][dk] in the input type (the scan reads it)
+  void* t_out = nullptr;   // if set, the prepare kernel also writes T itself
+                     // (without diag(beta)) as bf16 hi/lo 64x64 tiles,
+                     // kTuBytes per (batch, head, chunk) (the backward pass)
 };
+constexpr size_t kTuBytes = 2 * 64 * 64 * 2;
 inline QkArgs qk_identity(int dk) { return QkArgs{nullptr, dk, 0, 1.f, nullptr}; }
 
 // Bytes of the gathered q/k copy of a prefill with a channel subset.
@@ -158,5 +162,22 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const fl
                            const float* dST, float* dq, float* dk, float* dv_out,
                            float* dalpha, float* dbeta, float* dS0, int B, int T, int H,
                            int dkk, int dv, int in_dtype, float* ws, hipStream_t stream);
+
+// The backward pass in chunked form (bf16 inputs): workspace bytes (the
+// prepare phase's tiles, T itself, the state at the start and the state
+// gradient at the end of every chunk) and the launch (prepare, forward
+// sweep, backward chain, chunk gradients).
+size_t backward_chunked_ws_bytes(int B, int T, int H, int dk, int dv);
+hipError_t launch_backward_chunked(const void* q, const void* k, const void* v,
+                                   const float* alpha, const float* beta, const float* S0,
+                                   const void* d_o, const float* dST, float* dq, float* dkey,
+                                   float* dval, float* dalpha, float* dbeta, float* dS0,
+                                   int B, int T, int H, int dk, int dv, void* workspace,
+                                   hipStream_t stream);
+// The backward pass's forward sweep: the prefill scan storing the state at
+// the start of every chunk (bf16 inputs; ws holds the prepare tiles).
+hipError_t launch_scan_states(const void* k, const void* v, const float* S0,
+                              const float* ws, float* Sc, int B, int T, int H,
+                              int dk, int dv, hipStream_t stream);
 
 }  // namespace gdn

@@ -59,79 +59,13 @@
 
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
+#include "gdn_tiles.hpp"
 
 namespace gdn {
 
 namespace {
 
-constexpr int C = kChunk;
-constexpr float kLog2e = 1.4426950408889634f;
-
-// Workspace layout of one (batch, head, chunk), in bytes from its start.
-// The 64x64 tiles are lower triangular in 16x16 blocks; the scans read
-// 32-wide k-blocks at or below the diagonal only, so blocks (0,1) and (2,3)
-// hold zeros and rows 0..31, columns 32..63 are never written or read.
-constexpr int kWsTh = 0;                    // bf16 [64][64] hi part of T
-constexpr int kWsTl = 8192;                 // bf16 [64][64] lo part of T
-constexpr int kWsPh = 16384;                // bf16 [64][64] hi part of P
-constexpr int kWsPl = 24576;                // bf16 [64][64] lo part of P
-// fp32 [4][64] per-token rows: gamma nq (query side, for diag(gamma) Q S^T),
-// gamma_C (the chunk's total decay, repeated), gamma nk (key side, for
-// V - diag(gamma) K S^T) and e^{g_C - g} nk (for the state update); nq = nk
-// = 1 without the input path.
-constexpr int kWsG = 32768;
-static_assert(kWsG + 4 * 4 * C == kChunkWsFloats * 4, "workspace layout");
-
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) short4v lds_short4v_t;
-
-// First index of half `half` (0/1) of lane group g4's k-slots in 32-wide
-// k-block s: slots 0..3 are kslot_base(s, g4, 0) + 0..3, slots 4..7 are
-// kslot_base(s, g4, 1) + 0..3.  These are exactly the rows an accumulator
-// tile pair (16s.., 16s+16..) holds in a lane, so accumulators feed B
-// operands directly.
-__device__ __forceinline__ int kslot_base(int s, int g4, int half) {
-  return 32 * s + 16 * half + 4 * g4;
-}
-
-// 8 bf16 k-slots of row `row` from a row-major bf16 tile (row stride ld).
-__device__ __forceinline__ bf16x8 lds_slots(const bf16* X, int ld, int row,
-                                            int s, int g4) {
-  const uint2 a = *reinterpret_cast<const uint2*>(&X[row * ld + kslot_base(s, g4, 0)]);
-  const uint2 b = *reinterpret_cast<const uint2*>(&X[row * ld + kslot_base(s, g4, 1)]);
-  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
-}
-
-// Transposing read of a row-major bf16 tile X[row][col] (row stride ld):
-// returns, for lane (n = lane % 16), X[r0 + j][c0 + n], j = 0..3.
-// ds_read_b64_tr_b16 hands lane i of each 16-lane group element (i % 4) of
-// the 4 values read by lane 4 j + i / 4; lane n therefore reads row
-// r0 + n / 4, columns c0 + 4 (n % 4) .. + 3.
-__device__ __forceinline__ uint2 lds_tr4(const bf16* X, int ld, int r0, int c0,
-                                         int n) {
-  const bf16* p = &X[(r0 + (n >> 2)) * ld + c0 + 4 * (n & 3)];
-  const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_short4v_t*)(p));
-  return __builtin_bit_cast(uint2, r);
-}
-
-// 8 k-slots of k-block s (rows of X are the contraction index) for output
-// column c0 + n: X[kslot][c0 + n] via two transposing reads.
-__device__ __forceinline__ bf16x8 lds_slots_tr(const bf16* X, int ld, int c0,
-                                               int s, int g4, int n) {
-  const uint2 a = lds_tr4(X, ld, kslot_base(s, g4, 0), c0, n);
-  const uint2 b = lds_tr4(X, ld, kslot_base(s, g4, 1), c0, n);
-  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
-}
-
-// Accumulator tiles (2s, 2s+1) of a lane as the 8 k-slots of k-block s.
-__device__ __forceinline__ floatx8 acc_slots(const floatx4& lo, const floatx4& hi) {
-  const floatx8 x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return x;
-}
-
-__device__ __forceinline__ float bf16lo(uint32_t w) { return bf16_bits_to_f32(w & 0xFFFFu); }
-__device__ __forceinline__ float bf16hi(uint32_t w) { return bf16_bits_to_f32(w >> 16); }
+// (chunk size, workspace layout and the MFMA tile helpers: gdn_tiles.hpp)
 
 // 8 consecutive inputs as bf16 hi (and lo when the input is fp32).
 __device__ __forceinline__ void load_row8(const bf16* p, bf16x8& hi, bf16x8& lo) {
@@ -563,6 +497,13 @@ __global__ __launch_bounds__(64) void prepare_kernel(
     split8(x, hi, lo);
     *reinterpret_cast<bf16x8*>(wsc + kWsTh + (j * C + i0) * 2) = hi;
     *reinterpret_cast<bf16x8*>(wsc + kWsTl + (j * C + i0) * 2) = lo;
+    if (qa.t_out != nullptr) {            // T itself, for the backward pass
+      char* tu = static_cast<char*>(qa.t_out) + ((size_t)(b * H + h) * nchunks + chunk) * kTuBytes;
+      const floatx8 t = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      split8(t, hi, lo);
+      *reinterpret_cast<bf16x8*>(tu + (j * C + i0) * 2) = hi;
+      *reinterpret_cast<bf16x8*>(tu + C * C * 2 + (j * C + i0) * 2) = lo;
+    }
   }
 }
 
@@ -592,12 +533,14 @@ struct Stage {
 // workgroups share a CU so that one hides the other's LDS and memory
 // latency, at the price of a tighter register budget; it is used when the
 // grid has more workgroups than the GPU has CUs.
-template <int DK, typename TIn, typename TOut, int NW, int MINW>
+// SC: the backward pass's forward sweep: no outputs; the state at the
+// start of every chunk goes to Sc ([B*H][nchunks][DV][DK] fp32).
+template <int DK, typename TIn, typename TOut, int NW, int MINW, bool SC = false>
 __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const float* S0, TOut* __restrict__ o,
     float* ST, const float* __restrict__ ws, int T, int H, int DV,
-    int nchunks, int nblocks) {
+    int nchunks, int nblocks, float* __restrict__ Sc) {
   constexpr bool KEXACT = std::is_same<TIn, bf16>::value;   // q, k, v exact in bf16
   constexpr bool OPREC = std::is_same<TOut, float>::value;  // o stored in fp32
   constexpr int NT = 64 * NW;           // threads
@@ -665,7 +608,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
       const int c = u / UPR, cu = u - c * UPR;
       const size_t off = (size_t)(t0 + min(c, nvalid - 1)) * tok_k + cu * EPU;
       st.k[i] = *reinterpret_cast<const uint4*>(k_seq + off);
-      st.q[i] = *reinterpret_cast<const uint4*>(q_seq + off);
+      if constexpr (!SC) st.q[i] = *reinterpret_cast<const uint4*>(q_seq + off);
     }
 #pragma unroll
     for (int i = 0; i < St::UNITS_V; ++i) {
@@ -689,10 +632,10 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
       const int c = u / UPR, d0 = (u - c * UPR) * EPU;
       const uint32_t mk = c < nvalid ? 0xFFFFFFFFu : 0u;   // (a select on uint4 spills)
       const uint4 kx = make_uint4(st.k[i].x & mk, st.k[i].y & mk, st.k[i].z & mk, st.k[i].w & mk);
-      const uint4 qx = make_uint4(st.q[i].x & mk, st.q[i].y & mk, st.q[i].z & mk, st.q[i].w & mk);
+      const uint4 qx = SC ? kx : make_uint4(st.q[i].x & mk, st.q[i].y & mk, st.q[i].z & mk, st.q[i].w & mk);
       if constexpr (KEXACT) {
         *reinterpret_cast<uint4*>(&Khs[c * LDK + d0]) = kx;
-        *reinterpret_cast<uint4*>(&Qhs[c * LDK + d0]) = qx;
+        if constexpr (!SC) *reinterpret_cast<uint4*>(&Qhs[c * LDK + d0]) = qx;
       } else {
         const float4 kf = __builtin_bit_cast(float4, kx);
         const float4 qf = __builtin_bit_cast(float4, qx);
@@ -762,6 +705,13 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
     commit_stage(st, nvalid);
     __syncthreads();
     if (chunk + 1 < nchunks) load_stage(st, chunk + 1);   // prefetch
+    if constexpr (SC) {
+      const size_t srow = ((size_t)bh * nchunks + chunk) * DV + r0 + rw + n;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<float4*>(Sc + srow * DK + 16 * dt + 4 * g4) =
+            make_float4(S[dt][0], S[dt][1], S[dt][2], S[dt][3]);
+    }
 
     // split the state into bf16 hi/lo B operands, one per 32-wide k-block
     bf16x8 Sh[NKB], Sl[NKB];
@@ -781,6 +731,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
         acc = mfma(kh, Sh[s], acc);
         acc = mfma(kh, Sl[s], acc);
         if constexpr (!KEXACT) acc = mfma(lds_slots(Kls, LDK, 16 * ct + n, s, g4), Sh[s], acc);
+        if constexpr (SC) continue;
         accq = mfma(qh, Sh[s], accq);
         if constexpr (OPREC) {
           accq = mfma(qh, Sl[s], accq);
@@ -836,7 +787,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
 
     // ---- O = diag(gamma) Q S^T + P U ----
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
+    for (int ct = 0; ct < 4 && !SC; ++ct) {
       floatx4 acc = OQ[ct];
       const int c = 16 * ct + 4 * g4;
       const float4 gg = *reinterpret_cast<const float4*>(&Gs[c]);          // gamma nq
@@ -864,7 +815,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
         *reinterpret_cast<bf16x4*>(&Vhs[w * VBLK + n * LDO + c]) = ob;   // O^T[r][c]
       }
     }
-    if constexpr (!OPREC) {
+    if constexpr (!OPREC && !SC) {
       // O^T of this wave -> 16-byte stores: lane takes token
       // c = 32 m + 16 (g4 >> 1) + n and rows 8 (g4 & 1) .. + 7.
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1686,14 +1637,34 @@ static void launch_scan_t(const void* q, const void* k, const void* v,
                        dim3(64 * kScanWaves), 0, stream,
                        static_cast<const TIn*>(q), static_cast<const TIn*>(k),
                        static_cast<const TIn*>(v), S0, static_cast<TOut*>(o), ST,
-                       ws, T, H, dv, nchunks, nblocks);
+                       ws, T, H, dv, nchunks, nblocks, nullptr);
   } else {
     hipLaunchKernelGGL((scan_kernel<DK, TIn, TOut, kScanWaves, 1>), dim3(nblocks),
                        dim3(64 * kScanWaves), 0, stream,
                        static_cast<const TIn*>(q), static_cast<const TIn*>(k),
                        static_cast<const TIn*>(v), S0, static_cast<TOut*>(o), ST,
-                       ws, T, H, dv, nchunks, nblocks);
+                       ws, T, H, dv, nchunks, nblocks, nullptr);
   }
+}
+
+// The backward pass's forward sweep (bf16 inputs): the state at the start of
+// every chunk into Sc, no outputs.  ws holds the prepare phase's tiles.
+hipError_t launch_scan_states(const void* k, const void* v, const float* S0,
+                              const float* ws, float* Sc, int B, int T, int H,
+                              int dk, int dv, hipStream_t stream) {
+  const int nchunks = (T + C - 1) / C;
+  constexpr int ROWS = 16 * kScanWaves;
+  const int nblocks = B * H * (dv / ROWS < 1 ? 1 : dv / ROWS);
+#define GDN_SC(DK_, MW)                                                                    \
+  hipLaunchKernelGGL((scan_kernel<DK_, bf16, bf16, kScanWaves, MW, true>), dim3(nblocks), \
+                     dim3(64 * kScanWaves), 0, stream, static_cast<const bf16*>(k),        \
+                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), S0,         \
+                     static_cast<bf16*>(nullptr), static_cast<float*>(nullptr), ws, T, H,  \
+                     dv, nchunks, nblocks, Sc)
+  if (dk == 128) { if (nblocks > kNumCUs) GDN_SC(128, 2); else GDN_SC(128, 1); }
+  else { if (nblocks > kNumCUs) GDN_SC(64, 2); else GDN_SC(64, 1); }
+#undef GDN_SC
+  return hipGetLastError();
 }
 
 template <int DK>

@@ -271,7 +271,7 @@ int gdn_gated_recurrent(const void* q, const void* k, const void* v,
                         void* stream);
 
 /* ------------------------------------------------------------------------
- * Backward pass of gdn_prefill's recurrence (recurrent form).
+ * Backward pass of gdn_prefill's recurrence.
  *
  * The pages train these layers ("Linear Attention Architectures" reading
  * notes, the training set-ups of its experiments; "On State Reduction in
@@ -280,31 +280,48 @@ int gdn_gated_recurrent(const void* q, const void* k, const void* v,
  * gdn_prefill (S~ = alpha S_{t-1}, S_t = S~ + beta (v - S~ k) k^T,
  * o_t = S_t q_t) for the loss L = sum_t <do_t, o_t> + <dST, S_T>.
  *   q, k          [B, T, H, dk] in_dtype, 16-byte aligned.
- *   v, d_o        [B, T, H, dv] in_dtype (d_o: the gradient of o).
+ *   v             [B, T, H, dv] in_dtype, element-aligned.
+ *   d_o           [B, T, H, dv] in_dtype (the gradient of o), 16-byte
+ *                 aligned for bf16, element-aligned for fp32.
  *   alpha, beta   [B, T, H] float32.
  *   S0            [B, H, dv, dk] float32 or NULL (zero initial state).
  *   dST           [B, H, dv, dk] float32 or NULL (no gradient on S_T).
- *   dq, dk        [B, T, H, dk] float32, 16-byte aligned (written).
+ *   dq, dk        [B, T, H, dk] float32, 4-byte aligned (written).
  *   dv            [B, T, H, dv] float32 (written).
  *   dalpha, dbeta [B, T, H] float32 (written).
  *   dS0           [B, H, dv, dk] float32 or NULL (not wanted); it may alias
- *                 dST or S0 exactly (each state row is read before it is
- *                 written, by the same wave), not partly.
+ *                 dST or S0 exactly, not partly (every read of dST and S0
+ *                 precedes the write of dS0 on the stream).
  *   workspace     device memory of at least gdn_backward_workspace_bytes()
- *                 bytes, 16-byte aligned, owned by the caller (state
- *                 checkpoints every 8 tokens and per-workgroup partial
- *                 sums); NULL allowed when that size is 0 (T == 0).
+ *                 bytes for these sizes and in_dtype, 16-byte aligned,
+ *                 owned by the caller; NULL allowed when that size is 0
+ *                 (T == 0).
  * All pointers are device pointers; the call is asynchronous on `stream`.
- * Each wave reruns its state rows forward, storing a checkpoint every 8
- * tokens, then steps back through each 8-token block with the block's
- * states in registers.  Sums over the dv rows of a head (dq, dk, dalpha,
- * dbeta) are taken in a fixed order, so results are reproducible.
+ *
+ * bf16 inputs run the chunked form (64-token chunks, the products on bf16
+ * MFMA with split-bf16 operands wherever a state, a state gradient or an
+ * intermediate enters): the prepare phase of gdn_prefill (also storing T
+ * itself), a forward sweep that stores the state at the start of every
+ * chunk, a backward sweep over the chunks in reverse that stores the state
+ * gradient at the end of every chunk (and writes dS0), and one fully
+ * parallel pass over (batch, head, chunk) that forms every gradient of the
+ * chunk's tokens.  The workspace then holds, per head and chunk, the
+ * prepare tiles (33,792 bytes), T (16,384 bytes) and two dv x dk fp32
+ * states: 181,248 bytes per head and chunk at dk = dv = 128, so 1.48 GB at
+ * B = 8, T = 4096, H = 16.
+ * fp32 inputs run the recurrent form: each wave reruns its state rows
+ * forward, storing a checkpoint every 8 tokens, then steps back through
+ * each 8-token block with the block's states in registers; its workspace
+ * grows as B H (T / 8) dv dk 4 bytes (checkpoints) plus per-workgroup
+ * partial sums (4.3 GB + 2.2 GB at B = 8, T = 4096, H = 16, dk = dv = 128).
+ * Sums over the dv rows of a head (dq, dk, dalpha, dbeta) are taken in a
+ * fixed order in both forms, so results are reproducible bit for bit.
  * Errors: GDN_ESHAPE for dk or dv outside {64, 128} or an unknown dtype;
  * GDN_EINVAL for a NULL or misaligned required pointer, bad sizes or a
  * partial overlap of dS0; GDN_EWORKSPACE for a missing or short workspace;
  * GDN_EHIP if a launch fails.  T == 0 writes dS0 = dST (or zeros).
  */
-size_t gdn_backward_workspace_bytes(int B, int T, int H, int dk, int dv);
+size_t gdn_backward_workspace_bytes(int B, int T, int H, int dk, int dv, int in_dtype);
 int gdn_backward(const void* q, const void* k, const void* v,
                  const float* alpha, const float* beta, const float* S0,
                  const void* d_o, const float* dST, float* dq, float* dk,

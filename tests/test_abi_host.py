@@ -320,16 +320,24 @@ def test_gated_argument_errors(kw, status):
 # --- backward pass (gdn_backward) -------------------------------------------
 
 def test_backward_workspace_bytes():
-    # checkpoints every 8 tokens ([B H, ceil(T/8), dv, dk], rounded up to 64
-    # floats) + per-workgroup partials ([B H, T, dv / 32, 2 dk + 2])
     f = bd.lib.gdn_backward_workspace_bytes
-    assert f(1, 8, 1, 128, 128) == 4 * (128 * 128 + 8 * 4 * 258)
+    # fp32 inputs, recurrent form: checkpoints every 8 tokens ([B H,
+    # ceil(T/8), dv, dk], rounded up to 64 floats) + per-workgroup partials
+    # ([B H, T, dv / 32, 2 dk + 2])
+    assert f(1, 8, 1, 128, 128, 0) == 4 * (128 * 128 + 8 * 4 * 258)
     ck = 2 * 3 * 2 * 64 * 128                  # B=2, H=3, T=9 -> 2 checkpoints, dv=64, dk=128
-    assert f(2, 9, 3, 128, 64) == 4 * (ck + 6 * 9 * 2 * 258)
+    assert f(2, 9, 3, 128, 64, 0) == 4 * (ck + 6 * 9 * 2 * 258)
     ck = 2 * 3 * 64 * 64
-    assert f(1, 17, 2, 64, 64) == 4 * (ck + 2 * 17 * 2 * 130)
-    assert f(1, 0, 2, 64, 64) == 0
-    assert f(1, 8, 1, 96, 128) == 0 and f(0, 8, 1, 128, 128) == 0
+    assert f(1, 17, 2, 64, 64, 0) == 4 * (ck + 2 * 17 * 2 * 130)
+    # bf16 inputs, chunked form: per head and 64-token chunk the prepare
+    # tiles (33,792 B), T itself (16,384 B) and two dv x dk fp32 states
+    assert f(1, 64, 1, 128, 128, 1) == 33792 + 16384 + 2 * 128 * 128 * 4
+    assert f(2, 65, 3, 64, 128, 1) == 6 * 2 * (33792 + 16384 + 2 * 128 * 64 * 4)
+    assert f(8, 4096, 16, 128, 128, 1) == 8 * 16 * 64 * 181248
+    for dt in (0, 1):
+        assert f(1, 0, 2, 64, 64, dt) == 0
+        assert f(1, 8, 1, 96, 128, dt) == 0 and f(0, 8, 1, 128, 128, dt) == 0
+    assert f(1, 8, 1, 128, 128, 7) == 0
 
 
 def backward(**kw):
@@ -355,6 +363,7 @@ def backward(**kw):
     (dict(dk_=NULL), bd.GDN_EINVAL),
     (dict(k=MIS), bd.GDN_EINVAL),
     (dict(v=ctypes.c_void_p(0x10001)), bd.GDN_EINVAL),
+    (dict(d_o=ctypes.c_void_p(0x10008)), bd.GDN_EINVAL),       # bf16 d_o: 16-byte units
     (dict(S0=MIS), bd.GDN_EINVAL),
     (dict(dS0=MIS), bd.GDN_EINVAL),
     (dict(dST=ctypes.c_void_p(0x10000), dS0=ctypes.c_void_p(0x10100)), bd.GDN_EINVAL),

@@ -2,9 +2,11 @@
 sum <d_o, o> + <dST, S_T> through the gated delta rule with respect to q, k,
 v, alpha, beta and S_0) against the oracle's gdn_backward: every value
 finite, the per-head relative L2 within the fp32 tolerance (1e-3), and each
-token (each state row, for dS_0) within 1e-4 of its head's rms token norm
-(measured errors are ~1e-6, so one wrong element or token fails), at sizes
-that span several
+token (each state row, for dS_0) within a bound of its head's rms token norm:
+1e-4 for fp32 inputs (the recurrent form, measured errors ~1e-7) and 1e-3
+for bf16 inputs (the chunked form: split-bf16 products, measured per-head
+errors ~5e-6 and single-token outliers ~1.3e-4), so one wrong element or
+token fails, at sizes that span several
 checkpoint blocks of 8 tokens with ragged tails, at the batched prefill shape
 B=8, T=4096, H=16 on sampled heads, and for the edge cases (T = 0, T = 1, no
 initial state or state gradient, dS_0 written over dS_T)."""
@@ -21,7 +23,7 @@ from workloads import gdn_inputs as gi
 pytestmark = pytest.mark.gpu
 
 NAMES = ["dq", "dk", "dv", "dalpha", "dbeta", "dS0"]
-TOKEN_TOL = 1e-4
+TOKEN_TOL = {torch.float32: 1e-4, torch.bfloat16: 1e-3}
 
 
 def dev32(a):
@@ -38,7 +40,7 @@ def run(x, d_o, dST, S0="x", **kw):
     return g
 
 
-def compare(label, g, ref, heads=None, tol=TOL_F32):
+def compare(label, g, ref, heads=None, tol=TOL_F32, token_tol=1e-3):
     for i, name in enumerate(NAMES):
         if g.get(name) is None:
             continue
@@ -47,14 +49,14 @@ def compare(label, g, ref, heads=None, tol=TOL_F32):
         if name in ("dalpha", "dbeta"):
             got, want = got[..., None], want[..., None]
         chk = check_S if name == "dS0" else check_o
-        chk(f"{label} {name}", got, want, tol, heads, token_tol=TOKEN_TOL)
+        chk(f"{label} {name}", got, want, tol, heads, token_tol=token_tol)
 
 
 def check(x, d_o, dST, label="", heads=None):
     print(f"  case {label}: {x.q.shape} v{x.v.shape[-1]} {x.dtype}", flush=True)
     g = run(x, d_o, dST)
     ref = orc.gdn_backward(x.q, x.k, x.v, x.alpha, x.beta, x.S0, d_o, dST, heads=heads)
-    compare(label, g, ref, heads)
+    compare(label, g, ref, heads, token_tol=TOKEN_TOL[tdtype(x.dtype)])
     return g
 
 
@@ -133,3 +135,47 @@ def test_backward_batched_shape_sampled_heads(dk):
     ref = orc.gdn_backward(xs.q, xs.k, xs.v, xs.alpha, xs.beta, xs.S0, do_s, dST_s, heads=local)
     gs = {n: (None if g[n] is None else g[n][rows]) for n in NAMES}
     compare(f"B=8 T=4096 dk={dk}", gs, ref, local)
+
+
+@pytest.mark.parametrize("T", [63, 64, 65, 130, 200])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
+def test_backward_chunk_boundaries(T, dk, dv):
+    """bf16 inputs run the chunked form (64-token chunks): lengths around
+    one and several chunk boundaries, ragged last chunks."""
+    x = gi.generic(2, T, 3, dk, dv, 7800 + T + dk + dv, "bf16", S0_scale=0.3)
+    d_o, dST = gi.cotangents(2, T, 3, dk, dv, 7900 + T + dk + dv, "bf16")
+    check(x, d_o, dST, label=f"chunked T={T} dk={dk} dv={dv}")
+
+
+@pytest.mark.parametrize("case", ["beta0", "beta1", "alpha1", "alpha_small", "beta_mixed0"])
+def test_backward_gate_edge_values(case):
+    """Gate values at the ends of their ranges, in the chunked form."""
+    x = gi.generic(1, 150, 3, 128, 128, 8000, "bf16", S0_scale=0.5)
+    d_o, dST = gi.cotangents(1, 150, 3, 128, 128, 8001, "bf16")
+    if case == "beta0":
+        x.beta[:] = 0.0
+    elif case == "beta1":
+        x.beta[:] = 1.0
+    elif case == "alpha1":
+        x.alpha[:] = 1.0
+    elif case == "alpha_small":
+        x.alpha[:] = np.float32(np.exp(-3.0))
+    else:
+        x.beta[:, ::3] = 0.0          # beta = 0 on every third token only
+    check(x, d_o, dST, label=case)
+
+
+def test_backward_dS0_in_place_over_S0():
+    """dS0 written over S0 itself (allowed: S0 is read before dS0 is written)."""
+    x = gi.generic(1, 100, 2, 128, 64, 8100, "bf16", S0_scale=0.5)
+    d_o, dST = gi.cotangents(1, 100, 2, 128, 64, 8101, "bf16")
+    ref = run(x, d_o, dST)
+    d = to_dev(x)
+    s0 = d["S0"].clone()
+    g = gdn.backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], s0,
+                     torch.from_numpy(d_o).to("cuda").to(torch.bfloat16).contiguous(),
+                     dev32(dST), out={"dS0": s0})
+    torch.cuda.synchronize()
+    assert g["dS0"].data_ptr() == s0.data_ptr()
+    for name in NAMES:
+        assert torch.equal(g[name], ref[name]), name
