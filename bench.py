@@ -696,6 +696,11 @@ def main(argv=None):
             backward[f"B8_T4096_dk{dkb}"] = bench_backward(torch, gdn, dev, stream, up, dk=dkb)
         backward["time_dk64_vs_dk128"] = (backward["B8_T4096_dk64"]["us_per_call"] /
                                           backward["B8_T4096_dk128"]["us_per_call"])
+        for dkb in (128, 64):
+            if f"dk{dkb}" in batched:       # the forward prefill at the same shape
+                backward[f"B8_T4096_dk{dkb}"]["time_vs_forward"] = (
+                    backward[f"B8_T4096_dk{dkb}"]["us_per_call"] /
+                    batched[f"dk{dkb}"]["us_per_call"])
 
     # ---------------- segment-truncated prefill, r in {1, 4, 12, 32} ----------
     truncated = {}
@@ -1035,7 +1040,10 @@ def bench_gated_prefill(torch, gdn, dev, stream, up, B=8, T=4096, H=16, dk=64, d
     us = e0.elapsed_time(e1) * 1e3 / calls
     res = {"us_per_call": us, "tokens_per_s": B * T / (us * 1e-6),
            "us_per_token_step": us / T,
-           "bound": "latency of the per-token dependency chain (recurrent form)"}
+           "form": "chunked (bf16 inputs)",
+           "bound": "the two sequential sweeps over the chunks and the chunk kernel's "
+                    "split-bf16 MFMA work; the per-chunk states it stores and reads "
+                    "back are most of its HBM traffic"}
     log(f"generalised-gate prefill B={B} T={T} dk={dk} (recurrent form): {us:.0f} us, "
         f"{res['tokens_per_s'] / 1e6:.2f} M tokens/s, {us / T * 1e3:.0f} ns per token step")
     del q, k, v, al, bg, wg, o, ST
@@ -1047,11 +1055,10 @@ def bench_backward(torch, gdn, dev, stream, up, B=8, T=4096, H=16, dk=128, dv=12
                    calls=3):
     """The backward pass (gradients of q, k, v, alpha, beta and S_0) at the
     batched prefill's shape (d_k = 128, or the pruned 64), bf16 inputs and
-    d_o, fp32 gradients, in
-    recurrent form: bound by the per-token dependency chain, run three
-    times (forward to the checkpoints, forward again inside each block,
-    backward).  Reported as time, tokens/s and the HBM rate of its
-    algorithmic bytes (inputs, d_o, dST and S_0 read once; gradients
+    d_o, fp32 gradients, in chunked form (prepare, forward sweep storing
+    the chunk-start states, reverse chain of the state gradients, chunk-
+    parallel gradients).  Reported as time, tokens/s and the HBM rate of
+    its algorithmic bytes (inputs, d_o, dST and S_0 read once; gradients
     written once)."""
     x = gi.generic(B, T, H, dk, dv, gi.seed_for(4, 9), "bf16", S0_scale=0.3)
     d_o, dST = gi.cotangents(B, T, H, dk, dv, gi.seed_for(4, 10), "bf16")
@@ -1085,13 +1092,16 @@ def bench_backward(torch, gdn, dev, stream, up, B=8, T=4096, H=16, dk=128, dv=12
            "us_per_token_step": us / T, "algorithmic_bytes": nbytes,
            "hbm_frac": nbytes / (us * 1e-6) / HBM_PEAK,
            "workspace_bytes": ws.numel(),
-           "bound": "latency of the per-token dependency chain (recurrent form)"}
+           "form": "chunked (bf16 inputs)",
+           "bound": "the two sequential sweeps over the chunks and the chunk kernel's "
+                    "split-bf16 MFMA work; the per-chunk states it stores and reads "
+                    "back are most of its HBM traffic"}
     # HBM bytes per call from the committed counter runs (checkpoints and
     # partial sums included), and the rate they are moved at
     tr = measured_traffic(f"backward_B8_T4096_dk{dk}")
     res["traffic"] = tr
     res["traffic_GBps"] = None if tr is None else tr / (us * 1e-6) / 1e9
-    log(f"backward B={B} T={T} H={H} dk={dk} (recurrent form): {us:.0f} us, "
+    log(f"backward B={B} T={T} H={H} dk={dk} (chunked form): {us:.0f} us, "
         f"{res['tokens_per_s'] / 1e6:.2f} M tokens/s, {us / T * 1e3:.0f} ns per token step, "
         f"{100 * res['hbm_frac']:.1f} % of HBM for its algorithmic bytes")
     del q, k, v, al, be, S0, d_o, dST, ws, out

@@ -65,6 +65,31 @@ __device__ __forceinline__ void unpack8(const bf16x8& x, float (&f)[8]) {
   for (int e = 0; e < 8; ++e) f[e] = (float)x[e];
 }
 
+// Tiles without row padding (the chunk kernel's LDS has no room for it)
+// are swizzled: element (r, c) of a row-major bf16 tile with row stride ld
+// (a multiple of 64) sits at swz(r, c, ld), the row's 16-byte units
+// permuted by XOR with r & 7.  Operand reads of 16 rows at one column, and
+// the transposing reads of 4 rows, then fall on different banks instead of
+// all on the same ones.  Groups of 4 elements at c % 4 == 0 stay contiguous.
+__device__ __forceinline__ int swz(int r, int c, int ld) {
+  return r * ld + ((((c >> 3) ^ (r & 7)) << 3) | (c & 7));
+}
+__device__ __forceinline__ bf16x8 sw_slots(const bf16* X, int ld, int row, int s, int g4) {
+  const uint2 a = *reinterpret_cast<const uint2*>(&X[swz(row, kslot_base(s, g4, 0), ld)]);
+  const uint2 b = *reinterpret_cast<const uint2*>(&X[swz(row, kslot_base(s, g4, 1), ld)]);
+  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+__device__ __forceinline__ uint2 sw_tr4(const bf16* X, int ld, int r0, int c0, int n) {
+  const int r = r0 + (n >> 2), c = c0 + 4 * (n & 3);
+  const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v_t*)(&X[swz(r, c, ld)]));
+  return __builtin_bit_cast(uint2, v);
+}
+__device__ __forceinline__ bf16x8 sw_slots_tr(const bf16* X, int ld, int c0, int s, int g4, int n) {
+  const uint2 a = sw_tr4(X, ld, kslot_base(s, g4, 0), c0, n);
+  const uint2 b = sw_tr4(X, ld, kslot_base(s, g4, 1), c0, n);
+  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -377,7 +402,8 @@ __global__ __launch_bounds__(64 * (DK > DV ? DK : DV) / 16, 1) void bwd_chunk_ke
     for (int u = tid; u < 4 * C * C / 8; u += NT) {
       const int m = u / (C * C / 8), e = (u - m * (C * C / 8)) * 8;
       const char* src = m < 2 ? tuc + m * C * C * 2 : wsc + (m == 2 ? kWsPh : kWsPl);
-      *reinterpret_cast<uint4*>(&TT[m][e]) = *reinterpret_cast<const uint4*>(src + 2 * e);
+      const int r = e / C;
+      *reinterpret_cast<uint4*>(&TT[m][swz(r, e - r * C, C)]) = *reinterpret_cast<const uint4*>(src + 2 * e);
     }
     if (tid < C) {
       const bool ok = tid < nvalid;
@@ -480,8 +506,8 @@ __global__ __launch_bounds__(64 * (DK > DV ? DK : DV) / 16, 1) void bwd_chunk_ke
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s <= ct / 2; ++s) {
-          const bf16x8 th = lds_slots(TT[0], C, 16 * ct + n, s, g4);
-          const bf16x8 tl = lds_slots(TT[1], C, 16 * ct + n, s, g4);
+          const bf16x8 th = sw_slots(TT[0], C, 16 * ct + n, s, g4);
+          const bf16x8 tl = sw_slots(TT[1], C, 16 * ct + n, s, g4);
           acc = mfma(th, ubh[s], acc);
           acc = mfma(th, ubl[s], acc);
           acc = mfma(tl, ubh[s], acc);
@@ -497,8 +523,8 @@ __global__ __launch_bounds__(64 * (DK > DV ? DK : DV) / 16, 1) void bwd_chunk_ke
 #pragma unroll
       for (int s = ct / 2; s < 2; ++s) {
         const bf16x8 ob = lds_slots_tr(Os, LDO, rw, s, g4, n);
-        acc = mfma(lds_slots_tr(TT[2], C, 16 * ct, s, g4, n), ob, acc);
-        acc = mfma(lds_slots_tr(TT[3], C, 16 * ct, s, g4, n), ob, acc);
+        acc = mfma(sw_slots_tr(TT[2], C, 16 * ct, s, g4, n), ob, acc);
+        acc = mfma(sw_slots_tr(TT[3], C, 16 * ct, s, g4, n), ob, acc);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[e] += dlts[16 * ct + 4 * g4 + e] * Yp[ct][e];
@@ -513,8 +539,8 @@ __global__ __launch_bounds__(64 * (DK > DV ? DK : DV) / 16, 1) void bwd_chunk_ke
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = ct / 2; s < 2; ++s) {
-          const bf16x8 th = lds_slots_tr(TT[0], C, 16 * ct, s, g4, n);
-          const bf16x8 tl = lds_slots_tr(TT[1], C, 16 * ct, s, g4, n);
+          const bf16x8 th = sw_slots_tr(TT[0], C, 16 * ct, s, g4, n);
+          const bf16x8 tl = sw_slots_tr(TT[1], C, 16 * ct, s, g4, n);
           acc = mfma(th, uh[s], acc);
           acc = mfma(th, ul[s], acc);
           acc = mfma(tl, uh[s], acc);
@@ -543,10 +569,10 @@ __global__ __launch_bounds__(64 * (DK > DV ? DK : DV) / 16, 1) void bwd_chunk_ke
         bf16 uh, ul, dh, dl;
         split_bf16(U[ct][e], uh, ul);
         split_bf16(dUb[ct][e], dh, dl);
-        Ub[0][j * DV + rw + n] = uh;
-        Ub[1][j * DV + rw + n] = ul;
-        Ub[2][j * DV + rw + n] = dh;
-        Ub[3][j * DV + rw + n] = dl;
+        Ub[0][swz(j, rw + n, DV)] = uh;
+        Ub[1][swz(j, rw + n, DV)] = ul;
+        Ub[2][swz(j, rw + n, DV)] = dh;
+        Ub[3][swz(j, rw + n, DV)] = dl;
       }
     }
   }
@@ -579,15 +605,15 @@ __global__ __launch_bounds__(64 * (DK > DV ? DK : DV) / 16, 1) void bwd_chunk_ke
     floatx4 acc = {0.f, 0.f, 0.f, 0.f}, kk = acc;
 #pragma unroll
     for (int s = 0; s < NVB; ++s) {
-      const bf16x8 uh = lds_slots(Ub[0], DV, 16 * it + n, s, g4);
-      const bf16x8 ul = lds_slots(Ub[1], DV, 16 * it + n, s, g4);
+      const bf16x8 uh = sw_slots(Ub[0], DV, 16 * it + n, s, g4);
+      const bf16x8 ul = sw_slots(Ub[1], DV, 16 * it + n, s, g4);
       if (kind == 0) {
         const bf16x8 oa = lds_slots(Os, LDO, 16 * jt + n, s, g4);
         acc = mfma(oa, uh, acc);
         acc = mfma(oa, ul, acc);
       } else {
-        const bf16x8 dh = lds_slots(Ub[2], DV, 16 * jt + n, s, g4);
-        const bf16x8 dl = lds_slots(Ub[3], DV, 16 * jt + n, s, g4);
+        const bf16x8 dh = sw_slots(Ub[2], DV, 16 * jt + n, s, g4);
+        const bf16x8 dl = sw_slots(Ub[3], DV, 16 * jt + n, s, g4);
         acc = mfma(dh, uh, acc);
         acc = mfma(dh, ul, acc);
         acc = mfma(dl, uh, acc);
@@ -608,7 +634,7 @@ __global__ __launch_bounds__(64 * (DK > DV ? DK : DV) / 16, 1) void bwd_chunk_ke
       float c, d1, val;
       if (kind == 0) {
         const float dp = (i <= j) ? acc[e] : 0.f;
-        const float p = (float)TT[2][j * C + i] + (float)TT[3][j * C + i];
+        const float p = (float)TT[2][swz(j, i, C)] + (float)TT[3][swz(j, i, C)];
         val = dp * E;
         c = dp * p;
         d1 = 0.f;
@@ -648,14 +674,14 @@ __global__ __launch_bounds__(64 * (DK > DV ? DK : DV) / 16, 1) void bwd_chunk_ke
       const int j = 16 * jt + 4 * g4 + e, i = 16 * it + n;
       bf16 hi, lo;
       split_bf16(tv[it_][e], hi, lo);
-      TT[2 * kind][j * C + i] = hi;
-      TT[2 * kind + 1][j * C + i] = lo;
+      TT[2 * kind][swz(j, i, C)] = hi;
+      TT[2 * kind + 1][swz(j, i, C)] = lo;
     }
   }
   for (int u = tid; u < 4 * 2 * 256; u += NT) {
     const int m = u >> 9, rem = u & 511, tile = rem >> 8, e = rem & 255;
     const int j = 16 * (2 * tile) + (e >> 4), i = 16 * (2 * tile + 1) + (e & 15);
-    TT[m][j * C + i] = (bf16)0.f;
+    TT[m][swz(j, i, C)] = (bf16)0.f;
   }
   __syncthreads();
 
@@ -717,13 +743,13 @@ __global__ __launch_bounds__(64 * (DK > DV ? DK : DV) / 16, 1) void bwd_chunk_ke
         const bf16x8 oa = lds_slots(Os, LDO, 16 * ct + n, s, g4);
         q1 = mfma(oa, sh[s], q1);
         q1 = mfma(oa, sl[s], q1);
-        const bf16x8 uh = lds_slots(Ub[0], DV, 16 * ct + n, s, g4);
-        const bf16x8 ul = lds_slots(Ub[1], DV, 16 * ct + n, s, g4);
+        const bf16x8 uh = sw_slots(Ub[0], DV, 16 * ct + n, s, g4);
+        const bf16x8 ul = sw_slots(Ub[1], DV, 16 * ct + n, s, g4);
         k1 = mfma(uh, dh[s], k1);
         k1 = mfma(uh, dl[s], k1);
         k1 = mfma(ul, dh[s], k1);
-        const bf16x8 bh_ = lds_slots(Ub[2], DV, 16 * ct + n, s, g4);
-        const bf16x8 bl_ = lds_slots(Ub[3], DV, 16 * ct + n, s, g4);
+        const bf16x8 bh_ = sw_slots(Ub[2], DV, 16 * ct + n, s, g4);
+        const bf16x8 bl_ = sw_slots(Ub[3], DV, 16 * ct + n, s, g4);
         k2 = mfma(bh_, sh[s], k2);
         k2 = mfma(bh_, sl[s], k2);
         k2 = mfma(bl_, sh[s], k2);
@@ -732,17 +758,17 @@ __global__ __launch_bounds__(64 * (DK > DV ? DK : DV) / 16, 1) void bwd_chunk_ke
       for (int s = 0; s < 2; ++s) {
         const bf16x8 kt = lds_slots_tr(Ks, LDK, cw, s, g4, n);    // K[kslot][cw + n]
         if (s <= ct / 2) {                                        // lower: dP~ K, dM~ K
-          q2 = mfma(lds_slots(TT[0], C, 16 * ct + n, s, g4), kt, q2);
-          q2 = mfma(lds_slots(TT[1], C, 16 * ct + n, s, g4), kt, q2);
-          k3 = mfma(lds_slots(TT[2], C, 16 * ct + n, s, g4), kt, k3);
-          k3 = mfma(lds_slots(TT[3], C, 16 * ct + n, s, g4), kt, k3);
+          q2 = mfma(sw_slots(TT[0], C, 16 * ct + n, s, g4), kt, q2);
+          q2 = mfma(sw_slots(TT[1], C, 16 * ct + n, s, g4), kt, q2);
+          k3 = mfma(sw_slots(TT[2], C, 16 * ct + n, s, g4), kt, k3);
+          k3 = mfma(sw_slots(TT[3], C, 16 * ct + n, s, g4), kt, k3);
         }
         if (s >= ct / 2) {                                        // upper: dP~^T Q, dM~^T K
           const bf16x8 qt = lds_slots_tr(Qs, LDK, cw, s, g4, n);
-          k3 = mfma(lds_slots_tr(TT[0], C, 16 * ct, s, g4, n), qt, k3);
-          k3 = mfma(lds_slots_tr(TT[1], C, 16 * ct, s, g4, n), qt, k3);
-          k3 = mfma(lds_slots_tr(TT[2], C, 16 * ct, s, g4, n), kt, k3);
-          k3 = mfma(lds_slots_tr(TT[3], C, 16 * ct, s, g4, n), kt, k3);
+          k3 = mfma(sw_slots_tr(TT[0], C, 16 * ct, s, g4, n), qt, k3);
+          k3 = mfma(sw_slots_tr(TT[1], C, 16 * ct, s, g4, n), qt, k3);
+          k3 = mfma(sw_slots_tr(TT[2], C, 16 * ct, s, g4, n), kt, k3);
+          k3 = mfma(sw_slots_tr(TT[3], C, 16 * ct, s, g4, n), kt, k3);
         }
       }
 #pragma unroll
