@@ -52,6 +52,8 @@ SIGNATURES = {
                                 _i, _i, _vp]),
     "gdn_gated_recurrent": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "gdn_gated_prefill_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "gdn_gated_prefill": (_i, [_vp] * 9 + [_i] * 7 + [_vp, _sz, _vp]),
     "gdn_drrqr_select": (_i, [_vp, _i, _i, _i, ctypes.c_double, _i, _vp, _vp, _vp]),
     "gdn_backward_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "gdn_backward": (_i, [_vp] * 14 + [_i] * 6 + [_vp, _sz, _vp]),
@@ -444,6 +446,55 @@ def gated_recurrent(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                  _DTYPE_CODE[q.dtype], _DTYPE_CODE[out_dtype],
                                  _stream_handle(q, stream))
     _check(st, "gdn_gated_recurrent")
+    return o, ST
+
+
+def gated_prefill_workspace_bytes(B: int, T: int, H: int, dk: int, dv: int,
+                                  in_dtype=torch.bfloat16) -> int:
+    return int(lib.gdn_gated_prefill_workspace_bytes(B, T, H, dk, dv, _DTYPE_CODE[in_dtype]))
+
+
+def gated_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  alpha: torch.Tensor, b: torch.Tensor, w: torch.Tensor,
+                  S0: Optional[torch.Tensor] = None, *,
+                  out_dtype: Optional[torch.dtype] = None,
+                  o: Optional[torch.Tensor] = None,
+                  ST: Optional[torch.Tensor] = None,
+                  final_state: bool = True,
+                  workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """The generalised gates over whole sequences in chunked form (bf16
+    inputs; fp32 inputs run the recurrent form); arguments as
+    gated_recurrent, plus an optional uint8 `workspace` of at least
+    gated_prefill_workspace_bytes(...) bytes."""
+    _dev_tensor(q, "q", _DTYPE_CODE)
+    B, T, H, dk = q.shape
+    _dev_tensor(k, "k", (q.dtype,), q.shape)
+    _dev_tensor(v, "v", (q.dtype,))
+    if tuple(v.shape[:3]) != (B, T, H) or v.dim() != 4:
+        raise ValueError(f"v: shape {tuple(v.shape)} incompatible with q")
+    dv = v.shape[3]
+    _dev_tensor(alpha, "alpha", (torch.float32,), (B, T, H, dk))
+    _dev_tensor(b, "b", (torch.float32,), (B, T, H, dk))
+    _dev_tensor(w, "w", (torch.float32,), (B, T, H, dv))
+    if S0 is not None:
+        _dev_tensor(S0, "S0", (torch.float32,), (B, H, dv, dk))
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=q.device)
+    _dev_tensor(o, "o", (out_dtype,), (B, T, H, dv))
+    if ST is None and final_state:
+        ST = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    if ST is not None:
+        _dev_tensor(ST, "ST", (torch.float32,), (B, H, dv, dk))
+    need = gated_prefill_workspace_bytes(B, T, H, dk, dv, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib.gdn_gated_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
+                               _ptr(S0), _ptr(o), _ptr(ST), B, T, H, dk, dv,
+                               _DTYPE_CODE[q.dtype], _DTYPE_CODE[out_dtype],
+                               _ptr(workspace), workspace.numel(), _stream_handle(q, stream))
+    _check(st, "gdn_gated_prefill")
     return o, ST
 
 

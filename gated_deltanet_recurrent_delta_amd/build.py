@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 
-SOURCES = ["gdn_api.hip", "gdn_backward.hip", "gdn_backward_chunk.hip", "gdn_decode.hip", "gdn_gated.hip", "gdn_noalloc.hip",
+SOURCES = ["gdn_api.hip", "gdn_backward.hip", "gdn_backward_chunk.hip", "gdn_decode.hip", "gdn_gated.hip", "gdn_gated_chunk.hip", "gdn_noalloc.hip",
            "gdn_prefill.hip", "gdn_select.hip", "gdn_truncate.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -324,6 +324,35 @@ int gdn_gated_recurrent(const void* q, const void* k, const void* v,
       static_cast<hipStream_t>(stream)));
 }
 
+size_t gdn_gated_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int in_dtype) {
+  if (check_prefill_shape(B, T, H, dk, dv, in_dtype, GDN_F32) != GDN_OK || T == 0) return 0;
+  return in_dtype == GDN_BF16 ? gdn::gated_chunked_ws_bytes(B, T, H, dk) : 0;
+}
+
+int gdn_gated_prefill(const void* q, const void* k, const void* v, const float* alpha,
+                      const float* b, const float* w, const float* S0, void* o, float* ST,
+                      int B, int T, int H, int dk, int dv, int in_dtype, int out_dtype,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_prefill_shape(B, T, H, dk, dv, in_dtype, out_dtype);
+  if (st != GDN_OK) return st;
+  if (in_dtype != GDN_BF16 || T == 0)      // fp32 inputs (and T == 0): the recurrent form
+    return gdn_gated_recurrent(q, k, v, alpha, b, w, S0, o, ST, B, T, H, dk, dv, in_dtype,
+                               out_dtype, stream);
+  if ((S0 && !aligned(S0, 16)) || (ST && !aligned(ST, 16))) return GDN_EINVAL;
+  const size_t nstate = (size_t)B * H * dv * dk;
+  if (ST && S0 && ST != S0 && (ST < S0 + nstate && S0 < ST + nstate))
+    return GDN_EINVAL;                               // partial overlap
+  if (!q || !k || !v || !alpha || !b || !w || !o) return GDN_EINVAL;
+  if (!aligned(q, 2) || !aligned(k, 2) || !aligned(v, 2) || !aligned(alpha, 4) ||
+      !aligned(b, 4) || !aligned(w, 4) || !aligned(o, out_dtype == GDN_BF16 ? 2 : 4))
+    return GDN_EINVAL;
+  if (!workspace || !aligned(workspace, 16)) return GDN_EWORKSPACE;
+  if (workspace_bytes < gdn::gated_chunked_ws_bytes(B, T, H, dk)) return GDN_EWORKSPACE;
+  return to_status(gdn::launch_gated_chunked(q, k, v, alpha, b, w, S0, ST, o, B, T, H, dk, dv,
+                                             out_dtype, workspace,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 size_t gdn_backward_workspace_bytes(int B, int T, int H, int dk, int dv, int in_dtype) {
   if (check_prefill_shape(B, T, H, dk, dv, in_dtype, GDN_F32) != GDN_OK || T == 0) return 0;
   return in_dtype == GDN_BF16 ? gdn::backward_chunked_ws_bytes(B, T, H, dk, dv)

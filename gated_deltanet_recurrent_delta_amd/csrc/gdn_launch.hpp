@@ -174,6 +174,14 @@ hipError_t launch_backward_chunked(const void* q, const void* k, const void* v,
                                    float* dval, float* dalpha, float* dbeta, float* dS0,
                                    int B, int T, int H, int dk, int dv, void* workspace,
                                    hipStream_t stream);
+// The generalised gates in chunked form (bf16 inputs): workspace bytes and
+// the launch (prepare, then the scan).
+size_t gated_chunked_ws_bytes(int B, int T, int H, int dk);
+hipError_t launch_gated_chunked(const void* q, const void* k, const void* v,
+                                const float* alpha, const float* bgate, const float* wgate,
+                                const float* S0, float* ST, void* o, int B, int T, int H,
+                                int dk, int dv, int out_dtype, void* workspace,
+                                hipStream_t stream);
 // The backward pass's forward sweep: the prefill scan storing the state at
 // the start of every chunk (bf16 inputs; ws holds the prepare tiles).
 hipError_t launch_scan_states(const void* k, const void* v, const float* S0,

@@ -270,6 +270,33 @@ int gdn_gated_recurrent(const void* q, const void* k, const void* v,
                         int H, int dk, int dv, int in_dtype, int out_dtype,
                         void* stream);
 
+/*
+ * The same generalised gates over whole sequences in chunked form (64-token
+ * chunks; bf16 inputs).  Inside a chunk the per-key-channel retention enters
+ * through its per-channel cumulative log G_j: the erase and query keys of
+ * token j are weighted by e^{G_j}, the key of token i in the state update by
+ * e^{G_C - G_i}, and the chunk's key-key and query-key products by
+ * e^{G_j - G_i} per channel, formed as products of factors weighted against
+ * a reference token in the middle of each 16-token block; T = (I + A)^{-1}
+ * with A_ji = sum_d b_jd k_jd k_id e^{G_jd - G_id} (i < j).  The products run
+ * on bf16 MFMA with split-bf16 operands and fp32 accumulation.  Retentions
+ * below about 3e-5 per token (log2 < -15) may underflow a weighted factor;
+ * results are untested there.
+ * Arguments and layouts as gdn_gated_recurrent, plus
+ *   workspace   device memory of at least gdn_gated_prefill_workspace_bytes()
+ *               bytes, 16-byte aligned: per head and chunk the T and P tiles
+ *               (32,768 bytes), the weighted keys and queries (6 * 64 * dk * 2
+ *               bytes) and e^{G_C} (dk * 4 bytes).
+ * fp32 inputs (in_dtype GDN_F32) and T == 0 run gdn_gated_recurrent (no
+ * workspace used; the workspace size is then 0).  Errors as gdn_prefill.
+ */
+size_t gdn_gated_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int in_dtype);
+int gdn_gated_prefill(const void* q, const void* k, const void* v,
+                      const float* alpha, const float* b, const float* w,
+                      const float* S0, void* o, float* ST, int B, int T, int H,
+                      int dk, int dv, int in_dtype, int out_dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Backward pass of gdn_prefill's recurrence.
  *

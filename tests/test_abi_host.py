@@ -418,3 +418,38 @@ def test_prefill_noalloc_argument_errors(kw, status):
 
 def test_prefill_noalloc_empty_sequence_without_state_is_a_noop():
     assert prefill_noalloc(T=0, ST=NULL, q=NULL, k=NULL, v=NULL, o=NULL) == bd.GDN_OK
+
+
+def test_gated_prefill_workspace_bytes():
+    f = bd.lib.gdn_gated_prefill_workspace_bytes
+    # per head and 64-token chunk: T/P tiles 32,768 B, six [64][dk] bf16
+    # weighted-key matrices and e^{G_C} (dk fp32)
+    assert f(1, 64, 1, 128, 128, 1) == 32768 + 6 * 64 * 128 * 2 + 128 * 4
+    assert f(2, 65, 3, 64, 128, 1) == 6 * 2 * (32768 + 6 * 64 * 64 * 2 + 64 * 4)
+    assert f(2, 65, 3, 64, 128, 0) == 0              # fp32 inputs: recurrent form
+    assert f(1, 0, 1, 128, 128, 1) == 0 and f(1, 8, 1, 96, 128, 1) == 0
+
+
+def gated_prefill(**kw):
+    a = dict(q=P, k=P, v=P, alpha=P, b=P, w=P, S0=NULL, o=P, ST=P, B=1, T=100, H=2,
+             dk=128, dv=128, in_dtype=1, out_dtype=1, ws=P, ws_bytes=1 << 40, stream=NULL)
+    a.update(kw)
+    return bd.lib.gdn_gated_prefill(a["q"], a["k"], a["v"], a["alpha"], a["b"], a["w"],
+                                    a["S0"], a["o"], a["ST"], a["B"], a["T"], a["H"],
+                                    a["dk"], a["dv"], a["in_dtype"], a["out_dtype"],
+                                    a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), bd.GDN_EINVAL),
+    (dict(dk=96), bd.GDN_ESHAPE),
+    (dict(out_dtype=5), bd.GDN_ESHAPE),
+    (dict(q=NULL), bd.GDN_EINVAL),
+    (dict(w=NULL), bd.GDN_EINVAL),
+    (dict(alpha=ctypes.c_void_p(0x10002)), bd.GDN_EINVAL),
+    (dict(S0=MIS), bd.GDN_EINVAL),
+    (dict(ws=NULL), bd.GDN_EWORKSPACE),
+    (dict(ws_bytes=4096), bd.GDN_EWORKSPACE),
+])
+def test_gated_prefill_argument_errors(kw, status):
+    assert gated_prefill(**kw) == status

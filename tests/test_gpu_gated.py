@@ -120,3 +120,113 @@ def test_gated_zero_initial_state(B, H, T):
     assert x.S0 is None
     al, b, w = gi.gate_vectors(B, T, H, 64, 128, 6900 + B + T)
     check(x, al, b, w, "f32", label=f"S0=None B={B} T={T}")
+
+
+# ---------------------------------------------------------------------------
+# chunked form (gdn_gated_prefill, bf16 inputs)
+# ---------------------------------------------------------------------------
+
+def run_chunked(x, al, b, w, out_dt, S0=None, ST=None):
+    d = to_dev(x)
+    s0 = d["S0"] if S0 is None else S0
+    o, S = gdn.gated_prefill(d["q"], d["k"], d["v"], dev32(al), dev32(b), dev32(w), s0,
+                             out_dtype=tdtype(out_dt), ST=ST)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def check_chunked(x, al, b, w, out_dt=None, label="", heads=None):
+    out_dt = x.dtype if out_dt is None else out_dt
+    print(f"  case chunked {label}: {x.q.shape} out={out_dt}", flush=True)
+    o, S = run_chunked(x, al, b, w, out_dt)
+    o_ref, S_ref = orc.gdn2_prefill(x.q, x.k, x.v, al, b, w, x.S0, heads=heads)
+    tol_o = TOL_F32 if out_dt == "f32" else TOL_BF16
+    check_o(f"{label} o", host(o), o_ref, tol_o, heads)
+    check_S(f"{label} S_T", host(S), S_ref, TOL_F32, heads)
+
+
+@pytest.mark.parametrize("T", [1, 37, 63, 64, 65, 130, 200])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
+@pytest.mark.parametrize("out_dt", ["bf16", "f32"])
+def test_gated_chunked_matches_oracle(T, dk, dv, out_dt):
+    """Ragged chunks and several chunk boundaries, every head size, both
+    output dtypes."""
+    x = gi.generic(2, T, 3, dk, dv, 6500 + T + dk + dv, "bf16", S0_scale=0.3)
+    al, b, w = gi.gate_vectors(2, T, 3, dk, dv, 6600 + T + dk + dv)
+    check_chunked(x, al, b, w, out_dt, label=f"T={T} dk={dk} dv={dv}")
+
+
+@pytest.mark.parametrize("case", ["alpha1", "alpha_small", "alpha_mixed", "b0", "b1", "w0"])
+def test_gated_chunked_gate_edges(case):
+    """Retentions at 1 and down to e^-3 per token (several channels each way
+    in one head), erase gates 0 and 1, write gate 0."""
+    x = gi.generic(1, 150, 3, 128, 128, 6700, "bf16", S0_scale=0.5)
+    al, b, w = gi.gate_vectors(1, 150, 3, 128, 128, 6701)
+    if case == "alpha1":
+        al[:] = 1.0
+    elif case == "alpha_small":
+        al[:] = np.float32(np.exp(-3.0))
+    elif case == "alpha_mixed":
+        al[..., ::2] = np.float32(np.exp(-3.0))
+        al[..., 1::4] = 1.0
+    elif case == "b0":
+        b[:] = 0.0
+    elif case == "b1":
+        b[:] = 1.0
+    else:
+        w[:] = 0.0
+    check_chunked(x, al, b, w, "f32", label=case)
+
+
+def test_gated_chunked_reduces_to_gdn():
+    """b = w = beta 1 and alpha = a 1: the chunked generalised form equals
+    the chunked gated delta rule of gdn_prefill."""
+    x = gi.generic(2, 200, 3, 128, 128, 6800, "bf16", S0_scale=0.3)
+    rep = lambda a, n: np.ascontiguousarray(np.repeat(a[..., None], n, axis=-1), np.float32)
+    al, b, w = rep(x.alpha, 128), rep(x.beta, 128), rep(x.beta, 128)
+    o_g, S_g = run_chunked(x, al, b, w, "f32")
+    d = to_dev(x)
+    o_c, S_c = gdn.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"],
+                           out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, S_ref = orc.gdn_prefill(x.q, x.k, x.v, x.alpha, x.beta, x.S0)
+    check_o("chunked gated o vs oracle", host(o_g), o_ref, TOL_F32)
+    check_S("chunked gated S vs oracle", host(S_g), S_ref, TOL_F32)
+    check_o("chunked gated o vs gdn_prefill", host(o_g), host(o_c), TOL_F32)
+    check_S("chunked gated S vs gdn_prefill", host(S_g), host(S_c), TOL_F32)
+
+
+def test_gated_chunked_batched_shape_sampled_heads():
+    """B=8, T=4096, H=16, dk=64, dv=128 (the benchmark's shape): all heads
+    on the GPU, the oracle on sampled heads."""
+    B, T, H, dk, dv = 8, 4096, 16, 64, 128
+    heads = [(0, 0), (3, 7), (7, 15)]
+    rows = sorted({bb for bb, _ in heads})
+    x = gi.generic(B, T, H, dk, dv, gi.seed_for(4, 11), "bf16")
+    al, b, w = gi.gate_vectors(B, T, H, dk, dv, gi.seed_for(4, 12))
+    o, S = run_chunked(x, al, b, w, "bf16")
+    remap = {bb: i for i, bb in enumerate(rows)}
+    local = [(remap[bb], h) for bb, h in heads]
+    sl = lambda a: a[rows]
+    o_ref, S_ref = orc.gdn2_prefill(sl(x.q), sl(x.k), sl(x.v), sl(al), sl(b), sl(w), None,
+                                    heads=local)
+    check_o("batched o", host(o)[rows], o_ref, TOL_BF16, local)
+    check_S("batched S_T", host(S)[rows], S_ref, TOL_F32, local)
+
+
+def test_gated_chunked_in_place_deterministic_and_fp32_path():
+    x = gi.generic(2, 130, 3, 64, 128, 6900, "bf16", S0_scale=0.4)
+    al, b, w = gi.gate_vectors(2, 130, 3, 64, 128, 6901)
+    d = to_dev(x)
+    o1, S1 = run_chunked(x, al, b, w, "bf16")
+    o2, S2 = run_chunked(x, al, b, w, "bf16")
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    S = d["S0"].clone()
+    o3, S3 = run_chunked(x, al, b, w, "bf16", S0=S, ST=S)
+    assert S3.data_ptr() == S.data_ptr() and torch.equal(S3, S1) and torch.equal(o3, o1)
+    # fp32 inputs take the recurrent form: equal to gdn_gated_recurrent bitwise
+    xf = gi.generic(1, 40, 2, 128, 64, 6902, "f32", S0_scale=0.3)
+    alf, bf, wf = gi.gate_vectors(1, 40, 2, 128, 64, 6903)
+    of, Sf = run_chunked(xf, alf, bf, wf, "f32")
+    orr, Srr = run(xf, alf, bf, wf, "f32")
+    assert torch.equal(of, orr) and torch.equal(Sf, Srr)
