@@ -688,6 +688,9 @@ def main(argv=None):
                 gated[f"decode_B64_dk{dkg}"] = bench_gated_decode(
                     torch, gdn, dev, stream, 64, dkg, min(a.decode_steps, 64), a.layers, up)
         gated["prefill_B8_T4096_dk64"] = bench_gated_prefill(torch, gdn, dev, stream, up)
+        if "dk64" in batched:             # the plain chunked prefill at the same shape
+            gated["prefill_B8_T4096_dk64"]["time_vs_plain_chunked"] = (
+                gated["prefill_B8_T4096_dk64"]["us_per_call"] / batched["dk64"]["us_per_call"])
 
     # ---------------- backward pass (recurrent form) ----------------
     backward = {}
@@ -1017,9 +1020,12 @@ def bench_gated_decode(torch, gdn, dev, stream, B, dk, n_steps, layers, up):
 
 def bench_gated_prefill(torch, gdn, dev, stream, up, B=8, T=4096, H=16, dk=64, dv=128,
                         calls=3):
-    """The generalised gates over whole sequences in recurrent form (the
-    batched prefill's shape at dk = 64).  Its bound is the per-token
-    dependency chain, not HBM: reported as time and tokens/s."""
+    """The generalised gates over whole sequences at the batched prefill's
+    shape (dk = 64): the chunked form (gdn_gated_prefill: prepare, then the
+    scan) and, for comparison, the recurrent form (gdn_gated_recurrent).
+    Reported as time, tokens/s and the HBM rate of the chunked form's
+    algorithmic bytes (q, k, v read and o written in bf16; the three gate
+    tensors read in fp32; the final state written)."""
     x = gi.generic(B, T, H, dk, dv, gi.seed_for(4, 7), "bf16")
     al, bg, wg = gi.gate_vectors(B, T, H, dk, dv, gi.seed_for(4, 8))
     q, k, v, _, _ = up(x)
@@ -1027,26 +1033,35 @@ def bench_gated_prefill(torch, gdn, dev, stream, up, B=8, T=4096, H=16, dk=64, d
     al, bg, wg = (torch.from_numpy(z).to(dev) for z in (al, bg, wg))
     o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
     ST = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.gated_prefill_workspace_bytes(B, T, H, dk, dv), dtype=torch.uint8,
+                     device=dev)
 
-    def call():
-        gdn.gated_recurrent(q, k, v, al, bg, wg, o=o, ST=ST)
-    settle(torch, call, 1)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(calls):
-        call()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / calls
-    res = {"us_per_call": us, "tokens_per_s": B * T / (us * 1e-6),
-           "us_per_token_step": us / T,
-           "form": "chunked (bf16 inputs)",
-           "bound": "the two sequential sweeps over the chunks and the chunk kernel's "
-                    "split-bf16 MFMA work; the per-chunk states it stores and reads "
-                    "back are most of its HBM traffic"}
-    log(f"generalised-gate prefill B={B} T={T} dk={dk} (recurrent form): {us:.0f} us, "
-        f"{res['tokens_per_s'] / 1e6:.2f} M tokens/s, {us / T * 1e3:.0f} ns per token step")
-    del q, k, v, al, bg, wg, o, ST
+    def timed(call):
+        settle(torch, call, 1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(calls):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / calls
+
+    us = timed(lambda: gdn.gated_prefill(q, k, v, al, bg, wg, o=o, ST=ST, workspace=ws))
+    us_rec = timed(lambda: gdn.gated_recurrent(q, k, v, al, bg, wg, o=o, ST=ST))
+    ntok = B * T * H
+    nbytes = ntok * (2 * (2 * dk + 2 * dv) + 4 * (2 * dk + dv)) + B * H * dv * dk * 4
+    res = {"workload": f"B={B}, T={T}, H={H}, dk={dk}, dv={dv}, bf16 q/k/v/o, fp32 "
+                       "per-key-channel retention and erase gate, per-value-channel write gate",
+           "form": "chunked (gdn_gated_prefill, bf16 inputs)",
+           "us_per_call": us, "tokens_per_s": B * T / (us * 1e-6),
+           "algorithmic_bytes": nbytes, "hbm_frac": nbytes / (us * 1e-6) / HBM_PEAK,
+           "workspace_bytes": ws.numel(),
+           "recurrent_us_per_call": us_rec,
+           "speedup_vs_recurrent": us_rec / us}
+    log(f"generalised-gate prefill B={B} T={T} dk={dk}: chunked {us:.0f} us "
+        f"({res['tokens_per_s'] / 1e6:.2f} M tokens/s, {100 * res['hbm_frac']:.1f} % of HBM), "
+        f"recurrent {us_rec:.0f} us")
+    del q, k, v, al, bg, wg, o, ST, ws
     torch.cuda.empty_cache()
     return res
 

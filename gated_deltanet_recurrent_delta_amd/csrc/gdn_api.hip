@@ -343,8 +343,8 @@ int gdn_gated_prefill(const void* q, const void* k, const void* v, const float* 
   if (ST && S0 && ST != S0 && (ST < S0 + nstate && S0 < ST + nstate))
     return GDN_EINVAL;                               // partial overlap
   if (!q || !k || !v || !alpha || !b || !w || !o) return GDN_EINVAL;
-  if (!aligned(q, 2) || !aligned(k, 2) || !aligned(v, 2) || !aligned(alpha, 4) ||
-      !aligned(b, 4) || !aligned(w, 4) || !aligned(o, out_dtype == GDN_BF16 ? 2 : 4))
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 2) || !aligned(alpha, 16) ||
+      !aligned(b, 16) || !aligned(w, 4) || !aligned(o, out_dtype == GDN_BF16 ? 2 : 4))
     return GDN_EINVAL;
   if (!workspace || !aligned(workspace, 16)) return GDN_EWORKSPACE;
   if (workspace_bytes < gdn::gated_chunked_ws_bytes(B, T, H, dk)) return GDN_EWORKSPACE;

@@ -80,14 +80,15 @@ __global__ __launch_bounds__(256) void gated_prepare_kernel(
   constexpr int LKB = DK + 8;          // bf16 row stride of K, Q
   constexpr int LA = C + 1;            // fp32 row stride of A, P, T
   __shared__ float G2[C * LG];         // log2 a, then its prefix over tokens; later T
-  __shared__ float Ef[C * LG];         // e = b * k
+  __shared__ float Ef[C * LG];         // e = b * k; later A
   __shared__ __attribute__((aligned(16))) bf16 Kb[C * LKB];
   __shared__ __attribute__((aligned(16))) bf16 Qb[C * LKB];
-  __shared__ float Am[C * LA];
   __shared__ float Pm[C * LA];
   __shared__ float Wt[16 * 17];
-  static_assert(C * LA <= C * LG, "T fits in the prefix-sum buffer");
-  float* Tm = G2;                      // after the A / P tiles are formed
+  __shared__ float part[4 * DK];       // per-quarter sums of the prefix
+  static_assert(C * LA <= C * LG, "T and A fit in the prefix-sum and e buffers");
+  float* Tm = G2;                      // after the A / P operands are formed
+  float* Am = Ef;                      // likewise
 
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int t0 = chunk * C, nvalid = min(C, T - t0);
@@ -95,30 +96,51 @@ __global__ __launch_bounds__(256) void gated_prepare_kernel(
   const int n = lane & 15, g4 = lane >> 4;
   char* wsc = ws + ((size_t)(b * H + h) * nchunks + chunk) * gated_chunk_bytes(DK);
 
-  // 1. gates and inputs; tokens past the end are identity steps (a = 1,
-  //    b = k = q = 0)
-  for (int u = tid; u < C * DK; u += NT) {
-    const int j = u / DK, d = u - j * DK;
-    float la = 0.f, bb = 0.f, kk = 0.f, qq = 0.f;
+  // 1. gates and inputs, four channels per thread and step; tokens past
+  //    the end are identity steps (a = 1, b = k = q = 0)
+  for (int u = tid; u < C * DK / 4; u += NT) {
+    const int j = u / (DK / 4), d = (u - j * (DK / 4)) * 4;
+    float4 la = make_float4(0.f, 0.f, 0.f, 0.f), bb = la;
+    uint2 kk = make_uint2(0u, 0u), qq = kk;
     if (j < nvalid) {
       const size_t off = (((size_t)b * T + t0 + j) * H + h) * DK + d;
-      la = log2f(alpha[off]);
-      bb = bgate[off];
-      kk = (float)k[off];
-      qq = (float)q[off];
+      const float4 a4 = *reinterpret_cast<const float4*>(alpha + off);
+      la = make_float4(log2f(a4.x), log2f(a4.y), log2f(a4.z), log2f(a4.w));
+      bb = *reinterpret_cast<const float4*>(bgate + off);
+      kk = *reinterpret_cast<const uint2*>(k + off);
+      qq = *reinterpret_cast<const uint2*>(q + off);
     }
-    G2[j * LG + d] = la;
-    Ef[j * LG + d] = bb * kk;
-    Kb[j * LKB + d] = (bf16)kk;
-    Qb[j * LKB + d] = (bf16)qq;
+    const float kf[4] = {bf16lo(kk.x), bf16hi(kk.x), bf16lo(kk.y), bf16hi(kk.y)};
+    G2[j * LG + d] = la.x;
+    G2[j * LG + d + 1] = la.y;
+    G2[j * LG + d + 2] = la.z;
+    G2[j * LG + d + 3] = la.w;
+    Ef[j * LG + d] = bb.x * kf[0];
+    Ef[j * LG + d + 1] = bb.y * kf[1];
+    Ef[j * LG + d + 2] = bb.z * kf[2];
+    Ef[j * LG + d + 3] = bb.w * kf[3];
+    *reinterpret_cast<uint2*>(&Kb[j * LKB + d]) = kk;
+    *reinterpret_cast<uint2*>(&Qb[j * LKB + d]) = qq;
   }
   __syncthreads();
-  if (tid < DK) {                      // inclusive prefix over the tokens
+  // inclusive prefix over the tokens: four quarters of 16 tokens per
+  // channel, then each quarter adds the totals of those before it
+  for (int u = tid; u < 4 * DK; u += NT) {
+    const int d = u % DK, qt = u / DK;
     float g = 0.f;
-    for (int j = 0; j < C; ++j) {
-      g += G2[j * LG + tid];
-      G2[j * LG + tid] = g;
+    for (int j = 16 * qt; j < 16 * qt + 16; ++j) {
+      g += G2[j * LG + d];
+      G2[j * LG + d] = g;
     }
+    part[qt * DK + d] = g;
+  }
+  __syncthreads();
+  for (int u = tid; u < 3 * 16 * DK; u += NT) {
+    const int qt = 1 + u / (16 * DK), rem = u - (qt - 1) * 16 * DK;
+    const int j = 16 * qt + rem / DK, d = rem % DK;
+    float off = 0.f;
+    for (int p = 0; p < qt; ++p) off += part[p * DK + d];
+    G2[j * LG + d] += off;
   }
   __syncthreads();
 
@@ -171,6 +193,7 @@ __global__ __launch_bounds__(256) void gated_prepare_kernel(
       split8(f8(le), leh[s], lel[s]);
       split8(f8(lq), lqh[s], lql[s]);
     }
+    __syncthreads();                   // every read of e is done: A goes over it
     for (int ib = 0; ib <= jb; ++ib) {
       const int i = 16 * ib + n;                     // B-operand column of this lane
       floatx4 aa = {0.f, 0.f, 0.f, 0.f}, pp = aa;
@@ -307,37 +330,70 @@ __global__ __launch_bounds__(256, 1) void gated_scan_kernel(
     }
   }
 
-  for (int chunk = 0; chunk < nchunks; ++chunk) {
+  // The next chunk's tiles and gates are loaded into registers while this
+  // chunk computes, and committed to LDS at the top of the next step.
+  constexpr int NKT = 6 * C * DK / 8 / NT, NTP = 4 * C * C / 8 / NT;
+  static_assert(NKT * NT * 8 == 6 * C * DK && NTP * NT * 8 == 4 * C * C, "whole units per thread");
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // plain 16-byte loads
+  struct {
+    u32x4 kt[NKT], tp[NTP];
+    float lc, w[4][4];
+    bf16 v[4][4];
+  } st;
+  st.lc = 0.f;
+  auto load = [&](int chunk) {
     const int t0 = chunk * C, nvalid = min(C, T - t0);
     const char* wsc = ws + ((size_t)bh * nchunks + chunk) * gated_chunk_bytes(DK);
-    __syncthreads();                   // every read of the last chunk's tiles is done
-    for (int u = tid; u < 6 * C * DK / 8; u += NT) {
+#pragma unroll
+    for (int i = 0; i < NKT; ++i) {
+      const int u = tid + i * NT;
       const int m = u / (C * DK / 8), rem = u - m * (C * DK / 8);
-      const int j = rem / (DK / 8), d0 = (rem - j * (DK / 8)) * 8;
-      *reinterpret_cast<uint4*>(&KT[m][j * LDK + d0]) =
-          *reinterpret_cast<const uint4*>(wsc + kGOffOps + m * MB + (j * DK + d0) * 2);
+      st.kt[i] = *reinterpret_cast<const u32x4*>(wsc + kGOffOps + m * MB + rem * 16);
     }
-    for (int u = tid; u < 4 * C * C / 8; u += NT) {
-      const int m = u / (C * C / 8), rem = u - m * (C * C / 8);
-      const int j = rem / (C / 8), i0 = (rem - j * (C / 8)) * 8;
-      *reinterpret_cast<uint4*>(&TP[m][j * LDT + i0]) =
-          *reinterpret_cast<const uint4*>(wsc + m * (C * C * 2) + (j * C + i0) * 2);
+#pragma unroll
+    for (int i = 0; i < NTP; ++i) {
+      const int u = tid + i * NT;
+      st.tp[i] = *reinterpret_cast<const u32x4*>(wsc + u * 16);
     }
-    if (tid < DK) LC[tid] = reinterpret_cast<const float*>(wsc + kGOffOps + 6 * MB)[tid];
-    // z = w * v at this lane's tokens (c-tile ct: tokens 16 ct + 4 g4 + x)
-    float z[4][4];
+    if (tid < DK) st.lc = reinterpret_cast<const float*>(wsc + kGOffOps + 6 * MB)[tid];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int c = 16 * ct + 4 * g4 + x;
-        float zz = 0.f;
-        if (c < nvalid) {
-          const size_t off = (((size_t)b * T + t0 + c) * H + h) * DV + row;
-          zz = wgate[off] * (float)v[off];
-        }
-        z[ct][x] = zz;
+        const size_t off = (((size_t)b * T + t0 + min(c, nvalid - 1)) * H + h) * DV + row;
+        st.w[ct][x] = c < nvalid ? wgate[off] : 0.f;
+        st.v[ct][x] = c < nvalid ? v[off] : bf16(0.f);
       }
+  };
+  load(0);                             // T >= 1: the entry point returns earlier
+
+  for (int chunk = 0; chunk < nchunks; ++chunk) {
+    const int t0 = chunk * C, nvalid = min(C, T - t0);
+    __syncthreads();                   // every read of the last chunk's tiles is done
+#pragma unroll
+    for (int i = 0; i < NKT; ++i) {
+      const int u = tid + i * NT;
+      const int m = u / (C * DK / 8), rem = u - m * (C * DK / 8);
+      const int j = rem / (DK / 8), d0 = (rem - j * (DK / 8)) * 8;
+      *reinterpret_cast<u32x4*>(&KT[m][j * LDK + d0]) = st.kt[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NTP; ++i) {
+      const int u = tid + i * NT;
+      const int m = u / (C * C / 8), rem = u - m * (C * C / 8);
+      const int j = rem / (C / 8), i0 = (rem - j * (C / 8)) * 8;
+      *reinterpret_cast<u32x4*>(&TP[m][j * LDT + i0]) = st.tp[i];
+    }
+    if (tid < DK) LC[tid] = st.lc;
+    // z = w * v at this lane's tokens (c-tile ct: tokens 16 ct + 4 g4 + x);
+    // w is zero past the end
+    float z[4][4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) z[ct][x] = st.w[ct][x] * (float)st.v[ct][x];
+    if (chunk + 1 < nchunks) load(chunk + 1);
     __syncthreads();
 
     bf16x8 sh[NKB], sl[NKB];

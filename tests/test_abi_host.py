@@ -447,6 +447,10 @@ def gated_prefill(**kw):
     (dict(q=NULL), bd.GDN_EINVAL),
     (dict(w=NULL), bd.GDN_EINVAL),
     (dict(alpha=ctypes.c_void_p(0x10002)), bd.GDN_EINVAL),
+    # gates and keys are read four channels at a time (16-byte units)
+    (dict(alpha=ctypes.c_void_p(0x10008)), bd.GDN_EINVAL),
+    (dict(b=ctypes.c_void_p(0x10004)), bd.GDN_EINVAL),
+    (dict(k=ctypes.c_void_p(0x10008)), bd.GDN_EINVAL),
     (dict(S0=MIS), bd.GDN_EINVAL),
     (dict(ws=NULL), bd.GDN_EWORKSPACE),
     (dict(ws_bytes=4096), bd.GDN_EWORKSPACE),
