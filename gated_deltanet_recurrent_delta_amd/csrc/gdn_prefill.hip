@@ -1085,24 +1085,27 @@ __global__ __launch_bounds__(64 * (DV + DK) / (16 * NH), 1) void scan_wide_kerne
     for (int hf = 0; hf < NH; ++hf)
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) Y[hf][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // the hi parts of the split state are S rounded to bf16: kept for O
+    bf16x8 Sh[NKB][NH];
 #pragma unroll
     for (int s = 0; s < NKB; ++s) {
-      bf16x8 Sh[NH], Sl[NH];
+      bf16x8 Sl[NH];
 #pragma unroll
       for (int hf = 0; hf < NH; ++hf)
-        split8(acc_slots(S[hf][2 * s], S[hf][2 * s + 1]), Sh[hf], Sl[hf]);
+        split8(acc_slots(S[hf][2 * s], S[hf][2 * s + 1]), Sh[s][hf], Sl[hf]);
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         const bf16x8 kh = lds_slots(Ks, LDK, 16 * ct + n, s, g4);
 #pragma unroll
         for (int hf = 0; hf < NH; ++hf) {
-          Y[hf][ct] = mfma(kh, Sh[hf], Y[hf][ct]);
+          Y[hf][ct] = mfma(kh, Sh[s][hf], Y[hf][ct]);
           Y[hf][ct] = mfma(kh, Sl[hf], Y[hf][ct]);
         }
       }
     }
 
     // ---- Z = V - gamma nk Y (beta is in T), as split B operands over c ----
+    const uint32_t vmask = xrows ? 0u : 0xFFFFFFFFu;
     bf16x8 Zh[NH][2], Zl[NH][2];
 #pragma unroll
     for (int hf = 0; hf < NH; ++hf) {
@@ -1110,13 +1113,12 @@ __global__ __launch_bounds__(64 * (DV + DK) / (16 * NH), 1) void scan_wide_kerne
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         const int c = 16 * ct + 4 * g4;
-        // V[c + j][row]; transition rows read column 0 and scale it by 0
+        // V[c + j][row]; transition rows read column 0 and mask it to 0
         // (branch-free, so the read stays in the block the load tracking
         // knows does not touch the buffer being filled)
-        const uint2 vw = lds_tr4(Vs, LDV, c, xrows ? 0 : row0 + 16 * hf, n);
-        const float vs = xrows ? 0.f : 1.f;
-        const float vv[4] = {vs * bf16lo(vw.x), vs * bf16hi(vw.x), vs * bf16lo(vw.y),
-                             vs * bf16hi(vw.y)};
+        const uint2 vr = lds_tr4(Vs, LDV, c, xrows ? 0 : row0 + 16 * hf, n);
+        const uint2 vw = make_uint2(vr.x & vmask, vr.y & vmask);
+        const float vv[4] = {bf16lo(vw.x), bf16hi(vw.x), bf16lo(vw.y), bf16hi(vw.y)};
         const float4 gg = *reinterpret_cast<const float4*>(&Gs[2 * C + c]);   // gamma nk
         Z[ct] = floatx4{vv[0] - gg.x * Y[hf][ct][0], vv[1] - gg.y * Y[hf][ct][1],
                         vv[2] - gg.z * Y[hf][ct][2], vv[3] - gg.w * Y[hf][ct][3]};
@@ -1154,14 +1156,11 @@ __global__ __launch_bounds__(64 * (DV + DK) / (16 * NH), 1) void scan_wide_kerne
         for (int ct = 0; ct < 4; ++ct) OT[hf][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NKB; ++s) {
-        bf16x8 Sb[NH];
-#pragma unroll
-        for (int hf = 0; hf < NH; ++hf) Sb[hf] = to_bf16x8(acc_slots(S[hf][2 * s], S[hf][2 * s + 1]));
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
           const bf16x8 qh = lds_slots(Qs, LDK, 16 * ct + n, s, g4);
 #pragma unroll
-          for (int hf = 0; hf < NH; ++hf) OT[hf][ct] = mfma(Sb[hf], qh, OT[hf][ct]);
+          for (int hf = 0; hf < NH; ++hf) OT[hf][ct] = mfma(Sh[s][hf], qh, OT[hf][ct]);
         }
       }
       bf16x8 Uh[NH][2];
