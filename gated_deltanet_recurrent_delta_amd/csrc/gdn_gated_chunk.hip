@@ -69,7 +69,9 @@ size_t gated_chunked_ws_bytes(int B, int T, int H, int dk) {
 // prepare
 // ===========================================================================
 
-template <int DK>
+// LO: also the lo parts of Q~ and P, which only fp32 outputs use (bf16
+// outputs take single-pass Q~ S^T and P U, as the plain prefill does).
+template <int DK, bool LO>
 __global__ __launch_bounds__(256) void gated_prepare_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k,
     const float* __restrict__ alpha, const float* __restrict__ bgate,
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(256) void gated_prepare_kernel(
       *reinterpret_cast<bf16x8*>(kt + MB + o) = lo;
       split8(f8(c), hi, lo);
       *reinterpret_cast<bf16x8*>(kt + 2 * MB + o) = hi;
-      *reinterpret_cast<bf16x8*>(kt + 3 * MB + o) = lo;
+      if constexpr (LO) *reinterpret_cast<bf16x8*>(kt + 3 * MB + o) = lo;
       split8(f8(e), hi, lo);
       *reinterpret_cast<bf16x8*>(kt + 4 * MB + o) = hi;
       *reinterpret_cast<bf16x8*>(kt + 5 * MB + o) = lo;
@@ -288,7 +290,7 @@ __global__ __launch_bounds__(256) void gated_prepare_kernel(
     *reinterpret_cast<bf16x8*>(wsc + kWsTl + (j * C + i0) * 2) = lo;
     split8(f8(pv), hi, lo);
     *reinterpret_cast<bf16x8*>(wsc + kWsPh + (j * C + i0) * 2) = hi;
-    *reinterpret_cast<bf16x8*>(wsc + kWsPl + (j * C + i0) * 2) = lo;
+    if constexpr (LO) *reinterpret_cast<bf16x8*>(wsc + kWsPl + (j * C + i0) * 2) = lo;
   }
 }
 
@@ -305,8 +307,12 @@ __global__ __launch_bounds__(256, 1) void gated_scan_kernel(
   constexpr int LDK = DK + 8, LDT = C + 8;
   constexpr int NDT = DK / 16, NKB = DK / 32;
   constexpr int MB = C * DK * 2;
+  constexpr bool OPREC = std::is_same<TOut, float>::value;   // fp32 outputs
+  // staged [C][DK] matrices (K~ h/l, Q~ h[/l], K^ h/l) and 64x64 tiles
+  // (T h/l, P h[/l]): bf16 outputs skip the lo parts of Q~ and P
+  constexpr int NKM = OPREC ? 6 : 5, NTM = OPREC ? 4 : 3;
   __shared__ __attribute__((aligned(16))) bf16 KT[6][C * LDK];   // K~ h/l, Q~ h/l, K^ h/l
-  __shared__ __attribute__((aligned(16))) bf16 TP[4][C * LDT];   // T h/l, P h/l
+  __shared__ __attribute__((aligned(16))) bf16 TP[NTM][C * LDT];  // T h/l, P h[/l]
   __shared__ float LC[DK];
 
   int lin = blockIdx.x;
@@ -332,8 +338,11 @@ __global__ __launch_bounds__(256, 1) void gated_scan_kernel(
 
   // The next chunk's tiles and gates are loaded into registers while this
   // chunk computes, and committed to LDS at the top of the next step.
-  constexpr int NKT = 6 * C * DK / 8 / NT, NTP = 4 * C * C / 8 / NT;
-  static_assert(NKT * NT * 8 == 6 * C * DK && NTP * NT * 8 == 4 * C * C, "whole units per thread");
+  constexpr int NKT = NKM * C * DK / 8 / NT, NTP = NTM * C * C / 8 / NT;
+  static_assert(NKT * NT * 8 == NKM * C * DK && NTP * NT * 8 == NTM * C * C,
+                "whole units per thread");
+  // staged matrix m' -> workspace / LDS matrix (bf16 outputs skip Q~ lo)
+  auto kmat = [](int mp) { return OPREC ? mp : mp + (mp >= 3); };
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // plain 16-byte loads
   struct {
     u32x4 kt[NKT], tp[NTP];
@@ -347,8 +356,8 @@ __global__ __launch_bounds__(256, 1) void gated_scan_kernel(
 #pragma unroll
     for (int i = 0; i < NKT; ++i) {
       const int u = tid + i * NT;
-      const int m = u / (C * DK / 8), rem = u - m * (C * DK / 8);
-      st.kt[i] = *reinterpret_cast<const u32x4*>(wsc + kGOffOps + m * MB + rem * 16);
+      const int mp = u / (C * DK / 8), rem = u - mp * (C * DK / 8);
+      st.kt[i] = *reinterpret_cast<const u32x4*>(wsc + kGOffOps + kmat(mp) * MB + rem * 16);
     }
 #pragma unroll
     for (int i = 0; i < NTP; ++i) {
@@ -374,9 +383,9 @@ __global__ __launch_bounds__(256, 1) void gated_scan_kernel(
 #pragma unroll
     for (int i = 0; i < NKT; ++i) {
       const int u = tid + i * NT;
-      const int m = u / (C * DK / 8), rem = u - m * (C * DK / 8);
+      const int mp = u / (C * DK / 8), rem = u - mp * (C * DK / 8);
       const int j = rem / (DK / 8), d0 = (rem - j * (DK / 8)) * 8;
-      *reinterpret_cast<u32x4*>(&KT[m][j * LDK + d0]) = st.kt[i];
+      *reinterpret_cast<u32x4*>(&KT[kmat(mp)][j * LDK + d0]) = st.kt[i];
     }
 #pragma unroll
     for (int i = 0; i < NTP; ++i) {
@@ -409,13 +418,15 @@ __global__ __launch_bounds__(256, 1) void gated_scan_kernel(
         const bf16x8 kh = lds_slots(KT[0], LDK, 16 * ct + n, s, g4);
         const bf16x8 kl = lds_slots(KT[1], LDK, 16 * ct + n, s, g4);
         const bf16x8 qh = lds_slots(KT[2], LDK, 16 * ct + n, s, g4);
-        const bf16x8 ql = lds_slots(KT[3], LDK, 16 * ct + n, s, g4);
+        const bf16x8 ql = OPREC ? lds_slots(KT[3], LDK, 16 * ct + n, s, g4) : bf16x8{};
         y = mfma(kh, sh[s], y);
         y = mfma(kh, sl[s], y);
         y = mfma(kl, sh[s], y);
         oq = mfma(qh, sh[s], oq);
-        oq = mfma(qh, sl[s], oq);
-        oq = mfma(ql, sh[s], oq);
+        if constexpr (OPREC) {
+          oq = mfma(qh, sl[s], oq);
+          oq = mfma(ql, sh[s], oq);
+        }
       }
 #pragma unroll
       for (int x = 0; x < 4; ++x) Z[ct][x] = z[ct][x] - y[x];
@@ -449,10 +460,12 @@ __global__ __launch_bounds__(256, 1) void gated_scan_kernel(
 #pragma unroll
       for (int s = 0; s <= ct / 2; ++s) {
         const bf16x8 ph = lds_slots(TP[2], LDT, 16 * ct + n, s, g4);
-        const bf16x8 pl = lds_slots(TP[3], LDT, 16 * ct + n, s, g4);
         acc = mfma(ph, uh[s], acc);
-        acc = mfma(ph, ul[s], acc);
-        acc = mfma(pl, uh[s], acc);
+        if constexpr (OPREC) {
+          const bf16x8 pl = lds_slots(TP[3], LDT, 16 * ct + n, s, g4);
+          acc = mfma(ph, ul[s], acc);
+          acc = mfma(pl, uh[s], acc);
+        }
       }
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
@@ -496,14 +509,19 @@ hipError_t launch_gated_chunked(const void* q, const void* k, const void* v,
   const int nchunks = (T + C - 1) / C;
   char* ws = static_cast<char*>(workspace);
   const dim3 pgrid(nchunks, H, B);
-  if (dk == 128)
-    hipLaunchKernelGGL((gated_prepare_kernel<128>), pgrid, dim3(256), 0, stream,
-                       static_cast<const bf16*>(q), static_cast<const bf16*>(k), alpha, bgate,
-                       ws, T, H, nchunks);
-  else
-    hipLaunchKernelGGL((gated_prepare_kernel<64>), pgrid, dim3(256), 0, stream,
-                       static_cast<const bf16*>(q), static_cast<const bf16*>(k), alpha, bgate,
-                       ws, T, H, nchunks);
+#define GDN_GPREP(DK_, LO_)                                                                \
+  hipLaunchKernelGGL((gated_prepare_kernel<DK_, LO_>), pgrid, dim3(256), 0, stream,         \
+                     static_cast<const bf16*>(q), static_cast<const bf16*>(k), alpha, bgate, \
+                     ws, T, H, nchunks)
+  const bool lo = out_dtype != 1;          // fp32 outputs read the lo parts of Q~ and P
+  if (dk == 128) {
+    if (lo) GDN_GPREP(128, true);
+    else GDN_GPREP(128, false);
+  } else {
+    if (lo) GDN_GPREP(64, true);
+    else GDN_GPREP(64, false);
+  }
+#undef GDN_GPREP
   const int nblocks = B * H * (dv / 64);
 #define GDN_GSCAN(DK_, TO)                                                                      \
   hipLaunchKernelGGL((gated_scan_kernel<DK_, TO>), dim3(nblocks), dim3(256), 0, stream,         \
