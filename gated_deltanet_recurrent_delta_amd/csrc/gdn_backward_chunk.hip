@@ -143,7 +143,7 @@ __global__ __launch_bounds__(64 * kChainWaves, MINW) void bwd_chain_kernel(
   const bf16* o_seq = dout + ((size_t)b * T * H + h) * DV + r0;
   const size_t tok_k = (size_t)H * DK, tok_v = (size_t)H * DV;
 
-  uint4 sk[UK], sq[UK], so[UV], stp[UTP];
+  u32x4 sk[UK], sq[UK], so[UV], stp[UTP];
   float sg;
   // Rows past the end of the sequence load the last valid row (in bounds);
   // the commit zeroes them.
@@ -153,17 +153,17 @@ __global__ __launch_bounds__(64 * kChainWaves, MINW) void bwd_chain_kernel(
     for (int i = 0; i < UK; ++i) {
       const int u = tid + NT * i, c = u / UPR, cu = u - c * UPR;
       const size_t off = (size_t)(t0 + min(c, nvalid - 1)) * tok_k + cu * 8;
-      sk[i] = *reinterpret_cast<const uint4*>(k_seq + off);
-      sq[i] = *reinterpret_cast<const uint4*>(q_seq + off);
+      sk[i] = *reinterpret_cast<const u32x4*>(k_seq + off);
+      sq[i] = *reinterpret_cast<const u32x4*>(q_seq + off);
     }
 #pragma unroll
     for (int i = 0; i < UV; ++i) {
       const int u = tid + NT * i, c = u / VUPR, cu = u - c * VUPR;
-      so[i] = *reinterpret_cast<const uint4*>(o_seq + (size_t)(t0 + min(c, nvalid - 1)) * tok_v + cu * 8);
+      so[i] = *reinterpret_cast<const u32x4*>(o_seq + (size_t)(t0 + min(c, nvalid - 1)) * tok_v + cu * 8);
     }
     const char* wsc = reinterpret_cast<const char*>(ws) + ((size_t)bh * nchunks + chunk) * kChunkWsFloats * 4;
 #pragma unroll
-    for (int i = 0; i < UTP; ++i) stp[i] = *reinterpret_cast<const uint4*>(wsc + 16 * (tid + NT * i));
+    for (int i = 0; i < UTP; ++i) stp[i] = *reinterpret_cast<const u32x4*>(wsc + 16 * (tid + NT * i));
     sg = (tid < 4 * C) ? reinterpret_cast<const float*>(wsc + kWsG)[tid] : 0.f;
   };
   auto commit = [&](int nvalid) {
@@ -171,21 +171,20 @@ __global__ __launch_bounds__(64 * kChainWaves, MINW) void bwd_chain_kernel(
     for (int i = 0; i < UK; ++i) {
       const int u = tid + NT * i, c = u / UPR, d0 = (u - c * UPR) * 8;
       const uint32_t m = c < nvalid ? 0xFFFFFFFFu : 0u;
-      *reinterpret_cast<uint4*>(&Ks[c * LDK + d0]) = make_uint4(sk[i].x & m, sk[i].y & m, sk[i].z & m, sk[i].w & m);
-      *reinterpret_cast<uint4*>(&Qs[c * LDK + d0]) = make_uint4(sq[i].x & m, sq[i].y & m, sq[i].z & m, sq[i].w & m);
+      *reinterpret_cast<u32x4*>(&Ks[c * LDK + d0]) = sk[i] & m;
+      *reinterpret_cast<u32x4*>(&Qs[c * LDK + d0]) = sq[i] & m;
     }
 #pragma unroll
     for (int i = 0; i < UV; ++i) {
       const int u = tid + NT * i, c = u / VUPR, rr = (u - c * VUPR) * 8;
       const uint32_t m = c < nvalid ? 0xFFFFFFFFu : 0u;
-      *reinterpret_cast<uint4*>(&Os[(rr >> 4) * VBLK + c * LDV + (rr & 15)]) =
-          make_uint4(so[i].x & m, so[i].y & m, so[i].z & m, so[i].w & m);
+      *reinterpret_cast<u32x4*>(&Os[(rr >> 4) * VBLK + c * LDV + (rr & 15)]) = so[i] & m;
     }
 #pragma unroll
     for (int i = 0; i < UTP; ++i) {
       const int u = tid + NT * i, m = u >> 9, rem = u & 511;
       const int j = rem >> 3, i0 = (rem & 7) * 8;
-      *reinterpret_cast<uint4*>(&TPs[m][j * LDT + i0]) = stp[i];
+      *reinterpret_cast<u32x4*>(&TPs[m][j * LDT + i0]) = stp[i];
     }
     if (tid < 4 * C) Gs[tid] = sg;
   };
@@ -345,10 +344,10 @@ __global__ __launch_bounds__(64 * kChainWaves, MINW) void bwd_chain_kernel(
 template <int DK, int DV>
 __global__ __launch_bounds__(64 * (DK > DV ? DK : DV) / 16, 1) void bwd_chunk_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k,
-    const bf16* __restrict__ v, const bf16* __restrict__ dout,
+    const bf16* v, const bf16* __restrict__ dout,
     const float* __restrict__ alpha, const float* __restrict__ beta,
     const float* __restrict__ ws, const char* __restrict__ tu,
-    const float* __restrict__ Sc, const float* __restrict__ dSc,
+    const float* Sc, const float* dSc,
     float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
     float* __restrict__ dalpha, float* __restrict__ dbeta, int T, int H, int nchunks) {
   constexpr int NW = (DK > DV ? DK : DV) / 16;
@@ -376,73 +375,116 @@ __global__ __launch_bounds__(64 * (DK > DV ? DK : DV) / 16, 1) void bwd_chunk_ke
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 15, g4 = lane >> 4;
   const size_t tok0 = (size_t)b * T + t0;               // token row of chunk position 0
-
-  // ---- stage K, Q, dO (zero past the end), T, P; gate rows ----
-  {
-    constexpr int UPK = DK / 8, UPO = DV / 8;
-    for (int u = tid; u < C * UPK; u += NT) {
-      const int c = u / UPK, d0 = (u - c * UPK) * 8;
-      uint4 kx = make_uint4(0u, 0u, 0u, 0u), qx = kx;
-      if (c < nvalid) {
-        const size_t off = ((tok0 + c) * H + h) * DK + d0;
-        kx = *reinterpret_cast<const uint4*>(k + off);
-        qx = *reinterpret_cast<const uint4*>(q + off);
-      }
-      *reinterpret_cast<uint4*>(&Ks[c * LDK + d0]) = kx;
-      *reinterpret_cast<uint4*>(&Qs[c * LDK + d0]) = qx;
-    }
-    for (int u = tid; u < C * UPO; u += NT) {
-      const int c = u / UPO, d0 = (u - c * UPO) * 8;
-      uint4 ox = make_uint4(0u, 0u, 0u, 0u);
-      if (c < nvalid) ox = *reinterpret_cast<const uint4*>(dout + ((tok0 + c) * H + h) * DV + d0);
-      *reinterpret_cast<uint4*>(&Os[c * LDO + d0]) = ox;
-    }
-    const char* wsc = reinterpret_cast<const char*>(ws) + ((size_t)bh * nchunks + chunk) * kChunkWsFloats * 4;
-    const char* tuc = tu + ((size_t)bh * nchunks + chunk) * kTuBytes;
-    for (int u = tid; u < 4 * C * C / 8; u += NT) {
-      const int m = u / (C * C / 8), e = (u - m * (C * C / 8)) * 8;
-      const char* src = m < 2 ? tuc + m * C * C * 2 : wsc + (m == 2 ? kWsPh : kWsPl);
-      const int r = e / C;
-      *reinterpret_cast<uint4*>(&TT[m][swz(r, e - r * C, C)]) = *reinterpret_cast<const uint4*>(src + 2 * e);
-    }
-    if (tid < C) {
-      const bool ok = tid < nvalid;
-      const float a = ok ? alpha[(tok0 + tid) * H + h] : 1.f;
-      const float be = ok ? beta[(tok0 + tid) * H + h] : 0.f;
-      float g = logf(a);
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(g, off, 64);
-        if (lane >= off) g += y;
-      }
-      const float glast = __shfl(g, 63, 64);
-      g2s[tid] = g * kLog2e;
-      gams[tid] = expf(g);
-      dlts[tid] = expf(glast - g);
-      bets[tid] = be;
-      alps[tid] = a;
-    }
-  }
-  __syncthreads();
-
   const float* Sb = Sc + ((size_t)bh * nchunks + chunk) * DV * DK;
   const float* dSb = dSc + ((size_t)bh * nchunks + chunk) * DV * DK;
+
+  // ---- stage K, Q, dO (zero past the end), T, P; gate rows ----
+  // Every load is issued before any LDS write: the tiles into registers,
+  // then phase A's rows of S and dS' (wave w < DV/16: value channels
+  // 16 w + n), so that those arrive while the tiles are written.  Rows past
+  // the end of the sequence load the last valid row and are zeroed here.
+  constexpr int UPK = DK / 8, UPO = DV / 8;
+  constexpr int NKU = C * UPK / NT, NOU = C * UPO / NT, NTU = 4 * C * C / 8 / NT;
+  static_assert(NKU * NT == C * UPK && NOU * NT == C * UPO && NTU * NT * 8 == 4 * C * C,
+                "whole 16-byte units per thread");
+  // token `lane`'s gates, in every wave (identity past the end; loaded
+  // clamped): no load sits under a branch
+  const size_t gi = (tok0 + min(lane, nvalid - 1)) * H + h;
+  const float a_ld = alpha[gi], be_ld = beta[gi];
+  const float a_in = lane < nvalid ? a_ld : 1.f, be_in = lane < nvalid ? be_ld : 0.f;
+  u32x4 rk[NKU], rq[NKU], ro[NOU], rt[NTU];
+  const char* wsc = reinterpret_cast<const char*>(ws) + ((size_t)bh * nchunks + chunk) * kChunkWsFloats * 4;
+  const char* tuc = tu + ((size_t)bh * nchunks + chunk) * kTuBytes;
+#pragma unroll
+  for (int i = 0; i < NKU; ++i) {
+    const int u = tid + NT * i, c = u / UPK, d0 = (u - c * UPK) * 8;
+    const size_t off = ((tok0 + min(c, nvalid - 1)) * H + h) * DK + d0;
+    rk[i] = *reinterpret_cast<const u32x4*>(k + off);
+    rq[i] = *reinterpret_cast<const u32x4*>(q + off);
+  }
+#pragma unroll
+  for (int i = 0; i < NOU; ++i) {
+    const int u = tid + NT * i, c = u / UPO, d0 = (u - c * UPO) * 8;
+    ro[i] = *reinterpret_cast<const u32x4*>(dout + ((tok0 + min(c, nvalid - 1)) * H + h) * DV + d0);
+  }
+#pragma unroll
+  for (int i = 0; i < NTU; ++i) {
+    const int u = tid + NT * i, m = u / (C * C / 8), e = (u - m * (C * C / 8)) * 8;
+    const char* src = m < 2 ? tuc + m * C * C * 2 : wsc + (m == 2 ? kWsPh : kWsPl);
+    rt[i] = *reinterpret_cast<const u32x4*>(src + 2 * e);
+  }
+  // (unconditional, with the row clamped into the state for waves past the
+  // value channels: a load under a branch would make every later wait on
+  // the load counter drain all loads in flight)
+  floatx4 Sr[NDT], Dr[NDT];
+  bf16 vin[4][4];                          // v at this lane's tokens and value channel
+  {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = min(16 * ct + 4 * g4 + e, nvalid - 1);
+        vin[ct][e] = v[((tok0 + j) * H + h) * DV + min(16 * w + n, DV - 1)];
+      }
+    const size_t row = (size_t)min(16 * w + n, DV - 1) * DK;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const float4 a = *reinterpret_cast<const float4*>(Sb + row + 16 * dt + 4 * g4);
+      const float4 c = *reinterpret_cast<const float4*>(dSb + row + 16 * dt + 4 * g4);
+      Sr[dt] = floatx4{a.x, a.y, a.z, a.w};
+      Dr[dt] = floatx4{c.x, c.y, c.z, c.w};
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);       // every load above is issued before the writes below
+  {
+#pragma unroll
+    for (int i = 0; i < NKU; ++i) {
+      const int u = tid + NT * i, c = u / UPK, d0 = (u - c * UPK) * 8;
+      const uint32_t mk = c < nvalid ? 0xFFFFFFFFu : 0u;
+      *reinterpret_cast<u32x4*>(&Ks[c * LDK + d0]) = rk[i] & mk;
+      *reinterpret_cast<u32x4*>(&Qs[c * LDK + d0]) = rq[i] & mk;
+    }
+#pragma unroll
+    for (int i = 0; i < NOU; ++i) {
+      const int u = tid + NT * i, c = u / UPO, d0 = (u - c * UPO) * 8;
+      const uint32_t mk = c < nvalid ? 0xFFFFFFFFu : 0u;
+      *reinterpret_cast<u32x4*>(&Os[c * LDO + d0]) = ro[i] & mk;
+    }
+#pragma unroll
+    for (int i = 0; i < NTU; ++i) {
+      const int u = tid + NT * i, m = u / (C * C / 8), e = (u - m * (C * C / 8)) * 8;
+      const int r = e / C;
+      *reinterpret_cast<u32x4*>(&TT[m][swz(r, e - r * C, C)]) = rt[i];
+    }
+    // inclusive prefix of log alpha over the chunk (lane = token), formed
+    // and stored by every wave alike (the same values to the same slots:
+    // no branch for the compiler to sink the gate loads into)
+    float g = logf(a_in);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(g, off, 64);
+      if (lane >= off) g += y;
+    }
+    const float glast = __shfl(g, 63, 64);
+    const float gam = expf(g), dlt = expf(glast - g);
+    g2s[lane] = g * kLog2e;
+    gams[lane] = gam;
+    dlts[lane] = dlt;
+    bets[lane] = be_in;
+    alps[lane] = a_in;
+  }
+  __syncthreads();
 
   // ===================== phase A: value channels =====================
   if (w < NWV) {
     const int rw = 16 * w;
     floatx4 Y[4], X[4], Yp[4];
     {
-      floatx4 Sr[NDT], Dr[NDT];
       float sc = 0.f;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const float4 a = *reinterpret_cast<const float4*>(Sb + (size_t)(rw + n) * DK + 16 * dt + 4 * g4);
-        const float4 c = *reinterpret_cast<const float4*>(dSb + (size_t)(rw + n) * DK + 16 * dt + 4 * g4);
-        Sr[dt] = floatx4{a.x, a.y, a.z, a.w};
-        Dr[dt] = floatx4{c.x, c.y, c.z, c.w};
-        sc += a.x * c.x + a.y * c.y + a.z * c.z + a.w * c.w;
-      }
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc += Sr[dt][i] * Dr[dt][i];
       sc = wave_sum(sc);
       if (lane == 0) sCw[w] = sc;
       bf16x8 Sh[NKB], Sl[NKB];
@@ -486,7 +528,7 @@ __global__ __launch_bounds__(64 * (DK > DV ? DK : DV) / 16, 1) void bwd_chunk_ke
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = 16 * ct + 4 * g4 + e;
-          const float vv = j < nvalid ? (float)v[((tok0 + j) * H + h) * DV + rw + n] : 0.f;
+          const float vv = j < nvalid ? (float)vin[ct][e] : 0.f;
           Z[ct][e] = vv - gams[j] * Y[ct][e];
         }
       }
@@ -582,15 +624,18 @@ __global__ __launch_bounds__(64 * (DK > DV ? DK : DV) / 16, 1) void bwd_chunk_ke
   // S and dS' columns of this wave's key block for phase D: issued now so
   // that they arrive while the tiles compute.  Lane (n, g4) takes column
   // 16 w + n at the value channels of its k-slots.
+  // (unconditional, the column clamped into the state for waves past the
+  // key columns: no load under a branch)
   float sg[NVB][8], dg[NVB][8];
-  if (w < NWK) {
+  {
+    const int col = min(16 * w + n, DK - 1);
 #pragma unroll
     for (int s = 0; s < NVB; ++s)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int vr = kslot_base(s, g4, e >> 2) + (e & 3);
-        sg[s][e] = Sb[(size_t)vr * DK + 16 * w + n];
-        dg[s][e] = dSb[(size_t)vr * DK + 16 * w + n];
+        sg[s][e] = Sb[(size_t)vr * DK + col];
+        dg[s][e] = dSb[(size_t)vr * DK + col];
       }
   }
   constexpr int kTilesPerWave = (NTILE + NW - 1) / NW;

@@ -12,6 +12,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx8 __attribute__((ext_vector_type(8)));
+// 16 bytes as a native vector: register staging in arrays of these stays in
+// registers (arrays of the uint4 struct are copied with memcpy and can be
+// left in scratch memory)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // conversions

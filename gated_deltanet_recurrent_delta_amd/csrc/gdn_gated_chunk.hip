@@ -343,7 +343,6 @@ __global__ __launch_bounds__(256, 1) void gated_scan_kernel(
                 "whole units per thread");
   // staged matrix m' -> workspace / LDS matrix (bf16 outputs skip Q~ lo)
   auto kmat = [](int mp) { return OPREC ? mp : mp + (mp >= 3); };
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // plain 16-byte loads
   struct {
     u32x4 kt[NKT], tp[NTP];
     float lc, w[4][4];

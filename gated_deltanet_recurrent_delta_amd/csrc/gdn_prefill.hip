@@ -513,8 +513,9 @@ __global__ __launch_bounds__(64) void prepare_kernel(
 
 // Per-thread register staging of one chunk for NT threads.  NTP of the four
 // bf16 64x64 tiles (T hi, T lo, P hi, P lo) are staged: P lo only feeds
-// fp32 outputs.
-template <int DK, typename TIn, int NT, int ROWS, int NTP>
+// fp32 outputs.  U16: the 16-byte unit type (the state-storing sweep takes
+// the native vector, with which its staging stays out of scratch memory).
+template <int DK, typename TIn, int NT, int ROWS, int NTP, typename U16>
 struct Stage {
   static constexpr int UNITS_K = C * DK * (int)sizeof(TIn) / 16 / NT;    // 16B units
   static constexpr int UNITS_TP = NTP * C * C * 2 / 16 / NT;             // T, P tiles
@@ -522,10 +523,10 @@ struct Stage {
   static_assert(UNITS_K * NT * 16 == C * DK * (int)sizeof(TIn), "K staging");
   static_assert(UNITS_TP * NT * 16 == NTP * C * C * 2, "T/P staging");
   static_assert(UNITS_V * NT * 16 == C * ROWS * (int)sizeof(TIn), "V staging");
-  uint4 k[UNITS_K];
-  uint4 q[UNITS_K];
-  uint4 tp[UNITS_TP];
-  uint4 v[UNITS_V];
+  U16 k[UNITS_K];
+  U16 q[UNITS_K];
+  U16 tp[UNITS_TP];
+  U16 v[UNITS_V];
   float g;
 };
 
@@ -555,7 +556,8 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
   constexpr int UPR = DK / EPU;                 // 16B units per K/Q row
   constexpr int VUPR = ROWS / EPU;              // 16B units per V row
   constexpr int NTP = OPREC ? 4 : 3;    // staged T/P tiles
-  using St = Stage<DK, TIn, NT, ROWS, NTP>;
+  using U16 = typename std::conditional<SC, u32x4, uint4>::type;
+  using St = Stage<DK, TIn, NT, ROWS, NTP, U16>;
 
   __shared__ __attribute__((aligned(16))) bf16 Khs[C * LDK];
   __shared__ __attribute__((aligned(16))) bf16 Kls[KEXACT ? 8 : C * LDK];
@@ -607,21 +609,21 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
       const int u = tid + NT * i;
       const int c = u / UPR, cu = u - c * UPR;
       const size_t off = (size_t)(t0 + min(c, nvalid - 1)) * tok_k + cu * EPU;
-      st.k[i] = *reinterpret_cast<const uint4*>(k_seq + off);
-      if constexpr (!SC) st.q[i] = *reinterpret_cast<const uint4*>(q_seq + off);
+      st.k[i] = *reinterpret_cast<const U16*>(k_seq + off);
+      if constexpr (!SC) st.q[i] = *reinterpret_cast<const U16*>(q_seq + off);
     }
 #pragma unroll
     for (int i = 0; i < St::UNITS_V; ++i) {
       const int u = tid + NT * i;
       const int c = u / VUPR, cu = u - c * VUPR;
-      st.v[i] = *reinterpret_cast<const uint4*>(
+      st.v[i] = *reinterpret_cast<const U16*>(
           v_seq + (size_t)(t0 + min(c, nvalid - 1)) * tok_v + cu * EPU);
     }
     const char* wsc = reinterpret_cast<const char*>(ws) +
                       ((size_t)bh * nchunks + chunk) * kChunkWsFloats * 4;
 #pragma unroll
     for (int i = 0; i < St::UNITS_TP; ++i)
-      st.tp[i] = *reinterpret_cast<const uint4*>(wsc + 16 * (tid + NT * i));
+      st.tp[i] = *reinterpret_cast<const U16*>(wsc + 16 * (tid + NT * i));
     st.g = (tid < 4 * C) ? reinterpret_cast<const float*>(wsc + kWsG)[tid] : 0.f;
   };
 
@@ -655,7 +657,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void scan_kernel(
       const int u = tid + NT * i;             // 16B unit of [4][64][64] bf16
       const int m = u >> 9, rem = u & 511;    // 512 units per 64x64 matrix (m < NTP)
       const int j = rem >> 3, i0 = (rem & 7) * 8;
-      *reinterpret_cast<uint4*>(&TPs[m][j * LDT + i0]) = st.tp[i];
+      *reinterpret_cast<U16*>(&TPs[m][j * LDT + i0]) = st.tp[i];
     }
 #pragma unroll
     for (int i = 0; i < St::UNITS_V; ++i) {
