@@ -98,29 +98,39 @@ __global__ __launch_bounds__(256) void gated_prepare_kernel(
   const int n = lane & 15, g4 = lane >> 4;
   char* wsc = ws + ((size_t)(b * H + h) * nchunks + chunk) * gated_chunk_bytes(DK);
 
-  // 1. gates and inputs, four channels per thread and step; tokens past
-  //    the end are identity steps (a = 1, b = k = q = 0)
-  for (int u = tid; u < C * DK / 4; u += NT) {
-    const int j = u / (DK / 4), d = (u - j * (DK / 4)) * 4;
-    float4 la = make_float4(0.f, 0.f, 0.f, 0.f), bb = la;
-    uint2 kk = make_uint2(0u, 0u), qq = kk;
-    if (j < nvalid) {
-      const size_t off = (((size_t)b * T + t0 + j) * H + h) * DK + d;
-      const float4 a4 = *reinterpret_cast<const float4*>(alpha + off);
-      la = make_float4(log2f(a4.x), log2f(a4.y), log2f(a4.z), log2f(a4.w));
-      bb = *reinterpret_cast<const float4*>(bgate + off);
-      kk = *reinterpret_cast<const uint2*>(k + off);
-      qq = *reinterpret_cast<const uint2*>(q + off);
-    }
+  // 1. gates and inputs, four channels per thread and unit; tokens past
+  //    the end are identity steps (a = 1, b = k = q = 0).  Every load is
+  //    issued first, unconditionally (rows clamped to the last token), then
+  //    masked: a load under a branch would make each wait drain them all.
+  constexpr int NU1 = C * DK / 4 / NT;
+  static_assert(NU1 * NT * 4 == C * DK, "whole units per thread");
+  float4 ra[NU1], rb[NU1];
+  uint2 rk[NU1], rq[NU1];
+#pragma unroll
+  for (int i = 0; i < NU1; ++i) {
+    const int u = tid + NT * i, j = u / (DK / 4), d = (u - j * (DK / 4)) * 4;
+    const size_t off = (((size_t)b * T + t0 + min(j, nvalid - 1)) * H + h) * DK + d;
+    ra[i] = *reinterpret_cast<const float4*>(alpha + off);
+    rb[i] = *reinterpret_cast<const float4*>(bgate + off);
+    rk[i] = *reinterpret_cast<const uint2*>(k + off);
+    rq[i] = *reinterpret_cast<const uint2*>(q + off);
+  }
+#pragma unroll
+  for (int i = 0; i < NU1; ++i) {
+    const int u = tid + NT * i, j = u / (DK / 4), d = (u - j * (DK / 4)) * 4;
+    const bool ok = j < nvalid;
+    const uint32_t mk = ok ? 0xFFFFFFFFu : 0u;
+    const uint2 kk = make_uint2(rk[i].x & mk, rk[i].y & mk), qq = make_uint2(rq[i].x & mk, rq[i].y & mk);
+    const float4 a4 = ra[i], b4 = rb[i];
+    const float la[4] = {ok ? log2f(a4.x) : 0.f, ok ? log2f(a4.y) : 0.f,
+                         ok ? log2f(a4.z) : 0.f, ok ? log2f(a4.w) : 0.f};
+    const float bb[4] = {ok ? b4.x : 0.f, ok ? b4.y : 0.f, ok ? b4.z : 0.f, ok ? b4.w : 0.f};
     const float kf[4] = {bf16lo(kk.x), bf16hi(kk.x), bf16lo(kk.y), bf16hi(kk.y)};
-    G2[j * LG + d] = la.x;
-    G2[j * LG + d + 1] = la.y;
-    G2[j * LG + d + 2] = la.z;
-    G2[j * LG + d + 3] = la.w;
-    Ef[j * LG + d] = bb.x * kf[0];
-    Ef[j * LG + d + 1] = bb.y * kf[1];
-    Ef[j * LG + d + 2] = bb.z * kf[2];
-    Ef[j * LG + d + 3] = bb.w * kf[3];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      G2[j * LG + d + x] = la[x];
+      Ef[j * LG + d + x] = bb[x] * kf[x];
+    }
     *reinterpret_cast<uint2*>(&Kb[j * LKB + d]) = kk;
     *reinterpret_cast<uint2*>(&Qb[j * LKB + d]) = qq;
   }
