@@ -191,18 +191,27 @@ COUNTER_LEGS = {
     "batched_qk_norm_dk64": [("prepare_kernel", 64, 0, 64 * 16 * 8 * 64),
                              ("scan_kernel", 64, None, 8 * 16 * 2 * 256)],
     "decode_qk_norm_B64_dk64": [("decode_kernel", 64, 1, 64 * 16 * 8 * 64)],
-    # generalised gates, 16 rows per wave in both: the decode (B=64) and
-    # sequence (B=8) launches differ in grid
+    # generalised gates: the recurrent decode (B=64, 16 rows per wave); the
+    # sequence at B=8 in chunked form (prepare: one 256-thread workgroup per
+    # (b, h, chunk); scan: one per (b, h, 64 state rows)) and, for
+    # comparison, in recurrent form (16 rows per wave)
     "gated_decode_B64_dk128": [("gated_recurrent_kernel", 128, None, 64 * 16 * 8 * 64)],
     "gated_decode_B64_dk64": [("gated_recurrent_kernel", 64, None, 64 * 16 * 8 * 64)],
-    "gated_prefill_B8_T4096_dk64": [("gated_recurrent_kernel", 64, None, 8 * 16 * 8 * 64)],
-    # backward pass at B=8, T=4096, H=16, dk=dv=128: 4 workgroups of 256
-    # threads per head, then one reduction thread per (head, token, partial
-    # element), 2 dk + 2 elements
-    "backward_B8_T4096_dk128": [("backward_kernel", 128, None, 8 * 16 * 4 * 256),
-                                ("backward_reduce_kernel", 128, None, 8 * 16 * 4096 * 258)],
-    "backward_B8_T4096_dk64": [("backward_kernel", 64, None, 8 * 16 * 4 * 256),
-                               ("backward_reduce_kernel", 64, None, 8 * 16 * 4096 * 130)],
+    "gated_prefill_B8_T4096_dk64": [("gated_prepare_kernel", 64, 0, 8 * 16 * 64 * 256),
+                                    ("gated_scan_kernel", 64, None, 8 * 16 * 2 * 256)],
+    "gated_recurrent_B8_T4096_dk64": [("gated_recurrent_kernel", 64, None, 8 * 16 * 8 * 64)],
+    # backward pass at B=8, T=4096, H=16, d_v=128 in chunked form: the
+    # prefill's prepare (same grid as the batched prefill's: count them in
+    # runs of their own), the state-storing scan, the reverse chain (64 rows
+    # per workgroup) and the chunk kernel (8 waves per (b, h, chunk))
+    "backward_B8_T4096_dk128": [("prepare_kernel", 128, 0, 64 * 16 * 8 * 64),
+                                ("scan_kernel", 128, 1, 8 * 16 * 2 * 256),
+                                ("bwd_chain_kernel", 128, None, 8 * 16 * 2 * 256),
+                                ("bwd_chunk_kernel", 128, None, 8 * 16 * 64 * 512)],
+    "backward_B8_T4096_dk64": [("prepare_kernel", 64, 0, 64 * 16 * 8 * 64),
+                               ("scan_kernel", 64, 1, 8 * 16 * 2 * 256),
+                               ("bwd_chain_kernel", 64, None, 8 * 16 * 2 * 256),
+                               ("bwd_chunk_kernel", 64, None, 8 * 16 * 64 * 512)],
 }
 
 
@@ -217,7 +226,7 @@ def _legs_in_run(a):
     if not a.skip_gated:
         if 64 in a.decode_batch:
             legs += ["gated_decode_B64_dk128", "gated_decode_B64_dk64"]
-        legs.append("gated_prefill_B8_T4096_dk64")
+        legs += ["gated_prefill_B8_T4096_dk64", "gated_recurrent_B8_T4096_dk64"]
     if not a.skip_backward:
         legs += ["backward_B8_T4096_dk128", "backward_B8_T4096_dk64"]
     if not a.skip_qk:
@@ -1057,7 +1066,8 @@ def bench_gated_prefill(torch, gdn, dev, stream, up, B=8, T=4096, H=16, dk=64, d
            "algorithmic_bytes": nbytes, "hbm_frac": nbytes / (us * 1e-6) / HBM_PEAK,
            "workspace_bytes": ws.numel(),
            "recurrent_us_per_call": us_rec,
-           "speedup_vs_recurrent": us_rec / us}
+           "speedup_vs_recurrent": us_rec / us,
+           "traffic": measured_traffic("gated_prefill_B8_T4096_dk64")}
     log(f"generalised-gate prefill B={B} T={T} dk={dk}: chunked {us:.0f} us "
         f"({res['tokens_per_s'] / 1e6:.2f} M tokens/s, {100 * res['hbm_frac']:.1f} % of HBM), "
         f"recurrent {us_rec:.0f} us")
@@ -1111,8 +1121,8 @@ def bench_backward(torch, gdn, dev, stream, up, B=8, T=4096, H=16, dk=128, dv=12
            "bound": "the two sequential sweeps over the chunks and the chunk kernel's "
                     "split-bf16 MFMA work; the per-chunk states it stores and reads "
                     "back are most of its HBM traffic"}
-    # HBM bytes per call from the committed counter runs (checkpoints and
-    # partial sums included), and the rate they are moved at
+    # HBM bytes per call from the committed counter runs (the stored chunk
+    # states and state gradients included), and the rate they are moved at
     tr = measured_traffic(f"backward_B8_T4096_dk{dk}")
     res["traffic"] = tr
     res["traffic_GBps"] = None if tr is None else tr / (us * 1e-6) / 1e9
