@@ -167,8 +167,9 @@ def measured_traffic(kernel):
 # prompts (prefills of B=64 or B=1) have other grids and are not counted.
 COUNTER_LEGS = {
     # (kernel, d_k, last template argument or None, grid): the last template
-    # argument is prepare_kernel's gather flag (0, 1) and decode_kernel's
+    # argument is prepare_kernel's gather flag (0, 1), decode_kernel's
     # input-path mode (0 none, 1 norm + scale, 2 channel subset + norm + scale)
+    # and scan_kernel's state-storing flag (1 in the backward pass)
     # 16 heads x 16 segments: scan_wide 512 threads per head-segment,
     # combine 8 row groups x 9 waves per head, correction 15 segments x 10
     # waves per head (a B=1 decode prompt's combine has the same grid: count
@@ -182,14 +183,14 @@ COUNTER_LEGS = {
     "decode_B1_dk128": [("decode_kernel", 128, 0, 16 * 32 * 64)],
     "decode_B1_dk64": [("decode_kernel", 64, 0, 16 * 32 * 64)],
     "batched_dk128": [("prepare_kernel", 128, 0, 64 * 16 * 8 * 64),
-                      ("scan_kernel", 128, None, 8 * 16 * 2 * 256)],
+                      ("scan_kernel", 128, 0, 8 * 16 * 2 * 256)],
     "batched_dk64": [("prepare_kernel", 64, 0, 64 * 16 * 8 * 64),
-                     ("scan_kernel", 64, None, 8 * 16 * 2 * 256)],
+                     ("scan_kernel", 64, 0, 8 * 16 * 2 * 256)],
     "batched_qk_dk64": [("prepare_kernel", 64, 1, 64 * 16 * 8 * 64),
-                        ("scan_kernel", 64, None, 8 * 16 * 2 * 256)],
+                        ("scan_kernel", 64, 0, 8 * 16 * 2 * 256)],
     "decode_qk_B64_dk64": [("decode_kernel", 64, 2, 64 * 16 * 8 * 64)],
     "batched_qk_norm_dk64": [("prepare_kernel", 64, 0, 64 * 16 * 8 * 64),
-                             ("scan_kernel", 64, None, 8 * 16 * 2 * 256)],
+                             ("scan_kernel", 64, 0, 8 * 16 * 2 * 256)],
     "decode_qk_norm_B64_dk64": [("decode_kernel", 64, 1, 64 * 16 * 8 * 64)],
     # generalised gates: the recurrent decode (B=64, 16 rows per wave); the
     # sequence at B=8 in chunked form (prepare: one 256-thread workgroup per
@@ -216,6 +217,7 @@ COUNTER_LEGS = {
 
 
 def _legs_in_run(a):
+    """The legs a run with these flags times, in the order it runs them."""
     legs = []
     if not a.skip_prefill:
         legs.append("prefill")
@@ -223,12 +225,6 @@ def _legs_in_run(a):
         legs += [f"decode_B{b}_dk{d}" for b in a.decode_batch for d in (128, 64)]
     if not a.skip_batched:
         legs += ["batched_dk128", "batched_dk64"]
-    if not a.skip_gated:
-        if 64 in a.decode_batch:
-            legs += ["gated_decode_B64_dk128", "gated_decode_B64_dk64"]
-        legs += ["gated_prefill_B8_T4096_dk64", "gated_recurrent_B8_T4096_dk64"]
-    if not a.skip_backward:
-        legs += ["backward_B8_T4096_dk128", "backward_B8_T4096_dk64"]
     if not a.skip_qk:
         legs.append("batched_qk_dk64")
         if not a.qk_gather_only:
@@ -237,6 +233,12 @@ def _legs_in_run(a):
             legs.append("decode_qk_B64_dk64")
             if not a.qk_gather_only:
                 legs.append("decode_qk_norm_B64_dk64")
+    if not a.skip_gated:
+        if 64 in a.decode_batch:
+            legs += ["gated_decode_B64_dk128", "gated_decode_B64_dk64"]
+        legs += ["gated_prefill_B8_T4096_dk64", "gated_recurrent_B8_T4096_dk64"]
+    if not a.skip_backward:
+        legs += ["backward_B8_T4096_dk128", "backward_B8_T4096_dk64"]
     return legs
 
 
@@ -689,7 +691,7 @@ def main(argv=None):
                     qk[name]["time_vs_plain_dk64"] = (qk[name]["us_per_step"] /
                                                       decode["B64_dk64"]["us_per_step"])
 
-    # ---------------- generalised gates (recurrent form) ----------------
+    # ---------------- generalised gates (chunked and recurrent forms) --------
     gated = {}
     if not a.skip_gated:
         if 64 in a.decode_batch:
@@ -701,7 +703,7 @@ def main(argv=None):
             gated["prefill_B8_T4096_dk64"]["time_vs_plain_chunked"] = (
                 gated["prefill_B8_T4096_dk64"]["us_per_call"] / batched["dk64"]["us_per_call"])
 
-    # ---------------- backward pass (recurrent form) ----------------
+    # ---------------- backward pass (chunked form) ----------------
     backward = {}
     if not a.skip_backward:
         for dkb in (128, 64):

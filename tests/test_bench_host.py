@@ -16,9 +16,11 @@ FIELDS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id",
 
 PREP64 = "_ZN3gdn14prepare_kernelILi64EDF16bLb0EEEvPKT0_S3_PKfS5_PfiiiiNS_6QkArgsE"
 PREP64G = "void gdn::prepare_kernel<64, bool _Accum, bool, E>(bool _Accum const*)"
-SCAN64 = "_ZN3gdn11scan_kernelILi64EDF16bDF16bLi4ELi1EEEvPKT0_S3_S3_PKfPT1_PfS5_iiiii"
+SCAN64 = "_ZN3gdn11scan_kernelILi64EDF16bDF16bLi4ELi1ELb0EEEvPKT0_S3_S3_PKfPT1_PfS5_iiiiiS8_"
 PREP128 = "_ZN3gdn14prepare_kernelILi128EDF16bLb0EEEvPKT0_S3_PKfS5_PfiiiiNS_6QkArgsE"
-SCAN128 = "_ZN3gdn11scan_kernelILi128EDF16bDF16bLi4ELi1EEEvPKT0_S3_S3_PKfPT1_PfS5_iiiii"
+SCAN128 = "_ZN3gdn11scan_kernelILi128EDF16bDF16bLi4ELi1ELb0EEEvPKT0_S3_S3_PKfPT1_PfS5_iiiiiS8_"
+# the state-storing instance the backward pass launches at the same grid
+SCAN128_ST = "_ZN3gdn11scan_kernelILi128EDF16bDF16bLi4ELi1ELb1EEEvPKT0_S3_S3_PKfPT1_PfS5_iiiiiS8_"
 DEC64 = "_ZN3gdn13decode_kernelILi64ELi4EDF16bDF16bLi0EEEvPKT1_S3_S3_PKfS5_S5_PfPT2_iiiiNS_6QkArgsE"
 
 
@@ -71,6 +73,8 @@ def test_counters_attribution_and_calibration(tmp_path):
              for n, g, v in common] + [("__amd_rocclr_copyBuffer", 131072, 524288.0)] * 23
     fetch[7] = (PREP64, 2097152, 9e9)               # the prompt's prepare must not count
     write[7] = (PREP64, 2097152, 9e9)
+    fetch.insert(8, (SCAN128_ST, g_scan, 9e9))      # nor a state-storing scan
+    write.insert(8, (SCAN128_ST, g_scan, 9e9))
     write_csv(tmp_path / "f.csv", "FETCH_SIZE", fetch)
     write_csv(tmp_path / "w.csv", "WRITE_SIZE", write)
     out = tmp_path / "traffic.json"
@@ -95,3 +99,52 @@ def test_counters_refuse_pooled_legs(tmp_path):
         bench.summarize_counters(args(skip_batched=False, skip_qk=False),
                                  str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
                                  out_path=str(tmp_path / "t.json"))
+
+
+def test_trace_legs_split_in_run_order(tmp_path, capsys):
+    # three legs launch prepare_kernel<64, 0> at one grid, in the order the
+    # benchmark runs them (plain batched, the norm-only input path, then the
+    # backward pass), seconds apart, with the gathering input path's
+    # prepare_kernel<64, 1> between the first two; the backward's
+    # state-storing scan must not be taken for the forward scan of the
+    # batched legs
+    import sqlite3
+    SCAN64_ST = SCAN64.replace("Lb0E", "Lb1E")
+    PREP64_G = PREP64.replace("Lb0E", "Lb1E")
+    db = tmp_path / "t.db"
+    con = sqlite3.connect(db)
+    con.execute("create table rocpd_info_kernel_symbol (id integer, kernel_name text)")
+    con.execute("create table rocpd_kernel_dispatch (kernel_id integer, grid_size_x integer, "
+                "grid_size_y integer, grid_size_z integer, start integer, end integer)")
+    for i, n in enumerate((PREP64, SCAN64, SCAN64_ST, PREP64_G)):
+        con.execute("insert into rocpd_info_kernel_symbol values (?, ?)", (i, n))
+    g_prep, g_scan = 64 * 16 * 8 * 64, 8 * 16 * 2 * 256
+    t = 0
+    # (dispatch pairs, prepare kernel id, prepare us, scan kernel id, scan
+    # us) per leg in run order
+    for npair, prep_id, prep_us, scan_id, scan_us in ((5, 0, 60, 1, 180), (2, 3, 140, 1, 185),
+                                                       (4, 0, 70, 1, 190), (3, 0, 95, 2, 210)):
+        for _ in range(npair):
+            con.execute("insert into rocpd_kernel_dispatch values (?, ?, 1, 1, ?, ?)",
+                        (prep_id, g_prep, t, t + prep_us * 1000))
+            t += prep_us * 1000 + 1000
+            con.execute("insert into rocpd_kernel_dispatch values (?, ?, 1, 1, ?, ?)",
+                        (scan_id, g_scan, t, t + scan_us * 1000))
+            t += scan_us * 1000 + 1000
+        t += 5 * 10**9
+    con.commit()
+    con.close()
+    bench.summarize_trace(args(skip_qk=False, skip_backward=False, skip_batched=False,
+                               decode_batch=[1]), str(db))
+    rows = {}
+    for line in capsys.readouterr().out.splitlines()[2:]:
+        c = [x.strip() for x in line.split("|")]
+        rows[(c[1], c[2])] = (int(c[4]), float(c[5]))
+    assert rows[("batched_dk64", "prepare_kernel<64, 0>")] == (5, 60.0)
+    assert rows[("batched_dk64", "scan_kernel<64, 0>")] == (5, 180.0)
+    assert rows[("batched_qk_dk64", "prepare_kernel<64, 1>")] == (2, 140.0)
+    assert rows[("batched_qk_dk64", "scan_kernel<64, 0>")] == (2, 185.0)
+    assert rows[("batched_qk_norm_dk64", "prepare_kernel<64, 0>")] == (4, 70.0)
+    assert rows[("batched_qk_norm_dk64", "scan_kernel<64, 0>")] == (4, 190.0)
+    assert rows[("backward_B8_T4096_dk64", "prepare_kernel<64, 0>")] == (3, 95.0)
+    assert rows[("backward_B8_T4096_dk64", "scan_kernel<64, 1>")] == (3, 210.0)
