@@ -15,24 +15,35 @@
 // columns of a row with 16-byte loads: at dk=64 one wave instruction reads
 // four whole consecutive rows (1 KB), at dk=128 the first or second halves
 // of four rows.  A wave issues its few vector loads (k, q, v) first and then
-// every state load, and reduces and stores each group of four rows as soon
-// as its loads have arrived, so stores start while later rows are still in
-// flight.  The optional input path (per-head channel subset of dk_in-wide
-// q/k rows, L2 normalisation over the kept channels, query scale; "On State
-// Reduction in Linear Attention", paper Sec. 3.2-3.3) is applied to k and q in
-// registers before the row loop.  The two row dot products are reduced with four DPP steps and the
-// state is read and written with non-temporal accesses.
+// every state load.  Two store orders, chosen at launch by the grid:
+//   - streaming: each group of four rows is reduced and stored as soon as
+//     its loads have arrived, so stores start while later rows are still in
+//     flight (dk=128, and small batches);
+//   - paced (dk=64 with at least 16 waves of 32 rows per CU): every row is
+//     formed first, then the wave stores one 1 KB group at a time and waits
+//     for each store to complete before issuing the next.  Measured on
+//     MI355X at B=64, H=16, dv=128 (random states, fresh q/k/v per step),
+//     this keeps 4096 waves' reads ahead of their writes and moves the
+//     32 MiB state 4 % faster than the streaming order (11.8-11.9 against
+//     12.3-12.6 us per step in one job).
+// The optional input path (per-head channel subset of dk_in-wide q/k rows,
+// L2 normalisation over the kept channels, query scale; "On State Reduction
+// in Linear Attention", paper Sec. 3.2-3.3) is applied to k and q in
+// registers before the row loop.  The two row dot products are reduced with
+// four DPP steps and the state is read and written with non-temporal
+// accesses.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
 namespace gdn {
 
-// DK: key width; NG: groups of 4 rows per wave (rows per wave = 4 NG).
+// DK: key width; NG: groups of 4 rows per wave (rows per wave = 4 NG);
+// WPB: waves per workgroup; PACED: the paced store order (see above).
 // QK: the input path of a channel-pruned layer: 0 none (q, k used as
 // given), 1 L2 normalisation (if qa.l2norm) and query scale, 2 the same
 // after keeping the channels qa.chan[h][0 .. DK-1] of dk_in-wide rows.
-template <int DK, int NG, typename TIn, typename TOut, int QK>
-__global__ __launch_bounds__(256) void decode_kernel(
+template <int DK, int NG, int WPB, bool PACED, typename TIn, typename TOut, int QK>
+__global__ __launch_bounds__(64 * WPB) void decode_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, const float* S_in, float* S_out,
@@ -40,7 +51,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
     QkArgs qa) {
   constexpr int F = DK / 64;            // float4 per lane per row
   const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wave = blockIdx.x * WPB + (threadIdx.x >> 6);
   const int head = wave / slices_per_head;
   if (head >= BH) return;
   const int slice = wave - head * slices_per_head;
@@ -126,6 +137,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
           kk[f].w * qq[f].w;
   kq = sum16(kq);
 
+  float ov[NG];
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     float p = 0.f, r = 0.f;
@@ -139,34 +151,59 @@ __global__ __launch_bounds__(256) void decode_kernel(
     p = sum16(p);
     r = sum16(r);
     const float u = b * (vv[g] - a * p);
-    const int row = row0 + 4 * g + rg;
-    float* rowp = S_out + sbase + (size_t)row * DK;
 #pragma unroll
     for (int f = 0; f < F; ++f) {
-      floatx4 n;
-      n[0] = a * s[g][f][0] + u * kk[f].x;
-      n[1] = a * s[g][f][1] + u * kk[f].y;
-      n[2] = a * s[g][f][2] + u * kk[f].z;
-      n[3] = a * s[g][f][3] + u * kk[f].w;
-      __builtin_nontemporal_store(n, reinterpret_cast<floatx4*>(rowp + 64 * f + 4 * sub));
+      s[g][f][0] = a * s[g][f][0] + u * kk[f].x;
+      s[g][f][1] = a * s[g][f][1] + u * kk[f].y;
+      s[g][f][2] = a * s[g][f][2] + u * kk[f].z;
+      s[g][f][3] = a * s[g][f][3] + u * kk[f].w;
     }
-    if (sub == 0) store1(o + (size_t)head * dv + row, a * r + u * kq);
+    ov[g] = a * r + u * kq;
+    if constexpr (!PACED) {
+      const int row = row0 + 4 * g + rg;
+      float* rowp = S_out + sbase + (size_t)row * DK;
+#pragma unroll
+      for (int f = 0; f < F; ++f)
+        __builtin_nontemporal_store(s[g][f],
+                                    reinterpret_cast<floatx4*>(rowp + 64 * f + 4 * sub));
+      if (sub == 0) store1(o + (size_t)head * dv + row, ov[g]);
+    }
+  }
+  if constexpr (PACED) {
+    // every row is formed before the first store: without this barrier the
+    // scheduler moves each group's arithmetic between the waits, and the
+    // step measured 12.3 instead of 11.8 us (B=64, H=16, dk=64, dv=128)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      float* rowp = S_out + sbase + (size_t)(row0 + 4 * g + rg) * DK;
+#pragma unroll
+      for (int f = 0; f < F; ++f) {
+        __builtin_nontemporal_store(s[g][f],
+                                    reinterpret_cast<floatx4*>(rowp + 64 * f + 4 * sub));
+        if (g + 1 < NG || f + 1 < F) wait_vmem();
+      }
+    }
+    if (sub == 0) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) store1(o + (size_t)head * dv + row0 + 4 * g + rg, ov[g]);
+    }
   }
 }
 
-template <int DK, int NG, typename TIn, typename TOut>
+template <int DK, int NG, int WPB, bool PACED, typename TIn, typename TOut>
 static void launch_decode_g(hipStream_t stream, const void* q, const void* k,
                             const void* v, const float* alpha,
                             const float* beta, const float* S_in, float* S_out,
                             void* o, int BH, int H, int dv, const QkArgs& qa) {
   const int slices = dv / (4 * NG);
   const long waves = (long)BH * slices;
-  const dim3 grid((unsigned)((waves + 3) / 4));
-#define GDN_DEC_K(M)                                                               \
-  hipLaunchKernelGGL((decode_kernel<DK, NG, TIn, TOut, M>), grid, dim3(256), 0,     \
-                     stream, static_cast<const TIn*>(q),                           \
-                     static_cast<const TIn*>(k), static_cast<const TIn*>(v),       \
-                     alpha, beta, S_in, S_out, static_cast<TOut*>(o), BH, dv,      \
+  const dim3 grid((unsigned)((waves + WPB - 1) / WPB));
+#define GDN_DEC_K(M)                                                                \
+  hipLaunchKernelGGL((decode_kernel<DK, NG, WPB, PACED, TIn, TOut, M>), grid,        \
+                     dim3(64 * WPB), 0, stream, static_cast<const TIn*>(q),          \
+                     static_cast<const TIn*>(k), static_cast<const TIn*>(v),         \
+                     alpha, beta, S_in, S_out, static_cast<TOut*>(o), BH, dv,        \
                      slices, H, qa)
   if (qa.chan != nullptr) GDN_DEC_K(2);
   else if (qa.l2norm || qa.qscale != 1.f) GDN_DEC_K(1);
@@ -180,31 +217,46 @@ static hipError_t launch_decode_t(const void* q, const void* k, const void* v,
                                   const float* S_in, float* S_out, void* o,
                                   int BH, int H, int dv, const QkArgs& qa,
                                   hipStream_t stream) {
-  // Rows per wave, measured on MI355X at H=16, dv=128 over 18 rotating state
-  // sets (one process, one GPU): at dk=128 four rows per wave is best at every
-  // batch (B=64: 22.9 us per step, against 23.0 with 8 rows and 23.5 with
-  // the 8-lanes-per-row mapping).  At dk=64, 16 rows per wave (4 KB each)
-  // is best while the grid still has kFill such waves, so that every CU is
-  // full from the first dispatch (B=64: 12.57 us, against 12.75 with 8 rows
-  // and 13.4 with 4); with few heads, 4 rows per wave gives the most waves
-  // (B=1: 2.13 us, against 2.36 with 16 rows).
+  // Rows per wave and store order, measured on MI355X at H=16, dv=128 over
+  // 18 rotating state sets (one process, one GPU):
+  //   - dk=128: four rows per wave, streaming stores, at every batch (B=64:
+  //     22.7 us per step; 22.8 with the paced order, 23.3 with 8 rows
+  //     paced, 23.5 with the 8-lanes-per-row mapping).
+  //   - dk=64 with at least kPaced waves of 32 rows: the paced order, one
+  //     wave per workgroup.  B=64 with zero-filled buffers: 11.70 us, against
+  //     11.78 / 11.84 with 2 / 4 waves per workgroup, 12.55 for the same
+  //     layout without the waits, 12.7 waiting after every second store,
+  //     13.2 paced with 16 rows per wave, 14.0 with each XCD taking a
+  //     contiguous eighth of the rows, and 12.22 for the streaming order
+  //     with 16 rows per wave below.  With random states and fresh q/k/v
+  //     per step: 11.8-11.9 us against 12.5-12.6 for the streaming order.
+  //   - dk=64 with kFill waves of 16 rows: streaming, 16 rows per wave,
+  //     so that every CU is full from the first dispatch; else 8 rows under
+  //     the same test; else 4 rows, which gives the most waves at small
+  //     batches (B=1: 2.13 us, against 2.36 with 16 rows).
+  constexpr long kPaced = 4096;         // 16 resident waves on each of 256 CUs
   constexpr long kFill = 8192;          // 32 resident waves on each of 256 CUs
-  // dv is 64 or 128 (checked by the entry point), so 4, 8 and 16 rows
+  // dv is 64 or 128 (checked by the entry point), so 4, 8, 16 and 32 rows
   // divide it.
   if constexpr (DK == 64) {
+    if ((long)BH * dv / 32 >= kPaced) {
+      launch_decode_g<DK, 8, 1, true, TIn, TOut>(stream, q, k, v, alpha, beta, S_in,
+                                                 S_out, o, BH, H, dv, qa);
+      return hipGetLastError();
+    }
     if ((long)BH * dv / 16 >= kFill) {
-      launch_decode_g<DK, 4, TIn, TOut>(stream, q, k, v, alpha, beta, S_in,
-                                        S_out, o, BH, H, dv, qa);
+      launch_decode_g<DK, 4, 4, false, TIn, TOut>(stream, q, k, v, alpha, beta, S_in,
+                                                  S_out, o, BH, H, dv, qa);
       return hipGetLastError();
     }
     if ((long)BH * dv / 8 >= kFill) {
-      launch_decode_g<DK, 2, TIn, TOut>(stream, q, k, v, alpha, beta, S_in,
-                                        S_out, o, BH, H, dv, qa);
+      launch_decode_g<DK, 2, 4, false, TIn, TOut>(stream, q, k, v, alpha, beta, S_in,
+                                                  S_out, o, BH, H, dv, qa);
       return hipGetLastError();
     }
   }
-  launch_decode_g<DK, 1, TIn, TOut>(stream, q, k, v, alpha, beta, S_in, S_out,
-                                    o, BH, H, dv, qa);
+  launch_decode_g<DK, 1, 4, false, TIn, TOut>(stream, q, k, v, alpha, beta, S_in, S_out,
+                                              o, BH, H, dv, qa);
   return hipGetLastError();
 }
 

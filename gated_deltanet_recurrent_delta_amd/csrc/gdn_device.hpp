@@ -102,6 +102,13 @@ __device__ __forceinline__ float load1(const float* p) { return *p; }
 __device__ __forceinline__ void store1(bf16* p, float x) { *p = (bf16)x; }
 __device__ __forceinline__ void store1(float* p, float x) { *p = x; }
 
+// Wait until every vector-memory access this wave has issued is complete:
+// s_waitcnt vmcnt(0), with the export and LDS/scalar counters left alone
+// (simm16 fields on gfx9-family parts: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8).  On gfx950 the vector-memory counter also counts
+// stores, so this paces a wave's stores one at a time.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // ---------------------------------------------------------------------------
 // MFMA: D(16x16, f32) += A(16x32, bf16) * B(32x16, bf16)
 //   A: lane l holds row (l % 16), 8 k-values in "slot" order j = 0..7

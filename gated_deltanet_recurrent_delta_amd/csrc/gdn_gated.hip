@@ -23,9 +23,12 @@
 // tokens are not drained by the compiler's wait for a store.  T == 1 is the
 // decode step: a single streaming pass over the state, HBM-bound like the
 // plain decode kernel; it runs the P = 1 instance, whose small register
-// footprint keeps many waves (and bytes) in flight.  For long sequences
-// this form is bound by the per-token latency of the dependent chain (it
-// has no chunked, MFMA form yet).
+// footprint keeps many waves (and bytes) in flight, and at dk=64 with
+// enough waves it paces its state stores as the plain decode kernel does
+// (every row formed first, then one store at a time, each waited for).
+// Sequences of bf16 inputs have a chunked form (gdn_gated_chunk.hip); this
+// recurrent form serves fp32 inputs and is bound by the per-token latency
+// of the dependent chain.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -45,9 +48,11 @@ struct TokIn {
 // rows per wave (the token's key-side inputs are loaded once for all of
 // them); HAS_S0: an initial state is given (a compile-time choice keeps the
 // state loads out of a branch, after which the compiler's waits would drain
-// every load in flight).
-template <int DK, int P, int NG, bool HAS_S0, typename TIn, typename TOut>
-__global__ __launch_bounds__(256) void gated_recurrent_kernel(
+// every load in flight); WPB: waves per workgroup; PACED: the final state is
+// stored one 1 KB group at a time, each store waited for.
+template <int DK, int P, int NG, bool HAS_S0, typename TIn, typename TOut, int WPB = 4,
+          bool PACED = false>
+__global__ __launch_bounds__(64 * WPB) void gated_recurrent_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ bgate, const float* __restrict__ wgate,
@@ -55,7 +60,7 @@ __global__ __launch_bounds__(256) void gated_recurrent_kernel(
     int dv) {
   constexpr int F = DK / 64;            // float4 per lane per row
   const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wave = blockIdx.x * WPB + (threadIdx.x >> 6);
   const int slices = dv / (4 * NG);
   const int head = wave / slices;
   if (head >= BH) return;
@@ -168,18 +173,25 @@ __global__ __launch_bounds__(256) void gated_recurrent_kernel(
   }
 
   if (ST != nullptr) {
+    // paced: nothing of the arithmetic is scheduled between the waits
+    if constexpr (PACED) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const size_t srow = ((size_t)head * dv + row0 + 4 * g) * DK;
 #pragma unroll
-      for (int f = 0; f < F; ++f)
+      for (int f = 0; f < F; ++f) {
         __builtin_nontemporal_store(s[g][f],
                                     reinterpret_cast<floatx4*>(ST + srow + 64 * f + 4 * sub));
+        if constexpr (PACED) {
+          if (g + 1 < NG || f + 1 < F) wait_vmem();
+        }
+      }
     }
   }
 }
 
 constexpr long kSimds = 1024;   // 256 CUs x 4 SIMDs
+constexpr long kPaced = 4096;   // 16 resident waves on each of 256 CUs
 
 hipError_t launch_gated_recurrent(const void* q, const void* k, const void* v,
                                   const float* alpha, const float* bgate,
@@ -187,31 +199,44 @@ hipError_t launch_gated_recurrent(const void* q, const void* k, const void* v,
                                   void* o, int B, int T, int H, int dk, int dv,
                                   int in_dtype, int out_dtype, hipStream_t stream) {
   const int BH = B * H;
-  // T == 1 (decode): 16 rows per wave, so a token's key-side inputs (k, q
-  // and the two per-channel gates) are read once per 16 rows.  Longer
+  // T == 1 (decode), measured at B=64, H=16, dv=128 over 18 rotating random
+  // state sets with fresh inputs per step: at dk=64, 32 rows per wave with
+  // paced stores and one wave per workgroup once the grid has kPaced such
+  // waves (11.74 us per step, against 11.87 with 4 waves per workgroup,
+  // 12.73 for the same layout unpaced and 13.42 for 16 unpaced rows per
+  // wave); else 16 rows per wave.  At dk=128, 8 rows per wave (24.15 us,
+  // against 25.0 with 16, 27.6 with 4, and 25.2-25.3 paced with 8 or 16).
+  // A token's key-side inputs (k, q and the two per-channel gates) are read
+  // once per wave, i.e. once per 8-32 rows.  Longer
   // sequences: a ring of 4 tokens in flight (at B=8, T=4096, dk=64, 4 rows
   // per wave: 2.8 ms against 3.7 ms with 2), and as many rows per wave as
   // still leave one wave per SIMD: the sequence form is bound by VALU issue,
   // and the per-token work shared by a wave's rows (k.q, b * k, the
   // addresses and conversions) is then spread over more rows (same shape:
   // 2.68 ms with 4 rows, 1.67 ms with 8, 1.64 ms with 16 per wave).
-#define GDN_GATED_K(DK, P, NG, S0_, TI, TO)                                                  \
-  hipLaunchKernelGGL((gated_recurrent_kernel<DK, P, NG, S0_, TI, TO>),                       \
-                     dim3((unsigned)(((long)BH * (dv / (4 * NG)) + 3) / 4)), dim3(256), 0,   \
-                     stream, static_cast<const TI*>(q), static_cast<const TI*>(k),           \
-                     static_cast<const TI*>(v), alpha, bgate, wgate, S0, ST,                  \
+#define GDN_GATED_K(DK, P, NG, S0_, TI, TO, W, PC)                                            \
+  hipLaunchKernelGGL((gated_recurrent_kernel<DK, P, NG, S0_, TI, TO, W, PC>),                 \
+                     dim3((unsigned)(((long)BH * (dv / (4 * NG)) + W - 1) / W)), dim3(64 * W), \
+                     0, stream, static_cast<const TI*>(q), static_cast<const TI*>(k),          \
+                     static_cast<const TI*>(v), alpha, bgate, wgate, S0, ST,                   \
                      static_cast<TO*>(o), BH, H, T, dv)
-#define GDN_GATED_P(DK, P, NG, TI, TO)                          \
-  do {                                                          \
-    if (S0 != nullptr) GDN_GATED_K(DK, P, NG, true, TI, TO);    \
-    else GDN_GATED_K(DK, P, NG, false, TI, TO);                 \
+#define GDN_GATED_P(DK, P, NG, TI, TO, W, PC)                          \
+  do {                                                                 \
+    if (S0 != nullptr) GDN_GATED_K(DK, P, NG, true, TI, TO, W, PC);    \
+    else GDN_GATED_K(DK, P, NG, false, TI, TO, W, PC);                 \
   } while (0)
-#define GDN_GATED(DK, TI, TO)                                    \
-  do {                                                           \
-    if (T == 1) GDN_GATED_P(DK, 1, 4, TI, TO);                   \
-    else if ((long)BH * dv / 16 >= kSimds) GDN_GATED_P(DK, 4, 4, TI, TO); \
-    else if ((long)BH * dv / 8 >= kSimds) GDN_GATED_P(DK, 4, 2, TI, TO);  \
-    else GDN_GATED_P(DK, 4, 1, TI, TO);                          \
+#define GDN_GATED(DK, TI, TO)                                                                 \
+  do {                                                                                        \
+    if (T == 1) {                                                                             \
+      if constexpr (DK == 64) {                                                               \
+        if ((long)BH * dv / 32 >= kPaced) GDN_GATED_P(DK, 1, 8, TI, TO, 1, true);            \
+        else GDN_GATED_P(DK, 1, 4, TI, TO, 4, false);                                        \
+      } else {                                                                                \
+        GDN_GATED_P(DK, 1, 2, TI, TO, 4, false);                                              \
+      }                                                                                       \
+    } else if ((long)BH * dv / 16 >= kSimds) GDN_GATED_P(DK, 4, 4, TI, TO, 4, false);        \
+    else if ((long)BH * dv / 8 >= kSimds) GDN_GATED_P(DK, 4, 2, TI, TO, 4, false);           \
+    else GDN_GATED_P(DK, 4, 1, TI, TO, 4, false);                                            \
   } while (0)
   const bool ib = in_dtype == 1, ob = out_dtype == 1;
   if (dk == 128) {

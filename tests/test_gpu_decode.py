@@ -24,9 +24,31 @@ def one_step_inputs(B, H, dk, dv, dtype, seed, S_scale=0.5):
                                           ("bf16", "f32")])
 def test_decode_matches_oracle(B, H, dk, dv, in_dt, out_dt):
     """One step against the oracle.  At dk=64 the launch picks the rows per
-    wave from the number of heads: B=3 runs 4-row waves, B=64 with dv=64
-    8-row waves and B=64 with dv=128 16-row waves, so all three are covered."""
+    wave and the store order from the number of waves: B=3 runs 4-row waves,
+    B=64 with dv=64 8-row waves and B=64 with dv=128 32-row waves with paced
+    stores, so all three are covered."""
     x = one_step_inputs(B, H, dk, dv, in_dt, seed=1000 + dk + dv + B)
+    d = to_dev(x)
+    o, S1 = gdn.decode_step(d["q"][:, 0].contiguous(), d["k"][:, 0].contiguous(),
+                            d["v"][:, 0].contiguous(), d["alpha"][:, 0].contiguous(),
+                            d["beta"][:, 0].contiguous(), d["S0"],
+                            out_dtype=tdtype(out_dt))
+    torch.cuda.synchronize()
+    o_ref, S_ref = orc.gdn_decode_step(x.q[:, 0], x.k[:, 0], x.v[:, 0],
+                                       x.alpha[:, 0], x.beta[:, 0], x.S0)
+    tol_o = TOL_F32 if out_dt == "f32" else TOL_BF16
+    check_step("o", host(o), o_ref, tol_o)
+    check_S("S'", host(S1), S_ref, TOL_F32)
+
+
+@pytest.mark.parametrize("B,H,dv", [(96, 16, 128), (128, 16, 64), (40, 8, 128)])
+@pytest.mark.parametrize("in_dt,out_dt", [("bf16", "bf16"), ("f32", "f32")])
+def test_decode_dk64_layouts(B, H, dv, in_dt, out_dt):
+    """dk=64 at the grid sizes around the paced 32-row layout: more paced
+    waves than one per head slice of a B=64 step (B=96), the paced layout
+    with dv=64 (B=128), and a smaller batch that takes 4-row waves (B=40,
+    H=8: 1280 waves of 32 rows would be too few)."""
+    x = one_step_inputs(B, H, 64, dv, in_dt, seed=2000 + B + dv)
     d = to_dev(x)
     o, S1 = gdn.decode_step(d["q"][:, 0].contiguous(), d["k"][:, 0].contiguous(),
                             d["v"][:, 0].contiguous(), d["alpha"][:, 0].contiguous(),

@@ -57,11 +57,21 @@ def test_gated_long_sequence_fp32_out():
 
 
 def test_gated_decode_batch64():
-    """T = 1 over B=64, H=16 carried states: the decode step."""
+    """T = 1 over B=64, H=16 carried states: the decode step (8 rows per
+    wave at dk=128; 32 rows per wave with paced stores at dk=64)."""
     for dk in (128, 64):
         x = gi.generic(64, 1, 16, dk, 128, 6300 + dk, "bf16", S0_scale=0.5)
         al, b, w = gi.gate_vectors(64, 1, 16, dk, 128, 6301 + dk)
         check(x, al, b, w, label=f"decode B=64 dk={dk}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_gated_decode_paced_dv64(dt):
+    """The paced dk=64 decode layout with dv=64 (two 32-row slices per head,
+    B=128) and, with dt f32, fp32 inputs and outputs."""
+    x = gi.generic(128, 1, 16, 64, 64, 6350, dt, S0_scale=0.5)
+    al, b, w = gi.gate_vectors(128, 1, 16, 64, 64, 6351)
+    check(x, al, b, w, label=f"decode B=128 dk=64 dv=64 {dt}")
 
 
 def test_kda_and_gdn_reductions_match_chunked_prefill():
