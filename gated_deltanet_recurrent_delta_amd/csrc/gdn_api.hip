@@ -409,7 +409,7 @@ int gdn_drrqr_select(const double* M, int rows, int n, int k, double f,
 
 size_t gdn_truncate_workspace_bytes(int BH, int dv, int dk) {
   if (BH <= 0 || !dims_ok(dk, dv)) return 0;
-  return (size_t)BH * (dv < dk ? dv : dk) * dv * sizeof(float);
+  return (size_t)BH * (dv < dk ? dv : dk) * dv * sizeof(double);
 }
 
 int gdn_truncate_rank(float* S, int BH, int dv, int dk, int r, float* er_out,
@@ -425,7 +425,7 @@ int gdn_truncate_rank(float* S, int BH, int dv, int dk, int r, float* er_out,
       return GDN_EWORKSPACE;
   }
   return to_status(gdn::launch_truncate(
-      S, BH, dv, dk, r, er_out, static_cast<float*>(workspace),
+      S, BH, dv, dk, r, er_out, static_cast<double*>(workspace),
       static_cast<hipStream_t>(stream)));
 }
 

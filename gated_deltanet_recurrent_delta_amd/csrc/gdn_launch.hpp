@@ -135,9 +135,9 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v,
 
 // Rank-r truncation S <- U_r U_r^T S of BH states [dv, dk] in place, and
 // er[BH] (may be NULL) = stable rank of the result; U is a workspace of
-// BH * min(dv, dk) * dv floats (unused when r >= min(dv, dk)).
+// BH * min(dv, dk) * dv doubles (unused when r >= min(dv, dk)).
 hipError_t launch_truncate(float* S, int BH, int dv, int dk, int r, float* er,
-                           float* U, hipStream_t stream);
+                           double* U, hipStream_t stream);
 
 hipError_t launch_state_fill(const float* S0, float* ST, size_t n,
                              hipStream_t stream);

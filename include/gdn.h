@@ -398,7 +398,7 @@ int gdn_drrqr_select(const double* M, int rows, int n, int k, double f,
  * Reduction in Linear Attention", paper Sec. 2.2, Eq. (5).
  *
  * Bytes of workspace gdn_truncate_rank needs when r < min(dv, dk):
- * BH * min(dv, dk) * dv * 4 (the unit singular vectors, fp32).  0 for
+ * BH * min(dv, dk) * dv * 8 (the unit singular vectors, fp64).  0 for
  * invalid sizes.
  */
 size_t gdn_truncate_workspace_bytes(int BH, int dv, int dk);
@@ -411,10 +411,11 @@ size_t gdn_truncate_workspace_bytes(int BH, int dv, int dk);
  *              state), or NULL to skip it.
  *   workspace  device scratch of at least gdn_truncate_workspace_bytes();
  *              may be NULL when r >= min(dv, dk).
- * The singular vectors come from a Householder QR of S^T followed by a
- * one-sided Jacobi SVD of R^T, both in fp64; the projection is fp32.  When
- * sigma_r == sigma_{r+1} the leading r-dimensional subspace is not unique
- * and the result is one valid choice.  Errors as for the other entry points
+ * The left singular vectors are the leading eigenvectors of the symmetric
+ * S S^T, found in fp64 by Householder tridiagonalisation, Sturm-sequence
+ * bisection for the r largest eigenvalues and inverse iteration; the
+ * projection is fp32.  When sigma_r == sigma_{r+1} the leading
+ * r-dimensional subspace is not unique and the result is one valid choice.  Errors as for the other entry points
  * (GDN_EINVAL for r < 1, a null S, BH out of range or misalignment).
  */
 int gdn_truncate_rank(float* S, int BH, int dv, int dk, int r, float* er_out,

@@ -163,9 +163,9 @@ def test_python_wrappers_reject_host_tensors():
 
 def test_truncate_workspace_bytes():
     ws = bd.truncate_workspace_bytes
-    assert ws(16, 128, 128) == 16 * 128 * 128 * 4
-    assert ws(16, 128, 64) == 16 * 64 * 128 * 4
-    assert ws(16, 64, 128) == 16 * 64 * 64 * 4
+    assert ws(16, 128, 128) == 16 * 128 * 128 * 8
+    assert ws(16, 128, 64) == 16 * 64 * 128 * 8
+    assert ws(16, 64, 128) == 16 * 64 * 64 * 8
     assert ws(0, 128, 128) == 0
     assert ws(4, 96, 128) == 0
 
