@@ -179,7 +179,7 @@ COUNTER_LEGS = {
                 ("segment_combine_kernel", 128, None, 16 * 8 * 576),
                 ("segment_correct_kernel", 128, None, 16 * 15 * 640)],
     "decode_B64_dk128": [("decode_kernel", 128, 0, 64 * 16 * 32 * 64)],
-    "decode_B64_dk64": [("decode_kernel", 64, 0, 64 * 16 * 8 * 64)],
+    "decode_B64_dk64": [("decode_kernel", 64, 0, 64 * 16 * 4 * 64)],
     "decode_B1_dk128": [("decode_kernel", 128, 0, 16 * 32 * 64)],
     "decode_B1_dk64": [("decode_kernel", 64, 0, 16 * 32 * 64)],
     "batched_dk128": [("prepare_kernel", 128, 0, 64 * 16 * 8 * 64),
@@ -188,16 +188,16 @@ COUNTER_LEGS = {
                      ("scan_kernel", 64, 0, 8 * 16 * 2 * 256)],
     "batched_qk_dk64": [("prepare_kernel", 64, 1, 64 * 16 * 8 * 64),
                         ("scan_kernel", 64, 0, 8 * 16 * 2 * 256)],
-    "decode_qk_B64_dk64": [("decode_kernel", 64, 2, 64 * 16 * 8 * 64)],
+    "decode_qk_B64_dk64": [("decode_kernel", 64, 2, 64 * 16 * 4 * 64)],
     "batched_qk_norm_dk64": [("prepare_kernel", 64, 0, 64 * 16 * 8 * 64),
                              ("scan_kernel", 64, 0, 8 * 16 * 2 * 256)],
-    "decode_qk_norm_B64_dk64": [("decode_kernel", 64, 1, 64 * 16 * 8 * 64)],
-    # generalised gates: the recurrent decode (B=64, 16 rows per wave); the
-    # sequence at B=8 in chunked form (prepare: one 256-thread workgroup per
+    "decode_qk_norm_B64_dk64": [("decode_kernel", 64, 1, 64 * 16 * 4 * 64)],
+    # generalised gates: the recurrent decode (B=64; 8 rows per wave at
+    # d_k=128, 32 at d_k=64); the sequence at B=8 in chunked form (prepare: one 256-thread workgroup per
     # (b, h, chunk); scan: one per (b, h, 64 state rows)) and, for
     # comparison, in recurrent form (16 rows per wave)
-    "gated_decode_B64_dk128": [("gated_recurrent_kernel", 128, None, 64 * 16 * 8 * 64)],
-    "gated_decode_B64_dk64": [("gated_recurrent_kernel", 64, None, 64 * 16 * 8 * 64)],
+    "gated_decode_B64_dk128": [("gated_recurrent_kernel", 128, None, 64 * 16 * 16 * 64)],
+    "gated_decode_B64_dk64": [("gated_recurrent_kernel", 64, None, 64 * 16 * 4 * 64)],
     "gated_prefill_B8_T4096_dk64": [("gated_prepare_kernel", 64, 0, 8 * 16 * 64 * 256),
                                     ("gated_scan_kernel", 64, None, 8 * 16 * 2 * 256)],
     "gated_recurrent_B8_T4096_dk64": [("gated_recurrent_kernel", 64, None, 8 * 16 * 8 * 64)],
