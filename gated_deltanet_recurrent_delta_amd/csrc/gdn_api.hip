@@ -70,9 +70,12 @@ int prepare_checked(const void* q, const void* k, const float* alpha,
   if (!workspace || !aligned(workspace, 16)) return GDN_EWORKSPACE;
   if (workspace_bytes < prefill_qk_ws_bytes(B, T, H, dk, dv, in_dtype, qa.chan != nullptr))
     return GDN_EWORKSPACE;
+  // the segmented scan (bf16 in and out) forms P itself
+  const bool scan_forms_p = gdn::plan_prefill(B, T, H, dk, dv).nseg > 1 &&
+                            in_dtype == GDN_BF16 && out_dtype == GDN_BF16;
   return to_status(gdn::launch_prefill_prepare(
       q, k, alpha, beta, static_cast<float*>(workspace), B, T, H, dk, in_dtype,
-      out_dtype == GDN_F32, qa, static_cast<hipStream_t>(stream)));
+      out_dtype == GDN_F32, scan_forms_p, qa, static_cast<hipStream_t>(stream)));
 }
 
 // The scan's checks that do not depend on q/k (shared by the prefills).

@@ -853,7 +853,7 @@ hipError_t launch_backward_chunked(const void* q, const void* k, const void* v,
   float* dSc = Sc + BH * nchunks * (size_t)dv * dk;
   QkArgs qa = qk_identity(dk);
   qa.t_out = tu;
-  hipError_t e = launch_prefill_prepare(q, k, alpha, beta, tiles, B, T, H, dk, 1, true, qa, stream);
+  hipError_t e = launch_prefill_prepare(q, k, alpha, beta, tiles, B, T, H, dk, 1, true, false, qa, stream);
   if (e != hipSuccess) return e;
   e = launch_scan_states(k, v, S0, tiles, Sc, B, T, H, dk, dv, stream);
   if (e != hipSuccess) return e;

@@ -120,11 +120,13 @@ hipError_t launch_decode(const void* q, const void* k, const void* v,
                          const QkArgs& qa, hipStream_t stream);
 
 // write_pl: also store the lo part of P (read only when outputs are fp32).
+// scan_forms_p (bf16 inputs, segmented scan only): store no P; the scan forms
+// it from its K and Q tiles and two per-token exponent rows written instead.
 hipError_t launch_prefill_prepare(const void* q, const void* k,
                                   const float* alpha, const float* beta,
                                   float* ws, int B, int T, int H, int dk,
-                                  int in_dtype, bool write_pl, const QkArgs& qa,
-                                  hipStream_t stream);
+                                  int in_dtype, bool write_pl, bool scan_forms_p,
+                                  const QkArgs& qa, hipStream_t stream);
 
 // Phase 1 (+ phases 2 and 3 when the plan segments the sequence).  `ws` is
 // the whole workspace (per-chunk tiles first, then the segment buffers).

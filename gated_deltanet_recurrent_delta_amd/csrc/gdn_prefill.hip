@@ -161,7 +161,10 @@ __device__ __forceinline__ constexpr int lower_tile(int mi, int ni) {
 // (with A's diagonal blocks before it) passes through LDS, 17.9 KB per
 // wave, so eight waves share a CU and one wave's loads overlap another's
 // arithmetic.
-template <int DK, typename TIn, bool GATHER>
+// NOP: the segmented scan forms P itself from the staged K and Q tiles; the
+// kernel then skips P (and, without the input path's norms or gather, the
+// query rows) and writes the two exponent rows that scan needs instead.
+template <int DK, typename TIn, bool GATHER, bool NOP>
 __global__ __launch_bounds__(64) void prepare_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k,
     const float* __restrict__ alpha, const float* __restrict__ beta,
@@ -268,7 +271,8 @@ __global__ __launch_bounds__(64) void prepare_kernel(
           ssq[t] += sumsq8(xq);
         } else {
           Kh[t][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(k + off));
-          Qh[t][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(q + off));
+          if (!NOP || qa.l2norm)             // the query rows feed P or |q|
+            Qh[t][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(q + off));
         }
       }
     }
@@ -365,6 +369,13 @@ __global__ __launch_bounds__(64) void prepare_kernel(
     Gw[C + lane] = gamC;
     Gw[2 * C + lane] = gam * nk;
     Gw[3 * C + lane] = dec * nk;
+    if constexpr (NOP) {
+      // P_ji = 2^(a_j - b_i) q~_j . k~_i (i <= j) with a_j = log2 gamma_j
+      // + log2 nq_j and b_i = log2 gamma_i - log2 nk_i, over the staged rows
+      float* Ab = reinterpret_cast<float*>(wsc + kWsAB);
+      Ab[lane] = g2s[lane] + __builtin_amdgcn_logf(nq);
+      Ab[C + lane] = g2s[lane] - __builtin_amdgcn_logf(nk);
+    }
   }
 
   // 3. lower tiles of A (decay- and beta-weighted K K^T, strictly lower) and
@@ -381,12 +392,14 @@ __global__ __launch_bounds__(64) void prepare_kernel(
 #pragma unroll
       for (int s = 0; s < NKB; ++s) {
         ak = mfma(Kh[ni][s], Kh[mi][s], ak);
-        aq = mfma(Kh[ni][s], Qh[mi][s], aq);
+        if constexpr (!NOP) aq = mfma(Kh[ni][s], Qh[mi][s], aq);
         if constexpr (SPLIT) {
           ak = mfma(Kl[ni][s], Kh[mi][s], ak);
           ak = mfma(Kh[ni][s], Kl[mi][s], ak);
-          aq = mfma(Kl[ni][s], Qh[mi][s], aq);
-          aq = mfma(Kh[ni][s], Ql[mi][s], aq);
+          if constexpr (!NOP) {
+            aq = mfma(Kl[ni][s], Qh[mi][s], aq);
+            aq = mfma(Kh[ni][s], Ql[mi][s], aq);
+          }
         }
       }
       const int i0 = 16 * ni + 4 * g4;        // first column of this lane
@@ -402,10 +415,12 @@ __global__ __launch_bounds__(64) void prepare_kernel(
         a[e] = (i < j) ? bj * decay * ak[e] : 0.f;
         p[e] = qj * decay * aq[e];
       }
-      bf16x4 ph, pl;
-      split4(p, ph, pl);
-      *reinterpret_cast<bf16x4*>(wsc + kWsPh + (j * C + i0) * 2) = ph;
-      if (write_pl) *reinterpret_cast<bf16x4*>(wsc + kWsPl + (j * C + i0) * 2) = pl;
+      if constexpr (!NOP) {
+        bf16x4 ph, pl;
+        split4(p, ph, pl);
+        *reinterpret_cast<bf16x4*>(wsc + kWsPh + (j * C + i0) * 2) = ph;
+        if (write_pl) *reinterpret_cast<bf16x4*>(wsc + kWsPl + (j * C + i0) * 2) = pl;
+      }
       if (ni == mi)
         *reinterpret_cast<float4*>(&Ts[j * LDA + i0]) = make_float4(a[0], a[1], a[2], a[3]);
       else
@@ -415,7 +430,7 @@ __global__ __launch_bounds__(64) void prepare_kernel(
     // diagonal one ((0,1) and (2,3)): the scans read k-blocks s <= ct / 2
     // only, so rows 0..31 never read columns 32..63, which stay unwritten
     const bf16x4 zero4 = {};
-    if ((mi & 1) == 0) {
+    if (!NOP && (mi & 1) == 0) {
       const int ni = mi + 1;
       *reinterpret_cast<bf16x4*>(wsc + kWsPh + (j * C + 16 * ni + 4 * g4) * 2) = zero4;
       if (write_pl) *reinterpret_cast<bf16x4*>(wsc + kWsPl + (j * C + 16 * ni + 4 * g4) * 2) = zero4;
@@ -894,6 +909,16 @@ __device__ __forceinline__ void dma16(const void* g, void* lds_block) {
 // stored as 16 contiguous bytes, and the 64 lanes' operands for one
 // (w, kb) as one contiguous kilobyte, so every operand load reads whole
 // cache lines.
+// Workgroup execution barrier without a memory fence: orders this wave's
+// memory accesses in the compiler only.  Data handed over through it must
+// already be complete (here: an explicit wait on the loads that fill LDS),
+// and nothing before it waits on this wave's outstanding memory operations.
+__device__ __forceinline__ void exec_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int DK>
 __device__ __forceinline__ int xfin_index(int d, int e) {
   return ((d >> 4) * (DK / 32) + (e >> 5)) * 512 + (d & 15) * 32 + ((e >> 2) & 3) * 8 +
@@ -926,13 +951,16 @@ __global__ __launch_bounds__(64 * (DV + DK) / (16 * NH), 1) void scan_wide_kerne
   // banks).  UK, UT, UV: 16-byte units per row including the pad.
   constexpr int LDK = DK + 8, LDT = C + 8, LDV = DV + 8;
   constexpr int UK = LDK / 8, UT = LDT / 8, UV = LDV / 8;
-  // one buffer: K, Q [C][LDK]; T hi, T lo, P hi [C][LDT]; V [C][LDV]; gates fp32 [4][C]
+  // one buffer: K, Q [C][LDK]; T hi, T lo, P [C][LDT]; V [C][LDV]; gates fp32
+  // [4][C]; the exponent rows of P fp32 [2][C] (in a 1 KB load block).  P is
+  // formed here from K and Q; everything else is loaded.
   constexpr int OFF_Q = C * LDK, OFF_T = 2 * C * LDK, OFF_V = OFF_T + 3 * C * LDT;
+  constexpr int OFF_P = OFF_T + 2 * C * LDT;
   constexpr int OFF_G = OFF_V + C * LDV;
-  constexpr int BUF = OFF_G + 2 * 4 * C;                 // bf16 elements
+  constexpr int OFF_AB = OFF_G + 2 * 4 * C;
+  constexpr int BUF = OFF_AB + 512;                      // bf16 elements
   // 1 KB load blocks per buffer (64 rows of U units = U blocks per tile)
-  constexpr int NBK = UK, NBT = 3 * UT, NBV = UV;
-  constexpr int NB = 2 * NBK + NBT + NBV + 1;
+  constexpr int NBK = UK, NBT = 2 * UT, NBV = UV;
   __shared__ __attribute__((aligned(16))) bf16 buf0[BUF];
   __shared__ __attribute__((aligned(16))) bf16 buf1[BUF];
 
@@ -964,7 +992,7 @@ __global__ __launch_bounds__(64 * (DV + DK) / (16 * NH), 1) void scan_wide_kerne
   // stored.
   constexpr int MK = NBK / NW, MT = NBT / NW, MV = NBV / NW;   // blocks per wave
   constexpr int EK = NBK - NW * MK, ET = NBT - NW * MT, EV = NBV - NW * MV;
-  constexpr int NE = 2 * EK + ET + EV + 1;                      // left over
+  constexpr int NE = 2 * EK + ET + EV + 2;                      // left over
   auto issue = [&](bf16* X, int chunk) {
     const int t0 = chunk * C;
     const int last = min(C, T - t0) - 1;
@@ -1022,14 +1050,25 @@ __global__ __launch_bounds__(64 * (DV + DK) / (16 * NH), 1) void scan_wide_kerne
       } else if (e < 2 * EK + ET + EV) {
         const int jb = NW * MV + e - 2 * EK - ET;
         dma16(vc + row_off(jb, UV, tok_v), X + OFF_V + 512 * jb);
-      } else {
+      } else if (e == 2 * EK + ET + EV) {
         dma16(wsc + kWsG + 16 * ln, X + OFF_G);
+      } else {
+        dma16(wsc + kWsAB + 16 * ln, X + OFF_AB);
       }
     }
   };
-  static_assert(OFF_Q == 512 * NBK && OFF_T == 512 * 2 * NBK &&
-                OFF_V == 512 * (2 * NBK + NBT) && OFF_G == 512 * (2 * NBK + NBT + NBV),
-                "load blocks tile the buffer");
+  static_assert(OFF_Q == 512 * NBK && OFF_T == 512 * 2 * NBK && OFF_P == OFF_T + 512 * NBT &&
+                OFF_V == OFF_P + 512 * UT && OFF_G == OFF_V + 512 * NBV &&
+                OFF_AB == OFF_G + 512, "load blocks and P tile the buffer");
+
+  // P's upper tiles that the scan reads, (0,1) and (2,3), are zero in both
+  // buffers for good (no load writes P's space)
+  for (int idx = tid; idx < 2 * 256; idx += 64 * NW) {
+    const int tl = idx >> 8, r = (idx >> 4) & 15, cc = idx & 15;
+    const int off = OFF_P + (32 * tl + r) * LDT + 32 * tl + 16 + cc;
+    buf0[off] = bf16(0.f);
+    buf1[off] = bf16(0.f);
+  }
 
   // ---- carried state: S^T tiles of each slice, lane holds
   //      S^T[d = 16 dt + 4 g4 + i][row = 16 hf + n] ----
@@ -1065,20 +1104,56 @@ __global__ __launch_bounds__(64 * (DV + DK) / (16 * NH), 1) void scan_wide_kerne
   }
 
   // One chunk from buffer X (loaded), prefetching chunk + 1 into buffer Nx.
-  auto step = [&](const bf16* X, bf16* Nx, int chunk) {
+  auto step = [&](bf16* X, bf16* Nx, int chunk) {
     const int t0 = chunk * C;
     const int nvalid = min(C, T - t0);
     __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's loads of X
     __syncthreads();                          // everyone's loads of X; Nx is free
     if (chunk + 1 < c_end) issue(Nx, chunk + 1);
-    if (!active) return;
     const bf16* Ks = X;
     const bf16* Qs = X + OFF_Q;
     const bf16* Ths = X + OFF_T;
     const bf16* Tls = Ths + C * LDT;
-    const bf16* Phs = Tls + C * LDT;
+    const bf16* Phs = X + OFF_P;
     const bf16* Vs = X + OFF_V;
     const float* Gs = reinterpret_cast<const float*>(X + OFF_G);
+
+    // ---- P_ji = 2^(a_j - b_i) q~_j . k~_i for i <= j: the ten lower 16x16
+    //      tiles, shared out over the waves (tile (mi, ni): a lane holds row
+    //      j = 16 mi + n, columns 16 ni + 4 g4 .. + 3); read after the
+    //      barrier before the outputs ----
+    {
+      // an opaque copy of the lane index keeps these per-lane addresses from
+      // being hoisted out of the chunk loop (registers the products need)
+      unsigned ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int pn = ln & 15, pg = ln >> 4;
+      const float* Ab = reinterpret_cast<const float*>(X + OFF_AB);
+      for (int tp = w; tp < 10; tp += NW) {
+        const int mi = tp >= 6 ? 3 : tp >= 3 ? 2 : tp >= 1 ? 1 : 0;
+        const int ni = tp - mi * (mi + 1) / 2;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NKB; ++s)
+          acc = mfma(lds_slots(Ks, LDK, 16 * ni + pn, s, pg),
+                     lds_slots(Qs, LDK, 16 * mi + pn, s, pg), acc);
+        const int j = 16 * mi + pn, i0 = 16 * ni + 4 * pg;
+        const float aj = Ab[j];
+        const float4 b4 = *reinterpret_cast<const float4*>(&Ab[C + i0]);
+        const float bi[4] = {b4.x, b4.y, b4.z, b4.w};
+        bf16x4 pv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          pv[e] = (bf16)(i0 + e <= j ? __builtin_amdgcn_exp2f(aj - bi[e]) * acc[e] : 0.f);
+        *reinterpret_cast<bf16x4*>(X + OFF_P + j * LDT + i0) = pv;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);        // keep P's registers out of the products below
+    if (!active) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): this wave's P tiles
+      exec_barrier();
+      return;
+    }
 
     // ---- Y = K S^T for all slices (c-tile ct: rows c = 16 ct + 4 g4 + i,
     //      col = row n of the slice) ----
@@ -1147,6 +1222,9 @@ __global__ __launch_bounds__(64 * (DV + DK) / (16 * NH), 1) void scan_wide_kerne
         }
       }
     }
+
+    __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0): this wave's P tiles
+    exec_barrier();                           // every wave's P tiles are in LDS
 
     // ---- O^T = S Q^T diag(gamma) + U^T P^T (single-pass bf16: o is bf16);
     //      tile ct: rows r = 4 g4 + i of the slice, token c = 16 ct + n ----
@@ -1293,9 +1371,18 @@ hipError_t launch_state_fill(const float* S0, float* ST, size_t n,
 template <int DK, typename TIn, bool GATHER>
 static void launch_prepare_t(const void* q, const void* k, const float* alpha,
                              const float* beta, float* ws, int B, int T, int H,
-                             bool write_pl, const QkArgs& qa, hipStream_t stream) {
+                             bool write_pl, bool scan_forms_p, const QkArgs& qa,
+                             hipStream_t stream) {
   const int nchunks = (T + C - 1) / C;
-  hipLaunchKernelGGL((prepare_kernel<DK, TIn, GATHER>), dim3(nchunks, H, B), dim3(64),
+  if constexpr (std::is_same<TIn, bf16>::value) {
+    if (scan_forms_p) {
+      hipLaunchKernelGGL((prepare_kernel<DK, TIn, GATHER, true>), dim3(nchunks, H, B),
+                         dim3(64), 0, stream, static_cast<const TIn*>(q),
+                         static_cast<const TIn*>(k), alpha, beta, ws, T, H, nchunks, 0, qa);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((prepare_kernel<DK, TIn, GATHER, false>), dim3(nchunks, H, B), dim3(64),
                      0, stream, static_cast<const TIn*>(q),
                      static_cast<const TIn*>(k), alpha, beta, ws, T, H,
                      nchunks, write_pl ? 1 : 0, qa);
@@ -1304,10 +1391,10 @@ static void launch_prepare_t(const void* q, const void* k, const float* alpha,
 hipError_t launch_prefill_prepare(const void* q, const void* k,
                                   const float* alpha, const float* beta,
                                   float* ws, int B, int T, int H, int dk,
-                                  int in_dtype, bool write_pl, const QkArgs& qa,
-                                  hipStream_t stream) {
+                                  int in_dtype, bool write_pl, bool scan_forms_p,
+                                  const QkArgs& qa, hipStream_t stream) {
 #define GDN_PREP(DK, TI, G) \
-  launch_prepare_t<DK, TI, G>(q, k, alpha, beta, ws, B, T, H, write_pl, qa, stream)
+  launch_prepare_t<DK, TI, G>(q, k, alpha, beta, ws, B, T, H, write_pl, scan_forms_p, qa, stream)
   const bool g = qa.chan != nullptr;
   if (in_dtype == 1) {
     if (dk == 128) { if (g) GDN_PREP(128, bf16, true); else GDN_PREP(128, bf16, false); }
@@ -1318,16 +1405,6 @@ hipError_t launch_prefill_prepare(const void* q, const void* k,
   }
 #undef GDN_PREP
   return hipGetLastError();
-}
-
-// Workgroup execution barrier without a memory fence: orders this wave's
-// memory accesses in the compiler only.  Data handed over through it must
-// already be complete (here: an explicit wait on the loads that fill LDS),
-// and nothing before it waits on this wave's outstanding memory operations.
-__device__ __forceinline__ void exec_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 // ===========================================================================

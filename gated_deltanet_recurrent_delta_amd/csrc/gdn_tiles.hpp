@@ -26,6 +26,10 @@ constexpr int kWsPl = 24576;                // bf16 [64][64] lo part of P
 // V - diag(gamma) K S^T) and e^{g_C - g} nk (for the state update); nq = nk
 // = 1 without the input path.
 constexpr int kWsG = 32768;
+// When the segmented scan forms P itself, the space of P's hi part holds
+// fp32 [2][64] exponent rows instead: a_j = log2 gamma_j + log2 nq_j and
+// b_i = log2 gamma_i - log2 nk_i, so that P_ji = 2^(a_j - b_i) q~_j . k~_i.
+constexpr int kWsAB = kWsPh;
 static_assert(kWsG + 4 * 4 * C == kChunkWsFloats * 4, "workspace layout");
 
 typedef short short4v __attribute__((ext_vector_type(4)));
