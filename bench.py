@@ -80,20 +80,23 @@ def prefill_mfma_flops(B, T, H, dk, dv, nseg, seg_chunks):
     """bf16 MFMA flops the prefill kernels execute (bf16 in / bf16 out), from
     their structure; one v_mfma_f32_16x16x32_bf16 = 16384 flops.
       prepare: per chunk and head, 10 lower tiles of K K^T and of Q K^T,
-               dk/32 k-steps each.
+               dk/32 k-steps each (segmented: K K^T only).
       scan:    per chunk and 16-row wave: K S^T 4 x dk/32 x 2 (split state),
                Q S^T 4 x dk/32, T Z 6 k-blocks x 3, P U 6, state update
                dk/16 tiles x 2 k-blocks x 2; transition rows (dk per head)
-               run for the chunks of segments >= 1.
+               run for the chunks of segments >= 1; segmented, the 10
+               lower tiles of Q K^T per chunk and head-segment as well.
       combine: per later segment and 16-row wave: dk/16 x dk/32 x 3.
       correct: per chunk of later segments and 16-row wave: 4 x dk/32."""
     nch = -(-T // C)
     nkb, ndt = dk // 32, dk // 16
     f = 16 * 16 * 32 * 2
-    prep = B * H * nch * 20 * nkb
+    prep = B * H * nch * (10 if nseg > 1 else 20) * nkb
     per_wave_chunk = 4 * nkb * 2 + 4 * nkb + 6 * 3 + 6 + ndt * 2 * 2
     later = nch - seg_chunks if nseg > 1 else 0
     scan = B * H * (dv // 16 * nch + dk // 16 * later) * per_wave_chunk
+    if nseg > 1:
+        scan += B * H * nch * 10 * nkb
     comb = B * H * (nseg - 1) * (dv // 16) * ndt * nkb * 3
     corr = B * H * later * (dv // 16) * 4 * nkb
     return prep * f, (scan + comb + corr) * f
@@ -167,7 +170,9 @@ def measured_traffic(kernel):
 # prompts (prefills of B=64 or B=1) have other grids and are not counted.
 COUNTER_LEGS = {
     # (kernel, d_k, last template argument or None, grid): the last template
-    # argument is prepare_kernel's gather flag (0, 1), decode_kernel's
+    # argument is prepare_kernel's gather flag (0, 1; its third template
+    # argument: the segmented prefill's instance, which leaves P to the
+    # scan, has a grid of its own), decode_kernel's
     # input-path mode (0 none, 1 norm + scale, 2 channel subset + norm + scale)
     # and scan_kernel's state-storing flag (1 in the backward pass)
     # 16 heads x 16 segments: scan_wide 512 threads per head-segment,
@@ -256,6 +261,8 @@ def _kernel_key(name):
         tmpl = rest.split("EEv", 1)[0] + "E"
         di = re.match(r"ILi(\d+)E", rest)
         last = re.findall(r"L[bi](\d+)E", tmpl)
+        if base == "prepare_kernel" and len(last) > 2:
+            return base, int(last[0]), int(last[1])      # <dk, type, gather, no-P>
         return (base, int(di.group(1)) if di else None,
                 int(last[-1]) if len(last) > 1 or (last and not di) else None)
     m = re.search(r"(\w+)<([^>]*)>", name)
@@ -264,6 +271,8 @@ def _kernel_key(name):
     args = [x.strip() for x in m.group(2).split(",")]
     dk = int(args[0]) if args and args[0].lstrip("-").isdigit() else None
     tail = args[-1] if len(args) > 1 else ""
+    if m.group(1) == "prepare_kernel" and len(args) > 3:
+        tail = args[2]                                   # the gather flag
     flag = {"true": 1, "false": 0}.get(tail, int(tail) if tail.isdigit() else None)
     return m.group(1), dk, flag
 

@@ -55,6 +55,15 @@ def test_kernel_keys():
     assert bench._kernel_key("void gdn::prepare_kernel<128, __bf16, true>(int)") == (
         "prepare_kernel", 128, 1)
     assert bench._kernel_key("__amd_rocclr_copyBuffer")[0] == "__amd_rocclr_copyBuffer"
+    # prepare_kernel<dk, type, gather, no-P>: keyed by the gather flag
+    assert bench._kernel_key(
+        "_ZN3gdn14prepare_kernelILi128EDF16bLb0ELb1EEEvPKT0_S3_PKfS5_PfiiiiNS_6QkArgsE") == (
+        "prepare_kernel", 128, 0)
+    assert bench._kernel_key(
+        "_ZN3gdn14prepare_kernelILi64EDF16bLb1ELb0EEEvPKT0_S3_PKfS5_PfiiiiNS_6QkArgsE") == (
+        "prepare_kernel", 64, 1)
+    assert bench._kernel_key("void gdn::prepare_kernel<64, __bf16, true, false>(int)") == (
+        "prepare_kernel", 64, 1)
 
 
 def test_counters_attribution_and_calibration(tmp_path):
