@@ -1152,18 +1152,37 @@ def bench_truncated(torch, gdn, dev, stream, up, ranks=(1, 4, 12, 32),
     projected onto its top-r left singular directions.  Each r's whole pass
     (64 prefill calls + 63 truncations) is captured in one HIP graph and
     replayed; r = 128 is the untruncated control.  The truncation alone is
-    also timed on the 16 states met at the first boundary."""
-    x = gi.truncated_prefill()
+    also timed on the 16 states met at the first boundary.
+
+    The workload's inputs have the tiny case's distributions (per-token
+    log alpha ~ -U(0.001, 0.1): a horizon of about 20 tokens, so the state
+    at T is rebuilt from the last few hundred tokens whatever r is).  The
+    same pass is also run on the 16K benchmark step's inputs, whose six
+    long-horizon heads (log alpha ~ -U(1e-4, 1e-3)) carry the truncated
+    directions across boundaries: there the ranks at T depend on r."""
+    res = _truncated_pass(torch, gdn, dev, stream, up, gi.truncated_prefill(), ranks,
+                          segment, "tiny-case distributions")
+    res["c2_inputs"] = _truncated_pass(
+        torch, gdn, dev, stream, up, gi.prefill_16k(), ranks, segment,
+        "the 16K benchmark step's inputs (cone keys, 10 short- and 6 long-horizon heads)",
+        time_boundary=False)
+    return res
+
+
+def _truncated_pass(torch, gdn, dev, stream, up, x, ranks, segment, inputs,
+                    time_boundary=True):
     B, T, H, dk = x.q.shape
     dv = x.v.shape[-1]
     q, k, v, al, be = up(x)
     del x
-    _, S_b1 = gdn.prefill(q[:, :segment], k[:, :segment], v[:, :segment],
-                          al[:, :segment], be[:, :segment])
-    ws = torch.empty(gdn.truncate_workspace_bytes(B * H, dv, dk),
-                     dtype=torch.uint8, device=dev)
+    ws = None
+    if time_boundary:
+        _, S_b1 = gdn.prefill(q[:, :segment], k[:, :segment], v[:, :segment],
+                              al[:, :segment], be[:, :segment])
+        ws = torch.empty(gdn.truncate_workspace_bytes(B * H, dv, dk),
+                         dtype=torch.uint8, device=dev)
     res = {"workload": f"B={B}, H={H}, T={T}, dk=dv={dk}, bf16 in/out, "
-                       f"truncation every {segment} tokens",
+                       f"truncation every {segment} tokens; {inputs}",
            "boundaries": (T - 1) // segment}
     for r in (*ranks, min(dk, dv)):
         def run():
@@ -1204,7 +1223,7 @@ def bench_truncated(torch, gdn, dev, stream, up, ranks=(1, 4, 12, 32),
                 "rank_columns": "stable rank from gdn_truncate_rank's er_out (the "
                                 "primary figure); entropy erank and numerical rank "
                                 "from a host fp64 SVD of the same S_T"}
-        if r < min(dk, dv):
+        if time_boundary and r < min(dk, dv):
             times = []
             for _ in range(5):
                 Sx = S_b1.clone()
@@ -1216,14 +1235,17 @@ def bench_truncated(torch, gdn, dev, stream, up, ranks=(1, 4, 12, 32),
                 times.append(e0.elapsed_time(e1))
             item["one_boundary_truncate_us"] = float(np.median(times)) * 1e3
         res[f"r{r}"] = item
-        log(f"truncated prefill r={r}: {ms:.2f} ms/pass, er(S_T) mean "
-            f"{np.mean(erv):.2f}" + (f", one boundary {item['one_boundary_truncate_us']:.0f} us"
-                                     if "one_boundary_truncate_us" in item else ""))
+        log(f"truncated prefill ({inputs.split(' (')[0]}) r={r}: {ms:.2f} ms/pass, "
+            f"er(S_T) mean {np.mean(erv):.2f}, entropy erank {np.mean(ent):.1f}" +
+            (f", one boundary {item['one_boundary_truncate_us']:.0f} us"
+             if "one_boundary_truncate_us" in item else ""))
         del g, er, S_T
     base = res[f"r{min(dk, dv)}"]["ms_per_pass"]
     for r in ranks:
         res[f"r{r}"]["truncation_ms"] = res[f"r{r}"]["ms_per_pass"] - base
-    del q, k, v, al, be, S_b1, ws
+    del q, k, v, al, be, ws
+    if time_boundary:
+        del S_b1
     torch.cuda.empty_cache()
     return res
 
