@@ -207,6 +207,24 @@ def test_segmented_prefill_few_heads(T, dk, dv, nseg):
     check_full(x, "bf16", f"segmented T={T}")
 
 
+@pytest.mark.parametrize("case", ["beta0", "beta1", "alpha1", "alpha_small"])
+def test_segmented_gate_edge_values(case):
+    """Gate edge values on the segment-parallel path, whose scan forms the
+    masked Q K^T tiles from per-token exponent rows (e^-3 per token spans
+    about 277 powers of two inside a chunk)."""
+    x = gi.generic(1, 1100, 2, 128, 128, 78, "bf16", S0_scale=0.5)
+    assert gdn.prefill_segments(1, 1100, 2, 128, 128)[0] > 1
+    if case == "beta0":
+        x.beta[:] = 0.0
+    elif case == "beta1":
+        x.beta[:] = 1.0
+    elif case == "alpha1":
+        x.alpha[:] = 1.0
+    else:
+        x.alpha[:] = np.float32(np.exp(-3.0))
+    check_full(x, "bf16", f"segmented {case}")
+
+
 def test_segmented_prefill_in_place_state():
     x = gi.generic(1, 1300, 3, 128, 128, 31, "bf16", S0_scale=0.5)
     d = to_dev(x)
