@@ -130,7 +130,10 @@ int gdn_prefill(const void* q, const void* k, const void* v,
  *            sums and per-token decay factors, the unit-lower-triangular
  *            delta correction (I + A)^{-1} with A_ji = beta_j e^{g_j - g_i}
  *            k_j.k_i (i < j), stored times diag(beta), and the
- *            decay-masked query-key products; written to workspace.
+ *            decay-masked query-key products; written to workspace.  When
+ *            the scan will segment the sequence (below), it writes per-token
+ *            exponent rows instead of the query-key products, which that
+ *            scan forms itself from the q and k it stages.
  *   scan:    sequential over chunks, parallel over heads and 64-row groups
  *            of the state: reads q, k, v and the chunk tiles, writes o and
  *            ST.  With bf16 inputs and outputs and few heads it also splits
