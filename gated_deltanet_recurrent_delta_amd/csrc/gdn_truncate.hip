@@ -126,15 +126,46 @@ __device__ __forceinline__ double recip(double x) {
 // off-diagonal e2) below x: the negative pivots of T - x I, q_0 = d_0 - x,
 // q_i = d_i - x - e_{i-1}^2 / q_{i-1}, pivots smaller than pivmin replaced
 // by -pivmin.
+// The recurrence is a chain of dependent divisions; the diagonal and
+// off-diagonal entries it reads (the same for every lane) are loaded from
+// LDS one block of 8 steps ahead, so no step waits for them.
 template <int M>
 __device__ __forceinline__ int sturm_count(const double* dd, const double* e2, double x,
                                            double pivmin) {
+  static_assert((M - 1) % 8 == 7, "blocks of 8 steps, the last one of 7");
   double q = dd[0] - x;
   if (fabs(q) < pivmin) q = -pivmin;
   int c = q < 0.0;
-#pragma unroll 8
-  for (int i = 1; i < M; ++i) {
-    q = fma(-e2[i - 1], recip(q), dd[i] - x);
+  double dn[8], en[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    dn[j] = dd[1 + j];
+    en[j] = e2[j];
+  }
+#pragma unroll 1
+  for (int b = 1; b < M - 7; b += 8) {
+    double dc[8], ec[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      dc[j] = dn[j];
+      ec[j] = en[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {               // the next block (the last has 7)
+      const int i = min(b + 8 + j, M - 1);
+      dn[j] = dd[i];
+      en[j] = e2[i - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      q = fma(-ec[j], recip(q), dc[j] - x);
+      if (fabs(q) < pivmin) q = -pivmin;
+      c += q < 0.0;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    q = fma(-en[j], recip(q), dn[j] - x);
     if (fabs(q) < pivmin) q = -pivmin;
     c += q < 0.0;
   }
@@ -334,9 +365,14 @@ eig_top_kernel(const float* __restrict__ S, int r, int rv, double* __restrict__ 
   hi += 0x1p-46 * tnorm + pivmin;
   const bool zero = !(tnorm > 0.0);
   const int nl = rv > 0 ? rv : 1;                 // eigenvalues to locate
-  // P threads per eigenvalue and the multisection steps for ~50 bits
-  const int P = nl <= 8 ? 64 : nl <= 16 ? 32 : nl <= 32 ? 16 : nl <= 64 ? 8 : 4;
-  const int nit = P == 64 ? 9 : P == 32 ? 10 : P == 16 ? 13 : P == 8 ? 16 : 22;
+  // P threads per eigenvalue and the multisection steps for ~50 bits.  The
+  // counts are chains of fp64 divisions: with one wave per SIMD each chain
+  // runs at its latency, with two the SIMD's fp64 issue rate is the limit
+  // and costs more than the extra steps of a smaller P, so nl * P stays
+  // within 256 threads (measured on MI355X, 16 heads of 128 x 128: r = 12
+  // 417 -> 395 us, r = 32 516 -> 486 us per boundary).
+  const int P = nl <= 4 ? 64 : nl <= 8 ? 32 : nl <= 16 ? 16 : nl <= 32 ? 8 : nl <= 64 ? 4 : 2;
+  const int nit = P == 64 ? 9 : P == 32 ? 10 : P == 16 ? 13 : P == 8 ? 16 : P == 4 ? 22 : 32;
   __syncthreads();                                 // e2 complete
   {
     const int j = tid / P, p = tid - j * P;
