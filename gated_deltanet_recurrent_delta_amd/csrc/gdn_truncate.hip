@@ -208,8 +208,13 @@ eig_top_kernel(const float* __restrict__ S, int r, int rv, double* __restrict__ 
   // ---- 1. G = S S^T, each thread's tile of it kept in registers ----------
   // tile: rows r0 .. r0 + RT - 1, columns c0 .. c0 + CT - 1; the 16 lanes of
   // a DPP row hold the 16 tiles of one block of RT rows
+  // Wave wv holds row block rb (4 RT rows): waves wv and wv + 4, which
+  // share a SIMD, hold blocks b and 7 - b, so that as the reduction retires
+  // the leading blocks every SIMD keeps about the same work.
   constexpr int RT = M / 32, CT = M / 16;
-  const int r0 = RT * (tid >> 4), c0 = CT * (tid & 15);
+  static_assert(kEigThreads == 512, "eight row blocks, one per wave");
+  const int rb = wv < 4 ? wv : 11 - wv;
+  const int r0 = RT * (4 * rb + (lane >> 4)), c0 = CT * (tid & 15);
   double A[RT][CT];
 #pragma unroll
   for (int i = 0; i < RT; ++i)
@@ -257,8 +262,18 @@ eig_top_kernel(const float* __restrict__ S, int r, int rv, double* __restrict__ 
   // Wv); every wave computes and writes them itself (bitwise the same
   // values), so they need no barrier of their own.  Row k + 1 goes to Xr
   // for the next step.
+  // A wave whose rows are all <= k has nothing left to do: its rows are
+  // final (v and w vanish there) and no later step reads them, so it only
+  // passes the barriers; the wave with the last block (always active)
+  // records the tridiagonal entries and the reflectors.
   constexpr int EL = (M + 63) / 64;                // entries of a row per lane
+  const bool last_block = rb == 7;
   for (int k = 0; k < M - 2; ++k) {
+    if (4 * RT * rb + 4 * RT - 1 <= k) {
+      __syncthreads();
+      __syncthreads();
+      continue;
+    }
     double xl[EL];
     double s = 0.0;
 #pragma unroll
@@ -276,7 +291,7 @@ eig_top_kernel(const float* __restrict__ S, int r, int rv, double* __restrict__ 
       v0 = x0 - alpha;
       t = 1.0 / (nx * (nx + fabs(x0)));            // 2 / v^T v
     }
-    if (tid == 0) {
+    if (last_block && lane == 0) {
       dd[k] = Xr[k];
       ee[k] = alpha;
       tau[k] = t;
@@ -286,7 +301,7 @@ eig_top_kernel(const float* __restrict__ S, int r, int rv, double* __restrict__ 
       const int j = lane + 64 * e;
       const double vj = j == k + 1 ? v0 : xl[e];
       if (j < M) Vv[j] = vj;
-      if (wv == 0 && j > k && j < M) hv[hv_off<M>(k) + j - k - 1] = vj;
+      if (last_block && j > k && j < M) hv[hv_off<M>(k) + j - k - 1] = vj;
     }
     // p = t A v
     double vc[CT];
