@@ -8,8 +8,9 @@ Inputs stay exact and distinct per head without drawing gigabytes on the
 host: the prefill's batch entry b is a cyclic token shift, by 997 b tokens,
 of one of two seeded rows of the generic workload (its initial state a shift
 of the head axis); the decode's state of head i is a (row, column) cyclic
-shift of one of 64 seeded states.  The oracle receives the same shifted
-arrays, built with numpy.
+shift of one of 64 seeded states; the segmented prefill's sequence is 34
+copies of one seeded 32768-token row, copy j shifted by 7919 j tokens.  The
+oracle receives the same shifted arrays, built with numpy.
 """
 
 import numpy as np
@@ -105,4 +106,45 @@ def test_decode_offsets_past_2_31():
         check_step(f"o (head {i})", host(o[b, h])[None, None], o_ref, TOL_BF16)
         check_S(f"S' (head {i})", host(S1[b, h])[None, None], S_ref, TOL_F32)
     del S, S1, o
+    torch.cuda.empty_cache()
+
+
+def test_segmented_prefill_offsets_past_2_31():
+    """B=1, T=1,114,112, H=16, d=128, bf16 (the segmented path, 16 segments
+    per head): q, k, v, o and x^ hold 2.28e9 elements.
+
+    With log alpha <= -0.05 per token, the state before the last W = 4096
+    tokens reaches the end only through the product of the window's
+    transitions alpha_t (I - beta_t k_t k_t^T), whose norm is at most
+    prod alpha_t <= e^(-0.05 W); so the oracle run over the last W tokens
+    from a zero state gives S_T, and the outputs of the last W/2 tokens,
+    exactly up to e^(-102) of the state's scale."""
+    dev = torch.device("cuda", 0)
+    T0, NCOPY, H, d, W = 32768, 34, 16, 128, 4096
+    T = T0 * NCOPY
+    assert T * H * d > 2 ** 31
+    x = gi.generic(1, T0, H, d, d, gi.seed_for(2, 9), "bf16", log_alpha_range=(0.05, 0.1))
+    shift = lambda j: (7919 * j) % T0
+    big = {}
+    for n in ("q", "k", "v", "alpha", "beta"):
+        src = torch.from_numpy(getattr(x, n)[0]).to(dev)
+        if n in ("q", "k", "v"):
+            src = src.to(torch.bfloat16)
+        t = torch.empty((1, T) + tuple(src.shape[1:]), dtype=src.dtype, device=dev)
+        for j in range(NCOPY):
+            t[0, j * T0:(j + 1) * T0] = torch.roll(src, shifts=shift(j), dims=0)
+        big[n] = t
+        del src
+    o, ST = gdn.prefill(big["q"], big["k"], big["v"], big["alpha"], big["beta"])
+    torch.cuda.synchronize()
+    print(f"  segmented prefill T={T} H={H} d={d}: o holds {o.numel():.3e} elements", flush=True)
+    win = lambda a: np.roll(a[0], shift(NCOPY - 1), axis=0)[T0 - W:][None]
+    o_ref, S_ref = orc.gdn_prefill(win(x.q), win(x.k), win(x.v), win(x.alpha), win(x.beta),
+                                   heads=[(0, 0), (0, H - 1)])
+    o_dev = host(o[0, T - W // 2:])[None]
+    for h in (0, H - 1):
+        check_o(f"o, last {W // 2} tokens (h={h})", o_dev, o_ref[:, W // 2:], TOL_BF16,
+                heads=[(0, h)])
+        check_S(f"S_T (h={h})", host(ST), S_ref, TOL_F32, heads=[(0, h)])
+    del big, o, ST
     torch.cuda.empty_cache()
