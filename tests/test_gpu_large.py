@@ -9,8 +9,10 @@ host: the prefill's batch entry b is a cyclic token shift, by 997 b tokens,
 of one of two seeded rows of the generic workload (its initial state a shift
 of the head axis); the decode's state of head i is a (row, column) cyclic
 shift of one of 64 seeded states; the segmented prefill's sequence is 34
-copies of one seeded 32768-token row, copy j shifted by 7919 j tokens.  The
-oracle receives the same shifted arrays, built with numpy.
+copies of one seeded 32768-token row, copy j shifted by 7919 j tokens; the
+generalised-gate prefill and the backward pass shift two seeded rows like
+the plain prefill.  The oracle receives the same shifted arrays, built with
+numpy.
 """
 
 import numpy as np
@@ -147,4 +149,86 @@ def test_segmented_prefill_offsets_past_2_31():
                 heads=[(0, h)])
         check_S(f"S_T (h={h})", host(ST), S_ref, TOL_F32, heads=[(0, h)])
     del big, o, ST
+    torch.cuda.empty_cache()
+
+
+def test_gated_prefill_offsets_past_2_31():
+    """The generalised gates in chunked form at B=136, T=8192, H=16, dk=64,
+    dv=128, bf16: v, o and the fp32 write gate hold 2.28e9 elements (the
+    per-key-channel gates 1.14e9 fp32, 4.6 GB each); batch entry b is a
+    cyclic token shift, by 997 b, of one of two seeded rows."""
+    dev = torch.device("cuda", 0)
+    B, T, H, dk, dv = 136, 8192, 16, 64, 128
+    assert B * T * H * dv > 2 ** 31
+    x = gi.generic(2, T, H, dk, dv, gi.seed_for(4, 8), "bf16", S0_scale=0.3)
+    al, bg, wg = gi.gate_vectors(2, T, H, dk, dv, gi.seed_for(4, 9))
+    shift = lambda b: (997 * b) % T
+    rows = {"q": x.q, "k": x.k, "v": x.v, "alpha": al, "b": bg, "w": wg}
+    big = {}
+    for n, a in rows.items():
+        src = torch.from_numpy(a).to(dev)
+        if n in ("q", "k", "v"):
+            src = src.to(torch.bfloat16)
+        t = torch.empty((B,) + tuple(src.shape[1:]), dtype=src.dtype, device=dev)
+        for b in range(B):
+            t[b] = torch.roll(src[b % 2], shifts=shift(b), dims=0)
+        big[n] = t
+        del src
+    S0_dev = torch.from_numpy(x.S0).to(dev)
+    S0 = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    for b in range(B):
+        S0[b] = torch.roll(S0_dev[b % 2], shifts=b % H, dims=0)
+    o, ST = gdn.gated_prefill(big["q"], big["k"], big["v"], big["alpha"], big["b"], big["w"], S0)
+    torch.cuda.synchronize()
+    print(f"  gated prefill B={B} T={T} H={H} dk={dk} dv={dv}: o holds {o.numel():.3e} elements",
+          flush=True)
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        r, s = b % 2, shift(b)
+        one = lambda a: np.roll(a[r], s, axis=0)[None]
+        o_ref, S_ref = orc.gdn2_prefill(one(x.q), one(x.k), one(x.v), one(al), one(bg), one(wg),
+                                        np.roll(x.S0[r], b % H, axis=0)[None], heads=[(0, h)])
+        check_o(f"o (b={b}, h={h})", host(o[b])[None], o_ref, TOL_BF16, heads=[(0, h)])
+        check_S(f"S_T (b={b}, h={h})", host(ST[b])[None], S_ref, TOL_F32, heads=[(0, h)])
+    del big, o, ST, S0
+    torch.cuda.empty_cache()
+
+
+def test_backward_offsets_past_2_31():
+    """The chunked backward pass at B=136, T=8192, H=16, dk=dv=128, bf16
+    inputs: dq, dk and dv hold 2.28e9 floats each; batch entry b (inputs and
+    d_o) is a cyclic token shift, by 997 b, of one of two seeded rows, its
+    S0 and dS_T shifts of the head axis."""
+    from tests.test_gpu_backward import compare
+    dev = torch.device("cuda", 0)
+    B, T, H, d = 136, 8192, 16, 128
+    assert B * T * H * d > 2 ** 31
+    x = gi.generic(2, T, H, d, d, gi.seed_for(5, 8), "bf16", S0_scale=0.3)
+    d_o, dST = gi.cotangents(2, T, H, d, d, gi.seed_for(5, 9), "bf16")
+    shift = lambda b: (997 * b) % T
+    toks = {"q": x.q, "k": x.k, "v": x.v, "alpha": x.alpha, "beta": x.beta, "d_o": d_o}
+    states = {"S0": x.S0, "dST": dST}
+    big = {}
+    for n, a in list(toks.items()) + list(states.items()):
+        src = torch.from_numpy(a).to(dev)
+        if n in ("q", "k", "v", "d_o"):
+            src = src.to(torch.bfloat16)
+        t = torch.empty((B,) + tuple(src.shape[1:]), dtype=src.dtype, device=dev)
+        for b in range(B):
+            t[b] = torch.roll(src[b % 2], shifts=shift(b) if n in toks else b % H, dims=0)
+        big[n] = t
+        del src
+    g = gdn.backward(big["q"], big["k"], big["v"], big["alpha"], big["beta"], big["S0"],
+                     big["d_o"], big["dST"])
+    torch.cuda.synchronize()
+    print(f"  backward B={B} T={T} H={H} d={d}: dq holds {g['dq'].numel():.3e} floats", flush=True)
+    del big
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        r, s = b % 2, shift(b)
+        tk = lambda a: np.roll(a[r], s, axis=0)[None]
+        hd = lambda a: np.roll(a[r], b % H, axis=0)[None]
+        ref = orc.gdn_backward(tk(x.q), tk(x.k), tk(x.v), tk(x.alpha), tk(x.beta), hd(x.S0),
+                               tk(d_o), hd(dST), heads=[(0, h)])
+        gs = {n: (None if g[n] is None else g[n][b:b + 1]) for n in g}
+        compare(f"(b={b}, h={h})", gs, ref, [(0, h)])
+    del g
     torch.cuda.empty_cache()
