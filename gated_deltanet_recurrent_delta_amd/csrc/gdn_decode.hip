@@ -107,7 +107,13 @@ __global__ __launch_bounds__(64 * WPB) void decode_kernel(
 
   // input path: normalise k and q over the kept channels (the 16 lanes of
   // a row hold all DK of them), scale q
-  if (QK != 0 && qa.l2norm) {
+  if constexpr (QK != 0) {
+    // Branch-free: the norms are always formed and then selected, and the
+    // reciprocal square root is the hardware one (1 ulp), so the kernel has
+    // no branch here.  With a run-time branch (and the correctly rounded
+    // 1/sqrt, a branchy sequence) the compiler hoisted the v loads above the
+    // state loads, and the step took 12.5 instead of 11.9 us at B=64,
+    // dk=64 (the plain instance's time), with or without normalisation.
     float sk = 0.f, sq = 0.f;
 #pragma unroll
     for (int f = 0; f < F; ++f) {
@@ -116,17 +122,13 @@ __global__ __launch_bounds__(64 * WPB) void decode_kernel(
     }
     sk = sum16(sk);
     sq = sum16(sq);
-    const float nk = sk > 0.f ? 1.f / sqrtf(sk) : 0.f;
-    const float nq = (sq > 0.f ? 1.f / sqrtf(sq) : 0.f) * qa.qscale;
+    const bool nrm = qa.l2norm != 0;
+    const float nk = nrm ? (sk > 0.f ? __builtin_amdgcn_rsqf(sk) : 0.f) : 1.f;
+    const float nq = (nrm ? (sq > 0.f ? __builtin_amdgcn_rsqf(sq) : 0.f) : 1.f) * qa.qscale;
 #pragma unroll
     for (int f = 0; f < F; ++f) {
       kk[f].x *= nk; kk[f].y *= nk; kk[f].z *= nk; kk[f].w *= nk;
       qq[f].x *= nq; qq[f].y *= nq; qq[f].z *= nq; qq[f].w *= nq;
-    }
-  } else if (QK != 0) {
-#pragma unroll
-    for (int f = 0; f < F; ++f) {
-      qq[f].x *= qa.qscale; qq[f].y *= qa.qscale; qq[f].z *= qa.qscale; qq[f].w *= qa.qscale;
     }
   }
 
