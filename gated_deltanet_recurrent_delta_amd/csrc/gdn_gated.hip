@@ -58,6 +58,11 @@ __global__ __launch_bounds__(64 * WPB) void gated_recurrent_kernel(
     const float* __restrict__ bgate, const float* __restrict__ wgate,
     const float* S0, float* ST, TOut* __restrict__ o, int BH, int H, int T,
     int dv) {
+  // The one-token instance (P = 1) is launched only for T == 1; fixing T
+  // there leaves its step without a branch.  With the run-time T (a token
+  // loop, a guarded prefetch) the decode took 24.2 instead of 23.4 us at
+  // B=64, H=16, dk=dv=128.
+  if constexpr (P == 1) T = 1;
   constexpr int F = DK / 64;            // float4 per lane per row
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * WPB + (threadIdx.x >> 6);
@@ -123,13 +128,8 @@ __global__ __launch_bounds__(64 * WPB) void gated_recurrent_kernel(
       const TokIn<F, NG> x = ring[i];
       // unconditional (clamped) prefetch: a load under a branch would make
       // the compiler's waits after it drain every load in flight.  The
-      // one-token instance (launched for T == 1) skips it: there is no
-      // next token, and its loads are all needed at once anyway.
-      if constexpr (P > 1) {
-        load_tok(ring[i], min(t0 + j + P, T - 1));
-      } else {
-        if (T > 1) load_tok(ring[i], min(t0 + j + P, T - 1));
-      }
+      // one-token instance has no next token.
+      if constexpr (P > 1) load_tok(ring[i], min(t0 + j + P, T - 1));
 #pragma unroll
       for (int g = 0; g < NG; ++g) ob[j][g] = 0.f;
       if (t0 + j >= T) continue;          // past the last token (uniform per wave)
